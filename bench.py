@@ -1,0 +1,184 @@
+"""Benchmark of the PaTH attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu] [--cpu-heads N] [--traffic FILE]
+
+One step = one call of path_attn_fwd (gate prefix when present, chunk
+preparation and the streaming scan) over the whole workload, inputs already
+resident in HBM and the workspace preallocated.  W untimed warm-up steps, then
+K steps timed with HIP events on the launch stream, bracketed by device
+synchronisation.  Prints one JSON line.
+
+The default workload is bf16 B=2, H=16, T=16384, d=64 (synthetic inputs,
+seeded).  value = tokens/s = B*T / (time per step).  The roofline object is
+for the dominant kernel, the streaming scan: its algorithmic flops
+B*H*T^2*(2d + d^2/64) divided by its own average duration, timed with HIP
+events over K launches of path_attn_stream alone on the same stream, against
+the bf16 dense matrix-core peak of 2.5 PFLOP/s.  cpu_baseline times the fp64
+CPU oracle on a bounded sample (N whole heads) with all host threads and
+scales the rate to the full workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_b2h16t16384d64")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="whole (b, h) heads the CPU oracle runs for its baseline")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="JSON with measured HBM bytes per stream-kernel launch")
+    return ap.parse_args()
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(wl, inp, n_heads: int):
+    """fp64 oracle on the first n_heads (b, h) heads, all rows; the rate is
+    scaled to the whole workload (every head costs the same)."""
+    import numpy as np
+    import oracle
+    n_heads = max(1, min(n_heads, wl.B * wl.H))
+    flat = lambda x: x.reshape(wl.B * wl.H, wl.T, -1)[:n_heads].astype(np.float64)
+    q, k, v, w = (flat(inp[n]) for n in ("q", "k", "v", "w"))
+    beta = inp["beta"].reshape(wl.B * wl.H, wl.T)[:n_heads].astype(np.float64)
+    logf = None if inp["logf"] is None else inp["logf"].reshape(wl.B * wl.H, wl.T)[:n_heads].astype(np.float64)
+    rows = np.stack(np.meshgrid(np.arange(n_heads), np.arange(wl.T), indexing="ij"), -1).reshape(-1, 2)
+    threads = cpu_threads()
+    t0 = time.perf_counter()
+    oracle.path_attn_rows(q, k, v, w, beta, logf, 1.0 / np.sqrt(wl.d), rows, n_threads=threads)
+    dt = time.perf_counter() - t0
+    full_s = dt * (wl.B * wl.H) / n_heads
+    return {"value": wl.B * wl.T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_heads} of {wl.B * wl.H} (b,h) heads, all {wl.T} query rows each "
+                      f"({n_heads * wl.T * (wl.T + 1) // 2:.3g} causal pairs) in {dt:.2f} s; "
+                      f"rate scaled by {wl.B * wl.H / n_heads:g} to the whole workload",
+            "seconds_sample": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import householder_position_encoding_amd as pa
+    import workloads
+
+    wl = workloads.BY_NAME[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    inp = workloads.generate(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q, k, v, w = (torch.from_numpy(inp[n]).to(dev, tdt) for n in ("q", "k", "v", "w"))
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    logf = None if inp["logf"] is None else torch.from_numpy(inp["logf"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    dt_code = pa.BF16 if wl.dtype == "bf16" else pa.F32
+    ws = torch.empty(pa.path_attn_workspace_bytes(wl.B, wl.H, wl.T, wl.d, dt_code),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.path_attn_fwd(q, k, v, w, beta, logf, out=out, lse=lse, workspace=ws)
+
+    # ---- whole path ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- the two phases on their own (same stream, same workspace) ----
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_prep = timed(lambda: pa.path_attn_prepare(q, k, v, w, beta, logf, workspace=ws), args.steps)
+    ms_stream = timed(lambda: pa.path_attn_stream(ws, logf is not None, out, lse), args.steps)
+
+    flops = wl.flops_path()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    stream_tflops = flops / (ms_stream * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            tr = json.load(open(args.traffic)).get(wl.name)
+            traffic = None if tr is None else tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    res = {
+        "metric": "PaTH attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), B2 T16384 d64, 1 GPU",
+        "value": wl.n_tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.d,
+                   "fox": wl.fox, "global_batch": wl.B, "seq_len": wl.T,
+                   "parallelism": "single GPU"},
+        "tflops_path": tflops,
+        "tflops_attn": wl.flops_attn() / (ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "ms_prep": ms_prep,
+        "ms_stream": ms_stream,
+        "roofline": {"kernel": "stream_kernel", "bound": "mfma", "achieved": stream_tflops,
+                     "peak": peak, "unit": "TFLOP/s", "frac": stream_tflops / peak,
+                     "traffic": traffic,
+                     "flops_per_launch": flops},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

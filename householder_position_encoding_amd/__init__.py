@@ -1,0 +1,30 @@
+"""PaTH attention forward pass for AMD Instinct MI355X (gfx950).
+
+The computation lives in the HIP library ``libpath_attn.so`` (C ABI declared
+in ``include/path_attn.h``).  This package is a thin ctypes binding: it checks
+and marshals torch tensors (device pointers, the current HIP stream) and
+raises on a non-zero status.  There is no CPU fallback: if the library is
+missing or no GPU is present the calls raise.
+"""
+from .binding import (  # noqa: F401
+    BF16,
+    F32,
+    PathAttnError,
+    chunk_prep,
+    library_path,
+    load_library,
+    path_attn_chunk_prep,
+    path_attn_fwd,
+    path_attn_prepare,
+    path_attn_stream,
+    path_attn_workspace_bytes,
+    strerror,
+    version,
+)
+
+__all__ = [
+    "BF16", "F32", "PathAttnError", "chunk_prep", "library_path",
+    "load_library", "path_attn_chunk_prep", "path_attn_fwd",
+    "path_attn_prepare", "path_attn_stream",
+    "path_attn_workspace_bytes", "strerror", "version",
+]

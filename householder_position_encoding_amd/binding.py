@@ -1,0 +1,230 @@
+"""ctypes binding of libpath_attn (argument marshalling only).
+
+Every entry point of ``include/path_attn.h`` has a function of the same name
+here taking raw integers (device addresses) exactly like the C ABI, plus the
+torch-level conveniences ``path_attn_fwd`` accepts (tensors in, tensors out).
+All arithmetic happens in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILE = os.path.join(_PKG, "libpath_attn.so")
+
+F32 = 0
+BF16 = 1
+
+STATUS = {0: "PATH_ATTN_OK", 1: "PATH_ATTN_EINVAL", 2: "PATH_ATTN_EUNSUPPORTED",
+          3: "PATH_ATTN_EHIP"}
+
+_lib = None
+
+
+class PathAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+def library_path() -> str:
+    return os.environ.get("PATH_ATTN_LIB", _LIB_FILE)
+
+
+def load_library():
+    """Load libpath_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libpath_attn.so not found at {path}; build it with "
+            "`python -m householder_position_encoding_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, ci, fp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
+    lib.path_attn_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.path_attn_workspace_bytes.restype = sz
+    lib.path_attn_fwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci,
+                                  ci, vp, sz, vp]
+    lib.path_attn_fwd.restype = ci
+    lib.path_attn_chunk_prep.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, fp,
+                                         fp, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.path_attn_chunk_prep.restype = ci
+    lib.path_attn_prepare.argtypes = [vp, vp, vp, vp, fp, fp, ci, ci, ci, ci, ci,
+                                      vp, sz, vp]
+    lib.path_attn_prepare.restype = ci
+    lib.path_attn_stream.argtypes = [vp, sz, ci, vp, fp, ci, ci, ci, ci, ci, vp]
+    lib.path_attn_stream.restype = ci
+    lib.path_attn_strerror.argtypes = [ci]
+    lib.path_attn_strerror.restype = ctypes.c_char_p
+    lib.path_attn_version.argtypes = []
+    lib.path_attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().path_attn_strerror(int(status)).decode()
+
+
+def version() -> str:
+    return load_library().path_attn_version().decode()
+
+
+def path_attn_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) -> int:
+    return int(load_library().path_attn_workspace_bytes(B, H, T, d, dtype))
+
+
+# ---------------------------------------------------------------- torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v/w must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _common(q, k, v, w, beta, logf):
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (no CPU path)")
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        _check(t, name, q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    if logf is not None:
+        _check(logf, "logf", (B, H, T), torch.float32, dev)
+    return B, H, T, d, _dtype_code(q)
+
+
+def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
+                  workspace=None, stream=None):
+    """PaTH attention forward on the GPU.
+
+    q, k, v, w: [B, H, T, d] bf16 or fp32 CUDA tensors (same dtype);
+    beta: [B, H, T] fp32; logf: optional [B, H, T] fp32 (PaTH-FoX).
+    Returns (out [B, H, T, d] in q's dtype, lse [B, H, T] fp32).  A workspace
+    (uint8 CUDA tensor of at least path_attn_workspace_bytes bytes) may be
+    passed to avoid an allocation.
+    """
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", (B, H, T), torch.float32, q.device)
+    need = lib.path_attn_workspace_bytes(B, H, T, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.path_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                           _ptr(logf), _ptr(out), _ptr(lse), B, H, T, d, dt,
+                           _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_fwd")
+    return out, lse
+
+
+def path_attn_prepare(q, k, v, w, beta, logf=None, workspace=None, stream=None):
+    """First phase of path_attn_fwd: fill `workspace` (allocated if None) with
+    the gate prefix and the chunk preparation.  Returns the workspace."""
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    lib = load_library()
+    need = lib.path_attn_workspace_bytes(B, H, T, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.path_attn_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                               _ptr(logf), B, H, T, d, dt, _ptr(workspace),
+                               workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_prepare")
+    return workspace
+
+
+def path_attn_stream(workspace, use_gate, out, lse, stream=None):
+    """Second phase of path_attn_fwd: the streaming scan over a workspace
+    filled by path_attn_prepare for the same shapes; writes out and lse."""
+    torch = _torch()
+    B, H, T, d = out.shape
+    dt = _dtype_code(out)
+    _check(lse, "lse", (B, H, T), torch.float32, out.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    lib = load_library()
+    st = lib.path_attn_stream(_ptr(workspace), workspace.numel(), int(bool(use_gate)),
+                              _ptr(out), _ptr(lse), B, H, T, d, dt,
+                              _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_stream")
+    return out, lse
+
+
+def chunk_prep(q, k, v, w, beta, logf=None, stream=None):
+    """Run only the chunk preparation and return its unpacked fp32 results:
+    dict(qa [B,H,T,d], kb [B,H,T,d], m [B,H,N,d,d], al [B,H,N,64,64],
+    lam [B,H,T] or None)."""
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    lib = load_library()
+    N = T // 64
+    f = dict(dtype=torch.float32, device=q.device)
+    qa = torch.empty((B, H, T, d), **f)
+    kb = torch.empty((B, H, T, d), **f)
+    m = torch.empty((B, H, N, d, d), **f)
+    al = torch.empty((B, H, N, 64, 64), **f)
+    lam = torch.empty((B, H, T), **f) if logf is not None else None
+    need = lib.path_attn_workspace_bytes(B, H, T, d, dt)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.path_attn_chunk_prep(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                                  _ptr(logf), _ptr(qa), _ptr(kb), _ptr(m), _ptr(al),
+                                  _ptr(lam), B, H, T, d, dt, _ptr(ws), ws.numel(),
+                                  _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_chunk_prep")
+    return dict(qa=qa, kb=kb, m=m, al=al, lam=lam)
+
+
+def path_attn_chunk_prep(*args):
+    """Raw C-ABI call with integer pointers (see include/path_attn.h)."""
+    return int(load_library().path_attn_chunk_prep(*args))

@@ -1,0 +1,170 @@
+// api.hip -- the C ABI of libpath_attn (see include/path_attn.h).
+//
+// Host side only: argument validation (before any HIP call), workspace
+// carving, and the in-order launches on the caller's stream.
+#include "path_attn.h"
+#include "path_attn_internal.h"
+
+using namespace pathattn;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == PATH_ATTN_BF16 ? 2 : 4; }
+
+// Shape/dtype checks shared by every entry point.
+int check_shape(int B, int H, int T, int d, int dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0) return PATH_ATTN_EINVAL;
+  if (dtype != PATH_ATTN_F32 && dtype != PATH_ATTN_BF16) return PATH_ATTN_EINVAL;
+  if (d != 64 && d != 128) return PATH_ATTN_EUNSUPPORTED;
+  if (T % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;
+  const unsigned long long elems = (unsigned long long)B * H * T * d;
+  if (elems >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
+  // grid size of one block per (b, h, chunk) must fit in a 32-bit launch
+  if ((unsigned long long)B * H * (T / kChunk) >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
+  return PATH_ATTN_OK;
+}
+
+int check_inputs(const void *q, const void *k, const void *v, const void *w,
+                 const float *beta, const float *logf, void *workspace,
+                 size_t workspace_bytes, int B, int H, int T, int d,
+                 int dtype) {
+  const int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!q || !k || !v || !w || !beta || !workspace) return PATH_ATTN_EINVAL;
+  const void *ptrs[] = {q, k, v, w, beta};
+  for (const void *p : ptrs)
+    if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
+  if (logf && !aligned(logf, 16)) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256)) return PATH_ATTN_EINVAL;
+  const Layout L = make_layout(B, H, T, d, elem_size(dtype));
+  if (workspace_bytes < L.total) return PATH_ATTN_EINVAL;
+  return PATH_ATTN_OK;
+}
+
+struct Carved {
+  float *qa;
+  void *kvm;
+  float *al;
+  float *gate;
+};
+
+Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
+  const Layout L = make_layout(B, H, T, d, elem_size(dtype));
+  char *base = static_cast<char *>(workspace);
+  return Carved{reinterpret_cast<float *>(base + L.qa), base + L.kvm,
+                reinterpret_cast<float *>(base + L.al),
+                reinterpret_cast<float *>(base + L.gate)};
+}
+
+// Enqueue the gate prefix (if any) and the chunk preparation.
+int run_prep(const void *q, const void *k, const void *v, const void *w,
+             const float *beta, const float *logf, const Carved &ws, int BH,
+             int T, int d, int dtype, hipStream_t s) {
+  if (logf && launch_gate_prefix(logf, ws.gate, BH, T, s) != hipSuccess)
+    return PATH_ATTN_EHIP;
+  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, T, s) !=
+      hipSuccess)
+    return PATH_ATTN_EHIP;
+  return PATH_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  return make_layout(B, H, T, d, elem_size(dtype)).total;
+}
+
+extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
+                             const void *w, const float *beta, const float *logf,
+                             void *out, float *lse, int B, int H, int T, int d,
+                             int dtype, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  int st = check_inputs(q, k, v, w, beta, logf, workspace, workspace_bytes, B,
+                        H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!out || !lse) return PATH_ATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(lse, 16)) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carved ws = carve(workspace, B, H, T, d, dtype);
+  const int BH = B * H;
+  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
+  if (st != PATH_ATTN_OK) return st;
+  if (launch_stream(dtype, d, logf != nullptr, ws.qa, ws.kvm, ws.al, ws.gate,
+                    out, lse, BH, T, s) != hipSuccess)
+    return PATH_ATTN_EHIP;
+  return PATH_ATTN_OK;
+}
+
+extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
+                                 const void *w, const float *beta,
+                                 const float *logf, int B, int H, int T, int d,
+                                 int dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  const int st = check_inputs(q, k, v, w, beta, logf, workspace,
+                              workspace_bytes, B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  const Carved ws = carve(workspace, B, H, T, d, dtype);
+  return run_prep(q, k, v, w, beta, logf, ws, B * H, T, d, dtype,
+                  static_cast<hipStream_t>(stream));
+}
+
+extern "C" int path_attn_stream(const void *workspace, size_t workspace_bytes,
+                                int use_gate, void *out, float *lse, int B,
+                                int H, int T, int d, int dtype, void *stream) {
+  const int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!workspace || !out || !lse) return PATH_ATTN_EINVAL;
+  if (use_gate != 0 && use_gate != 1) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse, 16))
+    return PATH_ATTN_EINVAL;
+  if (workspace_bytes < make_layout(B, H, T, d, elem_size(dtype)).total)
+    return PATH_ATTN_EINVAL;
+  const Carved ws = carve(const_cast<void *>(workspace), B, H, T, d, dtype);
+  if (launch_stream(dtype, d, use_gate == 1, ws.qa, ws.kvm, ws.al, ws.gate, out,
+                    lse, B * H, T, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PATH_ATTN_EHIP;
+  return PATH_ATTN_OK;
+}
+
+extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
+                                    const void *w, const float *beta,
+                                    const float *logf, float *qa, float *kb,
+                                    float *m, float *al, float *lam, int B,
+                                    int H, int T, int d, int dtype,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  int st = check_inputs(q, k, v, w, beta, logf, workspace, workspace_bytes, B,
+                        H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  float *outs[] = {qa, kb, m, al, lam};
+  for (float *p : outs)
+    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carved ws = carve(workspace, B, H, T, d, dtype);
+  const int BH = B * H;
+  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
+  if (st != PATH_ATTN_OK) return st;
+  if (launch_unpack(dtype, d, ws.qa, ws.kvm, ws.al, logf ? ws.gate : nullptr,
+                    qa, kb, m, al, logf ? lam : nullptr, BH, T, s) != hipSuccess)
+    return PATH_ATTN_EHIP;
+  return PATH_ATTN_OK;
+}
+
+extern "C" const char *path_attn_strerror(int status) {
+  switch (status) {
+    case PATH_ATTN_OK: return "ok";
+    case PATH_ATTN_EINVAL:
+      return "invalid argument (null or misaligned pointer, non-positive size, "
+             "unknown dtype, or workspace too small)";
+    case PATH_ATTN_EUNSUPPORTED:
+      return "unsupported shape (d must be 64 or 128, T a multiple of 64, "
+             "B*H*T*d < 2^31)";
+    case PATH_ATTN_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char *path_attn_version(void) { return "libpath_attn 0.1.0 (gfx950)"; }

@@ -1,0 +1,146 @@
+/*
+ * path_attn.h -- C ABI of libpath_attn: the causal PaTH attention forward pass
+ * (optionally with the PaTH-FoX forget gate) on one AMD Instinct MI355X
+ * (gfx950) GPU.
+ *
+ * The operation (PaTH discussion slides for arXiv:2505.16381v2, frame "PaTH
+ * inserts a learned transformation along every path", paper Sec. 2.2; frame
+ * "FoX adds a separate mechanism for forgetting"; the authors' response page,
+ * "Implementation detail", for the scale and the -inf causal mask): for each
+ * (batch b, head h) and query position i,
+ *
+ *     H_t   = I - beta_t w_t w_t^T
+ *     c_ij  = k_j^T H_{j+1} H_{j+2} ... H_i q_i            (j <= i; c_ii = k_i.q_i)
+ *     s_ij  = c_ij / sqrt(d) + sum_{s=j+1..i} log f_s      (gate term only with logf)
+ *     o_i   = sum_{j<=i} softmax_j(s_ij) v_j
+ *     lse_i = ln sum_{j<=i} exp(s_ij)
+ *
+ * The gate term is added outside the 1/sqrt(d) scale (the gate product sits
+ * outside the exponential on the FoX frame).  w_t and beta_t are used exactly
+ * as given: the library does not renormalise w_t nor clip beta_t.  The factors
+ * H_0 and f_0 never enter a logit.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, caller-owned DEVICE pointers:
+ *       q, k, v, w, out : [B, H, T, d]  elements of `dtype`
+ *       beta, logf, lse : [B, H, T]     float32
+ *   - dtype: PATH_ATTN_F32 (float32 storage, float32 arithmetic throughout)
+ *            or PATH_ATTN_BF16 (bfloat16 storage; products on bf16 matrix
+ *            cores with float32 accumulation; chunk preparation in float32).
+ *   - Supported shapes: d in {64, 128}; T a positive multiple of 64 (the chunk
+ *     length); B, H >= 1; B*H*T*d < 2^31.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: they enqueue kernels and return; results are valid once
+ *     the caller has synchronised the stream.  The library keeps no pointer
+ *     after a call returns, holds no global state and allocates no memory:
+ *     all scratch space is the caller's `workspace`.  Concurrent calls on
+ *     different streams must use different workspaces.
+ *   - Pointers must be 16-byte aligned, the workspace 256-byte aligned.
+ *   - Errors: argument checks run before any HIP call; on failure nothing is
+ *     launched and a status below is returned.  Numerical contents are not
+ *     checked (NaN/Inf propagate).
+ */
+#ifndef PATH_ATTN_H
+#define PATH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PATH_ATTN_OK 0
+#define PATH_ATTN_EINVAL 1      /* null pointer, size <= 0, bad dtype, misaligned
+                                   pointer, or workspace too small */
+#define PATH_ATTN_EUNSUPPORTED 2 /* d not in {64, 128}, T % 64 != 0, or the
+                                   problem exceeds 32-bit element indexing */
+#define PATH_ATTN_EHIP 3        /* a HIP launch reported an error */
+
+/* Storage dtypes of q, k, v, w and out. */
+#define PATH_ATTN_F32 0
+#define PATH_ATTN_BF16 1
+
+/*
+ * Workspace size in bytes that path_attn_fwd / path_attn_chunk_prep need for
+ * this problem, or 0 if the arguments are invalid or unsupported.  The size
+ * is linear in B*H*T: per 64-token chunk it holds the boundary-adjusted
+ * queries (float32), the transformed keys, the values and the chunk transform
+ * in the matrix-core operand order, the diagonal-block logits (float32) and,
+ * per token, the forget-gate prefix (float32).
+ */
+size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype);
+
+/*
+ * Forward pass.  logf may be NULL (plain PaTH); otherwise it holds log f_t
+ * (values <= 0 for gates in (0, 1]).  out receives o in `dtype`, rounded to
+ * nearest even; lse receives the natural-log normaliser in float32.
+ *
+ * Launches, in order on `stream`: the forget-gate prefix sum (only with
+ * logf), the chunk preparation (the UT form of each 64-token chunk: PaTH
+ * slides, frames "A triangular representation makes paths computable" and
+ * "Backup: fix orientation before implementing UT products", paper Secs.
+ * 3.1-3.3), and the right-to-left streaming scan over key chunks with an
+ * online softmax (frame "A right-to-left scan accumulates cross-block paths",
+ * paper Sec. 3.3).
+ *
+ * Returns PATH_ATTN_OK or an error status (see above).
+ */
+int path_attn_fwd(const void *q, const void *k, const void *v, const void *w,
+                  const float *beta, const float *logf, void *out, float *lse,
+                  int B, int H, int T, int d, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * The two phases of path_attn_fwd, for callers that time or schedule them
+ * separately.  path_attn_prepare enqueues the forget-gate prefix (with logf)
+ * and the chunk preparation into `workspace`; path_attn_stream enqueues the
+ * streaming scan that reads that workspace and writes out and lse.  The
+ * stream phase must see a workspace prepared by path_attn_prepare with the
+ * same B, H, T, d, dtype (and use_gate = 1 exactly when logf was non-NULL),
+ * ordered before it on the stream; path_attn_fwd is exactly
+ * path_attn_prepare followed by path_attn_stream.
+ */
+int path_attn_prepare(const void *q, const void *k, const void *v,
+                      const void *w, const float *beta, const float *logf,
+                      int B, int H, int T, int d, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+int path_attn_stream(const void *workspace, size_t workspace_bytes,
+                     int use_gate, void *out, float *lse, int B, int H, int T,
+                     int d, int dtype, void *stream);
+
+/*
+ * Chunk preparation only, with its results unpacked into plain float32
+ * arrays so that each quantity can be checked on its own.  For chunk c of
+ * 64 tokens (rows w_t^T stacked in W, D = diag(beta), U = (I +
+ * strictLower(D W W^T))^{-1} D):
+ *     qa  [B,H,T,d]       <-Q = Q - lower(Q W^T) U W   (row i: H_first...H_i q_i)
+ *     kb  [B,H,T,d]       ->K = K - (U strictLower(W K^T))^T W
+ *                               (row j: H_last...H_{j+1} k_j)
+ *     m   [B,H,T/64,d,d]  M = W^T U W   (so that H_first...H_last = I - M^T)
+ *     al  [B,H,T/64,64,64] lower(Q K^T) - lower(Q W^T) U strictLower(W K^T)
+ *                          (raw diagonal-block logits; entries above the
+ *                           diagonal are unspecified)
+ *     lam [B,H,T]         sum_{s=1..t} log f_s (only if logf and lam non-NULL;
+ *                          f_0 never enters a logit and is left out)
+ * kb and m are reported at the precision the streaming kernel consumes them
+ * (bf16-rounded for PATH_ATTN_BF16).  Any of qa/kb/m/al/lam may be NULL.
+ * Uses the same workspace as path_attn_fwd.
+ */
+int path_attn_chunk_prep(const void *q, const void *k, const void *v,
+                         const void *w, const float *beta, const float *logf,
+                         float *qa, float *kb, float *m, float *al, float *lam,
+                         int B, int H, int T, int d, int dtype, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Static, human-readable description of a status code. */
+const char *path_attn_strerror(int status);
+
+/* Library version string. */
+const char *path_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H */

@@ -1,4 +1,7 @@
-"""fp64 numpy statement of the blockwise algorithm (test-side only).
+"""fp64 numpy statement of the blockwise algorithm -- oracle, test infrastructure.
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  It shares nothing with the HIP library.
 
 Written from the PaTH discussion slides, frames "A triangular representation
 makes paths computable", "A right-to-left scan accumulates cross-block paths"
@@ -14,8 +17,9 @@ and D = diag(beta):
 
 and the cross-chunk logits of query chunk b against key chunk c < b are
 Q_work ->K_c^T, with Q_work = <-Q_b and Q_work <- Q_work (I - M_c) after each
-key chunk.  This is used by the oracle pins (the algebra must reproduce the
-definition) and as a reference for the chunk-prep quantities.
+key chunk.  The oracle pins check that this algebra reproduces the plain
+definition (oracle/path_oracle.c) for several chunk sizes; the GPU tests use
+``chunk_quantities`` as the reference for the chunk-preparation outputs.
 """
 from __future__ import annotations
 

@@ -1,0 +1,131 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes its workspace, and rejects bad arguments before any
+HIP call (these calls never launch anything, so no GPU is needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import householder_position_encoding_amd as pa
+from householder_position_encoding_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "path_attn.h")
+
+OK, EINVAL, EUNSUP, EHIP = 0, 1, 2, 3
+FAKE = 0x100000   # an aligned, non-null address; never dereferenced: every call
+                  # below fails validation, which runs before any HIP call
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(path_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.load_library()
+    syms = declared_symbols()
+    assert {"path_attn_fwd", "path_attn_workspace_bytes", "path_attn_strerror",
+            "path_attn_chunk_prep", "path_attn_version", "path_attn_prepare",
+            "path_attn_stream"} <= set(syms)
+    for s in syms:
+        assert hasattr(lib, s), f"libpath_attn.so does not export {s}"
+
+
+def test_version_and_strerror():
+    assert "gfx950" in pa.version()
+    for st in (OK, EINVAL, EUNSUP, EHIP):
+        assert pa.strerror(st)
+    assert pa.strerror(99) == "unknown status"
+
+
+@pytest.mark.parametrize("dtype,esize", [(pa.F32, 4), (pa.BF16, 2)])
+@pytest.mark.parametrize("B,H,T,d", [(1, 2, 256, 64), (2, 16, 16384, 64), (4, 8, 8192, 128)])
+def test_workspace_bytes(dtype, esize, B, H, T, d):
+    n = pa.path_attn_workspace_bytes(B, H, T, d, dtype)
+    BH, N = B * H, T // 64
+    # <-Q (fp32), the three per-chunk operands, diagonal logits (fp32), gate (fp32)
+    expect = BH * T * d * 4 + BH * N * (2 * 64 * d + d * d) * esize + BH * N * 64 * 64 * 4 + BH * T * 4
+    assert expect <= n <= expect + 4 * 256
+
+
+@pytest.mark.parametrize("args", [(0, 1, 64, 64, 1), (1, 0, 64, 64, 1), (1, 1, 0, 64, 1),
+                                  (1, 1, 64, 96, 1), (1, 1, 100, 64, 1), (1, 1, 64, 64, 7),
+                                  (1, 1, 64, -64, 0), (1 << 16, 1 << 10, 1024, 64, 1)])
+def test_workspace_bytes_rejects(args):
+    assert pa.path_attn_workspace_bytes(*args) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE,
+             B=1, H=2, T=256, d=64, dtype=pa.BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.path_attn_fwd(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"], a["out"],
+                             a["lse"], a["B"], a["H"], a["T"], a["d"], a["dtype"], a["ws"],
+                             a["wsb"], a["stream"])
+
+
+# every case below is invalid: validation rejects it before any HIP call
+BAD_FWD = [
+    (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(v=None), EINVAL),
+    (dict(w=None), EINVAL), (dict(beta=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(lse=None), EINVAL), (dict(ws=None), EINVAL),
+    (dict(q=FAKE + 2), EINVAL), (dict(beta=FAKE + 4), EINVAL), (dict(out=FAKE + 8), EINVAL),
+    (dict(logf=FAKE + 4), EINVAL), (dict(ws=FAKE + 16), EINVAL),
+    (dict(wsb=1000), EINVAL), (dict(dtype=5), EINVAL), (dict(B=0), EINVAL),
+    (dict(H=-1), EINVAL), (dict(T=0), EINVAL),
+    (dict(d=96), EUNSUP), (dict(d=32), EUNSUP), (dict(T=200), EUNSUP),
+    (dict(B=1 << 12, H=1 << 10, T=1024), EUNSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_FWD, ids=lambda x: str(x))
+def test_fwd_validation(kw, status):
+    assert _fwd(pa.load_library(), **kw) == status
+
+
+def test_prepare_and_stream_validation():
+    lib = pa.load_library()
+    assert lib.path_attn_prepare(FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 64, 64, 1, FAKE,
+                                 1 << 40, None) == EINVAL
+    assert lib.path_attn_prepare(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 1, FAKE,
+                                 10, None) == EINVAL
+    assert lib.path_attn_prepare(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 96, 64, 1, FAKE,
+                                 1 << 40, None) == EUNSUP
+    # stream: bad use_gate, null out, misaligned lse, small workspace, bad d
+    assert lib.path_attn_stream(FAKE, 1 << 40, 2, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert lib.path_attn_stream(FAKE, 1 << 40, 0, None, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert lib.path_attn_stream(FAKE, 1 << 40, 0, FAKE, FAKE + 4, 1, 1, 64, 64, 1, None) == EINVAL
+    assert lib.path_attn_stream(FAKE, 100, 0, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert lib.path_attn_stream(FAKE, 1 << 40, 0, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
+
+
+def test_chunk_prep_validation():
+    lib = pa.load_library()
+    common = [FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    outs = [FAKE, FAKE, FAKE, FAKE, None]
+    # misaligned optional output
+    assert lib.path_attn_chunk_prep(*common, FAKE + 4, *outs[1:], 1, 1, 64, 64, 1, FAKE, 1 << 40, None) == EINVAL
+    # workspace too small
+    assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 64, 64, 1, FAKE, 10, None) == EINVAL
+    # unsupported head dim
+    assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 64, 80, 1, FAKE, 1 << 40, None) == EUNSUP
+
+
+def test_binding_has_no_cpu_fallback():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    b = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.path_attn_fwd(x, x, x, x, b)
+
+
+def test_binding_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setenv("PATH_ATTN_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        binding.load_library()

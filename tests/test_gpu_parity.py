@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs |GPU - oracle| over every compared element <= 1e-4 for float32
+inputs, and <= 2e-2 on o / 1e-2 on lse for bf16 inputs.  Small cases compare
+every row; the full-size workloads compare a stratified sample of rows (the
+whole last query chunk of each sampled head, chunk boundaries, random rows),
+computed row by row by the oracle, in the same launch configuration the
+benchmark uses.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle.chunked import chunk_quantities
+from tests.gpu_util import (TOL, oracle_full, oracle_rows, run_hip, sample_rows,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _assert_close(name, dtype, out, lse, o_ref, l_ref):
+    tol_o, tol_l = TOL[dtype]
+    eo = float(np.max(np.abs(out - o_ref)))
+    el = float(np.max(np.abs(lse - l_ref)))
+    _log(f"{name}: max|do|={eo:.3g} (tol {tol_o}) max|dlse|={el:.3g} (tol {tol_l})")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)), name
+    assert eo <= tol_o, f"{name}: o error {eo} > {tol_o}"
+    assert el <= tol_l, f"{name}: lse error {el} > {tol_l}"
+
+
+# ------------------------------------------------------------ chunk prep
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("fox", [False, True])
+def test_chunk_prep_matches_oracle_algebra(dtype, d, fox):
+    """Per-chunk <-Q, ->K, M, diagonal logits and the gate prefix against the
+    fp64 statement of the UT formulas (pinned to the definition on the CPU)."""
+    import householder_position_encoding_amd as pa
+    B, H, T = 1, 2, 192
+    inp = workloads.small(dtype, B, H, T, d, seed=21, beta_sigma=1.5, fox=fox)
+    dev = to_device(inp, dtype)
+    res = pa.chunk_prep(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"])
+    got = {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in res.items()}
+    C = 64
+    low = np.tril(np.ones((C, C), dtype=bool))
+    rel = 1e-4 if dtype == "f32" else 2.0 ** -8
+    for b in range(B):
+        for h in range(H):
+            for c in range(T // C):
+                sl = slice(c * C, (c + 1) * C)
+                args = [inp[x][b, h, sl].astype(np.float64) for x in ("q", "k", "w")]
+                U, Qa, Kb, M, Al = chunk_quantities(*args, inp["beta"][b, h, sl].astype(np.float64))
+                for name, ref, g, r in (("qa", Qa, got["qa"][b, h, sl], 1e-4),
+                                        ("kb", Kb, got["kb"][b, h, sl], rel),
+                                        ("m", M, got["m"][b, h, c], rel),
+                                        ("al", Al[low], got["al"][b, h, c][low], 1e-4)):
+                    scale = 1.0 + np.max(np.abs(ref))
+                    err = np.max(np.abs(g - ref) / (np.abs(ref) * r + 1e-4 * scale))
+                    assert err <= 1.0, f"{name} chunk {(b, h, c)}: normalised error {err}"
+    if fox:
+        f = inp["logf"].astype(np.float64).copy()
+        f[..., 0] = 0.0   # f_0 never enters a logit; the prefix starts at t = 1
+        lam_ref = np.cumsum(f, axis=-1)
+        assert np.max(np.abs(got["lam"] - lam_ref)) <= 1e-5 * (1 + np.max(np.abs(lam_ref)))
+
+
+# ------------------------------------------------------------ small, all rows
+
+SMALL_CASES = [
+    # dtype, d, fox, B, H, T, extra generator options
+    ("f32", 64, False, 1, 2, 64, {}),
+    ("f32", 64, False, 2, 2, 320, {}),
+    ("f32", 128, True, 1, 3, 256, {}),
+    ("f32", 128, False, 1, 1, 448, {"beta_sigma": 1.5, "near2_frac": 0.1}),
+    ("bf16", 64, False, 1, 2, 64, {}),
+    ("bf16", 64, False, 2, 3, 576, {"beta_sigma": 1.5}),
+    ("bf16", 64, True, 1, 2, 512, {}),
+    ("bf16", 128, False, 2, 2, 384, {"beta_sigma": 1.5, "near2_frac": 0.1}),
+    ("bf16", 128, True, 1, 2, 640, {}),
+    ("bf16", 64, False, 1, 2, 256, {"beta_const": 0.0}),     # plain causal attention
+    ("f32", 64, False, 1, 2, 512, {"beta_const": 2.0}),      # exact reflections
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: f"{c[0]}-d{c[1]}-fox{int(c[2])}-b{c[3]}h{c[4]}t{c[5]}-{'-'.join(f'{k}{v}' for k, v in c[6].items())}")
+def test_parity_small_all_rows(case):
+    dtype, d, fox, B, H, T, opts = case
+    inp = workloads.small(dtype, B, H, T, d, seed=7 + T + d, fox=fox, **opts)
+    out, lse = run_hip(to_device(inp, dtype))
+    o_ref, l_ref = oracle_full(inp)
+    _assert_close(f"small {case}", dtype, out, lse, o_ref, l_ref)
+
+
+# ------------------------------------------------------------ full workloads
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_parity_workload(wl):
+    """The five workloads at full size in the benchmark's launch configuration;
+    the tiny one compares every row, the others sampled rows of the first and
+    last (b, h)."""
+    _log(f"workload {wl.name}: generating")
+    inp = workloads.generate(wl)
+    out, lse = run_hip(to_device(inp, wl.dtype))
+    if wl.B * wl.H * wl.T <= 4096:
+        o_ref, l_ref = oracle_full(inp)
+        _assert_close(wl.name, wl.dtype, out, lse, o_ref, l_ref)
+        return
+    rng = np.random.default_rng(12345)
+    heads = [(0, 0), (wl.B - 1, wl.H - 1)]
+    rows = [sample_rows(wl.T, rng) for _ in heads]
+    o_ref, l_ref = oracle_rows(inp, heads, rows)
+    got_o = np.concatenate([out[b, h, r] for (b, h), r in zip(heads, rows)])
+    got_l = np.concatenate([lse[b, h, r] for (b, h), r in zip(heads, rows)])
+    _assert_close(wl.name, wl.dtype, got_o, got_l, o_ref, l_ref)
+
+
+# ------------------------------------------------------------ diagnostics
+
+def test_swap_closed_form_on_gpu():
+    """beta = 2, w_t = (e_a - e_b)/sqrt(2): every logit is k_j . (q_i with the
+    coordinate swaps t = i..j+1 applied), so the GPU result must match the
+    softmax of those closed-form logits (float32 path)."""
+    rng = np.random.default_rng(5)
+    B, H, T, d = 1, 1, 256, 64
+    q = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    w = np.zeros((B, H, T, d), dtype=np.float32)
+    pairs = []
+    for t in range(T):
+        a, b = rng.choice(d, size=2, replace=False)
+        pairs.append((a, b))
+        w[0, 0, t, a], w[0, 0, t, b] = np.float32(1 / np.sqrt(2)), -np.float32(1 / np.sqrt(2))
+    beta = np.full((B, H, T), 2.0, dtype=np.float32)
+    inp = dict(q=q, k=k, v=v, w=w, beta=beta, logf=None)
+    out, lse = run_hip(to_device(inp, "f32"))
+    scale = 1 / np.sqrt(d)
+    S = np.full((T, T), -np.inf)
+    for i in range(T):
+        z = q[0, 0, i].astype(np.float64)
+        for j in range(i, -1, -1):
+            S[i, j] = scale * (k[0, 0, j].astype(np.float64) @ z)
+            if j:
+                a, b = pairs[j]
+                z[a], z[b] = z[b], z[a]
+    m = S.max(1, keepdims=True)
+    P = np.exp(S - m)
+    Z = P.sum(1, keepdims=True)
+    _assert_close("swap closed form", "f32", out[0, 0], lse[0, 0],
+                  (P / Z) @ v[0, 0].astype(np.float64), (m + np.log(Z))[:, 0])
+
+
+@pytest.mark.parametrize("wl", [workloads.REFLECT_F32, workloads.REFLECT_BF16], ids=lambda w: w.name)
+def test_reflection_chain(wl):
+    """beta = 2 everywhere (nothing decays): errors of the long transform chain
+    stay visible.  float32 must meet its tolerance; the bf16 error is reported
+    and only sanity-bounded (the graded bf16 tolerances assume decaying
+    paths)."""
+    inp = workloads.generate(wl)
+    out, lse = run_hip(to_device(inp, wl.dtype))
+    rng = np.random.default_rng(2)
+    heads = [(0, 0), (0, 1)]
+    rows = [sample_rows(wl.T, rng, n_random=64) for _ in heads]
+    o_ref, l_ref = oracle_rows(inp, heads, rows)
+    got_o = np.concatenate([out[b, h, r] for (b, h), r in zip(heads, rows)])
+    got_l = np.concatenate([lse[b, h, r] for (b, h), r in zip(heads, rows)])
+    if wl.dtype == "f32":
+        _assert_close(wl.name, "f32", got_o, got_l, o_ref, l_ref)
+    else:
+        eo, el = np.max(np.abs(got_o - o_ref)), np.max(np.abs(got_l - l_ref))
+        _log(f"{wl.name}: max|do|={eo:.3g} max|dlse|={el:.3g} (reported)")
+        assert eo < 0.5 and el < 0.5
+
+
+def test_sharp_attention_diagnostic():
+    """q scaled by 3 (logits three times larger): the bf16 rounding of the
+    running query tile and of ->K grows with the logits, so this case is
+    reported and held to a looser sanity bound rather than the graded
+    tolerance."""
+    inp = workloads.small("bf16", 1, 2, 256, 64, seed=7 + 256 + 64, q_scale=3.0)
+    out, lse = run_hip(to_device(inp, "bf16"))
+    o_ref, l_ref = oracle_full(inp)
+    eo, el = np.max(np.abs(out - o_ref)), np.max(np.abs(lse - l_ref))
+    _log(f"sharp q x3: max|do|={eo:.3g} max|dlse|={el:.3g} (reported)")
+    assert eo < 5e-2 and el < 5e-2
+
+
+def test_bitwise_deterministic():
+    """No atomics: two runs give identical bits."""
+    inp = workloads.small("bf16", 2, 2, 512, 64, seed=3, fox=True)
+    dev = to_device(inp, "bf16")
+    o1, l1 = run_hip(dev)
+    o2, l2 = run_hip(dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_first_token_factors_unused(dtype, d):
+    """w_0, beta_0 and log f_0 never enter a logit: outputs are bitwise equal
+    after changing them."""
+    inp = workloads.small(dtype, 1, 2, 256, d, seed=9, fox=True)
+    o1, l1 = run_hip(to_device(inp, dtype))
+    inp2 = {k: (None if v is None else v.copy()) for k, v in inp.items()}
+    inp2["w"][:, :, 0] = inp2["w"][:, :, 5]
+    inp2["beta"][:, :, 0] = 1.75
+    inp2["logf"][:, :, 0] = -2.5
+    o2, l2 = run_hip(to_device(inp2, dtype))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_workspace_reuse_and_explicit_buffers():
+    """A caller-provided workspace reused by a second, smaller call gives the
+    same result as a fresh allocation."""
+    import torch
+    import householder_position_encoding_amd as pa
+    big = workloads.small("bf16", 1, 4, 512, 128, seed=31, fox=True)
+    small = workloads.small("bf16", 1, 2, 192, 128, seed=32)
+    need = pa.path_attn_workspace_bytes(1, 4, 512, 128, pa.BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ob, lb = run_hip(to_device(big, "bf16"), workspace=ws)
+    os_, ls_ = run_hip(to_device(small, "bf16"), workspace=ws)
+    os2, ls2 = run_hip(to_device(small, "bf16"))
+    assert np.array_equal(os_, os2) and np.array_equal(ls_, ls2)
+    o_ref, l_ref = oracle_full(small)
+    _assert_close("reused workspace", "bf16", os_, ls_, o_ref, l_ref)
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    import householder_position_encoding_amd as pa
+    inp = workloads.small("bf16", 1, 1, 128, 64, seed=1)
+    dev = to_device(inp, "bf16")
+    with pytest.raises(ValueError):
+        pa.path_attn_fwd(dev["q"][..., :32], dev["k"], dev["v"], dev["w"], dev["beta"])
+    with pytest.raises(TypeError):
+        pa.path_attn_fwd(dev["q"].half(), dev["k"], dev["v"], dev["w"], dev["beta"])
+    # T not a multiple of 64 is reported by the library as unsupported
+    t = lambda x: x[:, :, :100].contiguous()
+    with pytest.raises(pa.PathAttnError) as e:
+        pa.path_attn_fwd(t(dev["q"]), t(dev["k"]), t(dev["v"]), t(dev["w"]), t(dev["beta"]))
+    assert e.value.status == 2
+    torch.cuda.synchronize()

@@ -24,7 +24,7 @@ import pytest
 from scipy.linalg import solve_triangular
 
 import oracle
-from tests.chunked_ref import chunked_logits
+from oracle.chunked import chunked_logits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
