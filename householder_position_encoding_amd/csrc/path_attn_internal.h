@@ -1,37 +1,41 @@
 // path_attn_internal.h -- shared definitions of the libpath_attn kernels.
 //
+// Register image.  The streaming kernel keeps its running query tile, its
+// scores and its output in MFMA 32x32 accumulators in transposed orientation
+// (rows = d or key index, columns = the wave's 32 queries).  In a 32x32
+// accumulator block, lane l (g = l/32) register r (0..15) holds
+//
+//     row acc_row(r, g) = 8*(r/4) + 4*g + r%4,   column l%32.
+//
+// Taking KPL consecutive accumulator registers per k-step as the B operand of
+// the next MFMA makes the k-th contraction slot of lane group g correspond to
+// the physical row
+//
+//     frag_row(s, g, t) = 32*(rg/16) + acc_row(rg%16, g),  rg = s*KPL + t,
+//
+// with KPL = 8 for bf16 MFMA 32x32x16 and 1 for fp32 MFMA 32x32x2.  A operands
+// therefore carry the same permutation of their contraction index; the chunk
+// preparation writes them pre-permuted ("fragment order"): blob (mb, s) of an
+// operand X[R][Kc] holds, for lane l, the KPL values
+// X[32*mb + l%32][frag_row(s, l/32, t)] contiguously, blob index
+// mb * (Kc / (2*KPL)) + s.  A fragment is then one contiguous 64*KPL-element
+// block (conflict-free LDS reads, 16-byte global loads).
+//
 // Data layout in HBM (the caller's workspace), per (batch*head) bh and 64-token
 // chunk c (N = T/64 chunks per head):
 //
-//   qa   float [BH][T][D]        boundary-adjusted queries <-Q (row i holds
-//                                H_first...H_i q_i), the starting value of the
-//                                streaming kernel's running query tile.
-//   kvm  elem  [BH][N][KVM(D)]   per chunk, three matrix-core A operands stored
-//                                back to back in "fragment order" (below):
-//                                  KF: ->K   (64 keys x D, contraction over D)
-//                                  VF: V^T   (D x 64 keys, contraction over keys)
-//                                  MF: -M^T  (D x D, contraction over D),
-//                                      M = W^T U W, the chunk transform
-//   al   float [BH][N][64][64]   diagonal-block raw logits (row = query)
-//   gate float [BH][T]           a_t = -log2(e) * sum_{1<=s<=t} log f_s (FoX only)
-//
-// Fragment order.  The streaming kernel keeps its running query tile, scores
-// and output in MFMA accumulators laid out as X^T (rows = d or key index,
-// columns = the wave's 32 queries) and feeds an accumulator straight back as
-// the B operand of the next MFMA.  For a 32x32 accumulator block, lane l
-// (g = l/32) register r holds row 8*(r/4) + 4*g + r%4 of column l%32.  Taking
-// KPL consecutive accumulator registers per k-step as the B operand makes the
-// k-th contraction slot of lane group g correspond to the physical row
-//
-//     frag_row(s, g, t) = 32*(rg/16) + 8*((rg%16)/4) + 4*g + rg%4,
-//     rg = s*KPL + t,   t in [0, KPL),
-//
-// where KPL = 8 for bf16 MFMA 32x32x16 and 1 for fp32 MFMA 32x32x2.  The A
-// operand must use the same permutation of its contraction index, so the
-// chunk-prep kernel writes A operands pre-permuted: blob (mb, s) of an operand
-// X[R][Kc] holds, for lane l, the KPL values X[32*mb + l%32][frag_row(s,l/32,t)]
-// contiguously; blob index = mb * (Kc / (2*KPL)) + s.  A wave then reads one
-// A fragment as one contiguous 64*KPL-element block (conflict-free LDS reads).
+//   qa   float [BH][N][2][D/32][64][16]   boundary-adjusted queries <-Q
+//        (row i: H_first...H_i q_i) as register image: [query block w]
+//        [d block mb][lane][r] = <-Q[32w + lane%32][32mb + acc_row(r, lane/32)]
+//   kvm  elem  [BH][N][KVM(D)]   three A operands in fragment order:
+//          KF: ->K   (64 keys x D, contraction over D)
+//          VF: V^T   (D x 64 keys, contraction over keys)
+//          MF: -M^T  (D x D, contraction over D),  M = W^T U W
+//   al   float [BH][N][3][64][16]  diagonal-block raw logits as register image
+//        of the scores S^T: tiles (query block w, key block mb) = (0,0),
+//        (1,0), (1,1) (tile (0,1) lies wholly above the diagonal):
+//        [tile][lane][r] = Al[32w + lane%32][32mb + acc_row(r, lane/32)]
+//   gate float [BH][T]          a_t = -log2(e) * sum_{1<=s<=t} log f_s (FoX)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,18 +45,29 @@
 namespace pathattn {
 
 constexpr int kChunk = 64;
+constexpr int kAlTiles = 3;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+__host__ __device__ constexpr int acc_row(int r, int g) {
+  return 8 * (r / 4) + 4 * g + (r % 4);
+}
+
 __host__ __device__ constexpr int frag_row(int s, int g, int t, int kpl) {
-  return 32 * ((s * kpl + t) / 16) + 8 * (((s * kpl + t) % 16) / 4) + 4 * g +
-         ((s * kpl + t) % 4);
+  return 32 * ((s * kpl + t) / 16) + acc_row((s * kpl + t) % 16, g);
 }
 
 // Elements of one chunk's kvm block.
 __host__ __device__ constexpr int kvm_elems(int D) { return 2 * kChunk * D + D * D; }
+// Floats of one chunk's register images.
+__host__ __device__ constexpr int qa_floats(int D) { return kChunk * D; }
+__host__ __device__ constexpr int al_floats() { return kAlTiles * 64 * 16; }
+// Tile index of the diagonal-block image for (query block w, key block mb),
+// mb <= w.
+__host__ __device__ constexpr int al_tile(int w, int mb) { return w + mb; }
 
 struct Layout {
   size_t qa, kvm, al, gate, total;
@@ -65,11 +80,11 @@ inline Layout make_layout(int B, int H, int T, int D, size_t esize) {
   Layout L;
   size_t off = 0;
   L.qa = off;
-  off = align256(off + BH * T * D * sizeof(float));
+  off = align256(off + BH * N * qa_floats(D) * sizeof(float));
   L.kvm = off;
   off = align256(off + BH * N * kvm_elems(D) * esize);
   L.al = off;
-  off = align256(off + BH * N * kChunk * kChunk * sizeof(float));
+  off = align256(off + BH * N * al_floats() * sizeof(float));
   L.gate = off;
   off = align256(off + BH * T * sizeof(float));
   L.total = off;

@@ -116,16 +116,19 @@ __global__ __launch_bounds__(128) void stream_kernel(
     for (int i = tid; i < NV; i += 128) dst[i] = src[i];
   };
 
-  // Running query tile, from <-Q of this chunk.
+  // Running query tile, from the register image of <-Q of this chunk.
   f32x16 qw[NDB];
+  {
+    const float *src = qa + ((size_t)bh * N + qc) * qa_floats(D) + (size_t)wave * NDB * 1024 + lane * 16;
 #pragma unroll
-  for (int mb = 0; mb < NDB; ++mb)
+    for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(qa + qtok * D + 32 * mb + 8 * r4 + 4 * g);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(src + mb * 1024 + 4 * r4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qw[mb][4 * r4 + e] = x[e];
-    }
+        for (int e = 0; e < 4; ++e) qw[mb][4 * r4 + e] = x[e];
+      }
+  }
 
   f32x16 o[NDB];
 #pragma unroll
@@ -138,14 +141,17 @@ __global__ __launch_bounds__(128) void stream_kernel(
   // ---- diagonal block ----
   stage(qc);
   {
-    const float *al_c = al + ((size_t)bh * N + qc) * C * C + (size_t)qloc * C;
+    // Register image of the diagonal-block logits; the key block above the
+    // diagonal of wave 0 (keys 32..63, queries 0..31) is wholly masked.
+    const float *al_c = al + ((size_t)bh * N + qc) * al_floats() + lane * 16;
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int key0 = 32 * mb + 8 * r4 + 4 * g;
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(al_c + key0);
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (mb <= wave) x = *reinterpret_cast<const f32x4 *>(al_c + al_tile(wave, mb) * 1024 + 4 * r4);
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         if (FOX) a = *reinterpret_cast<const f32x4 *>(gate_h + (size_t)qc * C + key0);
 #pragma unroll

@@ -48,8 +48,8 @@ def test_version_and_strerror():
 def test_workspace_bytes(dtype, esize, B, H, T, d):
     n = pa.path_attn_workspace_bytes(B, H, T, d, dtype)
     BH, N = B * H, T // 64
-    # <-Q (fp32), the three per-chunk operands, diagonal logits (fp32), gate (fp32)
-    expect = BH * T * d * 4 + BH * N * (2 * 64 * d + d * d) * esize + BH * N * 64 * 64 * 4 + BH * T * 4
+    # <-Q (fp32), the three per-chunk operands, 3 of 4 diagonal-logit tiles (fp32), gate
+    expect = BH * T * d * 4 + BH * N * (2 * 64 * d + d * d) * esize + BH * N * 3 * 64 * 16 * 4 + BH * T * 4
     assert expect <= n <= expect + 4 * 256
 
 
