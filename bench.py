@@ -46,6 +46,9 @@ def parse():
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="JSON with measured HBM bytes per stream-kernel launch")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reference "
+                         "kernel for scaling HBM traffic counters) and report its GB/s")
     return ap.parse_args()
 
 
@@ -175,6 +178,13 @@ def main():
                      "traffic": traffic,
                      "flops_per_launch": flops},
     }
+    if args.calib_copy_mb > 0:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms_copy = timed(lambda: dst.copy_(src), 5)
+        res["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                                   "ms": ms_copy, "gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -21,6 +21,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # gfx950 matrix instructions read and write ordinary VGPRs; without this
+    # the accumulators are kept in AGPRs and copied to VGPRs for every
+    # vector-unit use (the softmax, the bf16 repacking of the running tile).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
