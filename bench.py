@@ -146,9 +146,15 @@ def main():
     stream_tflops = flops / (ms_stream * 1e-3) / 1e12
     traffic = None
     if os.path.exists(args.traffic):
+        # HBM bytes per stream-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE,
+        # valid only for the kernel source they were measured on.
         try:
+            import hashlib
             tr = json.load(open(args.traffic)).get(wl.name)
-            traffic = None if tr is None else tr.get("bytes_per_launch")
+            src = os.path.join(ROOT, "householder_position_encoding_amd", "csrc", "stream.hip")
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            if tr is not None and tr.get("stream_hip_sha256_16") == sha:
+                traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
 
