@@ -20,8 +20,10 @@
 //     K Q^T) are exact before the float32 sums; a float32 intermediate x enters
 //     a product as the pair hi = bf16(x), lo = bf16(x - hi) (about 16
 //     significant bits), with hi*hi + hi*lo + lo*hi for two such operands.
-//     The triangular inverse is a blocked float32 computation on the vector
-//     units.
+//     The triangular inverse is blocked (16 x 16): diagonal blocks by
+//     substitution on the vector units, off-diagonal blocks on float32 matrix
+//     cores.  Transposed copies (W^T, V^T in fragment order) are exact
+//     identity products on the matrix cores.
 //   * prep_f32_kernel (float32 inputs): plain float32 arithmetic on the vector
 //     units.
 // Only the operands handed to the streaming kernel's matrix cores (->K, V,
@@ -83,88 +85,136 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// acc += A[0..32)[0..K) * Bt[0..32)[0..K)^T on one wave: A and Bt are bf16 in
-// LDS with the contraction index contiguous (row pitches PA, PB elements).
+__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 32x32x(16*KS) product on a wave from bf16 rows with the contraction
+// index contiguous: lane l supplies row l%32, elements 8*(l/32) + 16*ks ...
+template <int KS>
+__device__ __forceinline__ void load_rows(bf16x8 (&f)[KS], const __bf16 *rows, int pitch, int lane) {
+  const __bf16 *p = rows + (lane & 31) * pitch + 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) f[ks] = *reinterpret_cast<const bf16x8 *>(p + 16 * ks);
+}
+template <int KS>
+__device__ __forceinline__ void mma_rows(f32x16 &acc, const bf16x8 (&a)[KS], const bf16x8 (&b)[KS]) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc = mma32(a[ks], b[ks], acc);
+}
+
+// acc += A[0..32)[0..K) * Bt[0..32)[0..K)^T with both operands in LDS.
 template <int K>
 __device__ __forceinline__ void tile_mma(f32x16 &acc, const __bf16 *A, int PA,
                                          const __bf16 *Bt, int PB, int lane) {
-  const __bf16 *a = A + (lane & 31) * PA + 8 * (lane >> 5);
-  const __bf16 *b = Bt + (lane & 31) * PB + 8 * (lane >> 5);
-#pragma unroll
-  for (int ks = 0; ks < K / 16; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8 *>(a + 16 * ks),
-        *reinterpret_cast<const bf16x8 *>(b + 16 * ks), acc, 0, 0, 0);
+  bf16x8 a[K / 16], b[K / 16];
+  load_rows<K / 16>(a, A, PA, lane);
+  load_rows<K / 16>(b, Bt, PB, lane);
+  mma_rows<K / 16>(acc, a, b);
 }
 
-__device__ __forceinline__ void store_split(__bf16 *hi, __bf16 *lo, int idx, float x) {
-  const __bf16 h = (__bf16)x;
-  hi[idx] = h;
-  lo[idx] = (__bf16)(x - (float)h);
+// Identity B operand for the exact MFMA transpose of a 32-column block:
+// k-step h of the block holds 1 where contraction index 16h + 8g + t equals
+// the lane's column l%32.
+__device__ __forceinline__ bf16x8 eye_frag(int h, int lane) {
+  bf16x8 f;
+  const int t0 = (lane & 31) - 16 * h - 8 * (lane >> 5);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f[t] = (__bf16)(t == t0 ? 1.f : 0.f);
+  return f;
 }
 
-// X_pq = -X_pp * sum_{t=16q}^{16p-1} N[16p+i][t] X[t][16q+j] for the blocks
-// (p, q) = (q + dist, q), q = 0 .. 3-dist, of the blocked unit-lower-triangular
-// inverse X = (I + N)^{-1} (16 x 16 blocks).  Ys holds 256 floats per block.
-template <int DIST>
-__device__ __forceinline__ void solve_band(const float *Ns, float *Xs, float *Ys,
-                                           int tid) {
-  constexpr int PN = 65, NB = 4 - DIST;
-  for (int o = tid; o < NB * 256; o += 256) {
-    const int q = o >> 8, i = (o >> 4) & 15, j = o & 15, p = q + DIST;
-    float y = 0.f;
-    for (int t = 16 * q; t < 16 * p; ++t) y += Ns[(16 * p + i) * PN + t] * Xs[t * PN + 16 * q + j];
-    Ys[o] = y;
-  }
-  __syncthreads();
-  for (int o = tid; o < NB * 256; o += 256) {
-    const int q = o >> 8, i = (o >> 4) & 15, j = o & 15, p = q + DIST;
-    float x = 0.f;
+// Store 4 accumulator values (rows acc_row(4*r4 + 0..3, g), consecutive) as
+// hi/lo bf16 pairs at dst_hi/dst_lo + offset (4 contiguous elements).
+__device__ __forceinline__ void store4_split(__bf16 *hi, __bf16 *lo, int off, f32x4 x) {
+  bf16x4 h, l;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) x -= Xs[(16 * p + i) * PN + 16 * p + t] * Ys[q * 256 + t * 16 + j];
-    Xs[(16 * p + i) * PN + 16 * q + j] = x;
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
   }
-  __syncthreads();
+  *reinterpret_cast<bf16x4 *>(hi + off) = h;
+  *reinterpret_cast<bf16x4 *>(lo + off) = l;
+}
+
+// f[idx] for a wave-uniform runtime idx without dynamic register indexing.
+template <int KS>
+__device__ __forceinline__ bf16x8 pick(const bf16x8 (&f)[KS], int idx) {
+  bf16x8 r = f[0];
+#pragma unroll
+  for (int i = 1; i < KS; ++i)
+    if (i == idx) r = f[i];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 quad(const f32x16 &a, int r4) {
+  return f32x4{a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+}
+
+__device__ __forceinline__ f32x4 mma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Off-diagonal block (p, q) of X = (I + N)^{-1}, 16 x 16 blocks, one wave, on
+// fp32 matrix cores:  X_pq = -X_pp * sum_{r=q}^{p-1} N_pr X_rq.
+// Xs holds N (strictly lower blocks), X_pp over the diagonal blocks and X_pq
+// (p > q) transposed in the upper block (q, p), which N leaves unused.
+// MFMA 16x16x4 layouts: A lane l -> A[l%16][k = l/16], B lane l ->
+// B[k = l/16][l%16], D lane l register r -> D[4*(l/16) + r][l%16].
+template <int PX>
+__device__ __forceinline__ void solve_block(float *Xs, int p, int q, int lane) {
+  const int m = lane & 15, g16 = lane >> 4;
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  for (int r = q; r < p; ++r) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = 4 * s + g16;
+      const float a = Xs[(16 * p + m) * PX + 16 * r + k];                      // N[16p+m][16r+k]
+      const float b = r == q ? Xs[(16 * q + k) * PX + 16 * q + m]               // X_qq[k][m]
+                             : Xs[(16 * q + m) * PX + 16 * r + k];              // X_rq[k][m], transposed
+      y = mma16(a, b, y);
+    }
+  }
+  // X_pq = X_pp * (-Y): lane holds Y rows 4*g16 + s; contraction slot
+  // 4*s + g16 of the MFMA maps to physical row 4*g16 + s.
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    x = mma16(Xs[(16 * p + m) * PX + 16 * p + 4 * g16 + s], -y[s], x);
+  // D rows i = 4*g16 + e, column j = m: stored transposed at (16q + j, 16p + i).
+  *reinterpret_cast<f32x4 *>(Xs + (16 * q + m) * PX + 16 * p + 4 * g16) = x;
 }
 
 // One block of 4 waves per (bh, chunk).  Every 64x64 product is split in four
-// 32x32 output tiles, one per wave (tile (w>>1, w&1)); products with a d-sized
-// output dimension give each wave several tiles (tile index w + 4u).
+// 32x32 output tiles, one per wave, tile (mt, nt) = (w>>1, w&1); products with
+// a d-sized dimension give each wave D/64 tiles.  Products whose result goes
+// to LDS are computed in the orientation where a lane's fixed column is the
+// destination row, so each lane stores 4 contiguous elements at a time.
 template <int D>
-__global__ __launch_bounds__(256) void prep_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const __bf16 *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa,
     __bf16 *__restrict__ kvm, float *__restrict__ al, int T) {
-  constexpr int C = kChunk, PD = D + 8, P64 = 72, PN = 65;
-  constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16;
-  constexpr int TPW = D / 64;  // d x 64 output tiles per wave
-  constexpr int A_BYTES = (3 * C * PD * 2 > 4 * C * P64 * 2) ? 3 * C * PD * 2 : 4 * C * P64 * 2;
-  constexpr int B_SOLVE = 2 * C * PN * 4 + 768 * 4;
-  constexpr int B_BYTES = (B_SOLVE > 2 * D * P64 * 2) ? B_SOLVE : 2 * D * P64 * 2;
-  constexpr int C_BYTES = 4 * C * P64 * 2 + D * P64 * 2 + C * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[A_BYTES + B_BYTES + C_BYTES];
-  // region A: W, Q, K (inputs), later U and T2^T (hi/lo planes)
-  __bf16 *Ws = reinterpret_cast<__bf16 *>(smem);
-  __bf16 *Qs = Ws + C * PD;
-  __bf16 *Ks = Qs + C * PD;
-  __bf16 *Uh = reinterpret_cast<__bf16 *>(smem);
-  __bf16 *Ul = Uh + C * P64;
-  __bf16 *T2h = Ul + C * P64;
-  __bf16 *T2l = T2h + C * P64;
-  // region B: the solve (N, X, scratch), later (U W)^T (hi/lo planes)
-  float *Ns = reinterpret_cast<float *>(smem + A_BYTES);
-  float *Xs = Ns + C * PN;
-  float *Ys = Xs + C * PN;
-  __bf16 *UWh = reinterpret_cast<__bf16 *>(smem + A_BYTES);
-  __bf16 *UWl = UWh + D * P64;
-  // region C: lower(Q W^T), strictLower(W K^T)^T (hi/lo planes), W^T, beta
-  __bf16 *P1h = reinterpret_cast<__bf16 *>(smem + A_BYTES + B_BYTES);
-  __bf16 *P1l = P1h + C * P64;
-  __bf16 *SKh = P1l + C * P64;
-  __bf16 *SKl = SKh + C * P64;
-  __bf16 *Wt = SKl + C * P64;
-  float *bs = reinterpret_cast<float *>(Wt + D * P64);
+  constexpr int C = kChunk, P = 72, PX = 72;
+  constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16, KSD = D / 16, KSC = C / 16;
+  constexpr int TPW = D / 64;                       // d x 64 tiles per wave
+  constexpr int PLANE = C * P * 2;                  // one 64 x 72 bf16 plane (bytes)
+  constexpr int SLOT = 2 * PLANE;                   // 18432 B: hi/lo planes or 64 x 72 fp32
+  constexpr int EXTRA = D == 128 ? SLOT : 0;        // second half of (U W)^T at d = 128
+  constexpr int WT_BYTES = D * P * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * SLOT + EXTRA + WT_BYTES + C * 4];
+  // slot 0: N / X (fp32), then U (hi/lo), then T2^T (hi/lo)
+  // slot 1: lower(Q W^T) (hi/lo)
+  // slot 2 (+ EXTRA): strictLower(W K^T)^T (hi/lo), then (U W)^T (hi/lo)
+  float *Xs = reinterpret_cast<float *>(smem);
+  __bf16 *Uh = reinterpret_cast<__bf16 *>(smem), *Ul = Uh + C * P;
+  __bf16 *T2h = Uh, *T2l = Ul;
+  __bf16 *P1h = reinterpret_cast<__bf16 *>(smem + SLOT), *P1l = P1h + C * P;
+  __bf16 *SKh = reinterpret_cast<__bf16 *>(smem + 2 * SLOT), *SKl = SKh + C * P;
+  __bf16 *UWh = SKh, *UWl = UWh + D * P;
+  __bf16 *Wt = reinterpret_cast<__bf16 *>(smem + 3 * SLOT + EXTRA);
+  float *bs = reinterpret_cast<float *>(smem + 3 * SLOT + EXTRA + WT_BYTES);
 
   const int N = T / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
@@ -179,64 +229,99 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
   __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D);
   __bf16 *vf = kf + C * D;
   __bf16 *mf = vf + C * D;
-
-  // VF: X[dd][key] = V[key][dd] in fragment order (global to global).
-  for (int item = tid; item < NDB * NSK * 64; item += 256) {
-    const int blob = item >> 6, mb = blob / NSK, s = blob % NSK;
-    const int dd = 32 * mb + n;
-    bf16x8 x;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) x[t] = vc[(size_t)frag_row(s, g, t, 8) * D + dd];
-    *reinterpret_cast<bf16x8 *>(vf + blob * 512 + lane * 8) = x;
-  }
-  // W, Q, K into LDS (natural layout, padded rows), beta.
-  for (int idx = tid; idx < C * D / 8; idx += 256) {
-    const int row = idx / (D / 8), c8 = idx % (D / 8);
-    *reinterpret_cast<bf16x8 *>(Ws + row * PD + 8 * c8) = *reinterpret_cast<const bf16x8 *>(wc + row * D + 8 * c8);
-    *reinterpret_cast<bf16x8 *>(Qs + row * PD + 8 * c8) = *reinterpret_cast<const bf16x8 *>(qc + row * D + 8 * c8);
-    *reinterpret_cast<bf16x8 *>(Ks + row * PD + 8 * c8) = *reinterpret_cast<const bf16x8 *>(kc + row * D + 8 * c8);
-  }
   if (tid < C) bs[tid] = beta[row0 + tid];
-  __syncthreads();
 
-  // ---- phase 1: products of the inputs (contraction over d) ----
-  f32x16 gacc = zero16(), p1acc = zero16(), skacc = zero16(), kq = zero16();
-  tile_mma<D>(gacc, Ws + 32 * mt * PD, PD, Ws + 32 * nt * PD, PD, lane);   // W W^T
-  tile_mma<D>(p1acc, Qs + 32 * mt * PD, PD, Ws + 32 * nt * PD, PD, lane);  // Q W^T
-  tile_mma<D>(skacc, Ks + 32 * mt * PD, PD, Ws + 32 * nt * PD, PD, lane);  // K W^T
-  tile_mma<D>(kq, Ks + 32 * mt * PD, PD, Qs + 32 * nt * PD, PD, lane);     // K Q^T
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 32 * mt + acc_row(r, g), col = 32 * nt + n;
-    Ns[row * PN + col] = col < row ? bs[row] * gacc[r] : 0.f;          // N = strictLower(D W W^T)
-    store_split(P1h, P1l, row * P64 + col, col <= row ? p1acc[r] : 0.f);  // lower(Q W^T)[i][t]
-    store_split(SKh, SKl, row * P64 + col, col > row ? skacc[r] : 0.f);   // strictLower(W K^T)^T[j][t]
-  }
-  // Initial values of the <-Q^T and ->K^T tiles: Q^T and K^T.
+  // ---- phase 1: products of the inputs, operands straight from global ----
+  f32x16 kq = zero16();
   f32x16 qinit[TPW], kinit[TPW];
+  {
+    bf16x8 wm[KSD], wn[KSD], qn[KSD], kn[KSD], km[KSD];
+    load_rows<KSD>(wm, wc + 32 * mt * D, D, lane);
+    load_rows<KSD>(wn, wc + 32 * nt * D, D, lane);
+    load_rows<KSD>(qn, qc + 32 * nt * D, D, lane);
+    load_rows<KSD>(kn, kc + 32 * nt * D, D, lane);
+    load_rows<KSD>(km, kc + 32 * mt * D, D, lane);
+    // <-Q^T and ->K^T start from Q^T and K^T: tiles (eb, xb) = (tau>>1, tau&1)
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
+    for (int u = 0; u < TPW; ++u) {
+      const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int e0 = 32 * eb + 8 * r4 + 4 * g, x = 32 * xb + n;
-      const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(Qs + x * PD + e0);
-      const bf16x4 kv = *reinterpret_cast<const bf16x4 *>(Ks + x * PD + e0);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const size_t off = (size_t)(32 * xb + n) * D + 32 * eb + 8 * r4 + 4 * g;
+        const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(qc + off);
+        const bf16x4 kv = *reinterpret_cast<const bf16x4 *>(kc + off);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qinit[u][4 * r4 + e] = (float)qv[e];
-        kinit[u][4 * r4 + e] = (float)kv[e];
+        for (int e = 0; e < 4; ++e) {
+          qinit[u][4 * r4 + e] = (float)qv[e];
+          kinit[u][4 * r4 + e] = (float)kv[e];
+        }
       }
     }
-  }
-  // W^T (rows e, contraction index t contiguous).
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int t = idx & 63, e = idx >> 6;
-    Wt[e * P64 + t] = Ws[t * PD + e];
+    f32x16 gacc = zero16(), p1acc = zero16(), skacc = zero16();
+    mma_rows<KSD>(gacc, wm, wn);    // [j][s]  = w_j . w_s
+    mma_rows<KSD>(p1acc, wm, qn);   // [t][i]  = w_t . q_i
+    mma_rows<KSD>(skacc, wm, kn);   // [t][j]  = w_t . k_j
+    mma_rows<KSD>(kq, km, qn);      // [j][i]  = k_j . q_i  (kept for the diagonal logits)
+    // W^T by exact identity products: tile (t block mt, e block eb)
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int eb = nt + 2 * u;
+      f32x16 acc = zero16();
+      acc = mma32(pick(wm, 2 * eb), eye_frag(0, lane), acc);
+      acc = mma32(pick(wm, 2 * eb + 1), eye_frag(1, lane), acc);
+      const int e = 32 * eb + n;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (__bf16)acc[4 * r4 + i];
+        *reinterpret_cast<bf16x4 *>(Wt + e * P + 32 * mt + 8 * r4 + 4 * g) = x;
+      }
+    }
+    // V^T in fragment order by exact identity products: tile (key block mt,
+    // d block db); register group h of the tile is blob (db, 2*mt + h).
+    {
+      bf16x8 vm[KSD];
+      load_rows<KSD>(vm, vc + 32 * mt * D, D, lane);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int db = nt + 2 * u;
+        f32x16 acc = zero16();
+        acc = mma32(pick(vm, 2 * db), eye_frag(0, lane), acc);
+        acc = mma32(pick(vm, 2 * db + 1), eye_frag(1, lane), acc);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 x;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = (__bf16)acc[8 * h + t];
+          *reinterpret_cast<bf16x8 *>(vf + ((db * NSK + 2 * mt + h) * 64 + lane) * 8) = x;
+        }
+      }
+    }
+    __syncthreads();   // beta visible
+    // N = strictLower(D W W^T) (fp32), lower(Q W^T), strictLower(W K^T)^T.
+    // Lane column = destination row (s, i or j); 4 consecutive rows of the
+    // accumulator = 4 contiguous destination columns.
+    const int col = 32 * nt + n;
+    const float bcol = bs[col];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int r0 = 32 * mt + 8 * r4 + 4 * g;
+      f32x4 nv, pv, sv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nv[e] = r0 + e < col ? bcol * gacc[4 * r4 + e] : 0.f;   // N[s = col][j = r0 + e]
+        pv[e] = r0 + e <= col ? p1acc[4 * r4 + e] : 0.f;        // P1[i = col][t]
+        sv[e] = r0 + e > col ? skacc[4 * r4 + e] : 0.f;         // SK^T[j = col][t]
+      }
+      *reinterpret_cast<f32x4 *>(Xs + col * PX + r0) = nv;
+      store4_split(P1h, P1l, col * P + r0, pv);
+      store4_split(SKh, SKl, col * P + r0, sv);
+    }
   }
   __syncthreads();
 
-  // ---- phase 2: U = (I + N)^{-1} D, blocked (16 x 16 blocks), float32 ----
+  // ---- phase 2: X = (I + N)^{-1}, 16 x 16 blocks; U = X D ----
   if (wv == 0) {
     // diagonal blocks by forward substitution: lane = (block b, column j)
     const int b = lane >> 4, j = lane & 15, base = 16 * b;
@@ -245,42 +330,87 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
     for (int i = 0; i < 16; ++i) {
       float acc = i == j ? 1.f : 0.f;
 #pragma unroll
-      for (int t = 0; t < i; ++t) acc -= Ns[(base + i) * PN + base + t] * x[t];
+      for (int t4 = 0; t4 < 4; ++t4) {
+        if (4 * t4 < i) {
+          const f32x4 nr = *reinterpret_cast<const f32x4 *>(Xs + (base + i) * PX + base + 4 * t4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * t4 + e < i) acc -= nr[e] * x[4 * t4 + e];
+        }
+      }
       x[i] = acc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Xs[(base + i) * PN + base + j] = x[i];
+    for (int i = 0; i < 16; ++i) Xs[(base + i) * PX + base + j] = x[i];
   }
   __syncthreads();
-  solve_band<1>(Ns, Xs, Ys, tid);
-  solve_band<2>(Ns, Xs, Ys, tid);
-  solve_band<3>(Ns, Xs, Ys, tid);
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int i = idx >> 6, j = idx & 63;
-    const float x = j < i ? Xs[i * PN + j] : (j == i ? 1.f : 0.f);
-    store_split(Uh, Ul, i * P64 + j, x * bs[j]);
+  if (wv < 3) solve_block<PX>(Xs, wv + 1, wv, lane);       // blocks (1,0) (2,1) (3,2)
+  __syncthreads();
+  if (wv < 2) solve_block<PX>(Xs, wv + 2, wv, lane);       // blocks (2,0) (3,1)
+  __syncthreads();
+  if (wv == 0) solve_block<PX>(Xs, 3, 0, lane);            // block (3,0)
+  __syncthreads();
+  {
+    // U[i][j] = X[i][j] beta_j (j < i), beta_i (j == i), 0 (j > i); four
+    // contiguous j per item; read everything before overwriting the slot.
+    f32x4 uv[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 256 * it, i = item >> 4, j0 = 4 * (item & 15);
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if ((j0 >> 4) == (i >> 4)) {
+        x = *reinterpret_cast<const f32x4 *>(Xs + i * PX + j0);
+      } else if ((j0 >> 4) < (i >> 4)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = Xs[(j0 + e) * PX + i];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        uv[it][e] = j < i ? x[e] * bs[j] : (j == i ? bs[j] : 0.f);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 256 * it, i = item >> 4, j0 = 4 * (item & 15);
+      store4_split(Uh, Ul, i * P + j0, uv[it]);
+    }
   }
   __syncthreads();
 
-  // ---- phase 3: (U W)^T and T2^T = (U strictLower(W K^T))^T ----
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tau = wv + 4 * u, eb = tau >> 1, sb = tau & 1;
-    f32x16 acc = zero16();
-    tile_mma<C>(acc, Wt + 32 * eb * P64, P64, Uh + 32 * sb * P64, P64, lane);
-    tile_mma<C>(acc, Wt + 32 * eb * P64, P64, Ul + 32 * sb * P64, P64, lane);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      store_split(UWh, UWl, (32 * eb + acc_row(r, g)) * P64 + 32 * sb + n, acc[r]);
-  }
+  // ---- phase 3: T2 = U strictLower(W K^T) and U W, stored transposed ----
   {
-    f32x16 acc = zero16();
-    tile_mma<C>(acc, SKh + 32 * mt * P64, P64, Uh + 32 * nt * P64, P64, lane);
-    tile_mma<C>(acc, SKh + 32 * mt * P64, P64, Ul + 32 * nt * P64, P64, lane);
-    tile_mma<C>(acc, SKl + 32 * mt * P64, P64, Uh + 32 * nt * P64, P64, lane);
+    bf16x8 uh[KSC], ul[KSC];
+    load_rows<KSC>(uh, Uh + 32 * mt * P, P, lane);
+    load_rows<KSC>(ul, Ul + 32 * mt * P, P, lane);
+    f32x16 t2 = zero16();
+    {
+      bf16x8 sh[KSC], sl[KSC];
+      load_rows<KSC>(sh, SKh + 32 * nt * P, P, lane);
+      load_rows<KSC>(sl, SKl + 32 * nt * P, P, lane);
+      mma_rows<KSC>(t2, uh, sh);
+      mma_rows<KSC>(t2, uh, sl);
+      mma_rows<KSC>(t2, ul, sh);
+    }
+    f32x16 uw[TPW];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      store_split(T2h, T2l, (32 * mt + acc_row(r, g)) * P64 + 32 * nt + n, acc[r]);
+    for (int u = 0; u < TPW; ++u) {
+      bf16x8 wt[KSC];
+      load_rows<KSC>(wt, Wt + 32 * (nt + 2 * u) * P, P, lane);
+      uw[u] = zero16();
+      mma_rows<KSC>(uw[u], uh, wt);
+      mma_rows<KSC>(uw[u], ul, wt);
+    }
+    __syncthreads();   // U and strictLower(W K^T)^T are dead
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int s0 = 32 * mt + 8 * r4 + 4 * g;
+      store4_split(T2h, T2l, (32 * nt + n) * P + s0, quad(t2, r4));             // T2^T[j][s]
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        store4_split(UWh, UWl, (32 * (nt + 2 * u) + n) * P + s0, quad(uw[u], r4));  // (UW)^T[e][s]
+    }
   }
   __syncthreads();
 
@@ -291,9 +421,9 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
     const int tau = wv + 4 * u, eb = tau >> 1, ib = tau & 1;
     // <-Q^T = Q^T - (U W)^T lower(Q W^T)^T
     f32x16 acc = zero16();
-    tile_mma<C>(acc, UWh + 32 * eb * P64, P64, P1h + 32 * ib * P64, P64, lane);
-    tile_mma<C>(acc, UWh + 32 * eb * P64, P64, P1l + 32 * ib * P64, P64, lane);
-    tile_mma<C>(acc, UWl + 32 * eb * P64, P64, P1h + 32 * ib * P64, P64, lane);
+    tile_mma<C>(acc, UWh + 32 * eb * P, P, P1h + 32 * ib * P, P, lane);
+    tile_mma<C>(acc, UWh + 32 * eb * P, P, P1l + 32 * ib * P, P, lane);
+    tile_mma<C>(acc, UWl + 32 * eb * P, P, P1h + 32 * ib * P, P, lane);
     float *dst = qa_c + ((ib * NDB + eb) * 64 + lane) * 16;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -304,8 +434,8 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
     }
     // ->K^T = K^T - W^T T2 (tile (eb, jb = ib)), into KF fragment blobs
     f32x16 kacc = zero16();
-    tile_mma<C>(kacc, Wt + 32 * eb * P64, P64, T2h + 32 * ib * P64, P64, lane);
-    tile_mma<C>(kacc, Wt + 32 * eb * P64, P64, T2l + 32 * ib * P64, P64, lane);
+    tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2h + 32 * ib * P, P, lane);
+    tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2l + 32 * ib * P, P, lane);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 x;
@@ -319,8 +449,8 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
   for (int u = 0; u < NDB * NDB / 4; ++u) {
     const int tau = wv + 4 * u, ab = tau / NDB, bb = tau % NDB;
     f32x16 acc = zero16();
-    tile_mma<C>(acc, Wt + 32 * ab * P64, P64, UWh + 32 * bb * P64, P64, lane);
-    tile_mma<C>(acc, Wt + 32 * ab * P64, P64, UWl + 32 * bb * P64, P64, lane);
+    tile_mma<C>(acc, Wt + 32 * ab * P, P, UWh + 32 * bb * P, P, lane);
+    tile_mma<C>(acc, Wt + 32 * ab * P, P, UWl + 32 * bb * P, P, lane);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 x;
@@ -333,9 +463,9 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(
   // keys 32..63 and queries 0..31 lies above the diagonal and is not stored.
   if (!(mt == 1 && nt == 0)) {
     f32x16 acc = zero16();
-    tile_mma<C>(acc, T2h + 32 * mt * P64, P64, P1h + 32 * nt * P64, P64, lane);
-    tile_mma<C>(acc, T2h + 32 * mt * P64, P64, P1l + 32 * nt * P64, P64, lane);
-    tile_mma<C>(acc, T2l + 32 * mt * P64, P64, P1h + 32 * nt * P64, P64, lane);
+    tile_mma<C>(acc, T2h + 32 * mt * P, P, P1h + 32 * nt * P, P, lane);
+    tile_mma<C>(acc, T2h + 32 * mt * P, P, P1l + 32 * nt * P, P, lane);
+    tile_mma<C>(acc, T2l + 32 * mt * P, P, P1h + 32 * nt * P, P, lane);
     float *dst = al + ((size_t)bh * N + c) * al_floats() + (al_tile(nt, mt) * 64 + lane) * 16;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
