@@ -229,12 +229,14 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D);
   __bf16 *vf = kf + C * D;
   __bf16 *mf = vf + C * D;
-  if (tid < C) bs[tid] = beta[row0 + tid];
 
   // ---- phase 1: products of the inputs, operands straight from global ----
+  // All global reads of this phase are issued before the first use of any of
+  // them, so their latencies overlap.
   f32x16 kq = zero16();
   f32x16 qinit[TPW], kinit[TPW];
   {
+    const float bval = tid < C ? beta[row0 + tid] : 0.f;
     bf16x8 wm[KSD], wn[KSD], qn[KSD], kn[KSD], km[KSD];
     load_rows<KSD>(wm, wc + 32 * mt * D, D, lane);
     load_rows<KSD>(wn, wc + 32 * nt * D, D, lane);
@@ -242,21 +244,26 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     load_rows<KSD>(kn, kc + 32 * nt * D, D, lane);
     load_rows<KSD>(km, kc + 32 * mt * D, D, lane);
     // <-Q^T and ->K^T start from Q^T and K^T: tiles (eb, xb) = (tau>>1, tau&1)
+    bf16x4 qv[TPW][4], kv[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const size_t off = (size_t)(32 * xb + n) * D + 32 * eb + 8 * r4 + 4 * g;
-        const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(qc + off);
-        const bf16x4 kv = *reinterpret_cast<const bf16x4 *>(kc + off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qinit[u][4 * r4 + e] = (float)qv[e];
-          kinit[u][4 * r4 + e] = (float)kv[e];
-        }
+        qv[u][r4] = *reinterpret_cast<const bf16x4 *>(qc + off);
+        kv[u][r4] = *reinterpret_cast<const bf16x4 *>(kc + off);
       }
     }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qinit[u][4 * r4 + e] = (float)qv[u][r4][e];
+          kinit[u][4 * r4 + e] = (float)kv[u][r4][e];
+        }
     f32x16 gacc = zero16(), p1acc = zero16(), skacc = zero16();
     mma_rows<KSD>(gacc, wm, wn);    // [j][s]  = w_j . w_s
     mma_rows<KSD>(p1acc, wm, qn);   // [t][i]  = w_t . q_i
@@ -298,6 +305,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
         }
       }
     }
+    if (tid < C) bs[tid] = bval;
     __syncthreads();   // beta visible
     // N = strictLower(D W W^T) (fp32), lower(Q W^T), strictLower(W K^T)^T.
     // Lane column = destination row (s, i or j); 4 consecutive rows of the
@@ -352,11 +360,13 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   __syncthreads();
   {
     // U[i][j] = X[i][j] beta_j (j < i), beta_i (j == i), 0 (j > i); four
-    // contiguous j per item; read everything before overwriting the slot.
+    // contiguous j per item, consecutive lanes on consecutive rows i (so the
+    // transposed reads of X are conflict-free); read everything before
+    // overwriting the slot.
     f32x4 uv[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it, i = item >> 4, j0 = 4 * (item & 15);
+      const int item = tid + 256 * it, i = item & 63, j0 = 4 * (item >> 6);
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       if ((j0 >> 4) == (i >> 4)) {
         x = *reinterpret_cast<const f32x4 *>(Xs + i * PX + j0);
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it, i = item >> 4, j0 = 4 * (item & 15);
+      const int item = tid + 256 * it, i = item & 63, j0 = 4 * (item >> 6);
       store4_split(Uh, Ul, i * P + j0, uv[it]);
     }
   }
