@@ -26,6 +26,8 @@
 // the serial chain S = K Q, Q <- Q - M^T Q, O += V^T P never touches LDS.
 // The running tile keeps a float32 master copy; the transform is applied as
 // Q + (-M^T) round(Q), so the identity part of F_c is exact.
+#include <type_traits>
+
 #include "path_attn_internal.h"
 
 namespace pathattn {
@@ -90,9 +92,37 @@ struct Mfma<float> {
 
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
-// NQC query chunks per block; NBUF = 2 double-buffers the staged operands
-// (NBUF = 1 is used only where two copies do not fit in LDS).
-template <typename E, int D, bool FOX, int NQC, int NBUF>
+// Workgroup barrier for the LDS operand ring.  __syncthreads() (and a
+// workgroup fence, even one restricted to LDS, since copies into LDS count as
+// LDS writes) waits for every outstanding global load of the wave, which would
+// drain the operand prefetch at each step.  Here the wave's own LDS reads are
+// completed (lgkmcnt 0, so a buffer can be refilled after the barrier), the
+// copies are waited for explicitly (vmcnt) by the caller, and the empty asm
+// statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima so they impose no wait).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// NQC query chunks per block.  Operand blocks are prefetched PD key chunks
+// ahead into a ring of PD + 1 + LAG LDS buffers (PD = 0: one buffer, loaded
+// synchronously, for shapes where two copies do not fit in LDS).  LAG = 1
+// software-pipelines each wave: the softmax and P.V of key chunk c+1 are
+// issued together with the S and transition MFMAs of chunk c (which depend
+// only on the running query tile), so vector and matrix work overlap within
+// the wave; V and the gate of chunk c+1 stay in the ring one step longer.
+template <typename E, int D, bool FOX, int NQC, int PD, int LAG>
 __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     const float *__restrict__ qa, const E *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
@@ -107,8 +137,11 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   constexpr int KVM_BYTES = KVM * (int)sizeof(E);
   constexpr int FRAG = 64 * KPL;        // elements of one A-operand fragment
   constexpr int NW = NQC * 2;           // waves per block
-  static_assert(KVM_BYTES % 1024 == 0, "operand block must be whole 1 KiB pieces");
+  constexpr int NBUF = PD + 1 + LAG;
+  constexpr int NL = KVM_BYTES / 1024 / NW;   // copy instructions per wave per chunk
+  static_assert(KVM_BYTES % (1024 * NW) == 0, "operand block must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
+  __shared__ __attribute__((aligned(16))) float gate_l[FOX ? NBUF * C : 1];
 
   const int N = T / C;
   const int NG = (N + NQC - 1) / NQC;
@@ -126,20 +159,32 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
 
   // Copy key chunk c's operand block into LDS buffer `buf`: 1 KiB per wave
   // instruction, lane l's 16 bytes landing at offset 16*l.
+  // With the forget gate, wave 0 first copies the chunk's 64 gate values
+  // (4 bytes per lane) into the matching slot of a small LDS ring.
   auto stage = [&](int c, int buf) {
+    if (FOX && wave == 0)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gate_h + (size_t)c * C + lane),
+                                       (lds_ptr_t)(gate_l + buf * C), 4, 0, 0);
     const unsigned char *src = reinterpret_cast<const unsigned char *>(kvm_h + (size_t)c * KVM);
     unsigned char *dst = lds + buf * KVM_BYTES;
-    for (int j = wave; j < KVM_BYTES / 1024; j += NW)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = wave + i * NW;
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + j * 1024 + lane * 16),
                                        (lds_ptr_t)(dst + j * 1024), 16, 0, 0);
+    }
   };
 
-  f32x16 qw[NDB], o[NDB], sc[2];
+  f32x16 qw[NDB], o[NDB], sA[2], sB[2];
   float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
   for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[mb][r] = sB[mb][r] = -INFINITY;
   if (valid) {  // running query tile, from the register image of <-Q
     const float *src = qa + ((size_t)bh * N + qcw) * qa_floats(D) + (size_t)half * NDB * 1024 + lane * 16;
 #pragma unroll
@@ -152,14 +197,81 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       }
   }
 
-  stage(c_top, NBUF == 2 ? (c_top & 1) : 0);
-  wait_all_memory();
-  __syncthreads();
+  // Online softmax, in log2 units (logit x = S * scale * log2(e) + a_j), in
+  // three pieces so that the exponentials need no branch:
+  //  exp_scores: x and the chunk max mx; exponentiate against the reference
+  //    m_ref = max(m_run, mx - 8), so every p = 2^(x - m_ref) is at most 2^8;
+  //    returns m_ref and the lane's partial sum of p (scores -> p in place);
+  //  rebase: if m_ref exceeds the running max (rare once the nearest chunks
+  //    are in), rescale O and l to the new reference;
+  //  pv: O^T += V^T P^T.
+  // The result is the same softmax: only the common reference changes.
+  auto exp_scores = [&](f32x16 (&s_in)[2], const float *gb, float &lsum) -> float {
+    float mx = -INFINITY;
+    if (FOX) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 a = *reinterpret_cast<const f32x4 *>(gb + 32 * mb + 8 * r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = __builtin_fmaf(s_in[mb][4 * r4 + e], sl2, a[e]);
+            s_in[mb][4 * r4 + e] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+    } else {
+      // the scale is positive: take the max of the raw scores, scale once
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_in[mb][r]);
+      mx *= sl2;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_ref = fmaxf(m_run, mx - 8.f);
+    lsum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(
+            FOX ? s_in[mb][r] - m_ref : __builtin_fmaf(s_in[mb][r], sl2, -m_ref));
+        s_in[mb][r] = pr;
+        lsum += pr;
+      }
+    return m_ref;
+  };
+  auto rebase = [&](float m_ref) {
+    if (__any(m_ref > m_run)) {   // wave-uniform
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      m_run = m_ref;
+    }
+  };
+  auto pv = [&](const f32x16 (&pr)[2], const E *vb) {
+#pragma unroll
+    for (int s = 0; s < NSK; ++s) {
+      const frag pb = MF::pack(pr, s);
+#pragma unroll
+      for (int mb = 0; mb < NDB; ++mb)
+        o[mb] = MF::run(MF::load(vb + (mb * NSK + s) * FRAG + lane * KPL), pb, o[mb]);
+    }
+  };
+  auto buf_ptr = [&](int b) { return reinterpret_cast<const E *>(lds + b * KVM_BYTES); };
 
-  for (int c = c_top; c >= 0; --c) {
-    const int buf = NBUF == 2 ? (c & 1) : 0;
-    if (NBUF == 2 && c > 0) stage(c - 1, (c - 1) & 1);
-    const E *kf_l = reinterpret_cast<const E *>(lds + buf * KVM_BYTES);
+  // One step of the walk against key chunk c.  snew receives this step's
+  // scores; with LAG, sprev holds the previous cross step's scores (or -inf)
+  // and is absorbed here, against V and the gate of chunk c+1.
+  auto step = [&](int c, f32x16 (&snew)[2], f32x16 (&sprev)[2]) {
+    const int buf = c % NBUF;
+    if (PD > 0 && c - PD >= 0) stage(c - PD, (c - PD) % NBUF);
+    const E *kf_l = buf_ptr(buf);
     const E *vf_l = kf_l + C * D;
     const E *mf_l = vf_l + C * D;
 
@@ -168,6 +280,7 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       // above the diagonal of the first half (keys 32..63, queries 0..31) is
       // wholly masked.
       const float *al_c = al + ((size_t)bh * N + qcw) * al_floats() + lane * 16;
+      const float *ga = gate_l + buf * C + 4 * g;
       float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -177,12 +290,12 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
           f32x4 x = {0.f, 0.f, 0.f, 0.f};
           if (mb <= half) x = *reinterpret_cast<const f32x4 *>(al_c + al_tile(half, mb) * 1024 + 4 * r4);
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
-          if (FOX) a = *reinterpret_cast<const f32x4 *>(gate_h + (size_t)c * C + key0);
+          if (FOX) a = *reinterpret_cast<const f32x4 *>(ga + 32 * mb + 8 * r4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float s = key0 + e <= qloc ? __builtin_fmaf(x[e], sl2, a[e]) : -INFINITY;
-            sc[mb][4 * r4 + e] = s;
-            mx = fmaxf(mx, s);
+            const float sv = key0 + e <= qloc ? __builtin_fmaf(x[e], sl2, a[e]) : -INFINITY;
+            snew[mb][4 * r4 + e] = sv;
+            mx = fmaxf(mx, sv);
           }
         }
       m_run = fmaxf(mx, __shfl_xor(mx, 32));
@@ -190,102 +303,103 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[mb][r] - m_run);
-          sc[mb][r] = p;
-          l_run += p;
+          const float pr = __builtin_amdgcn_exp2f(snew[mb][r] - m_run);
+          snew[mb][r] = pr;
+          l_run += pr;
         }
+      pv(snew, vf_l);
+      // nothing is pending for the first cross step
 #pragma unroll
-      for (int s = 0; s < NSK; ++s) {
-        const frag pb = MF::pack(sc, s);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
-          o[mb] = MF::run(MF::load(vf_l + (mb * NSK + s) * FRAG + lane * KPL), pb, o[mb]);
-      }
+        for (int r = 0; r < 16; ++r) snew[mb][r] = -INFINITY;
     } else if (valid && c < qcw) {
       // ---- cross step against key chunk c ----
       frag qb[NSD];
 #pragma unroll
       for (int s = 0; s < NSD; ++s) qb[s] = MF::pack(qw, s);
-      // S^T = ->K_c Q_work^T
+      // S^T = ->K_c Q_work^T, then Q_work^T <- Q_work^T - M_c^T round(Q_work^T)
+      // (crossing chunk c's transition; after chunk 0 the tile is not used)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[mb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) snew[mb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NSD; ++s)
-          sc[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], sc[mb]);
-      }
-      // Q_work^T <- Q_work^T - M_c^T round(Q_work^T): cross chunk c's transition.
-      if (c > 0) {
-#pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
-#pragma unroll
-          for (int s = 0; s < NSD; ++s)
-            qw[mb] = MF::run(MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], qw[mb]);
-      }
-      // Online softmax in log2 units: logit x = S * scale * log2(e) (+ a_j).
-      float mx = -INFINITY;
-      if (FOX) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(gate_h + (size_t)c * C + 32 * mb + 8 * r4 + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float s = __builtin_fmaf(sc[mb][4 * r4 + e], sl2, a[e]);
-              sc[mb][4 * r4 + e] = s;
-              mx = fmaxf(mx, s);
-            }
-          }
-      } else {
-        // the scale is positive: take the max of the raw scores, scale once
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
-        mx *= sl2;
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {   // wave-uniform: rescale only when a max grew
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-        m_run = m_new;
+          snew[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], snew[mb]);
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(
-              FOX ? sc[mb][r] - m_run : __builtin_fmaf(sc[mb][r], sl2, -m_run));
-          sc[mb][r] = p;
-          l_run += p;
+        for (int s = 0; s < NSD; ++s)
+          qw[mb] = MF::run(MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], qw[mb]);
+      float lsum;
+      if (LAG) {
+        // the previous chunk's softmax overlaps this step's MFMAs
+        const int pb_ = (c + 1) % NBUF;
+        const float m_ref = exp_scores(sprev, gate_l + pb_ * C + 4 * g, lsum);
+#pragma unroll
+        for (int i = 0; i < 2 * NSD + NDB * NSD; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
         }
-      // O^T += V_c^T P^T
-#pragma unroll
-      for (int s = 0; s < NSK; ++s) {
-        const frag pb = MF::pack(sc, s);
-#pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
-          o[mb] = MF::run(MF::load(vf_l + (mb * NSK + s) * FRAG + lane * KPL), pb, o[mb]);
+        rebase(m_ref);
+        l_run += lsum;
+        pv(sprev, buf_ptr(pb_) + C * D);
+      } else {
+        const float m_ref = exp_scores(snew, gate_l + buf * C + 4 * g, lsum);
+        rebase(m_ref);
+        l_run += lsum;
+        pv(snew, vf_l);
       }
     }
 
-    if (NBUF == 2) {
-      wait_all_memory();   // this wave's share of chunk c-1 has landed
-      __syncthreads();     // ... and everyone's; buffer c is free again
-    } else {
-      __syncthreads();
+    if (PD == 0) {
+      lds_barrier();
       if (c > 0) {
         stage(c - 1, 0);
         wait_all_memory();
       }
-      __syncthreads();
+      lds_barrier();
+    } else {
+      // This wave's share of chunk c-1 has landed once at most the copies of
+      // the chunks issued after it (c-2 .. c-PD, those that exist) are
+      // outstanding; the barrier then makes everyone's share visible and
+      // frees buffer c for the next prefetch.
+      if (PD >= 2 && c - 2 >= 0)
+        wait_vmcnt<(PD >= 2 ? NL : 0)>();
+      else
+        wait_all_memory();
+      lds_barrier();
+    }
+  };
+
+  for (int p = 0; p <= (PD > 0 ? PD - 1 : 0); ++p)
+    if (c_top - p >= 0) stage(c_top - p, (c_top - p) % NBUF);
+  wait_all_memory();
+  lds_barrier();
+
+  // Unrolled by two so that the pending and the fresh scores alternate
+  // between sA and sB without copies.
+  for (int c = c_top; c >= 0; c -= 2) {
+    step(c, sA, sB);
+    if (c >= 1) step(c - 1, sB, sA);
+  }
+
+  // the last cross step's scores (key chunk 0) are still pending with LAG;
+  // they sit in the array the step with c = 0 wrote
+  if (LAG && valid) {
+    float lsum;
+    if ((c_top & 1) == 0) {
+      const float m_ref = exp_scores(sA, gate_l + 4 * g, lsum);
+      rebase(m_ref);
+      l_run += lsum;
+      pv(sA, buf_ptr(0) + C * D);
+    } else {
+      const float m_ref = exp_scores(sB, gate_l + 4 * g, lsum);
+      rebase(m_ref);
+      l_run += lsum;
+      pv(sB, buf_ptr(0) + C * D);
     }
   }
 
@@ -310,27 +424,342 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   }
 }
 
-// Launch shapes: query chunks per block and staging buffers per (dtype, d).
+// Wide variant for bf16 operands: one wave holds a whole 64-query chunk as two
+// 32-query column blocks j = 0, 1, so every A fragment read from LDS (->K,
+// -M^T, V^T) feeds two matrix instructions.  This halves the LDS operand reads
+// and the staging per unit of work; the price is about 250 registers per lane
+// (running tile, output and scores for 64 queries), i.e. two waves per SIMD.
+// The softmax exponentiates against the reference max m_ref = max(m_run,
+// mx - 8), so p <= 2^8 and the rare rescale of O and l comes after the
+// exponentials; the row sums are taken from the bf16-rounded weights that the
+// P.V products use (dot with (1, 1)), so numerator and denominator match.
+template <int D, bool FOX, int NQC, int PD>
+__global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
+    const float *__restrict__ qa, const __bf16 *__restrict__ kvm,
+    const float *__restrict__ al, const float *__restrict__ gate,
+    __bf16 *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2) {
+  using E = __bf16;
+  using MF = Mfma<E>;
+  using frag = typename MF::frag;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  constexpr int C = kChunk, KPL = MF::KPL, KSTEP = 2 * KPL;
+  constexpr int NDB = D / 32;
+  constexpr int NSD = D / KSTEP;
+  constexpr int NSK = C / KSTEP;
+  constexpr int KVM = kvm_elems(D);
+  constexpr int KVM_BYTES = KVM * (int)sizeof(E);
+  constexpr int FRAG = 64 * KPL;
+  constexpr int NW = NQC;               // one wave per query chunk
+  constexpr int NBUF = PD + 1;
+  constexpr int NL = KVM_BYTES / 1024 / NW;
+  static_assert(PD >= 1, "the wide kernel always prefetches");
+  static_assert(KVM_BYTES % (1024 * NW) == 0, "operand block must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
+  __shared__ __attribute__((aligned(16))) float gate_l[FOX ? NBUF * C : 1];
+
+  const int N = T / C;
+  const int NG = (N + NQC - 1) / NQC;
+  const int bh = (int)(blockIdx.x % BH);
+  const int qc0 = (NG - 1 - (int)(blockIdx.x / BH)) * NQC;   // longest groups first
+  const int c_top = min(qc0 + NQC, N) - 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int qcw = qc0 + wave;
+  const bool valid = qcw < N;
+  const E *kvm_h = kvm + (size_t)bh * N * KVM;
+  const float *gate_h = FOX ? gate + (size_t)bh * T : nullptr;
+
+  auto stage = [&](int c, int buf) {
+    if (FOX && wave == 0)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gate_h + (size_t)c * C + lane),
+                                       (lds_ptr_t)(gate_l + buf * C), 4, 0, 0);
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kvm_h + (size_t)c * KVM);
+    unsigned char *dst = lds + buf * KVM_BYTES;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int jb = wave + i * NW;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + jb * 1024 + lane * 16),
+                                       (lds_ptr_t)(dst + jb * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 qw[2][NDB], o[2][NDB], sc[2][2];
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[j][mb][r] = 0.f;
+  if (valid) {
+    const float *src = qa + ((size_t)bh * N + qcw) * qa_floats(D) + lane * 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(src + (j * NDB + mb) * 1024 + 4 * r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qw[j][mb][4 * r4 + e] = x[e];
+        }
+  }
+
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  // p = 2^(x - m), packed to the bf16 B operands of P.V; returns the lane's
+  // partial sum of the packed weights.
+  // x is already in log2 units when mul == 1 (diagonal, gated scores),
+  // raw scores with mul = scale * log2(e) otherwise.
+  auto exp_pack = [&](const f32x16 (&x)[2], float mul, float m, frag (&pb)[NSK]) -> float {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSK; ++s) {
+      f32x16 pr[2];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rg = s * 8 + t;
+        pr[rg / 16][rg % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rg / 16][rg % 16], mul, -m));
+      }
+      pb[s] = MF::pack(pr, s);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const bf16x2 pair = {pb[s][2 * h], pb[s][2 * h + 1]};
+        part[h] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[h], false);
+      }
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+  auto pv = [&](const frag (&pb)[2][NSK], const E *vb) {
+#pragma unroll
+    for (int s = 0; s < NSK; ++s)
+#pragma unroll
+      for (int mb = 0; mb < NDB; ++mb) {
+        const frag a = MF::load(vb + (mb * NSK + s) * FRAG + lane * KPL);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[j][mb] = MF::run(a, pb[j][s], o[j][mb]);
+      }
+  };
+
+  for (int p = 0; p < PD; ++p)
+    if (c_top - p >= 0) stage(c_top - p, (c_top - p) % NBUF);
+  wait_all_memory();
+  lds_barrier();
+
+  for (int c = c_top; c >= 0; --c) {
+    const int buf = c % NBUF;
+    if (c - PD >= 0) stage(c - PD, (c - PD) % NBUF);
+    const E *kf_l = reinterpret_cast<const E *>(lds + buf * KVM_BYTES);
+    const E *vf_l = kf_l + C * D;
+    const E *mf_l = vf_l + C * D;
+    const float *ga = gate_l + buf * C + 4 * g;
+
+    if (valid && c == qcw) {
+      // ---- diagonal block: logits from the register image; key block 1 of
+      // query block 0 lies wholly above the diagonal.
+      const float *al_c = al + ((size_t)bh * N + qcw) * al_floats() + lane * 16;
+      frag pb[2][NSK];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int key0 = 32 * kb + 8 * r4 + 4 * g;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (kb <= j) x = *reinterpret_cast<const f32x4 *>(al_c + al_tile(j, kb) * 1024 + 4 * r4);
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            if (FOX) a = *reinterpret_cast<const f32x4 *>(ga + 32 * kb + 8 * r4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sv = key0 + e <= 32 * j + n ? __builtin_fmaf(x[e], sl2, a[e]) : -INFINITY;
+              sc[j][kb][4 * r4 + e] = sv;
+              mx = fmaxf(mx, sv);
+            }
+          }
+        m_run[j] = fmaxf(mx, __shfl_xor(mx, 32));
+        l_run[j] = exp_pack(sc[j], 1.f, m_run[j], pb[j]);
+      }
+      pv(pb, vf_l);
+    } else if (valid && c < qcw) {
+      // ---- cross step against key chunk c ----
+      frag qb[2][NSD];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) qb[j][s] = MF::pack(qw[j], s);
+      // S^T = ->K_c Q_work^T for both column blocks
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[j][kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          const frag a = MF::load(kf_l + (kb * NSD + s) * FRAG + lane * KPL);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sc[j][kb] = MF::run(a, qb[j][s], sc[j][kb]);
+        }
+      }
+      // Q_work^T <- Q_work^T - M_c^T round(Q_work^T) (unused after chunk 0)
+      if (c > 0) {
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+          for (int s = 0; s < NSD; ++s) {
+            const frag a = MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) qw[j][mb] = MF::run(a, qb[j][s], qw[j][mb]);
+          }
+      }
+      // online softmax in log2 units, x = S * scale * log2(e) + a_key; the
+      // gate of a key is read once and applied to both column blocks
+      float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          if (FOX) a = *reinterpret_cast<const f32x4 *>(ga + 32 * kb + 8 * r4);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = sc[j][kb][4 * r4 + e];
+              if (FOX) {
+                x = __builtin_fmaf(x, sl2, a[e]);
+                sc[j][kb][4 * r4 + e] = x;
+              }
+              mx[j] = fmaxf(mx[j], x);
+            }
+        }
+      float m_ref[2];
+      bool grow = false;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // without the gate the max is taken on the raw scores (scale > 0)
+        const float mj = FOX ? mx[j] : mx[j] * sl2;
+        m_ref[j] = fmaxf(m_run[j], fmaxf(mj, __shfl_xor(mj, 32)) - 8.f);
+        grow = grow || m_ref[j] > m_run[j];
+      }
+      frag pb[2][NSK];
+      float lsum[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) lsum[j] = exp_pack(sc[j], FOX ? 1.f : sl2, m_ref[j], pb[j]);
+      if (__any(grow)) {   // wave-uniform
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref[j]);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[j][mb][r] *= alpha;
+          m_run[j] = m_ref[j];
+        }
+      }
+      l_run[0] += lsum[0];
+      l_run[1] += lsum[1];
+      pv(pb, vf_l);
+    }
+
+    // chunk c-1 must have landed (this wave's share: at most the copies of
+    // chunks c-2 .. c-PD outstanding); the barrier then publishes every
+    // wave's share and frees buffer c for the next prefetch.
+    // (wave 0 also copies the gate: one more operation per chunk)
+    if (PD >= 2 && c - 2 >= 0) {
+      if (FOX && wave == 0)
+        wait_vmcnt<(PD >= 2 ? NL + 1 : 0)>();
+      else
+        wait_vmcnt<(PD >= 2 ? NL : 0)>();
+    } else {
+      wait_all_memory();
+    }
+    lds_barrier();
+  }
+
+  // ---- epilogue ----
+  if (!valid) return;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qloc = 32 * j + n;
+    const size_t qtok = (size_t)bh * T + (size_t)qcw * C + qloc;
+    const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
+    const float inv = 1.f / l_tot;
+    E *out_r = out + qtok * D;
+#pragma unroll
+    for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = o[j][mb][4 * r4 + e] * inv;
+        MF::store4(out_r + 32 * mb + 8 * r4 + 4 * g, x);
+      }
+    if (g == 0) {
+      const float a_i = FOX ? gate_h[(size_t)qcw * C + qloc] : 0.f;
+      lse[qtok] = kLn2 * (m_run[j] - a_i + __builtin_amdgcn_logf(l_tot));
+    }
+  }
+}
+
+// Launch shapes: query chunks per block (NQC) and prefetch distance (PD) per
+// (dtype, d).
+#ifndef PATH_ATTN_NQC_BF16_64
+#define PATH_ATTN_NQC_BF16_64 2
+#endif
+#ifndef PATH_ATTN_PD_BF16_64
+#define PATH_ATTN_PD_BF16_64 1
+#endif
+#ifndef PATH_ATTN_LAG_BF16_64
+#define PATH_ATTN_LAG_BF16_64 0
+#endif
+#ifndef PATH_ATTN_WIDE_BF16_64
+#define PATH_ATTN_WIDE_BF16_64 1
+#endif
+#ifndef PATH_ATTN_WIDE_NQC
+#define PATH_ATTN_WIDE_NQC 8
+#endif
+#ifndef PATH_ATTN_WIDE_PD
+#define PATH_ATTN_WIDE_PD 1
+#endif
+#ifndef PATH_ATTN_NQC_BF16_128
+#define PATH_ATTN_NQC_BF16_128 4
+#endif
+#ifndef PATH_ATTN_PD_BF16_128
+#define PATH_ATTN_PD_BF16_128 1
+#endif
 template <typename E, int D>
 struct Shape;
 template <>
-struct Shape<__bf16, 64> { static constexpr int NQC = 2, NBUF = 2; };
+struct Shape<__bf16, 64> {
+  static constexpr int NQC = PATH_ATTN_NQC_BF16_64, PD = PATH_ATTN_PD_BF16_64, LAG = PATH_ATTN_LAG_BF16_64;
+};
 template <>
-struct Shape<__bf16, 128> { static constexpr int NQC = 4, NBUF = 2; };
+struct Shape<__bf16, 128> { static constexpr int NQC = PATH_ATTN_NQC_BF16_128, PD = PATH_ATTN_PD_BF16_128, LAG = 0; };
 template <>
-struct Shape<float, 64> { static constexpr int NQC = 2, NBUF = 2; };
+struct Shape<float, 64> { static constexpr int NQC = 2, PD = 1, LAG = 0; };
 template <>
-struct Shape<float, 128> { static constexpr int NQC = 2, NBUF = 1; };
+struct Shape<float, 128> { static constexpr int NQC = 2, PD = 0, LAG = 0; };
 
 template <typename E, int D, bool FOX>
 hipError_t launch_stream_t(const float *qa, const void *kvm, const float *al,
                            const float *gate, void *out, float *lse, int BH,
                            int T, hipStream_t stream) {
-  constexpr int NQC = Shape<E, D>::NQC, NBUF = Shape<E, D>::NBUF;
   const int N = T / kChunk;
+  if constexpr (std::is_same<E, __bf16>::value && D == 64 && PATH_ATTN_WIDE_BF16_64) {
+    constexpr int NQC = PATH_ATTN_WIDE_NQC, PD = PATH_ATTN_WIDE_PD;
+    const int blocks = BH * ((N + NQC - 1) / NQC);
+    const float sl2 = kLog2e / sqrtf((float)D);
+    hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
+                       stream, qa, (const __bf16 *)kvm, al, gate, (__bf16 *)out, lse, BH, T, sl2);
+    return hipGetLastError();
+  }
+  constexpr int NQC = Shape<E, D>::NQC, PD = Shape<E, D>::PD, LAG = Shape<E, D>::LAG;
   const int blocks = BH * ((N + NQC - 1) / NQC);
   const float sl2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, NBUF>), dim3(blocks),
+  hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, PD, LAG>), dim3(blocks),
                      dim3(NQC * 128), 0, stream, qa, (const E *)kvm, al, gate,
                      (E *)out, lse, BH, T, sl2);
   return hipGetLastError();
