@@ -7,7 +7,8 @@ One step = one call of path_attn_fwd (gate prefix when present, chunk
 preparation and the streaming scan) over the whole workload, inputs already
 resident in HBM and the workspace preallocated.  W untimed warm-up steps, then
 K steps timed with HIP events on the launch stream, bracketed by device
-synchronisation.  Prints one JSON line.
+synchronisation (mean, plus median and min of the per-step times from events
+recorded between steps).  Prints one JSON line.
 
 The default workload is bf16 B=2, H=16, T=16384, d=64 (synthetic inputs,
 seeded).  value = tokens/s = B*T / (time per step).  The roofline object is
@@ -50,6 +51,13 @@ def parse():
                     help="also run a plain device copy of this many MiB (reference "
                          "kernel for scaling HBM traffic counters) and report its GB/s")
     return ap.parse_args()
+
+
+def stream_kernel_name(wl) -> str:
+    """The streaming-scan kernel that path_attn_stream launches for this shape."""
+    wide = wl.dtype == "bf16" and wl.d == 64
+    return ("stream_wide_kernel" if wide else "stream_kernel") + \
+        f"<{wl.dtype}, d={wl.d}, {'gate' if wl.fox else 'no gate'}>"
 
 
 def cpu_threads() -> int:
@@ -116,13 +124,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    # an event between consecutive steps gives per-step times as well
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     # ---- the two phases on their own (same stream, same workspace) ----
     def timed(fn, n):
@@ -166,6 +176,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_median": per_step[len(per_step) // 2],
+        "ms_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -179,7 +191,7 @@ def main():
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "ms_prep": ms_prep,
         "ms_stream": ms_stream,
-        "roofline": {"kernel": "stream_kernel", "bound": "mfma", "achieved": stream_tflops,
+        "roofline": {"kernel": stream_kernel_name(wl), "bound": "mfma", "achieved": stream_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": stream_tflops / peak,
                      "traffic": traffic,
                      "flops_per_launch": flops},
