@@ -150,6 +150,22 @@ def main():
     ms_prep = timed(lambda: pa.path_attn_prepare(q, k, v, w, beta, logf, workspace=ws), args.steps)
     ms_stream = timed(lambda: pa.path_attn_stream(ws, logf is not None, out, lse), args.steps)
 
+    fox_skip = None
+    if logf is not None:
+        # exact forget-gate block skip: share of cross steps it left out, and
+        # the scan's time with every block computed
+        cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+        pa.path_attn_stream(ws, True, out, lse, skipped=cnt)
+        torch.cuda.synchronize()
+        N = wl.T // 64
+        waves_per_chunk = 1 if (wl.dtype == "bf16" and wl.d == 64) else 2
+        cross_steps = wl.B * wl.H * N * (N - 1) // 2 * waves_per_chunk
+        ms_noskip = timed(lambda: pa.path_attn_stream(ws, True, out, lse, flags=pa.NO_SKIP),
+                          args.steps)
+        fox_skip = {"skipped_steps": int(cnt.item()), "cross_steps": cross_steps,
+                    "skipped_frac": int(cnt.item()) / max(1, cross_steps),
+                    "ms_stream_no_skip": ms_noskip}
+
     flops = wl.flops_path()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -196,6 +212,8 @@ def main():
                      "traffic": traffic,
                      "flops_per_launch": flops},
     }
+    if fox_skip is not None:
+        res["fox_skip"] = fox_skip
     if args.calib_copy_mb > 0:
         nbytes = args.calib_copy_mb << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)

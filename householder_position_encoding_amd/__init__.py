@@ -9,6 +9,7 @@ missing or no GPU is present the calls raise.
 from .binding import (  # noqa: F401
     BF16,
     F32,
+    NO_SKIP,
     PathAttnError,
     chunk_prep,
     library_path,
@@ -23,7 +24,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "BF16", "F32", "PathAttnError", "chunk_prep", "library_path",
+    "BF16", "F32", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
     "load_library", "path_attn_chunk_prep", "path_attn_fwd",
     "path_attn_prepare", "path_attn_stream",
     "path_attn_workspace_bytes", "strerror", "version",

@@ -58,6 +58,9 @@ def load_library():
     lib.path_attn_prepare.restype = ci
     lib.path_attn_stream.argtypes = [vp, sz, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.path_attn_stream.restype = ci
+    lib.path_attn_stream_ex.argtypes = [vp, sz, ci, ctypes.c_uint, vp, vp, fp, ci, ci,
+                                        ci, ci, ci, vp]
+    lib.path_attn_stream_ex.restype = ci
     lib.path_attn_strerror.argtypes = [ci]
     lib.path_attn_strerror.restype = ctypes.c_char_p
     lib.path_attn_version.argtypes = []
@@ -182,21 +185,31 @@ def path_attn_prepare(q, k, v, w, beta, logf=None, workspace=None, stream=None):
     return workspace
 
 
-def path_attn_stream(workspace, use_gate, out, lse, stream=None):
+NO_SKIP = 1   # PATH_ATTN_NO_SKIP
+
+
+def path_attn_stream(workspace, use_gate, out, lse, stream=None, flags=0,
+                     skipped=None):
     """Second phase of path_attn_fwd: the streaming scan over a workspace
-    filled by path_attn_prepare for the same shapes; writes out and lse."""
+    filled by path_attn_prepare for the same shapes; writes out and lse.
+
+    flags=NO_SKIP computes every key block (no exact forget-gate skip);
+    skipped, an int64 device tensor of one element, receives += the number of
+    skipped (wave, key block) steps (path_attn_stream_ex)."""
     torch = _torch()
     B, H, T, d = out.shape
     dt = _dtype_code(out)
     _check(lse, "lse", (B, H, T), torch.float32, out.device)
     if not out.is_contiguous():
         raise ValueError("out must be contiguous")
+    if skipped is not None:
+        _check(skipped, "skipped", (1,), torch.int64, out.device)
     lib = load_library()
-    st = lib.path_attn_stream(_ptr(workspace), workspace.numel(), int(bool(use_gate)),
-                              _ptr(out), _ptr(lse), B, H, T, d, dt,
-                              _stream_handle(stream))
+    st = lib.path_attn_stream_ex(_ptr(workspace), workspace.numel(), int(bool(use_gate)),
+                                 int(flags), _ptr(skipped), _ptr(out), _ptr(lse),
+                                 B, H, T, d, dt, _stream_handle(stream))
     if st != 0:
-        raise PathAttnError(st, "path_attn_stream")
+        raise PathAttnError(st, "path_attn_stream_ex")
     return out, lse
 
 

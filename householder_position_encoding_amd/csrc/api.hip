@@ -48,6 +48,7 @@ struct Carved {
   void *kvm;
   float *al;
   float *gate;
+  float2 *bnd;
 };
 
 Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
@@ -55,7 +56,26 @@ Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
   char *base = static_cast<char *>(workspace);
   return Carved{reinterpret_cast<float *>(base + L.qa), base + L.kvm,
                 reinterpret_cast<float *>(base + L.al),
-                reinterpret_cast<float *>(base + L.gate)};
+                reinterpret_cast<float *>(base + L.gate),
+                reinterpret_cast<float2 *>(base + L.bnd)};
+}
+
+int run_stream(const Carved &ws, bool gate, unsigned flags,
+               unsigned long long *skipped, void *out, float *lse, int BH,
+               int T, int d, int dtype, hipStream_t s) {
+  StreamArgs a;
+  a.qa = ws.qa;
+  a.kvm = ws.kvm;
+  a.al = ws.al;
+  a.gate = ws.gate;
+  a.bnd = ws.bnd;
+  a.skip = gate && !(flags & PATH_ATTN_NO_SKIP);
+  a.skipped = skipped;
+  a.out = out;
+  a.lse = lse;
+  a.BH = BH;
+  a.T = T;
+  return launch_stream(dtype, d, gate, a, s) == hipSuccess ? PATH_ATTN_OK : PATH_ATTN_EHIP;
 }
 
 // Enqueue the gate prefix (if any) and the chunk preparation.
@@ -66,6 +86,8 @@ int run_prep(const void *q, const void *k, const void *v, const void *w,
     return PATH_ATTN_EHIP;
   if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, T, s) !=
       hipSuccess)
+    return PATH_ATTN_EHIP;
+  if (logf && launch_chunk_bounds(dtype, d, ws.kvm, ws.gate, ws.bnd, BH, T, s) != hipSuccess)
     return PATH_ATTN_EHIP;
   return PATH_ATTN_OK;
 }
@@ -92,10 +114,7 @@ extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
   const int BH = B * H;
   st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
   if (st != PATH_ATTN_OK) return st;
-  if (launch_stream(dtype, d, logf != nullptr, ws.qa, ws.kvm, ws.al, ws.gate,
-                    out, lse, BH, T, s) != hipSuccess)
-    return PATH_ATTN_EHIP;
-  return PATH_ATTN_OK;
+  return run_stream(ws, logf != nullptr, 0u, nullptr, out, lse, BH, T, d, dtype, s);
 }
 
 extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
@@ -111,22 +130,31 @@ extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
                   static_cast<hipStream_t>(stream));
 }
 
-extern "C" int path_attn_stream(const void *workspace, size_t workspace_bytes,
-                                int use_gate, void *out, float *lse, int B,
-                                int H, int T, int d, int dtype, void *stream) {
+extern "C" int path_attn_stream_ex(const void *workspace, size_t workspace_bytes,
+                                   int use_gate, unsigned flags,
+                                   unsigned long long *skipped, void *out,
+                                   float *lse, int B, int H, int T, int d,
+                                   int dtype, void *stream) {
   const int st = check_shape(B, H, T, d, dtype);
   if (st != PATH_ATTN_OK) return st;
   if (!workspace || !out || !lse) return PATH_ATTN_EINVAL;
   if (use_gate != 0 && use_gate != 1) return PATH_ATTN_EINVAL;
+  if (flags & ~(unsigned)PATH_ATTN_NO_SKIP) return PATH_ATTN_EINVAL;
   if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse, 16))
     return PATH_ATTN_EINVAL;
+  if (skipped && !aligned(skipped, 8)) return PATH_ATTN_EINVAL;
   if (workspace_bytes < make_layout(B, H, T, d, elem_size(dtype)).total)
     return PATH_ATTN_EINVAL;
   const Carved ws = carve(const_cast<void *>(workspace), B, H, T, d, dtype);
-  if (launch_stream(dtype, d, use_gate == 1, ws.qa, ws.kvm, ws.al, ws.gate, out,
-                    lse, B * H, T, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return PATH_ATTN_EHIP;
-  return PATH_ATTN_OK;
+  return run_stream(ws, use_gate == 1, flags, skipped, out, lse, B * H, T, d, dtype,
+                    static_cast<hipStream_t>(stream));
+}
+
+extern "C" int path_attn_stream(const void *workspace, size_t workspace_bytes,
+                                int use_gate, void *out, float *lse, int B,
+                                int H, int T, int d, int dtype, void *stream) {
+  return path_attn_stream_ex(workspace, workspace_bytes, use_gate, 0u, nullptr,
+                             out, lse, B, H, T, d, dtype, stream);
 }
 
 extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,

@@ -36,6 +36,9 @@
 //        (1,0), (1,1) (tile (0,1) lies wholly above the diagonal):
 //        [tile][lane][r] = Al[32w + lane%32][32mb + acc_row(r, lane/32)]
 //   gate float [BH][T]          a_t = -log2(e) * sum_{1<=s<=t} log f_s (FoX)
+//   bnd  float2 [BH][N]         per key chunk, with the gate: (max_t a_t,
+//        max_j |k~_j|^2 of the bf16 (or float32) ->K rows the scan reads),
+//        inputs of the exact block skip; +inf where an input is not finite
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,7 +73,7 @@ __host__ __device__ constexpr int al_floats() { return kAlTiles * 64 * 16; }
 __host__ __device__ constexpr int al_tile(int w, int mb) { return w + mb; }
 
 struct Layout {
-  size_t qa, kvm, al, gate, total;
+  size_t qa, kvm, al, gate, bnd, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -87,6 +90,8 @@ inline Layout make_layout(int B, int H, int T, int D, size_t esize) {
   off = align256(off + BH * N * al_floats() * sizeof(float));
   L.gate = off;
   off = align256(off + BH * T * sizeof(float));
+  L.bnd = off;
+  off = align256(off + BH * N * 2 * sizeof(float));
   L.total = off;
   return L;
 }
@@ -98,9 +103,26 @@ hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
                        hipStream_t stream);
-hipError_t launch_stream(int dtype, int D, bool fox, const float *qa,
-                         const void *kvm, const float *al, const float *gate,
-                         void *out, float *lse, int BH, int T,
+hipError_t launch_chunk_bounds(int dtype, int D, const void *kvm,
+                               const float *gate, float2 *bnd, int BH, int T,
+                               hipStream_t stream);
+
+// Arguments of the streaming scan.  skip != 0 enables the exact block skip
+// with the gate (bnd must then hold the chunk bounds); skipped, if not null,
+// receives += the number of (wave, key chunk) steps skipped.
+struct StreamArgs {
+  const float *qa;
+  const void *kvm;
+  const float *al;
+  const float *gate;
+  const float2 *bnd;
+  int skip;
+  unsigned long long *skipped;
+  void *out;
+  float *lse;
+  int BH, T;
+};
+hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
                          hipStream_t stream);
 hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,
                          const float *al_ws, const float *gate, float *qa,

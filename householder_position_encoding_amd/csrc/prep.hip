@@ -721,6 +721,58 @@ hipError_t launch_prep_f32(const void *q, const void *k, const void *v,
   return hipGetLastError();
 }
 
+// Per key chunk, the two inputs of the exact block skip of the streaming scan
+// (forget gate only): the largest gate value a_t of the chunk and the largest
+// squared norm of its ->K rows as stored for the scan (bf16 values squared
+// exactly, summed in float32).  One wave per chunk, four chunks per block.
+// A non-finite value makes its bound +inf, so that no block is skipped on it.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void chunk_bounds_kernel(
+    const E *__restrict__ kvm, const float *__restrict__ gate,
+    float2 *__restrict__ bnd, int n_chunks, int T) {
+  constexpr int C = kChunk, KPL = Kpl<E>::value, NS = D / (2 * KPL);
+  const int lane = threadIdx.x & 63;
+  const int ci = blockIdx.x * 4 + (threadIdx.x >> 6);   // bh * N + c
+  if (ci >= n_chunks) return;
+  const int N = T / C;
+  const int bh = ci / N, c = ci % N;
+  float amax = gate[(size_t)bh * T + (size_t)c * C + lane];
+  if (!(amax <= 3.0e38f)) amax = INFINITY;   // NaN or +inf
+  // fragment order: in every blob of key block mb, lane l holds KPL values of
+  // row 32*mb + l%32
+  const E *kf = kvm + (size_t)ci * kvm_elems(D);
+  float kmax2 = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < KPL; ++t) {
+        const float x = to_f32(kf[((mb * NS + s) * 64 + lane) * KPL + t]);
+        ss = __builtin_fmaf(x, x, ss);
+      }
+    ss += __shfl_xor(ss, 32);
+    if (!(ss <= 3.0e38f)) ss = INFINITY;
+    kmax2 = fmaxf(kmax2, ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, o));
+  }
+  if (lane == 0) bnd[ci] = make_float2(amax, kmax2);
+}
+
+template <typename E, int D>
+hipError_t launch_chunk_bounds_t(const void *kvm, const float *gate, float2 *bnd,
+                                 int BH, int T, hipStream_t stream) {
+  const int n = BH * (T / kChunk);
+  hipLaunchKernelGGL((chunk_bounds_kernel<E, D>), dim3((n + 3) / 4), dim3(256), 0, stream,
+                     (const E *)kvm, gate, bnd, n, T);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t launch_unpack_t(const float *qa_ws, const void *kvm,
                            const float *al_ws, const float *gate, float *qa,
@@ -751,6 +803,17 @@ hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
   }
   if (D == 64) return launch_prep_f32<64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
   return launch_prep_f32<128>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
+}
+
+hipError_t launch_chunk_bounds(int dtype, int D, const void *kvm,
+                               const float *gate, float2 *bnd, int BH, int T,
+                               hipStream_t stream) {
+  if (dtype == 1) {
+    if (D == 64) return launch_chunk_bounds_t<__bf16, 64>(kvm, gate, bnd, BH, T, stream);
+    return launch_chunk_bounds_t<__bf16, 128>(kvm, gate, bnd, BH, T, stream);
+  }
+  if (D == 64) return launch_chunk_bounds_t<float, 64>(kvm, gate, bnd, BH, T, stream);
+  return launch_chunk_bounds_t<float, 128>(kvm, gate, bnd, BH, T, stream);
 }
 
 hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,

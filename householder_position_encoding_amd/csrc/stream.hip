@@ -115,17 +115,32 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// NQC query chunks per block.  Operand blocks are prefetched PD key chunks
-// ahead into a ring of PD + 1 + LAG LDS buffers (PD = 0: one buffer, loaded
-// synchronously, for shapes where two copies do not fit in LDS).  LAG = 1
-// software-pipelines each wave: the softmax and P.V of key chunk c+1 are
-// issued together with the S and transition MFMAs of chunk c (which depend
-// only on the running query tile), so vector and matrix work overlap within
-// the wave; V and the gate of chunk c+1 stay in the ring one step longer.
-template <typename E, int D, bool FOX, int NQC, int PD, int LAG>
+// Exact block skip with the forget gate.  For query i and key chunk c every
+// logit of the block obeys (log2 units, without the row constant -a_i)
+//     x_ij = scale*log2(e) * bf16(Q_work_i) . k~_j + a_j
+//         <= scale*log2(e) * |Q_work_i| * max_j |k~_j| * (1 + 2^-9 + ...) + max_j a_j,
+// with b = (max_j a_j, max_j |k~_j|^2) per chunk from the chunk preparation.
+// When this bound lies more than kSkipBelow under the running max for every
+// query of the wave, every weight 2^(x - m_ref) (m_ref >= m_run) of the block
+// is below 2^-160, i.e. exactly 0 in float32, the max does not move and l and
+// O would only add zeros: skipping S, the softmax and P.V of that block leaves
+// every result bit unchanged.  The transition of chunk c is still applied.
+constexpr float kSkipBelow = 160.f;
+
+__device__ __forceinline__ float logit_bound(float qn2, float2 b, float sl2) {
+  // 1.01 covers the bf16 rounding of the query tile, the float32 accumulation
+  // of the products and of the squared norms; +1 covers the gate's rounding.
+  return __builtin_fmaf(sl2 * __builtin_sqrtf(qn2 * b.y), 1.01f, b.x + 1.f);
+}
+
+// NQC query chunks per block, two waves per chunk.  Operand blocks are
+// prefetched PD key chunks ahead into a ring of PD + 1 LDS buffers (PD = 0:
+// one buffer, loaded synchronously, for shapes where two copies do not fit).
+template <typename E, int D, bool FOX, int NQC, int PD>
 __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     const float *__restrict__ qa, const E *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
+    const float2 *__restrict__ bnd, int skip, unsigned long long *__restrict__ skipped,
     E *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2) {
   using MF = Mfma<E>;
   using frag = typename MF::frag;
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   constexpr int KVM_BYTES = KVM * (int)sizeof(E);
   constexpr int FRAG = 64 * KPL;        // elements of one A-operand fragment
   constexpr int NW = NQC * 2;           // waves per block
-  constexpr int NBUF = PD + 1 + LAG;
+  constexpr int NBUF = PD + 1;
   constexpr int NL = KVM_BYTES / 1024 / NW;   // copy instructions per wave per chunk
   static_assert(KVM_BYTES % (1024 * NW) == 0, "operand block must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
@@ -175,16 +190,13 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     }
   };
 
-  f32x16 qw[NDB], o[NDB], sA[2], sB[2];
+  f32x16 qw[NDB], o[NDB], sc[2];
   float m_run = -INFINITY, l_run = 0.f;
+  unsigned n_skip = 0;
 #pragma unroll
   for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sA[mb][r] = sB[mb][r] = -INFINITY;
   if (valid) {  // running query tile, from the register image of <-Q
     const float *src = qa + ((size_t)bh * N + qcw) * qa_floats(D) + (size_t)half * NDB * 1024 + lane * 16;
 #pragma unroll
@@ -197,18 +209,16 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       }
   }
 
-  // Online softmax, in log2 units (logit x = S * scale * log2(e) + a_j), in
-  // three pieces so that the exponentials need no branch:
-  //  exp_scores: x and the chunk max mx; exponentiate against the reference
-  //    m_ref = max(m_run, mx - 8), so every p = 2^(x - m_ref) is at most 2^8;
-  //    returns m_ref and the lane's partial sum of p (scores -> p in place);
-  //  rebase: if m_ref exceeds the running max (rare once the nearest chunks
-  //    are in), rescale O and l to the new reference;
-  //  pv: O^T += V^T P^T.
-  // The result is the same softmax: only the common reference changes.
-  auto exp_scores = [&](f32x16 (&s_in)[2], const float *gb, float &lsum) -> float {
+  // Online softmax in log2 units (logit x = S * scale * log2(e) + a_j), lazy
+  // rescale: O and l are rescaled only when the wave-wide max grew.
+  auto softmax_pv = [&](f32x16 (&s_in)[2], const float *gb, const E *vb, bool scaled) {
     float mx = -INFINITY;
-    if (FOX) {
+    if (scaled) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_in[mb][r]);
+    } else if (FOX) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -230,58 +240,53 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       mx *= sl2;
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_ref = fmaxf(m_run, mx - 8.f);
-    lsum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(
-            FOX ? s_in[mb][r] - m_ref : __builtin_fmaf(s_in[mb][r], sl2, -m_ref));
-        s_in[mb][r] = pr;
-        lsum += pr;
-      }
-    return m_ref;
-  };
-  auto rebase = [&](float m_ref) {
-    if (__any(m_ref > m_run)) {   // wave-uniform
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    if (__any(mx > m_run)) {   // wave-uniform
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-      m_run = m_ref;
+      m_run = m_new;
     }
-  };
-  auto pv = [&](const f32x16 (&pr)[2], const E *vb) {
+    const bool raw = !scaled && !FOX;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(
+            raw ? __builtin_fmaf(s_in[mb][r], sl2, -m_run) : s_in[mb][r] - m_run);
+        s_in[mb][r] = pr;
+        l_run += pr;
+      }
 #pragma unroll
     for (int s = 0; s < NSK; ++s) {
-      const frag pb = MF::pack(pr, s);
+      const frag pb = MF::pack(s_in, s);
 #pragma unroll
       for (int mb = 0; mb < NDB; ++mb)
         o[mb] = MF::run(MF::load(vb + (mb * NSK + s) * FRAG + lane * KPL), pb, o[mb]);
     }
   };
-  auto buf_ptr = [&](int b) { return reinterpret_cast<const E *>(lds + b * KVM_BYTES); };
 
-  // One step of the walk against key chunk c.  snew receives this step's
-  // scores; with LAG, sprev holds the previous cross step's scores (or -inf)
-  // and is absorbed here, against V and the gate of chunk c+1.
-  auto step = [&](int c, f32x16 (&snew)[2], f32x16 (&sprev)[2]) {
+  for (int p = 0; p <= (PD > 0 ? PD - 1 : 0); ++p)
+    if (c_top - p >= 0) stage(c_top - p, (c_top - p) % NBUF);
+  wait_all_memory();
+  lds_barrier();
+
+  for (int c = c_top; c >= 0; --c) {
     const int buf = c % NBUF;
     if (PD > 0 && c - PD >= 0) stage(c - PD, (c - PD) % NBUF);
-    const E *kf_l = buf_ptr(buf);
+    const E *kf_l = reinterpret_cast<const E *>(lds + buf * KVM_BYTES);
     const E *vf_l = kf_l + C * D;
     const E *mf_l = vf_l + C * D;
+    const float *ga = gate_l + buf * C + 4 * g;
 
     if (valid && c == qcw) {
       // ---- diagonal block: register image of its logits; the key block
       // above the diagonal of the first half (keys 32..63, queries 0..31) is
       // wholly masked.
       const float *al_c = al + ((size_t)bh * N + qcw) * al_floats() + lane * 16;
-      const float *ga = gate_l + buf * C + 4 * g;
-      float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -292,66 +297,47 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
           if (FOX) a = *reinterpret_cast<const f32x4 *>(ga + 32 * mb + 8 * r4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sv = key0 + e <= qloc ? __builtin_fmaf(x[e], sl2, a[e]) : -INFINITY;
-            snew[mb][4 * r4 + e] = sv;
-            mx = fmaxf(mx, sv);
-          }
+          for (int e = 0; e < 4; ++e)
+            sc[mb][4 * r4 + e] = key0 + e <= qloc ? __builtin_fmaf(x[e], sl2, a[e]) : -INFINITY;
         }
-      m_run = fmaxf(mx, __shfl_xor(mx, 32));
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(snew[mb][r] - m_run);
-          snew[mb][r] = pr;
-          l_run += pr;
-        }
-      pv(snew, vf_l);
-      // nothing is pending for the first cross step
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) snew[mb][r] = -INFINITY;
+      softmax_pv(sc, ga, vf_l, true);
     } else if (valid && c < qcw) {
       // ---- cross step against key chunk c ----
+      bool skip_blk = false;
+      if (FOX && skip) {
+        float qn2 = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) qn2 = __builtin_fmaf(qw[mb][r], qw[mb][r], qn2);
+        qn2 += __shfl_xor(qn2, 32);
+        skip_blk = __all(logit_bound(qn2, bnd[(size_t)bh * N + c], sl2) < m_run - kSkipBelow);
+        n_skip += skip_blk;
+      }
       frag qb[NSD];
 #pragma unroll
       for (int s = 0; s < NSD; ++s) qb[s] = MF::pack(qw, s);
-      // S^T = ->K_c Q_work^T, then Q_work^T <- Q_work^T - M_c^T round(Q_work^T)
-      // (crossing chunk c's transition; after chunk 0 the tile is not used)
+      if (!skip_blk) {
+        // S^T = ->K_c Q_work^T
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) snew[mb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) sc[mb][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < NSD; ++s)
-          snew[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], snew[mb]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < NDB; ++mb)
-#pragma unroll
-        for (int s = 0; s < NSD; ++s)
-          qw[mb] = MF::run(MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], qw[mb]);
-      float lsum;
-      if (LAG) {
-        // the previous chunk's softmax overlaps this step's MFMAs
-        const int pb_ = (c + 1) % NBUF;
-        const float m_ref = exp_scores(sprev, gate_l + pb_ * C + 4 * g, lsum);
-#pragma unroll
-        for (int i = 0; i < 2 * NSD + NDB * NSD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+          for (int s = 0; s < NSD; ++s)
+            sc[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], sc[mb]);
         }
-        rebase(m_ref);
-        l_run += lsum;
-        pv(sprev, buf_ptr(pb_) + C * D);
-      } else {
-        const float m_ref = exp_scores(snew, gate_l + buf * C + 4 * g, lsum);
-        rebase(m_ref);
-        l_run += lsum;
-        pv(snew, vf_l);
       }
+      // Q_work^T <- Q_work^T - M_c^T round(Q_work^T): crossing chunk c's
+      // transition (after chunk 0 the tile is not used)
+      if (c > 0) {
+#pragma unroll
+        for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+          for (int s = 0; s < NSD; ++s)
+            qw[mb] = MF::run(MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], qw[mb]);
+      }
+      if (!skip_blk) softmax_pv(sc, ga, vf_l, false);
     }
 
     if (PD == 0) {
@@ -364,47 +350,24 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     } else {
       // This wave's share of chunk c-1 has landed once at most the copies of
       // the chunks issued after it (c-2 .. c-PD, those that exist) are
-      // outstanding; the barrier then makes everyone's share visible and
-      // frees buffer c for the next prefetch.
-      if (PD >= 2 && c - 2 >= 0)
-        wait_vmcnt<(PD >= 2 ? NL : 0)>();
-      else
+      // outstanding (wave 0 also copies the gate: one more operation per
+      // chunk); the barrier then makes everyone's share visible and frees
+      // buffer c for the next prefetch.
+      if (PD >= 2 && c - 2 >= 0) {
+        if (FOX && wave == 0)
+          wait_vmcnt<(PD >= 2 ? NL + 1 : 0)>();
+        else
+          wait_vmcnt<(PD >= 2 ? NL : 0)>();
+      } else {
         wait_all_memory();
+      }
       lds_barrier();
-    }
-  };
-
-  for (int p = 0; p <= (PD > 0 ? PD - 1 : 0); ++p)
-    if (c_top - p >= 0) stage(c_top - p, (c_top - p) % NBUF);
-  wait_all_memory();
-  lds_barrier();
-
-  // Unrolled by two so that the pending and the fresh scores alternate
-  // between sA and sB without copies.
-  for (int c = c_top; c >= 0; c -= 2) {
-    step(c, sA, sB);
-    if (c >= 1) step(c - 1, sB, sA);
-  }
-
-  // the last cross step's scores (key chunk 0) are still pending with LAG;
-  // they sit in the array the step with c = 0 wrote
-  if (LAG && valid) {
-    float lsum;
-    if ((c_top & 1) == 0) {
-      const float m_ref = exp_scores(sA, gate_l + 4 * g, lsum);
-      rebase(m_ref);
-      l_run += lsum;
-      pv(sA, buf_ptr(0) + C * D);
-    } else {
-      const float m_ref = exp_scores(sB, gate_l + 4 * g, lsum);
-      rebase(m_ref);
-      l_run += lsum;
-      pv(sB, buf_ptr(0) + C * D);
     }
   }
 
   // ---- epilogue: o_i = O_i / l_i, lse_i = ln 2 (m + log2 l - a_i) ----
   if (!valid) return;
+  if (FOX && skipped && lane == 0 && n_skip) atomicAdd(skipped, (unsigned long long)n_skip);
   const size_t qtok = (size_t)bh * T + (size_t)qcw * C + qloc;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
@@ -437,6 +400,7 @@ template <int D, bool FOX, int NQC, int PD>
 __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
     const float *__restrict__ qa, const __bf16 *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
+    const float2 *__restrict__ bnd, int skip, unsigned long long *__restrict__ skipped,
     __bf16 *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2) {
   using E = __bf16;
   using MF = Mfma<E>;
@@ -485,6 +449,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 
   f32x16 qw[2][NDB], o[2][NDB], sc[2][2];
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  unsigned n_skip = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -583,6 +548,22 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       pv(pb, vf_l);
     } else if (valid && c < qcw) {
       // ---- cross step against key chunk c ----
+      bool skip_blk = false;
+      if (FOX && skip) {   // exact block skip, see logit_bound
+        bool below = true;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float qn2 = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) qn2 = __builtin_fmaf(qw[j][mb][r], qw[j][mb][r], qn2);
+          qn2 += __shfl_xor(qn2, 32);
+          below = below && logit_bound(qn2, bnd[(size_t)bh * N + c], sl2) < m_run[j] - kSkipBelow;
+        }
+        skip_blk = __all(below);
+        n_skip += skip_blk;
+      }
       frag qb[2][NSD];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -590,7 +571,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
         for (int s = 0; s < NSD; ++s) qb[j][s] = MF::pack(qw[j], s);
       // S^T = ->K_c Q_work^T for both column blocks
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2 && !skip_blk; ++kb) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -613,6 +594,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
             for (int j = 0; j < 2; ++j) qw[j][mb] = MF::run(a, qb[j][s], qw[j][mb]);
           }
       }
+      if (!skip_blk) {
       // online softmax in log2 units, x = S * scale * log2(e) + a_key; the
       // gate of a key is read once and applied to both column blocks
       float mx[2] = {-INFINITY, -INFINITY};
@@ -662,6 +644,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       l_run[0] += lsum[0];
       l_run[1] += lsum[1];
       pv(pb, vf_l);
+      }
     }
 
     // chunk c-1 must have landed (this wave's share: at most the copies of
@@ -681,6 +664,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 
   // ---- epilogue ----
   if (!valid) return;
+  if (FOX && skipped && lane == 0 && n_skip) atomicAdd(skipped, (unsigned long long)n_skip);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int qloc = 32 * j + n;
@@ -704,17 +688,8 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
   }
 }
 
-// Launch shapes: query chunks per block (NQC) and prefetch distance (PD) per
-// (dtype, d).
-#ifndef PATH_ATTN_NQC_BF16_64
-#define PATH_ATTN_NQC_BF16_64 2
-#endif
-#ifndef PATH_ATTN_PD_BF16_64
-#define PATH_ATTN_PD_BF16_64 1
-#endif
-#ifndef PATH_ATTN_LAG_BF16_64
-#define PATH_ATTN_LAG_BF16_64 0
-#endif
+// Launch shapes: query chunks per block (NQC) and prefetch distance (PD) of
+// the narrow kernel per (dtype, d); bf16 d = 64 runs the wide kernel.
 #ifndef PATH_ATTN_WIDE_BF16_64
 #define PATH_ATTN_WIDE_BF16_64 1
 #endif
@@ -733,58 +708,50 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 template <typename E, int D>
 struct Shape;
 template <>
-struct Shape<__bf16, 64> {
-  static constexpr int NQC = PATH_ATTN_NQC_BF16_64, PD = PATH_ATTN_PD_BF16_64, LAG = PATH_ATTN_LAG_BF16_64;
-};
+struct Shape<__bf16, 64> { static constexpr int NQC = 2, PD = 1; };
 template <>
-struct Shape<__bf16, 128> { static constexpr int NQC = PATH_ATTN_NQC_BF16_128, PD = PATH_ATTN_PD_BF16_128, LAG = 0; };
+struct Shape<__bf16, 128> { static constexpr int NQC = PATH_ATTN_NQC_BF16_128, PD = PATH_ATTN_PD_BF16_128; };
 template <>
-struct Shape<float, 64> { static constexpr int NQC = 2, PD = 1, LAG = 0; };
+struct Shape<float, 64> { static constexpr int NQC = 2, PD = 1; };
 template <>
-struct Shape<float, 128> { static constexpr int NQC = 2, PD = 0, LAG = 0; };
+struct Shape<float, 128> { static constexpr int NQC = 2, PD = 0; };
 
 template <typename E, int D, bool FOX>
-hipError_t launch_stream_t(const float *qa, const void *kvm, const float *al,
-                           const float *gate, void *out, float *lse, int BH,
-                           int T, hipStream_t stream) {
-  const int N = T / kChunk;
+hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
+  const int N = a.T / kChunk;
+  const float sl2 = kLog2e / sqrtf((float)D);
   if constexpr (std::is_same<E, __bf16>::value && D == 64 && PATH_ATTN_WIDE_BF16_64) {
     constexpr int NQC = PATH_ATTN_WIDE_NQC, PD = PATH_ATTN_WIDE_PD;
-    const int blocks = BH * ((N + NQC - 1) / NQC);
-    const float sl2 = kLog2e / sqrtf((float)D);
+    const int blocks = a.BH * ((N + NQC - 1) / NQC);
     hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
-                       stream, qa, (const __bf16 *)kvm, al, gate, (__bf16 *)out, lse, BH, T, sl2);
+                       stream, a.qa, (const __bf16 *)a.kvm, a.al, a.gate, a.bnd, a.skip,
+                       a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2);
     return hipGetLastError();
   }
-  constexpr int NQC = Shape<E, D>::NQC, PD = Shape<E, D>::PD, LAG = Shape<E, D>::LAG;
-  const int blocks = BH * ((N + NQC - 1) / NQC);
-  const float sl2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, PD, LAG>), dim3(blocks),
-                     dim3(NQC * 128), 0, stream, qa, (const E *)kvm, al, gate,
-                     (E *)out, lse, BH, T, sl2);
+  constexpr int NQC = Shape<E, D>::NQC, PD = Shape<E, D>::PD;
+  const int blocks = a.BH * ((N + NQC - 1) / NQC);
+  hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 128), 0,
+                     stream, a.qa, (const E *)a.kvm, a.al, a.gate, a.bnd, a.skip, a.skipped,
+                     (E *)a.out, a.lse, a.BH, a.T, sl2);
   return hipGetLastError();
 }
 
 template <typename E, int D>
-hipError_t launch_stream_d(bool fox, const float *qa, const void *kvm,
-                           const float *al, const float *gate, void *out,
-                           float *lse, int BH, int T, hipStream_t stream) {
-  if (fox) return launch_stream_t<E, D, true>(qa, kvm, al, gate, out, lse, BH, T, stream);
-  return launch_stream_t<E, D, false>(qa, kvm, al, gate, out, lse, BH, T, stream);
+hipError_t launch_stream_d(bool fox, const StreamArgs &a, hipStream_t stream) {
+  if (fox) return launch_stream_t<E, D, true>(a, stream);
+  return launch_stream_t<E, D, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_stream(int dtype, int D, bool fox, const float *qa,
-                         const void *kvm, const float *al, const float *gate,
-                         void *out, float *lse, int BH, int T,
+hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
                          hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 64) return launch_stream_d<__bf16, 64>(fox, qa, kvm, al, gate, out, lse, BH, T, stream);
-    return launch_stream_d<__bf16, 128>(fox, qa, kvm, al, gate, out, lse, BH, T, stream);
+    if (D == 64) return launch_stream_d<__bf16, 64>(fox, a, stream);
+    return launch_stream_d<__bf16, 128>(fox, a, stream);
   }
-  if (D == 64) return launch_stream_d<float, 64>(fox, qa, kvm, al, gate, out, lse, BH, T, stream);
-  return launch_stream_d<float, 128>(fox, qa, kvm, al, gate, out, lse, BH, T, stream);
+  if (D == 64) return launch_stream_d<float, 64>(fox, a, stream);
+  return launch_stream_d<float, 128>(fox, a, stream);
 }
 
 }  // namespace pathattn

@@ -61,13 +61,18 @@ extern "C" {
 #define PATH_ATTN_F32 0
 #define PATH_ATTN_BF16 1
 
+/* Flags of path_attn_stream_ex. */
+#define PATH_ATTN_NO_SKIP 1u    /* compute every key block, even those the exact
+                                   forget-gate skip would leave out */
+
 /*
  * Workspace size in bytes that path_attn_fwd / path_attn_chunk_prep need for
  * this problem, or 0 if the arguments are invalid or unsupported.  The size
  * is linear in B*H*T: per 64-token chunk it holds the boundary-adjusted
  * queries (float32), the transformed keys, the values and the chunk transform
- * in the matrix-core operand order, the diagonal-block logits (float32) and,
- * per token, the forget-gate prefix (float32).
+ * in the matrix-core operand order, the diagonal-block logits (float32) and
+ * two float32 bounds used with the forget gate; per token, the forget-gate
+ * prefix (float32).
  */
 size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype);
 
@@ -108,6 +113,31 @@ int path_attn_prepare(const void *q, const void *k, const void *v,
 int path_attn_stream(const void *workspace, size_t workspace_bytes,
                      int use_gate, void *out, float *lse, int B, int H, int T,
                      int d, int dtype, void *stream);
+
+/*
+ * path_attn_stream with options.  With the forget gate (use_gate = 1) the
+ * scan leaves out the S, softmax and P.V work of a key block when a bound on
+ * every logit of the block (the query tile's norm times the chunk's largest
+ * key norm, times the scale, plus the chunk's largest gate term) lies more
+ * than 160 (log2 units) below every running max of the wave: each weight of
+ * such a block is then below 2^-160, exactly zero in float32, so the outputs
+ * are the same bits as without the skip (up to the sign of an output element
+ * that is exactly zero).  The gate makes far blocks vanish (FoX slides,
+ * "FoX adds a separate mechanism for forgetting"); the skip itself is this
+ * library's, not the pages'.  The chunk transitions are always applied.
+ *
+ * flags:   0 or PATH_ATTN_NO_SKIP (compute every block).
+ * skipped: NULL, or a device counter (8-byte aligned) to which the scan adds
+ *          the number of steps it skipped, one per wave and key block (a
+ *          wave covers 32 queries, 64 for bf16 d = 64); the caller zeroes it.
+ * Other arguments and errors as path_attn_stream; unknown flag bits give
+ * PATH_ATTN_EINVAL.  path_attn_stream(...) == path_attn_stream_ex(..., 0,
+ * NULL, ...), and path_attn_fwd uses the skip.
+ */
+int path_attn_stream_ex(const void *workspace, size_t workspace_bytes,
+                        int use_gate, unsigned flags,
+                        unsigned long long *skipped, void *out, float *lse,
+                        int B, int H, int T, int d, int dtype, void *stream);
 
 /*
  * Chunk preparation only, with its results unpacked into plain float32

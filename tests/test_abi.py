@@ -48,9 +48,11 @@ def test_version_and_strerror():
 def test_workspace_bytes(dtype, esize, B, H, T, d):
     n = pa.path_attn_workspace_bytes(B, H, T, d, dtype)
     BH, N = B * H, T // 64
-    # <-Q (fp32), the three per-chunk operands, 3 of 4 diagonal-logit tiles (fp32), gate
-    expect = BH * T * d * 4 + BH * N * (2 * 64 * d + d * d) * esize + BH * N * 3 * 64 * 16 * 4 + BH * T * 4
-    assert expect <= n <= expect + 4 * 256
+    # <-Q (fp32), the three per-chunk operands, 3 of 4 diagonal-logit tiles (fp32), gate,
+    # two float32 skip bounds per chunk
+    expect = (BH * T * d * 4 + BH * N * (2 * 64 * d + d * d) * esize + BH * N * 3 * 64 * 16 * 4
+              + BH * T * 4 + BH * N * 2 * 4)
+    assert expect <= n <= expect + 5 * 256
 
 
 @pytest.mark.parametrize("args", [(0, 1, 64, 64, 1), (1, 0, 64, 64, 1), (1, 1, 0, 64, 1),
@@ -102,6 +104,13 @@ def test_prepare_and_stream_validation():
     assert lib.path_attn_stream(FAKE, 1 << 40, 0, FAKE, FAKE + 4, 1, 1, 64, 64, 1, None) == EINVAL
     assert lib.path_attn_stream(FAKE, 100, 0, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
     assert lib.path_attn_stream(FAKE, 1 << 40, 0, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
+    # stream_ex: unknown flag bits, misaligned counter, plus the stream checks
+    ex = lib.path_attn_stream_ex
+    assert ex(FAKE, 1 << 40, 1, 2, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 1, 1, FAKE + 4, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 2, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 100, 1, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 1, 1, None, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
 
 
 def test_chunk_prep_validation():

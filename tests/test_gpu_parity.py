@@ -250,3 +250,54 @@ def test_binding_rejects_bad_tensors():
         pa.path_attn_fwd(t(dev["q"]), t(dev["k"]), t(dev["v"]), t(dev["w"]), t(dev["beta"]))
     assert e.value.status == 2
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ exact forget-gate skip
+
+@pytest.mark.parametrize("dtype,d,T", [("bf16", 64, 1024), ("bf16", 128, 1024),
+                                       ("f32", 64, 512), ("f32", 128, 256)])
+def test_fox_block_skip_is_exact(dtype, d, T):
+    """With strong forgetting (log f = logsigmoid(N(-1, 1)), about -1.9 in log2
+    units per token) every key block more than a chunk or two back has all its
+    weights below 2^-160: the scan skips them, and the outputs are the same
+    bits as with every block computed, and match the oracle."""
+    import torch
+    import householder_position_encoding_amd as pa
+    inp = dict(workloads.small(dtype, 1, 2, T, d, seed=31 + d, fox=True))
+    rng = np.random.default_rng(5 + d)
+    inp["logf"] = (-np.logaddexp(0.0, -rng.normal(-1.0, 1.0, size=(1, 2, T)))).astype(np.float32)
+    dev = to_device(inp, dtype)
+    ws = pa.path_attn_prepare(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"])
+    out_s, out_f = torch.empty_like(dev["q"]), torch.empty_like(dev["q"])
+    lse_s = torch.empty((1, 2, T), dtype=torch.float32, device="cuda")
+    lse_f = torch.empty_like(lse_s)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    pa.path_attn_stream(ws, True, out_s, lse_s, skipped=cnt)
+    pa.path_attn_stream(ws, True, out_f, lse_f, flags=pa.NO_SKIP)
+    torch.cuda.synchronize()
+    n_skip = int(cnt.item())
+    ibits = torch.int16 if dtype == "bf16" else torch.int32
+    _log(f"fox skip {dtype} d={d} T={T}: {n_skip} skipped steps")
+    assert n_skip > 0
+    assert torch.equal(out_s.view(ibits), out_f.view(ibits))
+    assert torch.equal(lse_s.view(torch.int32), lse_f.view(torch.int32))
+    o_ref, l_ref = oracle_full(inp)
+    _assert_close(f"fox skip {dtype} d={d}", dtype, out_s.float().cpu().numpy().astype(np.float64),
+                  lse_s.cpu().numpy().astype(np.float64), o_ref, l_ref)
+
+
+def test_fox_skip_counter_zero_without_decay():
+    """With no forgetting (log f = 0) no bound can fall 160 below the running
+    max, so nothing is skipped."""
+    import torch
+    import householder_position_encoding_amd as pa
+    inp = dict(workloads.small("bf16", 1, 2, 512, 64, seed=3, fox=True))
+    inp["logf"] = np.zeros_like(inp["logf"])
+    dev = to_device(inp, "bf16")
+    ws = pa.path_attn_prepare(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"])
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((1, 2, 512), dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    pa.path_attn_stream(ws, True, out, lse, skipped=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0
