@@ -8,6 +8,7 @@ missing or no GPU is present the calls raise.
 """
 from .binding import (  # noqa: F401
     BF16,
+    DecodeCache,
     F32,
     NO_SKIP,
     PathAttnError,
@@ -15,7 +16,9 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     path_attn_chunk_prep,
+    path_attn_decode_step,
     path_attn_fwd,
+    path_attn_prefill_cache,
     path_attn_prepare,
     path_attn_stream,
     path_attn_workspace_bytes,
@@ -24,8 +27,9 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "BF16", "F32", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
-    "load_library", "path_attn_chunk_prep", "path_attn_fwd",
+    "BF16", "DecodeCache", "F32", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
+    "load_library", "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd",
+    "path_attn_prefill_cache",
     "path_attn_prepare", "path_attn_stream",
     "path_attn_workspace_bytes", "strerror", "version",
 ]

@@ -61,6 +61,16 @@ def load_library():
     lib.path_attn_stream_ex.argtypes = [vp, sz, ci, ctypes.c_uint, vp, vp, fp, ci, ci,
                                         ci, ci, ci, vp]
     lib.path_attn_stream_ex.restype = ci
+    lib.path_attn_prefill_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.path_attn_prefill_workspace_bytes.restype = sz
+    lib.path_attn_prefill_cache.argtypes = [vp, vp, vp, fp, fp, vp, vp, vp, ci, ci, ci, ci,
+                                            ci, ci, ci, vp, sz, vp]
+    lib.path_attn_prefill_cache.restype = ci
+    lib.path_attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.path_attn_decode_workspace_bytes.restype = sz
+    lib.path_attn_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, vp, ci, vp, fp,
+                                          ci, ci, ci, ci, ci, ci, vp, sz, vp]
+    lib.path_attn_decode_step.restype = ci
     lib.path_attn_strerror.argtypes = [ci]
     lib.path_attn_strerror.restype = ctypes.c_char_p
     lib.path_attn_version.argtypes = []
@@ -241,3 +251,97 @@ def chunk_prep(q, k, v, w, beta, logf=None, stream=None):
 def path_attn_chunk_prep(*args):
     """Raw C-ABI call with integer pointers (see include/path_attn.h)."""
     return int(load_library().path_attn_chunk_prep(*args))
+
+
+# ---------------------------------------------------------------- decoding
+
+class DecodeCache:
+    """Caller-side caches for decoding with in-place key refinement.
+
+    kcache [B, H, T_cap, d] (kc_dtype), vcache [B, H, T_cap, d] (dtype),
+    gcache [B, H, T_cap] float64 (only with the forget gate), plus the
+    decode workspace.  `length` is the number of positions filled.
+    """
+
+    def __init__(self, B, H, T_cap, d, dtype, kc_dtype=None, fox=False, device="cuda"):
+        torch = _torch()
+        self.B, self.H, self.T_cap, self.d = B, H, T_cap, d
+        self.dtype = dtype
+        self.kc_dtype = torch.float32 if kc_dtype is None else kc_dtype
+        self.fox = fox
+        self.kcache = torch.zeros((B, H, T_cap, d), dtype=self.kc_dtype, device=device)
+        self.vcache = torch.zeros((B, H, T_cap, d), dtype=dtype, device=device)
+        self.gcache = torch.zeros((B, H, T_cap), dtype=torch.float64, device=device) if fox else None
+        need = load_library().path_attn_decode_workspace_bytes(B, H, T_cap, d)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        self.length = 0
+
+
+def _code_of(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def path_attn_prefill_cache(cache, k, v, w, beta, logf=None, workspace=None, stream=None):
+    """Fill positions 0..L-1 of `cache` from a prompt (k, v, w [B, H, L, d];
+    beta, logf [B, H, L]); L must be a multiple of 64."""
+    torch = _torch()
+    B, H, L, d = k.shape
+    dev = k.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (no CPU path)")
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        _check(t, name, (cache.B, cache.H, L, cache.d), cache.dtype, dev)
+    _check(beta, "beta", (B, H, L), torch.float32, dev)
+    if (logf is not None) != cache.fox:
+        raise ValueError("logf must be given exactly when the cache has a gate")
+    if logf is not None:
+        _check(logf, "logf", (B, H, L), torch.float32, dev)
+    lib = load_library()
+    need = lib.path_attn_prefill_workspace_bytes(B, H, L, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.path_attn_prefill_cache(
+        _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(cache.kcache),
+        _ptr(cache.vcache), _ptr(cache.gcache), B, H, L, cache.T_cap, d,
+        _code_of(cache.dtype), _code_of(cache.kc_dtype), _ptr(workspace), workspace.numel(),
+        _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_prefill_cache")
+    cache.length = L
+    return cache
+
+
+def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None, stream=None):
+    """One decode step at position cache.length: q, k, v, w [B, H, d];
+    beta, logf [B, H].  Returns (out [B, H, d], lse [B, H])."""
+    torch = _torch()
+    B, H, d = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (no CPU path)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("w", w)):
+        _check(t, name, (cache.B, cache.H, cache.d), cache.dtype, dev)
+    _check(beta, "beta", (B, H), torch.float32, dev)
+    if (logf is not None) != cache.fox:
+        raise ValueError("logf must be given exactly when the cache has a gate")
+    if logf is not None:
+        _check(logf, "logf", (B, H), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    lib = load_library()
+    st = lib.path_attn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(cache.kcache),
+        _ptr(cache.vcache), _ptr(cache.gcache), cache.length, _ptr(out), _ptr(lse), B, H,
+        cache.T_cap, d, _code_of(cache.dtype), _code_of(cache.kc_dtype),
+        _ptr(cache.workspace), cache.workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_decode_step")
+    cache.length += 1
+    return out, lse

@@ -181,6 +181,102 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
   return PATH_ATTN_OK;
 }
 
+// ---------------------------------------------------------------- decoding
+
+namespace {
+
+int check_decode_shape(int B, int H, int T_cap, int d, int dtype, int kc_dtype) {
+  if (B <= 0 || H <= 0 || T_cap <= 0 || d <= 0) return PATH_ATTN_EINVAL;
+  if ((dtype != PATH_ATTN_F32 && dtype != PATH_ATTN_BF16) ||
+      (kc_dtype != PATH_ATTN_F32 && kc_dtype != PATH_ATTN_BF16))
+    return PATH_ATTN_EINVAL;
+  if (d != 64 && d != 128) return PATH_ATTN_EUNSUPPORTED;
+  if ((unsigned long long)B * H * T_cap * d >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
+  if ((unsigned long long)B * H >= 65536ull) return PATH_ATTN_EUNSUPPORTED;
+  return PATH_ATTN_OK;
+}
+
+struct PrefillLayout {
+  size_t kb, m, total;
+};
+
+PrefillLayout prefill_layout(int B, int H, int L, int d) {
+  const size_t BH = (size_t)B * H, N = (size_t)L / kChunk;
+  PrefillLayout P;
+  P.kb = 0;
+  P.m = align256(BH * L * d * sizeof(float));
+  P.total = P.m + align256(BH * N * d * d * sizeof(float));
+  return P;
+}
+
+}  // namespace
+
+extern "C" size_t path_attn_prefill_workspace_bytes(int B, int H, int L, int d) {
+  if (B <= 0 || H <= 0 || L < 0 || (d != 64 && d != 128) || L % kChunk != 0) return 0;
+  return prefill_layout(B, H, L, d).total;
+}
+
+extern "C" int path_attn_prefill_cache(const void *k, const void *v, const void *w,
+                                       const float *beta, const float *logf, void *kcache,
+                                       void *vcache, double *gcache, int B, int H, int L,
+                                       int T_cap, int d, int dtype, int kc_dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_decode_shape(B, H, T_cap, d, dtype, kc_dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (L < 0 || L > T_cap) return PATH_ATTN_EINVAL;
+  if (L % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;
+  if (!kcache || !vcache) return PATH_ATTN_EINVAL;
+  if (logf && !gcache) return PATH_ATTN_EINVAL;
+  if (L > 0 && (!k || !v || !w || !beta)) return PATH_ATTN_EINVAL;
+  const void *ptrs[] = {k, v, w, beta, logf, kcache, vcache, gcache};
+  for (const void *p : ptrs)
+    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
+  const PrefillLayout P = prefill_layout(B, H, L, d);
+  if (L > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < P.total))
+    return PATH_ATTN_EINVAL;
+  if (L == 0) return PATH_ATTN_OK;
+  char *base = static_cast<char *>(workspace);
+  return launch_prefill_cache(dtype, kc_dtype, d, k, v, w, beta, logf, kcache, vcache, gcache,
+                              reinterpret_cast<float *>(base + P.kb),
+                              reinterpret_cast<float *>(base + P.m), B * H, L, T_cap,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PATH_ATTN_OK
+             : PATH_ATTN_EHIP;
+}
+
+extern "C" size_t path_attn_decode_workspace_bytes(int B, int H, int T_cap, int d) {
+  if (B <= 0 || H <= 0 || T_cap <= 0 || (d != 64 && d != 128)) return 0;
+  return align256(decode_partial_bytes(B * H, T_cap, d));
+}
+
+extern "C" int path_attn_decode_step(const void *q, const void *k, const void *v, const void *w,
+                                     const float *beta, const float *logf, void *kcache,
+                                     void *vcache, double *gcache, int t, void *out, float *lse,
+                                     int B, int H, int T_cap, int d, int dtype, int kc_dtype,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_decode_shape(B, H, T_cap, d, dtype, kc_dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (t < 0 || t >= T_cap) return PATH_ATTN_EINVAL;
+  if (!q || !k || !v || !w || !beta || !kcache || !vcache || !out || !lse || !workspace)
+    return PATH_ATTN_EINVAL;
+  if (logf && !gcache) return PATH_ATTN_EINVAL;
+  // vectors are read 16 bytes at a time; the per-head scalars one at a time
+  const void *vecs[] = {q, k, v, w, kcache, vcache, gcache, out};
+  for (const void *p : vecs)
+    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
+  const void *scalars[] = {beta, logf, lse};
+  for (const void *p : scalars)
+    if (p && !aligned(p, 4)) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256) ||
+      workspace_bytes < path_attn_decode_workspace_bytes(B, H, T_cap, d))
+    return PATH_ATTN_EINVAL;
+  return launch_decode_step(dtype, kc_dtype, d, q, k, v, w, beta, logf, kcache, vcache, gcache,
+                            out, lse, static_cast<float *>(workspace), B * H, t, T_cap,
+                            static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PATH_ATTN_OK
+             : PATH_ATTN_EHIP;
+}
+
 extern "C" const char *path_attn_strerror(int status) {
   switch (status) {
     case PATH_ATTN_OK: return "ok";

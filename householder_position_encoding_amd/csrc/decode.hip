@@ -1,0 +1,582 @@
+// decode.hip -- PaTH decoding with in-place key refinement.
+//
+// PaTH discussion slides for arXiv:2505.16381v2, frame "Decoding updates
+// historical keys in place" (paper Sec. 3.4, Eq. (1)): when token t arrives,
+// every cached key is reflected by H_t = I - beta_t w_t w_t^T,
+//
+//     k_j <- k_j - beta_t w_t (w_t . k_j),    j < t,
+//
+// after which k_j . q_t is the path logit k_j^T H_{j+1} ... H_t q_t and the
+// readout is ordinary softmax attention over the refined keys and the new key
+// k_t.  Before decoding, the cache of a prompt of length L must hold every key
+// aligned to the prompt end: k~_j = H_{L-1} ... H_{j+1} k_j.
+//
+// Prefill alignment.  Per 64-token chunk c the chunk algebra of the forward
+// pass gives ->K_c (row j: H_last ... H_{j+1} k_j) and M_c = W^T U W (H_last
+// ... H_first = I - M_c).  With G_c the transpose of the product of the
+// transforms of all later chunks, G_{N-1} = I and G_{c-1} = G_c - M_c^T G_c,
+// the aligned rows of chunk c are ->K_c G_c.  The right-to-left recurrence
+// runs per (batch, head); every column of G evolves on its own, so a head's
+// columns are split over several blocks.  Everything is float32.
+//
+// Decode step (flash-decoding with the refinement fused in): the cached keys
+// 0..t-1 are split over blocks; each block reflects its keys by H_t, writes
+// them back, forms the logits with q_t and keeps an online-softmax partial
+// (max, sum, weighted values) in log2 units.  A combine kernel merges the
+// partials with the new key k_t (whose logit has an empty path) and appends
+// k_t, v_t and the gate prefix to the caches.
+//
+// With the forget gate the logit of (t, j) gains Lambda_t - Lambda_j with
+// Lambda_t = sum_{1<=s<=t} log f_s, kept in float64 in the gate cache so that
+// the running sum does not drift over long decodes (PaTH slides, frame "FoX
+// adds a separate mechanism for forgetting").
+#include <type_traits>
+
+#include "path_attn_internal.h"
+
+namespace pathattn {
+
+namespace {
+
+constexpr float kLog2eD = 1.4426950408889634f;
+constexpr float kLn2D = 0.69314718055994531f;
+
+template <typename E>
+__device__ __forceinline__ float to_f(E x) { return (float)x; }
+template <typename E>
+__device__ __forceinline__ E from_f(float x) { return (E)x; }   // RNE for bf16
+
+// ------------------------------------------------------------ prefill: chunks
+
+// One block of 256 threads per (bh, chunk): ->K_c and M_c in float32, natural
+// layouts kb[bh][L][D] and m[bh][N][D][D] (M[a][b]).
+// U = (I + strictLower(D W W^T))^{-1} D by forward substitution,
+// T2 = U strictLower(W K^T), ->K = K - T2^T W, M = W^T (U W).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void align_prep_kernel(
+    const E *__restrict__ k, const E *__restrict__ w, const float *__restrict__ beta,
+    float *__restrict__ kb, float *__restrict__ m, int L) {
+  constexpr int C = kChunk, DP = D + 1, CP = C + 1, NT = 256;
+  __shared__ float Ws[C * DP];
+  __shared__ float UWs[C * DP];
+  __shared__ float Us[C * CP];
+  __shared__ float Xs[C * CP];
+  __shared__ float T2s[C * CP];
+  __shared__ float bs[C];
+  const int N = L / C;
+  const int bh = blockIdx.x / N, c = blockIdx.x % N;
+  const size_t row0 = (size_t)bh * L + (size_t)c * C;
+  const int tid = threadIdx.x;
+  const E *kc = k + row0 * D;
+  const E *wc = w + row0 * D;
+
+  for (int idx = tid; idx < C * D; idx += NT) Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
+  if (tid < C) bs[tid] = beta[row0 + tid];
+  __syncthreads();
+  // N[i][j] = beta_i (w_i . w_j), j < i
+  for (int idx = tid; idx < C * C; idx += NT) {
+    const int i = idx / C, j = idx % C;
+    float s = 0.f;
+    if (j < i) {
+      for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ws[i * DP + e], Ws[j * DP + e], s);
+      s *= bs[i];
+    }
+    Us[i * CP + j] = s;
+  }
+  __syncthreads();
+  // X = (I + N)^{-1} below the diagonal, one column per lane of wave 0:
+  // X[i][j] = -N[i][j] - sum_{j<t<i} N[i][t] X[t][j]
+  if (tid < C) {
+    const int j = tid;
+    for (int i = j + 1; i < C; ++i) {
+      float x = -Us[i * CP + j];
+      for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Us[i * CP + t], Xs[t * CP + j], x);
+      Xs[i * CP + j] = x;
+    }
+  }
+  __syncthreads();
+  // U = X D (unit diagonal of X times beta)
+  for (int idx = tid; idx < C * C; idx += NT) {
+    const int i = idx / C, j = idx % C;
+    Us[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);
+  }
+  __syncthreads();
+  // UW = U W;  SK[t][j] = w_t . k_j for t > j (into Xs)
+  for (int idx = tid; idx < C * D; idx += NT) {
+    const int s = idx / D, col = idx % D;
+    float acc = 0.f;
+    for (int t = 0; t <= s; ++t) acc = __builtin_fmaf(Us[s * CP + t], Ws[t * DP + col], acc);
+    UWs[s * DP + col] = acc;
+  }
+  for (int idx = tid; idx < C * C; idx += NT) {
+    const int t = idx / C, j = idx % C;
+    float acc = 0.f;
+    if (t > j)
+      for (int e = 0; e < D; ++e) acc = __builtin_fmaf(Ws[t * DP + e], to_f(kc[(size_t)j * D + e]), acc);
+    Xs[t * CP + j] = acc;
+  }
+  __syncthreads();
+  // T2[s][j] = sum_{j<t<=s} U[s][t] SK[t][j]
+  for (int idx = tid; idx < C * C; idx += NT) {
+    const int s = idx / C, j = idx % C;
+    float acc = 0.f;
+    for (int t = j + 1; t <= s; ++t) acc = __builtin_fmaf(Us[s * CP + t], Xs[t * CP + j], acc);
+    T2s[s * CP + j] = acc;
+  }
+  __syncthreads();
+  // ->K[j][col] = K[j][col] - sum_{s>j} T2[s][j] W[s][col]
+  float *kb_c = kb + row0 * D;
+  for (int idx = tid; idx < C * D; idx += NT) {
+    const int j = idx / D, col = idx % D;
+    float acc = to_f(kc[idx]);
+    for (int s = j + 1; s < C; ++s) acc = __builtin_fmaf(-T2s[s * CP + j], Ws[s * DP + col], acc);
+    kb_c[idx] = acc;
+  }
+  // M[a][b] = sum_s W[s][a] UW[s][b]
+  float *m_c = m + ((size_t)bh * N + c) * D * D;
+  for (int idx = tid; idx < D * D; idx += NT) {
+    const int a = idx / D, b = idx % D;
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc = __builtin_fmaf(Ws[s * DP + a], UWs[s * DP + b], acc);
+    m_c[idx] = acc;
+  }
+}
+
+// ------------------------------------------------------------ prefill: scan
+
+// One block per (bh, slice of CB columns of G).  Thread (rg, cb) = (tid / CB,
+// tid % CB) owns column cb of the slice, rows rg + RG*i.  Chunk by chunk from
+// the last: stage ->K_c and M_c in LDS, write the aligned rows ->K_c G_c of
+// this column slice, then G <- G - M_c^T G.
+template <typename KC, int D>
+__global__ __launch_bounds__(256) void align_scan_kernel(
+    const float *__restrict__ kb, const float *__restrict__ m, KC *__restrict__ kcache,
+    int L, int T_cap) {
+  constexpr int C = kChunk, NT = 256, CB = 16, RG = NT / CB;
+  constexpr int DP = D + 1;
+  constexpr int KR = C / RG;      // rows of ->K G per thread
+  constexpr int GR = D / RG;      // rows of G per thread
+  constexpr int NSL = D / CB;     // column slices per head
+  __shared__ float Ks[C * DP];
+  __shared__ float Ms[D * DP];
+  __shared__ float Gs[D * CB];
+  const int N = L / C;
+  const int bh = blockIdx.x / NSL, sl = blockIdx.x % NSL;
+  const int tid = threadIdx.x, cb = tid % CB, rg = tid / CB;
+  const int col = sl * CB + cb;   // column of G (and of the key) this thread owns
+
+  for (int i = 0; i < GR; ++i) {
+    const int a = rg + RG * i;
+    Gs[a * CB + cb] = a == col ? 1.f : 0.f;
+  }
+  for (int c = N - 1; c >= 0; --c) {
+    __syncthreads();   // previous chunk's reads of Ks/Ms/Gs are done
+    const float *kb_c = kb + ((size_t)bh * L + (size_t)c * C) * D;
+    const float *m_c = m + ((size_t)bh * N + c) * D * D;
+    for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = kb_c[idx];
+    for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
+    __syncthreads();
+    // aligned rows of chunk c: (->K_c G_c)[j][col]
+    float acc[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) acc[i] = 0.f;
+    for (int a = 0; a < D; ++a) {
+      const float g = Gs[a * CB + cb];
+#pragma unroll
+      for (int i = 0; i < KR; ++i) acc[i] = __builtin_fmaf(Ks[(rg + RG * i) * DP + a], g, acc[i]);
+    }
+    KC *dst = kcache + ((size_t)bh * T_cap + (size_t)c * C) * D + col;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) dst[(size_t)(rg + RG * i) * D] = from_f<KC>(acc[i]);
+    // G <- G - M_c^T G for this column
+    float gn[GR];
+#pragma unroll
+    for (int i = 0; i < GR; ++i) gn[i] = Gs[(rg + RG * i) * CB + cb];
+    for (int r = 0; r < D; ++r) {
+      const float g = Gs[r * CB + cb];
+#pragma unroll
+      for (int i = 0; i < GR; ++i) gn[i] = __builtin_fmaf(-Ms[r * DP + rg + RG * i], g, gn[i]);
+    }
+    __syncthreads();   // all reads of the old G are done
+#pragma unroll
+    for (int i = 0; i < GR; ++i) Gs[(rg + RG * i) * CB + cb] = gn[i];
+  }
+}
+
+// Values of the prompt into the value cache: vcache[bh][j] = v[bh][j], j < L.
+template <typename E>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const E *__restrict__ v, E *__restrict__ vcache,
+                                                        int L, int T_cap, int D) {
+  const size_t per_head = (size_t)L * D;
+  const size_t bh = blockIdx.y;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_head; i += (size_t)gridDim.x * 256)
+    vcache[bh * (size_t)T_cap * D + i] = v[bh * per_head + i];
+}
+
+// Gate cache of the prompt: Lambda_j = sum_{1<=s<=j} log f_s in float64 (f_0
+// never enters a logit), one block per (b, h), sequential in one thread.
+__global__ __launch_bounds__(64) void gate_cache_kernel(const float *__restrict__ logf,
+                                                        double *__restrict__ gcache, int L, int T_cap) {
+  const int bh = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  double acc = 0.0;
+  gcache[(size_t)bh * T_cap] = 0.0;
+  for (int j = 1; j < L; ++j) {
+    acc += (double)logf[(size_t)bh * L + j];
+    gcache[(size_t)bh * T_cap + j] = acc;
+  }
+}
+
+// ------------------------------------------------------------ decode step
+
+template <typename T>
+struct Vec16;   // 16 bytes of T
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct Vec16<__bf16> {
+  static constexpr int n = 8;
+  typedef __bf16 type __attribute__((ext_vector_type(8)));
+};
+
+// Load / store n consecutive elements as floats.
+template <typename T, int n>
+__device__ __forceinline__ void load_f(const T *p, float (&x)[n]) {
+  if constexpr (std::is_same<T, float>::value && n == 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v[e];
+  } else if constexpr (std::is_same<T, __bf16>::value && n == 8) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  } else if constexpr (std::is_same<T, __bf16>::value && n == 4) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+  } else {
+    static_assert(std::is_same<T, float>::value && n == 8, "unsupported vector");
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+}
+template <typename T, int n>
+__device__ __forceinline__ void store_f(T *p, const float (&x)[n]) {
+  if constexpr (std::is_same<T, float>::value && n == 4) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  } else {
+    static_assert(std::is_same<T, __bf16>::value && n == 8, "unsupported vector");
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    *reinterpret_cast<bf16x8 *>(p) = v;
+  }
+}
+
+// Sum over the LPK lanes of a key group (aligned groups of LPK lanes).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = LPK / 2; off >= 1; off /= 2) x += __shfl_xor(x, off);
+  return x;
+}
+
+constexpr int kKeysPerSplit = 512;
+constexpr int kUnroll = 4;
+
+// Partials per (bh, split): m, l (log2 units, max and sum), then o[D].
+template <int D>
+__host__ __device__ constexpr int partial_floats() { return D + 2; }
+
+// One block of 256 threads per (split, bh): keys [split*KPS, min(t, +KPS)).
+// A key row is spread over LPK lanes with EPL consecutive elements each
+// (16-byte loads of the key cache); a wave covers KPW = 64 / LPK keys at once.
+template <typename E, typename KC, int D, bool FOX>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const E *__restrict__ q, const E *__restrict__ w, const float *__restrict__ beta,
+    const float *__restrict__ logf, KC *__restrict__ kcache, const E *__restrict__ vcache,
+    const double *__restrict__ gcache, float *__restrict__ part, int t, int T_cap, int nsplit,
+    float sl2) {
+  constexpr int EPL = Vec16<KC>::n;
+  constexpr int LPK = D / EPL;
+  constexpr int KPW = 64 / LPK;
+  constexpr int NW = 4;
+  constexpr int STRIDE = NW * KPW;          // keys per block iteration
+  constexpr int PF = partial_floats<D>();
+  __shared__ float red_m[NW * KPW], red_l[NW * KPW];
+  __shared__ float red_o[NW * KPW][D];
+
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPK, e0 = (lane % LPK) * EPL;
+  const int j_begin = split * kKeysPerSplit;
+  const int j_end = min(t, j_begin + kKeysPerSplit);
+
+  float qv[EPL], wv[EPL];
+  load_f<E, EPL>(q + (size_t)bh * D + e0, qv);
+  load_f<E, EPL>(w + (size_t)bh * D + e0, wv);
+  const float bt = beta[bh];
+  double lam_t = 0.0;
+  if (FOX) lam_t = (t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] : 0.0) + (t >= 1 ? (double)logf[bh] : 0.0);
+  KC *kc_h = kcache + (size_t)bh * T_cap * D;
+  const E *vc_h = vcache + (size_t)bh * T_cap * D;
+  const double *gc_h = FOX ? gcache + (size_t)bh * T_cap : nullptr;
+
+  float m_run = -INFINITY, l_run = 0.f, o_run[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o_run[e] = 0.f;
+
+  for (int base = j_begin + wave * KPW + grp; base < j_end; base += kUnroll * STRIDE) {
+    float kk[kUnroll][EPL], vv[kUnroll][EPL], x[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = base + u * STRIDE;
+      ok[u] = j < j_end;
+      if (ok[u]) {
+        load_f<KC, EPL>(kc_h + (size_t)j * D + e0, kk[u]);
+        load_f<E, EPL>(vc_h + (size_t)j * D + e0, vv[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kk[u][e] = vv[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      // k_j <- k_j - beta_t w_t (w_t . k_j), written back in place
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = __builtin_fmaf(wv[e], kk[u][e], a);
+      a = group_sum<LPK>(a) * bt;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kk[u][e] = __builtin_fmaf(-a, wv[e], kk[u][e]);
+      const int j = base + u * STRIDE;
+      if (ok[u]) store_f<KC, EPL>(kc_h + (size_t)j * D + e0, kk[u]);
+      // the logit uses the key as stored (rounded to the cache type)
+      float kr[EPL];
+      if constexpr (std::is_same<KC, float>::value) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kr[e] = kk[u][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kr[e] = (float)(__bf16)kk[u][e];
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s = __builtin_fmaf(qv[e], kr[e], s);
+      s = group_sum<LPK>(s);
+      float xv = s * sl2;
+      if (FOX && ok[u]) xv += (float)((lam_t - gc_h[j]) * (double)kLog2eD);
+      x[u] = ok[u] ? xv : -INFINITY;
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, x[u]);
+    if (mx > -INFINITY) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o_run[e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float p = __builtin_amdgcn_exp2f(x[u] - mx);
+        l_run += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o_run[e] = __builtin_fmaf(p, vv[u][e], o_run[e]);
+      }
+      m_run = mx;
+    }
+  }
+
+  // combine the KPW key groups of every wave and the NW waves: slot
+  // (wave, grp) in LDS, then the first KPW*NW... reduced by wave 0
+  const int slot = wave * KPW + grp;
+  if (lane % LPK == 0) {
+    red_m[slot] = m_run;
+    red_l[slot] = l_run;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red_o[slot][e0 + e] = o_run[e];
+  __syncthreads();
+  float *dst = part + ((size_t)bh * nsplit + split) * PF;
+  if (threadIdx.x < D) {
+    float M = -INFINITY;
+    for (int s = 0; s < NW * KPW; ++s) M = fmaxf(M, red_m[s]);
+    float l = 0.f, o = 0.f;
+    if (M > -INFINITY) {
+      for (int s = 0; s < NW * KPW; ++s) {
+        const float f = __builtin_amdgcn_exp2f(red_m[s] - M);
+        l = __builtin_fmaf(f, red_l[s], l);
+        o = __builtin_fmaf(f, red_o[s][threadIdx.x], o);
+      }
+    }
+    dst[2 + threadIdx.x] = o;
+    if (threadIdx.x == 0) {
+      dst[0] = M;
+      dst[1] = l;
+    }
+  }
+}
+
+// One block of D threads per bh: merge the split partials with the new key
+// k_t (logit scale * q_t . k_t, no gate term), write o_t and lse_t, append
+// k_t, v_t and Lambda_t to the caches.
+template <typename E, typename KC, int D, bool FOX>
+__global__ __launch_bounds__(128) void decode_combine_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ logf, KC *__restrict__ kcache, E *__restrict__ vcache,
+    double *__restrict__ gcache, const float *__restrict__ part, E *__restrict__ out,
+    float *__restrict__ lse, int t, int T_cap, int nsplit, float sl2) {
+  constexpr int PF = partial_floats<D>();
+  __shared__ float red[D];
+  const int bh = blockIdx.x, e = threadIdx.x;
+  const float qe = to_f(q[(size_t)bh * D + e]);
+  const float ke = to_f(k[(size_t)bh * D + e]);
+  const float ve = to_f(v[(size_t)bh * D + e]);
+  red[e] = qe * ke;
+  __syncthreads();
+  for (int off = D / 2; off >= 1; off /= 2) {
+    if (e < off) red[e] += red[e + off];
+    __syncthreads();
+  }
+  const float x_new = red[0] * sl2;
+  float M = x_new;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[((size_t)bh * nsplit + s) * PF]);
+  const float f_new = __builtin_amdgcn_exp2f(x_new - M);
+  float l = f_new, o = f_new * ve;
+  for (int s = 0; s < nsplit; ++s) {
+    const float *p = part + ((size_t)bh * nsplit + s) * PF;
+    if (p[0] > -INFINITY) {
+      const float f = __builtin_amdgcn_exp2f(p[0] - M);
+      l = __builtin_fmaf(f, p[1], l);
+      o = __builtin_fmaf(f, p[2 + e], o);
+    }
+  }
+  out[(size_t)bh * D + e] = from_f<E>(o / l);
+  if (e == 0) lse[bh] = kLn2D * (M + __builtin_amdgcn_logf(l));
+  kcache[((size_t)bh * T_cap + t) * D + e] = from_f<KC>(ke);
+  vcache[((size_t)bh * T_cap + t) * D + e] = v[(size_t)bh * D + e];
+  if (FOX && e == 0)
+    gcache[(size_t)bh * T_cap + t] =
+        t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] + (double)logf[bh] : 0.0;
+}
+
+template <typename E, typename KC, int D>
+hipError_t prefill_t(const void *k, const void *v, const void *w, const float *beta,
+                     const float *logf, void *kcache, void *vcache, double *gcache, float *ws_kb,
+                     float *ws_m, int BH, int L, int T_cap, hipStream_t stream) {
+  const int N = L / kChunk;
+  if (N > 0) {
+    hipLaunchKernelGGL((align_prep_kernel<E, D>), dim3(BH * N), dim3(256), 0, stream,
+                       (const E *)k, (const E *)w, beta, ws_kb, ws_m, L);
+    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 16)), dim3(256), 0, stream,
+                       ws_kb, ws_m, (KC *)kcache, L, T_cap);
+    const int gx = min(1024, (int)(((size_t)L * D + 255) / 256));
+    hipLaunchKernelGGL((copy_rows_kernel<E>), dim3(gx, BH), dim3(256), 0, stream, (const E *)v,
+                       (E *)vcache, L, T_cap, D);
+    if (logf)
+      hipLaunchKernelGGL(gate_cache_kernel, dim3(BH), dim3(64), 0, stream, logf, gcache, L, T_cap);
+  }
+  return hipGetLastError();
+}
+
+template <typename E, typename KC, int D, bool FOX>
+hipError_t decode_t(const void *q, const void *k, const void *v, const void *w,
+                    const float *beta, const float *logf, void *kcache, void *vcache,
+                    double *gcache, void *out, float *lse, float *part, int BH, int t,
+                    int T_cap, hipStream_t stream) {
+  const float sl2 = kLog2eD / sqrtf((float)D);
+  const int nsplit = (t + kKeysPerSplit - 1) / kKeysPerSplit;
+  if (nsplit > 0)
+    hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0,
+                       stream, (const E *)q, (const E *)w, beta, logf, (KC *)kcache,
+                       (const E *)vcache, gcache, part, t, T_cap, nsplit, sl2);
+  hipLaunchKernelGGL((decode_combine_kernel<E, KC, D, FOX>), dim3(BH), dim3(D), 0, stream,
+                     (const E *)q, (const E *)k, (const E *)v, logf, (KC *)kcache, (E *)vcache,
+                     gcache, part, (E *)out, lse, t, T_cap, nsplit, sl2);
+  return hipGetLastError();
+}
+
+template <typename E, typename KC>
+hipError_t prefill_d(int D, const void *k, const void *v, const void *w, const float *beta,
+                     const float *logf, void *kcache, void *vcache, double *gcache,
+                     float *ws_kb, float *ws_m, int BH, int L, int T_cap, hipStream_t s) {
+  if (D == 64)
+    return prefill_t<E, KC, 64>(k, v, w, beta, logf, kcache, vcache, gcache, ws_kb, ws_m, BH, L,
+                                T_cap, s);
+  return prefill_t<E, KC, 128>(k, v, w, beta, logf, kcache, vcache, gcache, ws_kb, ws_m, BH, L,
+                               T_cap, s);
+}
+
+template <typename E, typename KC>
+hipError_t decode_d(int D, const void *q, const void *k, const void *v, const void *w,
+                    const float *beta, const float *logf, void *kcache, void *vcache,
+                    double *gcache, void *out, float *lse, float *part, int BH, int t,
+                    int T_cap, hipStream_t s) {
+  if (D == 64) {
+    if (logf)
+      return decode_t<E, KC, 64, true>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                       part, BH, t, T_cap, s);
+    return decode_t<E, KC, 64, false>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                      part, BH, t, T_cap, s);
+  }
+  if (logf)
+    return decode_t<E, KC, 128, true>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                      part, BH, t, T_cap, s);
+  return decode_t<E, KC, 128, false>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                     part, BH, t, T_cap, s);
+}
+
+}  // namespace
+
+size_t decode_partial_bytes(int BH, int T_cap, int D) {
+  const size_t nsplit = ((size_t)T_cap + kKeysPerSplit - 1) / kKeysPerSplit;
+  return (size_t)BH * (nsplit > 0 ? nsplit : 1) * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_prefill_cache(int dtype, int kc_dtype, int D, const void *k, const void *v,
+                                const void *w, const float *beta, const float *logf,
+                                void *kcache, void *vcache, double *gcache, float *ws_kb,
+                                float *ws_m, int BH, int L, int T_cap, hipStream_t s) {
+  if (dtype == 1) {
+    if (kc_dtype == 1)
+      return prefill_d<__bf16, __bf16>(D, k, v, w, beta, logf, kcache, vcache, gcache, ws_kb,
+                                       ws_m, BH, L, T_cap, s);
+    return prefill_d<__bf16, float>(D, k, v, w, beta, logf, kcache, vcache, gcache, ws_kb, ws_m,
+                                     BH, L, T_cap, s);
+  }
+  if (kc_dtype == 1)
+    return prefill_d<float, __bf16>(D, k, v, w, beta, logf, kcache, vcache, gcache, ws_kb, ws_m,
+                                    BH, L, T_cap, s);
+  return prefill_d<float, float>(D, k, v, w, beta, logf, kcache, vcache, gcache, ws_kb, ws_m, BH,
+                                 L, T_cap, s);
+}
+
+hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, const void *k,
+                              const void *v, const void *w, const float *beta,
+                              const float *logf, void *kcache, void *vcache, double *gcache,
+                              void *out, float *lse, float *part, int BH, int t, int T_cap,
+                              hipStream_t s) {
+  if (dtype == 1) {
+    if (kc_dtype == 1)
+      return decode_d<__bf16, __bf16>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out,
+                                      lse, part, BH, t, T_cap, s);
+    return decode_d<__bf16, float>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                   part, BH, t, T_cap, s);
+  }
+  if (kc_dtype == 1)
+    return decode_d<float, __bf16>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                   part, BH, t, T_cap, s);
+  return decode_d<float, float>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
+                                part, BH, t, T_cap, s);
+}
+
+}  // namespace pathattn

@@ -129,4 +129,16 @@ hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,
                          float *kb, float *m, float *al, float *lam, int BH,
                          int T, hipStream_t stream);
 
+// Decoding with in-place key refinement (decode.hip).
+size_t decode_partial_bytes(int BH, int T_cap, int D);
+hipError_t launch_prefill_cache(int dtype, int kc_dtype, int D, const void *k, const void *v,
+                                const void *w, const float *beta, const float *logf,
+                                void *kcache, void *vcache, double *gcache, float *ws_kb,
+                                float *ws_m, int BH, int L, int T_cap, hipStream_t s);
+hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, const void *k,
+                              const void *v, const void *w, const float *beta,
+                              const float *logf, void *kcache, void *vcache, double *gcache,
+                              void *out, float *lse, float *part, int BH, int t, int T_cap,
+                              hipStream_t s);
+
 }  // namespace pathattn

@@ -163,6 +163,79 @@ int path_attn_chunk_prep(const void *q, const void *k, const void *v,
                          int B, int H, int T, int d, int dtype, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * ------------------------------------------------------------------------
+ * Decoding with in-place key refinement (PaTH slides, frame "Decoding
+ * updates historical keys in place", paper Sec. 3.4, Eq. (1); the authors'
+ * response page, "Inference Latency", on fusing the refinement into
+ * flash-decoding).  When token t arrives, every cached key is reflected by
+ * H_t:  k_j <- k_j - beta_t w_t (w_t . k_j) for j < t; then k_j . q_t equals
+ * the path logit k_j^T H_{j+1} ... H_t q_t and the readout is ordinary
+ * softmax attention over the refined keys and the new key k_t.  A prompt's
+ * keys must first be aligned to its last position L-1:
+ *     kcache[j] = H_{L-1} ... H_{j+1} k_j    (j < L; kcache[L-1] = k_{L-1}).
+ *
+ * Caches (caller-owned device memory, capacity T_cap positions per head):
+ *     kcache [B, H, T_cap, d]  kc_dtype (PATH_ATTN_F32 or PATH_ATTN_BF16)
+ *     vcache [B, H, T_cap, d]  dtype
+ *     gcache [B, H, T_cap]     float64 Lambda_j = sum_{1<=s<=j} log f_s
+ *                              (only with the forget gate; NULL otherwise)
+ * Positions >= the current length are never read.  With kc_dtype =
+ * PATH_ATTN_BF16 every refinement rounds the stored key to bf16 again, so the
+ * error grows with the number of decode steps; PATH_ATTN_F32 keeps the
+ * refined keys in float32.  The logits use the keys as stored.
+ * ------------------------------------------------------------------------
+ */
+
+/* Workspace bytes of path_attn_prefill_cache, 0 for invalid arguments. */
+size_t path_attn_prefill_workspace_bytes(int B, int H, int L, int d);
+
+/*
+ * Fill positions 0..L-1 of the caches from a prompt of length L (a multiple
+ * of 64, 0 <= L <= T_cap): aligned keys (float32 arithmetic: per 64-token
+ * chunk the UT form of the forward pass, then the products of the later
+ * chunks' transforms applied right to left), values copied, and with logf
+ * the gate prefix Lambda_j (float64).  k, v, w: [B, H, L, d] of dtype; beta,
+ * logf: [B, H, L] float32 (logf may be NULL; gcache is then unused).
+ * Tokens of a prompt beyond a multiple of 64 are fed with
+ * path_attn_decode_step, which also returns their outputs.
+ * Errors: EINVAL for null/misaligned pointers (16 bytes; workspace 256),
+ * bad dtypes, L < 0, L > T_cap or a small workspace; EUNSUPPORTED for d not
+ * in {64, 128}, L % 64 != 0 or B*H*T_cap*d >= 2^31; EHIP on a launch error.
+ */
+int path_attn_prefill_cache(const void *k, const void *v, const void *w,
+                            const float *beta, const float *logf,
+                            void *kcache, void *vcache, double *gcache, int B,
+                            int H, int L, int T_cap, int d, int dtype,
+                            int kc_dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of path_attn_decode_step (partial softmax states), 0 for
+ * invalid arguments. */
+size_t path_attn_decode_workspace_bytes(int B, int H, int T_cap, int d);
+
+/*
+ * One decode step at position t (0 <= t < T_cap) for all B*H heads.  The
+ * caches must hold positions 0..t-1 aligned to t-1 (after a prefill of
+ * length t, or after the step at t-1).  The step reflects cached keys
+ * 0..t-1 by H_t in place, appends k_t, v_t (and Lambda_t = Lambda_{t-1} +
+ * log f_t, Lambda_0 = 0) at position t, and writes
+ *     out[b,h,:] = sum_{j<=t} softmax_j(s_tj) v_j        (dtype, RNE)
+ *     lse[b,h]   = ln sum_{j<=t} exp(s_tj)                (float32)
+ * with s_tj = (k_j . q_t) / sqrt(d) + Lambda_t - Lambda_j (gate term only
+ * with logf).  q, k, v, w, out: [B, H, d] of dtype; beta, logf, lse: [B, H]
+ * float32.  Keys are split over blocks (512 per block) and the partial
+ * softmax states merged in a second kernel.  Alignment: q, k, v, w, out and
+ * the caches 16 bytes; beta, logf and lse 4 bytes (one value per head).
+ * Errors as for path_attn_prefill_cache; t outside [0, T_cap) is EINVAL.
+ */
+int path_attn_decode_step(const void *q, const void *k, const void *v,
+                          const void *w, const float *beta, const float *logf,
+                          void *kcache, void *vcache, double *gcache, int t,
+                          void *out, float *lse, int B, int H, int T_cap, int d,
+                          int dtype, int kc_dtype, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static, human-readable description of a status code. */
 const char *path_attn_strerror(int status);
 

@@ -41,6 +41,23 @@ def refined_keys(k, w, beta, upto: int):
     return k
 
 
+def aligned_key_rows(k, w, beta, rows, upto: int):
+    """Selected keys of one head aligned to position `upto`: for each j in
+    `rows` (j <= upto), H_upto ... H_{j+1} k_j, fp64, obtained by applying
+    H_{j+1}, H_{j+2}, ..., H_upto to k_j one reflection at a time.  k, w:
+    [T, d]; beta: [T].  Returns [len(rows), d].  Cost O((upto - j) d) per
+    row, so full-length contexts can be sampled."""
+    w = np.asarray(w, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    out = []
+    for j in rows:
+        z = np.array(k[j], dtype=np.float64)
+        for t in range(j + 1, upto + 1):
+            z -= beta[t] * (w[t] @ z) * w[t]
+        out.append(z)
+    return np.stack(out) if out else np.zeros((0, np.shape(k)[-1]))
+
+
 def gate_prefix(logf):
     """Lambda_t = sum_{s=1..t} log f_s (fp64; f_0 never enters a logit).
     logf: [..., T]."""

@@ -125,6 +125,82 @@ def test_chunk_prep_validation():
     assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 64, 80, 1, FAKE, 1 << 40, None) == EUNSUP
 
 
+# ---- decoding entry points
+
+def test_decode_workspace_sizes():
+    # prefill: float32 ->K rows and per-chunk d x d transforms
+    B, H, L, d = 2, 16, 16384, 64
+    n = pa.load_library().path_attn_prefill_workspace_bytes(B, H, L, d)
+    expect = B * H * L * d * 4 + B * H * (L // 64) * d * d * 4
+    assert expect <= n <= expect + 512
+    assert pa.load_library().path_attn_prefill_workspace_bytes(1, 1, 100, 64) == 0
+    assert pa.load_library().path_attn_prefill_workspace_bytes(1, 1, 64, 96) == 0
+    # decode: one (max, sum, d values) partial per head and 512-key split
+    n = pa.load_library().path_attn_decode_workspace_bytes(B, H, 16386, d)
+    assert n >= B * H * 33 * (d + 2) * 4
+    assert pa.load_library().path_attn_decode_workspace_bytes(1, 1, 0, 64) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, kc=FAKE, vc=FAKE, gc=None,
+             B=1, H=2, L=128, T_cap=256, d=64, dtype=pa.BF16, kc_dtype=pa.F32, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.path_attn_prefill_cache(a["k"], a["v"], a["w"], a["beta"], a["logf"], a["kc"],
+                                       a["vc"], a["gc"], a["B"], a["H"], a["L"], a["T_cap"],
+                                       a["d"], a["dtype"], a["kc_dtype"], a["ws"], a["wsb"],
+                                       a["stream"])
+
+
+BAD_PREFILL = [
+    (dict(k=None), EINVAL), (dict(kc=None), EINVAL), (dict(vc=None), EINVAL),
+    (dict(logf=FAKE), EINVAL),                       # a gate needs the gate cache
+    (dict(k=FAKE + 2), EINVAL), (dict(gc=FAKE + 8, logf=FAKE), EINVAL),
+    (dict(ws=None), EINVAL), (dict(ws=FAKE + 16), EINVAL), (dict(wsb=100), EINVAL),
+    (dict(L=-64), EINVAL), (dict(L=512), EINVAL),    # longer than the cache
+    (dict(kc_dtype=3), EINVAL), (dict(dtype=2), EINVAL), (dict(T_cap=0), EINVAL),
+    (dict(L=100), EUNSUP), (dict(d=80), EUNSUP),
+    (dict(B=1 << 12, H=1 << 9, T_cap=1 << 14), EUNSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_PREFILL, ids=lambda x: str(x))
+def test_prefill_validation(kw, status):
+    assert _prefill(pa.load_library(), **kw) == status
+
+
+def test_prefill_empty_prompt_launches_nothing():
+    # L = 0 is valid and does nothing (no HIP call is made: the addresses are fake)
+    assert _prefill(pa.load_library(), L=0, k=None, v=None, w=None, beta=None, ws=None) == OK
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, kc=FAKE, vc=FAKE, gc=None,
+             t=5, out=FAKE, lse=FAKE, B=1, H=2, T_cap=256, d=64, dtype=pa.BF16,
+             kc_dtype=pa.F32, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.path_attn_decode_step(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"],
+                                     a["kc"], a["vc"], a["gc"], a["t"], a["out"], a["lse"],
+                                     a["B"], a["H"], a["T_cap"], a["d"], a["dtype"],
+                                     a["kc_dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+BAD_DECODE = [
+    (dict(q=None), EINVAL), (dict(w=None), EINVAL), (dict(beta=None), EINVAL),
+    (dict(kc=None), EINVAL), (dict(out=None), EINVAL), (dict(lse=None), EINVAL),
+    (dict(ws=None), EINVAL), (dict(logf=FAKE), EINVAL), (dict(lse=FAKE + 2), EINVAL),
+    (dict(beta=FAKE + 1), EINVAL), (dict(q=FAKE + 4), EINVAL),
+    (dict(ws=FAKE + 64), EINVAL), (dict(wsb=8), EINVAL),
+    (dict(t=-1), EINVAL), (dict(t=256), EINVAL), (dict(kc_dtype=-1), EINVAL),
+    (dict(d=32), EUNSUP), (dict(B=1 << 12, H=1 << 9, T_cap=1 << 14), EUNSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_DECODE, ids=lambda x: str(x))
+def test_decode_validation(kw, status):
+    assert _decode(pa.load_library(), **kw) == status
+
+
 def test_binding_has_no_cpu_fallback():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)

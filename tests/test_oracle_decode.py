@@ -69,6 +69,25 @@ def test_refined_keys_pin(pin):
     pin(decode.refined_keys)
 
 
+def _aligned_rows_all(k, w, beta, upto):
+    return decode.aligned_key_rows(k, w, beta, range(upto + 1), upto)
+
+
+@pytest.mark.parametrize("pin", REFINED_PINS, ids=lambda f: f.__name__[4:])
+def test_aligned_key_rows_pin(pin):
+    """The per-row alignment (used to sample full-length caches) meets the
+    same pins as the whole-cache recurrence."""
+    pin(_aligned_rows_all)
+
+
+def test_aligned_key_rows_sample_subset():
+    rng = np.random.default_rng(404)
+    q, k, w, beta = _inputs(rng, 40, 7)
+    rows = [0, 3, 39, 17]
+    np.testing.assert_allclose(decode.aligned_key_rows(k, w, beta, rows, 39),
+                               decode.refined_keys(k, w, beta, 39)[rows], rtol=1e-12, atol=1e-12)
+
+
 def test_gate_prefix():
     rng = np.random.default_rng(403)
     logf = -rng.uniform(0.0, 1.0, size=(2, 3, 9))
