@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu] [--cpu-heads N] [--traffic FILE]
+                    [--no-decode] [--decode-steps N]
 
 One step = one call of path_attn_fwd (gate prefix when present, chunk
 preparation and the streaming scan) over the whole workload, inputs already
@@ -17,7 +18,9 @@ B*H*T^2*(2d + d^2/64) divided by its own average duration, timed with HIP
 events over K launches of path_attn_stream alone on the same stream, against
 the bf16 dense matrix-core peak of 2.5 PFLOP/s.  cpu_baseline times the fp64
 CPU oracle on a bounded sample (N whole heads) with all host threads and
-scales the rate to the full workload.
+scales the rate to the full workload.  The decode object times decoding
+with in-place key refinement after the workload's prompt (prefill alignment of
+a float32 key cache, then decode steps), bound by HBM.
 """
 from __future__ import annotations
 
@@ -43,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bf16_b2h16t16384d64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decoding measurement")
+    ap.add_argument("--decode-steps", type=int, default=20,
+                    help="timed decode steps after the prompt (decoding measurement)")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -89,6 +95,57 @@ def cpu_baseline(wl, inp, n_heads: int):
                       f"({n_heads * wl.T * (wl.T + 1) // 2:.3g} causal pairs) in {dt:.2f} s; "
                       f"rate scaled by {wl.B * wl.H / n_heads:g} to the whole workload",
             "seconds_sample": dt}
+
+
+def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
+    """Decoding with in-place key refinement after the workload's prompt:
+    align the prompt's key cache (float32 cache), then time decode steps at
+    positions T, T+1, ...  Each step reads and writes every cached key and
+    reads every cached value, so it is bound by HBM: algorithmic bytes per
+    step = B*H*t*(2*4*d + e*d) (+ 8 per key for the float64 gate prefix),
+    e = value bytes."""
+    import torch
+    import householder_position_encoding_amd as pa
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    n_steps = max(2, args.decode_steps)
+    T_cap = T + 2 * n_steps + 8
+    cache = pa.DecodeCache(B, H, T_cap, d, q.dtype, kc_dtype=torch.float32, fox=logf is not None)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pre_ws = torch.empty(max(256, pa.load_library().path_attn_prefill_workspace_bytes(B, H, T, d)),
+                         dtype=torch.uint8, device=q.device)
+    torch.cuda.synchronize()
+    a.record(stream)
+    pa.path_attn_prefill_cache(cache, k, v, w, beta, logf, workspace=pre_ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_prefill = a.elapsed_time(b)
+    del pre_ws
+    # decode tokens: the last prompt token's vectors again (any values will do)
+    at = lambda x: None if x is None else x[:, :, T - 1].contiguous()
+    qt, kt, vt, wt, bt, ft = at(q), at(k), at(v), at(w), at(beta), at(logf)
+    out = torch.empty_like(qt)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    for _ in range(2):   # warm-up steps
+        pa.path_attn_decode_step(cache, qt, kt, vt, wt, bt, ft, out=out, lse=lse)
+    torch.cuda.synchronize()
+    t0 = cache.length
+    a.record(stream)
+    for _ in range(n_steps):
+        pa.path_attn_decode_step(cache, qt, kt, vt, wt, bt, ft, out=out, lse=lse)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / n_steps
+    t_mean = t0 + (n_steps - 1) / 2.0
+    e = 2 if wl.dtype == "bf16" else 4
+    per_key = 2 * 4 * d + e * d + (8 if logf is not None else 0)
+    nbytes = B * H * t_mean * per_key
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    return {"context": int(t_mean), "key_cache": "f32", "ms_per_step": ms_step,
+            "tokens_per_s": B / (ms_step * 1e-3), "ms_prefill_align": ms_prefill,
+            "roofline": {"kernel": "decode step (split-key refinement + combine)", "bound": "hbm",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": nbytes}}
 
 
 def main():
@@ -221,6 +278,8 @@ def main():
         ms_copy = timed(lambda: dst.copy_(src), 5)
         res["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
                                    "ms": ms_copy, "gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
+    if not args.no_decode:
+        res["decode"] = bench_decode(wl, q, k, v, w, beta, logf, args, timed)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
   __shared__ float Us[C * CP];
   __shared__ float Xs[C * CP];
   __shared__ float T2s[C * CP];
+  __shared__ float Ks[C * DP];
   __shared__ float bs[C];
   const int N = L / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
@@ -70,7 +71,10 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
   const E *kc = k + row0 * D;
   const E *wc = w + row0 * D;
 
-  for (int idx = tid; idx < C * D; idx += NT) Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
+  for (int idx = tid; idx < C * D; idx += NT) {
+    Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
+    Ks[(idx / D) * DP + idx % D] = to_f(kc[idx]);
+  }
   if (tid < C) bs[tid] = beta[row0 + tid];
   __syncthreads();
   // N[i][j] = beta_i (w_i . w_j), j < i
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
     const int t = idx / C, j = idx % C;
     float acc = 0.f;
     if (t > j)
-      for (int e = 0; e < D; ++e) acc = __builtin_fmaf(Ws[t * DP + e], to_f(kc[(size_t)j * D + e]), acc);
+      for (int e = 0; e < D; ++e) acc = __builtin_fmaf(Ws[t * DP + e], Ks[j * DP + e], acc);
     Xs[t * CP + j] = acc;
   }
   __syncthreads();
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
   float *kb_c = kb + row0 * D;
   for (int idx = tid; idx < C * D; idx += NT) {
     const int j = idx / D, col = idx % D;
-    float acc = to_f(kc[idx]);
+    float acc = Ks[j * DP + col];
     for (int s = j + 1; s < C; ++s) acc = __builtin_fmaf(-T2s[s * CP + j], Ws[s * DP + col], acc);
     kb_c[idx] = acc;
   }
@@ -157,6 +161,7 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
   constexpr int KR = C / RG;      // rows of ->K G per thread
   constexpr int GR = D / RG;      // rows of G per thread
   constexpr int NSL = D / CB;     // column slices per head
+  constexpr int NK4 = C * D / 4 / NT, NM4 = D * D / 4 / NT;   // float4 loads per thread
   __shared__ float Ks[C * DP];
   __shared__ float Ms[D * DP];
   __shared__ float Gs[D * CB];
@@ -165,17 +170,40 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
   const int tid = threadIdx.x, cb = tid % CB, rg = tid / CB;
   const int col = sl * CB + cb;   // column of G (and of the key) this thread owns
 
+  f32x4 kreg[NK4], mreg[NM4];
+  auto fetch = [&](int c) {       // chunk c's ->K and M into registers
+    const f32x4 *kb_c = reinterpret_cast<const f32x4 *>(kb + ((size_t)bh * L + (size_t)c * C) * D);
+    const f32x4 *m_c = reinterpret_cast<const f32x4 *>(m + ((size_t)bh * N + c) * D * D);
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) kreg[i] = kb_c[tid + NT * i];
+#pragma unroll
+    for (int i = 0; i < NM4; ++i) mreg[i] = m_c[tid + NT * i];
+  };
+  auto park = [&]() {             // registers into LDS (padded rows)
+#pragma unroll
+    for (int i = 0; i < NK4; ++i) {
+      const int idx = 4 * (tid + NT * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[((idx + e) / D) * DP + (idx + e) % D] = kreg[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < NM4; ++i) {
+      const int idx = 4 * (tid + NT * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ms[((idx + e) / D) * DP + (idx + e) % D] = mreg[i][e];
+    }
+  };
+
   for (int i = 0; i < GR; ++i) {
     const int a = rg + RG * i;
     Gs[a * CB + cb] = a == col ? 1.f : 0.f;
   }
+  if (N > 0) fetch(N - 1);
   for (int c = N - 1; c >= 0; --c) {
     __syncthreads();   // previous chunk's reads of Ks/Ms/Gs are done
-    const float *kb_c = kb + ((size_t)bh * L + (size_t)c * C) * D;
-    const float *m_c = m + ((size_t)bh * N + c) * D * D;
-    for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = kb_c[idx];
-    for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
+    park();
     __syncthreads();
+    if (c > 0) fetch(c - 1);   // in flight while chunk c is computed
     // aligned rows of chunk c: (->K_c G_c)[j][col]
     float acc[KR];
 #pragma unroll
@@ -426,47 +454,87 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-// One block of D threads per bh: merge the split partials with the new key
+// One block of 256 threads per bh: merge the split partials with the new key
 // k_t (logit scale * q_t . k_t, no gate term), write o_t and lse_t, append
-// k_t, v_t and Lambda_t to the caches.
+// k_t, v_t and Lambda_t to the caches.  The split weights are computed once in
+// LDS; each output element is reduced over the splits by 256/D threads.
 template <typename E, typename KC, int D, bool FOX>
-__global__ __launch_bounds__(128) void decode_combine_kernel(
+__global__ __launch_bounds__(256) void decode_combine_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ logf, KC *__restrict__ kcache, E *__restrict__ vcache,
     double *__restrict__ gcache, const float *__restrict__ part, E *__restrict__ out,
     float *__restrict__ lse, int t, int T_cap, int nsplit, float sl2) {
   constexpr int PF = partial_floats<D>();
-  __shared__ float red[D];
-  const int bh = blockIdx.x, e = threadIdx.x;
-  const float qe = to_f(q[(size_t)bh * D + e]);
-  const float ke = to_f(k[(size_t)bh * D + e]);
-  const float ve = to_f(v[(size_t)bh * D + e]);
-  red[e] = qe * ke;
+  constexpr int NT = 256, SPL = NT / D;   // threads per output element
+  constexpr int MAXS = 1024;              // splits held in LDS per pass
+  __shared__ float red[NT];
+  __shared__ float wsp[MAXS];             // weight of each split, then reused
+  __shared__ float sm[2];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float *ph = part + (size_t)bh * nsplit * PF;
+  // logit of the new key
+  float qk = 0.f;
+  if (tid < D) qk = to_f(q[(size_t)bh * D + tid]) * to_f(k[(size_t)bh * D + tid]);
+  red[tid] = qk;
   __syncthreads();
-  for (int off = D / 2; off >= 1; off /= 2) {
-    if (e < off) red[e] += red[e + off];
+  for (int off = NT / 2; off >= 1; off /= 2) {
+    if (tid < off) red[tid] += red[tid + off];
     __syncthreads();
   }
   const float x_new = red[0] * sl2;
-  float M = x_new;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[((size_t)bh * nsplit + s) * PF]);
-  const float f_new = __builtin_amdgcn_exp2f(x_new - M);
-  float l = f_new, o = f_new * ve;
-  for (int s = 0; s < nsplit; ++s) {
-    const float *p = part + ((size_t)bh * nsplit + s) * PF;
-    if (p[0] > -INFINITY) {
-      const float f = __builtin_amdgcn_exp2f(p[0] - M);
-      l = __builtin_fmaf(f, p[1], l);
-      o = __builtin_fmaf(f, p[2 + e], o);
-    }
+  __syncthreads();
+  // global max over the splits and the new key
+  float mx = x_new;
+  for (int s = tid; s < nsplit; s += NT) mx = fmaxf(mx, ph[(size_t)s * PF]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int off = NT / 2; off >= 1; off /= 2) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
   }
-  out[(size_t)bh * D + e] = from_f<E>(o / l);
-  if (e == 0) lse[bh] = kLn2D * (M + __builtin_amdgcn_logf(l));
-  kcache[((size_t)bh * T_cap + t) * D + e] = from_f<KC>(ke);
-  vcache[((size_t)bh * T_cap + t) * D + e] = v[(size_t)bh * D + e];
-  if (FOX && e == 0)
-    gcache[(size_t)bh * T_cap + t] =
-        t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] + (double)logf[bh] : 0.0;
+  const float M = red[0];
+  __syncthreads();
+  // split weights and the sum l
+  float lp = 0.f;
+  for (int s = tid; s < nsplit; s += NT) {
+    const float ms = ph[(size_t)s * PF];
+    const float f = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+    if (s < MAXS) wsp[s] = f;
+    lp = __builtin_fmaf(f, ph[(size_t)s * PF + 1], lp);
+  }
+  red[tid] = lp;
+  __syncthreads();
+  for (int off = NT / 2; off >= 1; off /= 2) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float f_new = __builtin_amdgcn_exp2f(x_new - M);
+  const float l = red[0] + f_new;
+  if (tid == 0) sm[0] = l;
+  __syncthreads();
+  // o[e] = f_new v_t[e] + sum_s w_s o_s[e]: thread (e, part) sums splits part, part + SPL, ...
+  const int e = tid % D, pr = tid / D;
+  float o = 0.f;
+  for (int s = pr; s < nsplit; s += SPL) {
+    const float f = s < MAXS ? wsp[s] : __builtin_amdgcn_exp2f(ph[(size_t)s * PF] - M);
+    if (f != 0.f) o = __builtin_fmaf(f, ph[(size_t)s * PF + 2 + e], o);
+  }
+  red[tid] = o;
+  __syncthreads();
+  if (tid < D) {
+    float acc = f_new * to_f(v[(size_t)bh * D + tid]);
+#pragma unroll
+    for (int p2 = 0; p2 < SPL; ++p2) acc += red[p2 * D + tid];
+    out[(size_t)bh * D + tid] = from_f<E>(acc / sm[0]);
+    kcache[((size_t)bh * T_cap + t) * D + tid] = from_f<KC>(to_f(k[(size_t)bh * D + tid]));
+    vcache[((size_t)bh * T_cap + t) * D + tid] = v[(size_t)bh * D + tid];
+  }
+  if (tid == 0) {
+    lse[bh] = kLn2D * (M + __builtin_amdgcn_logf(l));
+    if (FOX)
+      gcache[(size_t)bh * T_cap + t] =
+          t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] + (double)logf[bh] : 0.0;
+  }
 }
 
 template <typename E, typename KC, int D>
@@ -499,7 +567,7 @@ hipError_t decode_t(const void *q, const void *k, const void *v, const void *w,
     hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0,
                        stream, (const E *)q, (const E *)w, beta, logf, (KC *)kcache,
                        (const E *)vcache, gcache, part, t, T_cap, nsplit, sl2);
-  hipLaunchKernelGGL((decode_combine_kernel<E, KC, D, FOX>), dim3(BH), dim3(D), 0, stream,
+  hipLaunchKernelGGL((decode_combine_kernel<E, KC, D, FOX>), dim3(BH), dim3(256), 0, stream,
                      (const E *)q, (const E *)k, (const E *)v, logf, (KC *)kcache, (E *)vcache,
                      gcache, part, (E *)out, lse, t, T_cap, nsplit, sl2);
   return hipGetLastError();
