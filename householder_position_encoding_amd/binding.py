@@ -50,6 +50,9 @@ def load_library():
     lib.path_attn_fwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci,
                                   ci, vp, sz, vp]
     lib.path_attn_fwd.restype = ci
+    lib.path_attn_fwd_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci,
+                                     ci, ctypes.c_float, ctypes.c_uint, vp, sz, vp]
+    lib.path_attn_fwd_ex.restype = ci
     lib.path_attn_chunk_prep.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, fp,
                                          fp, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.path_attn_chunk_prep.restype = ci
@@ -58,8 +61,8 @@ def load_library():
     lib.path_attn_prepare.restype = ci
     lib.path_attn_stream.argtypes = [vp, sz, ci, vp, fp, ci, ci, ci, ci, ci, vp]
     lib.path_attn_stream.restype = ci
-    lib.path_attn_stream_ex.argtypes = [vp, sz, ci, ctypes.c_uint, vp, vp, fp, ci, ci,
-                                        ci, ci, ci, vp]
+    lib.path_attn_stream_ex.argtypes = [vp, sz, ci, ctypes.c_float, ctypes.c_uint, vp, vp,
+                                        fp, ci, ci, ci, ci, ci, vp]
     lib.path_attn_stream_ex.restype = ci
     lib.path_attn_prefill_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.path_attn_prefill_workspace_bytes.restype = sz
@@ -69,7 +72,7 @@ def load_library():
     lib.path_attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.path_attn_decode_workspace_bytes.restype = sz
     lib.path_attn_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, vp, ci, vp, fp,
-                                          ci, ci, ci, ci, ci, ci, vp, sz, vp]
+                                          ci, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_decode_step.restype = ci
     lib.path_attn_strerror.argtypes = [ci]
     lib.path_attn_strerror.restype = ctypes.c_char_p
@@ -147,14 +150,15 @@ def _common(q, k, v, w, beta, logf):
 
 
 def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, scale=None, flags=0):
     """PaTH attention forward on the GPU.
 
     q, k, v, w: [B, H, T, d] bf16 or fp32 CUDA tensors (same dtype);
     beta: [B, H, T] fp32; logf: optional [B, H, T] fp32 (PaTH-FoX).
     Returns (out [B, H, T, d] in q's dtype, lse [B, H, T] fp32).  A workspace
     (uint8 CUDA tensor of at least path_attn_workspace_bytes bytes) may be
-    passed to avoid an allocation.
+    passed to avoid an allocation.  scale: softmax scale (None: 1/sqrt(d));
+    flags: 0 or NO_SKIP (path_attn_fwd_ex).
     """
     torch = _torch()
     B, H, T, d, dt = _common(q, k, v, w, beta, logf)
@@ -170,11 +174,12 @@ def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
     need = lib.path_attn_workspace_bytes(B, H, T, d, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.path_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
-                           _ptr(logf), _ptr(out), _ptr(lse), B, H, T, d, dt,
-                           _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    st = lib.path_attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta),
+                              _ptr(logf), _ptr(out), _ptr(lse), B, H, T, d, dt,
+                              0.0 if scale is None else float(scale), int(flags),
+                              _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if st != 0:
-        raise PathAttnError(st, "path_attn_fwd")
+        raise PathAttnError(st, "path_attn_fwd_ex")
     return out, lse
 
 
@@ -199,7 +204,7 @@ NO_SKIP = 1   # PATH_ATTN_NO_SKIP
 
 
 def path_attn_stream(workspace, use_gate, out, lse, stream=None, flags=0,
-                     skipped=None):
+                     skipped=None, scale=None):
     """Second phase of path_attn_fwd: the streaming scan over a workspace
     filled by path_attn_prepare for the same shapes; writes out and lse.
 
@@ -216,7 +221,8 @@ def path_attn_stream(workspace, use_gate, out, lse, stream=None, flags=0,
         _check(skipped, "skipped", (1,), torch.int64, out.device)
     lib = load_library()
     st = lib.path_attn_stream_ex(_ptr(workspace), workspace.numel(), int(bool(use_gate)),
-                                 int(flags), _ptr(skipped), _ptr(out), _ptr(lse),
+                                 0.0 if scale is None else float(scale), int(flags),
+                                 _ptr(skipped), _ptr(out), _ptr(lse),
                                  B, H, T, d, dt, _stream_handle(stream))
     if st != 0:
         raise PathAttnError(st, "path_attn_stream_ex")
@@ -316,7 +322,8 @@ def path_attn_prefill_cache(cache, k, v, w, beta, logf=None, workspace=None, str
     return cache
 
 
-def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None, stream=None):
+def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None, stream=None,
+                          scale=None):
     """One decode step at position cache.length: q, k, v, w [B, H, d];
     beta, logf [B, H].  Returns (out [B, H, d], lse [B, H])."""
     torch = _torch()
@@ -340,6 +347,7 @@ def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None
         _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf), _ptr(cache.kcache),
         _ptr(cache.vcache), _ptr(cache.gcache), cache.length, _ptr(out), _ptr(lse), B, H,
         cache.T_cap, d, _code_of(cache.dtype), _code_of(cache.kc_dtype),
+        0.0 if scale is None else float(scale),
         _ptr(cache.workspace), cache.workspace.numel(), _stream_handle(stream))
     if st != 0:
         raise PathAttnError(st, "path_attn_decode_step")

@@ -13,17 +13,54 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t elem_size(int dtype) { return dtype == PATH_ATTN_BF16 ? 2 : 4; }
 
+// Lengths are padded to whole 64-token chunks (see pad.hip).
+int padded(int T) { return (T + kChunk - 1) / kChunk * kChunk; }
+
 // Shape/dtype checks shared by every entry point.
 int check_shape(int B, int H, int T, int d, int dtype) {
   if (B <= 0 || H <= 0 || T <= 0 || d <= 0) return PATH_ATTN_EINVAL;
   if (dtype != PATH_ATTN_F32 && dtype != PATH_ATTN_BF16) return PATH_ATTN_EINVAL;
   if (d != 64 && d != 128) return PATH_ATTN_EUNSUPPORTED;
-  if (T % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;
-  const unsigned long long elems = (unsigned long long)B * H * T * d;
+  const unsigned long long elems = (unsigned long long)B * H * padded(T) * d;
   if (elems >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
   // grid size of one block per (b, h, chunk) must fit in a 32-bit launch
-  if ((unsigned long long)B * H * (T / kChunk) >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
+  if ((unsigned long long)B * H * (padded(T) / kChunk) >= (1ull << 31)) return PATH_ATTN_EUNSUPPORTED;
   return PATH_ATTN_OK;
+}
+
+// Workspace: the per-chunk layout at the padded length, then, only when T is
+// not a multiple of 64, zero-padded staging copies of the inputs and outputs.
+struct FullLayout {
+  Layout base;
+  bool ragged;
+  size_t q, k, v, w, beta, logf, out, lse, total;
+};
+
+FullLayout full_layout(int B, int H, int T, int d, int dtype) {
+  const int Tp = padded(T);
+  const size_t e = elem_size(dtype);
+  FullLayout F{};
+  F.base = make_layout(B, H, Tp, d, e);
+  F.ragged = Tp != T;
+  size_t off = F.base.total;
+  if (F.ragged) {
+    const size_t rows = (size_t)B * H * Tp;
+    size_t *vecs[] = {&F.q, &F.k, &F.v, &F.w};
+    for (size_t *o : vecs) {
+      *o = off;
+      off = align256(off + rows * d * e);
+    }
+    F.beta = off;
+    off = align256(off + rows * 4);
+    F.logf = off;
+    off = align256(off + rows * 4);
+    F.out = off;
+    off = align256(off + rows * d * e);
+    F.lse = off;
+    off = align256(off + rows * 4);
+  }
+  F.total = off;
+  return F;
 }
 
 int check_inputs(const void *q, const void *k, const void *v, const void *w,
@@ -38,10 +75,14 @@ int check_inputs(const void *q, const void *k, const void *v, const void *w,
     if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
   if (logf && !aligned(logf, 16)) return PATH_ATTN_EINVAL;
   if (!aligned(workspace, 256)) return PATH_ATTN_EINVAL;
-  const Layout L = make_layout(B, H, T, d, elem_size(dtype));
-  if (workspace_bytes < L.total) return PATH_ATTN_EINVAL;
+  if (workspace_bytes < full_layout(B, H, T, d, dtype).total) return PATH_ATTN_EINVAL;
   return PATH_ATTN_OK;
 }
+
+// scale > 0 is used as given, 0 selects 1/sqrt(d); anything else is invalid
+// (the scan takes the block max on the raw scores, which needs scale > 0).
+bool scale_ok(float scale) { return scale == 0.f || (scale > 0.f && scale < INFINITY); }
+float scale_of(float scale, int d) { return scale > 0.f ? scale : 1.f / sqrtf((float)d); }
 
 struct Carved {
   float *qa;
@@ -49,20 +90,25 @@ struct Carved {
   float *al;
   float *gate;
   float2 *bnd;
+  char *base;
+  FullLayout F;
 };
 
 Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
-  const Layout L = make_layout(B, H, T, d, elem_size(dtype));
+  const FullLayout F = full_layout(B, H, T, d, dtype);
   char *base = static_cast<char *>(workspace);
-  return Carved{reinterpret_cast<float *>(base + L.qa), base + L.kvm,
-                reinterpret_cast<float *>(base + L.al),
-                reinterpret_cast<float *>(base + L.gate),
-                reinterpret_cast<float2 *>(base + L.bnd)};
+  return Carved{reinterpret_cast<float *>(base + F.base.qa), base + F.base.kvm,
+                reinterpret_cast<float *>(base + F.base.al),
+                reinterpret_cast<float *>(base + F.base.gate),
+                reinterpret_cast<float2 *>(base + F.base.bnd), base, F};
 }
 
+// The streaming scan at the padded length; for a ragged length into the
+// staging outputs, then the first T rows of each head copied out.
 int run_stream(const Carved &ws, bool gate, unsigned flags,
                unsigned long long *skipped, void *out, float *lse, int BH,
-               int T, int d, int dtype, hipStream_t s) {
+               int T, int d, int dtype, float scale, hipStream_t s) {
+  const int Tp = padded(T);
   StreamArgs a;
   a.qa = ws.qa;
   a.kvm = ws.kvm;
@@ -71,23 +117,52 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
   a.bnd = ws.bnd;
   a.skip = gate && !(flags & PATH_ATTN_NO_SKIP);
   a.skipped = skipped;
-  a.out = out;
-  a.lse = lse;
+  a.out = ws.F.ragged ? static_cast<void *>(ws.base + ws.F.out) : out;
+  a.lse = ws.F.ragged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
   a.BH = BH;
-  a.T = T;
-  return launch_stream(dtype, d, gate, a, s) == hipSuccess ? PATH_ATTN_OK : PATH_ATTN_EHIP;
+  a.T = Tp;
+  a.sl2 = 1.4426950408889634f * scale_of(scale, d);
+  if (launch_stream(dtype, d, gate, a, s) != hipSuccess) return PATH_ATTN_EHIP;
+  if (ws.F.ragged) {
+    const int row = d * (int)elem_size(dtype);
+    if (launch_copy_pad(a.out, out, BH, Tp, T, T, row, s) != hipSuccess ||
+        launch_copy_pad(a.lse, lse, BH, Tp, T, T, 4, s) != hipSuccess)
+      return PATH_ATTN_EHIP;
+  }
+  return PATH_ATTN_OK;
 }
 
-// Enqueue the gate prefix (if any) and the chunk preparation.
+// Enqueue the gate prefix (if any) and the chunk preparation, at the padded
+// length (inputs first copied into the zero-padded staging when ragged).
 int run_prep(const void *q, const void *k, const void *v, const void *w,
              const float *beta, const float *logf, const Carved &ws, int BH,
              int T, int d, int dtype, hipStream_t s) {
-  if (logf && launch_gate_prefix(logf, ws.gate, BH, T, s) != hipSuccess)
+  const int Tp = padded(T);
+  if (ws.F.ragged) {
+    const int row = d * (int)elem_size(dtype);
+    char *b = ws.base;
+    const void *src[] = {q, k, v, w};
+    const size_t dst[] = {ws.F.q, ws.F.k, ws.F.v, ws.F.w};
+    for (int i = 0; i < 4; ++i)
+      if (launch_copy_pad(src[i], b + dst[i], BH, T, Tp, T, row, s) != hipSuccess)
+        return PATH_ATTN_EHIP;
+    if (launch_copy_pad(beta, b + ws.F.beta, BH, T, Tp, T, 4, s) != hipSuccess)
+      return PATH_ATTN_EHIP;
+    if (logf && launch_copy_pad(logf, b + ws.F.logf, BH, T, Tp, T, 4, s) != hipSuccess)
+      return PATH_ATTN_EHIP;
+    q = b + ws.F.q;
+    k = b + ws.F.k;
+    v = b + ws.F.v;
+    w = b + ws.F.w;
+    beta = reinterpret_cast<const float *>(b + ws.F.beta);
+    if (logf) logf = reinterpret_cast<const float *>(b + ws.F.logf);
+  }
+  if (logf && launch_gate_prefix(logf, ws.gate, BH, Tp, s) != hipSuccess)
     return PATH_ATTN_EHIP;
-  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, T, s) !=
+  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, s) !=
       hipSuccess)
     return PATH_ATTN_EHIP;
-  if (logf && launch_chunk_bounds(dtype, d, ws.kvm, ws.gate, ws.bnd, BH, T, s) != hipSuccess)
+  if (logf && launch_chunk_bounds(dtype, d, ws.kvm, ws.gate, ws.bnd, BH, Tp, s) != hipSuccess)
     return PATH_ATTN_EHIP;
   return PATH_ATTN_OK;
 }
@@ -96,7 +171,26 @@ int run_prep(const void *q, const void *k, const void *v, const void *w,
 
 extern "C" size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype) {
   if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
-  return make_layout(B, H, T, d, elem_size(dtype)).total;
+  return full_layout(B, H, T, d, dtype).total;
+}
+
+extern "C" int path_attn_fwd_ex(const void *q, const void *k, const void *v,
+                                const void *w, const float *beta, const float *logf,
+                                void *out, float *lse, int B, int H, int T, int d,
+                                int dtype, float scale, unsigned flags, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  int st = check_inputs(q, k, v, w, beta, logf, workspace, workspace_bytes, B,
+                        H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!out || !lse) return PATH_ATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(lse, 16)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carved ws = carve(workspace, B, H, T, d, dtype);
+  const int BH = B * H;
+  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
+  if (st != PATH_ATTN_OK) return st;
+  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, BH, T, d, dtype, scale, s);
 }
 
 extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
@@ -104,17 +198,8 @@ extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
                              void *out, float *lse, int B, int H, int T, int d,
                              int dtype, void *workspace, size_t workspace_bytes,
                              void *stream) {
-  int st = check_inputs(q, k, v, w, beta, logf, workspace, workspace_bytes, B,
-                        H, T, d, dtype);
-  if (st != PATH_ATTN_OK) return st;
-  if (!out || !lse) return PATH_ATTN_EINVAL;
-  if (!aligned(out, 16) || !aligned(lse, 16)) return PATH_ATTN_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Carved ws = carve(workspace, B, H, T, d, dtype);
-  const int BH = B * H;
-  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
-  if (st != PATH_ATTN_OK) return st;
-  return run_stream(ws, logf != nullptr, 0u, nullptr, out, lse, BH, T, d, dtype, s);
+  return path_attn_fwd_ex(q, k, v, w, beta, logf, out, lse, B, H, T, d, dtype, 0.f, 0u,
+                          workspace, workspace_bytes, stream);
 }
 
 extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
@@ -131,7 +216,7 @@ extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
 }
 
 extern "C" int path_attn_stream_ex(const void *workspace, size_t workspace_bytes,
-                                   int use_gate, unsigned flags,
+                                   int use_gate, float scale, unsigned flags,
                                    unsigned long long *skipped, void *out,
                                    float *lse, int B, int H, int T, int d,
                                    int dtype, void *stream) {
@@ -139,21 +224,21 @@ extern "C" int path_attn_stream_ex(const void *workspace, size_t workspace_bytes
   if (st != PATH_ATTN_OK) return st;
   if (!workspace || !out || !lse) return PATH_ATTN_EINVAL;
   if (use_gate != 0 && use_gate != 1) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
   if (flags & ~(unsigned)PATH_ATTN_NO_SKIP) return PATH_ATTN_EINVAL;
   if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse, 16))
     return PATH_ATTN_EINVAL;
   if (skipped && !aligned(skipped, 8)) return PATH_ATTN_EINVAL;
-  if (workspace_bytes < make_layout(B, H, T, d, elem_size(dtype)).total)
-    return PATH_ATTN_EINVAL;
+  if (workspace_bytes < full_layout(B, H, T, d, dtype).total) return PATH_ATTN_EINVAL;
   const Carved ws = carve(const_cast<void *>(workspace), B, H, T, d, dtype);
-  return run_stream(ws, use_gate == 1, flags, skipped, out, lse, B * H, T, d, dtype,
+  return run_stream(ws, use_gate == 1, flags, skipped, out, lse, B * H, T, d, dtype, scale,
                     static_cast<hipStream_t>(stream));
 }
 
 extern "C" int path_attn_stream(const void *workspace, size_t workspace_bytes,
                                 int use_gate, void *out, float *lse, int B,
                                 int H, int T, int d, int dtype, void *stream) {
-  return path_attn_stream_ex(workspace, workspace_bytes, use_gate, 0u, nullptr,
+  return path_attn_stream_ex(workspace, workspace_bytes, use_gate, 0.f, 0u, nullptr,
                              out, lse, B, H, T, d, dtype, stream);
 }
 
@@ -167,6 +252,7 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
   int st = check_inputs(q, k, v, w, beta, logf, workspace, workspace_bytes, B,
                         H, T, d, dtype);
   if (st != PATH_ATTN_OK) return st;
+  if (T % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;   // whole chunks only
   float *outs[] = {qa, kb, m, al, lam};
   for (float *p : outs)
     if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
@@ -253,9 +339,11 @@ extern "C" int path_attn_decode_step(const void *q, const void *k, const void *v
                                      const float *beta, const float *logf, void *kcache,
                                      void *vcache, double *gcache, int t, void *out, float *lse,
                                      int B, int H, int T_cap, int d, int dtype, int kc_dtype,
-                                     void *workspace, size_t workspace_bytes, void *stream) {
+                                     float scale, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
   int st = check_decode_shape(B, H, T_cap, d, dtype, kc_dtype);
   if (st != PATH_ATTN_OK) return st;
+  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
   if (t < 0 || t >= T_cap) return PATH_ATTN_EINVAL;
   if (!q || !k || !v || !w || !beta || !kcache || !vcache || !out || !lse || !workspace)
     return PATH_ATTN_EINVAL;
@@ -272,6 +360,7 @@ extern "C" int path_attn_decode_step(const void *q, const void *k, const void *v
     return PATH_ATTN_EINVAL;
   return launch_decode_step(dtype, kc_dtype, d, q, k, v, w, beta, logf, kcache, vcache, gcache,
                             out, lse, static_cast<float *>(workspace), B * H, t, T_cap,
+                            1.4426950408889634f * scale_of(scale, d),
                             static_cast<hipStream_t>(stream)) == hipSuccess
              ? PATH_ATTN_OK
              : PATH_ATTN_EHIP;
@@ -282,10 +371,11 @@ extern "C" const char *path_attn_strerror(int status) {
     case PATH_ATTN_OK: return "ok";
     case PATH_ATTN_EINVAL:
       return "invalid argument (null or misaligned pointer, non-positive size, "
-             "unknown dtype, or workspace too small)";
+             "unknown dtype or flag, scale not positive, or workspace too small)";
     case PATH_ATTN_EUNSUPPORTED:
-      return "unsupported shape (d must be 64 or 128, T a multiple of 64, "
-             "B*H*T*d < 2^31)";
+      return "unsupported shape (d must be 64 or 128, B*H*T*d < 2^31 with T "
+             "rounded up to a multiple of 64; prefill lengths and the chunk "
+             "unpack need whole 64-token chunks)";
     case PATH_ATTN_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }

@@ -560,8 +560,7 @@ template <typename E, typename KC, int D, bool FOX>
 hipError_t decode_t(const void *q, const void *k, const void *v, const void *w,
                     const float *beta, const float *logf, void *kcache, void *vcache,
                     double *gcache, void *out, float *lse, float *part, int BH, int t,
-                    int T_cap, hipStream_t stream) {
-  const float sl2 = kLog2eD / sqrtf((float)D);
+                    int T_cap, float sl2, hipStream_t stream) {
   const int nsplit = (t + kKeysPerSplit - 1) / kKeysPerSplit;
   if (nsplit > 0)
     hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0,
@@ -588,19 +587,19 @@ template <typename E, typename KC>
 hipError_t decode_d(int D, const void *q, const void *k, const void *v, const void *w,
                     const float *beta, const float *logf, void *kcache, void *vcache,
                     double *gcache, void *out, float *lse, float *part, int BH, int t,
-                    int T_cap, hipStream_t s) {
+                    int T_cap, float sl2, hipStream_t s) {
   if (D == 64) {
     if (logf)
       return decode_t<E, KC, 64, true>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                       part, BH, t, T_cap, s);
+                                       part, BH, t, T_cap, sl2, s);
     return decode_t<E, KC, 64, false>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                      part, BH, t, T_cap, s);
+                                      part, BH, t, T_cap, sl2, s);
   }
   if (logf)
     return decode_t<E, KC, 128, true>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                      part, BH, t, T_cap, s);
+                                      part, BH, t, T_cap, sl2, s);
   return decode_t<E, KC, 128, false>(q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                     part, BH, t, T_cap, s);
+                                     part, BH, t, T_cap, sl2, s);
 }
 
 }  // namespace
@@ -632,19 +631,19 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
                               const void *v, const void *w, const float *beta,
                               const float *logf, void *kcache, void *vcache, double *gcache,
                               void *out, float *lse, float *part, int BH, int t, int T_cap,
-                              hipStream_t s) {
+                              float sl2, hipStream_t s) {
   if (dtype == 1) {
     if (kc_dtype == 1)
       return decode_d<__bf16, __bf16>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out,
-                                      lse, part, BH, t, T_cap, s);
+                                      lse, part, BH, t, T_cap, sl2, s);
     return decode_d<__bf16, float>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                   part, BH, t, T_cap, s);
+                                   part, BH, t, T_cap, sl2, s);
   }
   if (kc_dtype == 1)
     return decode_d<float, __bf16>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                   part, BH, t, T_cap, s);
+                                   part, BH, t, T_cap, sl2, s);
   return decode_d<float, float>(D, q, k, v, w, beta, logf, kcache, vcache, gcache, out, lse,
-                                part, BH, t, T_cap, s);
+                                part, BH, t, T_cap, sl2, s);
 }
 
 }  // namespace pathattn

@@ -121,6 +121,7 @@ struct StreamArgs {
   void *out;
   float *lse;
   int BH, T;
+  float sl2;   // softmax scale times log2(e)
 };
 hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
                          hipStream_t stream);
@@ -128,6 +129,11 @@ hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,
                          const float *al_ws, const float *gate, float *qa,
                          float *kb, float *m, float *al, float *lam, int BH,
                          int T, hipStream_t stream);
+
+// Row copy with zero fill into / out of padded staging (pad.hip): dst[bh][t]
+// = t < n_copy ? src[bh][t] : 0 for t < dst_rows, rows of row_bytes bytes.
+hipError_t launch_copy_pad(const void *src, void *dst, int BH, int src_rows, int dst_rows,
+                           int n_copy, int row_bytes, hipStream_t stream);
 
 // Decoding with in-place key refinement (decode.hip).
 size_t decode_partial_bytes(int BH, int T_cap, int D);
@@ -139,6 +145,6 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
                               const void *v, const void *w, const float *beta,
                               const float *logf, void *kcache, void *vcache, double *gcache,
                               void *out, float *lse, float *part, int BH, int t, int T_cap,
-                              hipStream_t s);
+                              float sl2, hipStream_t s);
 
 }  // namespace pathattn

@@ -719,7 +719,7 @@ struct Shape<float, 128> { static constexpr int NQC = 2, PD = 0; };
 template <typename E, int D, bool FOX>
 hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int N = a.T / kChunk;
-  const float sl2 = kLog2e / sqrtf((float)D);
+  const float sl2 = a.sl2;
   if constexpr (std::is_same<E, __bf16>::value && D == 64 && PATH_ATTN_WIDE_BF16_64) {
     constexpr int NQC = PATH_ATTN_WIDE_NQC, PD = PATH_ATTN_WIDE_PD;
     const int blocks = a.BH * ((N + NQC - 1) / NQC);

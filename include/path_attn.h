@@ -27,8 +27,16 @@
  *   - dtype: PATH_ATTN_F32 (float32 storage, float32 arithmetic throughout)
  *            or PATH_ATTN_BF16 (bfloat16 storage; products on bf16 matrix
  *            cores with float32 accumulation; chunk preparation in float32).
- *   - Supported shapes: d in {64, 128}; T a positive multiple of 64 (the chunk
- *     length); B, H >= 1; B*H*T*d < 2^31.
+ *   - Supported shapes: d in {64, 128}; T >= 1; B, H >= 1; B*H*Tp*d < 2^31
+ *     with Tp = T rounded up to a multiple of 64 (the chunk length).  A T that
+ *     is not a multiple of 64 is run at Tp with padded tokens whose factor is
+ *     the identity (beta = 0, w = 0) and whose q, k, v and gate are zero; they
+ *     come after every real token, so no real logit changes (they enter no
+ *     path H_{j+1}...H_i with i < T, and the causal mask hides them).  The
+ *     inputs are then copied into zero-padded staging inside the workspace and
+ *     the first T rows of out and lse copied back, which costs extra traffic;
+ *     a multiple of 64 needs no staging.  The authors' reference listing needs
+ *     L % BT == 0; padding with identity factors is this library's reading.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous: they enqueue kernels and return; results are valid once
  *     the caller has synchronised the stream.  The library keeps no pointer
@@ -53,8 +61,10 @@ extern "C" {
 #define PATH_ATTN_OK 0
 #define PATH_ATTN_EINVAL 1      /* null pointer, size <= 0, bad dtype, misaligned
                                    pointer, or workspace too small */
-#define PATH_ATTN_EUNSUPPORTED 2 /* d not in {64, 128}, T % 64 != 0, or the
-                                   problem exceeds 32-bit element indexing */
+#define PATH_ATTN_EUNSUPPORTED 2 /* d not in {64, 128}, the problem exceeds
+                                   32-bit element indexing, or a prefill
+                                   length / chunk unpack that is not a
+                                   multiple of 64 */
 #define PATH_ATTN_EHIP 3        /* a HIP launch reported an error */
 
 /* Storage dtypes of q, k, v, w and out. */
@@ -72,7 +82,8 @@ extern "C" {
  * queries (float32), the transformed keys, the values and the chunk transform
  * in the matrix-core operand order, the diagonal-block logits (float32) and
  * two float32 bounds used with the forget gate; per token, the forget-gate
- * prefix (float32).
+ * prefix (float32).  When T is not a multiple of 64, it also holds the
+ * zero-padded staging copies of q, k, v, w, beta, logf, out and lse.
  */
 size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype);
 
@@ -95,6 +106,20 @@ int path_attn_fwd(const void *q, const void *k, const void *v, const void *w,
                   const float *beta, const float *logf, void *out, float *lse,
                   int B, int H, int T, int d, int dtype, void *workspace,
                   size_t workspace_bytes, void *stream);
+
+/*
+ * path_attn_fwd with a softmax scale and flags.  scale > 0 multiplies the
+ * path logits c_ij in place of 1/sqrt(d) (the authors' listing passes
+ * `scale` as an argument); scale = 0 selects 1/sqrt(d).  A negative,
+ * infinite or NaN scale is EINVAL (the scan takes each block's maximum on the
+ * raw scores, which needs scale > 0).  flags: 0 or PATH_ATTN_NO_SKIP.
+ * path_attn_fwd(...) == path_attn_fwd_ex(..., 0.0f, 0, ...).
+ */
+int path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w,
+                     const float *beta, const float *logf, void *out, float *lse,
+                     int B, int H, int T, int d, int dtype, float scale,
+                     unsigned flags, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /*
  * The two phases of path_attn_fwd, for callers that time or schedule them
@@ -130,12 +155,13 @@ int path_attn_stream(const void *workspace, size_t workspace_bytes,
  * skipped: NULL, or a device counter (8-byte aligned) to which the scan adds
  *          the number of steps it skipped, one per wave and key block (a
  *          wave covers 32 queries, 64 for bf16 d = 64); the caller zeroes it.
+ * scale:   as for path_attn_fwd_ex (0 selects 1/sqrt(d)).
  * Other arguments and errors as path_attn_stream; unknown flag bits give
- * PATH_ATTN_EINVAL.  path_attn_stream(...) == path_attn_stream_ex(..., 0,
- * NULL, ...), and path_attn_fwd uses the skip.
+ * PATH_ATTN_EINVAL.  path_attn_stream(...) == path_attn_stream_ex(..., 0.0f,
+ * 0, NULL, ...), and path_attn_fwd uses the skip.
  */
 int path_attn_stream_ex(const void *workspace, size_t workspace_bytes,
-                        int use_gate, unsigned flags,
+                        int use_gate, float scale, unsigned flags,
                         unsigned long long *skipped, void *out, float *lse,
                         int B, int H, int T, int d, int dtype, void *stream);
 
@@ -155,7 +181,8 @@ int path_attn_stream_ex(const void *workspace, size_t workspace_bytes,
  *                          f_0 never enters a logit and is left out)
  * kb and m are reported at the precision the streaming kernel consumes them
  * (bf16-rounded for PATH_ATTN_BF16).  Any of qa/kb/m/al/lam may be NULL.
- * Uses the same workspace as path_attn_fwd.
+ * Uses the same workspace as path_attn_fwd.  T must be a multiple of 64
+ * (PATH_ATTN_EUNSUPPORTED otherwise).
  */
 int path_attn_chunk_prep(const void *q, const void *k, const void *v,
                          const void *w, const float *beta, const float *logf,
@@ -222,8 +249,8 @@ size_t path_attn_decode_workspace_bytes(int B, int H, int T_cap, int d);
  * log f_t, Lambda_0 = 0) at position t, and writes
  *     out[b,h,:] = sum_{j<=t} softmax_j(s_tj) v_j        (dtype, RNE)
  *     lse[b,h]   = ln sum_{j<=t} exp(s_tj)                (float32)
- * with s_tj = (k_j . q_t) / sqrt(d) + Lambda_t - Lambda_j (gate term only
- * with logf).  q, k, v, w, out: [B, H, d] of dtype; beta, logf, lse: [B, H]
+ * with s_tj = scale * (k_j . q_t) + Lambda_t - Lambda_j (gate term only
+ * with logf; scale as for path_attn_fwd_ex, 0 selects 1/sqrt(d)).  q, k, v, w, out: [B, H, d] of dtype; beta, logf, lse: [B, H]
  * float32.  Keys are split over blocks (512 per block) and the partial
  * softmax states merged in a second kernel.  Alignment: q, k, v, w, out and
  * the caches 16 bytes; beta, logf and lse 4 bytes (one value per head).
@@ -233,7 +260,7 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
                           const void *w, const float *beta, const float *logf,
                           void *kcache, void *vcache, double *gcache, int t,
                           void *out, float *lse, int B, int H, int T_cap, int d,
-                          int dtype, int kc_dtype, void *workspace,
+                          int dtype, int kc_dtype, float scale, void *workspace,
                           size_t workspace_bytes, void *stream);
 
 /* Static, human-readable description of a status code. */

@@ -56,10 +56,28 @@ def test_workspace_bytes(dtype, esize, B, H, T, d):
 
 
 @pytest.mark.parametrize("args", [(0, 1, 64, 64, 1), (1, 0, 64, 64, 1), (1, 1, 0, 64, 1),
-                                  (1, 1, 64, 96, 1), (1, 1, 100, 64, 1), (1, 1, 64, 64, 7),
+                                  (1, 1, 64, 96, 1), (1, 1, 64, 64, 7),
                                   (1, 1, 64, -64, 0), (1 << 16, 1 << 10, 1024, 64, 1)])
 def test_workspace_bytes_rejects(args):
     assert pa.path_attn_workspace_bytes(*args) == 0
+
+
+@pytest.mark.parametrize("dtype,esize", [(pa.F32, 4), (pa.BF16, 2)])
+@pytest.mark.parametrize("T", [1, 63, 65, 100, 16383])
+def test_workspace_bytes_ragged(dtype, esize, T):
+    # a length that is not a multiple of 64 runs at the padded length, plus
+    # zero-padded staging of q, k, v, w, out (d * esize per token) and beta,
+    # logf, lse (4 bytes per token each)
+    B, H, d = 2, 3, 64
+    Tp = (T + 63) // 64 * 64
+    base = pa.path_attn_workspace_bytes(B, H, Tp, d, dtype)
+    n = pa.path_attn_workspace_bytes(B, H, T, d, dtype)
+    if T == Tp:
+        assert n == base
+    else:
+        rows = B * H * Tp
+        expect = base + 5 * rows * d * esize + 3 * rows * 4
+        assert expect <= n <= expect + 8 * 256
 
 
 def _fwd(lib, **kw):
@@ -80,8 +98,9 @@ BAD_FWD = [
     (dict(logf=FAKE + 4), EINVAL), (dict(ws=FAKE + 16), EINVAL),
     (dict(wsb=1000), EINVAL), (dict(dtype=5), EINVAL), (dict(B=0), EINVAL),
     (dict(H=-1), EINVAL), (dict(T=0), EINVAL),
-    (dict(d=96), EUNSUP), (dict(d=32), EUNSUP), (dict(T=200), EUNSUP),
+    (dict(d=96), EUNSUP), (dict(d=32), EUNSUP),
     (dict(B=1 << 12, H=1 << 10, T=1024), EUNSUP),
+    (dict(T=200, wsb=1000), EINVAL),   # a ragged length still needs its staging
 ]
 
 
@@ -90,13 +109,23 @@ def test_fwd_validation(kw, status):
     assert _fwd(pa.load_library(), **kw) == status
 
 
+@pytest.mark.parametrize("scale,flags,status", [
+    (-1.0, 0, EINVAL), (float("inf"), 0, EINVAL), (float("nan"), 0, EINVAL),
+    (0.5, 2, EINVAL), (0.5, 0xFFFF, EINVAL)])
+def test_fwd_ex_validation(scale, flags, status):
+    # every case is invalid, so nothing is launched on the fake addresses
+    lib = pa.load_library()
+    assert lib.path_attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 256, 64,
+                                pa.BF16, scale, flags, FAKE, 1 << 40, None) == status
+
+
 def test_prepare_and_stream_validation():
     lib = pa.load_library()
     assert lib.path_attn_prepare(FAKE, FAKE, FAKE, None, FAKE, None, 1, 1, 64, 64, 1, FAKE,
                                  1 << 40, None) == EINVAL
     assert lib.path_attn_prepare(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 1, FAKE,
                                  10, None) == EINVAL
-    assert lib.path_attn_prepare(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 96, 64, 1, FAKE,
+    assert lib.path_attn_prepare(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 96, 96, 1, FAKE,
                                  1 << 40, None) == EUNSUP
     # stream: bad use_gate, null out, misaligned lse, small workspace, bad d
     assert lib.path_attn_stream(FAKE, 1 << 40, 2, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
@@ -106,11 +135,12 @@ def test_prepare_and_stream_validation():
     assert lib.path_attn_stream(FAKE, 1 << 40, 0, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
     # stream_ex: unknown flag bits, misaligned counter, plus the stream checks
     ex = lib.path_attn_stream_ex
-    assert ex(FAKE, 1 << 40, 1, 2, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
-    assert ex(FAKE, 1 << 40, 1, 1, FAKE + 4, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
-    assert ex(FAKE, 1 << 40, 2, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
-    assert ex(FAKE, 100, 1, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
-    assert ex(FAKE, 1 << 40, 1, 1, None, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
+    assert ex(FAKE, 1 << 40, 1, 0.0, 2, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 1, 0.0, 1, FAKE + 4, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 2, 0.0, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 100, 1, 0.0, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
+    assert ex(FAKE, 1 << 40, 1, 0.0, 1, None, FAKE, FAKE, 1, 1, 64, 48, 1, None) == EUNSUP
+    assert ex(FAKE, 1 << 40, 1, -2.0, 0, None, FAKE, FAKE, 1, 1, 64, 64, 1, None) == EINVAL
 
 
 def test_chunk_prep_validation():
@@ -123,6 +153,8 @@ def test_chunk_prep_validation():
     assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 64, 64, 1, FAKE, 10, None) == EINVAL
     # unsupported head dim
     assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 64, 80, 1, FAKE, 1 << 40, None) == EUNSUP
+    # the unpack needs whole chunks
+    assert lib.path_attn_chunk_prep(*common, *outs, 1, 1, 100, 64, 1, FAKE, 1 << 40, None) == EUNSUP
 
 
 # ---- decoding entry points
@@ -177,12 +209,12 @@ def test_prefill_empty_prompt_launches_nothing():
 def _decode(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, kc=FAKE, vc=FAKE, gc=None,
              t=5, out=FAKE, lse=FAKE, B=1, H=2, T_cap=256, d=64, dtype=pa.BF16,
-             kc_dtype=pa.F32, ws=FAKE, wsb=1 << 40, stream=None)
+             kc_dtype=pa.F32, scale=0.0, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.path_attn_decode_step(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"],
                                      a["kc"], a["vc"], a["gc"], a["t"], a["out"], a["lse"],
                                      a["B"], a["H"], a["T_cap"], a["d"], a["dtype"],
-                                     a["kc_dtype"], a["ws"], a["wsb"], a["stream"])
+                                     a["kc_dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
 
 
 BAD_DECODE = [
@@ -193,6 +225,7 @@ BAD_DECODE = [
     (dict(ws=FAKE + 64), EINVAL), (dict(wsb=8), EINVAL),
     (dict(t=-1), EINVAL), (dict(t=256), EINVAL), (dict(kc_dtype=-1), EINVAL),
     (dict(d=32), EUNSUP), (dict(B=1 << 12, H=1 << 9, T_cap=1 << 14), EUNSUP),
+    (dict(scale=-1.0), EINVAL),
 ]
 
 

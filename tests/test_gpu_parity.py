@@ -244,11 +244,15 @@ def test_binding_rejects_bad_tensors():
         pa.path_attn_fwd(dev["q"][..., :32], dev["k"], dev["v"], dev["w"], dev["beta"])
     with pytest.raises(TypeError):
         pa.path_attn_fwd(dev["q"].half(), dev["k"], dev["v"], dev["w"], dev["beta"])
-    # T not a multiple of 64 is reported by the library as unsupported
-    t = lambda x: x[:, :, :100].contiguous()
+    # a head dimension other than 64 or 128 is reported by the library as unsupported
+    x96 = torch.zeros((1, 1, 128, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pa.PathAttnError) as e:
-        pa.path_attn_fwd(t(dev["q"]), t(dev["k"]), t(dev["v"]), t(dev["w"]), t(dev["beta"]))
+        pa.path_attn_fwd(x96, x96, x96, x96, dev["beta"])
     assert e.value.status == 2
+    # a scale that is not positive is invalid
+    with pytest.raises(pa.PathAttnError) as e:
+        pa.path_attn_fwd(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], scale=-0.5)
+    assert e.value.status == 1
     torch.cuda.synchronize()
 
 

@@ -354,3 +354,22 @@ ALL_PINS = [
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__[4:])
 def test_oracle_pin(pin):
     pin(oracle.load())
+
+
+def test_partial_path_splits_into_path_and_plain_dot():
+    """Partial PaTH (the position transform acting on a subspace): with
+    w_t zero on the last coordinates, every H_t is the identity there, so the
+    path logit is the PaTH logit of the leading coordinates plus the ordinary
+    dot product of the trailing ones."""
+    rng = np.random.default_rng(501)
+    T, dp, dn = 23, 4, 3
+    q, k = rng.standard_normal((T, dp + dn)), rng.standard_normal((T, dp + dn))
+    w = np.zeros((T, dp + dn))
+    w[:, :dp] = rng.standard_normal((T, dp))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    beta = rng.uniform(0.0, 2.0, size=T)
+    S = oracle.path_logits(q, k, w, beta)
+    S_p = oracle.path_logits(q[:, :dp], k[:, :dp], w[:, :dp], beta)
+    plain = q[:, dp:] @ k[:, dp:].T
+    low = np.tril(np.ones((T, T), dtype=bool))
+    np.testing.assert_allclose(S[low], (S_p + plain)[low], rtol=1e-12, atol=1e-12)
