@@ -48,45 +48,75 @@ __device__ __forceinline__ E from_f(float x) { return (E)x; }   // RNE for bf16
 
 // ------------------------------------------------------------ prefill: chunks
 
+// acc[r][s] += sum_k A(r0 + 16 r, k) B(k, c0 + 16 s) over k < K for one
+// thread's 4 x 4 tile of a 64 x 64 output block, operands in LDS with
+// arbitrary row / column strides (so transposed reads need no copy).  Rows of
+// the tile are 16 apart and columns 16 apart: a wave's lanes read 4 distinct
+// A addresses and 16 consecutive B addresses per instruction.
+template <int K>
+__device__ __forceinline__ void tile_mm(float (&acc)[4][4], const float *A, int a_rs, int a_cs,
+                                        const float *B, int b_rs, int b_cs, int r0, int c0) {
+  for (int kk = 0; kk < K; ++kk) {
+    float a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = A[(r0 + 16 * r) * a_rs + kk * a_cs];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] = B[kk * b_rs + (c0 + 16 * c) * b_cs];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
+  }
+}
+
+__device__ __forceinline__ void tile_zero(float (&acc)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+}
+
 // One block of 256 threads per (bh, chunk): ->K_c and M_c in float32, natural
 // layouts kb[bh][L][D] and m[bh][N][D][D] (M[a][b]).
 // U = (I + strictLower(D W W^T))^{-1} D by forward substitution,
 // T2 = U strictLower(W K^T), ->K = K - T2^T W, M = W^T (U W).
+// Every product is a dense 64-wide product of LDS operands (U, the strict
+// lower W K^T and T2 hold zeros outside their triangles), each thread
+// computing 4 x 4 tiles in registers.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void align_prep_kernel(
     const E *__restrict__ k, const E *__restrict__ w, const float *__restrict__ beta,
     float *__restrict__ kb, float *__restrict__ m, int L) {
   constexpr int C = kChunk, DP = D + 1, CP = C + 1, NT = 256;
+  // LDS: W; U W, later K; N, then U, then T2; X, then strictLower(W K^T)
   __shared__ float Ws[C * DP];
   __shared__ float UWs[C * DP];
   __shared__ float Us[C * CP];
   __shared__ float Xs[C * CP];
-  __shared__ float T2s[C * CP];
-  __shared__ float Ks[C * DP];
   __shared__ float bs[C];
+  float *Ks = UWs;
+  float *T2s = Us;
   const int N = L / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
   const size_t row0 = (size_t)bh * L + (size_t)c * C;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
   const E *kc = k + row0 * D;
   const E *wc = w + row0 * D;
+  float acc[4][4];
 
-  for (int idx = tid; idx < C * D; idx += NT) {
-    Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
-    Ks[(idx / D) * DP + idx % D] = to_f(kc[idx]);
-  }
+  for (int idx = tid; idx < C * D; idx += NT) Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
   if (tid < C) bs[tid] = beta[row0 + tid];
   __syncthreads();
-  // N[i][j] = beta_i (w_i . w_j), j < i
-  for (int idx = tid; idx < C * C; idx += NT) {
-    const int i = idx / C, j = idx % C;
-    float s = 0.f;
-    if (j < i) {
-      for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ws[i * DP + e], Ws[j * DP + e], s);
-      s *= bs[i];
+  // N[i][j] = beta_i (w_i . w_j) for j < i (into Us)
+  tile_zero(acc);
+  tile_mm<D>(acc, Ws, DP, 1, Ws, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = r0 + 16 * r, j = c0 + 16 * q;
+      Us[i * CP + j] = j < i ? acc[r][q] * bs[i] : 0.f;
     }
-    Us[i * CP + j] = s;
-  }
   __syncthreads();
   // X = (I + N)^{-1} below the diagonal, one column per lane of wave 0:
   // X[i][j] = -N[i][j] - sum_{j<t<i} N[i][t] X[t][j]
@@ -99,56 +129,80 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
     }
   }
   __syncthreads();
-  // U = X D (unit diagonal of X times beta)
+  // U = X D (unit diagonal of X times beta), zero above the diagonal
   for (int idx = tid; idx < C * C; idx += NT) {
     const int i = idx / C, j = idx % C;
     Us[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);
   }
   __syncthreads();
-  // UW = U W;  SK[t][j] = w_t . k_j for t > j (into Xs)
-  for (int idx = tid; idx < C * D; idx += NT) {
-    const int s = idx / D, col = idx % D;
-    float acc = 0.f;
-    for (int t = 0; t <= s; ++t) acc = __builtin_fmaf(Us[s * CP + t], Ws[t * DP + col], acc);
-    UWs[s * DP + col] = acc;
-  }
-  for (int idx = tid; idx < C * C; idx += NT) {
-    const int t = idx / C, j = idx % C;
-    float acc = 0.f;
-    if (t > j)
-      for (int e = 0; e < D; ++e) acc = __builtin_fmaf(Ws[t * DP + e], Ks[j * DP + e], acc);
-    Xs[t * CP + j] = acc;
+  // UW = U W (64 x D)
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    tile_zero(acc);
+    tile_mm<C>(acc, Us, CP, 1, Ws + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) UWs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * q] = acc[r][q];
   }
   __syncthreads();
-  // T2[s][j] = sum_{j<t<=s} U[s][t] SK[t][j]
-  for (int idx = tid; idx < C * C; idx += NT) {
-    const int s = idx / C, j = idx % C;
-    float acc = 0.f;
-    for (int t = j + 1; t <= s; ++t) acc = __builtin_fmaf(Us[s * CP + t], Xs[t * CP + j], acc);
-    T2s[s * CP + j] = acc;
-  }
-  __syncthreads();
-  // ->K[j][col] = K[j][col] - sum_{s>j} T2[s][j] W[s][col]
-  float *kb_c = kb + row0 * D;
-  for (int idx = tid; idx < C * D; idx += NT) {
-    const int j = idx / D, col = idx % D;
-    float acc = Ks[j * DP + col];
-    for (int s = j + 1; s < C; ++s) acc = __builtin_fmaf(-T2s[s * CP + j], Ws[s * DP + col], acc);
-    kb_c[idx] = acc;
-  }
   // M[a][b] = sum_s W[s][a] UW[s][b]
   float *m_c = m + ((size_t)bh * N + c) * D * D;
-  for (int idx = tid; idx < D * D; idx += NT) {
-    const int a = idx / D, b = idx % D;
-    float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc = __builtin_fmaf(Ws[s * DP + a], UWs[s * DP + b], acc);
-    m_c[idx] = acc;
+#pragma unroll
+  for (int ha = 0; ha < D / 64; ++ha)
+#pragma unroll
+    for (int hb = 0; hb < D / 64; ++hb) {
+      tile_zero(acc);
+      tile_mm<C>(acc, Ws + 64 * ha, 1, DP, UWs + 64 * hb, DP, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          m_c[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * q] = acc[r][q];
+    }
+  __syncthreads();   // U W is no longer read: its buffer takes K
+  for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = to_f(kc[idx]);
+  __syncthreads();
+  // SK[t][j] = w_t . k_j for t > j, else 0 (into Xs)
+  tile_zero(acc);
+  tile_mm<D>(acc, Ws, DP, 1, Ks, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = r0 + 16 * r, j = c0 + 16 * q;
+      Xs[t * CP + j] = t > j ? acc[r][q] : 0.f;
+    }
+  __syncthreads();
+  // T2 = U SK (both triangular, dense product), written over U once every
+  // thread has read it
+  tile_zero(acc);
+  tile_mm<C>(acc, Us, CP, 1, Xs, CP, 1, r0, c0);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T2s[(r0 + 16 * r) * CP + c0 + 16 * q] = acc[r][q];
+  __syncthreads();
+  // ->K[j][col] = K[j][col] - sum_s T2[s][j] W[s][col]  (T2[s][j] = 0 for s <= j)
+  float *kb_c = kb + row0 * D;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    tile_zero(acc);
+    tile_mm<C>(acc, T2s, 1, CP, Ws + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = r0 + 16 * r, col = 64 * h + c0 + 16 * q;
+        kb_c[(size_t)j * D + col] = Ks[j * DP + col] - acc[r][q];
+      }
   }
 }
 
 // ------------------------------------------------------------ prefill: scan
 
-// One block per (bh, slice of CB columns of G).  Thread (rg, cb) = (tid / CB,
+// One block per (bh, slice of CB = D/8 columns of G).  Thread (rg, cb) = (tid / CB,
 // tid % CB) owns column cb of the slice, rows rg + RG*i.  Chunk by chunk from
 // the last: stage ->K_c and M_c in LDS, write the aligned rows ->K_c G_c of
 // this column slice, then G <- G - M_c^T G.
@@ -156,7 +210,7 @@ template <typename KC, int D>
 __global__ __launch_bounds__(256) void align_scan_kernel(
     const float *__restrict__ kb, const float *__restrict__ m, KC *__restrict__ kcache,
     int L, int T_cap) {
-  constexpr int C = kChunk, NT = 256, CB = 16, RG = NT / CB;
+  constexpr int C = kChunk, NT = 256, CB = D / 8, RG = NT / CB;   // 8 column slices per head
   constexpr int DP = D + 1;
   constexpr int KR = C / RG;      // rows of ->K G per thread
   constexpr int GR = D / RG;      // rows of G per thread
@@ -545,7 +599,7 @@ hipError_t prefill_t(const void *k, const void *v, const void *w, const float *b
   if (N > 0) {
     hipLaunchKernelGGL((align_prep_kernel<E, D>), dim3(BH * N), dim3(256), 0, stream,
                        (const E *)k, (const E *)w, beta, ws_kb, ws_m, L);
-    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 16)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * 8), dim3(256), 0, stream,
                        ws_kb, ws_m, (KC *)kcache, L, T_cap);
     const int gx = min(1024, (int)(((size_t)L * D + 255) / 256));
     hipLaunchKernelGGL((copy_rows_kernel<E>), dim3(gx, BH), dim3(256), 0, stream, (const E *)v,
