@@ -1,0 +1,114 @@
+"""Pins of the fp64 gradient oracle (oracle/backward.py) against what does not
+depend on it: the C oracle's forward pass (an independent walk), central
+finite differences of that forward pass, and the textbook gradients of
+softmax attention at beta = 0 (PaTH slides, frame "PaTH inserts a learned
+transformation along every path": with beta = 0 every H_t is the identity)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as ob
+
+
+def _inputs(rng, T, d, fox):
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    w = rng.standard_normal((T, d))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    beta = rng.uniform(0.05, 1.95, size=T)
+    logf = np.log(rng.uniform(0.5, 1.0, size=T)) if fox else None
+    return dict(q=q, k=k, v=v, w=w, beta=beta, logf=logf)
+
+
+def _loss_c(x, do, dlse):
+    o, lse = oracle.path_attn(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"])
+    return float(np.sum(o * do) + np.sum(lse * dlse))
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_forward_equals_c_oracle(fox):
+    import torch
+    rng = np.random.default_rng(600 + fox)
+    x = _inputs(rng, 21, 5, fox)
+    t = lambda a: None if a is None else torch.tensor(a)
+    o, lse = ob.forward(t(x["q"]), t(x["k"]), t(x["v"]), t(x["w"]), t(x["beta"]), t(x["logf"]))
+    o_c, l_c = oracle.path_attn(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"])
+    np.testing.assert_allclose(o.numpy(), o_c, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse.numpy(), l_c, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fox", [False, True])
+def test_gradients_match_finite_differences(fox):
+    rng = np.random.default_rng(610 + fox)
+    T, d = 17, 4
+    x = _inputs(rng, T, d, fox)
+    do, dlse = rng.standard_normal((T, d)), rng.standard_normal(T)
+    g = ob.gradients(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do, dlse)
+    eps = 1e-6
+    names = ["q", "k", "v", "w", "beta"] + (["logf"] if fox else [])
+    for name in names:
+        for _ in range(3):
+            delta = rng.standard_normal(np.shape(x[name]))
+            xp = dict(x); xp[name] = x[name] + eps * delta
+            xm = dict(x); xm[name] = x[name] - eps * delta
+            fd = (_loss_c(xp, do, dlse) - _loss_c(xm, do, dlse)) / (2 * eps)
+            an = float(np.sum(g["d" + name] * delta))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (name, fd, an)
+
+
+def test_beta0_textbook_gradients():
+    rng = np.random.default_rng(620)
+    T, d = 19, 6
+    x = _inputs(rng, T, d, False)
+    x["beta"] = np.zeros(T)
+    do, dlse = rng.standard_normal((T, d)), rng.standard_normal(T)
+    g = ob.gradients(x["q"], x["k"], x["v"], x["w"], x["beta"], None, do, dlse)
+    scale = 1.0 / np.sqrt(d)
+    s = scale * x["q"] @ x["k"].T
+    s[np.triu_indices(T, 1)] = -np.inf
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    o = p @ x["v"]
+    dp = do @ x["v"].T
+    ds = p * (dp - np.sum(do * o, 1, keepdims=True)) + p * dlse[:, None]
+    np.testing.assert_allclose(g["dv"], p.T @ do, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dq"], scale * ds @ x["k"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], scale * ds.T @ x["q"], rtol=1e-10, atol=1e-12)
+    assert np.all(g["dw"] == 0.0)
+
+
+def test_first_token_factors_get_zero_gradient():
+    """H_0 and f_0 enter no logit, so their gradients are exactly zero."""
+    rng = np.random.default_rng(630)
+    x = _inputs(rng, 9, 3, True)
+    do = rng.standard_normal((9, 3))
+    g = ob.gradients(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do)
+    assert np.all(g["dw"][0] == 0.0) and g["dbeta"][0] == 0.0 and g["dlogf"][0] == 0.0
+
+
+def test_pins_catch_reversed_product(monkeypatch):
+    """A planted mistake in a copy of the oracle (the factors applied in the
+    reverse order, H_i first for key j) must fail the finite-difference pin."""
+    import torch
+
+    def reversed_logits(q, k, w, beta):
+        T = q.shape[0]
+        c = torch.full((T, T), -torch.inf, dtype=q.dtype)
+        out = []
+        for i in range(T):
+            row = []
+            for j in range(T):
+                if j > i:
+                    row.append(torch.tensor(-torch.inf, dtype=q.dtype))
+                    continue
+                z = q[i]
+                for t in range(j + 1, i + 1):      # H_{j+1} first: wrong order
+                    z = z - beta[t] * (z @ w[t]) * w[t]
+                row.append(z @ k[j])
+            out.append(torch.stack(row))
+        return torch.stack(out)
+
+    monkeypatch.setattr(ob, "_logits", reversed_logits)
+    with pytest.raises(AssertionError):
+        test_gradients_match_finite_differences(False)
