@@ -112,3 +112,20 @@ def test_pins_catch_reversed_product(monkeypatch):
     monkeypatch.setattr(ob, "_logits", reversed_logits)
     with pytest.raises(AssertionError):
         test_gradients_match_finite_differences(False)
+
+
+@pytest.mark.parametrize("C,n,d,fox", [(4, 4, 5, False), (4, 5, 3, True), (8, 3, 6, True), (1, 6, 3, False)])
+def test_blockwise_backward_equals_autograd(C, n, d, fox):
+    """The blockwise backward (oracle/chunked_backward.py: key levels, the
+    downward sweep of the key-gradient accumulator, per-chunk adjoint of the
+    UT formulas) gives the gradients of the definition."""
+    from oracle import chunked_backward as cb
+    rng = np.random.default_rng(640 + C + n)
+    T = C * n
+    x = _inputs(rng, T, d, fox)
+    do, dlse = rng.standard_normal((T, d)), rng.standard_normal(T)
+    ref = ob.gradients(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do, dlse)
+    got = cb.sweep_backward(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do,
+                            ref["o"], ref["lse"], dlse=dlse, C=C)
+    for name in ("dq", "dk", "dv", "dw", "dbeta") + (("dlogf",) if fox else ()):
+        np.testing.assert_allclose(got[name], ref[name], rtol=1e-9, atol=1e-10, err_msg=name)
