@@ -74,6 +74,11 @@ def load_library():
     lib.path_attn_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, vp, ci, vp, fp,
                                           ci, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_decode_step.restype = ci
+    lib.path_attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.path_attn_bwd_workspace_bytes.restype = sz
+    lib.path_attn_bwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
+                                  fp, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
+    lib.path_attn_bwd.restype = ci
     lib.path_attn_strerror.argtypes = [ci]
     lib.path_attn_strerror.restype = ctypes.c_char_p
     lib.path_attn_version.argtypes = []
@@ -353,3 +358,38 @@ def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None
         raise PathAttnError(st, "path_attn_decode_step")
     cache.length += 1
     return out, lse
+
+
+# ---------------------------------------------------------------- backward
+
+def path_attn_bwd_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) -> int:
+    return int(load_library().path_attn_bwd_workspace_bytes(B, H, T, d, dtype))
+
+
+def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
+                  workspace=None, stream=None):
+    """Gradients of <dout, out> + <dlse, lse> for the forward of path_attn_fwd
+    (out, lse: that forward's outputs).  Returns (dq, dk, dv, dw, dbeta,
+    dlogf); dlogf is None without the gate.  T must be a multiple of 64."""
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    _check(out, "out", q.shape, q.dtype, q.device)
+    _check(dout, "dout", q.shape, q.dtype, q.device)
+    _check(lse, "lse", (B, H, T), torch.float32, q.device)
+    if dlse is not None:
+        _check(dlse, "dlse", (B, H, T), torch.float32, q.device)
+    lib = load_library()
+    dq, dk, dv, dw = (torch.empty_like(q) for _ in range(4))
+    dbeta = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    dlogf = None if logf is None else torch.empty_like(dbeta)
+    need = lib.path_attn_bwd_workspace_bytes(B, H, T, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.path_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk),
+                           _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), B, H, T, d, dt,
+                           0.0 if scale is None else float(scale), _ptr(workspace),
+                           workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_bwd")
+    return dq, dk, dv, dw, dbeta, dlogf

@@ -267,6 +267,58 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
   return PATH_ATTN_OK;
 }
 
+// ---------------------------------------------------------------- backward
+
+extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK || T % kChunk != 0) return 0;
+  return bwd_layout(B, H, T, d).total;
+}
+
+extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
+                             const float *beta, const float *logf, const void *out,
+                             const float *lse, const void *dout, const float *dlse, void *dq,
+                             void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
+                             int H, int T, int d, int dtype, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  const int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (T % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;   // whole chunks only
+  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
+  const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace};
+  for (const void *p : need)
+    if (!p) return PATH_ATTN_EINVAL;
+  if (logf && !dlogf) return PATH_ATTN_EINVAL;
+  const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
+  for (const void *p : all)
+    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < bwd_layout(B, H, T, d).total)
+    return PATH_ATTN_EINVAL;
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.w = w;
+  a.beta = beta;
+  a.logf = logf;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.dlse = dlse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dw = dw;
+  a.dbeta = dbeta;
+  a.dlogf = logf ? dlogf : nullptr;
+  a.B = B;
+  a.H = H;
+  a.T = T;
+  a.scale = scale_of(scale, d);
+  return launch_bwd(dtype, d, a, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PATH_ATTN_OK
+             : PATH_ATTN_EHIP;
+}
+
 // ---------------------------------------------------------------- decoding
 
 namespace {

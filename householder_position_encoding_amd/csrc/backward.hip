@@ -1,0 +1,827 @@
+// backward.hip -- gradients of PaTH attention (q, k, v, w, beta, log f).
+//
+// The pages time forward plus backward ([R]'s latency table) but describe
+// only the forward kernel; the backward here is this library's blockwise
+// derivation of the exact gradients, built on the forward's chunk algebra
+// (PaTH slides for arXiv:2505.16381v2, frames "A triangular representation
+// makes paths computable", "A right-to-left scan accumulates cross-block
+// paths", "Backup: fix orientation before implementing UT products") and on
+// the decoding view of frame "Decoding updates historical keys in place".
+//
+// Per 64-token chunk c the forward's UT quantities are Qa = <-Q_c, Kb = ->K_c,
+// M_c and the diagonal logits Al_c.  The keys of every chunk before c,
+// aligned to the start of chunk c ("key level" c), satisfy
+//     Khat[c+1] = [ Khat[c] (I - M_c)^T ; Kb_c ],
+// and the cross logits of query chunk c are Qa_c Khat[c]^T.  With the
+// forward's lse the weights P = exp(s - lse) are known, so the gradient of the
+// raw logits is g = scale * P o (dO V^T - rowdot(dO, O) + dlse).  Then, for
+// c = N-1 down to 1 (one launch per chunk, one block per earlier key chunk):
+//     dQa_c  = g Khat[c]                       (partials reduced per chunk)
+//     dV    += P^T dO_c,   dLambda_j -= colsum(dS)
+//     Gamma += g^T Qa_c                        (gradient of Khat[c])
+//     dKb_{c-1} = Gamma[chunk c-1],  dM_{c-1} = -Gamma[< c-1]^T Khat[c-1],
+//     Gamma <- Gamma[< c-1] (I - M_{c-1}).
+// The diagonal blocks give dAl and start dV; a per-chunk adjoint of the UT
+// formulas maps (dQa, dKb, dM, dAl) to dq, dk, dw, dbeta; suffix sums of
+// dLambda give d log f.  All arithmetic is float32; the key levels of a head
+// take 64*d*N(N-1)/2 floats of workspace.
+#include "path_attn_internal.h"
+#include "tile_fp32.h"
+
+namespace pathattn {
+
+namespace {
+
+constexpr int C = kChunk;
+constexpr int NT = 256;
+
+template <typename E>
+__device__ __forceinline__ float ld(const E *p) { return (float)*p; }
+
+// Offset (floats) of key level c, row block c', within one head's levels.
+__host__ __device__ inline size_t level_off(int c, int cp, int D) {
+  return ((size_t)c * (c - 1) / 2 + cp) * (size_t)C * D;
+}
+
+// ------------------------------------------------------------ chunk prep
+
+// One block per (bh, chunk): Qa, Kb (natural [T][D]), M ([N][D][D], M[a][b])
+// and Al ([N][64][64], zero above the diagonal) in float32.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
+    const float *__restrict__ beta, float *__restrict__ qa, float *__restrict__ kb,
+    float *__restrict__ m, float *__restrict__ al, int T) {
+  constexpr int DP = D + 1, CP = C + 1;
+  __shared__ float Ws[C * DP];
+  __shared__ float Bs[C * DP];   // U W, later K
+  __shared__ float Qs[C * DP];
+  __shared__ float Us[C * CP];   // N, U, then T2
+  __shared__ float Xs[C * CP];   // X, then lower(Q W^T)
+  __shared__ float Ys[C * CP];   // strictLower(W K^T)
+  __shared__ float bs[C];
+  const int N = T / C;
+  const int bh = blockIdx.x / N, c = blockIdx.x % N;
+  const size_t row0 = (size_t)bh * T + (size_t)c * C;
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  float acc[4][4], acc2[4][4];
+
+  for (int idx = tid; idx < C * D; idx += NT) {
+    Ws[(idx / D) * DP + idx % D] = ld(w + row0 * D + idx);
+    Qs[(idx / D) * DP + idx % D] = ld(q + row0 * D + idx);
+  }
+  if (tid < C) bs[tid] = beta[row0 + tid];
+  __syncthreads();
+  tile_zero(acc);
+  tile_mm<D>(acc, Ws, DP, 1, Ws, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      Us[i * CP + j] = j < i ? acc[r][s] * bs[i] : 0.f;   // N
+    }
+  __syncthreads();
+  if (tid < C) {   // X = (I + N)^{-1} below the diagonal, one column per lane
+    const int j = tid;
+    for (int i = j + 1; i < C; ++i) {
+      float x = -Us[i * CP + j];
+      for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Us[i * CP + t], Xs[t * CP + j], x);
+      Xs[i * CP + j] = x;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * C; idx += NT) {
+    const int i = idx / C, j = idx % C;
+    Us[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);   // U
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // U W
+    tile_zero(acc);
+    tile_mm<C>(acc, Us, CP, 1, Ws + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Bs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] = acc[r][s];
+  }
+  __syncthreads();
+  float *m_c = m + ((size_t)bh * N + c) * D * D;   // M = W^T (U W)
+#pragma unroll
+  for (int ha = 0; ha < D / 64; ++ha)
+#pragma unroll
+    for (int hb = 0; hb < D / 64; ++hb) {
+      tile_zero(acc);
+      tile_mm<C>(acc, Ws + 64 * ha, 1, DP, Bs + 64 * hb, DP, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          m_c[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * s] = acc[r][s];
+    }
+  tile_zero(acc);   // lower(Q W^T) into Xs
+  tile_mm<D>(acc, Qs, DP, 1, Ws, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      Xs[i * CP + j] = j <= i ? acc[r][s] : 0.f;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // <-Q = Q - lower(Q W^T) U W
+    tile_zero(acc);
+    tile_mm<C>(acc, Xs, CP, 1, Bs + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
+        qa[(row0 + i) * D + col] = Qs[i * DP + col] - acc[r][s];
+      }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * D; idx += NT) Bs[(idx / D) * DP + idx % D] = ld(k + row0 * D + idx);
+  __syncthreads();
+  tile_zero(acc);   // strictLower(W K^T)
+  tile_mm<D>(acc, Ws, DP, 1, Bs, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int t = r0 + 16 * r, j = c0 + 16 * s;
+      Ys[t * CP + j] = t > j ? acc[r][s] : 0.f;
+    }
+  __syncthreads();
+  tile_zero(acc);   // T2 = U strictLower(W K^T), over U
+  tile_mm<C>(acc, Us, CP, 1, Ys, CP, 1, r0, c0);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Us[(r0 + 16 * r) * CP + c0 + 16 * s] = acc[r][s];
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // ->K = K - T2^T W
+    tile_zero(acc);
+    tile_mm<C>(acc, Us, 1, CP, Ws + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
+        kb[(row0 + j) * D + col] = Bs[j * DP + col] - acc[r][s];
+      }
+  }
+  // Al = lower(Q K^T) - lower(Q W^T) T2
+  tile_zero(acc);
+  tile_mm<D>(acc, Qs, DP, 1, Bs, 1, DP, r0, c0);
+  tile_zero(acc2);
+  tile_mm<C>(acc2, Xs, CP, 1, Us, CP, 1, r0, c0);
+  float *al_c = al + ((size_t)bh * N + c) * C * C;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      al_c[i * C + j] = j <= i ? acc[r][s] - acc2[r][s] : 0.f;
+    }
+}
+
+// Lambda_t = sum_{1<=s<=t} log f_s (float64 running sum), one block per head.
+__global__ __launch_bounds__(64) void bwd_gate_kernel(const float *__restrict__ logf,
+                                                      float *__restrict__ lam, int T) {
+  if (threadIdx.x != 0) return;
+  const size_t base = (size_t)blockIdx.x * T;
+  double acc = 0.0;
+  lam[base] = 0.f;
+  for (int t = 1; t < T; ++t) {
+    acc += (double)logf[base + t];
+    lam[base + t] = (float)acc;
+  }
+}
+
+// ------------------------------------------------------------ key levels
+
+// One block per (key chunk c', bh): walks the levels c = c'+1 .. N-1 writing
+// the aligned rows of chunk c' (Kb_{c'} at level c'+1, then times
+// (I - M_c)^T per level).  Blocks of early chunks (the longest walks) first.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_levels_kernel(const float *__restrict__ kb,
+                                                         const float *__restrict__ m,
+                                                         float *__restrict__ levels, int T,
+                                                         int BH) {
+  constexpr int DP = D + 1;
+  __shared__ float Xs[C * DP];
+  __shared__ float Ms[D * DP];
+  const int N = T / C;
+  const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  const size_t lev_head = (size_t)bh * level_off(N, 0, D);
+  for (int idx = tid; idx < C * D; idx += NT)
+    Xs[(idx / D) * DP + idx % D] = kb[((size_t)bh * T + (size_t)cp * C) * D + idx];
+  __syncthreads();
+  for (int c = cp + 1; c < N; ++c) {
+    float *dst = levels + lev_head + level_off(c, cp, D);
+    for (int idx = tid; idx < C * D; idx += NT) dst[idx] = Xs[(idx / D) * DP + idx % D];
+    if (c + 1 >= N) break;
+    const float *m_c = m + ((size_t)bh * N + c) * D * D;
+    for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
+    __syncthreads();
+    float acc[D / 64][4][4];
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {   // X M^T: B(k, j) = M[j][k]
+      tile_zero(acc[h]);
+      tile_mm<D>(acc[h], Xs, DP, 1, Ms + 64 * h * DP, 1, DP, r0, c0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Xs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] -= acc[h][r][s];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ diagonal blocks
+
+// One block per (bh, chunk): rowdot(dO, O), the diagonal block's weights and
+// gradients; starts dV (P^T dO) and dLambda (dlse - colsum dS) of the chunk.
+template <typename E, int D, bool FOX>
+__global__ __launch_bounds__(256) void bwd_diag_kernel(
+    const float *__restrict__ al, const E *__restrict__ v, const E *__restrict__ o,
+    const E *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dlse,
+    const float *__restrict__ lam, float scale, float *__restrict__ dal,
+    float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dvec, int T) {
+  constexpr int DP = D + 1, CP = C + 1;
+  __shared__ float Os[C * DP];
+  __shared__ float Vs[C * DP];
+  __shared__ float Ps[C * CP];
+  __shared__ float rl[C], rd[C], rg[C], rdl[C];
+  const int N = T / C;
+  const int bh = blockIdx.x / N, c = blockIdx.x % N;
+  const size_t row0 = (size_t)bh * T + (size_t)c * C;
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  for (int idx = tid; idx < C * D; idx += NT) {
+    Os[(idx / D) * DP + idx % D] = ld(dout + row0 * D + idx);
+    Vs[(idx / D) * DP + idx % D] = ld(v + row0 * D + idx);
+  }
+  if (tid < C) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = __builtin_fmaf(ld(dout + (row0 + tid) * D + e), ld(o + (row0 + tid) * D + e), s);
+    rd[tid] = s;
+    dvec[row0 + tid] = s;
+    rl[tid] = lse[row0 + tid];
+    rg[tid] = FOX ? lam[row0 + tid] : 0.f;
+    rdl[tid] = dlse ? dlse[row0 + tid] : 0.f;
+  }
+  __syncthreads();
+  const float *al_c = al + ((size_t)bh * N + c) * C * C;
+  float p[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      p[r][s] = j <= i ? __expf(scale * al_c[i * C + j] + rg[i] - rg[j] - rl[i]) : 0.f;
+      Ps[i * CP + j] = p[r][s];
+    }
+  __syncthreads();
+  float acc[4][4];
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // dV_c = P^T dO
+    tile_zero(acc);
+    tile_mm<C>(acc, Ps, 1, CP, Os + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dv[(row0 + r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = acc[r][s];
+  }
+  tile_zero(acc);   // dP = dO V^T, dS = P (dP - D + dlse)
+  tile_mm<D>(acc, Os, DP, 1, Vs, 1, DP, r0, c0);
+  __syncthreads();
+  float *dal_c = dal + ((size_t)bh * N + c) * C * C;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      const float ds = p[r][s] * (acc[r][s] - rd[i] + rdl[i]);
+      Ps[i * CP + j] = ds;
+      dal_c[i * C + j] = scale * ds;
+    }
+  __syncthreads();
+  if (tid < C) {
+    float cs = 0.f;
+    for (int i = 0; i < C; ++i) cs += Ps[i * CP + tid];
+    dlam[row0 + tid] = rdl[tid] - cs;
+  }
+}
+
+// ------------------------------------------------------------ sweep
+
+// Step c of the downward sweep: one block per (earlier key chunk c' < c, bh).
+template <typename E, int D, bool FOX>
+__global__ __launch_bounds__(256) void bwd_sweep_kernel(
+    int c, const float *__restrict__ qa, const E *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ dlse,
+    const float *__restrict__ dvec, const float *__restrict__ lam,
+    const float *__restrict__ levels, const E *__restrict__ v, const float *__restrict__ m,
+    float scale, float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dqpart,
+    float *__restrict__ gam, float *__restrict__ dkb, float *__restrict__ dmpart, int T) {
+  constexpr int DP = D + 1, CP = C + 1;
+  // Qs | Os contiguous (later M, D x DP), Ks (later Khat[c-1]), Vs (later Gamma), Ps
+  __shared__ float pool[2 * C * DP + 2 * C * DP + C * CP];
+  __shared__ float rl[C], rd[C], rg[C], rdl[C], kg[C];
+  float *Qs = pool, *Os = pool + C * DP, *Ms = pool;
+  float *Ks = pool + 2 * C * DP, *Vs = pool + 3 * C * DP, *Gs = Vs;
+  float *Ps = pool + 4 * C * DP;
+  const int N = T / C;
+  const int cp = blockIdx.x % c, bh = blockIdx.x / c;
+  const size_t qrow = (size_t)bh * T + (size_t)c * C, krow = (size_t)bh * T + (size_t)cp * C;
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  const size_t lev_head = (size_t)bh * level_off(N, 0, D);
+  const float *khat = levels + lev_head + level_off(c, cp, D);
+
+  for (int idx = tid; idx < C * D; idx += NT) {
+    const int rr = idx / D, ee = idx % D;
+    Qs[rr * DP + ee] = qa[qrow * D + idx];
+    Os[rr * DP + ee] = ld(dout + qrow * D + idx);
+    Ks[rr * DP + ee] = khat[idx];
+    Vs[rr * DP + ee] = ld(v + krow * D + idx);
+  }
+  if (tid < C) {
+    rl[tid] = lse[qrow + tid];
+    rd[tid] = dvec[qrow + tid];
+    rdl[tid] = dlse ? dlse[qrow + tid] : 0.f;
+    rg[tid] = FOX ? lam[qrow + tid] : 0.f;
+    kg[tid] = FOX ? lam[krow + tid] : 0.f;
+  }
+  __syncthreads();
+  float acc[4][4], p[4][4];
+  tile_zero(acc);   // S = Qa Khat^T
+  tile_mm<D>(acc, Qs, DP, 1, Ks, 1, DP, r0, c0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      p[r][s] = __expf(scale * acc[r][s] + rg[i] - kg[j] - rl[i]);
+      Ps[i * CP + j] = p[r][s];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // dV_{c'} += P^T dO
+    tile_zero(acc);
+    tile_mm<C>(acc, Ps, 1, CP, Os + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dv[(krow + r0 + 16 * r) * D + 64 * h + c0 + 16 * s] += acc[r][s];
+  }
+  tile_zero(acc);   // dP = dO V^T
+  tile_mm<D>(acc, Os, DP, 1, Vs, 1, DP, r0, c0);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = r0 + 16 * r, j = c0 + 16 * s;
+      Ps[i * CP + j] = p[r][s] * (acc[r][s] - rd[i] + rdl[i]);   // dS
+    }
+  __syncthreads();
+  if (tid < C) {   // dLambda_j -= sum_i dS_ij
+    float cs = 0.f;
+    for (int i = 0; i < C; ++i) cs += Ps[i * CP + tid];
+    dlam[krow + tid] -= cs;
+  }
+  float gacc[D / 64][4][4];
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {   // partial dQa_c = g Khat,  Gamma += g^T Qa
+    tile_zero(acc);
+    tile_mm<C>(acc, Ps, CP, 1, Ks + 64 * h, DP, 1, r0, c0);
+    float *dst = dqpart + ((size_t)bh * N + cp) * C * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dst[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = scale * acc[r][s];
+    tile_zero(gacc[h]);
+    tile_mm<C>(gacc[h], Ps, 1, CP, Qs + 64 * h, DP, 1, r0, c0);
+    float *gsrc = gam + krow * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        gacc[h][r][s] = gsrc[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] + scale * gacc[h][r][s];
+  }
+  if (cp == c - 1) {   // chunk c-1's rows are ->K_{c-1} at level c: final gradient
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          dkb[(krow + r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = gacc[h][r][s];
+    return;
+  }
+  // cross chunk c-1's transition: dM part = -Gamma^T Khat[c-1], Gamma (I - M)
+  __syncthreads();
+  const float *khp = levels + lev_head + level_off(c - 1, cp, D);
+  const float *m_c = m + ((size_t)bh * N + (c - 1)) * D * D;
+  for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
+  for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = khp[idx];
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Gs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] = gacc[h][r][s];
+  __syncthreads();
+  float *mp = dmpart + ((size_t)bh * N + cp) * D * D;
+#pragma unroll
+  for (int ha = 0; ha < D / 64; ++ha)
+#pragma unroll
+    for (int hb = 0; hb < D / 64; ++hb) {
+      tile_zero(acc);
+      tile_mm<C>(acc, Gs + 64 * ha, 1, DP, Ks + 64 * hb, DP, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          mp[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * s] = -acc[r][s];
+    }
+  float *gdst = gam + krow * D;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    tile_zero(acc);
+    tile_mm<D>(acc, Gs, DP, 1, Ms + 64 * h, DP, 1, r0, c0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        gdst[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = gacc[h][r][s] - acc[r][s];
+  }
+}
+
+// dQa_c = sum over c' < c of the partials; dM_{c-1} = sum over c' < c-1.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(int c, const float *__restrict__ dqpart,
+                                                         const float *__restrict__ dmpart,
+                                                         float *__restrict__ dqa,
+                                                         float *__restrict__ dm, int T) {
+  const int N = T / C;
+  const int bh = blockIdx.y;
+  const int per = C * D + D * D;
+  for (int idx = blockIdx.x * NT + threadIdx.x; idx < per; idx += gridDim.x * NT) {
+    if (idx < C * D) {
+      float s = 0.f;
+      for (int cp = 0; cp < c; ++cp) s += dqpart[((size_t)bh * N + cp) * C * D + idx];
+      dqa[((size_t)bh * T + (size_t)c * C) * D + idx] = s;
+    } else {
+      const int e = idx - C * D;
+      float s = 0.f;
+      for (int cp = 0; cp < c - 1; ++cp) s += dmpart[((size_t)bh * N + cp) * D * D + e];
+      dm[((size_t)bh * N + (c - 1)) * D * D + e] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------ local adjoint
+
+// One block per (bh, chunk) (grid-stride over chunks with a per-block scratch
+// area): gradients of the chunk's inputs from those of its UT quantities.
+//   dA   = lower(-dQa (UW)^T - dAl T2^T)          A = lower(Q W^T)
+//   dUW  = -A^T dQa + W dM
+//   dT2  = -W dKb^T - A^T dAl
+//   dU   = dUW W^T + dT2 B^T,  dB = strictLower(U^T dT2)   B = strictLower(W K^T)
+//   dX   = lower(dU) D,  dbeta_j += sum_i X_ij dU_ij        U = X D
+//   dN   = strictLower(-X^T dX X^T)                         X = (I + N)^{-1}
+//   dbeta_i += sum_{j<i} dN_ij G_ij,  dG = strictLower(D dN)  N = strictLower(D G)
+//   dQ   = dQa + dAl K + dA W
+//   dK   = dKb + dAl^T Q + dB^T W
+//   dW   = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + (dG + dG^T) W
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_local_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
+    const float *__restrict__ beta, const float *__restrict__ dqa,
+    const float *__restrict__ dkb, const float *__restrict__ dm, const float *__restrict__ dal,
+    float *__restrict__ scratch, E *__restrict__ dq, E *__restrict__ dk, E *__restrict__ dw,
+    float *__restrict__ dbeta, int T, int n_chunks_total) {
+  constexpr int CP = C + 1;
+  // scratch per block (floats): R-sized = C*D, S-sized = C*C
+  constexpr int R = C * D, S = C * C;
+  float *base = scratch + (size_t)blockIdx.x * (6 * R + 11 * S);
+  float *Wg = base, *Qg = Wg + R, *Kg = Qg + R, *UWg = Kg + R, *dUWg = UWg + R, *Tmp = dUWg + R;
+  float *Gg = Tmp + R, *Xg = Gg + S, *Ug = Xg + S, *Ag = Ug + S, *Bg = Ag + S, *T2g = Bg + S;
+  float *dAg = T2g + S, *dT2g = dAg + S, *dUg = dT2g + S, *dBg = dUg + S, *dNg = dBg + S;
+  __shared__ float Ns[C * CP], Xs[C * CP];
+  __shared__ float bs[C], dbs[C];
+  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  const int N = T / C;
+  float acc[4][4];
+
+  // store a 64 x 64 tile (columns col0..) into a row-major matrix of row length ld
+  auto put = [&](float *dst, int ld, int col0, float (&a)[4][4], float sgn, int mask) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int i = r0 + 16 * r, j = c0 + 16 * s;
+        const bool keep = mask == 0 || (mask == 1 && j <= i) || (mask == 2 && j < i);
+        dst[i * ld + col0 + j] = keep ? sgn * a[r][s] : 0.f;
+      }
+  };
+
+  for (int blk = blockIdx.x; blk < n_chunks_total; blk += gridDim.x) {
+    const int bh = blk / N, c = blk % N;
+    const size_t row0 = (size_t)bh * T + (size_t)c * C;
+    const float *dQa = dqa + row0 * D, *dKb = dkb + row0 * D;
+    const float *dM = dm + ((size_t)bh * N + c) * D * D;
+    const float *dAl = dal + ((size_t)bh * N + c) * C * C;
+    __syncthreads();
+    for (int idx = tid; idx < R; idx += NT) {
+      Wg[idx] = ld(w + row0 * D + idx);
+      Qg[idx] = ld(q + row0 * D + idx);
+      Kg[idx] = ld(k + row0 * D + idx);
+    }
+    if (tid < C) {
+      bs[tid] = beta[row0 + tid];
+      dbs[tid] = 0.f;
+    }
+    __syncthreads();
+    // G = W W^T, N, X, U
+    tile_zero(acc);
+    tile_mm<D>(acc, Wg, D, 1, Wg, 1, D, r0, c0);
+    put(Gg, C, 0, acc, 1.f, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int i = r0 + 16 * r, j = c0 + 16 * s;
+        Ns[i * CP + j] = j < i ? acc[r][s] * bs[i] : 0.f;
+        Xs[i * CP + j] = j == i ? 1.f : 0.f;
+      }
+    __syncthreads();
+    if (tid < C) {
+      const int j = tid;
+      for (int i = j + 1; i < C; ++i) {
+        float x = -Ns[i * CP + j];
+        for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Ns[i * CP + t], Xs[t * CP + j], x);
+        Xs[i * CP + j] = x;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < S; idx += NT) {
+      const int i = idx / C, j = idx % C;
+      Xg[idx] = Xs[i * CP + j];
+      Ug[idx] = j <= i ? Xs[i * CP + j] * bs[j] : 0.f;
+    }
+    __syncthreads();
+    // UW = U W, A = lower(Q W^T), B = strictLower(W K^T)
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      tile_zero(acc);
+      tile_mm<C>(acc, Ug, C, 1, Wg + 64 * h, D, 1, r0, c0);
+      put(UWg, D, 64 * h, acc, 1.f, 0);
+    }
+    tile_zero(acc);
+    tile_mm<D>(acc, Qg, D, 1, Wg, 1, D, r0, c0);
+    put(Ag, C, 0, acc, 1.f, 1);
+    tile_zero(acc);
+    tile_mm<D>(acc, Wg, D, 1, Kg, 1, D, r0, c0);
+    put(Bg, C, 0, acc, 1.f, 2);
+    __syncthreads();
+    tile_zero(acc);   // T2 = U B
+    tile_mm<C>(acc, Ug, C, 1, Bg, C, 1, r0, c0);
+    put(T2g, C, 0, acc, 1.f, 0);
+    __syncthreads();
+    // dA = lower(-dQa UW^T - dAl T2^T)
+    tile_zero(acc);
+    tile_mm<D>(acc, dQa, D, 1, UWg, 1, D, r0, c0);
+    tile_mm<C>(acc, dAl, C, 1, T2g, 1, C, r0, c0);
+    put(dAg, C, 0, acc, -1.f, 1);
+    // dUW = -A^T dQa + W dM
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      float a2[4][4];
+      tile_zero(acc);
+      tile_mm<C>(acc, Ag, 1, C, dQa + 64 * h, D, 1, r0, c0);
+      tile_zero(a2);
+      tile_mm<D>(a2, Wg, D, 1, dM + 64 * h, D, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[r][s] = a2[r][s] - acc[r][s];
+      put(dUWg, D, 64 * h, acc, 1.f, 0);
+    }
+    // dT2 = -W dKb^T - A^T dAl
+    tile_zero(acc);
+    tile_mm<D>(acc, Wg, D, 1, dKb, 1, D, r0, c0);
+    tile_mm<C>(acc, Ag, 1, C, dAl, C, 1, r0, c0);
+    put(dT2g, C, 0, acc, -1.f, 0);
+    __syncthreads();
+    // dU = dUW W^T + dT2 B^T (lower part), dB = strictLower(U^T dT2)
+    tile_zero(acc);
+    tile_mm<D>(acc, dUWg, D, 1, Wg, 1, D, r0, c0);
+    tile_mm<C>(acc, dT2g, C, 1, Bg, 1, C, r0, c0);
+    put(dUg, C, 0, acc, 1.f, 1);
+    tile_zero(acc);
+    tile_mm<C>(acc, Ug, 1, C, dT2g, C, 1, r0, c0);
+    put(dBg, C, 0, acc, 1.f, 2);
+    __syncthreads();
+    // dbeta_j += sum_i X_ij dU_ij; dX = dU D (into Tmp as 64 x 64)
+    if (tid < C) {
+      float sacc = 0.f;
+      for (int i = 0; i < C; ++i) sacc += Xg[i * C + tid] * dUg[i * C + tid];
+      dbs[tid] += sacc;
+    }
+    for (int idx = tid; idx < S; idx += NT) Tmp[idx] = dUg[idx] * bs[idx % C];
+    __syncthreads();
+    // dN = strictLower(-X^T dX X^T): first Y = dX X^T (into dNg), then -X^T Y
+    tile_zero(acc);
+    tile_mm<C>(acc, Tmp, C, 1, Xg, 1, C, r0, c0);
+    put(dNg, C, 0, acc, 1.f, 0);
+    __syncthreads();
+    tile_zero(acc);
+    tile_mm<C>(acc, Xg, 1, C, dNg, C, 1, r0, c0);
+    __syncthreads();
+    put(dNg, C, 0, acc, -1.f, 2);
+    __syncthreads();
+    // dbeta_i += sum_{j<i} dN_ij G_ij; dG = D dN (strict lower, into Tmp)
+    if (tid < C) {
+      float sacc = 0.f;
+      for (int j = 0; j < tid; ++j) sacc += dNg[tid * C + j] * Gg[tid * C + j];
+      dbs[tid] += sacc;
+    }
+    for (int idx = tid; idx < S; idx += NT) Tmp[idx] = dNg[idx] * bs[idx / C];
+    __syncthreads();
+    // dQ = dQa + dAl K + dA W
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      tile_zero(acc);
+      tile_mm<C>(acc, dAl, C, 1, Kg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, dAg, C, 1, Wg + 64 * h, D, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
+          dq[(row0 + i) * D + col] = (E)(dQa[i * D + col] + acc[r][s]);
+        }
+    }
+    // dK = dKb + dAl^T Q + dB^T W
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      tile_zero(acc);
+      tile_mm<C>(acc, dAl, 1, C, Qg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, dBg, 1, C, Wg + 64 * h, D, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
+          dk[(row0 + i) * D + col] = (E)(dKb[i * D + col] + acc[r][s]);
+        }
+    }
+    // dW = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + (dG + dG^T) W
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h) {
+      float a2[4][4];
+      tile_zero(acc);
+      tile_mm<D>(acc, UWg, D, 1, dM + 64 * h * D, 1, D, r0, c0);
+      tile_mm<C>(acc, Ug, 1, C, dUWg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, dAg, 1, C, Qg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, dBg, C, 1, Kg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, Tmp, C, 1, Wg + 64 * h, D, 1, r0, c0);
+      tile_mm<C>(acc, Tmp, 1, C, Wg + 64 * h, D, 1, r0, c0);
+      tile_zero(a2);
+      tile_mm<C>(a2, T2g, C, 1, dKb + 64 * h, D, 1, r0, c0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
+          dw[(row0 + i) * D + col] = (E)(acc[r][s] - a2[r][s]);
+        }
+    }
+    __syncthreads();
+    if (tid < C) dbeta[row0 + tid] = dbs[tid];
+  }
+}
+
+// dv = dV in the input dtype; d log f_t = sum_{i >= t} dLambda_i (t >= 1),
+// d log f_0 = 0, one block per head for the suffix sums.
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_final_kernel(const float *__restrict__ dvacc,
+                                                        E *__restrict__ dv,
+                                                        const float *__restrict__ dlam,
+                                                        float *__restrict__ dlogf, int T, int D) {
+  const int bh = blockIdx.x;
+  const size_t n = (size_t)T * D;
+  for (size_t i = threadIdx.x; i < n; i += NT) dv[(size_t)bh * n + i] = (E)dvacc[(size_t)bh * n + i];
+  if (dlogf && threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int t = T - 1; t >= 1; --t) {
+      acc += (double)dlam[(size_t)bh * T + t];
+      dlogf[(size_t)bh * T + t] = (float)acc;
+    }
+    dlogf[(size_t)bh * T] = 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT) p[i] = 0.f;
+}
+
+void zero(float *p, size_t n, hipStream_t s) {
+  const size_t blocks = (n + NT - 1) / NT;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096)),
+                     dim3(NT), 0, s, p, n);
+}
+
+constexpr int kLocalBlocks = 1024;
+
+}  // namespace
+
+BwdLayout bwd_layout(int B, int H, int T, int D) {
+  const size_t BH = (size_t)B * H, N = (size_t)T / C;
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off = align256(off + floats * sizeof(float));
+    return o;
+  };
+  L.qa = take(BH * T * D);
+  L.kb = take(BH * T * D);
+  L.m = take(BH * N * D * D);
+  L.al = take(BH * N * C * C);
+  L.lam = take(BH * T);
+  L.dvec = take(BH * T);
+  L.levels = take(BH * level_off((int)N, 0, D));
+  L.gam = take(BH * T * D);
+  L.dv = take(BH * T * D);
+  L.dlam = take(BH * T);
+  L.dqpart = take(BH * N * C * D);
+  L.dmpart = take(BH * N * D * D);
+  L.dqa = take(BH * T * D);
+  L.dkb = take(BH * T * D);
+  L.dm = take(BH * N * D * D);
+  L.dal = take(BH * N * C * C);
+  L.scratch = take((size_t)kLocalBlocks * (6 * C * D + 11 * C * C));
+  L.total = off;
+  return L;
+}
+
+template <typename E, int D, bool FOX>
+hipError_t bwd_t(const BwdArgs &a, char *ws, hipStream_t s) {
+  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D);
+  const int BH = a.B * a.H, T = a.T, N = T / C;
+  auto f = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+  const E *q = (const E *)a.q, *k = (const E *)a.k, *v = (const E *)a.v, *w = (const E *)a.w;
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
+                     f(L.qa), f(L.kb), f(L.m), f(L.al), T);
+  if (FOX) hipLaunchKernelGGL(bwd_gate_kernel, dim3(BH), dim3(64), 0, s, a.logf, f(L.lam), T);
+  if (N > 1)
+    hipLaunchKernelGGL((bwd_levels_kernel<D>), dim3(BH * (N - 1)), dim3(NT), 0, s, f(L.kb), f(L.m),
+                       f(L.levels), T, BH);
+  zero(f(L.gam), (size_t)BH * T * D, s);
+  zero(f(L.dqa), (size_t)BH * T * D, s);   // chunk 0 has no earlier keys: its dQa stays zero
+  zero(f(L.dkb), (size_t)BH * T * D, s);
+  zero(f(L.dm), (size_t)BH * N * D * D, s);
+  hipLaunchKernelGGL((bwd_diag_kernel<E, D, FOX>), dim3(BH * N), dim3(NT), 0, s, f(L.al), v,
+                     (const E *)a.out, (const E *)a.dout, a.lse, a.dlse, f(L.lam), a.scale, f(L.dal),
+                     f(L.dv), f(L.dlam), f(L.dvec), T);
+  for (int c = N - 1; c >= 1; --c) {
+    hipLaunchKernelGGL((bwd_sweep_kernel<E, D, FOX>), dim3(c * BH), dim3(NT), 0, s, c, f(L.qa),
+                       (const E *)a.dout, a.lse, a.dlse, f(L.dvec), f(L.lam), f(L.levels), v, f(L.m),
+                       a.scale, f(L.dv), f(L.dlam), f(L.dqpart), f(L.gam), f(L.dkb), f(L.dmpart), T);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(8, BH), dim3(NT), 0, s, c, f(L.dqpart),
+                       f(L.dmpart), f(L.dqa), f(L.dm), T);
+  }
+  const int nloc = BH * N < kLocalBlocks ? BH * N : kLocalBlocks;
+  hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(nloc), dim3(NT), 0, s, q, k, w, a.beta,
+                     f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.scratch), (E *)a.dq, (E *)a.dk,
+                     (E *)a.dw, a.dbeta, T, BH * N);
+  hipLaunchKernelGGL((bwd_final_kernel<E>), dim3(BH), dim3(NT), 0, s, f(L.dv), (E *)a.dv, f(L.dlam),
+                     FOX ? a.dlogf : nullptr, T, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipStream_t s) {
+  char *ws = static_cast<char *>(workspace);
+  const bool fox = a.logf != nullptr;
+  if (dtype == 1) {
+    if (D == 64) return fox ? bwd_t<__bf16, 64, true>(a, ws, s) : bwd_t<__bf16, 64, false>(a, ws, s);
+    return fox ? bwd_t<__bf16, 128, true>(a, ws, s) : bwd_t<__bf16, 128, false>(a, ws, s);
+  }
+  if (D == 64) return fox ? bwd_t<float, 64, true>(a, ws, s) : bwd_t<float, 64, false>(a, ws, s);
+  return fox ? bwd_t<float, 128, true>(a, ws, s) : bwd_t<float, 128, false>(a, ws, s);
+}
+
+}  // namespace pathattn

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "path_attn_internal.h"
+#include "tile_fp32.h"
 
 namespace pathattn {
 
@@ -47,34 +48,6 @@ template <typename E>
 __device__ __forceinline__ E from_f(float x) { return (E)x; }   // RNE for bf16
 
 // ------------------------------------------------------------ prefill: chunks
-
-// acc[r][s] += sum_k A(r0 + 16 r, k) B(k, c0 + 16 s) over k < K for one
-// thread's 4 x 4 tile of a 64 x 64 output block, operands in LDS with
-// arbitrary row / column strides (so transposed reads need no copy).  Rows of
-// the tile are 16 apart and columns 16 apart: a wave's lanes read 4 distinct
-// A addresses and 16 consecutive B addresses per instruction.
-template <int K>
-__device__ __forceinline__ void tile_mm(float (&acc)[4][4], const float *A, int a_rs, int a_cs,
-                                        const float *B, int b_rs, int b_cs, int r0, int c0) {
-  for (int kk = 0; kk < K; ++kk) {
-    float a[4], b[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = A[(r0 + 16 * r) * a_rs + kk * a_cs];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) b[c] = B[kk * b_rs + (c0 + 16 * c) * b_cs];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(a[r], b[c], acc[r][c]);
-  }
-}
-
-__device__ __forceinline__ void tile_zero(float (&acc)[4][4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-}
 
 // One block of 256 threads per (bh, chunk): ->K_c and M_c in float32, natural
 // layouts kb[bh][L][D] and m[bh][N][D][D] (M[a][b]).

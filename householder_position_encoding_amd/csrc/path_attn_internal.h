@@ -147,4 +147,26 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
                               void *out, float *lse, float *part, int BH, int t, int T_cap,
                               float sl2, hipStream_t s);
 
+// Backward pass (backward.hip).  Workspace offsets in bytes; the key levels
+// of one head take 64*D*N(N-1)/2 floats, N = T/64.
+struct BwdLayout {
+  size_t qa, kb, m, al, lam, dvec, levels, gam, dv, dlam, dqpart, dmpart, dqa, dkb, dm, dal,
+      scratch, total;
+};
+BwdLayout bwd_layout(int B, int H, int T, int D);
+
+struct BwdArgs {
+  const void *q, *k, *v, *w;
+  const float *beta, *logf;
+  const void *out;
+  const float *lse;
+  const void *dout;
+  const float *dlse;
+  void *dq, *dk, *dv, *dw;
+  float *dbeta, *dlogf;
+  int B, H, T;
+  float scale;
+};
+hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipStream_t s);
+
 }  // namespace pathattn

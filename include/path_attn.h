@@ -263,6 +263,54 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
                           int dtype, int kc_dtype, float scale, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * ------------------------------------------------------------------------
+ * Backward pass.  The pages time forward plus backward (the authors'
+ * response page, "Efficiency Evaluation" table) without giving the backward
+ * algorithm; this library computes the exact gradients of the forward's
+ * definition, blockwise over the same 64-token chunks (per-chunk UT
+ * quantities of frames "A triangular representation makes paths computable"
+ * and "Backup: fix orientation before implementing UT products", keys of
+ * earlier chunks aligned chunk by chunk as in frame "Decoding updates
+ * historical keys in place", a downward sweep over query chunks, then the
+ * per-chunk adjoint of the UT formulas).  Float32 arithmetic throughout.
+ * ------------------------------------------------------------------------
+ */
+
+/* Workspace bytes of path_attn_bwd, 0 for invalid or unsupported arguments.
+ * It grows as B*H*d*T^2/128 floats (the aligned key levels): about 17 GB at
+ * B=2, H=16, T=16384, d=64. */
+size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
+
+/*
+ * Gradients of  L = sum <dout, out> + sum <dlse, lse>  with respect to q, k,
+ * v, w, beta and (with the gate) log f, for the forward of path_attn_fwd_ex
+ * with the same inputs and scale.  out and lse must be that forward's
+ * outputs (the softmax weights are rebuilt as exp(s - lse)).
+ *   q, k, v, w, out, dout : [B, H, T, d] of dtype     (inputs)
+ *   beta, logf, lse       : [B, H, T] float32         (inputs; logf may be NULL)
+ *   dlse                  : [B, H, T] float32 or NULL (NULL = zero)
+ *   dq, dk, dv, dw        : [B, H, T, d] of dtype     (outputs, overwritten)
+ *   dbeta, dlogf          : [B, H, T] float32         (outputs; dlogf only with
+ *                                                      logf, where it is required;
+ *                                                      dlogf[.., 0] = 0 as f_0
+ *                                                      enters no logit)
+ * scale: as for path_attn_fwd_ex (0 selects 1/sqrt(d)).  Gradients with
+ * dtype PATH_ATTN_BF16 are computed in float32 and rounded once (RNE).
+ * T must be a multiple of 64.  Every pointer 16-byte aligned, the workspace
+ * 256-byte aligned.
+ * Errors: EINVAL for null or misaligned pointers, a bad dtype or scale,
+ * logf without dlogf, or a small workspace; EUNSUPPORTED for d not in
+ * {64, 128}, T % 64 != 0 or B*H*T*d >= 2^31; EHIP on a launch error.
+ */
+int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
+                  const float *beta, const float *logf, const void *out,
+                  const float *lse, const void *dout, const float *dlse,
+                  void *dq, void *dk, void *dv, void *dw, float *dbeta,
+                  float *dlogf, int B, int H, int T, int d, int dtype,
+                  float scale, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
 /* Static, human-readable description of a status code. */
 const char *path_attn_strerror(int status);
 

@@ -247,3 +247,49 @@ def test_binding_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("PATH_ATTN_LIB", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not found"):
         binding.load_library()
+
+
+# ---- backward
+
+def test_bwd_workspace_bytes():
+    lib = pa.load_library()
+    B, H, T, d = 2, 16, 2048, 64
+    n = lib.path_attn_bwd_workspace_bytes(B, H, T, d, pa.BF16)
+    BH, N = B * H, T // 64
+    levels = BH * N * (N - 1) // 2 * 64 * d * 4
+    assert levels < n < levels + BH * T * d * 4 * 16 + 1024 * (6 * 64 * d + 11 * 64 * 64) * 4
+    assert lib.path_attn_bwd_workspace_bytes(1, 1, 100, 64, pa.F32) == 0   # whole chunks only
+    assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 96, pa.F32) == 0
+    assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 4) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE,
+             dout=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, dbeta=FAKE, dlogf=None,
+             B=1, H=2, T=256, d=64, dtype=pa.BF16, scale=0.0, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.path_attn_bwd(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"], a["out"],
+                             a["lse"], a["dout"], a["dlse"], a["dq"], a["dk"], a["dv"], a["dw"],
+                             a["dbeta"], a["dlogf"], a["B"], a["H"], a["T"], a["d"], a["dtype"],
+                             a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+# every case fails validation (the addresses are fake and must never be launched on)
+BAD_BWD = [
+    (dict(q=None), EINVAL), (dict(v=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(lse=None), EINVAL), (dict(dout=None), EINVAL), (dict(dq=None), EINVAL),
+    (dict(dw=None), EINVAL), (dict(dbeta=None), EINVAL), (dict(ws=None), EINVAL),
+    (dict(logf=FAKE), EINVAL),                      # the gate needs dlogf
+    (dict(q=FAKE + 4), EINVAL), (dict(dlse=FAKE + 4), EINVAL), (dict(dbeta=FAKE + 8), EINVAL),
+    (dict(logf=FAKE, dlogf=FAKE + 2), EINVAL),
+    (dict(ws=FAKE + 64), EINVAL), (dict(wsb=100), EINVAL),
+    (dict(scale=-1.0), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(dtype=5), EINVAL),
+    (dict(T=100), EUNSUP), (dict(d=96), EUNSUP), (dict(B=0), EINVAL),
+    (dict(B=1 << 12, H=1 << 9, T=1 << 14), EUNSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_BWD, ids=lambda x: str(x))
+def test_bwd_validation(kw, status):
+    assert _bwd(pa.load_library(), **kw) == status

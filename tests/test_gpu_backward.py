@@ -1,0 +1,153 @@
+"""GPU parity of the backward pass (path_attn_bwd) against the float64
+gradient oracles.
+
+The forward runs on the GPU (path_attn_fwd) and its out and lse feed the
+GPU backward, as a training step would use them.  The oracle recomputes
+everything in float64 from the same stored inputs and cotangents.
+
+  * Small cases (several chunks, d = 64 and 128, with and without the gate,
+    with and without a gradient on lse): every gradient of every head
+    against oracle.backward.gradients (autograd of the definition).
+  * The workloads at full size: sampled heads against
+    oracle.chunked_backward.sweep_backward (the blockwise float64 statement,
+    pinned to the autograd oracle on the CPU), the GPU run covering the whole
+    batch in the same launch configuration as any other call.
+
+Bar, per gradient tensor g with float64 reference r:
+    max |g - r| <= tol * max(1, max |r|)
+with tol = 2e-4 for float32 inputs (float32 arithmetic; the longest sums
+run over T keys or T queries, sqrt(T) * 2^-24 ~ 1e-6 typical, plus the
+float32 forward's out and lse) and tol = 2e-2 for bf16 inputs (the forward's
+out is rounded to bf16, 2^-9 relative, which enters rowdot(dout, out) and so
+every softmax gradient; each gradient is rounded to bf16 once more on
+output).  dlogf at position 0 must be exactly zero (f_0 enters no logit).
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle.backward import gradients as oracle_gradients
+from oracle.chunked_backward import sweep_backward
+from tests.gpu_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-4, "bf16": 2e-2}
+NAMES = ("dq", "dk", "dv", "dw", "dbeta", "dlogf")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run_gpu(inp, cot, dtype, scale=None):
+    import torch
+    import householder_position_encoding_amd as pa
+    dev = to_device(inp, dtype)
+    tdt = dev["q"].dtype
+    dout = torch.from_numpy(cot["dout"]).to(device="cuda", dtype=tdt).contiguous()
+    dlse = None if cot["dlse"] is None else torch.from_numpy(cot["dlse"]).cuda().contiguous()
+    out, lse = pa.path_attn_fwd(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"],
+                                scale=scale)
+    grads = pa.path_attn_bwd(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"],
+                             out, lse, dout, dlse, scale=scale)
+    torch.cuda.synchronize()
+    return {n: (None if g is None else _to_np(g)) for n, g in zip(NAMES, grads)}
+
+
+def _head(inp, cot, b, h):
+    sel = lambda x: None if x is None else np.asarray(x[b, h], dtype=np.float64)
+    return (sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["w"]), sel(inp["beta"]),
+            sel(inp["logf"]), sel(cot["dout"]), sel(cot["dlse"]))
+
+
+def _compare(tag, dtype, got, ref, b, h):
+    tol = TOL[dtype]
+    worst = 0.0
+    for n in NAMES:
+        r = ref[n]
+        if r is None:
+            assert got[n] is None, f"{tag}: {n} returned without the gate"
+            continue
+        g = got[n][b, h]
+        assert np.all(np.isfinite(g)), f"{tag}: {n} not finite"
+        scale = max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(g - r))) / scale
+        worst = max(worst, err)
+        _log(f"{tag} head ({b},{h}) {n}: max|err|/max(1,max|ref|) = {err:.3g} (tol {tol})")
+        assert err <= tol, f"{tag}: {n} of head ({b},{h}) off by {err:.3g} > {tol}"
+    if ref["dlogf"] is not None:
+        assert got["dlogf"][b, h, 0] == 0.0
+    return worst
+
+
+SMALL = [
+    # dtype, d, fox, dlse, B, H, T
+    ("f32", 64, False, False, 1, 2, 256),
+    ("f32", 64, True, True, 1, 2, 256),
+    ("f32", 128, True, True, 2, 1, 192),
+    ("f32", 64, False, True, 1, 1, 64),
+    ("f32", 128, False, False, 1, 1, 128),
+    ("bf16", 64, True, True, 1, 2, 256),
+    ("bf16", 128, False, True, 1, 2, 192),
+    ("bf16", 64, False, False, 2, 1, 320),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_backward_small_all_heads(case):
+    dtype, d, fox, with_dlse, B, H, T = case
+    _log(f"backward small {case}")
+    inp = workloads.small(dtype, B, H, T, d, seed=70 + T + d, fox=fox, beta_sigma=1.5)
+    cot = workloads.cotangents(dtype, B, H, T, d, seed=170 + T + d, with_dlse=with_dlse)
+    got = _run_gpu(inp, cot, dtype)
+    for b in range(B):
+        for h in range(H):
+            ref = oracle_gradients(*_head(inp, cot, b, h))
+            _compare(f"small {case}", dtype, got, ref, b, h)
+
+
+def test_backward_custom_scale_and_near_reflections():
+    """An explicit softmax scale, and betas close to 2 (near reflections)."""
+    dtype, d, B, H, T = "f32", 64, 1, 2, 256
+    inp = workloads.small(dtype, B, H, T, d, seed=91, fox=True, near2_frac=0.3)
+    cot = workloads.cotangents(dtype, B, H, T, d, seed=191)
+    got = _run_gpu(inp, cot, dtype, scale=0.3)
+    for h in range(H):
+        q, k, v, w, beta, logf, do, dl = _head(inp, cot, 0, h)
+        ref = oracle_gradients(q, k, v, w, beta, logf, do, dl, scale=0.3)
+        _compare("scale 0.3, near-2 betas", dtype, got, ref, 0, h)
+
+
+FULL = [
+    (workloads.MID_D64, [(0, 0), (15, 15)]),
+    (workloads.MID_D128_NEAR2, [(7, 3)]),
+    (workloads.FOX_D128, [(3, 7)]),
+    (workloads.LONG_D64, [(1, 15)]),
+]
+
+
+@pytest.mark.parametrize("wl,heads", FULL, ids=lambda x: getattr(x, "name", "heads"))
+def test_backward_full_size_sampled_heads(wl, heads):
+    _log(f"backward full size {wl.name}: generating inputs")
+    inp = workloads.generate(wl)
+    cot = workloads.cotangents(wl.dtype, wl.B, wl.H, wl.T, wl.d, seed=1000 + wl.seed)
+    t0 = time.time()
+    got = _run_gpu(inp, cot, wl.dtype)
+    _log(f"{wl.name}: GPU forward + backward done in {time.time() - t0:.1f} s")
+    for b, h in heads:
+        q, k, v, w, beta, logf, do, dl = _head(inp, cot, b, h)
+        import oracle
+        o, lse = oracle.path_attn(q, k, v, w, beta, logf)
+        t0 = time.time()
+        ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
+        _log(f"{wl.name}: oracle head ({b},{h}) in {time.time() - t0:.1f} s")
+        _compare(wl.name, wl.dtype, got, ref, b, h)

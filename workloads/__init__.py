@@ -159,3 +159,17 @@ def small(dtype: str, B: int, H: int, T: int, d: int, seed: int, *,
                   seed=seed, beta_sigma=beta_sigma, near2_frac=near2_frac,
                   fox=fox, q_scale=q_scale, beta_const=beta_const)
     return generate(wl)
+
+
+def cotangents(dtype: str, B: int, H: int, T: int, d: int, seed: int,
+               with_dlse: bool = True) -> dict:
+    """Seeded output gradients for the backward pass: dout ~ N(0, 1) of shape
+    [B, H, T, d] (stored like q: bf16-representable for bf16) and, if asked,
+    dlse ~ N(0, 1) of shape [B, H, T] in float32 (else None).  Drawn with
+    ``numpy.random.default_rng(seed)`` in the order dout, dlse."""
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    if dtype == "bf16":
+        dout = bf16_round(dout)
+    dlse = rng.standard_normal((B, H, T)).astype(np.float32) if with_dlse else None
+    return dict(dout=dout, dlse=dlse)
