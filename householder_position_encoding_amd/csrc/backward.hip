@@ -249,7 +249,11 @@ __global__ __launch_bounds__(256) void bwd_levels_kernel(const float *__restrict
 // ------------------------------------------------------------ diagonal blocks
 
 // One block per (bh, chunk): rowdot(dO, O), the diagonal block's weights and
-// gradients; starts dV (P^T dO) and dLambda (dlse - colsum dS) of the chunk.
+// gradients; starts dV (P^T dO) and, with the gate, dLambda (row sums minus
+// column sums of dS) of the chunk.  The row sums of dS equal dlse in exact
+// arithmetic, but taking them from the computed dS makes the rounding of
+// rowdot(dO, O) cancel in the suffix sums of dLambda: what remains of it in
+// d log f_t is weighted by the softmax mass on keys before t.
 template <typename E, int D, bool FOX>
 __global__ __launch_bounds__(256) void bwd_diag_kernel(
     const float *__restrict__ al, const E *__restrict__ v, const E *__restrict__ o,
@@ -315,10 +319,13 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
       dal_c[i * C + j] = scale * ds;
     }
   __syncthreads();
-  if (tid < C) {
-    float cs = 0.f;
-    for (int i = 0; i < C; ++i) cs += Ps[i * CP + tid];
-    dlam[row0 + tid] = rdl[tid] - cs;
+  if (FOX && tid < C) {   // dLambda_t = sum_j dS_tj - sum_i dS_it over the diagonal block
+    float cs = 0.f, rs = 0.f;
+    for (int i = 0; i < C; ++i) {
+      cs += Ps[i * CP + tid];
+      rs += Ps[tid * CP + i];
+    }
+    dlam[row0 + tid] = rs - cs;
   }
 }
 
@@ -332,7 +339,8 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(
     const float *__restrict__ dvec, const float *__restrict__ lam,
     const float *__restrict__ levels, const E *__restrict__ v, const float *__restrict__ m,
     float scale, float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dqpart,
-    float *__restrict__ gam, float *__restrict__ dkb, float *__restrict__ dmpart, int T) {
+    float *__restrict__ gam, float *__restrict__ dkb, float *__restrict__ dmpart,
+    float *__restrict__ rowpart, int T) {
   constexpr int DP = D + 1, CP = C + 1;
   // Qs | Os contiguous (later M, D x DP), Ks (later Khat[c-1]), Vs (later Gamma), Ps
   __shared__ float pool[2 * C * DP + 2 * C * DP + C * CP];
@@ -395,10 +403,15 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(
       Ps[i * CP + j] = p[r][s] * (acc[r][s] - rd[i] + rdl[i]);   // dS
     }
   __syncthreads();
-  if (tid < C) {   // dLambda_j -= sum_i dS_ij
+  if (FOX && tid < C) {   // dLambda_j -= sum_i dS_ij (key rows of chunk c')
     float cs = 0.f;
     for (int i = 0; i < C; ++i) cs += Ps[i * CP + tid];
     dlam[krow + tid] -= cs;
+  } else if (FOX && tid < 2 * C) {   // partial sum_j dS_ij (query rows of chunk c)
+    const int i = tid - C;
+    float rs = 0.f;
+    for (int j = 0; j < C; ++j) rs += Ps[i * CP + j];
+    rowpart[((size_t)bh * N + cp) * C + i] = rs;
   }
   float gacc[D / 64][4][4];
 #pragma unroll
@@ -468,25 +481,33 @@ __global__ __launch_bounds__(256) void bwd_sweep_kernel(
   }
 }
 
-// dQa_c = sum over c' < c of the partials; dM_{c-1} = sum over c' < c-1.
+// dQa_c = sum over c' < c of the partials; dM_{c-1} = sum over c' < c-1;
+// with the gate, dLambda of chunk c's rows += the partial row sums of dS.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(int c, const float *__restrict__ dqpart,
                                                          const float *__restrict__ dmpart,
+                                                         const float *__restrict__ rowpart,
                                                          float *__restrict__ dqa,
-                                                         float *__restrict__ dm, int T) {
+                                                         float *__restrict__ dm,
+                                                         float *__restrict__ dlam, int T) {
   const int N = T / C;
   const int bh = blockIdx.y;
-  const int per = C * D + D * D;
+  const int per = C * D + D * D + (rowpart ? C : 0);
   for (int idx = blockIdx.x * NT + threadIdx.x; idx < per; idx += gridDim.x * NT) {
     if (idx < C * D) {
       float s = 0.f;
       for (int cp = 0; cp < c; ++cp) s += dqpart[((size_t)bh * N + cp) * C * D + idx];
       dqa[((size_t)bh * T + (size_t)c * C) * D + idx] = s;
-    } else {
+    } else if (idx < C * D + D * D) {
       const int e = idx - C * D;
       float s = 0.f;
       for (int cp = 0; cp < c - 1; ++cp) s += dmpart[((size_t)bh * N + cp) * D * D + e];
       dm[((size_t)bh * N + (c - 1)) * D * D + e] = s;
+    } else {
+      const int i = idx - C * D - D * D;
+      float s = 0.f;
+      for (int cp = 0; cp < c; ++cp) s += rowpart[((size_t)bh * N + cp) * C + i];
+      dlam[(size_t)bh * T + (size_t)c * C + i] += s;
     }
   }
 }
@@ -769,6 +790,7 @@ BwdLayout bwd_layout(int B, int H, int T, int D) {
   L.dlam = take(BH * T);
   L.dqpart = take(BH * N * C * D);
   L.dmpart = take(BH * N * D * D);
+  L.rowpart = take(BH * N * C);
   L.dqa = take(BH * T * D);
   L.dkb = take(BH * T * D);
   L.dm = take(BH * N * D * D);
@@ -800,9 +822,10 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, hipStream_t s) {
   for (int c = N - 1; c >= 1; --c) {
     hipLaunchKernelGGL((bwd_sweep_kernel<E, D, FOX>), dim3(c * BH), dim3(NT), 0, s, c, f(L.qa),
                        (const E *)a.dout, a.lse, a.dlse, f(L.dvec), f(L.lam), f(L.levels), v, f(L.m),
-                       a.scale, f(L.dv), f(L.dlam), f(L.dqpart), f(L.gam), f(L.dkb), f(L.dmpart), T);
+                       a.scale, f(L.dv), f(L.dlam), f(L.dqpart), f(L.gam), f(L.dkb), f(L.dmpart),
+                       f(L.rowpart), T);
     hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(8, BH), dim3(NT), 0, s, c, f(L.dqpart),
-                       f(L.dmpart), f(L.dqa), f(L.dm), T);
+                       f(L.dmpart), FOX ? f(L.rowpart) : nullptr, f(L.dqa), f(L.dm), f(L.dlam), T);
   }
   const int nloc = BH * N < kLocalBlocks ? BH * N : kLocalBlocks;
   hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(nloc), dim3(NT), 0, s, q, k, w, a.beta,

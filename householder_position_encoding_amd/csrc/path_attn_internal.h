@@ -150,7 +150,7 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
 // Backward pass (backward.hip).  Workspace offsets in bytes; the key levels
 // of one head take 64*D*N(N-1)/2 floats, N = T/64.
 struct BwdLayout {
-  size_t qa, kb, m, al, lam, dvec, levels, gam, dv, dlam, dqpart, dmpart, dqa, dkb, dm, dal,
+  size_t qa, kb, m, al, lam, dvec, levels, gam, dv, dlam, dqpart, dmpart, rowpart, dqa, dkb, dm, dal,
       scratch, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D);
