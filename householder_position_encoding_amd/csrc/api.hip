@@ -271,7 +271,7 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
 
 extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
   if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK || T % kChunk != 0) return 0;
-  return bwd_layout(B, H, T, d).total;
+  return bwd_layout(B, H, T, d, dtype).total;
 }
 
 extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
@@ -291,7 +291,7 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
   for (const void *p : all)
     if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
-  if (!aligned(workspace, 256) || workspace_bytes < bwd_layout(B, H, T, d).total)
+  if (!aligned(workspace, 256) || workspace_bytes < bwd_layout(B, H, T, d, dtype).total)
     return PATH_ATTN_EINVAL;
   BwdArgs a{};
   a.q = q;

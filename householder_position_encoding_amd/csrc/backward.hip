@@ -38,155 +38,93 @@ constexpr int NT = 256;
 template <typename E>
 __device__ __forceinline__ float ld(const E *p) { return (float)*p; }
 
-// Offset (floats) of key level c, row block c', within one head's levels.
-__host__ __device__ inline size_t level_off(int c, int cp, int D) {
-  return ((size_t)c * (c - 1) / 2 + cp) * (size_t)C * D;
-}
-
 // ------------------------------------------------------------ chunk prep
 
-// One block per (bh, chunk): Qa, Kb (natural [T][D]), M ([N][D][D], M[a][b])
-// and Al ([N][64][64], zero above the diagonal) in float32.
+// Per-chunk float32 matrices kept from the preparation for the adjoint:
+// X = (I + N)^{-1}, U, A = lower(Q W^T), B = strictLower(W K^T), T2 = U B
+// (64 x 64 each) and U W (64 x D).
+__host__ __device__ constexpr size_t saved_floats(int D) { return 5 * 4096 + 64 * (size_t)D; }
+// Per-chunk adjoint intermediates: dA, dT2, dX, Y, dN, dB (64 x 64) and dUW (64 x D).
+__host__ __device__ constexpr size_t adj_floats(int D) { return 6 * 4096 + 64 * (size_t)D; }
+
+// One block per (bh, chunk), float32 matrix cores: Qa, Kb ([T][D]), M
+// ([N][D][D]), Al ([N][64][64], zero above the diagonal) and the saved
+// matrices of the chunk.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa, float *__restrict__ kb,
-    float *__restrict__ m, float *__restrict__ al, int T) {
-  constexpr int DP = D + 1, CP = C + 1;
-  __shared__ float Ws[C * DP];
-  __shared__ float Bs[C * DP];   // U W, later K
-  __shared__ float Qs[C * DP];
-  __shared__ float Us[C * CP];   // N, U, then T2
-  __shared__ float Xs[C * CP];   // X, then lower(Q W^T)
-  __shared__ float Ys[C * CP];   // strictLower(W K^T)
-  __shared__ float bs[C];
+    float *__restrict__ m, float *__restrict__ al, float *__restrict__ saved, int T) {
+  __shared__ float PX[kPanelFloats], PY[kPanelFloats];
+  __shared__ float tmp[768], bs[C];
   const int N = T / C;
-  const int bh = blockIdx.x / N, c = blockIdx.x % N;
+  const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
   const size_t row0 = (size_t)bh * T + (size_t)c * C;
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
-  float acc[4][4], acc2[4][4];
-
-  for (int idx = tid; idx < C * D; idx += NT) {
-    Ws[(idx / D) * DP + idx % D] = ld(w + row0 * D + idx);
-    Qs[(idx / D) * DP + idx % D] = ld(q + row0 * D + idx);
-  }
+  const int tid = threadIdx.x;
+  const E *Q = q + row0 * D, *K = k + row0 * D, *W = w + row0 * D;
+  float *Xg = saved + (size_t)chunk * saved_floats(D);
+  float *Ug = Xg + 4096, *Ag = Ug + 4096, *Bg = Ag + 4096, *T2g = Bg + 4096, *UWg = T2g + 4096;
+  float *qa_c = qa + row0 * D, *kb_c = kb + row0 * D;
+  float *m_c = m + (size_t)chunk * D * D, *al_c = al + (size_t)chunk * C * C;
   if (tid < C) bs[tid] = beta[row0 + tid];
+  f32x16 acc, acc2;
+
+  zero16(acc);   // G = W W^T -> N = strictLower(D G) -> X -> U
+  gmm<D, false, true>(acc, W, D, W, D, PX, PY, tid);
   __syncthreads();
-  tile_zero(acc);
-  tile_mm<D>(acc, Ws, DP, 1, Ws, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = r0 + 16 * r, j = c0 + 16 * s;
-      Us[i * CP + j] = j < i ? acc[r][s] * bs[i] : 0.f;   // N
-    }
+  tile_each(tid, [&](int i, int j, int r) { PX[i * 65 + j] = j < i ? bs[i] * acc[r] : 0.f; });
   __syncthreads();
-  if (tid < C) {   // X = (I + N)^{-1} below the diagonal, one column per lane
-    const int j = tid;
-    for (int i = j + 1; i < C; ++i) {
-      float x = -Us[i * CP + j];
-      for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Us[i * CP + t], Xs[t * CP + j], x);
-      Xs[i * CP + j] = x;
-    }
+  unit_lower_inverse(PX, PY, tmp, tid);
+  for (int idx = tid; idx < 4096; idx += NT) {
+    const int i = idx >> 6, j = idx & 63;
+    const float x = PY[i * 65 + j];
+    Xg[idx] = x;
+    Ug[idx] = j <= i ? x * bs[j] : 0.f;
   }
-  __syncthreads();
-  for (int idx = tid; idx < C * C; idx += NT) {
-    const int i = idx / C, j = idx % C;
-    Us[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);   // U
+#pragma unroll
+  for (int nb = 0; nb < D / 64; ++nb) {   // U W
+    zero16(acc);
+    gmm<64, false, false>(acc, Ug, 64, W + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) { UWg[i * D + 64 * nb + j] = acc[r]; });
   }
-  __syncthreads();
 #pragma unroll
-  for (int h = 0; h < D / 64; ++h) {   // U W
-    tile_zero(acc);
-    tile_mm<C>(acc, Us, CP, 1, Ws + 64 * h, DP, 1, r0, c0);
+  for (int ma = 0; ma < D / 64; ++ma)   // M = W^T (U W)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int nb = 0; nb < D / 64; ++nb) {
+      zero16(acc);
+      gmm<64, true, false>(acc, W + 64 * ma, D, UWg + 64 * nb, D, PX, PY, tid);
+      tile_each(tid, [&](int i, int j, int r) { m_c[(size_t)(64 * ma + i) * D + 64 * nb + j] = acc[r]; });
+    }
+  zero16(acc);   // A = lower(Q W^T)
+  gmm<D, false, true>(acc, Q, D, W, D, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { Ag[i * 64 + j] = j <= i ? acc[r] : 0.f; });
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Bs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] = acc[r][s];
+  for (int nb = 0; nb < D / 64; ++nb) {   // <-Q = Q - A (U W)
+    zero16(acc);
+    gmm<64, false, false>(acc, Ag, 64, UWg + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) {
+      qa_c[i * D + 64 * nb + j] = (float)Q[i * D + 64 * nb + j] - acc[r];
+    });
   }
-  __syncthreads();
-  float *m_c = m + ((size_t)bh * N + c) * D * D;   // M = W^T (U W)
+  zero16(acc);   // B = strictLower(W K^T)
+  gmm<D, false, true>(acc, W, D, K, D, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { Bg[i * 64 + j] = j < i ? acc[r] : 0.f; });
+  zero16(acc);   // T2 = U B
+  gmm<64, false, false>(acc, Ug, 64, Bg, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { T2g[i * 64 + j] = acc[r]; });
 #pragma unroll
-  for (int ha = 0; ha < D / 64; ++ha)
-#pragma unroll
-    for (int hb = 0; hb < D / 64; ++hb) {
-      tile_zero(acc);
-      tile_mm<C>(acc, Ws + 64 * ha, 1, DP, Bs + 64 * hb, DP, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          m_c[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * s] = acc[r][s];
-    }
-  tile_zero(acc);   // lower(Q W^T) into Xs
-  tile_mm<D>(acc, Qs, DP, 1, Ws, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = r0 + 16 * r, j = c0 + 16 * s;
-      Xs[i * CP + j] = j <= i ? acc[r][s] : 0.f;
-    }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {   // <-Q = Q - lower(Q W^T) U W
-    tile_zero(acc);
-    tile_mm<C>(acc, Xs, CP, 1, Bs + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
-        qa[(row0 + i) * D + col] = Qs[i * DP + col] - acc[r][s];
-      }
+  for (int nb = 0; nb < D / 64; ++nb) {   // ->K = K - T2^T W
+    zero16(acc);
+    gmm<64, true, false>(acc, T2g, 64, W + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) {
+      kb_c[i * D + 64 * nb + j] = (float)K[i * D + 64 * nb + j] - acc[r];
+    });
   }
-  __syncthreads();
-  for (int idx = tid; idx < C * D; idx += NT) Bs[(idx / D) * DP + idx % D] = ld(k + row0 * D + idx);
-  __syncthreads();
-  tile_zero(acc);   // strictLower(W K^T)
-  tile_mm<D>(acc, Ws, DP, 1, Bs, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int t = r0 + 16 * r, j = c0 + 16 * s;
-      Ys[t * CP + j] = t > j ? acc[r][s] : 0.f;
-    }
-  __syncthreads();
-  tile_zero(acc);   // T2 = U strictLower(W K^T), over U
-  tile_mm<C>(acc, Us, CP, 1, Ys, CP, 1, r0, c0);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) Us[(r0 + 16 * r) * CP + c0 + 16 * s] = acc[r][s];
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {   // ->K = K - T2^T W
-    tile_zero(acc);
-    tile_mm<C>(acc, Us, 1, CP, Ws + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int j = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
-        kb[(row0 + j) * D + col] = Bs[j * DP + col] - acc[r][s];
-      }
-  }
-  // Al = lower(Q K^T) - lower(Q W^T) T2
-  tile_zero(acc);
-  tile_mm<D>(acc, Qs, DP, 1, Bs, 1, DP, r0, c0);
-  tile_zero(acc2);
-  tile_mm<C>(acc2, Xs, CP, 1, Us, CP, 1, r0, c0);
-  float *al_c = al + ((size_t)bh * N + c) * C * C;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = r0 + 16 * r, j = c0 + 16 * s;
-      al_c[i * C + j] = j <= i ? acc[r][s] - acc2[r][s] : 0.f;
-    }
+  zero16(acc);   // Al = lower(Q K^T) - A T2
+  gmm<D, false, true>(acc, Q, D, K, D, PX, PY, tid);
+  zero16(acc2);
+  gmm<64, false, false>(acc2, Ag, 64, T2g, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { al_c[i * 64 + j] = j <= i ? acc[r] - acc2[r] : 0.f; });
 }
 
 // Lambda_t = sum_{1<=s<=t} log f_s (float64 running sum), one block per head.
@@ -199,50 +137,6 @@ __global__ __launch_bounds__(64) void bwd_gate_kernel(const float *__restrict__ 
   for (int t = 1; t < T; ++t) {
     acc += (double)logf[base + t];
     lam[base + t] = (float)acc;
-  }
-}
-
-// ------------------------------------------------------------ key levels
-
-// One block per (key chunk c', bh): walks the levels c = c'+1 .. N-1 writing
-// the aligned rows of chunk c' (Kb_{c'} at level c'+1, then times
-// (I - M_c)^T per level).  Blocks of early chunks (the longest walks) first.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_levels_kernel(const float *__restrict__ kb,
-                                                         const float *__restrict__ m,
-                                                         float *__restrict__ levels, int T,
-                                                         int BH) {
-  constexpr int DP = D + 1;
-  __shared__ float Xs[C * DP];
-  __shared__ float Ms[D * DP];
-  const int N = T / C;
-  const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
-  const size_t lev_head = (size_t)bh * level_off(N, 0, D);
-  for (int idx = tid; idx < C * D; idx += NT)
-    Xs[(idx / D) * DP + idx % D] = kb[((size_t)bh * T + (size_t)cp * C) * D + idx];
-  __syncthreads();
-  for (int c = cp + 1; c < N; ++c) {
-    float *dst = levels + lev_head + level_off(c, cp, D);
-    for (int idx = tid; idx < C * D; idx += NT) dst[idx] = Xs[(idx / D) * DP + idx % D];
-    if (c + 1 >= N) break;
-    const float *m_c = m + ((size_t)bh * N + c) * D * D;
-    for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
-    __syncthreads();
-    float acc[D / 64][4][4];
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {   // X M^T: B(k, j) = M[j][k]
-      tile_zero(acc[h]);
-      tile_mm<D>(acc[h], Xs, DP, 1, Ms + 64 * h * DP, 1, DP, r0, c0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Xs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] -= acc[h][r][s];
-    __syncthreads();
   }
 }
 
@@ -329,410 +223,130 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
   }
 }
 
-// ------------------------------------------------------------ sweep
-
-// Step c of the downward sweep: one block per (earlier key chunk c' < c, bh).
-template <typename E, int D, bool FOX>
-__global__ __launch_bounds__(256) void bwd_sweep_kernel(
-    int c, const float *__restrict__ qa, const E *__restrict__ dout,
-    const float *__restrict__ lse, const float *__restrict__ dlse,
-    const float *__restrict__ dvec, const float *__restrict__ lam,
-    const float *__restrict__ levels, const E *__restrict__ v, const float *__restrict__ m,
-    float scale, float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dqpart,
-    float *__restrict__ gam, float *__restrict__ dkb, float *__restrict__ dmpart,
-    float *__restrict__ rowpart, int T) {
-  constexpr int DP = D + 1, CP = C + 1;
-  // Qs | Os contiguous (later M, D x DP), Ks (later Khat[c-1]), Vs (later Gamma), Ps
-  __shared__ float pool[2 * C * DP + 2 * C * DP + C * CP];
-  __shared__ float rl[C], rd[C], rg[C], rdl[C], kg[C];
-  float *Qs = pool, *Os = pool + C * DP, *Ms = pool;
-  float *Ks = pool + 2 * C * DP, *Vs = pool + 3 * C * DP, *Gs = Vs;
-  float *Ps = pool + 4 * C * DP;
-  const int N = T / C;
-  const int cp = blockIdx.x % c, bh = blockIdx.x / c;
-  const size_t qrow = (size_t)bh * T + (size_t)c * C, krow = (size_t)bh * T + (size_t)cp * C;
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
-  const size_t lev_head = (size_t)bh * level_off(N, 0, D);
-  const float *khat = levels + lev_head + level_off(c, cp, D);
-
-  for (int idx = tid; idx < C * D; idx += NT) {
-    const int rr = idx / D, ee = idx % D;
-    Qs[rr * DP + ee] = qa[qrow * D + idx];
-    Os[rr * DP + ee] = ld(dout + qrow * D + idx);
-    Ks[rr * DP + ee] = khat[idx];
-    Vs[rr * DP + ee] = ld(v + krow * D + idx);
-  }
-  if (tid < C) {
-    rl[tid] = lse[qrow + tid];
-    rd[tid] = dvec[qrow + tid];
-    rdl[tid] = dlse ? dlse[qrow + tid] : 0.f;
-    rg[tid] = FOX ? lam[qrow + tid] : 0.f;
-    kg[tid] = FOX ? lam[krow + tid] : 0.f;
-  }
-  __syncthreads();
-  float acc[4][4], p[4][4];
-  tile_zero(acc);   // S = Qa Khat^T
-  tile_mm<D>(acc, Qs, DP, 1, Ks, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = r0 + 16 * r, j = c0 + 16 * s;
-      p[r][s] = __expf(scale * acc[r][s] + rg[i] - kg[j] - rl[i]);
-      Ps[i * CP + j] = p[r][s];
-    }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {   // dV_{c'} += P^T dO
-    tile_zero(acc);
-    tile_mm<C>(acc, Ps, 1, CP, Os + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dv[(krow + r0 + 16 * r) * D + 64 * h + c0 + 16 * s] += acc[r][s];
-  }
-  tile_zero(acc);   // dP = dO V^T
-  tile_mm<D>(acc, Os, DP, 1, Vs, 1, DP, r0, c0);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = r0 + 16 * r, j = c0 + 16 * s;
-      Ps[i * CP + j] = p[r][s] * (acc[r][s] - rd[i] + rdl[i]);   // dS
-    }
-  __syncthreads();
-  if (FOX && tid < C) {   // dLambda_j -= sum_i dS_ij (key rows of chunk c')
-    float cs = 0.f;
-    for (int i = 0; i < C; ++i) cs += Ps[i * CP + tid];
-    dlam[krow + tid] -= cs;
-  } else if (FOX && tid < 2 * C) {   // partial sum_j dS_ij (query rows of chunk c)
-    const int i = tid - C;
-    float rs = 0.f;
-    for (int j = 0; j < C; ++j) rs += Ps[i * CP + j];
-    rowpart[((size_t)bh * N + cp) * C + i] = rs;
-  }
-  float gacc[D / 64][4][4];
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {   // partial dQa_c = g Khat,  Gamma += g^T Qa
-    tile_zero(acc);
-    tile_mm<C>(acc, Ps, CP, 1, Ks + 64 * h, DP, 1, r0, c0);
-    float *dst = dqpart + ((size_t)bh * N + cp) * C * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dst[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = scale * acc[r][s];
-    tile_zero(gacc[h]);
-    tile_mm<C>(gacc[h], Ps, 1, CP, Qs + 64 * h, DP, 1, r0, c0);
-    float *gsrc = gam + krow * D;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        gacc[h][r][s] = gsrc[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] + scale * gacc[h][r][s];
-  }
-  if (cp == c - 1) {   // chunk c-1's rows are ->K_{c-1} at level c: final gradient
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          dkb[(krow + r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = gacc[h][r][s];
-    return;
-  }
-  // cross chunk c-1's transition: dM part = -Gamma^T Khat[c-1], Gamma (I - M)
-  __syncthreads();
-  const float *khp = levels + lev_head + level_off(c - 1, cp, D);
-  const float *m_c = m + ((size_t)bh * N + (c - 1)) * D * D;
-  for (int idx = tid; idx < D * D; idx += NT) Ms[(idx / D) * DP + idx % D] = m_c[idx];
-  for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = khp[idx];
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Gs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * s] = gacc[h][r][s];
-  __syncthreads();
-  float *mp = dmpart + ((size_t)bh * N + cp) * D * D;
-#pragma unroll
-  for (int ha = 0; ha < D / 64; ++ha)
-#pragma unroll
-    for (int hb = 0; hb < D / 64; ++hb) {
-      tile_zero(acc);
-      tile_mm<C>(acc, Gs + 64 * ha, 1, DP, Ks + 64 * hb, DP, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          mp[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * s] = -acc[r][s];
-    }
-  float *gdst = gam + krow * D;
-#pragma unroll
-  for (int h = 0; h < D / 64; ++h) {
-    tile_zero(acc);
-    tile_mm<D>(acc, Gs, DP, 1, Ms + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        gdst[(r0 + 16 * r) * D + 64 * h + c0 + 16 * s] = gacc[h][r][s] - acc[r][s];
-  }
-}
-
-// dQa_c = sum over c' < c of the partials; dM_{c-1} = sum over c' < c-1;
-// with the gate, dLambda of chunk c's rows += the partial row sums of dS.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(int c, const float *__restrict__ dqpart,
-                                                         const float *__restrict__ dmpart,
-                                                         const float *__restrict__ rowpart,
-                                                         float *__restrict__ dqa,
-                                                         float *__restrict__ dm,
-                                                         float *__restrict__ dlam, int T) {
-  const int N = T / C;
-  const int bh = blockIdx.y;
-  const int per = C * D + D * D + (rowpart ? C : 0);
-  for (int idx = blockIdx.x * NT + threadIdx.x; idx < per; idx += gridDim.x * NT) {
-    if (idx < C * D) {
-      float s = 0.f;
-      for (int cp = 0; cp < c; ++cp) s += dqpart[((size_t)bh * N + cp) * C * D + idx];
-      dqa[((size_t)bh * T + (size_t)c * C) * D + idx] = s;
-    } else if (idx < C * D + D * D) {
-      const int e = idx - C * D;
-      float s = 0.f;
-      for (int cp = 0; cp < c - 1; ++cp) s += dmpart[((size_t)bh * N + cp) * D * D + e];
-      dm[((size_t)bh * N + (c - 1)) * D * D + e] = s;
-    } else {
-      const int i = idx - C * D - D * D;
-      float s = 0.f;
-      for (int cp = 0; cp < c; ++cp) s += rowpart[((size_t)bh * N + cp) * C + i];
-      dlam[(size_t)bh * T + (size_t)c * C + i] += s;
-    }
-  }
-}
-
 // ------------------------------------------------------------ local adjoint
 
-// One block per (bh, chunk) (grid-stride over chunks with a per-block scratch
-// area): gradients of the chunk's inputs from those of its UT quantities.
-//   dA   = lower(-dQa (UW)^T - dAl T2^T)          A = lower(Q W^T)
+// One block per (bh, chunk), float32 matrix cores: gradients of the chunk's
+// inputs from those of its UT quantities (dQa, dKb, dM, dAl), with
+// A = lower(Q W^T), B = strictLower(W K^T), T2 = U B, N = strictLower(D G),
+// G = W W^T, D = diag(beta), X = (I + N)^{-1}, U = X D:
+//   dA   = lower(-dQa (UW)^T - dAl T2^T)
 //   dUW  = -A^T dQa + W dM
 //   dT2  = -W dKb^T - A^T dAl
-//   dU   = dUW W^T + dT2 B^T,  dB = strictLower(U^T dT2)   B = strictLower(W K^T)
-//   dX   = lower(dU) D,  dbeta_j += sum_i X_ij dU_ij        U = X D
-//   dN   = strictLower(-X^T dX X^T)                         X = (I + N)^{-1}
-//   dbeta_i += sum_{j<i} dN_ij G_ij,  dG = strictLower(D dN)  N = strictLower(D G)
+//   dU   = lower(dUW W^T + dT2 B^T),  dB = strictLower(U^T dT2)
+//   dX   = dU D,  dbeta_j += sum_i X_ij dU_ij
+//   dN   = strictLower(-X^T dX X^T)
+//   dG   = D dN,  dbeta_i += sum_j dN_ij G_ij = w_i . (dN W)_i
 //   dQ   = dQa + dAl K + dA W
 //   dK   = dKb + dAl^T Q + dB^T W
-//   dW   = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + (dG + dG^T) W
+//   dW   = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + dG W + dG^T W
 template <typename E, int D>
-__global__ __launch_bounds__(256) void bwd_local_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_local_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
     const float *__restrict__ beta, const float *__restrict__ dqa,
     const float *__restrict__ dkb, const float *__restrict__ dm, const float *__restrict__ dal,
-    float *__restrict__ scratch, E *__restrict__ dq, E *__restrict__ dk, E *__restrict__ dw,
-    float *__restrict__ dbeta, int T, int n_chunks_total) {
-  constexpr int CP = C + 1;
-  // scratch per block (floats): R-sized = C*D, S-sized = C*C
-  constexpr int R = C * D, S = C * C;
-  float *base = scratch + (size_t)blockIdx.x * (6 * R + 11 * S);
-  float *Wg = base, *Qg = Wg + R, *Kg = Qg + R, *UWg = Kg + R, *dUWg = UWg + R, *Tmp = dUWg + R;
-  float *Gg = Tmp + R, *Xg = Gg + S, *Ug = Xg + S, *Ag = Ug + S, *Bg = Ag + S, *T2g = Bg + S;
-  float *dAg = T2g + S, *dT2g = dAg + S, *dUg = dT2g + S, *dBg = dUg + S, *dNg = dBg + S;
-  __shared__ float Ns[C * CP], Xs[C * CP];
+    const float *__restrict__ saved, float *__restrict__ adj, E *__restrict__ dq,
+    E *__restrict__ dk, E *__restrict__ dw, float *__restrict__ dbeta, int T) {
+  __shared__ float PX[kPanelFloats], PY[kPanelFloats];
   __shared__ float bs[C], dbs[C];
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
   const int N = T / C;
-  float acc[4][4];
-
-  // store a 64 x 64 tile (columns col0..) into a row-major matrix of row length ld
-  auto put = [&](float *dst, int ld, int col0, float (&a)[4][4], float sgn, int mask) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i = r0 + 16 * r, j = c0 + 16 * s;
-        const bool keep = mask == 0 || (mask == 1 && j <= i) || (mask == 2 && j < i);
-        dst[i * ld + col0 + j] = keep ? sgn * a[r][s] : 0.f;
-      }
-  };
-
-  for (int blk = blockIdx.x; blk < n_chunks_total; blk += gridDim.x) {
-    const int bh = blk / N, c = blk % N;
-    const size_t row0 = (size_t)bh * T + (size_t)c * C;
-    const float *dQa = dqa + row0 * D, *dKb = dkb + row0 * D;
-    const float *dM = dm + ((size_t)bh * N + c) * D * D;
-    const float *dAl = dal + ((size_t)bh * N + c) * C * C;
-    __syncthreads();
-    for (int idx = tid; idx < R; idx += NT) {
-      Wg[idx] = ld(w + row0 * D + idx);
-      Qg[idx] = ld(q + row0 * D + idx);
-      Kg[idx] = ld(k + row0 * D + idx);
-    }
-    if (tid < C) {
-      bs[tid] = beta[row0 + tid];
-      dbs[tid] = 0.f;
-    }
-    __syncthreads();
-    // G = W W^T, N, X, U
-    tile_zero(acc);
-    tile_mm<D>(acc, Wg, D, 1, Wg, 1, D, r0, c0);
-    put(Gg, C, 0, acc, 1.f, 0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int i = r0 + 16 * r, j = c0 + 16 * s;
-        Ns[i * CP + j] = j < i ? acc[r][s] * bs[i] : 0.f;
-        Xs[i * CP + j] = j == i ? 1.f : 0.f;
-      }
-    __syncthreads();
-    if (tid < C) {
-      const int j = tid;
-      for (int i = j + 1; i < C; ++i) {
-        float x = -Ns[i * CP + j];
-        for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Ns[i * CP + t], Xs[t * CP + j], x);
-        Xs[i * CP + j] = x;
-      }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < S; idx += NT) {
-      const int i = idx / C, j = idx % C;
-      Xg[idx] = Xs[i * CP + j];
-      Ug[idx] = j <= i ? Xs[i * CP + j] * bs[j] : 0.f;
-    }
-    __syncthreads();
-    // UW = U W, A = lower(Q W^T), B = strictLower(W K^T)
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {
-      tile_zero(acc);
-      tile_mm<C>(acc, Ug, C, 1, Wg + 64 * h, D, 1, r0, c0);
-      put(UWg, D, 64 * h, acc, 1.f, 0);
-    }
-    tile_zero(acc);
-    tile_mm<D>(acc, Qg, D, 1, Wg, 1, D, r0, c0);
-    put(Ag, C, 0, acc, 1.f, 1);
-    tile_zero(acc);
-    tile_mm<D>(acc, Wg, D, 1, Kg, 1, D, r0, c0);
-    put(Bg, C, 0, acc, 1.f, 2);
-    __syncthreads();
-    tile_zero(acc);   // T2 = U B
-    tile_mm<C>(acc, Ug, C, 1, Bg, C, 1, r0, c0);
-    put(T2g, C, 0, acc, 1.f, 0);
-    __syncthreads();
-    // dA = lower(-dQa UW^T - dAl T2^T)
-    tile_zero(acc);
-    tile_mm<D>(acc, dQa, D, 1, UWg, 1, D, r0, c0);
-    tile_mm<C>(acc, dAl, C, 1, T2g, 1, C, r0, c0);
-    put(dAg, C, 0, acc, -1.f, 1);
-    // dUW = -A^T dQa + W dM
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {
-      float a2[4][4];
-      tile_zero(acc);
-      tile_mm<C>(acc, Ag, 1, C, dQa + 64 * h, D, 1, r0, c0);
-      tile_zero(a2);
-      tile_mm<D>(a2, Wg, D, 1, dM + 64 * h, D, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[r][s] = a2[r][s] - acc[r][s];
-      put(dUWg, D, 64 * h, acc, 1.f, 0);
-    }
-    // dT2 = -W dKb^T - A^T dAl
-    tile_zero(acc);
-    tile_mm<D>(acc, Wg, D, 1, dKb, 1, D, r0, c0);
-    tile_mm<C>(acc, Ag, 1, C, dAl, C, 1, r0, c0);
-    put(dT2g, C, 0, acc, -1.f, 0);
-    __syncthreads();
-    // dU = dUW W^T + dT2 B^T (lower part), dB = strictLower(U^T dT2)
-    tile_zero(acc);
-    tile_mm<D>(acc, dUWg, D, 1, Wg, 1, D, r0, c0);
-    tile_mm<C>(acc, dT2g, C, 1, Bg, 1, C, r0, c0);
-    put(dUg, C, 0, acc, 1.f, 1);
-    tile_zero(acc);
-    tile_mm<C>(acc, Ug, 1, C, dT2g, C, 1, r0, c0);
-    put(dBg, C, 0, acc, 1.f, 2);
-    __syncthreads();
-    // dbeta_j += sum_i X_ij dU_ij; dX = dU D (into Tmp as 64 x 64)
-    if (tid < C) {
-      float sacc = 0.f;
-      for (int i = 0; i < C; ++i) sacc += Xg[i * C + tid] * dUg[i * C + tid];
-      dbs[tid] += sacc;
-    }
-    for (int idx = tid; idx < S; idx += NT) Tmp[idx] = dUg[idx] * bs[idx % C];
-    __syncthreads();
-    // dN = strictLower(-X^T dX X^T): first Y = dX X^T (into dNg), then -X^T Y
-    tile_zero(acc);
-    tile_mm<C>(acc, Tmp, C, 1, Xg, 1, C, r0, c0);
-    put(dNg, C, 0, acc, 1.f, 0);
-    __syncthreads();
-    tile_zero(acc);
-    tile_mm<C>(acc, Xg, 1, C, dNg, C, 1, r0, c0);
-    __syncthreads();
-    put(dNg, C, 0, acc, -1.f, 2);
-    __syncthreads();
-    // dbeta_i += sum_{j<i} dN_ij G_ij; dG = D dN (strict lower, into Tmp)
-    if (tid < C) {
-      float sacc = 0.f;
-      for (int j = 0; j < tid; ++j) sacc += dNg[tid * C + j] * Gg[tid * C + j];
-      dbs[tid] += sacc;
-    }
-    for (int idx = tid; idx < S; idx += NT) Tmp[idx] = dNg[idx] * bs[idx / C];
-    __syncthreads();
-    // dQ = dQa + dAl K + dA W
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {
-      tile_zero(acc);
-      tile_mm<C>(acc, dAl, C, 1, Kg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, dAg, C, 1, Wg + 64 * h, D, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
-          dq[(row0 + i) * D + col] = (E)(dQa[i * D + col] + acc[r][s]);
-        }
-    }
-    // dK = dKb + dAl^T Q + dB^T W
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {
-      tile_zero(acc);
-      tile_mm<C>(acc, dAl, 1, C, Qg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, dBg, 1, C, Wg + 64 * h, D, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
-          dk[(row0 + i) * D + col] = (E)(dKb[i * D + col] + acc[r][s]);
-        }
-    }
-    // dW = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + (dG + dG^T) W
-#pragma unroll
-    for (int h = 0; h < D / 64; ++h) {
-      float a2[4][4];
-      tile_zero(acc);
-      tile_mm<D>(acc, UWg, D, 1, dM + 64 * h * D, 1, D, r0, c0);
-      tile_mm<C>(acc, Ug, 1, C, dUWg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, dAg, 1, C, Qg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, dBg, C, 1, Kg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, Tmp, C, 1, Wg + 64 * h, D, 1, r0, c0);
-      tile_mm<C>(acc, Tmp, 1, C, Wg + 64 * h, D, 1, r0, c0);
-      tile_zero(a2);
-      tile_mm<C>(a2, T2g, C, 1, dKb + 64 * h, D, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int i = r0 + 16 * r, col = 64 * h + c0 + 16 * s;
-          dw[(row0 + i) * D + col] = (E)(acc[r][s] - a2[r][s]);
-        }
-    }
-    __syncthreads();
-    if (tid < C) dbeta[row0 + tid] = dbs[tid];
+  const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
+  const size_t row0 = (size_t)bh * T + (size_t)c * C;
+  const int tid = threadIdx.x;
+  const E *Q = q + row0 * D, *K = k + row0 * D, *W = w + row0 * D;
+  const float *dQa = dqa + row0 * D, *dKb = dkb + row0 * D;
+  const float *dM = dm + (size_t)chunk * D * D, *dAl = dal + (size_t)chunk * C * C;
+  const float *Xg = saved + (size_t)chunk * saved_floats(D);
+  const float *Ug = Xg + 4096, *Ag = Ug + 4096, *Bg = Ag + 4096, *T2g = Bg + 4096, *UWg = T2g + 4096;
+  float *dAg = adj + (size_t)chunk * adj_floats(D);
+  float *dT2g = dAg + 4096, *dXg = dT2g + 4096, *Yg = dXg + 4096, *dNg = Yg + 4096, *dBg = dNg + 4096;
+  float *dUWg = dBg + 4096;
+  if (tid < C) {
+    bs[tid] = beta[row0 + tid];
+    dbs[tid] = 0.f;
   }
+  f32x16 acc, acc2;
+
+  zero16(acc);   // dA
+  gmm<D, false, true>(acc, dQa, D, UWg, D, PX, PY, tid);
+  gmm<64, false, true>(acc, dAl, 64, T2g, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { dAg[i * 64 + j] = j <= i ? -acc[r] : 0.f; });
+#pragma unroll
+  for (int nb = 0; nb < D / 64; ++nb) {   // dUW
+    zero16(acc);
+    gmm<D, false, false>(acc, W, D, dM + 64 * nb, D, PX, PY, tid);
+    zero16(acc2);
+    gmm<64, true, false>(acc2, Ag, 64, dQa + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) { dUWg[i * D + 64 * nb + j] = acc[r] - acc2[r]; });
+  }
+  zero16(acc);   // dT2
+  gmm<D, false, true>(acc, W, D, dKb, D, PX, PY, tid);
+  gmm<64, true, false>(acc, Ag, 64, dAl, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { dT2g[i * 64 + j] = -acc[r]; });
+  zero16(acc);   // dU -> dX, dbeta_j
+  gmm<D, false, true>(acc, dUWg, D, W, D, PX, PY, tid);
+  gmm<64, false, true>(acc, dT2g, 64, Bg, 64, PX, PY, tid);
+  {
+    float part = 0.f;
+    int col = 0;
+    tile_each(tid, [&](int i, int j, int r) {
+      const float du = j <= i ? acc[r] : 0.f;
+      part = __builtin_fmaf(Xg[i * 64 + j], du, part);
+      col = j;
+      dXg[i * 64 + j] = du * bs[j];
+    });
+    atomicAdd(&dbs[col], part);
+  }
+  zero16(acc);   // dB
+  gmm<64, true, false>(acc, Ug, 64, dT2g, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { dBg[i * 64 + j] = j < i ? acc[r] : 0.f; });
+  zero16(acc);   // Y = dX X^T
+  gmm<64, false, true>(acc, dXg, 64, Xg, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { Yg[i * 64 + j] = acc[r]; });
+  zero16(acc);   // dN = strictLower(-X^T Y)
+  gmm<64, true, false>(acc, Xg, 64, Yg, 64, PX, PY, tid);
+  tile_each(tid, [&](int i, int j, int r) { dNg[i * 64 + j] = j < i ? -acc[r] : 0.f; });
+#pragma unroll
+  for (int nb = 0; nb < D / 64; ++nb) {   // dQ
+    zero16(acc);
+    gmm<64, false, false>(acc, dAl, 64, K + 64 * nb, D, PX, PY, tid);
+    gmm<64, false, false>(acc, dAg, 64, W + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) {
+      const size_t o = (size_t)i * D + 64 * nb + j;
+      dq[row0 * D + o] = (E)(dQa[o] + acc[r]);
+    });
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 64; ++nb) {   // dK
+    zero16(acc);
+    gmm<64, true, false>(acc, dAl, 64, Q + 64 * nb, D, PX, PY, tid);
+    gmm<64, true, false>(acc, dBg, 64, W + 64 * nb, D, PX, PY, tid);
+    tile_each(tid, [&](int i, int j, int r) {
+      const size_t o = (size_t)i * D + 64 * nb + j;
+      dk[row0 * D + o] = (E)(dKb[o] + acc[r]);
+    });
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 64; ++nb) {   // dW
+    f32x16 accn;
+    zero16(accn);   // dN W
+    gmm<64, false, false>(accn, dNg, 64, W + 64 * nb, D, PX, PY, tid);
+    zero16(acc2);   // T2 dKb
+    gmm<64, false, false>(acc2, T2g, 64, dKb + 64 * nb, D, PX, PY, tid);
+    zero16(acc);
+    gmm<64, true, false>(acc, dNg, 64, W + 64 * nb, D, PX, PY, tid, bs);   // dG^T W
+    gmm<D, false, true>(acc, UWg, D, dM + (size_t)64 * nb * D, D, PX, PY, tid);   // UW dM^T
+    gmm<64, true, false>(acc, Ug, 64, dUWg + 64 * nb, D, PX, PY, tid);   // U^T dUW
+    gmm<64, true, false>(acc, dAg, 64, Q + 64 * nb, D, PX, PY, tid);     // dA^T Q
+    gmm<64, false, false>(acc, dBg, 64, K + 64 * nb, D, PX, PY, tid);    // dB K
+    tile_each(tid, [&](int i, int j, int r) {
+      const size_t o = (size_t)i * D + 64 * nb + j;
+      const float wv = (float)W[o];
+      atomicAdd(&dbs[i], wv * accn[r]);
+      dw[row0 * D + o] = (E)(acc[r] - acc2[r] + bs[i] * accn[r]);
+    });
+  }
+  __syncthreads();
+  if (tid < C) dbeta[row0 + tid] = dbs[tid];
 }
 
 // dv = dV in the input dtype; d log f_t = sum_{i >= t} dLambda_i (t >= 1),
@@ -755,22 +369,11 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(const float *__restrict_
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT) p[i] = 0.f;
-}
-
-void zero(float *p, size_t n, hipStream_t s) {
-  const size_t blocks = (n + NT - 1) / NT;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096)),
-                     dim3(NT), 0, s, p, n);
-}
-
-constexpr int kLocalBlocks = 1024;
-
 }  // namespace
 
-BwdLayout bwd_layout(int B, int H, int T, int D) {
+BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
   const size_t BH = (size_t)B * H, N = (size_t)T / C;
+  const size_t esize = dtype == 1 ? 2 : 4;
   BwdLayout L;
   size_t off = 0;
   auto take = [&](size_t floats) {
@@ -784,53 +387,56 @@ BwdLayout bwd_layout(int B, int H, int T, int D) {
   L.al = take(BH * N * C * C);
   L.lam = take(BH * T);
   L.dvec = take(BH * T);
-  L.levels = take(BH * level_off((int)N, 0, D));
-  L.gam = take(BH * T * D);
+  L.levels = take((bwd_levels_elems((int)BH, T, D) * esize + 3) / 4);
+  L.dmpart = take(bwd_dmpart_floats(dtype, (int)BH, T, D));
   L.dv = take(BH * T * D);
   L.dlam = take(BH * T);
-  L.dqpart = take(BH * N * C * D);
-  L.dmpart = take(BH * N * D * D);
-  L.rowpart = take(BH * N * C);
   L.dqa = take(BH * T * D);
   L.dkb = take(BH * T * D);
   L.dm = take(BH * N * D * D);
   L.dal = take(BH * N * C * C);
-  L.scratch = take((size_t)kLocalBlocks * (6 * C * D + 11 * C * C));
+  L.saved = take(BH * N * saved_floats(D));
+  L.adj = take(BH * N * adj_floats(D));
   L.total = off;
   return L;
 }
 
 template <typename E, int D, bool FOX>
-hipError_t bwd_t(const BwdArgs &a, char *ws, hipStream_t s) {
-  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D);
+hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
+  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D, dtype);
   const int BH = a.B * a.H, T = a.T, N = T / C;
   auto f = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
   const E *q = (const E *)a.q, *k = (const E *)a.k, *v = (const E *)a.v, *w = (const E *)a.w;
   hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
-                     f(L.qa), f(L.kb), f(L.m), f(L.al), T);
+                     f(L.qa), f(L.kb), f(L.m), f(L.al), f(L.saved), T);
   if (FOX) hipLaunchKernelGGL(bwd_gate_kernel, dim3(BH), dim3(64), 0, s, a.logf, f(L.lam), T);
-  if (N > 1)
-    hipLaunchKernelGGL((bwd_levels_kernel<D>), dim3(BH * (N - 1)), dim3(NT), 0, s, f(L.kb), f(L.m),
-                       f(L.levels), T, BH);
-  zero(f(L.gam), (size_t)BH * T * D, s);
-  zero(f(L.dqa), (size_t)BH * T * D, s);   // chunk 0 has no earlier keys: its dQa stays zero
-  zero(f(L.dkb), (size_t)BH * T * D, s);
-  zero(f(L.dm), (size_t)BH * N * D * D, s);
   hipLaunchKernelGGL((bwd_diag_kernel<E, D, FOX>), dim3(BH * N), dim3(NT), 0, s, f(L.al), v,
                      (const E *)a.out, (const E *)a.dout, a.lse, a.dlse, f(L.lam), a.scale, f(L.dal),
                      f(L.dv), f(L.dlam), f(L.dvec), T);
-  for (int c = N - 1; c >= 1; --c) {
-    hipLaunchKernelGGL((bwd_sweep_kernel<E, D, FOX>), dim3(c * BH), dim3(NT), 0, s, c, f(L.qa),
-                       (const E *)a.dout, a.lse, a.dlse, f(L.dvec), f(L.lam), f(L.levels), v, f(L.m),
-                       a.scale, f(L.dv), f(L.dlam), f(L.dqpart), f(L.gam), f(L.dkb), f(L.dmpart),
-                       f(L.rowpart), T);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(8, BH), dim3(NT), 0, s, c, f(L.dqpart),
-                       f(L.dmpart), FOX ? f(L.rowpart) : nullptr, f(L.dqa), f(L.dm), f(L.dlam), T);
-  }
-  const int nloc = BH * N < kLocalBlocks ? BH * N : kLocalBlocks;
-  hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(nloc), dim3(NT), 0, s, q, k, w, a.beta,
-                     f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.scratch), (E *)a.dq, (E *)a.dk,
-                     (E *)a.dw, a.dbeta, T, BH * N);
+  SweepArgs sa{};
+  sa.qa = f(L.qa);
+  sa.kb = f(L.kb);
+  sa.m = f(L.m);
+  sa.dout = a.dout;
+  sa.v = a.v;
+  sa.lse = a.lse;
+  sa.dlse = a.dlse;
+  sa.dvec = f(L.dvec);
+  sa.lam = f(L.lam);
+  sa.levels = ws + L.levels;
+  sa.dmpart = f(L.dmpart);
+  sa.dqa = f(L.dqa);
+  sa.dkb = f(L.dkb);
+  sa.dv = f(L.dv);
+  sa.dlam = f(L.dlam);
+  sa.dm = f(L.dm);
+  sa.scale = a.scale;
+  sa.BH = BH;
+  sa.T = T;
+  if (launch_bwd_sweep(dtype, D, FOX, sa, s) != hipSuccess) return hipGetLastError();
+  hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
+                     f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.saved), f(L.adj), (E *)a.dq,
+                     (E *)a.dk, (E *)a.dw, a.dbeta, T);
   hipLaunchKernelGGL((bwd_final_kernel<E>), dim3(BH), dim3(NT), 0, s, f(L.dv), (E *)a.dv, f(L.dlam),
                      FOX ? a.dlogf : nullptr, T, D);
   return hipGetLastError();
@@ -840,11 +446,13 @@ hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipSt
   char *ws = static_cast<char *>(workspace);
   const bool fox = a.logf != nullptr;
   if (dtype == 1) {
-    if (D == 64) return fox ? bwd_t<__bf16, 64, true>(a, ws, s) : bwd_t<__bf16, 64, false>(a, ws, s);
-    return fox ? bwd_t<__bf16, 128, true>(a, ws, s) : bwd_t<__bf16, 128, false>(a, ws, s);
+    if (D == 64)
+      return fox ? bwd_t<__bf16, 64, true>(a, ws, dtype, s) : bwd_t<__bf16, 64, false>(a, ws, dtype, s);
+    return fox ? bwd_t<__bf16, 128, true>(a, ws, dtype, s) : bwd_t<__bf16, 128, false>(a, ws, dtype, s);
   }
-  if (D == 64) return fox ? bwd_t<float, 64, true>(a, ws, s) : bwd_t<float, 64, false>(a, ws, s);
-  return fox ? bwd_t<float, 128, true>(a, ws, s) : bwd_t<float, 128, false>(a, ws, s);
+  if (D == 64)
+    return fox ? bwd_t<float, 64, true>(a, ws, dtype, s) : bwd_t<float, 64, false>(a, ws, dtype, s);
+  return fox ? bwd_t<float, 128, true>(a, ws, dtype, s) : bwd_t<float, 128, false>(a, ws, dtype, s);
 }
 
 }  // namespace pathattn

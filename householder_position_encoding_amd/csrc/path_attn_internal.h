@@ -147,13 +147,28 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
                               void *out, float *lse, float *part, int BH, int t, int T_cap,
                               float sl2, hipStream_t s);
 
-// Backward pass (backward.hip).  Workspace offsets in bytes; the key levels
-// of one head take 64*D*N(N-1)/2 floats, N = T/64.
+// Backward pass (backward.hip, bwd_sweep.hip).  Workspace offsets in bytes;
+// the key levels of one head take 64*D*N(N-1)/2 elements of the input dtype,
+// N = T/64.
 struct BwdLayout {
-  size_t qa, kb, m, al, lam, dvec, levels, gam, dv, dlam, dqpart, dmpart, rowpart, dqa, dkb, dm, dal,
-      scratch, total;
+  size_t qa, kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, total;
 };
-BwdLayout bwd_layout(int B, int H, int T, int D);
+BwdLayout bwd_layout(int B, int H, int T, int D, int dtype);
+size_t bwd_levels_elems(int BH, int T, int D);
+size_t bwd_dmpart_floats(int dtype, int BH, int T, int D);
+
+// The quadratic part (bwd_sweep.hip): key levels, dQa (+ dLambda row sums),
+// dKb, dV (+= onto the diagonal part), dLambda column sums, dM.
+struct SweepArgs {
+  const float *qa, *kb, *m;
+  const void *dout, *v;
+  const float *lse, *dlse, *dvec, *lam;
+  void *levels;
+  float *dmpart, *dqa, *dkb, *dv, *dlam, *dm;
+  float scale;
+  int BH, T;
+};
+hipError_t launch_bwd_sweep(int dtype, int D, bool fox, const SweepArgs &a, hipStream_t s);
 
 struct BwdArgs {
   const void *q, *k, *v, *w;

@@ -1,9 +1,12 @@
-// tile_fp32.h -- float32 4 x 4 register tiles of 64 x 64 products with
-// operands in LDS or global memory (256 threads: thread t owns rows
-// t/16 + 16 r and columns t%16 + 16 s).  Used by the prefill alignment and
-// the backward pass, whose per-chunk algebra runs in float32 on the vector
-// units.
+// tile_fp32.h -- float32 products of 64 x 64 blocks for 256-thread blocks:
+// 4 x 4 register tiles on the vector units (thread t owns rows t/16 + 16 r
+// and columns t%16 + 16 s), and 32 x 32 tiles on the float32 matrix cores with
+// operands staged through LDS panels; plus the blocked unit-triangular
+// inverse of the chunk algebra.  Used by the prefill alignment and the
+// backward pass, whose per-chunk algebra runs in float32.
 #pragma once
+
+#include "path_attn_internal.h"
 
 namespace pathattn {
 
@@ -33,6 +36,119 @@ __device__ __forceinline__ void tile_zero(float (&acc)[4][4]) {
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+}
+
+}  // namespace pathattn
+
+namespace pathattn {
+
+// ---------------------------------------------------------------------------
+// float32 matrix-core products of 64 x 64 blocks (v_mfma_f32_32x32x2f32) with
+// both operands staged through LDS panels, for 256-thread blocks: wave w owns
+// the 32 x 32 output tile (w >> 1, w & 1).  In a tile, lane l register r
+// holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 (acc_row).
+
+// Floats of one panel: a 64 x K block (K <= 128) or a K x 64 block, each
+// stored with pitch (columns + 1) so row and column reads are conflict-free.
+constexpr int kPanelFloats = 128 * 65;
+
+// dst[r][c] = src[r * ld + c] (times rscale[r] if given), r < rows, c < cols.
+template <typename T>
+__device__ __forceinline__ void load_panel(float *dst, const T *src, int ld, int rows, int cols,
+                                           const float *rscale, int tid) {
+  const int pitch = cols + 1;
+  for (int idx = tid; idx < rows * cols; idx += 256) {
+    const int r = idx / cols, c = idx - r * cols;
+    float v = (float)src[(size_t)r * ld + c];
+    if (rscale) v *= rscale[r];
+    dst[r * pitch + c] = v;
+  }
+}
+
+// acc += op(X)[64 x K] op(Y)[K x 64] for this wave's tile, X and Y row-major
+// in global memory:  op(X) = X (a 64 x K block) or, with TX, X^T (X a K x 64
+// block); op(Y) = Y (a K x 64 block) or, with TY, Y^T (Y a 64 x K block).
+// yscale (optional, not with TY) multiplies row k of Y.  Starts and ends with
+// the block-wide barriers that make the panels (and earlier global writes of
+// the block) safe to reuse.
+template <int K, bool TX, bool TY, typename TXe, typename TYe>
+__device__ __forceinline__ void gmm(f32x16 &acc, const TXe *X, int ldx, const TYe *Y, int ldy,
+                                    float *PX, float *PY, int tid,
+                                    const float *yscale = nullptr) {
+  __syncthreads();
+  if (TX) load_panel(PX, X, ldx, K, 64, nullptr, tid);
+  else load_panel(PX, X, ldx, 64, K, nullptr, tid);
+  if (TY) load_panel(PY, Y, ldy, 64, K, nullptr, tid);
+  else load_panel(PY, Y, ldy, K, 64, yscale, tid);
+  __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6, i = lane & 31, k0 = lane >> 5;
+  constexpr int a_rs = TX ? 1 : K + 1, a_cs = TX ? 65 : 1;
+  constexpr int b_rs = TY ? 1 : 65, b_cs = TY ? K + 1 : 1;
+  const float *pa = PX + (32 * (wv >> 1) + i) * a_rs + k0 * a_cs;
+  const float *pb = PY + k0 * b_rs + (32 * (wv & 1) + i) * b_cs;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[k * a_cs], pb[k * b_rs], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero16(f32x16 &a) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = 0.f;
+}
+
+// f(row, col, r) for each of this wave's 16 tile elements (acc[r] is element
+// (row, col) of the 64 x 64 block).
+template <typename F>
+__device__ __forceinline__ void tile_each(int tid, F f) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const int col = 32 * (wv & 1) + (lane & 31), g = lane >> 5, row0 = 32 * (wv >> 1);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) f(row0 + acc_row(r, g), col, r);
+}
+
+// X = (I + N)^{-1} for a strictly lower triangular 64 x 64 N (LDS, pitch 65),
+// written in full to Xs (pitch 65), by blocked forward substitution on 16 x 16
+// blocks: diagonal blocks by substitution, then X_pq = -X_pp sum_{r=q}^{p-1}
+// N_pr X_rq one block diagonal at a time.  tmp: 768 floats of LDS.
+__device__ __forceinline__ void unit_lower_inverse(const float *Ns, float *Xs, float *tmp,
+                                                   int tid) {
+  constexpr int P = 65;
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int i = idx >> 6, j = idx & 63;
+    if ((i >> 4) < (j >> 4)) Xs[i * P + j] = 0.f;
+  }
+  if (tid < 64) {
+    const int base = 16 * (tid >> 4), j = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = i == j ? 1.f : 0.f;
+#pragma unroll
+      for (int t = 0; t < i; ++t) a = __builtin_fmaf(-Ns[(base + i) * P + base + t], x[t], a);
+      x[i] = a;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Xs[(base + i) * P + base + j] = x[i];
+  }
+  __syncthreads();
+  for (int lev = 1; lev < 4; ++lev) {
+    const int nb = 4 - lev;
+    for (int idx = tid; idx < nb * 256; idx += 256) {
+      const int q = idx >> 8, e = idx & 255, i = e >> 4, j = e & 15, p = q + lev;
+      float y = 0.f;
+      for (int t = 16 * q; t < 16 * p; ++t) y = __builtin_fmaf(Ns[(16 * p + i) * P + t], Xs[t * P + 16 * q + j], y);
+      tmp[idx] = y;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nb * 256; idx += 256) {
+      const int q = idx >> 8, e = idx & 255, i = e >> 4, j = e & 15, p = q + lev;
+      float x = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) x = __builtin_fmaf(-Xs[(16 * p + i) * P + 16 * p + t], tmp[(q << 8) + t * 16 + j], x);
+      Xs[(16 * p + i) * P + 16 * q + j] = x;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace pathattn
