@@ -25,6 +25,8 @@
 // formulas maps (dQa, dKb, dM, dAl) to dq, dk, dw, dbeta; suffix sums of
 // dLambda give d log f.  All arithmetic is float32; the key levels of a head
 // take 64*d*N(N-1)/2 floats of workspace.
+#include <type_traits>
+
 #include "path_attn_internal.h"
 #include "tile_fp32.h"
 
@@ -49,13 +51,18 @@ __host__ __device__ constexpr size_t adj_floats(int D) { return 6 * 4096 + 64 * 
 
 // One block per (bh, chunk), float32 matrix cores: Qa, Kb ([T][D]), M
 // ([N][D][D]), Al ([N][64][64], zero above the diagonal) and the saved
-// matrices of the chunk.
+// matrices of the chunk; for the matrix-core sweep also Qa in the input dtype
+// (rows [T][D] and per chunk transposed [D][64]) and -M, -M^T per chunk in the
+// input dtype.
 template <typename E, int D>
-__global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa, float *__restrict__ kb,
-    float *__restrict__ m, float *__restrict__ al, float *__restrict__ saved, int T) {
-  __shared__ float PX[kPanelFloats], PY[kPanelFloats];
+    float *__restrict__ m, float *__restrict__ al, float *__restrict__ saved, E *__restrict__ qae,
+    E *__restrict__ qat, E *__restrict__ nm, E *__restrict__ nmt, E *__restrict__ qimg,
+    E *__restrict__ mimg, int T) {
+  constexpr bool IMG = std::is_same<E, __bf16>::value && D == 64;
+  __shared__ float PX[panel_floats(D)], PY[panel_floats(D)];
   __shared__ float tmp[768], bs[C];
   const int N = T / C;
   const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
@@ -93,7 +100,13 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     for (int nb = 0; nb < D / 64; ++nb) {
       zero16(acc);
       gmm<64, true, false>(acc, W + 64 * ma, D, UWg + 64 * nb, D, PX, PY, tid);
-      tile_each(tid, [&](int i, int j, int r) { m_c[(size_t)(64 * ma + i) * D + 64 * nb + j] = acc[r]; });
+      tile_each(tid, [&](int i, int j, int r) {
+        const int a = 64 * ma + i, b = 64 * nb + j;
+        m_c[(size_t)a * D + b] = acc[r];
+        nm[(size_t)chunk * D * D + (size_t)a * D + b] = (E)(-acc[r]);
+        nmt[(size_t)chunk * D * D + (size_t)b * D + a] = (E)(-acc[r]);
+        if (IMG) mimg[(size_t)chunk * kMImgElems + mimg_index(a, b)] = (E)(-acc[r]);
+      });
     }
   zero16(acc);   // A = lower(Q W^T)
   gmm<D, false, true>(acc, Q, D, W, D, PX, PY, tid);
@@ -103,8 +116,21 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     zero16(acc);
     gmm<64, false, false>(acc, Ag, 64, UWg + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
-      qa_c[i * D + 64 * nb + j] = (float)Q[i * D + 64 * nb + j] - acc[r];
+      const int d = 64 * nb + j;
+      const float x = (float)Q[i * D + d] - acc[r];
+      qa_c[i * D + d] = x;
+      qae[(row0 + i) * D + d] = (E)x;
+      qat[(size_t)chunk * D * C + (size_t)d * C + i] = (E)x;
+      if (IMG) {
+        E *img = qimg + (size_t)chunk * kQImgElems;
+        img[i * kImgPitch + d] = (E)x;
+        img[64 * kImgPitch + d * kImgPitch + i] = (E)x;
+      }
     });
+  if (IMG)   // zero padding of the image rows
+    for (int idx = tid; idx < 2 * 64 * (kImgPitch - 64); idx += NT)
+      qimg[(size_t)chunk * kQImgElems + (idx / (kImgPitch - 64)) * kImgPitch + 64 +
+           idx % (kImgPitch - 64)] = (E)0.f;
   }
   zero16(acc);   // B = strictLower(W K^T)
   gmm<D, false, true>(acc, W, D, K, D, PX, PY, tid);
@@ -127,16 +153,23 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   tile_each(tid, [&](int i, int j, int r) { al_c[i * 64 + j] = j <= i ? acc[r] - acc2[r] : 0.f; });
 }
 
-// Lambda_t = sum_{1<=s<=t} log f_s (float64 running sum), one block per head.
-__global__ __launch_bounds__(64) void bwd_gate_kernel(const float *__restrict__ logf,
-                                                      float *__restrict__ lam, int T) {
-  if (threadIdx.x != 0) return;
+// Lambda_t = sum_{1<=s<=t} log f_s in float64, rounded once: one block per
+// head, each thread a contiguous segment, then a scan of the segment totals.
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const float *__restrict__ logf,
+                                                       float *__restrict__ lam, int T) {
+  __shared__ double tot[NT];
   const size_t base = (size_t)blockIdx.x * T;
-  double acc = 0.0;
-  lam[base] = 0.f;
-  for (int t = 1; t < T; ++t) {
-    acc += (double)logf[base + t];
-    lam[base + t] = (float)acc;
+  const int tid = threadIdx.x, seg = (T + NT - 1) / NT;
+  const int lo = tid * seg, hi = lo + seg < T ? lo + seg : T;
+  double s = 0.0;
+  for (int t = lo > 1 ? lo : 1; t < hi; ++t) s += (double)logf[base + t];
+  tot[tid] = s;
+  __syncthreads();
+  double before = 0.0;
+  for (int u = 0; u < tid; ++u) before += tot[u];
+  for (int t = lo; t < hi; ++t) {
+    if (t >= 1) before += (double)logf[base + t];
+    lam[base + t] = (float)before;
   }
 }
 
@@ -153,7 +186,9 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     const float *__restrict__ al, const E *__restrict__ v, const E *__restrict__ o,
     const E *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dlse,
     const float *__restrict__ lam, float scale, float *__restrict__ dal,
-    float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dvec, int T) {
+    float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dvec,
+    E *__restrict__ dot, E *__restrict__ oimg, float4 *__restrict__ qst, int T) {
+  constexpr bool IMG = std::is_same<E, __bf16>::value && D == 64;
   constexpr int DP = D + 1, CP = C + 1;
   __shared__ float Os[C * DP];
   __shared__ float Vs[C * DP];
@@ -177,6 +212,17 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     rdl[tid] = dlse ? dlse[row0 + tid] : 0.f;
   }
   __syncthreads();
+  for (int idx = tid; idx < C * D; idx += NT)   // dO^T of the chunk, [D][64]
+    dot[((size_t)bh * N + c) * C * D + idx] = (E)Os[(idx % C) * DP + idx / C];
+  if (IMG) {
+    E *img = oimg + ((size_t)bh * N + c) * kQImgElems;
+    for (int idx = tid; idx < 64 * kImgPitch; idx += NT) {
+      const int r = idx / kImgPitch, cc = idx % kImgPitch;
+      img[idx] = cc < 64 ? (E)Os[r * DP + cc] : (E)0.f;                       // dO rows
+      img[64 * kImgPitch + idx] = cc < 64 ? (E)Os[cc * DP + r] : (E)0.f;      // dO^T rows
+    }
+    if (tid < C) qst[row0 + tid] = make_float4(rl[tid], rd[tid], rdl[tid], rg[tid]);
+  }
   const float *al_c = al + ((size_t)bh * N + c) * C * C;
   float p[4][4];
 #pragma unroll
@@ -240,13 +286,13 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
 //   dK   = dKb + dAl^T Q + dB^T W
 //   dW   = -T2 dKb + UW dM^T + U^T dUW + dA^T Q + dB K + dG W + dG^T W
 template <typename E, int D>
-__global__ __launch_bounds__(256, 2) void bwd_local_kernel(
+__global__ __launch_bounds__(256) void bwd_local_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
     const float *__restrict__ beta, const float *__restrict__ dqa,
     const float *__restrict__ dkb, const float *__restrict__ dm, const float *__restrict__ dal,
     const float *__restrict__ saved, float *__restrict__ adj, E *__restrict__ dq,
     E *__restrict__ dk, E *__restrict__ dw, float *__restrict__ dbeta, int T) {
-  __shared__ float PX[kPanelFloats], PY[kPanelFloats];
+  __shared__ float PX[panel_floats(D)], PY[panel_floats(D)];
   __shared__ float bs[C], dbs[C];
   const int N = T / C;
   const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
@@ -349,24 +395,34 @@ __global__ __launch_bounds__(256, 2) void bwd_local_kernel(
   if (tid < C) dbeta[row0 + tid] = dbs[tid];
 }
 
-// dv = dV in the input dtype; d log f_t = sum_{i >= t} dLambda_i (t >= 1),
-// d log f_0 = 0, one block per head for the suffix sums.
+// dv = dV in the input dtype (grid-stride over all heads).
 template <typename E>
-__global__ __launch_bounds__(256) void bwd_final_kernel(const float *__restrict__ dvacc,
-                                                        E *__restrict__ dv,
-                                                        const float *__restrict__ dlam,
-                                                        float *__restrict__ dlogf, int T, int D) {
-  const int bh = blockIdx.x;
-  const size_t n = (size_t)T * D;
-  for (size_t i = threadIdx.x; i < n; i += NT) dv[(size_t)bh * n + i] = (E)dvacc[(size_t)bh * n + i];
-  if (dlogf && threadIdx.x == 0) {
-    double acc = 0.0;
-    for (int t = T - 1; t >= 1; --t) {
-      acc += (double)dlam[(size_t)bh * T + t];
-      dlogf[(size_t)bh * T + t] = (float)acc;
-    }
-    dlogf[(size_t)bh * T] = 0.f;
+__global__ __launch_bounds__(256) void bwd_cast_kernel(const float *__restrict__ src,
+                                                       E *__restrict__ dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT)
+    dst[i] = (E)src[i];
+}
+
+// d log f_t = sum_{i >= t} dLambda_i for t >= 1, d log f_0 = 0: one block
+// per head, float64 suffix sums (each thread a contiguous segment, then a
+// scan of the segment totals).
+__global__ __launch_bounds__(256) void bwd_gate_grad_kernel(const float *__restrict__ dlam,
+                                                            float *__restrict__ dlogf, int T) {
+  __shared__ double tot[NT];
+  const size_t base = (size_t)blockIdx.x * T;
+  const int tid = threadIdx.x, seg = (T + NT - 1) / NT;
+  const int lo = tid * seg, hi = lo + seg < T ? lo + seg : T;
+  double s = 0.0;
+  for (int t = lo; t < hi; ++t) s += (double)dlam[base + t];
+  tot[tid] = s;
+  __syncthreads();
+  double after = 0.0;   // sum of the segments to the right
+  for (int u = tid + 1; u < NT; ++u) after += tot[u];
+  for (int t = hi - 1; t >= lo; --t) {
+    after += (double)dlam[base + t];
+    if (t >= 1) dlogf[base + t] = (float)after;
   }
+  if (tid == 0) dlogf[base] = 0.f;
 }
 
 }  // namespace
@@ -396,6 +452,18 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
   L.dm = take(BH * N * D * D);
   L.dal = take(BH * N * C * C);
   L.saved = take(BH * N * saved_floats(D));
+  auto take_e = [&](size_t elems) { return take((elems * esize + 3) / 4); };
+  L.qae = take_e(BH * T * D);
+  L.qat = take_e(BH * T * D);
+  L.nm = take_e(BH * N * D * D);
+  L.nmt = take_e(BH * N * D * D);
+  L.dot = take_e(BH * T * D);
+  L.levt = take_e(bwd_levels_elems((int)BH, T, D));
+  const bool img = dtype == 1 && D == 64;
+  L.qimg = take_e(img ? BH * N * kQImgElems : 0);
+  L.oimg = take_e(img ? BH * N * kQImgElems : 0);
+  L.mimg = take_e(img ? BH * N * kMImgElems : 0);
+  L.qst = take(img ? BH * T * 4 : 0);
   L.adj = take(BH * N * adj_floats(D));
   L.total = off;
   return L;
@@ -407,13 +475,26 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   const int BH = a.B * a.H, T = a.T, N = T / C;
   auto f = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
   const E *q = (const E *)a.q, *k = (const E *)a.k, *v = (const E *)a.v, *w = (const E *)a.w;
+  auto e = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
   hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
-                     f(L.qa), f(L.kb), f(L.m), f(L.al), f(L.saved), T);
-  if (FOX) hipLaunchKernelGGL(bwd_gate_kernel, dim3(BH), dim3(64), 0, s, a.logf, f(L.lam), T);
+                     f(L.qa), f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
+                     e(L.nmt), e(L.qimg), e(L.mimg), T);
+  if (FOX) hipLaunchKernelGGL(bwd_gate_kernel, dim3(BH), dim3(NT), 0, s, a.logf, f(L.lam), T);
   hipLaunchKernelGGL((bwd_diag_kernel<E, D, FOX>), dim3(BH * N), dim3(NT), 0, s, f(L.al), v,
                      (const E *)a.out, (const E *)a.dout, a.lse, a.dlse, f(L.lam), a.scale, f(L.dal),
-                     f(L.dv), f(L.dlam), f(L.dvec), T);
+                     f(L.dv), f(L.dlam), f(L.dvec), e(L.dot), e(L.oimg),
+                     reinterpret_cast<float4 *>(ws + L.qst), T);
   SweepArgs sa{};
+  sa.qae = ws + L.qae;
+  sa.qat = ws + L.qat;
+  sa.nm = ws + L.nm;
+  sa.nmt = ws + L.nmt;
+  sa.dot = ws + L.dot;
+  sa.levt = ws + L.levt;
+  sa.qimg = ws + L.qimg;
+  sa.oimg = ws + L.oimg;
+  sa.mimg = ws + L.mimg;
+  sa.qst = ws + L.qst;
   sa.qa = f(L.qa);
   sa.kb = f(L.kb);
   sa.m = f(L.m);
@@ -437,8 +518,11 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
                      f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.saved), f(L.adj), (E *)a.dq,
                      (E *)a.dk, (E *)a.dw, a.dbeta, T);
-  hipLaunchKernelGGL((bwd_final_kernel<E>), dim3(BH), dim3(NT), 0, s, f(L.dv), (E *)a.dv, f(L.dlam),
-                     FOX ? a.dlogf : nullptr, T, D);
+  const size_t nv = (size_t)BH * T * D;
+  const size_t cb = (nv + NT - 1) / NT;
+  hipLaunchKernelGGL((bwd_cast_kernel<E>), dim3((unsigned)(cb < 8192 ? cb : 8192)), dim3(NT), 0, s,
+                     f(L.dv), (E *)a.dv, nv);
+  if (FOX) hipLaunchKernelGGL(bwd_gate_grad_kernel, dim3(BH), dim3(NT), 0, s, f(L.dlam), a.dlogf, T);
   return hipGetLastError();
 }
 

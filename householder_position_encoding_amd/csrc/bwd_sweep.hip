@@ -108,70 +108,80 @@ __device__ __forceinline__ void st_tile(E *dst, int rs, int cs, const f32x16 &a,
   for (int r = 0; r < 16; ++r) dst[acc_row(r, g) * rs + j * cs] = (E)a[r];
 }
 
+// Wave-scope ordering of LDS accesses: a wave's later reads see its earlier
+// writes (other lanes included) and its later writes follow its earlier reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------------ levels
 
 __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
   return ((size_t)c * (c - 1) / 2 + cp) * (size_t)C * D;
 }
 
-// One block of 2 waves (32 keys each) per (key chunk c' < N-1, bh).
+// Each wave walks the levels of 32 keys of one key chunk c' < N-1 (blocks of
+// 2 waves, one per key half) and stores level c in rows [64 keys][D] and
+// transposed [D][64 keys] (both at lev_off(c, c')).  -M_c is read in the
+// input dtype from global memory (shared by every block of the head).
 template <typename E, int D>
 __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ kb,
-                                                     const float *__restrict__ m,
-                                                     E *__restrict__ levels, int T, int BH) {
+                                                     const E *__restrict__ nm,
+                                                     E *__restrict__ levels,
+                                                     E *__restrict__ levt, int T, int BH) {
   constexpr int P = D + MM<E>::PAD;
-  __shared__ __attribute__((aligned(16))) E Xs[C * P];
-  __shared__ __attribute__((aligned(16))) E Ms[D * P];
+  __shared__ __attribute__((aligned(16))) E Xs[2 * 32 * P];
   const int N = T / C;
   const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
+  E *Xw = Xs + wv * 32 * P;
   f32x16 x[D / 32];
   const float *src = kb + ((size_t)bh * T + (size_t)cp * C + 32 * wv) * D;
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
-  E *head = levels + (size_t)bh * lev_off(N, 0, D);
+  const size_t head = (size_t)bh * lev_off(N, 0, D);
   for (int c = cp + 1; c < N; ++c) {
-    E *dst = head + lev_off(c, cp, D) + (size_t)32 * wv * D;
+    const size_t off = head + lev_off(c, cp, D);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) st_tile(dst + 32 * t, D, 1, x[t], lane);
+    for (int t = 0; t < D / 32; ++t) {
+      st_tile(levels + off + (size_t)32 * wv * D + 32 * t, D, 1, x[t], lane);
+      st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
+    }
     if (c + 1 >= N) break;
-    __syncthreads();
-    const float *mc = m + ((size_t)bh * N + c) * D * D;
-    for (int idx = tid; idx < D * D; idx += 128) Ms[(idx / D) * P + idx % D] = (E)(-mc[idx]);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) st_tile(Xs + 32 * wv * P + 32 * t, P, 1, x[t], lane);
-    __syncthreads();
+    for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
+    wave_sync();
     // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
+    const E *nmc = nm + ((size_t)bh * N + c) * D * D;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-      mma_tile<E, D>(x[t], Xs + 32 * wv * P, P, 1, Ms + 32 * t * P, P, 1, lane);
+    for (int t = 0; t < D / 32; ++t) mma_tile<E, D>(x[t], Xw, P, 1, nmc + 32 * t * D, D, 1, lane);
+    wave_sync();
   }
 }
 
 // ------------------------------------------------------------------ dq
 
 // One block of 4 waves per (bh, query chunk c): wave (qh, kh) = (w & 1, w >> 1)
-// takes queries 32 qh.. and, at each key chunk, keys 32 kh...  Chunk 0 has no
-// earlier keys: its dQa is zero.
+// takes queries 32 qh.. and, at each key chunk, keys 32 kh..; the block
+// synchronises only to stage its queries and to combine the key halves.
+// Chunk 0 has no earlier keys: its dQa is zero.
 template <typename E, int D, bool FOX>
 __global__ __launch_bounds__(256) void dq_kernel(
-    const float *__restrict__ qa, const E *__restrict__ dout, const float *__restrict__ lse,
+    const E *__restrict__ qae, const E *__restrict__ dout, const float *__restrict__ lse,
     const float *__restrict__ dlse, const float *__restrict__ dvec, const float *__restrict__ lam,
-    const E *__restrict__ levels, const E *__restrict__ v, float scale, float *__restrict__ dqa,
-    float *__restrict__ dlam, int T, int BH) {
-  constexpr bool BF = std::is_same<E, __bf16>::value;
+    const E *__restrict__ levels, const E *__restrict__ levt, const E *__restrict__ v,
+    float scale, float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH) {
   constexpr int PQ = D + MM<E>::PAD;          // Qs, Os: [64 q][D]
-  constexpr int PK = C + MM<E>::PAD;          // Kt: [D][64 keys] (bf16) ; float: Khat rows [64][D]
-  constexpr int PKF = D + MM<E>::PAD;
   constexpr int PG = 32 + MM<E>::PAD;         // Gs: per wave [32 q][32 keys]
   __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
   __shared__ __attribute__((aligned(16))) E Os[C * PQ];
-  __shared__ __attribute__((aligned(16))) E Kt[BF ? D * PK : C * PKF];
   __shared__ __attribute__((aligned(16))) E Gs[4 * 32 * PG];
   __shared__ float red[2 * 32 * (D + 1)];
-  __shared__ float lamk[C];
+  __shared__ float rsum[C];
   const int N = T / C;
   const int bh = blockIdx.x % BH, c = N - 1 - blockIdx.x / BH;   // longest walks first
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
     return;
   }
   for (int idx = tid; idx < C * D; idx += 256) {
-    Qs[(idx / D) * PQ + idx % D] = (E)qa[qrow * D + idx];
+    Qs[(idx / D) * PQ + idx % D] = qae[qrow * D + idx];
     Os[(idx / D) * PQ + idx % D] = dout[qrow * D + idx];
   }
   const int myq = 32 * qh + col;
@@ -193,57 +203,45 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) zero16(dq[t]);
   float rowsum = 0.f;
-  const E *lev_c = levels + (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
+  const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
   E *Gw = Gs + wv * 32 * PG;
+  __syncthreads();
   for (int cp = c - 1; cp >= 0; --cp) {
-    const E *kh_rows = lev_c + (size_t)cp * C * D;   // Khat[c]_{c'}: [64 keys][D]
-    const size_t krow = (size_t)bh * T + (size_t)cp * C;
-    __syncthreads();
-    for (int idx = tid; idx < C * D; idx += 256) {
-      const int key = idx / D, d = idx % D;
-      if constexpr (BF) Kt[d * PK + key] = kh_rows[idx];
-      else Kt[key * PKF + d] = kh_rows[idx];
-    }
-    if (FOX && tid < C) lamk[tid] = lam[krow + tid];
-    __syncthreads();
+    const size_t blk = lev_c + (size_t)cp * C * D;   // Khat[c]_{c'}
+    const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
     // S^T and dP^T tiles: rows = keys 32 kh.., columns = queries 32 qh..
     f32x16 s, dp;
     zero16(s);
     zero16(dp);
-    mma_tile<E, D>(s, kh_rows + 32 * kh * D, D, 1, Qs + 32 * qh * PQ, PQ, 1, lane);
-    mma_tile<E, D>(dp, v + (krow + 32 * kh) * D, D, 1, Os + 32 * qh * PQ, PQ, 1, lane);
+    mma_tile<E, D>(s, levels + blk + (size_t)32 * kh * D, D, 1, Qs + 32 * qh * PQ, PQ, 1, lane);
+    mma_tile<E, D>(dp, v + krow * D, D, 1, Os + 32 * qh * PQ, PQ, 1, lane);
     f32x16 gt;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kh + acc_row(r, g);
-      const float kl = FOX ? lamk[key] : 0.f;
+      const float kl = FOX ? lam[krow + acc_row(r, g)] : 0.f;
       const float p = __expf(scale * s[r] + q_lam - kl - q_lse);
       const float ds = p * (dp[r] - q_d + q_dl);
       rowsum += ds;
       gt[r] = scale * ds;
     }
     st_tile(Gw, 1, PG, gt, lane);   // Gw[q][key] = g(q, key)
-    __syncthreads();
+    wave_sync();
     // dQa^T(d, q) += sum_key Khat(key, d) g(q, key)
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      if constexpr (BF)
-        mma_tile<E, 32>(dq[t], Kt + 32 * t * PK + 32 * kh, PK, 1, Gw, PG, 1, lane);
-      else
-        mma_tile<E, 32>(dq[t], Kt + 32 * kh * PKF + 32 * t, 1, PKF, Gw, PG, 1, lane);
-    }
+    for (int t = 0; t < D / 32; ++t)
+      mma_tile<E, 32>(dq[t], levt + blk + (size_t)32 * t * C + 32 * kh, C, 1, Gw, PG, 1, lane);
+    wave_sync();
   }
   // combine the two key halves, then store dQa rows
-  __syncthreads();
   float *rq = red + qh * 32 * (D + 1);
+  rowsum += __shfl_xor(rowsum, 32);
   if (kh == 1) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) rq[col * (D + 1) + 32 * t + acc_row(r, g)] = dq[t][r];
+    if (g == 0) rsum[myq] = rowsum;
   }
-  rowsum += __shfl_xor(rowsum, 32);
-  if (kh == 1 && g == 0) lamk[32 * qh + col] = rowsum;
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
@@ -253,13 +251,13 @@ __global__ __launch_bounds__(256) void dq_kernel(
         const int d = 32 * t + acc_row(r, g);
         dqa[(qrow + myq) * D + d] = dq[t][r] + rq[col * (D + 1) + d];
       }
-    if (FOX && g == 0) dlam[qrow + myq] += rowsum + lamk[myq];
+    if (FOX && g == 0) dlam[qrow + myq] += rowsum + rsum[myq];
   }
 }
 
 // ------------------------------------------------------------------ dk
 
-// Staging sizes (elements of E) of the dk kernel.
+// LDS layout (elements of E) of the dk kernel.
 template <typename E, int D, int G>
 struct DkLds {
   static constexpr bool BF = std::is_same<E, __bf16>::value;
@@ -268,34 +266,31 @@ struct DkLds {
   static constexpr int PQT = C + PAD;             // Qt, Ot rows [D][64 q] (bf16 only)
   static constexpr int PP = C + PAD;              // per-wave P^T, g^T rows [32 keys][64 q]
   static constexpr int KG = 64 * G;               // keys of a group
-  static constexpr int PGT = KG + PAD;            // crossing: Gamma^T, Khat^T rows [D][KG] (bf16)
-  static constexpr int PGN = D + PAD;             // crossing (float): Gamma, Khat rows [KG][D]
-  static constexpr int PM = D + PAD;              // -M^T rows [D][D] (bf16 only)
+  static constexpr int PGT = KG + PAD;            // Gamma^T rows [D][KG] (bf16)
+  static constexpr int PGN = D + PAD;             // Gamma rows [KG][D] (float); rounded Gamma rows (bf16)
   static constexpr int STAGE = BF ? 2 * C * PQ + 2 * D * PQT : 2 * C * PQ;
-  static constexpr int CROSS = BF ? 2 * D * PGT : 2 * KG * PGN;
-  static constexpr int AREA1 = STAGE > CROSS ? STAGE : CROSS;
+  static constexpr int GX = BF ? D * PGT : KG * PGN;
   static constexpr int WAVES = 2 * G;
-  static constexpr int PERWAVE = 2 * 32 * PP;     // P^T and g^T
-  static constexpr int GR = 32 * PGN;             // rounded Gamma rows (bf16 transition)
-  static constexpr int AREA2 = WAVES * (PERWAVE > GR ? PERWAVE : GR);
-  static constexpr int MS = BF ? D * PM : 0;
+  static constexpr int PERWAVE = 2 * 32 * PP;     // P^T and g^T; rounded Gamma rows at crossings
+  static_assert(32 * PGN <= PERWAVE, "rounded Gamma rows must fit the wave's P/g area");
 };
 
 // One block of 2G waves per (group of G key chunks, bh); wave w takes keys
 // 32 (w & 1).. of chunk c' = G*group + (w >> 1).
 template <typename E, int D, int G, bool FOX>
 __global__ __launch_bounds__(128 * G) void dk_kernel(
-    const float *__restrict__ qa, const E *__restrict__ dout, const float *__restrict__ lse,
-    const float *__restrict__ dlse, const float *__restrict__ dvec, const float *__restrict__ lam,
-    const E *__restrict__ levels, const E *__restrict__ v, const float *__restrict__ m,
+    const E *__restrict__ qae, const E *__restrict__ qat, const E *__restrict__ dout,
+    const E *__restrict__ dot, const float *__restrict__ lse, const float *__restrict__ dlse,
+    const float *__restrict__ dvec, const float *__restrict__ lam, const E *__restrict__ levels,
+    const E *__restrict__ levt, const E *__restrict__ v, const E *__restrict__ nmt,
     float scale, float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
     float *__restrict__ dmpart, int T, int BH) {
   using L = DkLds<E, D, G>;
   constexpr bool BF = L::BF;
   constexpr int NW = L::WAVES, NTH = 64 * NW;
-  __shared__ __attribute__((aligned(16))) E area1[L::AREA1];
-  __shared__ __attribute__((aligned(16))) E area2[L::AREA2];
-  __shared__ __attribute__((aligned(16))) E Ms[L::MS > 0 ? L::MS : 1];
+  __shared__ __attribute__((aligned(16))) E stage[L::STAGE];
+  __shared__ __attribute__((aligned(16))) E gx[L::GX];
+  __shared__ __attribute__((aligned(16))) E pw[NW * L::PERWAVE];
   __shared__ float4 qst[C];
   const int N = T / C, NG = (N + G - 1) / G;
   const int grp = blockIdx.x / BH, bh = blockIdx.x % BH;
@@ -304,13 +299,12 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   const size_t head = (size_t)bh * T;
   const size_t krow = head + (size_t)cp * C + 32 * kh;   // first key row of this wave
   const bool member = cp < N;
-  // staging views
-  E *Qs = area1, *Os = area1 + C * L::PQ;
-  E *Qt = area1 + 2 * C * L::PQ, *Ot = Qt + D * L::PQT;   // bf16 only
-  E *PT = area2 + wv * L::PERWAVE, *GT = PT + 32 * L::PP;
-  E *GR = area2 + wv * L::GR;                             // aliases P^T / g^T at crossings
-  E *Gx = area1, *Kx = area1 + (BF ? D * L::PGT : L::KG * L::PGN);   // crossing staging
-  const E *lev_head = levels + (size_t)bh * lev_off(N, 0, D);
+  E *Qs = stage, *Os = stage + C * L::PQ;
+  E *Qt = stage + 2 * C * L::PQ, *Ot = Qt + D * L::PQT;   // bf16 only
+  E *PT = pw + wv * L::PERWAVE, *GT = PT + 32 * L::PP;
+  E *GR = PT;                                             // rounded Gamma rows at crossings
+  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
+  const int kbase = 64 * (wv >> 1) + 32 * kh;             // this wave's keys within the group
 
   f32x16 gam[D / 32], dva[D / 32];
 #pragma unroll
@@ -325,32 +319,29 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     const bool active = member && c > cp;
     const size_t qrow = head + (size_t)c * C;
     __syncthreads();
-    for (int idx = tid; idx < C * D; idx += NTH) {
-      const int q = idx / D, d = idx % D;
-      const E a = (E)qa[qrow * D + idx], o = dout[qrow * D + idx];
-      Qs[q * L::PQ + d] = a;
-      Os[q * L::PQ + d] = o;
-      if constexpr (BF) {
-        Qt[d * L::PQT + q] = a;
-        Ot[d * L::PQT + q] = o;
+    if constexpr (BF) {   // 16-byte copies of Qa, dO (rows) and Qa^T, dO^T
+      const E *sq = qae + qrow * D, *so = dout + qrow * D;
+      const E *sqt = qat + qrow * D, *sot = dot + qrow * D;   // chunk c block [D][64]
+      for (int vi = tid; vi < C * D / 8; vi += NTH) {
+        const int r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
+        *reinterpret_cast<bf16x8 *>(Qs + r * L::PQ + c8) = *reinterpret_cast<const bf16x8 *>(sq + r * D + c8);
+        *reinterpret_cast<bf16x8 *>(Os + r * L::PQ + c8) = *reinterpret_cast<const bf16x8 *>(so + r * D + c8);
+        const int rt = vi / (C / 8), ct = 8 * (vi % (C / 8));
+        *reinterpret_cast<bf16x8 *>(Qt + rt * L::PQT + ct) = *reinterpret_cast<const bf16x8 *>(sqt + rt * C + ct);
+        *reinterpret_cast<bf16x8 *>(Ot + rt * L::PQT + ct) = *reinterpret_cast<const bf16x8 *>(sot + rt * C + ct);
+      }
+    } else {
+      for (int idx = tid; idx < C * D; idx += NTH) {
+        Qs[(idx / D) * L::PQ + idx % D] = qae[qrow * D + idx];
+        Os[(idx / D) * L::PQ + idx % D] = dout[qrow * D + idx];
       }
     }
     if (tid < C)
       qst[tid] = make_float4(lse[qrow + tid], dvec[qrow + tid], dlse ? dlse[qrow + tid] : 0.f,
                              FOX ? lam[qrow + tid] : 0.f);
-    const bool crossing = c - 1 > G * grp;   // some chunk of the group crosses m = c-1
-    if constexpr (BF) {
-      if (crossing) {
-        const float *mm = m + (head / T * N + (size_t)(c - 1)) * D * D;
-        for (int idx = tid; idx < D * D; idx += NTH) {
-          const int d = idx / D, dp = idx % D;   // M[d][d'] -> Ms[d'][d] = -M[d][d']
-          Ms[dp * L::PM + d] = (E)(-mm[idx]);
-        }
-      }
-    }
     __syncthreads();
-    const E *kl = lev_head + lev_off(c, cp < c ? cp : 0, D) + (size_t)32 * kh * D;   // Khat[c] rows
     if (active) {
+      const E *kl = levels + lev_head + lev_off(c, cp, D) + (size_t)32 * kh * D;   // Khat[c] rows
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -370,13 +361,10 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
           s[qt][r] = p;
           dp[qt][r] = scale * ds;
         }
-        // P^T[key][q], g^T[key][q]
-        st_tile(PT + 32 * qt, 1, L::PP, s[qt], lane);
-        st_tile(GT + 32 * qt, 1, L::PP, dp[qt], lane);
+        st_tile(PT + 32 * qt, 1, L::PP, s[qt], lane);   // P^T[key][q]
+        st_tile(GT + 32 * qt, 1, L::PP, dp[qt], lane);  // g^T[key][q]
       }
-    }
-    __syncthreads();
-    if (active) {
+      wave_sync();
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
         if constexpr (BF) {
@@ -395,76 +383,269 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
             dkb[(krow + acc_row(r, g)) * D + 32 * t + col] = gam[t][r];
       }
     }
-    if (!crossing) continue;
-    // ---- crossing of chunk m = c-1 by the group's chunks c' < m
     const int mch = c - 1;
+    if (!(mch > G * grp)) continue;   // no chunk of the group crosses m = c-1
+    // ---- crossing of chunk m = c-1 by the group's chunks c' < m
     const bool crosses = member && cp < mch;
-    __syncthreads();
-    {
-      const E *km = lev_head + lev_off(mch, crosses ? cp : 0, D) + (size_t)32 * kh * D;
-      const int kbase = 64 * (wv >> 1) + 32 * kh;   // this wave's keys within the group
+    wave_sync();   // this wave's reads of P^T / g^T are done before GR overwrites them
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      f32x16 z = gam[t];
+      if (!crosses) zero16(z);
       if constexpr (BF) {
-        // Gx = Gamma^T [D][KG], Kx = Khat[m]^T [D][KG]; GR = round(Gamma) rows
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          f32x16 z = gam[t];
-          if (!crosses) zero16(z);
-          st_tile(Gx + 32 * t * L::PGT + kbase, 1, L::PGT, z, lane);
-          st_tile(GR + 32 * t, L::PGN, 1, z, lane);
-        }
-        for (int e = lane; e < 32 * D; e += 64) {
-          const int key = e / D, d = e % D;
-          Kx[d * L::PGT + kbase + key] = crosses ? km[e] : (E)0.f;
-        }
+        st_tile(gx + 32 * t * L::PGT + kbase, 1, L::PGT, z, lane);   // Gamma^T [D][KG]
+        st_tile(GR + 32 * t, L::PGN, 1, z, lane);                    // round(Gamma) rows
       } else {
-        // float: Gx = Gamma rows [KG][D] (also the transition operand), Kx = Khat[m] rows
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          f32x16 z = gam[t];
-          if (!crosses) zero16(z);
-          st_tile(Gx + kbase * L::PGN + 32 * t, L::PGN, 1, z, lane);
-        }
-        for (int e = lane; e < 32 * D; e += 64) {
-          const int key = e / D, d = e % D;
-          Kx[(kbase + key) * L::PGN + d] = crosses ? km[e] : (E)0.f;
-        }
+        st_tile(gx + kbase * L::PGN + 32 * t, L::PGN, 1, z, lane);   // Gamma rows [KG][D]
       }
     }
     __syncthreads();
-    // dM_m partial of the group: -sum_keys Gamma(key, d) Khat[m](key, d')
+    // dM_m partial of the group: -sum_keys Gamma(key, d) Khat[m](key, d'), over
+    // the chunks c' < m of the group (Khat[m]^T read from the transposed levels)
     {
       constexpr int TILES = (D / 32) * (D / 32);
+      const int nch = mch - G * grp < G ? mch - G * grp : G;
       float *dst = dmpart + (((size_t)bh * N + mch) * NG + grp) * D * D;
+      const size_t lm = lev_head + lev_off(mch, G * grp, D);   // chunk blocks are consecutive
       for (int tI = wv; tI < TILES; tI += NW) {
         const int ta = tI / (D / 32), tb = tI % (D / 32);
         f32x16 acc;
         zero16(acc);
-        if constexpr (BF)
-          mma_tile<E, L::KG>(acc, Gx + 32 * ta * L::PGT, L::PGT, 1, Kx + 32 * tb * L::PGT,
-                             L::PGT, 1, lane);
-        else
-          mma_tile<E, L::KG>(acc, Gx + 32 * ta, 1, L::PGN, Kx + 32 * tb, 1, L::PGN, lane);
+        for (int j = 0; j < nch; ++j) {
+          const E *kt = levt + lm + (size_t)j * C * D + (size_t)32 * tb * C;   // [d'][64 keys]
+          if constexpr (BF)
+            mma_tile<E, C>(acc, gx + 32 * ta * L::PGT + 64 * j, L::PGT, 1, kt, C, 1, lane);
+          else
+            mma_tile<E, C>(acc, gx + 64 * j * L::PGN + 32 * ta, 1, L::PGN, kt, C, 1, lane);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           dst[(size_t)(32 * ta + acc_row(r, g)) * D + 32 * tb + col] = -acc[r];
       }
     }
-    if (crosses) {   // Gamma <- Gamma + round(Gamma) (-M_m)
+    if (crosses) {   // Gamma <- Gamma + round(Gamma) (-M_m): B(d', d) = -M_m[d][d'] = (-M^T)[d'][d]
+      const E *nb = nmt + ((size_t)bh * N + mch) * D * D;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        if constexpr (BF) {
-          mma_tile<E, D>(gam[t], GR, L::PGN, 1, Ms + 32 * t * L::PM, L::PM, 1, lane);
-        } else {
-          // B(d', d) = -M[d][d'] read from global memory
-          const float *mm = m + ((size_t)bh * N + mch) * D * D;
-          f32x16 acc;
-          zero16(acc);
-          mma_tile<E, D>(acc, Gx + (64 * (wv >> 1) + 32 * kh) * L::PGN, L::PGN, 1, mm + 32 * t,
-                         1, D, lane);
+        if constexpr (BF)
+          mma_tile<E, D>(gam[t], GR, L::PGN, 1, nb + 32 * t * D, D, 1, lane);
+        else
+          mma_tile<E, D>(gam[t], gx + kbase * L::PGN, L::PGN, 1, nb + 32 * t * D, D, 1, lane);
+      }
+    }
+  }
+  if (!member) return;
+  if (cp == N - 1) {   // no later query chunk: dKb = 0
+    for (int e = lane; e < 32 * D; e += 64) dkb[krow * D + e] = 0.f;
+    return;
+  }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) gam[t][r] -= acc[r];
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[(krow + acc_row(r, g)) * D + 32 * t + col] += dva[t][r];
+  if (FOX) {
+    colsum += __shfl_xor(colsum, 32);
+    if (g == 0) dlam[krow + col] -= colsum;
+  }
+}
+
+// ------------------------------------------------------------------ dk, bf16, d = 64
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *gbl_ptr_t;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt at maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Block barrier that completes the wave's LDS accesses but leaves its global
+// loads (the next step's operand copies) in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Same walk as dk_kernel for bf16 inputs and d = 64, G = 4 key chunks per
+// block (8 waves).  The query-side operands of step c (Qa and dO rows and
+// transposes, -M_{c-1}^T in fragment order, per-query statistics: 45 KiB of
+// per-chunk images) are copied straight into one of two LDS buffers one step
+// ahead (global_load_lds); V and the level rows Khat[c]_{c'} are matrix-core
+// B operands held in registers, the latter loaded one step ahead.  Gamma is
+// kept transposed (d x keys) so that the transition Gamma^T <- Gamma^T +
+// (-M^T) round(Gamma^T) takes its B operand from the accumulators (the
+// contraction index permuted as frag_row, matched by the image of -M^T).
+template <bool FOX>
+__global__ __launch_bounds__(512) void dk64_kernel(
+    const __bf16 *__restrict__ qimg, const __bf16 *__restrict__ oimg,
+    const __bf16 *__restrict__ mimg, const float4 *__restrict__ qstat,
+    const float *__restrict__ lam, const __bf16 *__restrict__ levels,
+    const __bf16 *__restrict__ levt, const __bf16 *__restrict__ v, float scale,
+    float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
+    float *__restrict__ dmpart, int T, int BH) {
+  using E = __bf16;
+  constexpr int D = 64, G = 4, NW = 8, P = kImgPitch, KG = 64 * G, PGT = KG + 8;
+  constexpr int QB = kQImgElems * 2, MB = kMImgElems * 2, SB = 64 * 16;   // bytes
+  constexpr int BUF = 2 * QB + MB + SB;                                   // 45 KiB
+  constexpr int NCOPY = BUF / 1024;
+  static_assert(BUF % 1024 == 0, "whole 1 KiB copies");
+  __shared__ __attribute__((aligned(16))) unsigned char sbuf[2 * BUF];
+  __shared__ __attribute__((aligned(16))) E gx[D * PGT];
+  __shared__ __attribute__((aligned(16))) E pw[NW * 32 * P];
+  const int N = T / C, NG = (N + G - 1) / G;
+  const int grp = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int kh = wv & 1, cp = G * grp + (wv >> 1);
+  const size_t head = (size_t)bh * T;
+  const size_t krow = head + (size_t)cp * C + 32 * kh;
+  const bool member = cp < N;
+  const int kbase = 64 * (wv >> 1) + 32 * kh;
+  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
+  E *PW = pw + wv * 32 * P;
+  const int c_low = G * grp + 1;
+
+  auto stage = [&](int c, int b) {
+    const size_t ch = (size_t)bh * N + c;
+    const unsigned char *q = reinterpret_cast<const unsigned char *>(qimg + ch * kQImgElems);
+    const unsigned char *o = reinterpret_cast<const unsigned char *>(oimg + ch * kQImgElems);
+    const unsigned char *mm = reinterpret_cast<const unsigned char *>(mimg + (ch - 1) * kMImgElems);
+    const unsigned char *st = reinterpret_cast<const unsigned char *>(qstat + ch * C);
+    for (int j = wv; j < NCOPY; j += NW) {
+      const unsigned char *src = j < QB / 1024 ? q + j * 1024
+                                 : j < 2 * QB / 1024 ? o + (j - QB / 1024) * 1024
+                                 : j < (2 * QB + MB) / 1024 ? mm + (j - 2 * QB / 1024) * 1024
+                                                            : st;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + lane * 16),
+                                       (lds_ptr_t)(sbuf + b * BUF + j * 1024), 16, 0, 0);
+    }
+  };
+  auto load_rows = [&](bf16x8 (&f)[D / 16], const E *rows) {   // B operand: this wave's 32 rows
+    const E *p = rows + (size_t)col * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) f[ks] = *reinterpret_cast<const bf16x8 *>(p + 16 * ks);
+  };
+
+  f32x16 gamT[D / 32], dva[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    zero16(gamT[t]);
+    zero16(dva[t]);
+  }
+  float colsum = 0.f;
+  const float my_lam = (FOX && member) ? lam[krow + col] : 0.f;
+  bf16x8 vf[D / 16], kf[D / 16];
+  if (member) load_rows(vf, v + krow * D);
+  if (N - 1 >= c_low) {
+    stage(N - 1, (N - 1) & 1);
+    if (member && N - 1 > cp) load_rows(kf, levels + lev_head + lev_off(N - 1, cp, D) + (size_t)32 * kh * D);
+  }
+  for (int c = N - 1; c >= c_low; --c) {
+    const bool active = member && c > cp;
+    const int b = c & 1;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (c - 1 >= c_low) stage(c - 1, b ^ 1);
+    bf16x8 kn[D / 16];
+    const bool next_active = member && c - 1 > cp && c - 1 >= c_low;
+    if (next_active) load_rows(kn, levels + lev_head + lev_off(c - 1, cp, D) + (size_t)32 * kh * D);
+    const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *Qt = Qs + 64 * P;
+    const E *Os = reinterpret_cast<const E *>(sbuf + b * BUF + QB), *Ot = Os + 64 * P;
+    const E *Ms = reinterpret_cast<const E *>(sbuf + b * BUF + 2 * QB);
+    const float4 *qs = reinterpret_cast<const float4 *>(sbuf + b * BUF + 2 * QB + MB);
+    if (active) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        zero16(s[qt]);
+        zero16(dp[qt]);
+        const E *qa = Qs + (32 * qt + col) * P + 8 * g, *oa = Os + (32 * qt + col) * P + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          s[qt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(qa + 16 * ks), kf[ks], s[qt]);
+          dp[qt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(oa + 16 * ks), vf[ks], dp[qt]);
         }
       }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float4 st = qs[32 * qt + acc_row(r, g)];
+          const float p = __expf(scale * s[qt][r] + st.w - my_lam - st.x);
+          const float ds = p * (dp[qt][r] - st.y + st.z);
+          colsum += ds;
+          s[qt][r] = p;
+          dp[qt][r] = scale * ds;
+        }
+        st_tile(PW + 32 * qt, 1, P, s[qt], lane);   // P^T[key][q]
+      }
+      wave_sync();
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) mma_tile<E, C>(dva[t], PW, P, 1, Ot + 32 * t * P, P, 1, lane);
+      wave_sync();
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) st_tile(PW + 32 * qt, 1, P, dp[qt], lane);   // g^T[key][q]
+      wave_sync();
+      // Gamma^T(d, key) += sum_q Qa(q, d) g(q, key)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) mma_tile<E, C>(gamT[t], Qt + 32 * t * P, P, 1, PW, P, 1, lane);
+      if (c == cp + 1) {   // chunk c' is done: dKb = Gamma
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4 *>(dkb + (krow + col) * D + 32 * t + 8 * q4 + 4 * g) =
+                make_float4(gamT[t][4 * q4], gamT[t][4 * q4 + 1], gamT[t][4 * q4 + 2],
+                            gamT[t][4 * q4 + 3]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = kn[ks];
+    const int mch = c - 1;
+    if (!(mch > G * grp)) continue;
+    // ---- crossing of chunk m = c-1 by the group's chunks c' < m
+    const bool crosses = member && cp < mch;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      f32x16 z = gamT[t];
+      if (!crosses) zero16(z);
+      st_tile(gx + 32 * t * PGT + kbase, PGT, 1, z, lane);   // Gamma^T [d][KG]
+    }
+    lds_barrier();
+    {
+      constexpr int TILES = (D / 32) * (D / 32);
+      const int nch = mch - G * grp < G ? mch - G * grp : G;
+      float *dst = dmpart + (((size_t)bh * N + mch) * NG + grp) * D * D;
+      const size_t lm = lev_head + lev_off(mch, G * grp, D);
+      for (int tI = wv; tI < TILES; tI += NW) {
+        const int ta = tI / (D / 32), tb = tI % (D / 32);
+        f32x16 acc;
+        zero16(acc);
+        for (int j = 0; j < nch; ++j)
+          mma_tile<E, C>(acc, gx + 32 * ta * PGT + 64 * j, PGT, 1,
+                         levt + lm + (size_t)j * C * D + (size_t)32 * tb * C, C, 1, lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          dst[(size_t)(32 * ta + acc_row(r, g)) * D + 32 * tb + col] = -acc[r];
+      }
+    }
+    if (crosses) {   // Gamma^T <- Gamma^T + (-M_m^T) round(Gamma^T)
+      bf16x8 bfr[D / 16];
+#pragma unroll
+      for (int sI = 0; sI < D / 16; ++sI)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bfr[sI][t] = (E)gamT[sI / 2][8 * (sI % 2) + t];
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int sI = 0; sI < D / 16; ++sI)
+          gamT[mt] = MM<E>::mma(
+              *reinterpret_cast<const bf16x8 *>(Ms + (mt * (D / 16) + sI) * 512 + lane * 8),
+              bfr[sI], gamT[mt]);
     }
   }
   if (!member) return;
@@ -519,17 +700,24 @@ template <typename E, int D, bool FOX>
 static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   const int BH = a.BH, T = a.T, N = T / C;
   constexpr int G = group_of<E, D>();
-  E *lev = static_cast<E *>(a.levels);
+  E *lev = static_cast<E *>(a.levels), *levt = static_cast<E *>(a.levt);
+  const E *qae = (const E *)a.qae, *dout = (const E *)a.dout, *v = (const E *)a.v;
   if (N > 1)
-    hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb, a.m, lev,
-                       T, BH);
-  hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * N), dim3(256), 0, s, a.qa,
-                     (const E *)a.dout, a.lse, a.dlse, a.dvec, a.lam, lev, (const E *)a.v, a.scale,
-                     a.dqa, a.dlam, T, BH);
+    hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
+                       (const E *)a.nm, lev, levt, T, BH);
+  hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * N), dim3(256), 0, s, qae, dout, a.lse,
+                     a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH);
   const int NG = (N + G - 1) / G;
-  hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * NG), dim3(128 * G), 0, s, a.qa,
-                     (const E *)a.dout, a.lse, a.dlse, a.dvec, a.lam, lev, (const E *)a.v, a.m,
-                     a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
+  if constexpr (std::is_same<E, __bf16>::value && D == 64) {
+    static_assert(G == 4, "dk64_kernel takes groups of 4 key chunks");
+    hipLaunchKernelGGL((dk64_kernel<FOX>), dim3(BH * NG), dim3(512), 0, s, (const E *)a.qimg,
+                       (const E *)a.oimg, (const E *)a.mimg, (const float4 *)a.qst, a.lam, lev,
+                       levt, v, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
+  } else {
+    hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * NG), dim3(128 * G), 0, s, qae,
+                       (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam, lev,
+                       levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
+  }
   constexpr int XB = D * D / 256;
   hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * N * XB), dim3(256), 0, s, a.dmpart, a.dm, N,
                      D * D, XB);

@@ -151,7 +151,8 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
 // the key levels of one head take 64*D*N(N-1)/2 elements of the input dtype,
 // N = T/64.
 struct BwdLayout {
-  size_t qa, kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, total;
+  size_t qa, kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
+      nm, nmt, dot, levt, qimg, oimg, mimg, qst, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D, int dtype);
 size_t bwd_levels_elems(int BH, int T, int D);
@@ -161,6 +162,10 @@ size_t bwd_dmpart_floats(int dtype, int BH, int T, int D);
 // dKb, dV (+= onto the diagonal part), dLambda column sums, dM.
 struct SweepArgs {
   const float *qa, *kb, *m;
+  const void *qae, *qat, *nm, *nmt, *dot;   // input-dtype copies: Qa rows, Qa^T, -M, -M^T, dO^T
+  void *levt;                               // key levels transposed, [D][64] per (level, chunk)
+  // bf16, d = 64 only: per-chunk LDS images of the dk kernel's operands
+  const void *qimg, *oimg, *mimg, *qst;
   const void *dout, *v;
   const float *lse, *dlse, *dvec, *lam;
   void *levels;
@@ -169,6 +174,24 @@ struct SweepArgs {
   int BH, T;
 };
 hipError_t launch_bwd_sweep(int dtype, int D, bool fox, const SweepArgs &a, hipStream_t s);
+
+// LDS images of the bf16 d = 64 dk kernel, per 64-token chunk: rows padded
+// to kImgPitch elements.  qimg: Qa rows [64 q][64 d] then Qa^T rows [64 d][64
+// q]; oimg: the same for dO; mimg: -M^T as matrix-core A operand in fragment
+// order (blob (mt, s) of 64 lanes x 8 values: lane l holds
+// -M[frag_row(s, l/32, t)][32 mt + l%32], t < 8); qst: float4 (lse, rowdot(dO,
+// O), dlse, Lambda) per query.
+constexpr int kImgPitch = 72;
+constexpr int kQImgElems = 2 * 64 * kImgPitch;
+constexpr int kMImgElems = 64 * 64;
+// Position of -M[a][b] (d = 64) in the fragment-order image.
+__host__ __device__ inline int mimg_index(int a, int b) {
+  const int u = a / 32, w = a % 32;
+  const int r = 4 * (w / 8) + (w % 4), g = (w / 4) & 1;
+  const int rg = 16 * u + r, s = rg >> 3, t = rg & 7;
+  const int lane = 32 * g + (b % 32), mt = b / 32;
+  return (mt * 4 + s) * 512 + lane * 8 + t;
+}
 
 struct BwdArgs {
   const void *q, *k, *v, *w;

@@ -48,20 +48,43 @@ namespace pathattn {
 // the 32 x 32 output tile (w >> 1, w & 1).  In a tile, lane l register r
 // holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 (acc_row).
 
-// Floats of one panel: a 64 x K block (K <= 128) or a K x 64 block, each
+// Floats of one panel: a 64 x K block or a K x 64 block (K <= KMAX), each
 // stored with pitch (columns + 1) so row and column reads are conflict-free.
-constexpr int kPanelFloats = 128 * 65;
+__host__ __device__ constexpr int panel_floats(int kmax) { return kmax * 65 > 64 * (kmax + 1) ? kmax * 65 : 64 * (kmax + 1); }
 
-// dst[r][c] = src[r * ld + c] (times rscale[r] if given), r < rows, c < cols.
-template <typename T>
-__device__ __forceinline__ void load_panel(float *dst, const T *src, int ld, int rows, int cols,
-                                           const float *rscale, int tid) {
-  const int pitch = cols + 1;
-  for (int idx = tid; idx < rows * cols; idx += 256) {
-    const int r = idx / cols, c = idx - r * cols;
-    float v = (float)src[(size_t)r * ld + c];
-    if (rscale) v *= rscale[r];
-    dst[r * pitch + c] = v;
+__device__ __forceinline__ void load4(const float *p, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4 *>(p);
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
+__device__ __forceinline__ void load4(const __bf16 *p, float (&v)[4]) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (float)x[e];
+}
+
+// dst[r][c] = src[r * ld + c] (times rscale[r] if given) for a ROWS x COLS
+// block (rows 16-byte aligned for float, 8-byte for bf16; COLS % 4 == 0):
+// every thread issues its vector loads before its LDS stores.
+template <int ROWS, int COLS, typename T>
+__device__ __forceinline__ void load_panel(float *dst, const T *src, int ld, const float *rscale,
+                                           int tid) {
+  constexpr int CV = COLS / 4, PER = ROWS * CV / 256;
+  static_assert(ROWS * CV % 256 == 0, "panel must split evenly over 256 threads");
+  float v[PER][4];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int vi = tid + 256 * it, r = vi / CV, c4 = 4 * (vi % CV);
+    load4(src + (size_t)r * ld + c4, v[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int vi = tid + 256 * it, r = vi / CV, c4 = 4 * (vi % CV);
+    const float sc = rscale ? rscale[r] : 1.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[r * (COLS + 1) + c4 + e] = sc * v[it][e];
   }
 }
 
@@ -76,10 +99,10 @@ __device__ __forceinline__ void gmm(f32x16 &acc, const TXe *X, int ldx, const TY
                                     float *PX, float *PY, int tid,
                                     const float *yscale = nullptr) {
   __syncthreads();
-  if (TX) load_panel(PX, X, ldx, K, 64, nullptr, tid);
-  else load_panel(PX, X, ldx, 64, K, nullptr, tid);
-  if (TY) load_panel(PY, Y, ldy, 64, K, nullptr, tid);
-  else load_panel(PY, Y, ldy, K, 64, yscale, tid);
+  if (TX) load_panel<K, 64>(PX, X, ldx, nullptr, tid);
+  else load_panel<64, K>(PX, X, ldx, nullptr, tid);
+  if (TY) load_panel<64, K>(PY, Y, ldy, nullptr, tid);
+  else load_panel<K, 64>(PY, Y, ldy, yscale, tid);
   __syncthreads();
   const int lane = tid & 63, wv = tid >> 6, i = lane & 31, k0 = lane >> 5;
   constexpr int a_rs = TX ? 1 : K + 1, a_cs = TX ? 65 : 1;

@@ -251,13 +251,17 @@ def test_binding_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 # ---- backward
 
-def test_bwd_workspace_bytes():
+@pytest.mark.parametrize("dtype,esize", [(pa.F32, 4), (pa.BF16, 2)])
+@pytest.mark.parametrize("B,H,T,d", [(2, 16, 2048, 64), (1, 2, 256, 128)])
+def test_bwd_workspace_bytes(dtype, esize, B, H, T, d):
     lib = pa.load_library()
-    B, H, T, d = 2, 16, 2048, 64
-    n = lib.path_attn_bwd_workspace_bytes(B, H, T, d, pa.BF16)
+    n = lib.path_attn_bwd_workspace_bytes(B, H, T, d, dtype)
     BH, N = B * H, T // 64
-    levels = BH * N * (N - 1) // 2 * 64 * d * 4
-    assert levels < n < levels + BH * T * d * 4 * 16 + 1024 * (6 * 64 * d + 11 * 64 * 64) * 4
+    # key levels in rows and transposed (input dtype), dM partials per key-chunk group
+    G = (4 if d == 64 else 2) if dtype == pa.BF16 else (2 if d == 64 else 1)
+    big = 2 * BH * N * (N - 1) // 2 * 64 * d * esize + BH * N * ((N + G - 1) // G) * d * d * 4
+    # plus per-token and per-chunk arrays
+    assert big < n < big + BH * T * d * 4 * 24 + BH * N * (d * d + 64 * 64) * 4 * 16
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 100, 64, pa.F32) == 0   # whole chunks only
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 96, pa.F32) == 0
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 4) == 0
