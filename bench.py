@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu] [--cpu-heads N] [--traffic FILE]
-                    [--no-decode] [--decode-steps N]
+                    [--no-decode] [--decode-steps N] [--no-backward] [--backward-steps N]
 
 One step = one call of path_attn_fwd (gate prefix when present, chunk
 preparation and the streaming scan) over the whole workload, inputs already
@@ -20,7 +20,13 @@ the bf16 dense matrix-core peak of 2.5 PFLOP/s.  cpu_baseline times the fp64
 CPU oracle on a bounded sample (N whole heads) with all host threads and
 scales the rate to the full workload.  The decode object times decoding
 with in-place key refinement after the workload's prompt (prefill alignment of
-a float32 key cache, then decode steps), bound by HBM.
+a float32 key cache, then decode steps), bound by HBM.  The backward object
+times path_attn_bwd (all gradients, from the forward's out and lse and seeded
+cotangents dout, dlse) on the same workload: algorithmic flops
+B*H*T^2*(5d + 3d^2/64) (the causal products S, dP, dV, dQ, dK of 2d each per
+query-key pair, plus three d x d chunk-transition products per pair of 64-token
+chunks: key levels, the key-gradient transition and dM), without the
+recomputation the kernels do.
 """
 from __future__ import annotations
 
@@ -49,6 +55,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding measurement")
     ap.add_argument("--decode-steps", type=int, default=20,
                     help="timed decode steps after the prompt (decoding measurement)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -114,6 +122,7 @@ def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pre_ws = torch.empty(max(256, pa.load_library().path_attn_prefill_workspace_bytes(B, H, T, d)),
                          dtype=torch.uint8, device=q.device)
+    pa.path_attn_prefill_cache(cache, k, v, w, beta, logf, workspace=pre_ws)   # warm-up
     torch.cuda.synchronize()
     a.record(stream)
     pa.path_attn_prefill_cache(cache, k, v, w, beta, logf, workspace=pre_ws)
@@ -146,6 +155,43 @@ def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
             "roofline": {"kernel": "decode step (split-key refinement + combine)", "bound": "hbm",
                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": nbytes}}
+
+
+def bench_backward(wl, q, k, v, w, beta, logf, out, lse, args):
+    """path_attn_bwd over the whole workload (inputs, forward outputs and
+    cotangents resident in HBM, workspace preallocated)."""
+    import torch
+    import householder_position_encoding_amd as pa
+    import workloads
+    cot = workloads.cotangents(wl.dtype, wl.B, wl.H, wl.T, wl.d, seed=1000 + wl.seed)
+    dout = torch.from_numpy(cot["dout"]).to(q.device, q.dtype)
+    dlse = torch.from_numpy(cot["dlse"]).to(q.device)
+    dt_code = pa.BF16 if wl.dtype == "bf16" else pa.F32
+    ws = torch.empty(pa.path_attn_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.d, dt_code),
+                     dtype=torch.uint8, device=q.device)
+    fn = lambda: pa.path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, workspace=ws)
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    n = max(1, args.backward_steps)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    flops = float(wl.B * wl.H) * wl.T * wl.T * (5 * wl.d + 3 * wl.d * wl.d / 64.0)
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    res = {"ms": ms, "steps": n, "tokens_per_s": wl.n_tokens / (ms * 1e-3),
+           "workspace_gib": ws.numel() / 2**30,
+           "roofline": {"kernel": "path_attn_bwd (whole call)", "bound": "mfma", "achieved": tf,
+                        "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                        "flops_per_call": flops}}
+    del ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -280,6 +326,10 @@ def main():
                                    "ms": ms_copy, "gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
     if not args.no_decode:
         res["decode"] = bench_decode(wl, q, k, v, w, beta, logf, args, timed)
+    if not args.no_backward:
+        step()
+        torch.cuda.synchronize()
+        res["backward"] = bench_backward(wl, q, k, v, w, beta, logf, out, lse, args)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -125,13 +125,21 @@ __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
 // Each wave walks the levels of 32 keys of one key chunk c' < N-1 (blocks of
 // 2 waves, one per key half) and stores level c in rows [64 keys][D] and
 // transposed [D][64 keys] (both at lev_off(c, c')).  -M_c is read in the
-// input dtype from global memory (shared by every block of the head).
+// input dtype from global memory (shared by every block of the head), one
+// level ahead, before the level's stores: loads and stores share one counter
+// of outstanding memory operations, so a load issued behind a long train of
+// stores would wait for them.  The row layout is written from the LDS copy
+// of the rounded level (16-byte stores).
 template <typename E, int D>
 __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ kb,
                                                      const E *__restrict__ nm,
                                                      E *__restrict__ levels,
                                                      E *__restrict__ levt, int T, int BH) {
-  constexpr int P = D + MM<E>::PAD;
+  using frag = typename MM<E>::frag;
+  constexpr int KPL = MM<E>::KPL, KS = D / (2 * KPL);
+  constexpr bool PF = KPL > 1;          // bf16: -M_c fragments fetched one level ahead
+  constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
+  constexpr int P = D + EPV;            // rows stay 16-byte aligned
   __shared__ __attribute__((aligned(16))) E Xs[2 * 32 * P];
   const int N = T / C;
   const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
@@ -144,22 +152,57 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
   const size_t head = (size_t)bh * lev_off(N, 0, D);
-  for (int c = cp + 1; c < N; ++c) {
+  // B operand of step c: rows d' = 32 t + col of -M_c, contraction values k0.. of each k-step
+  using MF = frag[D / 32][PF ? KS : 1];
+  auto load_m = [&](int c, MF &mf) {
+    if constexpr (!PF) return;
+    const E *p = nm + ((size_t)bh * N + c) * D * D + (size_t)col * D + KPL * g;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mf[t][ks] = MM<E>::ld(p + (size_t)32 * t * D + 2 * KPL * ks, 1);
+  };
+  // one level: store level c, then (if c + 1 < N) step to level c + 1 with the
+  // fragments of -M_c in cur, fetching those of -M_{c+1} into nxt first
+  auto level = [&](int c, MF &cur, MF &nxt) {
     const size_t off = head + lev_off(c, cp, D);
+    if (c + 1 < N - 1) load_m(c + 1, nxt);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      st_tile(levels + off + (size_t)32 * wv * D + 32 * t, D, 1, x[t], lane);
       st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
+      st_tile(Xw + 32 * t, P, 1, x[t], lane);
     }
-    if (c + 1 >= N) break;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
     wave_sync();
+    // level rows from the LDS copy, 16 bytes per lane and store
+    E *dst = levels + off + (size_t)32 * wv * D;
+#pragma unroll
+    for (int j = 0; j < 32 * D / EPV / 64; ++j) {
+      const int vi = j * 64 + lane, row = vi / (D / EPV), c16 = EPV * (vi % (D / EPV));
+      *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
+          *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+    }
+    if (c + 1 >= N) return;
     // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
-    const E *nmc = nm + ((size_t)bh * N + c) * D * D;
+    const E *pa = Xw + col * P + KPL * g;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) mma_tile<E, D>(x[t], Xw, P, 1, nmc + 32 * t * D, D, 1, lane);
+    for (int t = 0; t < D / 32; ++t) {
+      if constexpr (PF) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          x[t] = MM<E>::mma(MM<E>::ld(pa + 2 * KPL * ks, 1), cur[t][ks], x[t]);
+      } else {
+        mma_tile<E, D>(x[t], Xw, P, 1, nm + ((size_t)bh * N + c) * D * D + (size_t)32 * t * D, D,
+                       1, lane);
+      }
+    }
     wave_sync();
+  };
+  MF ma, mb;
+  if (cp + 1 < N - 1) load_m(cp + 1, ma);
+  for (int c = cp + 1; c < N; c += 2) {
+    level(c, ma, mb);
+    if (c + 1 >= N) break;
+    level(c + 1, mb, ma);
   }
 }
 
@@ -191,9 +234,21 @@ __global__ __launch_bounds__(256) void dq_kernel(
     for (int idx = tid; idx < C * D; idx += 256) dqa[qrow * D + idx] = 0.f;
     return;
   }
-  for (int idx = tid; idx < C * D; idx += 256) {
-    Qs[(idx / D) * PQ + idx % D] = qae[qrow * D + idx];
-    Os[(idx / D) * PQ + idx % D] = dout[qrow * D + idx];
+  {
+    constexpr int EPV = 16 / sizeof(E);
+    static_assert(PQ % EPV == 0 || !std::is_same<E, __bf16>::value, "16-byte LDS rows");
+    if constexpr (std::is_same<E, __bf16>::value) {
+      for (int vi = tid; vi < C * D / EPV; vi += 256) {
+        const int r = vi / (D / EPV), c8 = EPV * (vi % (D / EPV));
+        *reinterpret_cast<uint4 *>(Qs + r * PQ + c8) = *reinterpret_cast<const uint4 *>(qae + (qrow + r) * D + c8);
+        *reinterpret_cast<uint4 *>(Os + r * PQ + c8) = *reinterpret_cast<const uint4 *>(dout + (qrow + r) * D + c8);
+      }
+    } else {
+      for (int idx = tid; idx < C * D; idx += 256) {
+        Qs[(idx / D) * PQ + idx % D] = qae[qrow * D + idx];
+        Os[(idx / D) * PQ + idx % D] = dout[qrow * D + idx];
+      }
+    }
   }
   const int myq = 32 * qh + col;
   const float q_lse = lse[qrow + myq], q_d = dvec[qrow + myq];
@@ -206,15 +261,52 @@ __global__ __launch_bounds__(256) void dq_kernel(
   const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
   E *Gw = Gs + wv * 32 * PG;
   __syncthreads();
-  for (int cp = c - 1; cp >= 0; --cp) {
+  // Matrix-core A operands of one key chunk for this wave: Khat[c]_{c'} rows
+  // (keys 32 kh..), V rows, Khat[c]_{c'}^T rows (d, contraction over keys
+  // 32 kh..); bf16 with d = 64 fetches the next key chunk's one step ahead.
+  using frag = typename MM<E>::frag;
+  constexpr int KPL = MM<E>::KPL, KSD = D / (2 * KPL), KSK = 32 / (2 * KPL);
+  constexpr bool PF = KPL > 1 && D == 64;
+  struct Frags {
+    frag k[PF ? KSD : 1], v[PF ? KSD : 1], kt[PF ? D / 32 : 1][PF ? KSK : 1];
+  };
+  auto fetch = [&](int cp, Frags &f) {
+    if constexpr (PF) {
+      const size_t blk = lev_c + (size_t)cp * C * D;
+      const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
+      const E *pk = levels + blk + (size_t)(32 * kh + col) * D + KPL * g;
+      const E *pv = v + (krow + col) * D + KPL * g;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        f.k[ks] = MM<E>::ld(pk + 2 * KPL * ks, 1);
+        f.v[ks] = MM<E>::ld(pv + 2 * KPL * ks, 1);
+      }
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          f.kt[t][ks] = MM<E>::ld(levt + blk + (size_t)(32 * t + col) * C + 32 * kh + KPL * g + 2 * KPL * ks, 1);
+    }
+  };
+  const E *qb = Qs + (32 * qh + col) * PQ + KPL * g, *ob = Os + (32 * qh + col) * PQ + KPL * g;
+  auto step = [&](int cp, Frags &fc, Frags &fn) {
     const size_t blk = lev_c + (size_t)cp * C * D;   // Khat[c]_{c'}
     const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
+    if (PF && cp >= 1) fetch(cp - 1, fn);
     // S^T and dP^T tiles: rows = keys 32 kh.., columns = queries 32 qh..
     f32x16 s, dp;
     zero16(s);
     zero16(dp);
-    mma_tile<E, D>(s, levels + blk + (size_t)32 * kh * D, D, 1, Qs + 32 * qh * PQ, PQ, 1, lane);
-    mma_tile<E, D>(dp, v + krow * D, D, 1, Os + 32 * qh * PQ, PQ, 1, lane);
+    if constexpr (PF) {
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        s = MM<E>::mma(fc.k[ks], MM<E>::ld(qb + 2 * KPL * ks, 1), s);
+        dp = MM<E>::mma(fc.v[ks], MM<E>::ld(ob + 2 * KPL * ks, 1), dp);
+      }
+    } else {
+      mma_tile<E, D>(s, levels + blk + (size_t)32 * kh * D, D, 1, Qs + 32 * qh * PQ, PQ, 1, lane);
+      mma_tile<E, D>(dp, v + krow * D, D, 1, Os + 32 * qh * PQ, PQ, 1, lane);
+    }
     f32x16 gt;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -228,9 +320,24 @@ __global__ __launch_bounds__(256) void dq_kernel(
     wave_sync();
     // dQa^T(d, q) += sum_key Khat(key, d) g(q, key)
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-      mma_tile<E, 32>(dq[t], levt + blk + (size_t)32 * t * C + 32 * kh, C, 1, Gw, PG, 1, lane);
+    for (int t = 0; t < D / 32; ++t) {
+      if constexpr (PF) {
+        const E *gb = Gw + col * PG + KPL * g;
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          dq[t] = MM<E>::mma(fc.kt[t][ks], MM<E>::ld(gb + 2 * KPL * ks, 1), dq[t]);
+      } else {
+        mma_tile<E, 32>(dq[t], levt + blk + (size_t)32 * t * C + 32 * kh, C, 1, Gw, PG, 1, lane);
+      }
+    }
     wave_sync();
+  };
+  Frags fa, fb;
+  fetch(c - 1, fa);
+  for (int cp = c - 1; cp >= 0; cp -= 2) {
+    step(cp, fa, fb);
+    if (cp - 1 < 0) break;
+    step(cp - 1, fb, fa);
   }
   // combine the two key halves, then store dQa rows
   float *rq = red + qh * 32 * (D + 1);
@@ -544,13 +651,13 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     stage(N - 1, (N - 1) & 1);
     if (member && N - 1 > cp) load_rows(kf, levels + lev_head + lev_off(N - 1, cp, D) + (size_t)32 * kh * D);
   }
-  for (int c = N - 1; c >= c_low; --c) {
+  // one step: query chunk c with level fragments kf; the next step's go to kn
+  auto step = [&](int c, bf16x8 (&kf)[D / 16], bf16x8 (&kn)[D / 16]) {
     const bool active = member && c > cp;
     const int b = c & 1;
     wait_vmcnt<0>();
     lds_barrier();
     if (c - 1 >= c_low) stage(c - 1, b ^ 1);
-    bf16x8 kn[D / 16];
     const bool next_active = member && c - 1 > cp && c - 1 >= c_low;
     if (next_active) load_rows(kn, levels + lev_head + lev_off(c - 1, cp, D) + (size_t)32 * kh * D);
     const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *Qt = Qs + 64 * P;
@@ -603,10 +710,8 @@ __global__ __launch_bounds__(512) void dk64_kernel(
                             gamT[t][4 * q4 + 3]);
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = kn[ks];
     const int mch = c - 1;
-    if (!(mch > G * grp)) continue;
+    if (!(mch > G * grp)) return;
     // ---- crossing of chunk m = c-1 by the group's chunks c' < m
     const bool crosses = member && cp < mch;
 #pragma unroll
@@ -647,6 +752,12 @@ __global__ __launch_bounds__(512) void dk64_kernel(
               *reinterpret_cast<const bf16x8 *>(Ms + (mt * (D / 16) + sI) * 512 + lane * 8),
               bfr[sI], gamT[mt]);
     }
+  };
+  bf16x8 kf2[D / 16];
+  for (int c = N - 1; c >= c_low; c -= 2) {
+    step(c, kf, kf2);
+    if (c - 1 < c_low) break;
+    step(c - 1, kf2, kf);
   }
   if (!member) return;
   if (cp == N - 1) {   // no later query chunk: dKb = 0
