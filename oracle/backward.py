@@ -72,6 +72,9 @@ def gradients(q, k, v, w, beta, logf, do, dlse=None, scale=None):
     if dlse is not None:
         loss = loss + (lse * torch.tensor(np.asarray(dlse, dtype=np.float64))).sum()
     loss.backward()
-    g = lambda x: None if x is None else x.grad.numpy().copy()
+    # an input the loss does not depend on (w, beta, log f when T = 1: H_0 and
+    # f_0 enter no logit) has no .grad; its gradient is exactly zero
+    g = lambda x: None if x is None else (x.grad.numpy().copy() if x.grad is not None
+                                          else np.zeros(tuple(x.shape)))
     return dict(dq=g(tq), dk=g(tk), dv=g(tv), dw=g(tw), dbeta=g(tb), dlogf=g(tf),
                 o=o.detach().numpy(), lse=lse.detach().numpy())
