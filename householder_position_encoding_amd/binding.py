@@ -370,7 +370,8 @@ def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
                   workspace=None, stream=None):
     """Gradients of <dout, out> + <dlse, lse> for the forward of path_attn_fwd
     (out, lse: that forward's outputs).  Returns (dq, dk, dv, dw, dbeta,
-    dlogf); dlogf is None without the gate.  T must be a multiple of 64."""
+    dlogf); dlogf is None without the gate.  Any T >= 1 (padded inside the
+    library as in the forward)."""
     torch = _torch()
     B, H, T, d, dt = _common(q, k, v, w, beta, logf)
     _check(out, "out", q.shape, q.dtype, q.device)

@@ -269,9 +269,44 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
 
 // ---------------------------------------------------------------- backward
 
+namespace {
+
+// Backward workspace: the layout at the padded length, then, only when T is
+// not a multiple of 64, zero-padded staging rows: q, k, v, w, out, dout and
+// dq, dk, dv, dw (input dtype), beta, logf, lse, dlse and dbeta, dlogf (fp32).
+// Padded tokens have identity factors and zero q, k, v, dout, dlse and gate,
+// and lse = 0: their logits are <= 0, so exp(s - lse) stays finite, and every
+// gradient contribution they make is exactly zero.
+struct BwdFull {
+  size_t vec[10], sca[6], total;
+  bool ragged;
+};
+
+BwdFull bwd_full(int B, int H, int T, int d, int dtype) {
+  const int Tp = padded(T);
+  BwdFull F{};
+  size_t off = bwd_layout(B, H, Tp, d, dtype).total;
+  F.ragged = Tp != T;
+  if (F.ragged) {
+    const size_t rows = (size_t)B * H * Tp;
+    for (size_t &o : F.vec) {
+      o = off;
+      off = align256(off + rows * d * elem_size(dtype));
+    }
+    for (size_t &o : F.sca) {
+      o = off;
+      off = align256(off + rows * 4);
+    }
+  }
+  F.total = off;
+  return F;
+}
+
+}  // namespace
+
 extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
-  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK || T % kChunk != 0) return 0;
-  return bwd_layout(B, H, T, d, dtype).total;
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  return bwd_full(B, H, T, d, dtype).total;
 }
 
 extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
@@ -282,7 +317,6 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
                              size_t workspace_bytes, void *stream) {
   const int st = check_shape(B, H, T, d, dtype);
   if (st != PATH_ATTN_OK) return st;
-  if (T % kChunk != 0) return PATH_ATTN_EUNSUPPORTED;   // whole chunks only
   if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
   const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace};
   for (const void *p : need)
@@ -291,8 +325,11 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
   for (const void *p : all)
     if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
-  if (!aligned(workspace, 256) || workspace_bytes < bwd_layout(B, H, T, d, dtype).total)
-    return PATH_ATTN_EINVAL;
+  const BwdFull F = bwd_full(B, H, T, d, dtype);
+  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H, Tp = padded(T);
+  char *ws = static_cast<char *>(workspace);
   BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -312,11 +349,44 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   a.dlogf = logf ? dlogf : nullptr;
   a.B = B;
   a.H = H;
-  a.T = T;
+  a.T = Tp;
   a.scale = scale_of(scale, d);
-  return launch_bwd(dtype, d, a, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? PATH_ATTN_OK
-             : PATH_ATTN_EHIP;
+  const int row = d * (int)elem_size(dtype);
+  if (F.ragged) {   // stage the inputs at the padded length
+    const void *vin[] = {q, k, v, w, out, dout};
+    const void **vdst[] = {&a.q, &a.k, &a.v, &a.w, &a.out, &a.dout};
+    for (int i = 0; i < 6; ++i) {
+      if (launch_copy_pad(vin[i], ws + F.vec[i], BH, T, Tp, T, row, s) != hipSuccess)
+        return PATH_ATTN_EHIP;
+      *vdst[i] = ws + F.vec[i];
+    }
+    const float *sin[] = {beta, logf, lse, dlse};
+    const float **sdst[] = {&a.beta, &a.logf, &a.lse, &a.dlse};
+    for (int i = 0; i < 4; ++i) {
+      if (!sin[i]) continue;
+      if (launch_copy_pad(sin[i], ws + F.sca[i], BH, T, Tp, T, 4, s) != hipSuccess)
+        return PATH_ATTN_EHIP;
+      *sdst[i] = reinterpret_cast<const float *>(ws + F.sca[i]);
+    }
+    a.dq = ws + F.vec[6];
+    a.dk = ws + F.vec[7];
+    a.dv = ws + F.vec[8];
+    a.dw = ws + F.vec[9];
+    a.dbeta = reinterpret_cast<float *>(ws + F.sca[4]);
+    if (logf) a.dlogf = reinterpret_cast<float *>(ws + F.sca[5]);
+  }
+  if (launch_bwd(dtype, d, a, workspace, s) != hipSuccess) return PATH_ATTN_EHIP;
+  if (F.ragged) {   // the first T rows of each head's gradients
+    void *vout[] = {dq, dk, dv, dw};
+    for (int i = 0; i < 4; ++i)
+      if (launch_copy_pad(ws + F.vec[6 + i], vout[i], BH, Tp, T, T, row, s) != hipSuccess)
+        return PATH_ATTN_EHIP;
+    if (launch_copy_pad(ws + F.sca[4], dbeta, BH, Tp, T, T, 4, s) != hipSuccess)
+      return PATH_ATTN_EHIP;
+    if (logf && launch_copy_pad(ws + F.sca[5], dlogf, BH, Tp, T, T, 4, s) != hipSuccess)
+      return PATH_ATTN_EHIP;
+  }
+  return PATH_ATTN_OK;
 }
 
 // ---------------------------------------------------------------- decoding

@@ -278,8 +278,9 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
  */
 
 /* Workspace bytes of path_attn_bwd, 0 for invalid or unsupported arguments.
- * It grows as B*H*d*T^2/128 floats (the aligned key levels): about 17 GB at
- * B=2, H=16, T=16384, d=64. */
+ * It grows as B*H*d*T^2/64 elements of the input dtype (the aligned key
+ * levels, stored in rows and transposed): about 27 GB at B=2, H=16, T=16384,
+ * d=64 in bf16. */
 size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 
 /*
@@ -297,11 +298,15 @@ size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
  *                                                      enters no logit)
  * scale: as for path_attn_fwd_ex (0 selects 1/sqrt(d)).  Gradients with
  * dtype PATH_ATTN_BF16 are computed in float32 and rounded once (RNE).
- * T must be a multiple of 64.  Every pointer 16-byte aligned, the workspace
+ * Any T >= 1: a T that is not a multiple of 64 is run at the next multiple
+ * with padded tokens as in the forward (identity factors, zero q, k, v, dout,
+ * dlse and gate, lse = 0), which contribute nothing to any gradient; the
+ * inputs are then staged in the workspace and the first T rows of the
+ * gradients copied back.  Every pointer 16-byte aligned, the workspace
  * 256-byte aligned.
  * Errors: EINVAL for null or misaligned pointers, a bad dtype or scale,
  * logf without dlogf, or a small workspace; EUNSUPPORTED for d not in
- * {64, 128}, T % 64 != 0 or B*H*T*d >= 2^31; EHIP on a launch error.
+ * {64, 128} or B*H*Tp*d >= 2^31; EHIP on a launch error.
  */
 int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
                   const float *beta, const float *logf, const void *out,

@@ -262,7 +262,8 @@ def test_bwd_workspace_bytes(dtype, esize, B, H, T, d):
     big = 2 * BH * N * (N - 1) // 2 * 64 * d * esize + BH * N * ((N + G - 1) // G) * d * d * 4
     # plus per-token and per-chunk arrays
     assert big < n < big + BH * T * d * 4 * 24 + BH * N * (d * d + 64 * 64) * 4 * 16
-    assert lib.path_attn_bwd_workspace_bytes(1, 1, 100, 64, pa.F32) == 0   # whole chunks only
+    # a ragged length runs at the next multiple of 64 plus staging rows
+    assert lib.path_attn_bwd_workspace_bytes(1, 1, 100, 64, pa.F32) > lib.path_attn_bwd_workspace_bytes(1, 1, 128, 64, pa.F32)
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 96, pa.F32) == 0
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 4) == 0
 
@@ -289,7 +290,7 @@ BAD_BWD = [
     (dict(logf=FAKE, dlogf=FAKE + 2), EINVAL),
     (dict(ws=FAKE + 64), EINVAL), (dict(wsb=100), EINVAL),
     (dict(scale=-1.0), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(dtype=5), EINVAL),
-    (dict(T=100), EUNSUP), (dict(d=96), EUNSUP), (dict(B=0), EINVAL),
+    (dict(T=100, wsb=100), EINVAL), (dict(T=0), EINVAL), (dict(d=96), EUNSUP), (dict(B=0), EINVAL),
     (dict(B=1 << 12, H=1 << 9, T=1 << 14), EUNSUP),
 ]
 

@@ -6,8 +6,9 @@ GPU backward, as a training step would use them.  The oracle recomputes
 everything in float64 from the same stored inputs and cotangents.
 
   * Small cases (several chunks, d = 64 and 128, with and without the gate,
-    with and without a gradient on lse): every gradient of every head
-    against oracle.backward.gradients (autograd of the definition).
+    with and without a gradient on lse, and lengths that are not a multiple
+    of 64): every gradient of every head against oracle.backward.gradients
+    (autograd of the definition).
   * The workloads at full size: sampled heads against
     oracle.chunked_backward.sweep_backward (the blockwise float64 statement,
     pinned to the autograd oracle on the CPU), the GPU run covering the whole
@@ -113,6 +114,32 @@ def test_backward_small_all_heads(case):
         for h in range(H):
             ref = oracle_gradients(*_head(inp, cot, b, h))
             _compare(f"small {case}", dtype, got, ref, b, h)
+
+
+RAGGED = [
+    # dtype, d, fox, dlse, B, H, T
+    ("f32", 64, True, True, 1, 2, 1),
+    ("f32", 64, False, True, 1, 1, 63),
+    ("f32", 128, True, False, 1, 1, 100),
+    ("bf16", 64, True, True, 2, 1, 130),
+    ("bf16", 128, False, True, 1, 2, 65),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "-".join(map(str, c)))
+def test_backward_ragged_length(case):
+    """Lengths that are not a multiple of 64: every gradient of every head
+    against the oracle on the unpadded sequence."""
+    dtype, d, fox, with_dlse, B, H, T = case
+    _log(f"backward ragged {case}")
+    inp = workloads.small(dtype, B, H, T, d, seed=80 + T + d, fox=fox, beta_sigma=1.5)
+    cot = workloads.cotangents(dtype, B, H, T, d, seed=180 + T + d, with_dlse=with_dlse)
+    got = _run_gpu(inp, cot, dtype)
+    assert got["dq"].shape == (B, H, T, d) and got["dbeta"].shape == (B, H, T)
+    for b in range(B):
+        for h in range(H):
+            ref = oracle_gradients(*_head(inp, cot, b, h))
+            _compare(f"ragged {case}", dtype, got, ref, b, h)
 
 
 def test_backward_custom_scale_and_near_reflections():
