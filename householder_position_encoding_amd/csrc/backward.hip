@@ -458,8 +458,8 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
   L.nm = take_e(BH * N * D * D);
   L.nmt = take_e(BH * N * D * D);
   L.dot = take_e(BH * T * D);
-  L.levt = take_e(bwd_levels_elems((int)BH, T, D));
-  const bool img = dtype == 1 && D == 64;
+  const bool img = dtype == 1 && D == 64;   // bf16, d = 64: operand images, no transposed levels
+  L.levt = take_e(img ? 0 : bwd_levels_elems((int)BH, T, D));
   L.qimg = take_e(img ? BH * N * kQImgElems : 0);
   L.oimg = take_e(img ? BH * N * kQImgElems : 0);
   L.mimg = take_e(img ? BH * N * kMImgElems : 0);

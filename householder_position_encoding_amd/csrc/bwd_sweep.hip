@@ -83,6 +83,9 @@ __device__ __forceinline__ void mma_tile(f32x16 &acc, const E *A, int ars, int a
     acc = MM<E>::mma(MM<E>::ld(pa + k * acs, acs), MM<E>::ld(pb + k * bcs, bcs), acc);
 }
 
+template <typename E>
+constexpr int KPL_OF() { return MM<E>::KPL; }
+
 __device__ __forceinline__ void zero16(f32x16 &a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) a[r] = 0.f;
@@ -123,7 +126,8 @@ __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
 }
 
 // Each wave walks the levels of 32 keys of one key chunk c' < N-1 (blocks of
-// 2 waves, one per key half) and stores level c in rows [64 keys][D] and
+// 2 waves, one per key half) and stores level c in rows [64 keys][D] and,
+// except for bf16 with d = 64 (whose consumers transpose on chip),
 // transposed [D][64 keys] (both at lev_off(c, c')).  -M_c is read in the
 // input dtype from global memory (shared by every block of the head), one
 // level ahead, before the level's stores: loads and stores share one counter
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
   using frag = typename MM<E>::frag;
   constexpr int KPL = MM<E>::KPL, KS = D / (2 * KPL);
   constexpr bool PF = KPL > 1;          // bf16: -M_c fragments fetched one level ahead
+  constexpr bool WT = !(KPL > 1 && D == 64);   // transposed copy (bf16, d = 64 transposes on chip)
   constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
   constexpr int P = D + EPV;            // rows stay 16-byte aligned
   __shared__ __attribute__((aligned(16))) E Xs[2 * 32 * P];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
     if (c + 1 < N - 1) load_m(c + 1, nxt);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
+      if (WT) st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
       st_tile(Xw + 32 * t, P, 1, x[t], lane);
     }
     wave_sync();
@@ -223,6 +228,8 @@ __global__ __launch_bounds__(256) void dq_kernel(
   __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
   __shared__ __attribute__((aligned(16))) E Os[C * PQ];
   __shared__ __attribute__((aligned(16))) E Gs[4 * 32 * PG];
+  // bf16, d = 64: per wave, the key block transposed [D][32 keys]
+  __shared__ __attribute__((aligned(16))) E KtS[(KPL_OF<E>() > 1 && D == 64) ? 4 * D * PG : 1];
   __shared__ float red[2 * 32 * (D + 1)];
   __shared__ float rsum[C];
   const int N = T / C;
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   constexpr int KPL = MM<E>::KPL, KSD = D / (2 * KPL), KSK = 32 / (2 * KPL);
   constexpr bool PF = KPL > 1 && D == 64;
   struct Frags {
-    frag k[PF ? KSD : 1], v[PF ? KSD : 1], kt[PF ? D / 32 : 1][PF ? KSK : 1];
+    frag k[PF ? KSD : 1], v[PF ? KSD : 1];
   };
   auto fetch = [&](int cp, Frags &f) {
     if constexpr (PF) {
@@ -281,11 +288,6 @@ __global__ __launch_bounds__(256) void dq_kernel(
         f.k[ks] = MM<E>::ld(pk + 2 * KPL * ks, 1);
         f.v[ks] = MM<E>::ld(pv + 2 * KPL * ks, 1);
       }
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int ks = 0; ks < KSK; ++ks)
-          f.kt[t][ks] = MM<E>::ld(levt + blk + (size_t)(32 * t + col) * C + 32 * kh + KPL * g + 2 * KPL * ks, 1);
     }
   };
   const E *qb = Qs + (32 * qh + col) * PQ + KPL * g, *ob = Os + (32 * qh + col) * PQ + KPL * g;
@@ -317,15 +319,23 @@ __global__ __launch_bounds__(256) void dq_kernel(
       gt[r] = scale * ds;
     }
     st_tile(Gw, 1, PG, gt, lane);   // Gw[q][key] = g(q, key)
+    if constexpr (PF) {   // this wave's key block transposed: Kt[d][key]
+      E *kt = KtS + wv * D * PG;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+        for (int t = 0; t < KPL; ++t) kt[(KPL * g + 2 * KPL * ks + t) * PG + col] = fc.k[ks][t];
+    }
     wave_sync();
     // dQa^T(d, q) += sum_key Khat(key, d) g(q, key)
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       if constexpr (PF) {
         const E *gb = Gw + col * PG + KPL * g;
+        const E *ka = KtS + wv * D * PG + (32 * t + col) * PG + KPL * g;
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
-          dq[t] = MM<E>::mma(fc.kt[t][ks], MM<E>::ld(gb + 2 * KPL * ks, 1), dq[t]);
+          dq[t] = MM<E>::mma(MM<E>::ld(ka + 2 * KPL * ks, 1), MM<E>::ld(gb + 2 * KPL * ks, 1), dq[t]);
       } else {
         mma_tile<E, 32>(dq[t], levt + blk + (size_t)32 * t * C + 32 * kh, C, 1, Gw, PG, 1, lane);
       }
@@ -714,25 +724,33 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     if (!(mch > G * grp)) return;
     // ---- crossing of chunk m = c-1 by the group's chunks c' < m
     const bool crosses = member && cp < mch;
+    // Khat[m]^T [d][KG] from the next step's level fragments (lane = key),
+    // written over buffer b's query rows, which this step no longer reads
+    E *Kx = reinterpret_cast<E *>(sbuf + b * BUF);
+    lds_barrier();   // every wave is done with buffer b's query operands
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       f32x16 z = gamT[t];
       if (!crosses) zero16(z);
       st_tile(gx + 32 * t * PGT + kbase, PGT, 1, z, lane);   // Gamma^T [d][KG]
     }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        Kx[(8 * g + 16 * ks + t) * PGT + kbase + col] = crosses ? kn[ks][t] : (E)0.f;
     lds_barrier();
     {
       constexpr int TILES = (D / 32) * (D / 32);
       const int nch = mch - G * grp < G ? mch - G * grp : G;
       float *dst = dmpart + (((size_t)bh * N + mch) * NG + grp) * D * D;
-      const size_t lm = lev_head + lev_off(mch, G * grp, D);
       for (int tI = wv; tI < TILES; tI += NW) {
         const int ta = tI / (D / 32), tb = tI % (D / 32);
         f32x16 acc;
         zero16(acc);
         for (int j = 0; j < nch; ++j)
-          mma_tile<E, C>(acc, gx + 32 * ta * PGT + 64 * j, PGT, 1,
-                         levt + lm + (size_t)j * C * D + (size_t)32 * tb * C, C, 1, lane);
+          mma_tile<E, C>(acc, gx + 32 * ta * PGT + 64 * j, PGT, 1, Kx + 32 * tb * PGT + 64 * j,
+                         PGT, 1, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           dst[(size_t)(32 * ta + acc_row(r, g)) * D + 32 * tb + col] = -acc[r];

@@ -257,9 +257,10 @@ def test_bwd_workspace_bytes(dtype, esize, B, H, T, d):
     lib = pa.load_library()
     n = lib.path_attn_bwd_workspace_bytes(B, H, T, d, dtype)
     BH, N = B * H, T // 64
-    # key levels in rows and transposed (input dtype), dM partials per key-chunk group
+    # key levels (input dtype), dM partials per key-chunk group
     G = (4 if d == 64 else 2) if dtype == pa.BF16 else (2 if d == 64 else 1)
-    big = 2 * BH * N * (N - 1) // 2 * 64 * d * esize + BH * N * ((N + G - 1) // G) * d * d * 4
+    copies = 1 if (dtype == pa.BF16 and d == 64) else 2   # rows, and transposed where needed
+    big = copies * BH * N * (N - 1) // 2 * 64 * d * esize + BH * N * ((N + G - 1) // G) * d * d * 4
     # plus per-token and per-chunk arrays
     assert big < n < big + BH * T * d * 4 * 24 + BH * N * (d * d + 64 * 64) * 4 * 16
     # a ragged length runs at the next multiple of 64 plus staging rows
