@@ -372,6 +372,163 @@ __global__ __launch_bounds__(256) void dq_kernel(
   }
 }
 
+// bf16, d = 64: one block of 2 waves per (bh, query chunk c); wave kh takes
+// keys 32 kh.. of each key chunk against all 64 queries, so each level block
+// is read from HBM once.  The key block's fragments (for S^T) are fetched one
+// key chunk ahead and transposed on chip for the dQa product.
+template <bool FOX>
+__global__ __launch_bounds__(128) void dq64_kernel(
+    const __bf16 *__restrict__ qae, const __bf16 *__restrict__ dout,
+    const float *__restrict__ lse, const float *__restrict__ dlse,
+    const float *__restrict__ dvec, const float *__restrict__ lam,
+    const __bf16 *__restrict__ levels, const __bf16 *__restrict__ v, float scale,
+    float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH) {
+  using E = __bf16;
+  constexpr int D = 64, PQ = D + 8, PG = 32 + 8, KS = D / 16;
+  __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
+  __shared__ __attribute__((aligned(16))) E Os[C * PQ];
+  // per wave g[q][key] and Khat^T[d][key]; at the end the key-half reduction
+  __shared__ __attribute__((aligned(16))) E pool[2 * C * PG + 2 * D * PG];
+  __shared__ float rsum[C];
+  E *Gs = pool, *KtS = pool + 2 * C * PG;
+  const int N = T / C;
+  const int bh = blockIdx.x % BH, c = N - 1 - blockIdx.x / BH;   // longest walks first
+  const int tid = threadIdx.x, lane = tid & 63, kh = tid >> 6, g = lane >> 5, col = lane & 31;
+  const size_t qrow = (size_t)bh * T + (size_t)c * C;
+  if (c == 0) {
+    for (int idx = tid; idx < C * D; idx += 128) dqa[qrow * D + idx] = 0.f;
+    return;
+  }
+  for (int vi = tid; vi < C * D / 8; vi += 128) {
+    const int r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
+    *reinterpret_cast<uint4 *>(Qs + r * PQ + c8) = *reinterpret_cast<const uint4 *>(qae + (qrow + r) * D + c8);
+    *reinterpret_cast<uint4 *>(Os + r * PQ + c8) = *reinterpret_cast<const uint4 *>(dout + (qrow + r) * D + c8);
+  }
+  float q_lse[2], q_d[2], q_dl[2], q_lam[2], rowsum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int q = 32 * qt + col;
+    q_lse[qt] = lse[qrow + q];
+    q_d[qt] = dvec[qrow + q];
+    q_dl[qt] = dlse ? dlse[qrow + q] : 0.f;
+    q_lam[qt] = FOX ? lam[qrow + q] : 0.f;
+  }
+  f32x16 dq[D / 32][2];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    zero16(dq[t][0]);
+    zero16(dq[t][1]);
+  }
+  const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
+  E *Gw = Gs + kh * C * PG, *Kt = KtS + kh * D * PG;
+  __syncthreads();
+  struct Frags {
+    bf16x8 k[KS], v[KS];
+  };
+  auto fetch = [&](int cp, Frags &f) {
+    const E *pk = levels + lev_c + (size_t)cp * C * D + (size_t)(32 * kh + col) * D + 8 * g;
+    const E *pv = v + ((size_t)bh * T + (size_t)cp * C + 32 * kh + col) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f.k[ks] = *reinterpret_cast<const bf16x8 *>(pk + 16 * ks);
+      f.v[ks] = *reinterpret_cast<const bf16x8 *>(pv + 16 * ks);
+    }
+  };
+  auto step = [&](int cp, Frags &fc, Frags &fn) {
+    const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
+    if (cp >= 1) fetch(cp - 1, fn);
+    float kl[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) kl[r] = FOX ? lam[krow + acc_row(r, g)] : 0.f;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      // S^T and dP^T: rows = this wave's 32 keys, columns = queries 32 qt..
+      f32x16 s, dp;
+      zero16(s);
+      zero16(dp);
+      const E *qb = Qs + (32 * qt + col) * PQ + 8 * g, *ob = Os + (32 * qt + col) * PQ + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = MM<E>::mma(fc.k[ks], *reinterpret_cast<const bf16x8 *>(qb + 16 * ks), s);
+        dp = MM<E>::mma(fc.v[ks], *reinterpret_cast<const bf16x8 *>(ob + 16 * ks), dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __expf(scale * s[r] + q_lam[qt] - kl[r] - q_lse[qt]);
+        const float ds = p * (dp[r] - q_d[qt] + q_dl[qt]);
+        rowsum[qt] += ds;
+        s[r] = scale * ds;
+      }
+      st_tile(Gw + 32 * qt * PG, 1, PG, s, lane);   // Gw[q][key] = g(q, key)
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)   // Kt[d][key]
+#pragma unroll
+      for (int t = 0; t < 8; ++t) Kt[(8 * g + 16 * ks + t) * PG + col] = fc.k[ks][t];
+    wave_sync();
+    // dQa^T(d, q) += sum_key Khat(key, d) g(q, key)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const E *ka = Kt + (32 * t + col) * PG + 8 * g;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const E *gb = Gw + (32 * qt + col) * PG + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          dq[t][qt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(ka + 16 * ks),
+                                 *reinterpret_cast<const bf16x8 *>(gb + 16 * ks), dq[t][qt]);
+      }
+    }
+    wave_sync();
+  };
+  Frags fa, fb;
+  fetch(c - 1, fa);
+  for (int cp = c - 1; cp >= 0; cp -= 2) {
+    step(cp, fa, fb);
+    if (cp - 1 < 0) break;
+    step(cp - 1, fb, fa);
+  }
+  // combine the two key halves (wave 1's partial through LDS, over Gs and KtS)
+  __syncthreads();
+  float *red = reinterpret_cast<float *>(pool);   // [64 q][D + 1] floats
+  static_assert(C * (D + 1) * 4 <= (2 * C * PG + 2 * D * PG) * 2, "reduction area");
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) rowsum[qt] += __shfl_xor(rowsum[qt], 32);
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[(32 * qt + col) * (D + 1) + 32 * t + acc_row(r, g)] = dq[t][qt][r];
+    if (g == 0) {
+      rsum[col] = rowsum[0];
+      rsum[32 + col] = rowsum[1];
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int q = 32 * qt + col;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * t + 8 * r4 + 4 * g;
+          float4 o;
+          o.x = dq[t][qt][4 * r4] + red[q * (D + 1) + d0];
+          o.y = dq[t][qt][4 * r4 + 1] + red[q * (D + 1) + d0 + 1];
+          o.z = dq[t][qt][4 * r4 + 2] + red[q * (D + 1) + d0 + 2];
+          o.w = dq[t][qt][4 * r4 + 3] + red[q * (D + 1) + d0 + 3];
+          *reinterpret_cast<float4 *>(dqa + (qrow + q) * D + d0) = o;
+        }
+      if (FOX && g == 0) dlam[qrow + q] += rowsum[qt] + rsum[q];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dk
 
 // LDS layout (elements of E) of the dk kernel.
@@ -834,8 +991,12 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   if (N > 1)
     hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
                        (const E *)a.nm, lev, levt, T, BH);
-  hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * N), dim3(256), 0, s, qae, dout, a.lse,
-                     a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH);
+  if constexpr (std::is_same<E, __bf16>::value && D == 64)
+    hipLaunchKernelGGL((dq64_kernel<FOX>), dim3(BH * N), dim3(128), 0, s, qae, dout, a.lse, a.dlse,
+                       a.dvec, a.lam, lev, v, a.scale, a.dqa, a.dlam, T, BH);
+  else
+    hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * N), dim3(256), 0, s, qae, dout, a.lse,
+                       a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH);
   const int NG = (N + G - 1) / G;
   if constexpr (std::is_same<E, __bf16>::value && D == 64) {
     static_assert(G == 4, "dk64_kernel takes groups of 4 key chunks");
