@@ -123,12 +123,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
       qat[(size_t)chunk * D * C + (size_t)d * C + i] = (E)x;
       if (IMG) {
         E *img = qimg + (size_t)chunk * kQImgElems;
-        img[i * kImgPitch + d] = (E)x;
-        img[64 * kImgPitch + d * kImgPitch + i] = (E)x;
+        img[i * kImgPitch + d] = (E)x;                  // rows
+        img[64 * kImgPitch + mimg_index(i, d)] = (E)x;  // fragment order
       }
     });
   if (IMG)   // zero padding of the image rows
-    for (int idx = tid; idx < 2 * 64 * (kImgPitch - 64); idx += NT)
+    for (int idx = tid; idx < 64 * (kImgPitch - 64); idx += NT)
       qimg[(size_t)chunk * kQImgElems + (idx / (kImgPitch - 64)) * kImgPitch + 64 +
            idx % (kImgPitch - 64)] = (E)0.f;
   }
@@ -216,11 +216,12 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     dot[((size_t)bh * N + c) * C * D + idx] = (E)Os[(idx % C) * DP + idx / C];
   if (IMG) {
     E *img = oimg + ((size_t)bh * N + c) * kQImgElems;
-    for (int idx = tid; idx < 64 * kImgPitch; idx += NT) {
+    for (int idx = tid; idx < 64 * kImgPitch; idx += NT) {   // dO rows
       const int r = idx / kImgPitch, cc = idx % kImgPitch;
-      img[idx] = cc < 64 ? (E)Os[r * DP + cc] : (E)0.f;                       // dO rows
-      img[64 * kImgPitch + idx] = cc < 64 ? (E)Os[cc * DP + r] : (E)0.f;      // dO^T rows
+      img[idx] = cc < 64 ? (E)Os[r * DP + cc] : (E)0.f;
     }
+    for (int idx = tid; idx < 64 * 64; idx += NT)   // dO in fragment order
+      img[64 * kImgPitch + mimg_index(idx / 64, idx % 64)] = (E)Os[(idx / 64) * DP + idx % 64];
     if (tid < C) qst[row0 + tid] = make_float4(rl[tid], rd[tid], rdl[tid], rg[tid]);
   }
   const float *al_c = al + ((size_t)bh * N + c) * C * C;

@@ -746,14 +746,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Same walk as dk_kernel for bf16 inputs and d = 64, G = 4 key chunks per
-// block (8 waves).  The query-side operands of step c (Qa and dO rows and
-// transposes, -M_{c-1}^T in fragment order, per-query statistics: 45 KiB of
-// per-chunk images) are copied straight into one of two LDS buffers one step
-// ahead (global_load_lds); V and the level rows Khat[c]_{c'} are matrix-core
-// B operands held in registers, the latter loaded one step ahead.  Gamma is
-// kept transposed (d x keys) so that the transition Gamma^T <- Gamma^T +
-// (-M^T) round(Gamma^T) takes its B operand from the accumulators (the
-// contraction index permuted as frag_row, matched by the image of -M^T).
+// block (8 waves).  The query-side operands of step c (Qa and dO as rows and
+// in fragment order, -M_{c-1}^T in fragment order, per-query statistics: 43
+// KiB of per-chunk images) are copied straight into one of two LDS buffers one
+// step ahead (global_load_lds); V and the level rows Khat[c]_{c'} are
+// matrix-core B operands held in registers, the latter loaded one step ahead.
+// dV, Gamma and the S, dP tiles keep one key per lane (dV, Gamma transposed:
+// d x keys), so the products that contract over queries (dV^T += dO^T P,
+// Gamma^T += Qa^T g) and the transition Gamma^T <- Gamma^T + (-M^T)
+// round(Gamma^T) take their B operands straight from the accumulators (the
+// contraction index permuted as frag_row, matched by the fragment-order
+// images).
 template <bool FOX>
 __global__ __launch_bounds__(512) void dk64_kernel(
     const __bf16 *__restrict__ qimg, const __bf16 *__restrict__ oimg,
@@ -765,12 +768,12 @@ __global__ __launch_bounds__(512) void dk64_kernel(
   using E = __bf16;
   constexpr int D = 64, G = 4, NW = 8, P = kImgPitch, KG = 64 * G, PGT = KG + 8;
   constexpr int QB = kQImgElems * 2, MB = kMImgElems * 2, SB = 64 * 16;   // bytes
-  constexpr int BUF = 2 * QB + MB + SB;                                   // 45 KiB
+  constexpr int BUF = 2 * QB + MB + SB;                                   // 43 KiB
   constexpr int NCOPY = BUF / 1024;
   static_assert(BUF % 1024 == 0, "whole 1 KiB copies");
   __shared__ __attribute__((aligned(16))) unsigned char sbuf[2 * BUF];
-  __shared__ __attribute__((aligned(16))) E gx[D * PGT];
-  __shared__ __attribute__((aligned(16))) E pw[NW * 32 * P];
+  __shared__ __attribute__((aligned(16))) E gx[D * PGT];   // Gamma^T [d][KG] at crossings
+  __shared__ __attribute__((aligned(16))) E kx[D * PGT];   // Khat[m]^T [d][KG] at crossings
   const int N = T / C, NG = (N + G - 1) / G;
   const int grp = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
@@ -780,7 +783,6 @@ __global__ __launch_bounds__(512) void dk64_kernel(
   const bool member = cp < N;
   const int kbase = 64 * (wv >> 1) + 32 * kh;
   const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
-  E *PW = pw + wv * 32 * P;
   const int c_low = G * grp + 1;
 
   auto stage = [&](int c, int b) {
@@ -804,11 +806,11 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     for (int ks = 0; ks < D / 16; ++ks) f[ks] = *reinterpret_cast<const bf16x8 *>(p + 16 * ks);
   };
 
-  f32x16 gamT[D / 32], dva[D / 32];
+  f32x16 gamT[D / 32], dvT[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
     zero16(gamT[t]);
-    zero16(dva[t]);
+    zero16(dvT[t]);
   }
   float colsum = 0.f;
   const float my_lam = (FOX && member) ? lam[krow + col] : 0.f;
@@ -827,8 +829,8 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     if (c - 1 >= c_low) stage(c - 1, b ^ 1);
     const bool next_active = member && c - 1 > cp && c - 1 >= c_low;
     if (next_active) load_rows(kn, levels + lev_head + lev_off(c - 1, cp, D) + (size_t)32 * kh * D);
-    const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *Qt = Qs + 64 * P;
-    const E *Os = reinterpret_cast<const E *>(sbuf + b * BUF + QB), *Ot = Os + 64 * P;
+    const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *QF = Qs + 64 * P;
+    const E *Os = reinterpret_cast<const E *>(sbuf + b * BUF + QB), *OF = Os + 64 * P;
     const E *Ms = reinterpret_cast<const E *>(sbuf + b * BUF + 2 * QB);
     const float4 *qs = reinterpret_cast<const float4 *>(sbuf + b * BUF + 2 * QB + MB);
     if (active) {
@@ -844,6 +846,7 @@ __global__ __launch_bounds__(512) void dk64_kernel(
           dp[qt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(oa + 16 * ks), vf[ks], dp[qt]);
         }
       }
+      bf16x8 pf[4], gf[4];   // P and g as B operands: k-step s covers queries frag_row(s, g, .)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
@@ -852,21 +855,20 @@ __global__ __launch_bounds__(512) void dk64_kernel(
           const float p = __expf(scale * s[qt][r] + st.w - my_lam - st.x);
           const float ds = p * (dp[qt][r] - st.y + st.z);
           colsum += ds;
-          s[qt][r] = p;
-          dp[qt][r] = scale * ds;
+          pf[2 * qt + r / 8][r % 8] = (E)p;
+          gf[2 * qt + r / 8][r % 8] = (E)(scale * ds);
         }
-        st_tile(PW + 32 * qt, 1, P, s[qt], lane);   // P^T[key][q]
       }
-      wave_sync();
+      // dV^T(d, key) += sum_q dO(q, d) P(q, key);  Gamma^T(d, key) += sum_q Qa(q, d) g(q, key)
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) mma_tile<E, C>(dva[t], PW, P, 1, Ot + 32 * t * P, P, 1, lane);
-      wave_sync();
+      for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) st_tile(PW + 32 * qt, 1, P, dp[qt], lane);   // g^T[key][q]
-      wave_sync();
-      // Gamma^T(d, key) += sum_q Qa(q, d) g(q, key)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) mma_tile<E, C>(gamT[t], Qt + 32 * t * P, P, 1, PW, P, 1, lane);
+        for (int sI = 0; sI < 4; ++sI) {
+          dvT[mt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(OF + (mt * 4 + sI) * 512 + lane * 8),
+                               pf[sI], dvT[mt]);
+          gamT[mt] = MM<E>::mma(*reinterpret_cast<const bf16x8 *>(QF + (mt * 4 + sI) * 512 + lane * 8),
+                                gf[sI], gamT[mt]);
+        }
       if (c == cp + 1) {   // chunk c' is done: dKb = Gamma
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
@@ -881,10 +883,8 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     if (!(mch > G * grp)) return;
     // ---- crossing of chunk m = c-1 by the group's chunks c' < m
     const bool crosses = member && cp < mch;
-    // Khat[m]^T [d][KG] from the next step's level fragments (lane = key),
-    // written over buffer b's query rows, which this step no longer reads
-    E *Kx = reinterpret_cast<E *>(sbuf + b * BUF);
-    lds_barrier();   // every wave is done with buffer b's query operands
+    // Khat[m]^T [d][KG] from the next step's level fragments (lane = key)
+    E *Kx = kx;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       f32x16 z = gamT[t];
@@ -942,7 +942,15 @@ __global__ __launch_bounds__(512) void dk64_kernel(
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dv[(krow + acc_row(r, g)) * D + 32 * t + col] += dva[t][r];
+    for (int q4 = 0; q4 < 4; ++q4) {   // dV^T tile: this lane's key row, 4 consecutive d
+      float4 *p4 = reinterpret_cast<float4 *>(dv + (krow + col) * D + 32 * t + 8 * q4 + 4 * g);
+      float4 x = *p4;
+      x.x += dvT[t][4 * q4];
+      x.y += dvT[t][4 * q4 + 1];
+      x.z += dvT[t][4 * q4 + 2];
+      x.w += dvT[t][4 * q4 + 3];
+      *p4 = x;
+    }
   if (FOX) {
     colsum += __shfl_xor(colsum, 32);
     if (g == 0) dlam[krow + col] -= colsum;

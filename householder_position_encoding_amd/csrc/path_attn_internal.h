@@ -175,16 +175,18 @@ struct SweepArgs {
 };
 hipError_t launch_bwd_sweep(int dtype, int D, bool fox, const SweepArgs &a, hipStream_t s);
 
-// LDS images of the bf16 d = 64 dk kernel, per 64-token chunk: rows padded
-// to kImgPitch elements.  qimg: Qa rows [64 q][64 d] then Qa^T rows [64 d][64
-// q]; oimg: the same for dO; mimg: -M^T as matrix-core A operand in fragment
-// order (blob (mt, s) of 64 lanes x 8 values: lane l holds
-// -M[frag_row(s, l/32, t)][32 mt + l%32], t < 8); qst: float4 (lse, rowdot(dO,
-// O), dlse, Lambda) per query.
+// LDS images of the bf16 d = 64 dk kernel, per 64-token chunk.  A 64 x 64
+// matrix X in "fragment order" is the matrix-core A operand of a product that
+// contracts X's row index against accumulator registers: blob (mt, s) of 64
+// lanes x 8 values, lane l holding X[frag_row(s, l/32, t)][32 mt + l%32], t < 8
+// (mimg_index below).  qimg: Qa rows [64 q][64 d] padded to kImgPitch, then
+// Qa in fragment order; oimg: the same for dO; mimg: -M^T in fragment order
+// (X = -M, i.e. lane l holds -M[frag_row(s, l/32, t)][32 mt + l%32]); qst:
+// float4 (lse, rowdot(dO, O), dlse, Lambda) per query.
 constexpr int kImgPitch = 72;
-constexpr int kQImgElems = 2 * 64 * kImgPitch;
+constexpr int kQImgElems = 64 * kImgPitch + 64 * 64;
 constexpr int kMImgElems = 64 * 64;
-// Position of -M[a][b] (d = 64) in the fragment-order image.
+// Position of X[a][b] (64 x 64) in the fragment-order image.
 __host__ __device__ inline int mimg_index(int a, int b) {
   const int u = a / 32, w = a % 32;
   const int r = 4 * (w / 8) + (w % 4), g = (w / 4) & 1;
