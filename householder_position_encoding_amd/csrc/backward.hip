@@ -49,15 +49,15 @@ __host__ __device__ constexpr size_t saved_floats(int D) { return 5 * 4096 + 64 
 // Per-chunk adjoint intermediates: dA, dT2, dX, Y, dN, dB (64 x 64) and dUW (64 x D).
 __host__ __device__ constexpr size_t adj_floats(int D) { return 6 * 4096 + 64 * (size_t)D; }
 
-// One block per (bh, chunk), float32 matrix cores: Qa, Kb ([T][D]), M
+// One block per (bh, chunk), float32 matrix cores: Kb ([T][D]), M
 // ([N][D][D]), Al ([N][64][64], zero above the diagonal) and the saved
-// matrices of the chunk; for the matrix-core sweep also Qa in the input dtype
-// (rows [T][D] and per chunk transposed [D][64]) and -M, -M^T per chunk in the
-// input dtype.
+// matrices of the chunk; for the matrix-core sweep Qa and -M in the input
+// dtype (Qa rows [T][D], -M per chunk), and either the bf16 d = 64 operand
+// images or Qa^T and -M^T per chunk for the general kernel.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
-    const float *__restrict__ beta, float *__restrict__ qa, float *__restrict__ kb,
+    const float *__restrict__ beta, float *__restrict__ kb,
     float *__restrict__ m, float *__restrict__ al, float *__restrict__ saved, E *__restrict__ qae,
     E *__restrict__ qat, E *__restrict__ nm, E *__restrict__ nmt, E *__restrict__ qimg,
     E *__restrict__ mimg, int T) {
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const E *Q = q + row0 * D, *K = k + row0 * D, *W = w + row0 * D;
   float *Xg = saved + (size_t)chunk * saved_floats(D);
   float *Ug = Xg + 4096, *Ag = Ug + 4096, *Bg = Ag + 4096, *T2g = Bg + 4096, *UWg = T2g + 4096;
-  float *qa_c = qa + row0 * D, *kb_c = kb + row0 * D;
+  float *kb_c = kb + row0 * D;
   float *m_c = m + (size_t)chunk * D * D, *al_c = al + (size_t)chunk * C * C;
   if (tid < C) bs[tid] = beta[row0 + tid];
   f32x16 acc, acc2;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         const int a = 64 * ma + i, b = 64 * nb + j;
         m_c[(size_t)a * D + b] = acc[r];
         nm[(size_t)chunk * D * D + (size_t)a * D + b] = (E)(-acc[r]);
-        nmt[(size_t)chunk * D * D + (size_t)b * D + a] = (E)(-acc[r]);
+        if (!IMG) nmt[(size_t)chunk * D * D + (size_t)b * D + a] = (E)(-acc[r]);
         if (IMG) mimg[(size_t)chunk * kMImgElems + mimg_index(a, b)] = (E)(-acc[r]);
       });
     }
@@ -118,9 +118,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     tile_each(tid, [&](int i, int j, int r) {
       const int d = 64 * nb + j;
       const float x = (float)Q[i * D + d] - acc[r];
-      qa_c[i * D + d] = x;
       qae[(row0 + i) * D + d] = (E)x;
-      qat[(size_t)chunk * D * C + (size_t)d * C + i] = (E)x;
+      if (!IMG) qat[(size_t)chunk * D * C + (size_t)d * C + i] = (E)x;
       if (IMG) {
         E *img = qimg + (size_t)chunk * kQImgElems;
         img[i * kImgPitch + d] = (E)x;                  // rows
@@ -212,8 +211,9 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     rdl[tid] = dlse ? dlse[row0 + tid] : 0.f;
   }
   __syncthreads();
-  for (int idx = tid; idx < C * D; idx += NT)   // dO^T of the chunk, [D][64]
-    dot[((size_t)bh * N + c) * C * D + idx] = (E)Os[(idx % C) * DP + idx / C];
+  if (!IMG)
+    for (int idx = tid; idx < C * D; idx += NT)   // dO^T of the chunk, [D][64]
+      dot[((size_t)bh * N + c) * C * D + idx] = (E)Os[(idx % C) * DP + idx / C];
   if (IMG) {
     E *img = oimg + ((size_t)bh * N + c) * kQImgElems;
     for (int idx = tid; idx < 64 * kImgPitch; idx += NT) {   // dO rows
@@ -438,7 +438,6 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
     off = align256(off + floats * sizeof(float));
     return o;
   };
-  L.qa = take(BH * T * D);
   L.kb = take(BH * T * D);
   L.m = take(BH * N * D * D);
   L.al = take(BH * N * C * C);
@@ -454,11 +453,12 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
   L.dal = take(BH * N * C * C);
   L.saved = take(BH * N * saved_floats(D));
   auto take_e = [&](size_t elems) { return take((elems * esize + 3) / 4); };
+  const bool general = !(dtype == 1 && D == 64);   // the general dk kernel's operands
   L.qae = take_e(BH * T * D);
-  L.qat = take_e(BH * T * D);
+  L.qat = take_e(general ? BH * T * D : 0);
   L.nm = take_e(BH * N * D * D);
-  L.nmt = take_e(BH * N * D * D);
-  L.dot = take_e(BH * T * D);
+  L.nmt = take_e(general ? BH * N * D * D : 0);
+  L.dot = take_e(general ? BH * T * D : 0);
   const bool img = dtype == 1 && D == 64;   // bf16, d = 64: operand images, no transposed levels
   L.levt = take_e(img ? 0 : bwd_levels_elems((int)BH, T, D));
   L.qimg = take_e(img ? BH * N * kQImgElems : 0);
@@ -478,7 +478,7 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   const E *q = (const E *)a.q, *k = (const E *)a.k, *v = (const E *)a.v, *w = (const E *)a.w;
   auto e = [&](size_t off) { return reinterpret_cast<E *>(ws + off); };
   hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
-                     f(L.qa), f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
+                     f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
                      e(L.nmt), e(L.qimg), e(L.mimg), T);
   if (FOX) hipLaunchKernelGGL(bwd_gate_kernel, dim3(BH), dim3(NT), 0, s, a.logf, f(L.lam), T);
   hipLaunchKernelGGL((bwd_diag_kernel<E, D, FOX>), dim3(BH * N), dim3(NT), 0, s, f(L.al), v,
@@ -496,7 +496,6 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.oimg = ws + L.oimg;
   sa.mimg = ws + L.mimg;
   sa.qst = ws + L.qst;
-  sa.qa = f(L.qa);
   sa.kb = f(L.kb);
   sa.m = f(L.m);
   sa.dout = a.dout;

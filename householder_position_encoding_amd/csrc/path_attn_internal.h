@@ -151,7 +151,7 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
 // the key levels of one head take 64*D*N(N-1)/2 elements of the input dtype,
 // N = T/64.
 struct BwdLayout {
-  size_t qa, kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
+  size_t kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
       nm, nmt, dot, levt, qimg, oimg, mimg, qst, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D, int dtype);
@@ -161,7 +161,7 @@ size_t bwd_dmpart_floats(int dtype, int BH, int T, int D);
 // The quadratic part (bwd_sweep.hip): key levels, dQa (+ dLambda row sums),
 // dKb, dV (+= onto the diagonal part), dLambda column sums, dM.
 struct SweepArgs {
-  const float *qa, *kb, *m;
+  const float *kb, *m;
   const void *qae, *qat, *nm, *nmt, *dot;   // input-dtype copies: Qa rows, Qa^T, -M, -M^T, dO^T
   void *levt;                               // key levels transposed, [D][64] per (level, chunk)
   // bf16, d = 64 only: per-chunk LDS images of the dk kernel's operands
