@@ -57,6 +57,8 @@ def parse():
                     help="timed decode steps after the prompt (decoding measurement)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the strided / packed forward measurement")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
@@ -194,6 +196,61 @@ def bench_backward(wl, q, k, v, w, beta, logf, out, lse, args):
     return res
 
 
+def bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms_dense):
+    """The forward (and backward) on views of the same workload: q, k, v, w as
+    slices of one fused token-major [B, T, 4, H, d] projection buffer, beta
+    and log f of a [B, T, H, 2] buffer, out and lse into [B, T, H, ...]
+    buffers (strided); and the same tokens packed as [B*T, H, d] sequences
+    with cu_seqlens (packed).  Views are gathered into zero-padded staging and
+    the outputs scattered back, so the difference to the dense call is the
+    staging traffic: per (token, head) every input and output row is read
+    and written once more."""
+    import torch
+    import householder_position_encoding_amd as pa
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    dev, tdt = q.device, q.dtype
+    fused = torch.empty(B, T, 4, H, d, dtype=tdt, device=dev)
+    for i, x in enumerate((q, k, v, w)):
+        fused[:, :, i] = x.permute(0, 2, 1, 3)
+    sc = torch.zeros(B, T, H, 2, dtype=torch.float32, device=dev)
+    sc[..., 0] = beta.permute(0, 2, 1)
+    if logf is not None:
+        sc[..., 1] = logf.permute(0, 2, 1)
+    views = [fused[:, :, i].permute(0, 2, 1, 3) for i in range(4)]
+    vb = sc[..., 0].permute(0, 2, 1)
+    vl = None if logf is None else sc[..., 1].permute(0, 2, 1)
+    out_b = torch.empty(B, T, H, d, dtype=tdt, device=dev)
+    lse_b = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+    dt_code = pa.BF16 if wl.dtype == "bf16" else pa.F32
+    ws = torch.empty(pa.path_attn_varlen_workspace_bytes(B, H, T, d, dt_code),
+                     dtype=torch.uint8, device=dev)
+    n = max(1, args.steps // 2)
+    ms_strided = timed(lambda: pa.path_attn_fwd_varlen(
+        *views, vb, vl, out=out_b.permute(0, 2, 1, 3), lse=lse_b.permute(0, 2, 1),
+        workspace=ws), n)
+    # packed: the same tokens as B sequences of T tokens, token-major
+    flat = fused.view(B * T, 4, H, d)
+    pv = [flat[:, i] for i in range(4)]
+    scf = sc.view(B * T, H, 2)
+    pb, pl = scf[..., 0], (None if logf is None else scf[..., 1])
+    cu = torch.arange(0, B * T + 1, T, dtype=torch.int32, device=dev)
+    out_p = torch.empty(B * T, H, d, dtype=tdt, device=dev)
+    lse_p = torch.empty(B * T, H, dtype=torch.float32, device=dev)
+    ms_packed = timed(lambda: pa.path_attn_fwd_varlen(
+        *pv, pb, pl, cu_seqlens=cu, max_seqlen=T, out=out_p, lse=lse_p, workspace=ws), n)
+    e = 2 if wl.dtype == "bf16" else 4
+    # staging bytes: 4 input vectors + beta (+ log f) gathered (read + write),
+    # out and lse scattered (read + write)
+    per_row = 2 * (5 * d * e + 4 + (4 if logf is not None else 0) + 4)
+    nbytes = B * H * T * per_row
+    over = ms_strided - ms_dense
+    gbs = nbytes / (over * 1e-3) / 1e9 if over > 0 else None
+    return {"ms_dense": ms_dense, "ms_strided_fwd": ms_strided, "ms_packed_fwd": ms_packed,
+            "tokens_per_s_strided_fwd": wl.n_tokens / (ms_strided * 1e-3),
+            "staging_bytes": nbytes, "staging_ms": over,
+            "staging_gbs": gbs, "staging_frac_hbm": None if gbs is None else gbs / PEAK_HBM_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -324,6 +381,9 @@ def main():
         ms_copy = timed(lambda: dst.copy_(src), 5)
         res["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
                                    "ms": ms_copy, "gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
+    if not args.no_varlen:
+        res["varlen"] = bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = bench_decode(wl, q, k, v, w, beta, logf, args, timed)
     if not args.no_backward:

@@ -79,6 +79,17 @@ def load_library():
     lib.path_attn_bwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
                                   fp, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_bwd.restype = ci
+    lib.path_attn_varlen_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.path_attn_varlen_workspace_bytes.restype = sz
+    lib.path_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, vp, ci, ci, ci,
+                                         ci, ci, ctypes.c_float, ctypes.c_uint, vp, sz, vp]
+    lib.path_attn_fwd_varlen.restype = ci
+    lib.path_attn_bwd_varlen_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.path_attn_bwd_varlen_workspace_bytes.restype = sz
+    lib.path_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp,
+                                         vp, fp, fp, vp, vp, ci, ci, ci, ci, ci,
+                                         ctypes.c_float, vp, sz, vp]
+    lib.path_attn_bwd_varlen.restype = ci
     lib.path_attn_strerror.argtypes = [ci]
     lib.path_attn_strerror.restype = ctypes.c_char_p
     lib.path_attn_version.argtypes = []
@@ -393,4 +404,145 @@ def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
                            workspace.numel(), _stream_handle(stream))
     if st != 0:
         raise PathAttnError(st, "path_attn_bwd")
+    return dq, dk, dv, dw, dbeta, dlogf
+
+
+# ------------------------------------------------- strided and packed batches
+
+def path_attn_varlen_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) -> int:
+    return int(load_library().path_attn_varlen_workspace_bytes(B, H, T, d, dtype))
+
+
+def path_attn_bwd_varlen_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) -> int:
+    return int(load_library().path_attn_bwd_varlen_workspace_bytes(B, H, T, d, dtype))
+
+
+class _Views:
+    """Shapes and (s_b, s_h, s_t) element strides of the tensors of a varlen
+    call.  Without cu_seqlens the vectors are [B, H, T, d] views and the
+    scalars [B, H, T] views; with cu_seqlens (int32 CUDA tensor [B + 1]) the
+    vectors are token-major [total, H, d] views and the scalars [total, H]."""
+
+    def __init__(self, q, cu_seqlens, max_seqlen):
+        torch = _torch()
+        if q.device.type != "cuda":
+            raise ValueError("tensors must live on a GPU (no CPU path)")
+        self.device, self.dtype = q.device, q.dtype
+        self.packed = cu_seqlens is not None
+        if self.packed:
+            if q.dim() != 3:
+                raise ValueError("with cu_seqlens, q must be [total, H, d]")
+            if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or \
+                    cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
+                raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] tensor on q's device")
+            self.B = cu_seqlens.numel() - 1
+            if self.B < 1:
+                raise ValueError("cu_seqlens needs at least two entries")
+            total, self.H, self.d = q.shape
+            if max_seqlen is None:   # host read of the lengths (synchronises)
+                max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+            self.T = int(max_seqlen)
+            self.vshape, self.sshape = tuple(q.shape), (total, self.H)
+        else:
+            if q.dim() != 4:
+                raise ValueError("q must be [B, H, T, d]")
+            self.B, self.H, self.T, self.d = q.shape
+            self.vshape, self.sshape = tuple(q.shape), (self.B, self.H, self.T)
+
+    def strides(self, t, name, vector, dtype=None):
+        torch = _torch()
+        if t is None:
+            return (0, 0, 0)
+        want = dtype if dtype is not None else (self.dtype if vector else torch.float32)
+        shape = self.vshape if vector else self.sshape
+        if t.device != self.device:
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+        st = t.stride()
+        if vector and st[-1] != 1 and t.shape[-1] > 1:
+            raise ValueError(f"{name}: the d elements of a row must be contiguous")
+        if self.packed:
+            return (0, st[1], st[0])
+        return (st[0], st[1], st[2])
+
+    def new_vector(self):
+        return _torch().zeros(self.vshape, dtype=self.dtype, device=self.device)
+
+    def new_scalar(self):
+        return _torch().zeros(self.sshape, dtype=_torch().float32, device=self.device)
+
+
+def _stride_array(triples):
+    flat = [int(x) for tr in triples for x in tr]
+    return (ctypes.c_longlong * len(flat))(*flat)
+
+
+def path_attn_fwd_varlen(q, k, v, w, beta, logf=None, cu_seqlens=None, max_seqlen=None,
+                         out=None, lse=None, scale=None, flags=0, workspace=None, stream=None):
+    """PaTH attention forward on strided views or packed sequences
+    (path_attn_fwd_varlen of the C ABI).
+
+    Without cu_seqlens: q, k, v, w are [B, H, T, d] views with any strides
+    (each row's d elements contiguous), beta and logf [B, H, T] views.  With
+    cu_seqlens (int32 CUDA [B + 1], the start of each sequence in tokens):
+    q, k, v, w are token-major [total, H, d] views, beta and logf [total, H],
+    and each sequence is attended on its own; max_seqlen is the longest
+    sequence (read from cu_seqlens, with a synchronisation, if None).
+    Returns (out, lse) of the vector and scalar shapes (new zero-filled
+    tensors unless given; rows outside every sequence are not written).
+    """
+    V = _Views(q, cu_seqlens, max_seqlen)
+    out = V.new_vector() if out is None else out
+    lse = V.new_scalar() if lse is None else lse
+    tensors = [(q, "q", True), (k, "k", True), (v, "v", True), (w, "w", True),
+               (out, "out", True), (beta, "beta", False), (logf, "logf", False),
+               (lse, "lse", False)]
+    strides = _stride_array(V.strides(t, n, vec) for t, n, vec in tensors)
+    lib = load_library()
+    dt = _dtype_code(q)
+    need = lib.path_attn_varlen_workspace_bytes(V.B, V.H, V.T, V.d, dt)
+    if workspace is None:
+        workspace = _torch().empty(max(need, 256), dtype=_torch().uint8, device=q.device)
+    st = lib.path_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                                  _ptr(out), _ptr(lse), strides, _ptr(cu_seqlens), V.B, V.H,
+                                  V.T, V.d, dt, 0.0 if scale is None else float(scale),
+                                  int(flags), _ptr(workspace), workspace.numel(),
+                                  _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_fwd_varlen")
+    return out, lse
+
+
+def path_attn_bwd_varlen(q, k, v, w, beta, logf, out, lse, dout, dlse=None, cu_seqlens=None,
+                         max_seqlen=None, scale=None, workspace=None, stream=None):
+    """Backward of path_attn_fwd_varlen (path_attn_bwd_varlen of the C ABI),
+    with the same views and cu_seqlens.  Returns (dq, dk, dv, dw, dbeta,
+    dlogf) as new zero-filled tensors of the vector and scalar shapes; dlogf
+    is None without the gate."""
+    V = _Views(q, cu_seqlens, max_seqlen)
+    dq, dk, dv, dw = (V.new_vector() for _ in range(4))
+    dbeta = V.new_scalar()
+    dlogf = None if logf is None else V.new_scalar()
+    tensors = [(q, "q", True), (k, "k", True), (v, "v", True), (w, "w", True),
+               (out, "out", True), (dout, "dout", True), (dq, "dq", True), (dk, "dk", True),
+               (dv, "dv", True), (dw, "dw", True), (beta, "beta", False),
+               (logf, "logf", False), (lse, "lse", False), (dlse, "dlse", False),
+               (dbeta, "dbeta", False), (dlogf, "dlogf", False)]
+    strides = _stride_array(V.strides(t, n, vec) for t, n, vec in tensors)
+    lib = load_library()
+    dt = _dtype_code(q)
+    need = lib.path_attn_bwd_varlen_workspace_bytes(V.B, V.H, V.T, V.d, dt)
+    if workspace is None:
+        workspace = _torch().empty(max(need, 256), dtype=_torch().uint8, device=q.device)
+    st = lib.path_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                                  _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf),
+                                  strides, _ptr(cu_seqlens), V.B, V.H, V.T, V.d, dt,
+                                  0.0 if scale is None else float(scale), _ptr(workspace),
+                                  workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_bwd_varlen")
     return dq, dk, dv, dw, dbeta, dlogf

@@ -28,22 +28,23 @@ int check_shape(int B, int H, int T, int d, int dtype) {
   return PATH_ATTN_OK;
 }
 
-// Workspace: the per-chunk layout at the padded length, then, only when T is
-// not a multiple of 64, zero-padded staging copies of the inputs and outputs.
+// Workspace: the per-chunk layout at the padded length, then, when T is not a
+// multiple of 64 or the tensors are general views, zero-padded staging copies
+// of the inputs and outputs.
 struct FullLayout {
   Layout base;
-  bool ragged;
+  bool staged;
   size_t q, k, v, w, beta, logf, out, lse, total;
 };
 
-FullLayout full_layout(int B, int H, int T, int d, int dtype) {
+FullLayout full_layout(int B, int H, int T, int d, int dtype, bool views = false) {
   const int Tp = padded(T);
   const size_t e = elem_size(dtype);
   FullLayout F{};
   F.base = make_layout(B, H, Tp, d, e);
-  F.ragged = Tp != T;
+  F.staged = views || Tp != T;
   size_t off = F.base.total;
-  if (F.ragged) {
+  if (F.staged) {
     const size_t rows = (size_t)B * H * Tp;
     size_t *vecs[] = {&F.q, &F.k, &F.v, &F.w};
     for (size_t *o : vecs) {
@@ -61,6 +62,17 @@ FullLayout full_layout(int B, int H, int T, int d, int dtype) {
   }
   F.total = off;
   return F;
+}
+
+// Views of the forward tensors, in the order q, k, v, w, out, beta, logf, lse.
+struct FwdViews {
+  RowView v[8];
+};
+
+FwdViews dense_fwd_views(int H, int T, int d) {
+  FwdViews V;
+  for (int i = 0; i < 8; ++i) V.v[i] = dense_view(H, T, i < 5 ? d : 1);
+  return V;
 }
 
 int check_inputs(const void *q, const void *k, const void *v, const void *w,
@@ -94,8 +106,8 @@ struct Carved {
   FullLayout F;
 };
 
-Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
-  const FullLayout F = full_layout(B, H, T, d, dtype);
+Carved carve(void *workspace, int B, int H, int T, int d, int dtype, bool views = false) {
+  const FullLayout F = full_layout(B, H, T, d, dtype, views);
   char *base = static_cast<char *>(workspace);
   return Carved{reinterpret_cast<float *>(base + F.base.qa), base + F.base.kvm,
                 reinterpret_cast<float *>(base + F.base.al),
@@ -103,11 +115,11 @@ Carved carve(void *workspace, int B, int H, int T, int d, int dtype) {
                 reinterpret_cast<float2 *>(base + F.base.bnd), base, F};
 }
 
-// The streaming scan at the padded length; for a ragged length into the
-// staging outputs, then the first T rows of each head copied out.
+// The streaming scan at the padded length; with staging into the staging
+// outputs, then each existing row written to the caller's out and lse views.
 int run_stream(const Carved &ws, bool gate, unsigned flags,
-               unsigned long long *skipped, void *out, float *lse, int BH,
-               int T, int d, int dtype, float scale, hipStream_t s) {
+               unsigned long long *skipped, void *out, float *lse, int B, int H,
+               int T, int d, int dtype, float scale, const FwdViews &views, hipStream_t s) {
   const int Tp = padded(T);
   StreamArgs a;
   a.qa = ws.qa;
@@ -117,38 +129,42 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
   a.bnd = ws.bnd;
   a.skip = gate && !(flags & PATH_ATTN_NO_SKIP);
   a.skipped = skipped;
-  a.out = ws.F.ragged ? static_cast<void *>(ws.base + ws.F.out) : out;
-  a.lse = ws.F.ragged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
-  a.BH = BH;
+  a.out = ws.F.staged ? static_cast<void *>(ws.base + ws.F.out) : out;
+  a.lse = ws.F.staged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
+  a.BH = B * H;
   a.T = Tp;
   a.sl2 = 1.4426950408889634f * scale_of(scale, d);
   if (launch_stream(dtype, d, gate, a, s) != hipSuccess) return PATH_ATTN_EHIP;
-  if (ws.F.ragged) {
-    const int row = d * (int)elem_size(dtype);
-    if (launch_copy_pad(a.out, out, BH, Tp, T, T, row, s) != hipSuccess ||
-        launch_copy_pad(a.lse, lse, BH, Tp, T, T, 4, s) != hipSuccess)
+  if (ws.F.staged) {
+    const int e = (int)elem_size(dtype);
+    if (launch_view_rows(false, a.out, out, views.v[4], B, H, T, Tp, e, d * e, s) != hipSuccess ||
+        launch_view_rows(false, a.lse, lse, views.v[7], B, H, T, Tp, 4, 4, s) != hipSuccess)
       return PATH_ATTN_EHIP;
   }
   return PATH_ATTN_OK;
 }
 
 // Enqueue the gate prefix (if any) and the chunk preparation, at the padded
-// length (inputs first copied into the zero-padded staging when ragged).
+// length (inputs first gathered into the zero-padded staging when staged).
 int run_prep(const void *q, const void *k, const void *v, const void *w,
-             const float *beta, const float *logf, const Carved &ws, int BH,
-             int T, int d, int dtype, hipStream_t s) {
-  const int Tp = padded(T);
-  if (ws.F.ragged) {
-    const int row = d * (int)elem_size(dtype);
+             const float *beta, const float *logf, const Carved &ws, int B, int H,
+             int T, int d, int dtype, const FwdViews &views, hipStream_t s) {
+  const int Tp = padded(T), BH = B * H;
+  if (ws.F.staged) {
+    const int e = (int)elem_size(dtype);
     char *b = ws.base;
     const void *src[] = {q, k, v, w};
     const size_t dst[] = {ws.F.q, ws.F.k, ws.F.v, ws.F.w};
     for (int i = 0; i < 4; ++i)
-      if (launch_copy_pad(src[i], b + dst[i], BH, T, Tp, T, row, s) != hipSuccess)
+      if (launch_view_rows(true, src[i], b + dst[i], views.v[i], B, H, T, Tp, e, d * e, s) !=
+          hipSuccess)
         return PATH_ATTN_EHIP;
-    if (launch_copy_pad(beta, b + ws.F.beta, BH, T, Tp, T, 4, s) != hipSuccess)
+    if (launch_view_rows(true, beta, b + ws.F.beta, views.v[5], B, H, T, Tp, 4, 4, s) !=
+        hipSuccess)
       return PATH_ATTN_EHIP;
-    if (logf && launch_copy_pad(logf, b + ws.F.logf, BH, T, Tp, T, 4, s) != hipSuccess)
+    if (logf &&
+        launch_view_rows(true, logf, b + ws.F.logf, views.v[6], B, H, T, Tp, 4, 4, s) !=
+            hipSuccess)
       return PATH_ATTN_EHIP;
     q = b + ws.F.q;
     k = b + ws.F.k;
@@ -187,10 +203,11 @@ extern "C" int path_attn_fwd_ex(const void *q, const void *k, const void *v,
   if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Carved ws = carve(workspace, B, H, T, d, dtype);
-  const int BH = B * H;
-  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
+  const FwdViews views = dense_fwd_views(H, T, d);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
   if (st != PATH_ATTN_OK) return st;
-  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, BH, T, d, dtype, scale, s);
+  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, B, H, T, d, dtype, scale,
+                    views, s);
 }
 
 extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
@@ -202,6 +219,56 @@ extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
                           workspace, workspace_bytes, stream);
 }
 
+namespace {
+
+// A caller-described view: a row start at a 4-byte boundary for every row
+// (base pointer and each stride in bytes multiples of 4), strides >= 0 and
+// below 2^40 elements.  The strides of an absent (null) optional tensor are
+// not read.
+bool view_ok(const void *p, const long long *st, size_t esize) {
+  if (!p) return true;
+  if (!aligned(p, 4)) return false;
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || st[i] >= (1ll << 40) || (st[i] * (long long)esize) % 4 != 0) return false;
+  return true;
+}
+
+RowView make_view(const long long *st, const int *cu) { return RowView{cu, st[0], st[1], st[2]}; }
+
+}  // namespace
+
+extern "C" size_t path_attn_varlen_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  return full_layout(B, H, T, d, dtype, true).total;
+}
+
+extern "C" int path_attn_fwd_varlen(const void *q, const void *k, const void *v, const void *w,
+                                    const float *beta, const float *logf, void *out, float *lse,
+                                    const long long *strides, const int *cu_seqlens, int B,
+                                    int H, int T, int d, int dtype, float scale, unsigned flags,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!q || !k || !v || !w || !beta || !out || !lse || !strides || !workspace)
+    return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return PATH_ATTN_EINVAL;
+  const void *ptrs[] = {q, k, v, w, out, beta, logf, lse};
+  const size_t e = elem_size(dtype);
+  for (int i = 0; i < 8; ++i)
+    if (!view_ok(ptrs[i], strides + 3 * i, i < 5 ? e : 4)) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256) || workspace_bytes < full_layout(B, H, T, d, dtype, true).total)
+    return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carved ws = carve(workspace, B, H, T, d, dtype, true);
+  FwdViews views;
+  for (int i = 0; i < 8; ++i) views.v[i] = make_view(strides + 3 * i, cu_seqlens);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
+  if (st != PATH_ATTN_OK) return st;
+  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, B, H, T, d, dtype, scale,
+                    views, s);
+}
+
 extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
                                  const void *w, const float *beta,
                                  const float *logf, int B, int H, int T, int d,
@@ -211,7 +278,7 @@ extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,
                               workspace_bytes, B, H, T, d, dtype);
   if (st != PATH_ATTN_OK) return st;
   const Carved ws = carve(workspace, B, H, T, d, dtype);
-  return run_prep(q, k, v, w, beta, logf, ws, B * H, T, d, dtype,
+  return run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, dense_fwd_views(H, T, d),
                   static_cast<hipStream_t>(stream));
 }
 
@@ -231,8 +298,8 @@ extern "C" int path_attn_stream_ex(const void *workspace, size_t workspace_bytes
   if (skipped && !aligned(skipped, 8)) return PATH_ATTN_EINVAL;
   if (workspace_bytes < full_layout(B, H, T, d, dtype).total) return PATH_ATTN_EINVAL;
   const Carved ws = carve(const_cast<void *>(workspace), B, H, T, d, dtype);
-  return run_stream(ws, use_gate == 1, flags, skipped, out, lse, B * H, T, d, dtype, scale,
-                    static_cast<hipStream_t>(stream));
+  return run_stream(ws, use_gate == 1, flags, skipped, out, lse, B, H, T, d, dtype, scale,
+                    dense_fwd_views(H, T, d), static_cast<hipStream_t>(stream));
 }
 
 extern "C" int path_attn_stream(const void *workspace, size_t workspace_bytes,
@@ -259,7 +326,7 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Carved ws = carve(workspace, B, H, T, d, dtype);
   const int BH = B * H;
-  st = run_prep(q, k, v, w, beta, logf, ws, BH, T, d, dtype, s);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, dense_fwd_views(H, T, d), s);
   if (st != PATH_ATTN_OK) return st;
   if (launch_unpack(dtype, d, ws.qa, ws.kvm, ws.al, logf ? ws.gate : nullptr,
                     qa, kb, m, al, logf ? lam : nullptr, BH, T, s) != hipSuccess)
@@ -271,23 +338,24 @@ extern "C" int path_attn_chunk_prep(const void *q, const void *k, const void *v,
 
 namespace {
 
-// Backward workspace: the layout at the padded length, then, only when T is
-// not a multiple of 64, zero-padded staging rows: q, k, v, w, out, dout and
-// dq, dk, dv, dw (input dtype), beta, logf, lse, dlse and dbeta, dlogf (fp32).
-// Padded tokens have identity factors and zero q, k, v, dout, dlse and gate,
-// and lse = 0: their logits are <= 0, so exp(s - lse) stays finite, and every
-// gradient contribution they make is exactly zero.
+// Backward workspace: the layout at the padded length, then, when T is not a
+// multiple of 64 or the tensors are general views, zero-padded staging rows:
+// q, k, v, w, out, dout and dq, dk, dv, dw (input dtype), beta, logf, lse,
+// dlse and dbeta, dlogf (fp32).  Padded tokens have identity factors and zero
+// q, k, v, dout, dlse and gate, and lse = 0: their logits are <= 0, so
+// exp(s - lse) stays finite, and every gradient contribution they make is
+// exactly zero.
 struct BwdFull {
   size_t vec[10], sca[6], total;
-  bool ragged;
+  bool staged;
 };
 
-BwdFull bwd_full(int B, int H, int T, int d, int dtype) {
+BwdFull bwd_full(int B, int H, int T, int d, int dtype, bool views = false) {
   const int Tp = padded(T);
   BwdFull F{};
   size_t off = bwd_layout(B, H, Tp, d, dtype).total;
-  F.ragged = Tp != T;
-  if (F.ragged) {
+  F.staged = views || Tp != T;
+  if (F.staged) {
     const size_t rows = (size_t)B * H * Tp;
     for (size_t &o : F.vec) {
       o = off;
@@ -302,33 +370,16 @@ BwdFull bwd_full(int B, int H, int T, int d, int dtype) {
   return F;
 }
 
-}  // namespace
-
-extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
-  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
-  return bwd_full(B, H, T, d, dtype).total;
-}
-
-extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
-                             const float *beta, const float *logf, const void *out,
-                             const float *lse, const void *dout, const float *dlse, void *dq,
-                             void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
-                             int H, int T, int d, int dtype, float scale, void *workspace,
-                             size_t workspace_bytes, void *stream) {
-  const int st = check_shape(B, H, T, d, dtype);
-  if (st != PATH_ATTN_OK) return st;
-  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
-  const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace};
-  for (const void *p : need)
-    if (!p) return PATH_ATTN_EINVAL;
-  if (logf && !dlogf) return PATH_ATTN_EINVAL;
-  const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
-  for (const void *p : all)
-    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
-  const BwdFull F = bwd_full(B, H, T, d, dtype);
-  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int BH = B * H, Tp = padded(T);
+// Everything after argument checks: stage (gather) the inputs when staged,
+// run the backward at the padded length, scatter the gradients.  views holds
+// the 16 tensors in the order q, k, v, w, out, dout, dq, dk, dv, dw, beta,
+// logf, lse, dlse, dbeta, dlogf.
+int run_bwd(const void *q, const void *k, const void *v, const void *w, const float *beta,
+            const float *logf, const void *out, const float *lse, const void *dout,
+            const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta,
+            float *dlogf, int B, int H, int T, int d, int dtype, float scale,
+            const RowView *views, const BwdFull &F, void *workspace, hipStream_t s) {
+  const int Tp = padded(T);
   char *ws = static_cast<char *>(workspace);
   BwdArgs a{};
   a.q = q;
@@ -351,12 +402,13 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   a.H = H;
   a.T = Tp;
   a.scale = scale_of(scale, d);
-  const int row = d * (int)elem_size(dtype);
-  if (F.ragged) {   // stage the inputs at the padded length
+  const int e = (int)elem_size(dtype), row = d * e;
+  if (F.staged) {   // gather the inputs at the padded length
     const void *vin[] = {q, k, v, w, out, dout};
     const void **vdst[] = {&a.q, &a.k, &a.v, &a.w, &a.out, &a.dout};
     for (int i = 0; i < 6; ++i) {
-      if (launch_copy_pad(vin[i], ws + F.vec[i], BH, T, Tp, T, row, s) != hipSuccess)
+      if (launch_view_rows(true, vin[i], ws + F.vec[i], views[i], B, H, T, Tp, e, row, s) !=
+          hipSuccess)
         return PATH_ATTN_EHIP;
       *vdst[i] = ws + F.vec[i];
     }
@@ -364,7 +416,8 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
     const float **sdst[] = {&a.beta, &a.logf, &a.lse, &a.dlse};
     for (int i = 0; i < 4; ++i) {
       if (!sin[i]) continue;
-      if (launch_copy_pad(sin[i], ws + F.sca[i], BH, T, Tp, T, 4, s) != hipSuccess)
+      if (launch_view_rows(true, sin[i], ws + F.sca[i], views[10 + i], B, H, T, Tp, 4, 4, s) !=
+          hipSuccess)
         return PATH_ATTN_EHIP;
       *sdst[i] = reinterpret_cast<const float *>(ws + F.sca[i]);
     }
@@ -376,17 +429,86 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
     if (logf) a.dlogf = reinterpret_cast<float *>(ws + F.sca[5]);
   }
   if (launch_bwd(dtype, d, a, workspace, s) != hipSuccess) return PATH_ATTN_EHIP;
-  if (F.ragged) {   // the first T rows of each head's gradients
+  if (F.staged) {   // scatter the gradients of the rows that exist
     void *vout[] = {dq, dk, dv, dw};
     for (int i = 0; i < 4; ++i)
-      if (launch_copy_pad(ws + F.vec[6 + i], vout[i], BH, Tp, T, T, row, s) != hipSuccess)
+      if (launch_view_rows(false, ws + F.vec[6 + i], vout[i], views[6 + i], B, H, T, Tp, e, row,
+                           s) != hipSuccess)
         return PATH_ATTN_EHIP;
-    if (launch_copy_pad(ws + F.sca[4], dbeta, BH, Tp, T, T, 4, s) != hipSuccess)
+    if (launch_view_rows(false, ws + F.sca[4], dbeta, views[14], B, H, T, Tp, 4, 4, s) !=
+        hipSuccess)
       return PATH_ATTN_EHIP;
-    if (logf && launch_copy_pad(ws + F.sca[5], dlogf, BH, Tp, T, T, 4, s) != hipSuccess)
+    if (logf && launch_view_rows(false, ws + F.sca[5], dlogf, views[15], B, H, T, Tp, 4, 4, s) !=
+                    hipSuccess)
       return PATH_ATTN_EHIP;
   }
   return PATH_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  return bwd_full(B, H, T, d, dtype).total;
+}
+
+extern "C" size_t path_attn_bwd_varlen_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  return bwd_full(B, H, T, d, dtype, true).total;
+}
+
+extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
+                             const float *beta, const float *logf, const void *out,
+                             const float *lse, const void *dout, const float *dlse, void *dq,
+                             void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
+                             int H, int T, int d, int dtype, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  const int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
+  const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace};
+  for (const void *p : need)
+    if (!p) return PATH_ATTN_EINVAL;
+  if (logf && !dlogf) return PATH_ATTN_EINVAL;
+  const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
+  for (const void *p : all)
+    if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
+  const BwdFull F = bwd_full(B, H, T, d, dtype);
+  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
+  RowView views[16];
+  for (int i = 0; i < 16; ++i) views[i] = dense_view(H, T, i < 10 ? d : 1);
+  return run_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf, B,
+                 H, T, d, dtype, scale, views, F, workspace, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int path_attn_bwd_varlen(const void *q, const void *k, const void *v, const void *w,
+                                    const float *beta, const float *logf, const void *out,
+                                    const float *lse, const void *dout, const float *dlse,
+                                    void *dq, void *dk, void *dv, void *dw, float *dbeta,
+                                    float *dlogf, const long long *strides,
+                                    const int *cu_seqlens, int B, int H, int T, int d, int dtype,
+                                    float scale, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  const int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
+  const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace,
+                        strides};
+  for (const void *p : need)
+    if (!p) return PATH_ATTN_EINVAL;
+  if (logf && !dlogf) return PATH_ATTN_EINVAL;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return PATH_ATTN_EINVAL;
+  const void *all[] = {q, k, v, w, out, dout, dq, dk, dv, dw,
+                       beta, logf, lse, dlse, dbeta, dlogf};
+  const size_t e = elem_size(dtype);
+  for (int i = 0; i < 16; ++i)
+    if (!view_ok(all[i], strides + 3 * i, i < 10 ? e : 4)) return PATH_ATTN_EINVAL;
+  const BwdFull F = bwd_full(B, H, T, d, dtype, true);
+  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
+  RowView views[16];
+  for (int i = 0; i < 16; ++i) views[i] = make_view(strides + 3 * i, cu_seqlens);
+  return run_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf, B,
+                 H, T, d, dtype, scale, views, F, workspace, static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------- decoding

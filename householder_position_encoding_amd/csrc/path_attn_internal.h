@@ -130,10 +130,25 @@ hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,
                          float *kb, float *m, float *al, float *lam, int BH,
                          int T, hipStream_t stream);
 
-// Row copy with zero fill into / out of padded staging (pad.hip): dst[bh][t]
-// = t < n_copy ? src[bh][t] : 0 for t < dst_rows, rows of row_bytes bytes.
-hipError_t launch_copy_pad(const void *src, void *dst, int BH, int src_rows, int dst_rows,
-                           int n_copy, int row_bytes, hipStream_t stream);
+// A caller's [B, H, T, row] tensor as a view (pad.hip): row (b, h, t) starts at
+// element (off_b + t) * s_tok + b * s_b + h * s_h, off_b = cu ? cu[b] : 0, and
+// exists for t < (cu ? cu[b+1] - cu[b] : T).  cu is a device array of B + 1
+// sequence starts (packed batches) or null.
+struct RowView {
+  const int *cu;
+  long long s_b, s_h, s_tok;
+};
+// The view of a dense [B, H, T, row] tensor, row_elems elements per row.
+inline RowView dense_view(int H, int T, int row_elems) {
+  return RowView{nullptr, (long long)H * T * row_elems, (long long)T * row_elems, row_elems};
+}
+// gather: dst[b][h][t] (padded layout, Tp rows per head) = view row (b, h, t),
+// zero beyond the row's sequence; scatter: view row (b, h, t) = src[b][h][t]
+// for the rows that exist.  Rows are row_bytes bytes, copied in 16-byte words
+// where view_rows_vec16 holds, else 4-byte words.
+bool view_rows_vec16(const void *base, const RowView &view, int esize, int row_bytes);
+hipError_t launch_view_rows(bool gather, const void *src, void *dst, const RowView &view, int B,
+                            int H, int T, int Tp, int esize, int row_bytes, hipStream_t stream);
 
 // Decoding with in-place key refinement (decode.hip).
 size_t decode_partial_bytes(int BH, int T_cap, int D);

@@ -316,6 +316,80 @@ int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
                   float scale, void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* ------------------------------------------------------------------------
+ * Strided and packed (variable-length) batches.
+ *
+ * The same operation as path_attn_fwd_ex / path_attn_bwd (definition at the
+ * top of this header), with every tensor given as a view instead of a dense
+ * [B, H, T, ...] array; the pages' own listing takes dense [B, H, L, D]
+ * arrays of one length, so views and packing are this library's extension.
+ *
+ * A view row (b, h, t) of a tensor (d elements for q, k, v, w, out, dout and
+ * the vector gradients; one float32 for beta, logf, lse, dlse, dbeta, dlogf)
+ * starts at element
+ *
+ *     (off_b + t) * s_t + b * s_b + h * s_h        of that tensor's pointer,
+ *
+ * with off_b = cu_seqlens[b] for packed batches (cu_seqlens non-NULL) and 0
+ * otherwise; the d elements of a row are contiguous.  Sequence b has
+ * len_b = cu_seqlens[b+1] - cu_seqlens[b] tokens (T without cu_seqlens), and
+ * its tokens t < len_b are attended causally among themselves only: each
+ * sequence is its own path, with its own first factor and gate prefix, as
+ * if it were run alone.
+ *
+ *   strides    : HOST array of 3 long long per tensor, (s_b, s_h, s_t) in
+ *                elements of that tensor, in the tensor order stated below.
+ *                A packed token-major tensor [total, H, d] has (0, d, H*d);
+ *                a dense one [B, H, T, d] has (H*T*d, T*d, d); the strides of
+ *                an absent optional tensor (logf, dlse, dlogf when NULL) are
+ *                not read.
+ *   cu_seqlens : DEVICE int32 array of B + 1 sequence starts in tokens,
+ *                non-decreasing, with every len_b <= T; or NULL.  A length
+ *                above T is cut to T and a negative one read as 0 (the
+ *                library reads cu_seqlens only on the device, so it cannot
+ *                report them).
+ *   T          : the longest sequence (the padded per-sequence length is T
+ *                rounded up to 64; workspace and work scale with B*H*T).
+ *
+ * The caller guarantees that every existing row lies inside its allocation
+ * and that output rows do not overlap one another or any input.  Output
+ * rows of tokens t >= len_b are not written.  Pointers need 4-byte alignment
+ * and every stride times the element size must be a multiple of 4 bytes (an
+ * even stride for bf16); rows are moved 16 bytes at a time where base and
+ * strides allow.  The inputs are always gathered into zero-padded staging in
+ * the workspace (an extra read and write of each input and output) and the
+ * results scattered back.  Errors as for the dense entry points, plus EINVAL
+ * for a NULL strides, a negative stride or one of 2^40 elements or more, or a
+ * misaligned base or stride.
+ * ------------------------------------------------------------------------
+ */
+
+/* Workspace bytes of path_attn_fwd_varlen (0 for invalid arguments). */
+size_t path_attn_varlen_workspace_bytes(int B, int H, int T, int d, int dtype);
+
+/* Forward pass on views.  strides: 8 x 3 values for q, k, v, w, out, beta,
+ * logf, lse (in this order).  scale and flags as for path_attn_fwd_ex. */
+int path_attn_fwd_varlen(const void *q, const void *k, const void *v, const void *w,
+                         const float *beta, const float *logf, void *out, float *lse,
+                         const long long *strides, const int *cu_seqlens, int B,
+                         int H, int T, int d, int dtype, float scale, unsigned flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of path_attn_bwd_varlen (0 for invalid arguments). */
+size_t path_attn_bwd_varlen_workspace_bytes(int B, int H, int T, int d, int dtype);
+
+/* Backward pass on views.  strides: 16 x 3 values for q, k, v, w, out,
+ * dout, dq, dk, dv, dw, beta, logf, lse, dlse, dbeta, dlogf (in this order).
+ * out and lse are path_attn_fwd_varlen's outputs for the same inputs, views
+ * and cu_seqlens.  Other arguments as for path_attn_bwd. */
+int path_attn_bwd_varlen(const void *q, const void *k, const void *v, const void *w,
+                         const float *beta, const float *logf, const void *out,
+                         const float *lse, const void *dout, const float *dlse,
+                         void *dq, void *dk, void *dv, void *dw, float *dbeta,
+                         float *dlogf, const long long *strides, const int *cu_seqlens,
+                         int B, int H, int T, int d, int dtype, float scale,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable description of a status code. */
 const char *path_attn_strerror(int status);
 

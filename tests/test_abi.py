@@ -299,3 +299,109 @@ BAD_BWD = [
 @pytest.mark.parametrize("kw,status", BAD_BWD, ids=lambda x: str(x))
 def test_bwd_validation(kw, status):
     assert _bwd(pa.load_library(), **kw) == status
+
+
+# ---- strided and packed batches
+
+def test_varlen_workspace_bytes():
+    lib = pa.load_library()
+    for dt, e in ((pa.F32, 4), (pa.BF16, 2)):
+        # views are always staged: the dense layout plus 4 vector and 4 scalar staging arrays
+        dense = pa.path_attn_workspace_bytes(2, 3, 128, 64, dt)
+        n = pa.path_attn_varlen_workspace_bytes(2, 3, 128, 64, dt)
+        assert n >= dense + 6 * 128 * (5 * 64 * e + 3 * 4)
+        # a ragged dense call stages too, with the same layout
+        assert pa.path_attn_varlen_workspace_bytes(2, 3, 100, 64, dt) == \
+            pa.path_attn_workspace_bytes(2, 3, 100, 64, dt)
+        nb = lib.path_attn_bwd_varlen_workspace_bytes(2, 3, 128, 64, dt)
+        assert nb >= lib.path_attn_bwd_workspace_bytes(2, 3, 128, 64, dt) + \
+            6 * 128 * (10 * 64 * e + 6 * 4)
+        assert lib.path_attn_bwd_varlen_workspace_bytes(2, 3, 100, 64, dt) == \
+            lib.path_attn_bwd_workspace_bytes(2, 3, 100, 64, dt)
+    assert pa.path_attn_varlen_workspace_bytes(1, 1, 64, 80, pa.F32) == 0
+    assert lib.path_attn_bwd_varlen_workspace_bytes(0, 1, 64, 64, pa.F32) == 0
+
+
+def _dense_strides(n, H, T, d):
+    return [(H * T * d, T * d, d)] * n
+
+
+def _fwd_varlen(lib, strides=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE,
+             cu=None, B=1, H=2, T=256, d=64, dtype=pa.BF16, scale=0.0, flags=0, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    if strides is None:
+        strides = _dense_strides(5, a["H"], a["T"], a["d"]) + _dense_strides(3, a["H"], a["T"], 1)
+    arr = None if strides == "null" else binding._stride_array(strides)
+    return lib.path_attn_fwd_varlen(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"],
+                                    a["out"], a["lse"], arr, a["cu"], a["B"], a["H"], a["T"],
+                                    a["d"], a["dtype"], a["scale"], a["flags"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+def _with(strides_index, value, n_vec=5, n=8):
+    st = _dense_strides(n_vec, 2, 256, 64) + _dense_strides(n - n_vec, 2, 256, 1)
+    st[strides_index] = value
+    return st
+
+
+# every case fails validation (fake addresses, never launched on)
+BAD_FWD_VARLEN = [
+    (dict(strides="null"), EINVAL), (dict(q=None), EINVAL), (dict(out=None), EINVAL),
+    (dict(lse=None), EINVAL), (dict(beta=None), EINVAL), (dict(ws=None), EINVAL),
+    (dict(q=FAKE + 2), EINVAL), (dict(lse=FAKE + 2), EINVAL), (dict(cu=FAKE + 2), EINVAL),
+    (dict(logf=FAKE + 1), EINVAL), (dict(ws=FAKE + 64), EINVAL), (dict(wsb=100), EINVAL),
+    (dict(strides=_with(0, (-1, 64, 64))), EINVAL),        # negative stride
+    (dict(strides=_with(2, (0, 64, 65))), EINVAL),         # odd bf16 stride: 2-byte rows
+    (dict(strides=_with(4, (1 << 40, 64, 64))), EINVAL),   # stride too large
+    (dict(strides=_with(6, (0, -4, 1)), logf=FAKE), EINVAL),
+    (dict(scale=-1.0), EINVAL), (dict(flags=4), EINVAL), (dict(dtype=3), EINVAL),
+    (dict(T=0), EINVAL), (dict(d=96), EUNSUP), (dict(B=1 << 12, H=1 << 9, T=1 << 14), EUNSUP),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_FWD_VARLEN, ids=lambda x: str(x))
+def test_fwd_varlen_validation(kw, status):
+    assert _fwd_varlen(pa.load_library(), **kw) == status
+
+
+def _bwd_varlen(lib, strides=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE,
+             dout=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, dbeta=FAKE, dlogf=None,
+             cu=None, B=1, H=2, T=256, d=64, dtype=pa.BF16, scale=0.0, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    if strides is None:
+        strides = _dense_strides(10, a["H"], a["T"], a["d"]) + _dense_strides(6, a["H"], a["T"], 1)
+    arr = None if strides == "null" else binding._stride_array(strides)
+    return lib.path_attn_bwd_varlen(a["q"], a["k"], a["v"], a["w"], a["beta"], a["logf"],
+                                    a["out"], a["lse"], a["dout"], a["dlse"], a["dq"], a["dk"],
+                                    a["dv"], a["dw"], a["dbeta"], a["dlogf"], arr, a["cu"],
+                                    a["B"], a["H"], a["T"], a["d"], a["dtype"], a["scale"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+BAD_BWD_VARLEN = [
+    (dict(strides="null"), EINVAL), (dict(dout=None), EINVAL), (dict(dq=None), EINVAL),
+    (dict(dbeta=None), EINVAL), (dict(logf=FAKE), EINVAL),   # the gate needs dlogf
+    (dict(dk=FAKE + 2), EINVAL), (dict(dlse=FAKE + 1), EINVAL), (dict(cu=FAKE + 1), EINVAL),
+    (dict(wsb=100), EINVAL), (dict(ws=FAKE + 32), EINVAL), (dict(scale=float("inf")), EINVAL),
+    (dict(strides=_with(7, (0, 64, 63), n_vec=10, n=16)), EINVAL),
+    (dict(strides=_with(13, (-1, 0, 1), n_vec=10, n=16), dlse=FAKE), EINVAL),
+    (dict(T=0), EINVAL), (dict(d=32), EUNSUP), (dict(dtype=-1), EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_BWD_VARLEN, ids=lambda x: str(x))
+def test_bwd_varlen_validation(kw, status):
+    assert _bwd_varlen(pa.load_library(), **kw) == status
+
+
+def test_varlen_binding_needs_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 2, 64, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.path_attn_fwd_varlen(x, x, x, x, torch.zeros(1, 2, 64))
+    with pytest.raises(ValueError, match="GPU"):
+        pa.path_attn_bwd_varlen(x, x, x, x, torch.zeros(1, 2, 64), None, x, None, x)
