@@ -392,10 +392,17 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
 // -M^T, V^T) feeds two matrix instructions.  This halves the LDS operand reads
 // and the staging per unit of work; the price is about 250 registers per lane
 // (running tile, output and scores for 64 queries), i.e. two waves per SIMD.
-// The softmax exponentiates against the reference max m_ref = max(m_run,
-// mx - 8), so p <= 2^8 and the rare rescale of O and l comes after the
-// exponentials; the row sums are taken from the bf16-rounded weights that the
-// P.V products use (dot with (1, 1)), so numerator and denominator match.
+// Without the gate, a cross step exponentiates against the running max m_run
+// with no max pass over the block: the lane's sum of the weights bounds every
+// weight, and if it exceeds 2^11 (or is not finite) the block is redone
+// against m_ref = max(m_run, block max - 8) after rescaling O and l.  This is
+// the usual online softmax with another choice of reference (any reference
+// gives the same normalised result); the bound keeps every weight below 2^11,
+// far inside float32 and bf16 range.  With the gate (and on the diagonal) the
+// block max is taken first and the reference is max(m_run, mx - 8), so
+// p <= 2^8 and the rare rescale comes after the exponentials.  The row sums
+// are taken from the bf16-rounded weights that the P.V products use (dot with
+// (1, 1)), so numerator and denominator match.
 template <int D, bool FOX, int NQC, int PD>
 __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
     const float *__restrict__ qa, const __bf16 *__restrict__ kvm,
@@ -595,6 +602,42 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
           }
       }
       if (!skip_blk) {
+      if (!FOX) {
+        // weights against the running max without a max pass; a chunk whose
+        // weights exceed 2^11 (or are not finite) is redone against
+        // max(m_run, chunk max - 8) after rescaling O and l
+        frag pb[2][NSK];
+        float lsum[2];
+        bool big = false;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          lsum[j] = exp_pack(sc[j], sl2, m_run[j], pb[j]);
+          big = big || !(lsum[j] <= 2048.f);
+        }
+        if (__any(big)) {   // wave-uniform, rare
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[j][kb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+            const float m_new = fmaxf(m_run[j], mx - 8.f);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_new);
+            l_run[j] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < NDB; ++mb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[j][mb][r] *= alpha;
+            m_run[j] = m_new;
+            lsum[j] = exp_pack(sc[j], sl2, m_new, pb[j]);
+          }
+        }
+        l_run[0] += lsum[0];
+        l_run[1] += lsum[1];
+        pv(pb, vf_l);
+      } else {
       // online softmax in log2 units, x = S * scale * log2(e) + a_key; the
       // gate of a key is read once and applied to both column blocks
       float mx[2] = {-INFINITY, -INFINITY};
@@ -644,6 +687,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       l_run[0] += lsum[0];
       l_run[1] += lsum[1];
       pv(pb, vf_l);
+      }
       }
     }
 

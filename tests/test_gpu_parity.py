@@ -195,6 +195,29 @@ def test_sharp_attention_diagnostic():
     assert eo < 5e-2 and el < 5e-2
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_far_keys_above_running_max(dtype, d):
+    """Keys of the first chunk scaled by 5, so later queries meet logits far
+    above the maxima of their own diagonal blocks: the scan's reference max
+    must move up (weights of such a chunk would exceed 2^11 against the old
+    reference, which the scan detects and redoes).  Against the oracle on the
+    same values; the larger logits enlarge the bf16 rounding of the walk, so
+    bf16 is held to the looser bound of the sharp-attention case."""
+    inp = workloads.small(dtype, 1, 2, 256, d, seed=41 + d)
+    k = inp["k"].copy()
+    k[:, :, :64] *= 5.0
+    inp["k"] = workloads.bf16_round(k.astype(np.float32)).astype(k.dtype) if dtype == "bf16" else k
+    out, lse = run_hip(to_device(inp, dtype))
+    o_ref, l_ref = oracle_full(inp)
+    eo, el = np.max(np.abs(out - o_ref)), np.max(np.abs(lse - l_ref))
+    _log(f"far keys {dtype} d={d}: max|do|={eo:.3g} max|dlse|={el:.3g}")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    if dtype == "f32":
+        assert eo <= 1e-4 and el <= 1e-4
+    else:
+        assert eo < 5e-2 and el < 5e-2
+
+
 def test_bitwise_deterministic():
     """No atomics: two runs give identical bits."""
     inp = workloads.small("bf16", 2, 2, 512, 64, seed=3, fox=True)
