@@ -97,6 +97,21 @@ __device__ __forceinline__ void load_rows(bf16x8 (&f)[KS], const __bf16 *rows, i
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) f[ks] = *reinterpret_cast<const bf16x8 *>(p + 16 * ks);
 }
+// Inputs of one chunk staged in LDS at d = 64: a 64 x 64 bf16 tile, rows of
+// 128 bytes, the 16-byte column cc of row r stored at slot cc ^ (r & 7), so
+// eight consecutive rows of one column fall in eight different slots (the
+// fragment reads below are free of bank conflicts).
+__device__ __forceinline__ int sw_off(int r, int cc) { return r * 128 + ((cc ^ (r & 7)) << 4); }
+// load_rows from a staged tile: rows row0 + l%32, columns 8*(l/32) + 16*ks.
+template <int KS>
+__device__ __forceinline__ void load_rows_sw(bf16x8 (&f)[KS], const unsigned char *tile, int row0,
+                                             int lane) {
+  const int r = row0 + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    f[ks] = *reinterpret_cast<const bf16x8 *>(tile + sw_off(r, (lane >> 5) + 2 * ks));
+}
+
 template <int KS>
 __device__ __forceinline__ void mma_rows(f32x16 &acc, const bf16x8 (&a)[KS], const bf16x8 (&b)[KS]) {
 #pragma unroll
@@ -235,24 +250,63 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   // them, so their latencies overlap.
   f32x16 kq = zero16();
   f32x16 qinit[TPW], kinit[TPW];
+  // d = 64: q, k, v, w of the chunk (32 KiB) are copied once into slots 0
+  // and 1 (direct global-to-LDS copies, 8 per wave, rows swizzled as in
+  // sw_off) and every wave reads its operands from there; the slots are
+  // overwritten only after the barrier below.  d = 128 reads from global.
+  constexpr bool STAGE = D == 64;
+  const unsigned char *st_q = smem, *st_k = smem + 8192;
+  const unsigned char *st_v = smem + SLOT, *st_w = smem + SLOT + 8192;
+  if constexpr (STAGE) {
+    const __bf16 *src[4] = {qc, kc, vc, wc};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int job = wv + 4 * i, t = job >> 3, ch = job & 7;   // tensor, 8-row chunk
+      const int r = 8 * ch + (lane >> 3), cc = (lane & 7) ^ (r & 7);
+      unsigned char *dst = smem + (t >> 1) * SLOT + (t & 1) * 8192 + ch * 1024;
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void *)(src[t] + r * D + cc * 8),
+          (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+  }
   {
     const float bval = tid < C ? beta[row0 + tid] : 0.f;
     bf16x8 wm[KSD], wn[KSD], qn[KSD], kn[KSD], km[KSD];
-    load_rows<KSD>(wm, wc + 32 * mt * D, D, lane);
-    load_rows<KSD>(wn, wc + 32 * nt * D, D, lane);
-    load_rows<KSD>(qn, qc + 32 * nt * D, D, lane);
-    load_rows<KSD>(kn, kc + 32 * nt * D, D, lane);
-    load_rows<KSD>(km, kc + 32 * mt * D, D, lane);
     // <-Q^T and ->K^T start from Q^T and K^T: tiles (eb, xb) = (tau>>1, tau&1)
     bf16x4 qv[TPW][4], kv[TPW][4];
+    if constexpr (STAGE) {
+      __syncthreads();   // the staged inputs have landed
+      load_rows_sw<KSD>(wm, st_w, 32 * mt, lane);
+      load_rows_sw<KSD>(wn, st_w, 32 * nt, lane);
+      load_rows_sw<KSD>(qn, st_q, 32 * nt, lane);
+      load_rows_sw<KSD>(kn, st_k, 32 * nt, lane);
+      load_rows_sw<KSD>(km, st_k, 32 * mt, lane);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
+      for (int u = 0; u < TPW; ++u) {
+        const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
+        const int r = 32 * xb + n;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const size_t off = (size_t)(32 * xb + n) * D + 32 * eb + 8 * r4 + 4 * g;
-        qv[u][r4] = *reinterpret_cast<const bf16x4 *>(qc + off);
-        kv[u][r4] = *reinterpret_cast<const bf16x4 *>(kc + off);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int off = sw_off(r, 4 * eb + r4) + 8 * g;
+          qv[u][r4] = *reinterpret_cast<const bf16x4 *>(st_q + off);
+          kv[u][r4] = *reinterpret_cast<const bf16x4 *>(st_k + off);
+        }
+      }
+    } else {
+      load_rows<KSD>(wm, wc + 32 * mt * D, D, lane);
+      load_rows<KSD>(wn, wc + 32 * nt * D, D, lane);
+      load_rows<KSD>(qn, qc + 32 * nt * D, D, lane);
+      load_rows<KSD>(kn, kc + 32 * nt * D, D, lane);
+      load_rows<KSD>(km, kc + 32 * mt * D, D, lane);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const size_t off = (size_t)(32 * xb + n) * D + 32 * eb + 8 * r4 + 4 * g;
+          qv[u][r4] = *reinterpret_cast<const bf16x4 *>(qc + off);
+          kv[u][r4] = *reinterpret_cast<const bf16x4 *>(kc + off);
+        }
       }
     }
 #pragma unroll
@@ -289,7 +343,10 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     // d block db); register group h of the tile is blob (db, 2*mt + h).
     {
       bf16x8 vm[KSD];
-      load_rows<KSD>(vm, vc + 32 * mt * D, D, lane);
+      if constexpr (STAGE)
+        load_rows_sw<KSD>(vm, st_v, 32 * mt, lane);
+      else
+        load_rows<KSD>(vm, vc + 32 * mt * D, D, lane);
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int db = nt + 2 * u;
