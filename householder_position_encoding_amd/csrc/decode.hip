@@ -351,15 +351,158 @@ constexpr int kUnroll = 4;
 template <int D>
 __host__ __device__ constexpr int partial_floats() { return D + 2; }
 
-// One block of 256 threads per (split, bh): keys [split*KPS, min(t, +KPS)).
+// Decode workspace: the partials of up to ceil(T_cap / 512) splits per head,
+// then (256-byte aligned) one 32-bit arrival counter per head.
+inline size_t decode_counter_offset(int BH, int T_cap, int D) {
+  const size_t nsplit = ((size_t)T_cap + kKeysPerSplit - 1) / kKeysPerSplit;
+  return align256((size_t)BH * (nsplit > 0 ? nsplit : 1) * (D + 2) * sizeof(float));
+}
+inline unsigned *decode_counters(float *part, int BH, int T_cap, int D) {
+  return reinterpret_cast<unsigned *>(reinterpret_cast<char *>(part) +
+                                      decode_counter_offset(BH, T_cap, D));
+}
+
+// The merge, run by the last split block of a head to finish (256 threads):
+// the split partials and the new key k_t (logit scale * q_t . k_t, no gate
+// term) give o_t and lse_t; k_t, v_t and Lambda_t are appended to the caches.  The merge is an online softmax over
+// batches of up to 64 splits: each batch's partials are copied into LDS in
+// one coalesced pass, its max and weights come from one wave's shuffles, and
+// the running (M, l, o) is rescaled once per batch.  It starts from the new
+// key itself: M = x_new, l = 1, o = v_t.
+constexpr int kMergeBatch = 64;   // splits per merge batch
+
+// Device-coherent store / load of a split partial (agent scope, relaxed).
+__device__ __forceinline__ void st_coherent(float *p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+struct MergeLds {
+  float sp[kMergeBatch * partial_floats<D>()];   // partials of the batch
+  float wsp[kMergeBatch];                        // weight of each split of the batch
+  float bc[4];                                   // broadcast: x_new, batch max, batch l
+};
+
+template <typename E, typename KC, int D, bool FOX>
+__device__ __forceinline__ void merge_head(
+    MergeLds<D> &sm, int bh, const E *__restrict__ q, const E *__restrict__ k,
+    const E *__restrict__ v, const float *__restrict__ logf, KC *__restrict__ kcache,
+    E *__restrict__ vcache, double *__restrict__ gcache, const float *part, E *__restrict__ out,
+    float *__restrict__ lse, int t, int T_cap, int nsplit, float sl2) {
+  constexpr int PF = partial_floats<D>();
+  constexpr int NT = 256, SB = kMergeBatch;
+  float *sp = sm.sp, *wsp = sm.wsp, *bc = sm.bc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float *ph = part + (size_t)bh * nsplit * PF;
+  // every global read the merge needs is issued up front (first batch of
+  // partials into registers, q, k, v), so the kernel waits on memory once
+  constexpr int PER = (SB * PF + NT - 1) / NT;
+  float pre[PER];
+  const int ns0 = min(SB, nsplit);
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = tid + r * NT;
+    pre[r] = i < ns0 * PF ? ld_coherent(ph + i) : 0.f;
+  }
+  const float vt = tid < D ? to_f(v[(size_t)bh * D + tid]) : 0.f;
+  const float kt = tid < D ? to_f(k[(size_t)bh * D + tid]) : 0.f;
+  float qk = 0.f;
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i)
+      qk = __builtin_fmaf(to_f(q[(size_t)bh * D + lane + 64 * i]),
+                          to_f(k[(size_t)bh * D + lane + 64 * i]), qk);
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = tid + r * NT;
+    if (i < ns0 * PF) sp[i] = pre[r];
+  }
+  // logit of the new key: wave 0, D / 64 elements per lane
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) qk += __shfl_xor(qk, off);
+    if (lane == 0) bc[0] = qk * sl2;
+  }
+  __syncthreads();
+  float M = bc[0], l = 1.f;
+  float o = vt;
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    const int ns = min(SB, nsplit - s0);
+    if (s0 > 0) {
+      __syncthreads();   // the previous batch is consumed
+      for (int i = tid; i < ns * PF; i += NT) sp[i] = ld_coherent(ph + (size_t)s0 * PF + i);
+      __syncthreads();
+    }
+    if (wave == 0) {
+      const float ms = lane < ns ? sp[lane * PF] : -INFINITY;
+      float mc = ms;
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) mc = fmaxf(mc, __shfl_xor(mc, off));
+      const float Mn = fmaxf(M, mc);
+      const float f = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - Mn) : 0.f;
+      wsp[lane] = f;
+      float lb = lane < ns ? f * sp[lane * PF + 1] : 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) lb += __shfl_xor(lb, off);
+      if (lane == 0) {
+        bc[1] = Mn;
+        bc[2] = lb;
+      }
+    }
+    __syncthreads();
+    const float Mn = bc[1];
+    const float alpha = __builtin_amdgcn_exp2f(M - Mn);   // M finite: it includes x_new
+    l = __builtin_fmaf(l, alpha, bc[2]);
+    if (tid < D) {
+      float acc = o * alpha;
+      for (int sidx = 0; sidx < ns; ++sidx) {
+        const float f = wsp[sidx];
+        if (f != 0.f) acc = __builtin_fmaf(f, sp[sidx * PF + 2 + tid], acc);
+      }
+      o = acc;
+    }
+    M = Mn;
+  }
+  if (tid < D) {
+    out[(size_t)bh * D + tid] = from_f<E>(o / l);
+    kcache[((size_t)bh * T_cap + t) * D + tid] = from_f<KC>(kt);
+    vcache[((size_t)bh * T_cap + t) * D + tid] = from_f<E>(vt);
+  }
+  if (tid == 0) {
+    lse[bh] = kLn2D * (M + __builtin_amdgcn_logf(l));
+    if (FOX)
+      gcache[(size_t)bh * T_cap + t] =
+          t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] + (double)logf[bh] : 0.0;
+  }
+}
+
+// Arrival count of a head's split blocks in one decode step (a split-K
+// semaphore): each block adds 1 once it has stored its partial; the block that
+// draws ticket nsplit - 1 is the last, merges, and resets the count to 0, so
+// the counter is 0 between steps (the workspace is zero-filled before the
+// first step).  A single atomic add per block: nothing waits or retries.
+__device__ __forceinline__ bool arrive_last(unsigned *c, int nsplit) {
+  const unsigned ticket = atomicAdd(c, 1u);
+  const bool last = ticket == (unsigned)nsplit - 1u;
+  if (last) atomicExch(c, 0u);
+  return last;
+}
+
+// One block of 256 threads per (split, bh): keys [split*KPS, min(t, +KPS))
+// (an empty range when t == 0: the step then has one block with no keys).
 // A key row is spread over LPK lanes with EPL consecutive elements each
 // (16-byte loads of the key cache); a wave covers KPW = 64 / LPK keys at once.
 template <typename E, typename KC, int D, bool FOX>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const E *__restrict__ q, const E *__restrict__ w, const float *__restrict__ beta,
-    const float *__restrict__ logf, KC *__restrict__ kcache, const E *__restrict__ vcache,
-    const double *__restrict__ gcache, float *__restrict__ part, int t, int T_cap, int nsplit,
-    float sl2) {
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const E *__restrict__ w, const float *__restrict__ beta, const float *__restrict__ logf,
+    KC *__restrict__ kcache, E *__restrict__ vcache, double *__restrict__ gcache, float *part,
+    unsigned *__restrict__ cnt, E *__restrict__ out, float *__restrict__ lse, int t,
+    int T_cap, int nsplit, float sl2) {
   constexpr int EPL = Vec16<KC>::n;
   constexpr int LPK = D / EPL;
   constexpr int KPW = 64 / LPK;
@@ -368,6 +511,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int PF = partial_floats<D>();
   __shared__ float red_m[NW * KPW], red_l[NW * KPW];
   __shared__ float red_o[NW * KPW][D];
+  __shared__ MergeLds<D> msm;
+  __shared__ int last;
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -473,95 +618,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         o = __builtin_fmaf(f, red_o[s][threadIdx.x], o);
       }
     }
-    dst[2 + threadIdx.x] = o;
+    st_coherent(dst + 2 + threadIdx.x, o);
     if (threadIdx.x == 0) {
-      dst[0] = M;
-      dst[1] = l;
+      st_coherent(dst, M);
+      st_coherent(dst + 1, l);
     }
   }
-}
-
-// One block of 256 threads per bh: merge the split partials with the new key
-// k_t (logit scale * q_t . k_t, no gate term), write o_t and lse_t, append
-// k_t, v_t and Lambda_t to the caches.  The split weights are computed once in
-// LDS; each output element is reduced over the splits by 256/D threads.
-template <typename E, typename KC, int D, bool FOX>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
-    const float *__restrict__ logf, KC *__restrict__ kcache, E *__restrict__ vcache,
-    double *__restrict__ gcache, const float *__restrict__ part, E *__restrict__ out,
-    float *__restrict__ lse, int t, int T_cap, int nsplit, float sl2) {
-  constexpr int PF = partial_floats<D>();
-  constexpr int NT = 256, SPL = NT / D;   // threads per output element
-  constexpr int MAXS = 1024;              // splits held in LDS per pass
-  __shared__ float red[NT];
-  __shared__ float wsp[MAXS];             // weight of each split, then reused
-  __shared__ float sm[2];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const float *ph = part + (size_t)bh * nsplit * PF;
-  // logit of the new key
-  float qk = 0.f;
-  if (tid < D) qk = to_f(q[(size_t)bh * D + tid]) * to_f(k[(size_t)bh * D + tid]);
-  red[tid] = qk;
+  // the last block of this head to finish merges every split.  The partials
+  // are the only data passed between blocks: they are written and read with
+  // device-coherent (agent-scope) accesses, which go past the per-XCD L2, and
+  // every store of the block has completed (vmcnt 0 in each wave, then the
+  // barrier) before the block is counted; no whole-cache fence is needed.
+  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's stores are done
   __syncthreads();
-  for (int off = NT / 2; off >= 1; off /= 2) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float x_new = red[0] * sl2;
+  if (threadIdx.x == 0) last = arrive_last(cnt + bh, nsplit);
   __syncthreads();
-  // global max over the splits and the new key
-  float mx = x_new;
-  for (int s = tid; s < nsplit; s += NT) mx = fmaxf(mx, ph[(size_t)s * PF]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int off = NT / 2; off >= 1; off /= 2) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  // split weights and the sum l
-  float lp = 0.f;
-  for (int s = tid; s < nsplit; s += NT) {
-    const float ms = ph[(size_t)s * PF];
-    const float f = ms > -INFINITY ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
-    if (s < MAXS) wsp[s] = f;
-    lp = __builtin_fmaf(f, ph[(size_t)s * PF + 1], lp);
-  }
-  red[tid] = lp;
-  __syncthreads();
-  for (int off = NT / 2; off >= 1; off /= 2) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float f_new = __builtin_amdgcn_exp2f(x_new - M);
-  const float l = red[0] + f_new;
-  if (tid == 0) sm[0] = l;
-  __syncthreads();
-  // o[e] = f_new v_t[e] + sum_s w_s o_s[e]: thread (e, part) sums splits part, part + SPL, ...
-  const int e = tid % D, pr = tid / D;
-  float o = 0.f;
-  for (int s = pr; s < nsplit; s += SPL) {
-    const float f = s < MAXS ? wsp[s] : __builtin_amdgcn_exp2f(ph[(size_t)s * PF] - M);
-    if (f != 0.f) o = __builtin_fmaf(f, ph[(size_t)s * PF + 2 + e], o);
-  }
-  red[tid] = o;
-  __syncthreads();
-  if (tid < D) {
-    float acc = f_new * to_f(v[(size_t)bh * D + tid]);
-#pragma unroll
-    for (int p2 = 0; p2 < SPL; ++p2) acc += red[p2 * D + tid];
-    out[(size_t)bh * D + tid] = from_f<E>(acc / sm[0]);
-    kcache[((size_t)bh * T_cap + t) * D + tid] = from_f<KC>(to_f(k[(size_t)bh * D + tid]));
-    vcache[((size_t)bh * T_cap + t) * D + tid] = v[(size_t)bh * D + tid];
-  }
-  if (tid == 0) {
-    lse[bh] = kLn2D * (M + __builtin_amdgcn_logf(l));
-    if (FOX)
-      gcache[(size_t)bh * T_cap + t] =
-          t >= 1 ? gcache[(size_t)bh * T_cap + t - 1] + (double)logf[bh] : 0.0;
-  }
+  if (!last) return;
+  merge_head<E, KC, D, FOX>(msm, bh, q, k, v, logf, kcache, vcache, gcache, part, out, lse, t,
+                            T_cap, nsplit, sl2);
 }
 
 template <typename E, typename KC, int D>
@@ -588,14 +662,12 @@ hipError_t decode_t(const void *q, const void *k, const void *v, const void *w,
                     const float *beta, const float *logf, void *kcache, void *vcache,
                     double *gcache, void *out, float *lse, float *part, int BH, int t,
                     int T_cap, float sl2, hipStream_t stream) {
-  const int nsplit = (t + kKeysPerSplit - 1) / kKeysPerSplit;
-  if (nsplit > 0)
-    hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0,
-                       stream, (const E *)q, (const E *)w, beta, logf, (KC *)kcache,
-                       (const E *)vcache, gcache, part, t, T_cap, nsplit, sl2);
-  hipLaunchKernelGGL((decode_combine_kernel<E, KC, D, FOX>), dim3(BH), dim3(256), 0, stream,
-                     (const E *)q, (const E *)k, (const E *)v, logf, (KC *)kcache, (E *)vcache,
-                     gcache, part, (E *)out, lse, t, T_cap, nsplit, sl2);
+  const int nsplit = t > 0 ? (t + kKeysPerSplit - 1) / kKeysPerSplit : 1;
+  unsigned *cnt = decode_counters(part, BH, T_cap, D);
+  hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0, stream,
+                     (const E *)q, (const E *)k, (const E *)v, (const E *)w, beta, logf,
+                     (KC *)kcache, (E *)vcache, gcache, part, cnt, (E *)out, lse, t, T_cap, nsplit,
+                     sl2);
   return hipGetLastError();
 }
 
@@ -632,8 +704,7 @@ hipError_t decode_d(int D, const void *q, const void *k, const void *v, const vo
 }  // namespace
 
 size_t decode_partial_bytes(int BH, int T_cap, int D) {
-  const size_t nsplit = ((size_t)T_cap + kKeysPerSplit - 1) / kKeysPerSplit;
-  return (size_t)BH * (nsplit > 0 ? nsplit : 1) * (D + 2) * sizeof(float);
+  return decode_counter_offset(BH, T_cap, D) + (size_t)BH * sizeof(unsigned);
 }
 
 hipError_t launch_prefill_cache(int dtype, int kc_dtype, int D, const void *k, const void *v,

@@ -192,3 +192,20 @@ def test_decode_full_context_sampled():
         ek = max(ek, float(np.max(np.abs(kc_np[b, h, rows] - ref))))
     _log(f"  max|do|={eo:.3g} max|dlse|={el:.3g} max|dk| (sampled)={ek:.3g}")
     assert eo <= tol_o and el <= tol_l and ek <= 1e-3
+
+
+def test_decode_counters_back_to_zero():
+    """The decode workspace carries one arrival counter per head after the
+    split partials (256-byte aligned); every step must leave them at zero,
+    so later steps (and other caches using the same workspace) start clean."""
+    import torch
+    dtype, d, B, H, L, n_dec, T_cap = "bf16", 64, 2, 3, 64, 5, 1100
+    inp = workloads.small(dtype, B, H, L + n_dec, d, seed=5)
+    outs, lses, cache = _run(inp, dtype, "f32", L, n_dec, T_cap)
+    assert np.all(np.isfinite(outs)) and np.all(np.isfinite(lses))
+    nsplit_cap = (T_cap + 511) // 512
+    part_bytes = B * H * nsplit_cap * (d + 2) * 4
+    off = (part_bytes + 255) // 256 * 256
+    counters = cache.workspace[off:off + 4 * B * H]
+    assert counters.numel() == 4 * B * H
+    assert int(torch.count_nonzero(counters)) == 0
