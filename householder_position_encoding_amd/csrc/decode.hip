@@ -51,7 +51,7 @@ __device__ __forceinline__ E from_f(float x) { return (E)x; }   // RNE for bf16
 
 // One block of 256 threads per (bh, chunk): ->K_c and M_c in float32, natural
 // layouts kb[bh][L][D] and m[bh][N][D][D] (M[a][b]).
-// U = (I + strictLower(D W W^T))^{-1} D by forward substitution,
+// U = (I + strictLower(D W W^T))^{-1} D (blocked unit-lower inverse),
 // T2 = U strictLower(W K^T), ->K = K - T2^T W, M = W^T (U W).
 // Every product is a dense 64-wide product of LDS operands (U, the strict
 // lower W K^T and T2 hold zeros outside their triangles), each thread
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
   __shared__ float Us[C * CP];
   __shared__ float Xs[C * CP];
   __shared__ float bs[C];
+  __shared__ float tmp[768];
   float *Ks = UWs;
   float *T2s = Us;
   const int N = L / C;
@@ -91,16 +92,9 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
       Us[i * CP + j] = j < i ? acc[r][q] * bs[i] : 0.f;
     }
   __syncthreads();
-  // X = (I + N)^{-1} below the diagonal, one column per lane of wave 0:
-  // X[i][j] = -N[i][j] - sum_{j<t<i} N[i][t] X[t][j]
-  if (tid < C) {
-    const int j = tid;
-    for (int i = j + 1; i < C; ++i) {
-      float x = -Us[i * CP + j];
-      for (int t = j + 1; t < i; ++t) x = __builtin_fmaf(-Us[i * CP + t], Xs[t * CP + j], x);
-      Xs[i * CP + j] = x;
-    }
-  }
+  // X = (I + N)^{-1}: blocked unit-lower inverse (16 x 16 diagonal blocks by
+  // substitution, the off-diagonal blocks level by level with the whole block)
+  unit_lower_inverse(Us, Xs, tmp, tid);
   __syncthreads();
   // U = X D (unit diagonal of X times beta), zero above the diagonal
   for (int idx = tid; idx < C * C; idx += NT) {
