@@ -10,10 +10,12 @@
 // historical keys in place").  With the forward's lse, P = exp(s - lse) and
 // g = scale * P o (dO V^T - rowdot(dO, O) + dlse).  Three kernels:
 //
-//   levels  one block per key chunk c' walks c upward, Khat[c+1] =
-//           Khat[c] - Khat[c] M_c^T, and stores every level in the input dtype
-//           (float32 running value, the product taken on the rounded value,
-//           as the forward scan does for its running query tile).
+//   levels  one block per key chunk c' (bf16 with d = 64: per four key
+//           chunks, which share each -M_c through LDS) walks c upward,
+//           Khat[c+1] = Khat[c] - Khat[c] M_c^T, and stores every level in the
+//           input dtype (float32 running value, the product taken on the
+//           rounded value, as the forward scan does for its running query
+//           tile).
 //   dq      one block per query chunk c: dQa_c = sum_{c'<c} g Khat[c]_{c'},
 //           and the row sums of dS for the forget-gate gradient.
 //   dk      one block per group of G key chunks walks c downward keeping,
@@ -119,6 +121,26 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *gbl_ptr_t;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt at maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Block barrier that completes the wave's LDS accesses but leaves its global
+// loads (the next step's operand copies) in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ levels
 
 __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
@@ -209,6 +231,112 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
     if (c + 1 >= N) break;
     level(c + 1, mb, ma);
   }
+}
+
+// The same walk for bf16 inputs and d = 64, four key chunks c' = 4 grp + j
+// per block (8 waves, a wave per 32 keys), walking the levels together so
+// that each -M_c is fetched once per block instead of once per wave.  Each
+// wave loads one eighth of -M_c (one 16-byte piece per lane) into registers
+// two levels ahead and writes it into an LDS double buffer one level ahead,
+// where it is the B operand of every wave's product; one barrier per level
+// publishes it and frees the other buffer.  Row r of -M_c keeps its 16-byte
+// piece p at position p ^ (r & 7), so a fragment read (32 rows, one piece
+// each) touches every bank once.  The per-level sequence of global loads and
+// stores is the same in every iteration of the walk (the fetch index is
+// clamped at the last chunk), so the compiler's wait for a fetched piece
+// covers only operations issued two levels back: the walk's warm-up levels,
+// in which the later chunks of the group have not started, are peeled off
+// and end with every memory operation complete.
+__global__ __launch_bounds__(512) void levels64_kernel(const float *__restrict__ kb,
+                                                       const __bf16 *__restrict__ nm,
+                                                       __bf16 *__restrict__ levels, int T, int BH) {
+  using E = __bf16;
+  constexpr int D = 64, G = 4, P = D + 8, WARM = G - 1;
+  __shared__ __attribute__((aligned(16))) E ring[2][D * D];
+  __shared__ __attribute__((aligned(16))) E Xs[2 * G * 32 * P];
+  const int N = T / C;
+  const int grp = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, col = lane & 31;
+  // the wave index as a scalar: member-dependent branches stay wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wv & 1, cp = G * grp + (wv >> 1);
+  const bool member = cp < N - 1;   // key chunk N-1 has no level beyond its own
+  const int c_lo = G * grp + 1;
+  E *Xw = Xs + wv * 32 * P;
+  f32x16 x[D / 32];
+  const float *src = kb + ((size_t)bh * T + (size_t)(member ? cp : 0) * C + 32 * kh) * D;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
+  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
+  const E *nmh = nm + (size_t)bh * N * D * D;
+  // this wave's piece of -M_c: row pr, 16-byte piece pp
+  const int pr = 8 * wv + (lane >> 3), pp = lane & 7;
+  auto fetch = [&](int c) {
+    c = c < N - 1 ? c : N - 1;
+    return *reinterpret_cast<const uint4 *>(nmh + (size_t)c * D * D + pr * D + 8 * pp);
+  };
+  auto put = [&](int b, const uint4 &u) {
+    *reinterpret_cast<uint4 *>(&ring[b][pr * D + 8 * (pp ^ (pr & 7))]) = u;
+  };
+  // level c: store it; step to level c + 1 with -M_c from ring[b]; publish
+  // -M_{c+1} (in nx) into ring[b ^ 1] and fetch -M_{c+3} into nx
+  auto level = [&](int c, bool active, uint4 &nx) {
+    const int b = (c - c_lo) & 1;
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
+      wave_sync();
+      E *dst = levels + lev_head + lev_off(c, cp, D) + (size_t)32 * kh * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int vi = j * 64 + lane, row = vi / 8, c16 = 8 * (vi % 8);
+        *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
+            *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+      }
+      if (c + 1 < N) {   // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
+        const E *pa = Xw + col * P + 8 * g;
+        const unsigned char *mb = reinterpret_cast<const unsigned char *>(ring[b]);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks)
+            x[t] = MM<E>::mma(
+                *reinterpret_cast<const bf16x8 *>(pa + 16 * ks),
+                *reinterpret_cast<const bf16x8 *>(mb + (32 * t + col) * 2 * D +
+                                                  (((2 * ks + g) ^ (col & 7)) << 4)),
+                x[t]);
+      }
+    }
+    put(b ^ 1, nx);
+    nx = fetch(c + 3);
+  };
+  uint4 na, nb;
+  put(0, fetch(c_lo));
+  na = fetch(c_lo + 1);
+  nb = fetch(c_lo + 2);
+  // warm-up: chunk c' = c_lo - 1 + j starts at level c_lo + j
+  for (int j = 0; j < WARM && c_lo + j < N; ++j) {
+    const int c = c_lo + j;
+    const bool active = member && c > cp;
+    if (j & 1) level(c, active, nb);
+    else level(c, active, na);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  // steady state: level c_lo + WARM on takes the register set (c - c_lo) & 1
+  static_assert(WARM % 2 == 1, "the walk resumes with the second register set");
+  auto walk = [&](auto stores) {
+    int c = c_lo + WARM;
+    for (; c + 1 < N; c += 2) {   // no exit between the halves: one wait per piece
+      level(c, decltype(stores)::value, nb);
+      level(c + 1, decltype(stores)::value, na);
+    }
+    if (c < N) level(c, decltype(stores)::value, nb);
+  };
+  if (member) walk(std::true_type{});
+  else walk(std::false_type{});
 }
 
 // ------------------------------------------------------------------ dq
@@ -725,26 +853,6 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
 
 // ------------------------------------------------------------------ dk, bf16, d = 64
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef __attribute__((address_space(1))) void *gbl_ptr_t;
-
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt at maxima).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Block barrier that completes the wave's LDS accesses but leaves its global
-// loads (the next step's operand copies) in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Same walk as dk_kernel for bf16 inputs and d = 64, G = 4 key chunks per
 // block (8 waves).  The query-side operands of step c (Qa and dO as rows and
 // in fragment order, -M_{c-1}^T in fragment order, per-query statistics: 43
@@ -996,9 +1104,14 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   constexpr int G = group_of<E, D>();
   E *lev = static_cast<E *>(a.levels), *levt = static_cast<E *>(a.levt);
   const E *qae = (const E *)a.qae, *dout = (const E *)a.dout, *v = (const E *)a.v;
-  if (N > 1)
+  if constexpr (std::is_same<E, __bf16>::value && D == 64) {
+    if (N > 1)
+      hipLaunchKernelGGL(levels64_kernel, dim3(BH * ((N - 1 + 3) / 4)), dim3(512), 0, s, a.kb,
+                         (const E *)a.nm, lev, T, BH);
+  } else if (N > 1) {
     hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
                        (const E *)a.nm, lev, levt, T, BH);
+  }
   if constexpr (std::is_same<E, __bf16>::value && D == 64)
     hipLaunchKernelGGL((dq64_kernel<FOX>), dim3(BH * N), dim3(128), 0, s, qae, dout, a.lse, a.dlse,
                        a.dvec, a.lam, lev, v, a.scale, a.dqa, a.dlam, T, BH);
