@@ -550,10 +550,17 @@ __global__ __launch_bounds__(128) void dq64_kernel(
   const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
   E *Gw = Gs + kh * C * PG, *Kt = KtS + kh * D * PG;
   __syncthreads();
+  // one key chunk's operands: level rows and V rows (B operands) and, with the
+  // gate, Lambda of the wave's keys
   struct Frags {
     bf16x8 k[KS], v[KS];
+    float kl[FOX ? 16 : 1];
   };
+  // The fetch index is clamped at chunk 0 and every step fetches, so the
+  // sequence of loads is the same in every step and the compiler's wait for
+  // a step's operands leaves the next step's loads in flight.
   auto fetch = [&](int cp, Frags &f) {
+    cp = cp > 0 ? cp : 0;
     const E *pk = levels + lev_c + (size_t)cp * C * D + (size_t)(32 * kh + col) * D + 8 * g;
     const E *pv = v + ((size_t)bh * T + (size_t)cp * C + 32 * kh + col) * D + 8 * g;
 #pragma unroll
@@ -561,13 +568,18 @@ __global__ __launch_bounds__(128) void dq64_kernel(
       f.k[ks] = *reinterpret_cast<const bf16x8 *>(pk + 16 * ks);
       f.v[ks] = *reinterpret_cast<const bf16x8 *>(pv + 16 * ks);
     }
+    if constexpr (FOX) {
+      const float *pl = lam + (size_t)bh * T + (size_t)cp * C + 32 * kh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f.kl[r] = pl[acc_row(r, g)];
+    }
   };
   auto step = [&](int cp, Frags &fc, Frags &fn) {
-    const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
-    if (cp >= 1) fetch(cp - 1, fn);
+    fetch(cp - 1, fn);
+    __builtin_amdgcn_sched_barrier(0);   // issue the loads before this step's products
     float kl[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) kl[r] = FOX ? lam[krow + acc_row(r, g)] : 0.f;
+    for (int r = 0; r < 16; ++r) kl[r] = FOX ? fc.kl[r] : 0.f;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       // S^T and dP^T: rows = this wave's 32 keys, columns = queries 32 qt..
@@ -611,11 +623,12 @@ __global__ __launch_bounds__(128) void dq64_kernel(
   };
   Frags fa, fb;
   fetch(c - 1, fa);
-  for (int cp = c - 1; cp >= 0; cp -= 2) {
+  int cp = c - 1;
+  for (; cp >= 1; cp -= 2) {   // no exit between the halves
     step(cp, fa, fb);
-    if (cp - 1 < 0) break;
     step(cp - 1, fb, fa);
   }
+  if (cp == 0) step(0, fa, fb);
   // combine the two key halves (wave 1's partial through LDS, over Gs and KtS)
   __syncthreads();
   float *red = reinterpret_cast<float *>(pool);   // [64 q][D + 1] floats
@@ -1066,21 +1079,42 @@ __global__ __launch_bounds__(512) void dk64_kernel(
 }
 
 // dM_m = sum over the groups that cross m (m in [1, N-2]); 0 otherwise.
-// One block per (bh, m) and slice of DD / XB elements (XB blocks per matrix).
+// One block per (bh, m) and slice of 1024 elements (DD / 1024 blocks per
+// matrix), four consecutive elements per thread; the partials are summed in
+// group order, eight loads in flight.
 template <int G>
-__global__ __launch_bounds__(256) void dm_reduce_kernel(const float *__restrict__ dmpart,
-                                                        float *__restrict__ dm, int N, int DD,
+__global__ __launch_bounds__(256) void dm_reduce_kernel(const float4 *__restrict__ dmpart,
+                                                        float4 *__restrict__ dm, int N, int DD,
                                                         int XB) {
-  const int NG = (N + G - 1) / G;
+  constexpr int U = 8;
+  const int NG = (N + G - 1) / G, DD4 = DD / 4;
   const size_t bm = blockIdx.x / XB;   // bh * N + m
-  const int xb = blockIdx.x % XB;
+  const int e = (blockIdx.x % XB) * 256 + threadIdx.x;
   const int mch = (int)(bm % N);
   const int ng = (mch >= 1 && mch <= N - 2) ? (mch + G - 1) / G : 0;
-  for (int e = xb * 256 + threadIdx.x; e < DD; e += XB * 256) {
-    float s = 0.f;
-    for (int gi = 0; gi < ng; ++gi) s += dmpart[(bm * NG + gi) * DD + e];
-    dm[bm * DD + e] = s;
+  const float4 *src = dmpart + bm * NG * DD4 + e;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int gi = 0;
+  for (; gi + U <= ng; gi += U) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[(size_t)(gi + u) * DD4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
   }
+  for (; gi < ng; ++gi) {
+    const float4 v = src[(size_t)gi * DD4];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  dm[bm * DD4 + e] = acc;
 }
 
 template <typename E, int D>
@@ -1129,9 +1163,10 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
                        (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam, lev,
                        levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
   }
-  constexpr int XB = D * D / 256;
-  hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * N * XB), dim3(256), 0, s, a.dmpart, a.dm, N,
-                     D * D, XB);
+  constexpr int XB = D * D / 1024;
+  static_assert(D * D % 1024 == 0, "whole 1024-element slices");
+  hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * N * XB), dim3(256), 0, s,
+                     (const float4 *)a.dmpart, (float4 *)a.dm, N, D * D, XB);
   return hipGetLastError();
 }
 
