@@ -141,6 +141,27 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds wave-uniform).  Written as assembly so that the compiler, which does
+// not see it, adds no wait for it before the wave's later LDS reads (it cannot
+// tell them apart from the copy's destination): the caller waits for the copy
+// itself (vmcnt) and publishes it with a barrier before any wave reads it.
+// The compiler's own waits stay correct, only more conservative: it counts
+// fewer outstanding operations than there are.  M0 (the LDS address) is a
+// register the compiler reserves; the kernels that use this make no other
+// use of M0 (no LDS copy intrinsics, messages or indexed register moves), as
+// their generated code shows, so nothing of the compiler's lives in it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(uintptr_t)(lds_ptr_t)(p);
+}
+
 // ------------------------------------------------------------------ levels
 
 __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
@@ -897,7 +918,8 @@ __global__ __launch_bounds__(512) void dk64_kernel(
   __shared__ __attribute__((aligned(16))) E kx[D * PGT];   // Khat[m]^T [d][KG] at crossings
   const int N = T / C, NG = (N + G - 1) / G;
   const int grp = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, col = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: uniform branches
   const int kh = wv & 1, cp = G * grp + (wv >> 1);
   const size_t head = (size_t)bh * T;
   const size_t krow = head + (size_t)cp * C + 32 * kh;
@@ -917,8 +939,7 @@ __global__ __launch_bounds__(512) void dk64_kernel(
                                  : j < 2 * QB / 1024 ? o + (j - QB / 1024) * 1024
                                  : j < (2 * QB + MB) / 1024 ? mm + (j - 2 * QB / 1024) * 1024
                                                             : st;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + lane * 16),
-                                       (lds_ptr_t)(sbuf + b * BUF + j * 1024), 16, 0, 0);
+      copy16_to_lds(src + lane * 16, lds_addr(sbuf + b * BUF + j * 1024));
     }
   };
   auto load_rows = [&](bf16x8 (&f)[D / 16], const E *rows) {   // B operand: this wave's 32 rows
@@ -948,8 +969,10 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     wait_vmcnt<0>();
     lds_barrier();
     if (c - 1 >= c_low) stage(c - 1, b ^ 1);
+    // the next step's level rows; every step loads (a valid block when there
+    // is no next level), so the sequence of loads is the same in every step
     const bool next_active = member && c - 1 > cp && c - 1 >= c_low;
-    if (next_active) load_rows(kn, levels + lev_head + lev_off(c - 1, cp, D) + (size_t)32 * kh * D);
+    load_rows(kn, levels + lev_head + (next_active ? lev_off(c - 1, cp, D) : 0) + (size_t)32 * kh * D);
     const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *QF = Qs + 64 * P;
     const E *Os = reinterpret_cast<const E *>(sbuf + b * BUF + QB), *OF = Os + 64 * P;
     const E *Ms = reinterpret_cast<const E *>(sbuf + b * BUF + 2 * QB);
