@@ -141,26 +141,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (lds wave-uniform).  Written as assembly so that the compiler, which does
-// not see it, adds no wait for it before the wave's later LDS reads (it cannot
-// tell them apart from the copy's destination): the caller waits for the copy
-// itself (vmcnt) and publishes it with a barrier before any wave reads it.
-// The compiler's own waits stay correct, only more conservative: it counts
-// fewer outstanding operations than there are.  M0 (the LDS address) is a
-// register the compiler reserves; the kernels that use this make no other
-// use of M0 (no LDS copy intrinsics, messages or indexed register moves), as
-// their generated code shows, so nothing of the compiler's lives in it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ unsigned lds_addr(const void *p) {
-  return (unsigned)(uintptr_t)(lds_ptr_t)(p);
-}
 
 // ------------------------------------------------------------------ levels
 

@@ -72,6 +72,35 @@ __host__ __device__ constexpr int al_floats() { return kAlTiles * 64 * 16; }
 // mb <= w.
 __host__ __device__ constexpr int al_tile(int w, int mb) { return w + mb; }
 
+// Copies from global memory straight into LDS (lane l's bytes landing at
+// lds + size * l, lds wave-uniform), written as assembly so that the compiler,
+// which does not see them, places no wait for them before the wave's later LDS
+// reads: through the intrinsic it waits for every outstanding copy before the
+// first read it cannot tell apart from a copy's destination, which for a
+// double buffer with a runtime index is every read of the other buffer.  The
+// caller waits for its copies itself (vmcnt) and publishes them with a
+// barrier before any wave reads them.  The compiler's own waits stay correct,
+// only more conservative: it counts fewer outstanding operations than there
+// are.  M0 (the LDS address) is a register the compiler reserves; the kernels
+// that use these make no other use of M0 (no LDS copy intrinsics, messages or
+// indexed register moves), as their generated code shows.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void *gsrc, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void *gsrc, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// The LDS address of a pointer into shared memory, as a wave-uniform scalar.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  typedef __attribute__((address_space(3))) const void *lds_cptr;
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_cptr)(p));
+}
+
 struct Layout {
   size_t qa, kvm, al, gate, bnd, total;
 };

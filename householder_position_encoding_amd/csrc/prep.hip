@@ -216,20 +216,21 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   constexpr int TPW = D / 64;                       // d x 64 tiles per wave
   constexpr int PLANE = C * P * 2;                  // one 64 x 72 bf16 plane (bytes)
   constexpr int SLOT = 2 * PLANE;                   // 18432 B: hi/lo planes or 64 x 72 fp32
-  constexpr int EXTRA = D == 128 ? SLOT : 0;        // second half of (U W)^T at d = 128
   constexpr int WT_BYTES = D * P * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * SLOT + EXTRA + WT_BYTES + C * 4];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[3 * SLOT + WT_BYTES + C * 4];
   // slot 0: N / X (fp32), then U (hi/lo), then T2^T (hi/lo)
   // slot 1: lower(Q W^T) (hi/lo)
-  // slot 2 (+ EXTRA): strictLower(W K^T)^T (hi/lo), then (U W)^T (hi/lo)
+  // slot 2: strictLower(W K^T)^T (hi/lo), then (U W)^T (hi/lo) for 64 of the
+  // d columns at a time (d = 128: two halves, the second kept in registers
+  // meanwhile, so that two blocks fit a CU)
   float *Xs = reinterpret_cast<float *>(smem);
   __bf16 *Uh = reinterpret_cast<__bf16 *>(smem), *Ul = Uh + C * P;
   __bf16 *T2h = Uh, *T2l = Ul;
   __bf16 *P1h = reinterpret_cast<__bf16 *>(smem + SLOT), *P1l = P1h + C * P;
   __bf16 *SKh = reinterpret_cast<__bf16 *>(smem + 2 * SLOT), *SKl = SKh + C * P;
-  __bf16 *UWh = SKh, *UWl = UWh + D * P;
-  __bf16 *Wt = reinterpret_cast<__bf16 *>(smem + 3 * SLOT + EXTRA);
-  float *bs = reinterpret_cast<float *>(smem + 3 * SLOT + EXTRA + WT_BYTES);
+  __bf16 *UWh = SKh, *UWl = UWh + C * P;
+  __bf16 *Wt = reinterpret_cast<__bf16 *>(smem + 3 * SLOT);
+  float *bs = reinterpret_cast<float *>(smem + 3 * SLOT + WT_BYTES);
 
   const int N = T / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
@@ -447,6 +448,9 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   __syncthreads();
 
   // ---- phase 3: T2 = U strictLower(W K^T) and U W, stored transposed ----
+  // uw[u] holds (U W)^T tile (e block nt + 2u, s block mt): u = 0 is the
+  // first 64 d columns, u = 1 (d = 128) the second.
+  f32x16 uw[TPW];
   {
     bf16x8 uh[KSC], ul[KSC];
     load_rows<KSC>(uh, Uh + 32 * mt * P, P, lane);
@@ -460,7 +464,6 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
       mma_rows<KSC>(t2, uh, sl);
       mma_rows<KSC>(t2, ul, sh);
     }
-    f32x16 uw[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       bf16x8 wt[KSC];
@@ -473,57 +476,67 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int s0 = 32 * mt + 8 * r4 + 4 * g;
-      store4_split(T2h, T2l, (32 * nt + n) * P + s0, quad(t2, r4));             // T2^T[j][s]
-#pragma unroll
-      for (int u = 0; u < TPW; ++u)
-        store4_split(UWh, UWl, (32 * (nt + 2 * u) + n) * P + s0, quad(uw[u], r4));  // (UW)^T[e][s]
+      store4_split(T2h, T2l, (32 * nt + n) * P + s0, quad(t2, r4));         // T2^T[j][s]
+      store4_split(UWh, UWl, (32 * nt + n) * P + s0, quad(uw[0], r4));      // (UW)^T[e][s], e < 64
     }
   }
   __syncthreads();
 
-  // ---- phase 4: outputs ----
+  // ---- phase 4: outputs, in TPW passes over 64 d columns of (U W)^T ----
   float *qa_c = qa + ((size_t)bh * N + c) * qa_floats(D);
+  constexpr int MPP = NDB * NDB / 4 / TPW;   // -M tiles per wave and pass
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tau = wv + 4 * u, eb = tau >> 1, ib = tau & 1;
-    // <-Q^T = Q^T - (U W)^T lower(Q W^T)^T
-    f32x16 acc = zero16();
-    tile_mma<C>(acc, UWh + 32 * eb * P, P, P1h + 32 * ib * P, P, lane);
-    tile_mma<C>(acc, UWh + 32 * eb * P, P, P1l + 32 * ib * P, P, lane);
-    tile_mma<C>(acc, UWl + 32 * eb * P, P, P1h + 32 * ib * P, P, lane);
-    float *dst = qa_c + ((ib * NDB + eb) * 64 + lane) * 16;
+  for (int h = 0; h < TPW; ++h) {
+    if (h > 0) {   // the next 64 columns of (U W)^T replace the previous ones
+      __syncthreads();
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = qinit[u][4 * r4 + e] - acc[4 * r4 + e];
-      *reinterpret_cast<f32x4 *>(dst + 4 * r4) = x;
+      for (int r4 = 0; r4 < 4; ++r4)
+        store4_split(UWh, UWl, (32 * nt + n) * P + 32 * mt + 8 * r4 + 4 * g, quad(uw[h], r4));
+      __syncthreads();
     }
-    // ->K^T = K^T - W^T T2 (tile (eb, jb = ib)), into KF fragment blobs
-    f32x16 kacc = zero16();
-    tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2h + 32 * ib * P, P, lane);
-    tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2l + 32 * ib * P, P, lane);
+    // tile tau = wv + 4h: d block eb (in this pass's columns), query / key block ib
+    const int tau = wv + 4 * h, eb = tau >> 1, ib = tau & 1, ebl = eb - 2 * h;
+    {
+      // <-Q^T = Q^T - (U W)^T lower(Q W^T)^T
+      f32x16 acc = zero16();
+      tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
+      tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1l + 32 * ib * P, P, lane);
+      tile_mma<C>(acc, UWl + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
+      float *dst = qa_c + ((ib * NDB + eb) * 64 + lane) * 16;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 x;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 x;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = (__bf16)(kinit[u][8 * h + t] - kacc[8 * h + t]);
-      *reinterpret_cast<bf16x8 *>(kf + ((ib * NSD + 2 * eb + h) * 64 + lane) * 8) = x;
+        for (int e = 0; e < 4; ++e) x[e] = qinit[h][4 * r4 + e] - acc[4 * r4 + e];
+        *reinterpret_cast<f32x4 *>(dst + 4 * r4) = x;
+      }
+      // ->K^T = K^T - W^T T2 (tile (eb, jb = ib)), into KF fragment blobs
+      f32x16 kacc = zero16();
+      tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2h + 32 * ib * P, P, lane);
+      tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2l + 32 * ib * P, P, lane);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 x;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = (__bf16)(kinit[h][8 * hh + t] - kacc[8 * hh + t]);
+        *reinterpret_cast<bf16x8 *>(kf + ((ib * NSD + 2 * eb + hh) * 64 + lane) * 8) = x;
+      }
     }
-  }
-  // -M^T in MF fragment blobs: M = W^T (U W), tiles (ab, bb).
+    // -M^T in MF fragment blobs: M = W^T (U W), tile (ab, bb) = (tau % NDB,
+    // tau / NDB) for tau = wv + 4u, so this pass's columns bb are 2h, 2h + 1.
 #pragma unroll
-  for (int u = 0; u < NDB * NDB / 4; ++u) {
-    const int tau = wv + 4 * u, ab = tau / NDB, bb = tau % NDB;
-    f32x16 acc = zero16();
-    tile_mma<C>(acc, Wt + 32 * ab * P, P, UWh + 32 * bb * P, P, lane);
-    tile_mma<C>(acc, Wt + 32 * ab * P, P, UWl + 32 * bb * P, P, lane);
+    for (int v = 0; v < MPP; ++v) {
+      const int tm = wv + 4 * (h * MPP + v), ab = tm % NDB, bb = tm / NDB, bbl = bb - 2 * h;
+      f32x16 acc = zero16();
+      tile_mma<C>(acc, Wt + 32 * ab * P, P, UWh + 32 * bbl * P, P, lane);
+      tile_mma<C>(acc, Wt + 32 * ab * P, P, UWl + 32 * bbl * P, P, lane);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 x;
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 x;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) x[t] = (__bf16)(-acc[8 * h + t]);
-      *reinterpret_cast<bf16x8 *>(mf + ((bb * NSD + 2 * ab + h) * 64 + lane) * 8) = x;
+        for (int t = 0; t < 8; ++t) x[t] = (__bf16)(-acc[8 * hh + t]);
+        *reinterpret_cast<bf16x8 *>(mf + ((bb * NSD + 2 * ab + hh) * 64 + lane) * 8) = x;
+      }
     }
   }
   // Al^T = K Q^T - T2^T lower(Q W^T)^T, tile (jb = mt, ib = nt); the tile with

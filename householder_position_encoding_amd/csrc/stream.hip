@@ -37,8 +37,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef __attribute__((address_space(1))) void *gbl_ptr_t;
 
 template <typename E>
 struct Mfma;
@@ -178,15 +176,13 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   // (4 bytes per lane) into the matching slot of a small LDS ring.
   auto stage = [&](int c, int buf) {
     if (FOX && wave == 0)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gate_h + (size_t)c * C + lane),
-                                       (lds_ptr_t)(gate_l + buf * C), 4, 0, 0);
+      copy4_to_lds(gate_h + (size_t)c * C + lane, lds_addr(gate_l + buf * C));
     const unsigned char *src = reinterpret_cast<const unsigned char *>(kvm_h + (size_t)c * KVM);
     unsigned char *dst = lds + buf * KVM_BYTES;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int j = wave + i * NW;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + j * 1024 + lane * 16),
-                                       (lds_ptr_t)(dst + j * 1024), 16, 0, 0);
+      copy16_to_lds(src + j * 1024 + lane * 16, lds_addr(dst + j * 1024));
     }
   };
 
@@ -442,15 +438,13 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 
   auto stage = [&](int c, int buf) {
     if (FOX && wave == 0)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gate_h + (size_t)c * C + lane),
-                                       (lds_ptr_t)(gate_l + buf * C), 4, 0, 0);
+      copy4_to_lds(gate_h + (size_t)c * C + lane, lds_addr(gate_l + buf * C));
     const unsigned char *src = reinterpret_cast<const unsigned char *>(kvm_h + (size_t)c * KVM);
     unsigned char *dst = lds + buf * KVM_BYTES;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int jb = wave + i * NW;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + jb * 1024 + lane * 16),
-                                       (lds_ptr_t)(dst + jb * 1024), 16, 0, 0);
+      copy16_to_lds(src + jb * 1024 + lane * 16, lds_addr(dst + jb * 1024));
     }
   };
 
