@@ -49,7 +49,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU clock settles over the first tens of steps (kernel durations drift
+    # by up to 20 % meanwhile); 50 untimed steps reach the steady state.
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="bf16_b2h16t16384d64")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding measurement")
