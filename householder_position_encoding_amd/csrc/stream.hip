@@ -731,9 +731,6 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 #ifndef PATH_ATTN_WIDE_BF16_64
 #define PATH_ATTN_WIDE_BF16_64 1
 #endif
-#ifndef PATH_ATTN_WIDE_NQC
-#define PATH_ATTN_WIDE_NQC 8
-#endif
 #ifndef PATH_ATTN_WIDE_PD
 #define PATH_ATTN_WIDE_PD 1
 #endif
@@ -759,12 +756,23 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int N = a.T / kChunk;
   const float sl2 = a.sl2;
   if constexpr (std::is_same<E, __bf16>::value && D == 64 && PATH_ATTN_WIDE_BF16_64) {
-    constexpr int NQC = PATH_ATTN_WIDE_NQC, PD = PATH_ATTN_WIDE_PD;
-    const int blocks = a.BH * ((N + NQC - 1) / NQC);
-    hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
-                       stream, a.qa, (const __bf16 *)a.kvm, a.al, a.gate, a.bnd, a.skip,
-                       a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2);
-    return hipGetLastError();
+    // A block runs as long as its longest wave, and wave j of query group g
+    // walks NQC g + j + 1 key chunks.  Eight chunks per block share each staged
+    // operand block among twice the queries of four, but at N <= 64 chunks the
+    // shorter waves of each block idle 10 % of the time or more: four chunks
+    // per block (two blocks per CU) are faster there (B16 H16 T2048: 0.258 ->
+    // 0.242 ms), eight above (B2 H16 T16384: 1.462 against 1.475 ms).
+    constexpr int PD = PATH_ATTN_WIDE_PD;
+    auto go = [&](auto nqc) {
+      constexpr int NQC = decltype(nqc)::value;
+      const int blocks = a.BH * ((N + NQC - 1) / NQC);
+      hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
+                         stream, a.qa, (const __bf16 *)a.kvm, a.al, a.gate, a.bnd, a.skip,
+                         a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2);
+      return hipGetLastError();
+    };
+    if (N <= 64) return go(std::integral_constant<int, 4>{});
+    return go(std::integral_constant<int, 8>{});
   }
   constexpr int NQC = Shape<E, D>::NQC, PD = Shape<E, D>::PD;
   const int blocks = a.BH * ((N + NQC - 1) / NQC);

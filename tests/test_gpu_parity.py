@@ -124,6 +124,23 @@ def test_parity_workload(wl):
     _assert_close(wl.name, wl.dtype, got_o, got_l, o_ref, l_ref)
 
 
+@pytest.mark.parametrize("T,fox", [(4096, False), (4096, True), (4160, False), (4200, True)])
+def test_wide_scan_both_block_shapes(T, fox):
+    """bf16 d = 64 runs four query chunks per block up to 64 chunks and eight
+    beyond: both shapes, with and without the gate, just either side of the
+    switch (4200 is ragged, 66 chunks after padding); sampled rows of both
+    heads against the oracle."""
+    inp = workloads.small("bf16", 1, 2, T, 64, seed=61 + T, fox=fox)
+    out, lse = run_hip(to_device(inp, "bf16"))
+    rng = np.random.default_rng(T)
+    heads = [(0, 0), (0, 1)]
+    rows = [sample_rows(T, rng, n_random=48) for _ in heads]
+    o_ref, l_ref = oracle_rows(inp, heads, rows)
+    got_o = np.concatenate([out[b, h, r] for (b, h), r in zip(heads, rows)])
+    got_l = np.concatenate([lse[b, h, r] for (b, h), r in zip(heads, rows)])
+    _assert_close(f"wide T={T} fox={fox}", "bf16", got_o, got_l, o_ref, l_ref)
+
+
 # ------------------------------------------------------------ diagnostics
 
 def test_swap_closed_form_on_gpu():
