@@ -178,3 +178,21 @@ def test_backward_full_size_sampled_heads(wl, heads):
         ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
         _log(f"{wl.name}: oracle head ({b},{h}) in {time.time() - t0:.1f} s")
         _compare(wl.name, wl.dtype, got, ref, b, h)
+
+
+def test_backward_fox_d64_medium():
+    """bf16, d = 64, with the gate, at T = 2048 (32 chunks): the level walk,
+    dq64 and dk64 run their steady loops (warm-up levels, unrolled step pairs,
+    gate values fetched with the level rows), which the small cases are too
+    short to reach; one head against the blockwise float64 oracle."""
+    B, H, T, d = 1, 2, 2048, 64
+    inp = workloads.small("bf16", B, H, T, d, seed=2048 + 64, fox=True)
+    cot = workloads.cotangents("bf16", B, H, T, d, seed=3072)
+    got = _run_gpu(inp, cot, "bf16")
+    q, k, v, w, beta, logf, do, dl = _head(inp, cot, 0, 1)
+    import oracle
+    o, lse = oracle.path_attn(q, k, v, w, beta, logf)
+    t0 = time.time()
+    ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
+    _log(f"fox d64 T={T}: oracle head (0,1) in {time.time() - t0:.1f} s")
+    _compare("fox d64 medium", "bf16", got, ref, 0, 1)
