@@ -10,8 +10,8 @@
 // historical keys in place").  With the forward's lse, P = exp(s - lse) and
 // g = scale * P o (dO V^T - rowdot(dO, O) + dlse).  Three kernels:
 //
-//   levels  one block per key chunk c' (bf16 with d = 64: per four key
-//           chunks, which share each -M_c through LDS) walks c upward,
+//   levels  one block per key chunk c' (bf16: per four key chunks, which
+//           share each -M_c through LDS) walks c upward,
 //           Khat[c+1] = Khat[c] - Khat[c] M_c^T, and stores every level in the
 //           input dtype (float32 running value, the product taken on the
 //           rounded value, as the forward scan does for its running query
@@ -234,12 +234,12 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
   }
 }
 
-// The same walk for bf16 inputs and d = 64, four key chunks c' = 4 grp + j
-// per block (8 waves, a wave per 32 keys), walking the levels together so
-// that each -M_c is fetched once per block instead of once per wave.  Each
-// wave loads one eighth of -M_c (one 16-byte piece per lane) into registers
-// two levels ahead and writes it into an LDS double buffer one level ahead,
-// where it is the B operand of every wave's product; one barrier per level
+// The same walk for bf16 inputs, four key chunks c' = 4 grp + j per block
+// (8 waves, a wave per 32 keys), walking the levels together so that each
+// -M_c is fetched once per block instead of once per wave.  Each wave loads
+// one eighth of -M_c (D / 64 16-byte pieces per lane) into registers two
+// levels ahead and writes it into an LDS double buffer one level ahead, where
+// it is the B operand of every wave's product; one barrier per level
 // publishes it and frees the other buffer.  Row r of -M_c keeps its 16-byte
 // piece p at position p ^ (r & 7), so a fragment read (32 rows, one piece
 // each) touches every bank once.  The per-level sequence of global loads and
@@ -247,12 +247,23 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
 // clamped at the last chunk), so the compiler's wait for a fetched piece
 // covers only operations issued two levels back: the walk's warm-up levels,
 // in which the later chunks of the group have not started, are peeled off
-// and end with every memory operation complete.
-__global__ __launch_bounds__(512) void levels64_kernel(const float *__restrict__ kb,
-                                                       const __bf16 *__restrict__ nm,
-                                                       __bf16 *__restrict__ levels, int T, int BH) {
+// and end with every memory operation complete.  d = 128 also stores each
+// level transposed ([D][64 keys], for its dq and dk kernels), straight from
+// the register tiles.
+template <int D>
+__global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restrict__ kb,
+                                                            const __bf16 *__restrict__ nm,
+                                                            __bf16 *__restrict__ levels,
+                                                            __bf16 *__restrict__ levt, int T,
+                                                            int BH) {
   using E = __bf16;
-  constexpr int D = 64, G = 4, P = D + 8, WARM = G - 1;
+  constexpr int G = 4, P = D + 8, WARM = G - 1;
+  constexpr bool WT = D != 64;            // transposed copy
+  constexpr int NP = D * D / 8 / 512;     // 16-byte pieces of -M_c per lane
+  constexpr int RV = 32 * D / 8 / 64;     // 16-byte row-store vectors per lane
+  // d = 128 keeps 256 registers and spills a few (44 bytes) even so, but two
+  // sets of pieces in flight beat one (level walk of B4 H8 T8192: 2.36
+  // against 2.60 ms; the per-wave walk took 3.48 ms)
   __shared__ __attribute__((aligned(16))) E ring[2][D * D];
   __shared__ __attribute__((aligned(16))) E Xs[2 * G * 32 * P];
   const int N = T / C;
@@ -272,28 +283,39 @@ __global__ __launch_bounds__(512) void levels64_kernel(const float *__restrict__
     for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
   const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
   const E *nmh = nm + (size_t)bh * N * D * D;
-  // this wave's piece of -M_c: row pr, 16-byte piece pp
-  const int pr = 8 * wv + (lane >> 3), pp = lane & 7;
-  auto fetch = [&](int c) {
+  // piece i of this wave: row pr(i) of -M_c, 16-byte piece pp(i) of the row
+  auto pr = [&](int i) __attribute__((always_inline)) { return ((wv * NP + i) * 64 + lane) / (D / 8); };
+  auto pp = [&](int i) __attribute__((always_inline)) { return ((wv * NP + i) * 64 + lane) % (D / 8); };
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  using Pieces = u32x4[NP];
+  auto fetch = [&](int c, Pieces &u) __attribute__((always_inline)) {
     c = c < N - 1 ? c : N - 1;
-    return *reinterpret_cast<const uint4 *>(nmh + (size_t)c * D * D + pr * D + 8 * pp);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      u[i] = *reinterpret_cast<const u32x4 *>(nmh + (size_t)c * D * D + pr(i) * D + 8 * pp(i));
   };
-  auto put = [&](int b, const uint4 &u) {
-    *reinterpret_cast<uint4 *>(&ring[b][pr * D + 8 * (pp ^ (pr & 7))]) = u;
+  auto put = [&](int b, const Pieces &u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      *reinterpret_cast<u32x4 *>(&ring[b][pr(i) * D + 8 * (pp(i) ^ (pr(i) & 7))]) = u[i];
   };
   // level c: store it; step to level c + 1 with -M_c from ring[b]; publish
   // -M_{c+1} (in nx) into ring[b ^ 1] and fetch -M_{c+3} into nx
-  auto level = [&](int c, bool active, uint4 &nx) {
+  auto level = [&](int c, bool active, Pieces &nx) __attribute__((always_inline)) {
     const int b = (c - c_lo) & 1;
     __syncthreads();
     if (active) {
+      const size_t off = lev_head + lev_off(c, cp, D);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
+      for (int t = 0; t < D / 32; ++t) {
+        if constexpr (WT) st_tile(levt + off + (size_t)32 * t * C + 32 * kh, 1, C, x[t], lane);
+        st_tile(Xw + 32 * t, P, 1, x[t], lane);
+      }
       wave_sync();
-      E *dst = levels + lev_head + lev_off(c, cp, D) + (size_t)32 * kh * D;
+      E *dst = levels + off + (size_t)32 * kh * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int vi = j * 64 + lane, row = vi / 8, c16 = 8 * (vi % 8);
+      for (int j = 0; j < RV; ++j) {
+        const int vi = j * 64 + lane, row = vi / (D / 8), c16 = 8 * (vi % (D / 8));
         *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
             *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
       }
@@ -312,23 +334,25 @@ __global__ __launch_bounds__(512) void levels64_kernel(const float *__restrict__
       }
     }
     put(b ^ 1, nx);
-    nx = fetch(c + 3);
+    fetch(c + 3, nx);
   };
-  uint4 na, nb;
-  put(0, fetch(c_lo));
-  na = fetch(c_lo + 1);
-  nb = fetch(c_lo + 2);
-  // warm-up: chunk c' = c_lo - 1 + j starts at level c_lo + j
-  for (int j = 0; j < WARM && c_lo + j < N; ++j) {
-    const int c = c_lo + j;
-    const bool active = member && c > cp;
-    if (j & 1) level(c, active, nb);
-    else level(c, active, na);
+  Pieces na, nb;
+  {
+    Pieces n0;
+    fetch(c_lo, n0);
+    put(0, n0);
   }
+  fetch(c_lo + 1, na);
+  fetch(c_lo + 2, nb);
+  // warm-up: chunk c' = c_lo - 1 + j starts at level c_lo + j (register sets
+  // named at compile time, so that both stay in registers)
+  static_assert(WARM == 3, "three warm-up levels");
+  if (c_lo < N) level(c_lo, member && c_lo > cp, na);
+  if (c_lo + 1 < N) level(c_lo + 1, member && c_lo + 1 > cp, nb);
+  if (c_lo + 2 < N) level(c_lo + 2, member && c_lo + 2 > cp, na);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   // steady state: level c_lo + WARM on takes the register set (c - c_lo) & 1
-  static_assert(WARM % 2 == 1, "the walk resumes with the second register set");
-  auto walk = [&](auto stores) {
+  auto walk = [&](auto stores) __attribute__((always_inline)) {
     int c = c_lo + WARM;
     for (; c + 1 < N; c += 2) {   // no exit between the halves: one wait per piece
       level(c, decltype(stores)::value, nb);
@@ -1141,10 +1165,10 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   constexpr int G = group_of<E, D>();
   E *lev = static_cast<E *>(a.levels), *levt = static_cast<E *>(a.levt);
   const E *qae = (const E *)a.qae, *dout = (const E *)a.dout, *v = (const E *)a.v;
-  if constexpr (std::is_same<E, __bf16>::value && D == 64) {
+  if constexpr (std::is_same<E, __bf16>::value) {
     if (N > 1)
-      hipLaunchKernelGGL(levels64_kernel, dim3(BH * ((N - 1 + 3) / 4)), dim3(512), 0, s, a.kb,
-                         (const E *)a.nm, lev, T, BH);
+      hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((N - 1 + 3) / 4)), dim3(512), 0,
+                         s, a.kb, (const E *)a.nm, lev, levt, T, BH);
   } else if (N > 1) {
     hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
                        (const E *)a.nm, lev, levt, T, BH);
