@@ -241,14 +241,18 @@ def bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms_dense):
     ms_packed = timed(lambda: pa.path_attn_fwd_varlen(
         *pv, pb, pl, cu_seqlens=cu, max_seqlen=T, out=out_p, lse=lse_p, workspace=ws), n)
     e = 2 if wl.dtype == "bf16" else 4
-    # staging bytes: 4 input vectors + beta (+ log f) gathered (read + write),
-    # out and lse scattered (read + write)
+    # The strided views are read and written in place (bf16, whole chunks,
+    # 16-byte rows); the packed batch is staged.  Staging bytes: 4 input
+    # vectors + beta (+ log f) gathered (read + write), out and lse scattered
+    # (read + write).
     per_row = 2 * (5 * d * e + 4 + (4 if logf is not None else 0) + 4)
     nbytes = B * H * T * per_row
-    over = ms_strided - ms_dense
+    over = ms_packed - ms_dense
     gbs = nbytes / (over * 1e-3) / 1e9 if over > 0 else None
     return {"ms_dense": ms_dense, "ms_strided_fwd": ms_strided, "ms_packed_fwd": ms_packed,
             "tokens_per_s_strided_fwd": wl.n_tokens / (ms_strided * 1e-3),
+            "strided_in_place": wl.dtype == "bf16" and T % 64 == 0,
+            "strided_overhead_ms": ms_strided - ms_dense,
             "staging_bytes": nbytes, "staging_ms": over,
             "staging_gbs": gbs, "staging_frac_hbm": None if gbs is None else gbs / PEAK_HBM_GBS}
 

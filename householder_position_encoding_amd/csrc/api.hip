@@ -69,6 +69,8 @@ struct FwdViews {
   RowView v[8];
 };
 
+TokStrides tok_strides(const RowView &v) { return TokStrides{v.s_b, v.s_h, v.s_tok}; }
+
 FwdViews dense_fwd_views(int H, int T, int d) {
   FwdViews V;
   for (int i = 0; i < 8; ++i) V.v[i] = dense_view(H, T, i < 5 ? d : 1);
@@ -119,7 +121,8 @@ Carved carve(void *workspace, int B, int H, int T, int d, int dtype, bool views 
 // outputs, then each existing row written to the caller's out and lse views.
 int run_stream(const Carved &ws, bool gate, unsigned flags,
                unsigned long long *skipped, void *out, float *lse, int B, int H,
-               int T, int d, int dtype, float scale, const FwdViews &views, hipStream_t s) {
+               int T, int d, int dtype, float scale, const FwdViews &views, hipStream_t s,
+               bool in_place = false) {
   const int Tp = padded(T);
   StreamArgs a;
   a.qa = ws.qa;
@@ -129,13 +132,17 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
   a.bnd = ws.bnd;
   a.skip = gate && !(flags & PATH_ATTN_NO_SKIP);
   a.skipped = skipped;
-  a.out = ws.F.staged ? static_cast<void *>(ws.base + ws.F.out) : out;
-  a.lse = ws.F.staged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
+  const bool staged = ws.F.staged && !in_place;
+  a.out = staged ? static_cast<void *>(ws.base + ws.F.out) : out;
+  a.lse = staged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
   a.BH = B * H;
   a.T = Tp;
   a.sl2 = 1.4426950408889634f * scale_of(scale, d);
+  a.H = H;
+  a.so = in_place ? tok_strides(views.v[4]) : dense_strides(H, Tp, d);
+  a.sl = in_place ? tok_strides(views.v[7]) : dense_strides(H, Tp, 1);
   if (launch_stream(dtype, d, gate, a, s) != hipSuccess) return PATH_ATTN_EHIP;
-  if (ws.F.staged) {
+  if (staged) {
     const int e = (int)elem_size(dtype);
     if (launch_view_rows(false, a.out, out, views.v[4], B, H, T, Tp, e, d * e, s) != hipSuccess ||
         launch_view_rows(false, a.lse, lse, views.v[7], B, H, T, Tp, 4, 4, s) != hipSuccess)
@@ -148,9 +155,20 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
 // length (inputs first gathered into the zero-padded staging when staged).
 int run_prep(const void *q, const void *k, const void *v, const void *w,
              const float *beta, const float *logf, const Carved &ws, int B, int H,
-             int T, int d, int dtype, const FwdViews &views, hipStream_t s) {
+             int T, int d, int dtype, const FwdViews &views, hipStream_t s,
+             bool in_place = false) {
   const int Tp = padded(T), BH = B * H;
-  if (ws.F.staged) {
+  FwdIo io = dense_io(H, Tp, d);
+  if (in_place) {   // the kernels address the caller's views directly
+    io.q = tok_strides(views.v[0]);
+    io.k = tok_strides(views.v[1]);
+    io.v = tok_strides(views.v[2]);
+    io.w = tok_strides(views.v[3]);
+    io.out = tok_strides(views.v[4]);
+    io.beta = tok_strides(views.v[5]);
+    io.logf = tok_strides(views.v[6]);
+    io.lse = tok_strides(views.v[7]);
+  } else if (ws.F.staged) {
     const int e = (int)elem_size(dtype);
     char *b = ws.base;
     const void *src[] = {q, k, v, w};
@@ -173,9 +191,9 @@ int run_prep(const void *q, const void *k, const void *v, const void *w,
     beta = reinterpret_cast<const float *>(b + ws.F.beta);
     if (logf) logf = reinterpret_cast<const float *>(b + ws.F.logf);
   }
-  if (logf && launch_gate_prefix(logf, ws.gate, BH, Tp, s) != hipSuccess)
+  if (logf && launch_gate_prefix(logf, ws.gate, BH, Tp, io, s) != hipSuccess)
     return PATH_ATTN_EHIP;
-  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, s) !=
+  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, io, s) !=
       hipSuccess)
     return PATH_ATTN_EHIP;
   if (logf && launch_chunk_bounds(dtype, d, ws.kvm, ws.gate, ws.bnd, BH, Tp, s) != hipSuccess)
@@ -235,6 +253,24 @@ bool view_ok(const void *p, const long long *st, size_t esize) {
 
 RowView make_view(const long long *st, const int *cu) { return RowView{cu, st[0], st[1], st[2]}; }
 
+// Whether the forward can address the views in place, without staging: bf16
+// (its chunk preparation reads rows through the view strides; float32 does
+// not), no packed sequences and whole chunks (no row needs zero padding), and
+// every vector row (q, k, v, w, out) starting at a 16-byte boundary with a
+// token pitch below 2^31 elements.  ptrs and strides in the order q, k, v, w,
+// out, beta, logf, lse; the scalar views are already known to be usable.
+bool in_place_ok(const void *const *ptrs, const long long *strides, const int *cu, int T,
+                 int dtype) {
+  if (cu || T % kChunk != 0 || dtype != 1) return false;
+  for (int i = 0; i < 5; ++i) {
+    if (!aligned(ptrs[i], 16)) return false;
+    for (int j = 0; j < 3; ++j)
+      if ((strides[3 * i + j] * 2) % 16 != 0) return false;
+    if (strides[3 * i + 2] >= (1ll << 31)) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" size_t path_attn_varlen_workspace_bytes(int B, int H, int T, int d, int dtype) {
@@ -263,10 +299,11 @@ extern "C" int path_attn_fwd_varlen(const void *q, const void *k, const void *v,
   const Carved ws = carve(workspace, B, H, T, d, dtype, true);
   FwdViews views;
   for (int i = 0; i < 8; ++i) views.v[i] = make_view(strides + 3 * i, cu_seqlens);
-  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
+  const bool direct = in_place_ok(ptrs, strides, cu_seqlens, T, dtype);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s, direct);
   if (st != PATH_ATTN_OK) return st;
   return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, B, H, T, d, dtype, scale,
-                    views, s);
+                    views, s, direct);
 }
 
 extern "C" int path_attn_prepare(const void *q, const void *k, const void *v,

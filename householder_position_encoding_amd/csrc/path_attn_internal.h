@@ -101,6 +101,25 @@ __device__ __forceinline__ unsigned lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_cptr)(p));
 }
 
+// Element strides over (batch, head, token) of a [B, H, T, row] tensor that
+// a kernel reads or writes in place; the flat head index is bh = b * H + h.
+struct TokStrides {
+  long long b, h, t;
+};
+inline TokStrides dense_strides(int H, int T, int row) {
+  return TokStrides{(long long)H * T * row, (long long)T * row, row};
+}
+// The forward's tensors as its kernels address them: inputs q, k, v, w, beta,
+// logf and outputs out, lse.
+struct FwdIo {
+  int H;
+  TokStrides q, k, v, w, beta, logf, out, lse;
+};
+inline FwdIo dense_io(int H, int T, int d) {
+  const TokStrides vec = dense_strides(H, T, d), sca = dense_strides(H, T, 1);
+  return FwdIo{H, vec, vec, vec, vec, sca, sca, vec, sca};
+}
+
 struct Layout {
   size_t qa, kvm, al, gate, bnd, total;
 };
@@ -126,12 +145,14 @@ inline Layout make_layout(int B, int H, int T, int D, size_t esize) {
 }
 
 // Launchers (return hipGetLastError() after the launch).
-hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T,
+// io: how the inputs are addressed (the padded dense layout, or the caller's
+// views when they are read in place: bf16 with whole chunks only).
+hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, const FwdIo &io,
                               hipStream_t stream);
 hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
-                       hipStream_t stream);
+                       const FwdIo &io, hipStream_t stream);
 hipError_t launch_chunk_bounds(int dtype, int D, const void *kvm,
                                const float *gate, float2 *bnd, int BH, int T,
                                hipStream_t stream);
@@ -151,6 +172,8 @@ struct StreamArgs {
   float *lse;
   int BH, T;
   float sl2;   // softmax scale times log2(e)
+  int H;                // bh = b * H + h
+  TokStrides so, sl;    // out and lse row (b, h, t) at b so.b + h so.h + t so.t
 };
 hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
                          hipStream_t stream);

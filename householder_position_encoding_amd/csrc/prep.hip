@@ -49,15 +49,17 @@ struct Kpl<float> { static constexpr int value = 1; };
 // sum_{s=j+1..i} log f_s = Lambda_i - Lambda_j, so f_0 never enters; leaving it
 // out of the prefix keeps the result bitwise independent of it.
 __global__ __launch_bounds__(256) void gate_prefix_kernel(
-    const float *__restrict__ logf, float *__restrict__ gate, int T) {
+    const float *__restrict__ logf, float *__restrict__ gate, int T, int H, TokStrides sf) {
   __shared__ double part[256];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const float *f = logf + (size_t)bh * T;
+  // log f_t of head (b, h) at f[t * sf.t]
+  const float *f0 = logf + (long long)(bh / H) * sf.b + (long long)(bh % H) * sf.h;
+  auto f = [&](int t) { return f0[(long long)t * sf.t]; };
   float *a = gate + (size_t)bh * T;
   const int per = (T + 255) / 256;
   const int t0 = min(T, tid * per), t1 = min(T, t0 + per);
   double s = 0.0;
-  for (int t = max(t0, 1); t < t1; ++t) s += (double)f[t];
+  for (int t = max(t0, 1); t < t1; ++t) s += (double)f(t);
   part[tid] = s;
   __syncthreads();
   if (tid == 0) {
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void gate_prefix_kernel(
   __syncthreads();
   double run = part[tid];
   for (int t = t0; t < t1; ++t) {
-    if (t > 0) run += (double)f[t];
+    if (t > 0) run += (double)f(t);
     a[t] = (float)(-1.4426950408889634 * run);
   }
 }
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const __bf16 *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa,
-    __bf16 *__restrict__ kvm, float *__restrict__ al, int T) {
+    __bf16 *__restrict__ kvm, float *__restrict__ al, int T, FwdIo io) {
   constexpr int C = kChunk, P = 72, PX = 72;
   constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16, KSD = D / 16, KSC = C / 16;
   constexpr int TPW = D / 64;                       // d x 64 tiles per wave
@@ -234,14 +236,17 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
 
   const int N = T / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
-  const size_t row0 = (size_t)bh * T + (size_t)c * C;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int mt = wv >> 1, nt = wv & 1;
-  const __bf16 *qc = q + row0 * D;
-  const __bf16 *kc = k + row0 * D;
-  const __bf16 *vc = v + row0 * D;
-  const __bf16 *wc = w + row0 * D;
+  // the chunk's first row of each input, and the rows' pitch (elements)
+  const long long hb = bh / io.H, hh = bh % io.H;
+  auto first = [&](const TokStrides &st) { return hb * st.b + hh * st.h + (long long)c * C * st.t; };
+  const __bf16 *qc = q + first(io.q);
+  const __bf16 *kc = k + first(io.k);
+  const __bf16 *vc = v + first(io.v);
+  const __bf16 *wc = w + first(io.w);
+  const int sq = (int)io.q.t, sk = (int)io.k.t, sv = (int)io.v.t, sw = (int)io.w.t;
   __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D);
   __bf16 *vf = kf + C * D;
   __bf16 *mf = vf + C * D;
@@ -260,18 +265,19 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   const unsigned char *st_v = smem + SLOT, *st_w = smem + SLOT + 8192;
   if constexpr (STAGE) {
     const __bf16 *src[4] = {qc, kc, vc, wc};
+    const int pitch[4] = {sq, sk, sv, sw};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int job = wv + 4 * i, t = job >> 3, ch = job & 7;   // tensor, 8-row chunk
       const int r = 8 * ch + (lane >> 3), cc = (lane & 7) ^ (r & 7);
       unsigned char *dst = smem + (t >> 1) * SLOT + (t & 1) * 8192 + ch * 1024;
       __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void *)(src[t] + r * D + cc * 8),
+          (__attribute__((address_space(1))) void *)(src[t] + (long long)r * pitch[t] + cc * 8),
           (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
     }
   }
   {
-    const float bval = tid < C ? beta[row0 + tid] : 0.f;
+    const float bval = tid < C ? beta[first(io.beta) + (long long)tid * io.beta.t] : 0.f;
     bf16x8 wm[KSD], wn[KSD], qn[KSD], kn[KSD], km[KSD];
     // <-Q^T and ->K^T start from Q^T and K^T: tiles (eb, xb) = (tau>>1, tau&1)
     bf16x4 qv[TPW][4], kv[TPW][4];
@@ -294,19 +300,19 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
         }
       }
     } else {
-      load_rows<KSD>(wm, wc + 32 * mt * D, D, lane);
-      load_rows<KSD>(wn, wc + 32 * nt * D, D, lane);
-      load_rows<KSD>(qn, qc + 32 * nt * D, D, lane);
-      load_rows<KSD>(kn, kc + 32 * nt * D, D, lane);
-      load_rows<KSD>(km, kc + 32 * mt * D, D, lane);
+      load_rows<KSD>(wm, wc + 32 * mt * (long long)sw, sw, lane);
+      load_rows<KSD>(wn, wc + 32 * nt * (long long)sw, sw, lane);
+      load_rows<KSD>(qn, qc + 32 * nt * (long long)sq, sq, lane);
+      load_rows<KSD>(kn, kc + 32 * nt * (long long)sk, sk, lane);
+      load_rows<KSD>(km, kc + 32 * mt * (long long)sk, sk, lane);
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int tau = wv + 4 * u, eb = tau >> 1, xb = tau & 1;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const size_t off = (size_t)(32 * xb + n) * D + 32 * eb + 8 * r4 + 4 * g;
-          qv[u][r4] = *reinterpret_cast<const bf16x4 *>(qc + off);
-          kv[u][r4] = *reinterpret_cast<const bf16x4 *>(kc + off);
+          const int cidx = 32 * eb + 8 * r4 + 4 * g, r = 32 * xb + n;
+          qv[u][r4] = *reinterpret_cast<const bf16x4 *>(qc + (long long)r * sq + cidx);
+          kv[u][r4] = *reinterpret_cast<const bf16x4 *>(kc + (long long)r * sk + cidx);
         }
       }
     }
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
       if constexpr (STAGE)
         load_rows_sw<KSD>(vm, st_v, 32 * mt, lane);
       else
-        load_rows<KSD>(vm, vc + 32 * mt * D, D, lane);
+        load_rows<KSD>(vm, vc + 32 * mt * (long long)sv, sv, lane);
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int db = nt + 2 * u;
@@ -770,12 +776,12 @@ __global__ __launch_bounds__(256) void unpack_kernel(
 template <int D>
 hipError_t launch_prep_bf16(const void *q, const void *k, const void *v,
                             const void *w, const float *beta, float *qa,
-                            void *kvm, float *al, int BH, int T,
+                            void *kvm, float *al, int BH, int T, const FwdIo &io,
                             hipStream_t stream) {
   hipLaunchKernelGGL((prep_bf16_kernel<D>), dim3(BH * (T / kChunk)), dim3(256), 0,
                      stream, (const __bf16 *)q, (const __bf16 *)k,
                      (const __bf16 *)v, (const __bf16 *)w, beta, qa,
-                     (__bf16 *)kvm, al, T);
+                     (__bf16 *)kvm, al, T, io);
   return hipGetLastError();
 }
 
@@ -856,20 +862,21 @@ hipError_t launch_unpack_t(const float *qa_ws, const void *kvm,
 
 }  // namespace
 
-hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T,
+hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, const FwdIo &io,
                               hipStream_t stream) {
   hipLaunchKernelGGL(gate_prefix_kernel, dim3(BH), dim3(256), 0, stream, logf,
-                     gate, T);
+                     gate, T, io.H, io.logf);
   return hipGetLastError();
 }
 
+// float32 inputs are always read in the padded dense layout (io unused).
 hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
-                       hipStream_t stream) {
+                       const FwdIo &io, hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 64) return launch_prep_bf16<64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
-    return launch_prep_bf16<128>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
+    if (D == 64) return launch_prep_bf16<64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
+    return launch_prep_bf16<128>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
   }
   if (D == 64) return launch_prep_f32<64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
   return launch_prep_f32<128>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);

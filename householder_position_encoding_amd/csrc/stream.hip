@@ -139,7 +139,8 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     const float *__restrict__ qa, const E *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
     const float2 *__restrict__ bnd, int skip, unsigned long long *__restrict__ skipped,
-    E *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2) {
+    E *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2, int H,
+    TokStrides so, TokStrides sl) {
   using MF = Mfma<E>;
   using frag = typename MF::frag;
   constexpr int C = kChunk, KPL = MF::KPL, KSTEP = 2 * KPL;
@@ -364,10 +365,12 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   // ---- epilogue: o_i = O_i / l_i, lse_i = ln 2 (m + log2 l - a_i) ----
   if (!valid) return;
   if (FOX && skipped && lane == 0 && n_skip) atomicAdd(skipped, (unsigned long long)n_skip);
-  const size_t qtok = (size_t)bh * T + (size_t)qcw * C + qloc;
+  const long long tq = (long long)qcw * C + qloc;
+  const long long ob = (long long)(bh / H) * so.b + (long long)(bh % H) * so.h;
+  const long long lb = (long long)(bh / H) * sl.b + (long long)(bh % H) * sl.h;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
-  E *out_r = out + qtok * D;
+  E *out_r = out + ob + tq * so.t;
 #pragma unroll
   for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     }
   if (g == 0) {
     const float a_i = FOX ? gate_h[(size_t)qcw * C + qloc] : 0.f;
-    lse[qtok] = kLn2 * (m_run - a_i + __builtin_amdgcn_logf(l_tot));
+    lse[lb + tq * sl.t] = kLn2 * (m_run - a_i + __builtin_amdgcn_logf(l_tot));
   }
 }
 
@@ -404,7 +407,8 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
     const float *__restrict__ qa, const __bf16 *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
     const float2 *__restrict__ bnd, int skip, unsigned long long *__restrict__ skipped,
-    __bf16 *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2) {
+    __bf16 *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2, int H,
+    TokStrides so, TokStrides sl) {
   using E = __bf16;
   using MF = Mfma<E>;
   using frag = typename MF::frag;
@@ -703,13 +707,15 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
   // ---- epilogue ----
   if (!valid) return;
   if (FOX && skipped && lane == 0 && n_skip) atomicAdd(skipped, (unsigned long long)n_skip);
+  const long long ob = (long long)(bh / H) * so.b + (long long)(bh % H) * so.h;
+  const long long lb = (long long)(bh / H) * sl.b + (long long)(bh % H) * sl.h;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int qloc = 32 * j + n;
-    const size_t qtok = (size_t)bh * T + (size_t)qcw * C + qloc;
+    const long long tq = (long long)qcw * C + qloc;
     const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
     const float inv = 1.f / l_tot;
-    E *out_r = out + qtok * D;
+    E *out_r = out + ob + tq * so.t;
 #pragma unroll
     for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
@@ -721,7 +727,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       }
     if (g == 0) {
       const float a_i = FOX ? gate_h[(size_t)qcw * C + qloc] : 0.f;
-      lse[qtok] = kLn2 * (m_run[j] - a_i + __builtin_amdgcn_logf(l_tot));
+      lse[lb + tq * sl.t] = kLn2 * (m_run[j] - a_i + __builtin_amdgcn_logf(l_tot));
     }
   }
 }
@@ -768,7 +774,7 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
       const int blocks = a.BH * ((N + NQC - 1) / NQC);
       hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
                          stream, a.qa, (const __bf16 *)a.kvm, a.al, a.gate, a.bnd, a.skip,
-                         a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2);
+                         a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl);
       return hipGetLastError();
     };
     if (N <= 64) return go(std::integral_constant<int, 4>{});
@@ -778,7 +784,7 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int blocks = a.BH * ((N + NQC - 1) / NQC);
   hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 128), 0,
                      stream, a.qa, (const E *)a.kvm, a.al, a.gate, a.bnd, a.skip, a.skipped,
-                     (E *)a.out, a.lse, a.BH, a.T, sl2);
+                     (E *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl);
   return hipGetLastError();
 }
 

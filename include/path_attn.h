@@ -361,9 +361,12 @@ int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
  * rows of tokens t >= len_b are not written.  Pointers need 4-byte alignment
  * and every stride times the element size must be a multiple of 4 bytes (an
  * even stride for bf16); rows are moved 16 bytes at a time where base and
- * strides allow.  The inputs are always gathered into zero-padded staging in
- * the workspace (an extra read and write of each input and output) and the
- * results scattered back.  Errors as for the dense entry points, plus EINVAL
+ * strides allow.  bf16 views without cu_seqlens, with T a multiple of 64 and
+ * every q, k, v, w and out row on a 16-byte boundary (base and strides) with
+ * a token stride below 2^31 elements, are read and written in place.  Other
+ * calls gather the inputs into zero-padded staging in the workspace (an extra
+ * read and write of each input and output) and scatter the results back.
+ * Errors as for the dense entry points, plus EINVAL
  * for a NULL strides, a negative stride or one of 2^40 elements or more, or a
  * misaligned base or stride.
  * ------------------------------------------------------------------------

@@ -77,10 +77,14 @@ def _check_grads(tag, dtype, got, ref):
 # ------------------------------------------------------------------ strided
 
 STRIDED = [
-    # dtype, d, fox, B, H, T
+    # dtype, d, fox, B, H, T   (bf16 with T a multiple of 64 is read and
+    # written in place; the others go through the staging)
     ("bf16", 64, True, 2, 3, 100),
     ("f32", 128, False, 1, 2, 128),
     ("f32", 64, True, 2, 1, 65),
+    ("bf16", 64, True, 2, 3, 256),
+    ("bf16", 128, False, 2, 2, 192),
+    ("bf16", 64, False, 1, 2, 512),
 ]
 
 
