@@ -148,26 +148,20 @@ __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
   return ((size_t)c * (c - 1) / 2 + cp) * (size_t)C * D;
 }
 
-// Each wave walks the levels of 32 keys of one key chunk c' < N-1 (blocks of
-// 2 waves, one per key half) and stores level c in rows [64 keys][D] and,
-// except for bf16 with d = 64 (whose consumers transpose on chip),
-// transposed [D][64 keys] (both at lev_off(c, c')).  -M_c is read in the
-// input dtype from global memory (shared by every block of the head), one
-// level ahead, before the level's stores: loads and stores share one counter
-// of outstanding memory operations, so a load issued behind a long train of
-// stores would wait for them.  The row layout is written from the LDS copy
-// of the rounded level (16-byte stores).
-template <typename E, int D>
-__global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ kb,
-                                                     const E *__restrict__ nm,
-                                                     E *__restrict__ levels,
-                                                     E *__restrict__ levt, int T, int BH) {
-  using frag = typename MM<E>::frag;
-  constexpr int KPL = MM<E>::KPL, KS = D / (2 * KPL);
-  constexpr bool PF = KPL > 1;          // bf16: -M_c fragments fetched one level ahead
-  constexpr bool WT = !(KPL > 1 && D == 64);   // transposed copy (bf16, d = 64 transposes on chip)
-  constexpr int EPV = 16 / sizeof(E);   // elements per 16-byte vector
-  constexpr int P = D + EPV;            // rows stay 16-byte aligned
+// float32 inputs: each wave walks the levels of 32 keys of one key chunk
+// c' < N-1 (blocks of 2 waves, one per key half) and stores level c in rows
+// [64 keys][D] and transposed [D][64 keys] (both at lev_off(c, c')).  The
+// product takes -M_c straight from global memory (shared by every block of
+// the head) and the rounded level from its LDS copy; the row layout is
+// written from that copy too.
+template <int D>
+__global__ __launch_bounds__(128) void levels_f32_kernel(const float *__restrict__ kb,
+                                                         const float *__restrict__ nm,
+                                                         float *__restrict__ levels,
+                                                         float *__restrict__ levt, int T, int BH) {
+  using E = float;
+  constexpr int EPV = 4;            // elements per 16-byte vector
+  constexpr int P = D + EPV;        // rows stay 16-byte aligned
   __shared__ __attribute__((aligned(16))) E Xs[2 * 32 * P];
   const int N = T / C;
   const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
@@ -180,28 +174,15 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
   const size_t head = (size_t)bh * lev_off(N, 0, D);
-  // B operand of step c: rows d' = 32 t + col of -M_c, contraction values k0.. of each k-step
-  using MF = frag[D / 32][PF ? KS : 1];
-  auto load_m = [&](int c, MF &mf) {
-    if constexpr (!PF) return;
-    const E *p = nm + ((size_t)bh * N + c) * D * D + (size_t)col * D + KPL * g;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mf[t][ks] = MM<E>::ld(p + (size_t)32 * t * D + 2 * KPL * ks, 1);
-  };
-  // one level: store level c, then (if c + 1 < N) step to level c + 1 with the
-  // fragments of -M_c in cur, fetching those of -M_{c+1} into nxt first
-  auto level = [&](int c, MF &cur, MF &nxt) {
+  for (int c = cp + 1; c < N; ++c) {
     const size_t off = head + lev_off(c, cp, D);
-    if (c + 1 < N - 1) load_m(c + 1, nxt);
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      if (WT) st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
+      st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
       st_tile(Xw + 32 * t, P, 1, x[t], lane);
     }
     wave_sync();
-    // level rows from the LDS copy, 16 bytes per lane and store
+    // level rows from the LDS copy, 16 bytes per lane
     E *dst = levels + off + (size_t)32 * wv * D;
 #pragma unroll
     for (int j = 0; j < 32 * D / EPV / 64; ++j) {
@@ -209,28 +190,13 @@ __global__ __launch_bounds__(128) void levels_kernel(const float *__restrict__ k
       *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
           *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
     }
-    if (c + 1 >= N) return;
-    // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
-    const E *pa = Xw + col * P + KPL * g;
+    if (c + 1 < N) {   // Khat[c+1] = Khat[c] + Khat[c] (-M_c)^T
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      if constexpr (PF) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          x[t] = MM<E>::mma(MM<E>::ld(pa + 2 * KPL * ks, 1), cur[t][ks], x[t]);
-      } else {
+      for (int t = 0; t < D / 32; ++t)
         mma_tile<E, D>(x[t], Xw, P, 1, nm + ((size_t)bh * N + c) * D * D + (size_t)32 * t * D, D,
                        1, lane);
-      }
     }
     wave_sync();
-  };
-  MF ma, mb;
-  if (cp + 1 < N - 1) load_m(cp + 1, ma);
-  for (int c = cp + 1; c < N; c += 2) {
-    level(c, ma, mb);
-    if (c + 1 >= N) break;
-    level(c + 1, mb, ma);
   }
 }
 
@@ -1170,8 +1136,8 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
       hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((N - 1 + 3) / 4)), dim3(512), 0,
                          s, a.kb, (const E *)a.nm, lev, levt, T, BH);
   } else if (N > 1) {
-    hipLaunchKernelGGL((levels_kernel<E, D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
-                       (const E *)a.nm, lev, levt, T, BH);
+    hipLaunchKernelGGL((levels_f32_kernel<D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
+                       (const float *)a.nm, lev, levt, T, BH);
   }
   if constexpr (std::is_same<E, __bf16>::value && D == 64)
     hipLaunchKernelGGL((dq64_kernel<FOX>), dim3(BH * N), dim3(128), 0, s, qae, dout, a.lse, a.dlse,
