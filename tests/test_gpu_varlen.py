@@ -268,3 +268,35 @@ def test_packed_equal_lengths_match_dense_bit_for_bit():
             continue
         assert torch.equal(pk(a), b), f"{n} differs between the dense and the packed call"
     _log("packed equal lengths: forward and backward identical to the dense call")
+
+
+def test_strided_misaligned_rows_are_staged():
+    """bf16 views of whole chunks whose rows start 4 bytes off a 16-byte
+    boundary cannot be read in place (the chunk preparation copies 16-byte
+    pieces): the call falls back to the staging copies and still matches the
+    oracle, inputs and outputs alike."""
+    import torch
+    import householder_position_encoding_amd as pa
+    B, H, T, d = 1, 2, 128, 64
+    inp = workloads.small("bf16", B, H, T, d, seed=777, fox=True)
+    n = B * H * T * d
+
+    def shifted(arr):
+        buf = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")
+        view = buf.as_strided((B, H, T, d), (H * T * d, T * d, d, 1), 2)
+        if arr is not None:
+            view.copy_(torch.from_numpy(arr).to(torch.bfloat16))
+        return view
+
+    x = {k: shifted(inp[k]) for k in ("q", "k", "v", "w")}
+    beta = torch.from_numpy(inp["beta"]).cuda()
+    logf = torch.from_numpy(inp["logf"]).cuda()
+    out = shifted(None)
+    lse = torch.zeros(B, H, T, dtype=torch.float32, device="cuda")
+    assert x["q"].data_ptr() % 16 == 4
+    out, lse = pa.path_attn_fwd_varlen(x["q"], x["k"], x["v"], x["w"], beta, logf, out=out,
+                                       lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.path_attn(inp["q"], inp["k"], inp["v"], inp["w"], inp["beta"],
+                                    inp["logf"])
+    _check_fwd("strided misaligned", "bf16", _np(out), _np(lse), o_ref, l_ref)
