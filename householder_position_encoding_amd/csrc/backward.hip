@@ -40,6 +40,28 @@ constexpr int NT = 256;
 template <typename E>
 __device__ __forceinline__ float ld(const E *p) { return (float)*p; }
 
+// 16 bytes of a row as floats: 8 bf16 or 4 float32 elements (p 16-byte aligned).
+template <typename E>
+struct Row16;
+template <>
+struct Row16<__bf16> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void load(float (&x)[N], const __bf16 *p) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int t = 0; t < N; ++t) x[t] = (float)v[t];
+  }
+};
+template <>
+struct Row16<float> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void load(float (&x)[N], const float *p) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int t = 0; t < N; ++t) x[t] = v[t];
+  }
+};
+
 // ------------------------------------------------------------ chunk prep
 
 // Per-chunk float32 matrices kept from the preparation for the adjoint:
@@ -197,18 +219,42 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
   const size_t row0 = (size_t)bh * T + (size_t)c * C;
   const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
-  for (int idx = tid; idx < C * D; idx += NT) {
-    Os[(idx / D) * DP + idx % D] = ld(dout + row0 * D + idx);
-    Vs[(idx / D) * DP + idx % D] = ld(v + row0 * D + idx);
+  // dO and V rows to LDS as floats, 16 bytes per load
+  using RV = Row16<E>;
+  constexpr int VPR = D / RV::N;   // 16-byte loads per row
+  for (int vi = tid; vi < C * VPR; vi += NT) {
+    const int r = vi / VPR, e0 = RV::N * (vi % VPR);
+    float xo[RV::N], xv[RV::N];
+    RV::load(xo, dout + (row0 + r) * D + e0);
+    RV::load(xv, v + (row0 + r) * D + e0);
+#pragma unroll
+    for (int t = 0; t < RV::N; ++t) {
+      Os[r * DP + e0 + t] = xo[t];
+      Vs[r * DP + e0 + t] = xv[t];
+    }
   }
-  if (tid < C) {
+  {   // rowdot(dO, O): four threads per row, each a quarter of the columns
+    static_assert(NT == 4 * C, "four threads per row");
+    const int r = tid >> 2, part = tid & 3;
+    const E *pd = dout + (row0 + r) * D + part * (D / 4), *po = o + (row0 + r) * D + part * (D / 4);
     float s = 0.f;
-    for (int e = 0; e < D; ++e) s = __builtin_fmaf(ld(dout + (row0 + tid) * D + e), ld(o + (row0 + tid) * D + e), s);
-    rd[tid] = s;
-    dvec[row0 + tid] = s;
-    rl[tid] = lse[row0 + tid];
-    rg[tid] = FOX ? lam[row0 + tid] : 0.f;
-    rdl[tid] = dlse ? dlse[row0 + tid] : 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 4; e += RV::N) {
+      float xd[RV::N], xo[RV::N];
+      RV::load(xd, pd + e);
+      RV::load(xo, po + e);
+#pragma unroll
+      for (int t = 0; t < RV::N; ++t) s = __builtin_fmaf(xd[t], xo[t], s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (part == 0) {
+      rd[r] = s;
+      dvec[row0 + r] = s;
+      rl[r] = lse[row0 + r];
+      rg[r] = FOX ? lam[row0 + r] : 0.f;
+      rdl[r] = dlse ? dlse[row0 + r] : 0.f;
+    }
   }
   __syncthreads();
   if (!IMG)
