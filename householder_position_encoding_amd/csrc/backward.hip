@@ -260,14 +260,25 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
   if (!IMG)
     for (int idx = tid; idx < C * D; idx += NT)   // dO^T of the chunk, [D][64]
       dot[((size_t)bh * N + c) * C * D + idx] = (E)Os[(idx % C) * DP + idx / C];
-  if (IMG) {
+  if (IMG) {   // bf16, d = 64: 16-byte stores of 8 values each
     E *img = oimg + ((size_t)bh * N + c) * kQImgElems;
-    for (int idx = tid; idx < 64 * kImgPitch; idx += NT) {   // dO rows
-      const int r = idx / kImgPitch, cc = idx % kImgPitch;
-      img[idx] = cc < 64 ? (E)Os[r * DP + cc] : (E)0.f;
+    for (int vi = tid; vi < 64 * (kImgPitch / 8); vi += NT) {   // dO rows, zero padded
+      const int r = vi / (kImgPitch / 8), c8 = 8 * (vi % (kImgPitch / 8));
+      bf16x8 x;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) x[t] = c8 < 64 ? (E)Os[r * DP + c8 + t] : (E)0.f;
+      *reinterpret_cast<bf16x8 *>(img + r * kImgPitch + c8) = x;
     }
-    for (int idx = tid; idx < 64 * 64; idx += NT)   // dO in fragment order
-      img[64 * kImgPitch + mimg_index(idx / 64, idx % 64)] = (E)Os[(idx / 64) * DP + idx % 64];
+    // dO in fragment order: blob (mt, s), lane l holds the 8 values
+    // dO[frag_row(s, l/32, t)][32 mt + l%32], t < 8, contiguously
+    for (int vi = tid; vi < 8 * 64; vi += NT) {
+      const int blob = vi / 64, l = vi % 64, mt = blob / 4, sI = blob % 4;
+      bf16x8 x;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        x[t] = (E)Os[frag_row(sI, l / 32, t, 8) * DP + 32 * mt + l % 32];
+      *reinterpret_cast<bf16x8 *>(img + 64 * kImgPitch + (blob * 64 + l) * 8) = x;
+    }
     if (tid < C) qst[row0 + tid] = make_float4(rl[tid], rd[tid], rdl[tid], rg[tid]);
   }
   const float *al_c = al + ((size_t)bh * N + c) * C * C;
