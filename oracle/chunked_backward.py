@@ -5,9 +5,11 @@ The pages give no backward algorithm; this module states, in plain fp64
 numpy, the blockwise decomposition the GPU path computes, so that each of its
 intermediate quantities can be checked on its own.  It is pinned to
 oracle/backward.py (autograd of the definition) in
-tests/test_oracle_backward.py: the final gradients must agree.
+tests/test_oracle_backward.py: the final gradients must agree, for small
+chunk sizes and at the chunk length 64 with head dims 64 and 128 (the sizes at
+which the GPU tests use it).
 
-Forward algebra (oracle/chunked.py; PaTH slides, frames "A triangular
+Forward algebra (oracle/chunked.py, ut_chunk_quantities; PaTH slides, frames "A triangular
 representation makes paths computable", "A right-to-left scan accumulates
 cross-block paths", "Backup: fix orientation before implementing UT
 products"): per chunk c, Qa = <-Q_c, Kb = ->K_c, M_c, Al_c.  Keys of chunks
@@ -34,7 +36,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from oracle.chunked import chunk_quantities
+from oracle.chunked import ut_chunk_quantities
 
 
 def _chunk_forward_torch(Q, K, W, beta):
@@ -93,11 +95,11 @@ def sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=None, scale=None, C=
     else:
         lam = np.zeros(T)
     sl = lambda c: slice(c * C, (c + 1) * C)
-    parts = [chunk_quantities(q[sl(c)], k[sl(c)], w[sl(c)], beta[sl(c)]) for c in range(n)]
-    Qa = [p[1] for p in parts]
-    Kb = [p[2] for p in parts]
-    M = [p[3] for p in parts]
-    Al = [p[4] for p in parts]
+    parts = [ut_chunk_quantities(q[sl(c)], k[sl(c)], w[sl(c)], beta[sl(c)]) for c in range(n)]
+    Qa = [p["qa"] for p in parts]
+    Kb = [p["kb"] for p in parts]
+    M = [p["m"] for p in parts]
+    Al = [p["al"] for p in parts]
     lev = key_levels(Kb, M, C)
     Dv = np.sum(do * o, axis=1)
 

@@ -59,11 +59,11 @@ def test_chunk_prep_matches_oracle_algebra(dtype, d, fox):
             for c in range(T // C):
                 sl = slice(c * C, (c + 1) * C)
                 args = [inp[x][b, h, sl].astype(np.float64) for x in ("q", "k", "w")]
-                U, Qa, Kb, M, Al = chunk_quantities(*args, inp["beta"][b, h, sl].astype(np.float64))
-                for name, ref, g, r in (("qa", Qa, got["qa"][b, h, sl], 1e-4),
-                                        ("kb", Kb, got["kb"][b, h, sl], rel),
-                                        ("m", M, got["m"][b, h, c], rel),
-                                        ("al", Al[low], got["al"][b, h, c][low], 1e-4)):
+                ref_q = chunk_quantities(*args, inp["beta"][b, h, sl].astype(np.float64))
+                for name, ref, g, r in (("qa", ref_q["qa"], got["qa"][b, h, sl], 1e-4),
+                                        ("kb", ref_q["kb"], got["kb"][b, h, sl], rel),
+                                        ("m", ref_q["m"], got["m"][b, h, c], rel),
+                                        ("al", ref_q["al"][low], got["al"][b, h, c][low], 1e-4)):
                     scale = 1.0 + np.max(np.abs(ref))
                     err = np.max(np.abs(g - ref) / (np.abs(ref) * r + 1e-4 * scale))
                     assert err <= 1.0, f"{name} chunk {(b, h, c)}: normalised error {err}"

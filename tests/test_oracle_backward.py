@@ -129,3 +129,25 @@ def test_blockwise_backward_equals_autograd(C, n, d, fox):
                             ref["o"], ref["lse"], dlse=dlse, C=C)
     for name in ("dq", "dk", "dv", "dw", "dbeta") + (("dlogf",) if fox else ()):
         np.testing.assert_allclose(got[name], ref[name], rtol=1e-9, atol=1e-10, err_msg=name)
+
+
+@pytest.mark.parametrize("T,d,fox,near2", [(256, 64, False, 0.0), (384, 64, True, 0.0),
+                                           (256, 128, True, 0.0), (320, 128, False, 0.1)])
+def test_blockwise_backward_equals_autograd_at_chunk_64(T, d, fox, near2):
+    """The same pin at the chunk length the GPU path and the full-size GPU
+    tests use (C = 64), at the head dims 64 and 128 and 4-6 chunks, on inputs
+    of the workloads' recipe (unit-norm w, beta = 2 sigmoid(N(0, 1.5)), 10 %
+    of beta in [1.9, 2) in one case, log f = logsigmoid(N(3, 1)))."""
+    import workloads
+    from oracle import chunked_backward as cb
+    x = workloads.small("f32", 1, 1, T, d, seed=650 + T + d, beta_sigma=1.5,
+                        near2_frac=near2, fox=fox)
+    x = {n: (None if a is None else np.asarray(a[0, 0], dtype=np.float64)) for n, a in x.items()}
+    cot = workloads.cotangents("f32", 1, 1, T, d, seed=660 + T)
+    do, dlse = cot["dout"][0, 0].astype(np.float64), cot["dlse"][0, 0].astype(np.float64)
+    ref = ob.gradients(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do, dlse)
+    got = cb.sweep_backward(x["q"], x["k"], x["v"], x["w"], x["beta"], x["logf"], do,
+                            ref["o"], ref["lse"], dlse=dlse, C=64)
+    for name in ("dq", "dk", "dv", "dw", "dbeta") + (("dlogf",) if fox else ()):
+        scale = max(1.0, float(np.max(np.abs(ref[name]))))
+        np.testing.assert_allclose(got[name], ref[name], rtol=0, atol=1e-11 * scale, err_msg=name)

@@ -24,7 +24,7 @@ import pytest
 from scipy.linalg import solve_triangular
 
 import oracle
-from oracle.chunked import chunked_logits
+from oracle.chunked import chunk_quantities, chunked_logits, ut_chunk_quantities
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -203,15 +203,52 @@ def pin_global_ut_formula(lib):
 
 def pin_chunked_algorithm(lib):
     """The blockwise right-to-left scan reproduces the definition for several
-    chunk sizes (C = 1 is the walk itself)."""
+    chunk sizes (C = 1 is the walk itself), including the chunk length 64 of
+    the GPU path."""
     rng = np.random.default_rng(107)
-    T, d = 32, 6
-    q, k, _, w, beta = _rand_inputs(rng, T, d)
+    for T, d, Cs in ((32, 6, (1, 2, 4, 16)), (192, 8, (64,))):
+        q, k, _, w, beta = _rand_inputs(rng, T, d)
+        S = oracle.path_logits(q, k, w, beta, lib=lib)
+        low = np.tril(np.ones((T, T), dtype=bool))
+        for C in Cs:
+            A = chunked_logits(q, k, w, beta, C)
+            np.testing.assert_allclose(S[low], A[low], rtol=1e-11, atol=1e-11)
+            assert np.all(A[~low] == -np.inf)
+
+
+def pin_chunk_quantities(lib):
+    """Per-chunk quantities: the definitions (explicit products of the H_t)
+    agree with the UT form of the backup frame (U from a library triangular
+    solve), and the diagonal-block logits and the moved queries and keys agree
+    with the walk: Al[i, j] is the path logit c_ij of the chunk alone, <-Q row
+    i is the walk of q_i down to the chunk start, and ->K row j dotted with a
+    query moved to the chunk end gives the path logit from that end."""
+    rng = np.random.default_rng(110)
+    C, d = 24, 7
+    q, k, _, w, beta = _rand_inputs(rng, C, d)
+    got = chunk_quantities(q, k, w, beta)
+    ut = ut_chunk_quantities(q, k, w, beta)
+    low = np.tril(np.ones((C, C), dtype=bool))
+    for name in ("qa", "kb", "m"):
+        np.testing.assert_allclose(got[name], ut[name], rtol=1e-12, atol=1e-12, err_msg=name)
+    np.testing.assert_allclose(got["al"][low], ut["al"][low], rtol=1e-12, atol=1e-12)
     S = oracle.path_logits(q, k, w, beta, lib=lib)
-    low = np.tril(np.ones((T, T), dtype=bool))
-    for C in (1, 2, 4, 16):
-        A = chunked_logits(q, k, w, beta, C)
-        np.testing.assert_allclose(S[low], A[low], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(got["al"][low], S[low], rtol=1e-12, atol=1e-12)
+    # with one token put before the chunk, the walk of row i + 1 down to that
+    # token has crossed H_first ... H_i of the chunk: <-Q row i
+    q1, w1 = np.vstack([np.zeros((1, d)), q]), np.vstack([w[:1], w])
+    for i in (0, 5, C - 1):
+        Z = oracle.path_walk(q1, w1, np.append(0.0, beta), i + 1, lib=lib)
+        np.testing.assert_allclose(got["qa"][i], Z[i + 1], rtol=1e-12, atol=1e-12)
+    # a query placed just after the chunk (beta = 0 for it) sees key j through
+    # H_{j+1} ... H_last, i.e. through ->K row j
+    q2 = np.vstack([q, rng.standard_normal((1, d))])
+    k2 = np.vstack([k, np.zeros((1, d))])
+    w2 = np.vstack([w, w[:1]])
+    S2 = oracle.path_logits(q2, k2, w2, np.append(beta, 0.0), lib=lib)
+    np.testing.assert_allclose(S2[C, :C], got["kb"] @ q2[C], rtol=1e-12, atol=1e-12)
+    # the backup frame's transposed UT factor gives F itself
+    np.testing.assert_allclose(got["F"], np.eye(d) - w.T @ ut["U"].T @ w, rtol=1e-12, atol=1e-12)
 
 
 def pin_softmax_readout(lib):
@@ -341,6 +378,7 @@ ALL_PINS = [
     pin_decode_key_refinement,
     pin_global_ut_formula,
     pin_chunked_algorithm,
+    pin_chunk_quantities,
     pin_softmax_readout,
     pin_eigen_direction_golden,
     pin_walk_invariants,
