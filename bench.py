@@ -63,8 +63,18 @@ def parse():
                     help="skip the strided / packed forward measurement")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
-                    help="JSON with measured HBM bytes per stream-kernel launch")
+    ap.add_argument("--counters", default=os.path.join(ROOT, "profiles", "counters.json"),
+                    help="JSON of per-launch hardware-counter figures (HBM bytes, matrix-core "
+                         "use) of the stream kernel, written by --pmc-report")
+    ap.add_argument("--pmc-report", nargs="+", metavar="DIR", default=None,
+                    help="do not run: summarise the rocprofv3 --pmc output directories given "
+                         "(run_counter_collection.csv below each) per kernel, write the "
+                         "markdown summary (--pmc-md) and this workload's record in --counters")
+    ap.add_argument("--pmc-md", default=None,
+                    help="markdown file of --pmc-report (default profiles/counters_<workload>.md)")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command line that produced a --pmc-report input (repeatable; "
+                         "quoted in the summary)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference "
                          "kernel for scaling HBM traffic counters) and report its GB/s")
@@ -86,27 +96,46 @@ def cpu_threads() -> int:
     return max(1, n)
 
 
-def cpu_baseline(wl, inp, n_heads: int):
-    """fp64 oracle on the first n_heads (b, h) heads, all rows; the rate is
-    scaled to the whole workload (every head costs the same)."""
+def cpu_baseline(wl, inp, n_heads: int, out=None, lse=None):
+    """fp64 oracle on n_heads whole (b, h) heads spread over the flat head
+    index, all rows; the rate is scaled to the whole workload (every head
+    costs the same).  With the GPU's out and lse of the same inputs, also the
+    max-abs errors of every row of those heads against the oracle."""
     import numpy as np
     import oracle
-    n_heads = max(1, min(n_heads, wl.B * wl.H))
-    flat = lambda x: x.reshape(wl.B * wl.H, wl.T, -1)[:n_heads].astype(np.float64)
+    BH = wl.B * wl.H
+    n_heads = max(1, min(n_heads, BH))
+    heads = np.unique(np.linspace(0, BH - 1, n_heads).round().astype(np.int64))
+    n_heads = len(heads)
+    flat = lambda x: x.reshape(BH, wl.T, -1)[heads].astype(np.float64)
     q, k, v, w = (flat(inp[n]) for n in ("q", "k", "v", "w"))
-    beta = inp["beta"].reshape(wl.B * wl.H, wl.T)[:n_heads].astype(np.float64)
-    logf = None if inp["logf"] is None else inp["logf"].reshape(wl.B * wl.H, wl.T)[:n_heads].astype(np.float64)
+    beta = inp["beta"].reshape(BH, wl.T)[heads].astype(np.float64)
+    logf = None if inp["logf"] is None else inp["logf"].reshape(BH, wl.T)[heads].astype(np.float64)
     rows = np.stack(np.meshgrid(np.arange(n_heads), np.arange(wl.T), indexing="ij"), -1).reshape(-1, 2)
     threads = cpu_threads()
     t0 = time.perf_counter()
-    oracle.path_attn_rows(q, k, v, w, beta, logf, 1.0 / np.sqrt(wl.d), rows, n_threads=threads)
+    o_ref, l_ref = oracle.path_attn_rows(q, k, v, w, beta, logf, 1.0 / np.sqrt(wl.d), rows,
+                                         n_threads=threads)
     dt = time.perf_counter() - t0
-    full_s = dt * (wl.B * wl.H) / n_heads
-    return {"value": wl.B * wl.T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_heads} of {wl.B * wl.H} (b,h) heads, all {wl.T} query rows each "
-                      f"({n_heads * wl.T * (wl.T + 1) // 2:.3g} causal pairs) in {dt:.2f} s; "
-                      f"rate scaled by {wl.B * wl.H / n_heads:g} to the whole workload",
-            "seconds_sample": dt}
+    full_s = dt * BH / n_heads
+    res = {"value": wl.B * wl.T / full_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_heads} of {BH} (b,h) heads (flat indices {heads.tolist()}), all {wl.T} "
+                     f"query rows each ({n_heads * wl.T * (wl.T + 1) // 2:.3g} causal pairs) in "
+                     f"{dt:.2f} s; rate scaled by {BH / n_heads:g} to the whole workload",
+           "seconds_sample": dt}
+    parity = None
+    if out is not None:
+        got_o = out.reshape(BH, wl.T, wl.d)[heads.tolist()].float().cpu().numpy().astype(np.float64)
+        got_l = lse.reshape(BH, wl.T)[heads.tolist()].cpu().numpy().astype(np.float64)
+        tol_o, tol_l = (2e-2, 1e-2) if wl.dtype == "bf16" else (1e-4, 1e-4)
+        eo = float(np.max(np.abs(got_o.reshape(-1, wl.d) - o_ref)))
+        el = float(np.max(np.abs(got_l.reshape(-1) - l_ref)))
+        parity = {"max_abs_err_o": eo, "max_abs_err_lse": el, "tol_o": tol_o, "tol_lse": tol_l,
+                  "within_tol": eo <= tol_o and el <= tol_l, "rows": int(n_heads * wl.T),
+                  "heads_flat": heads.tolist(),
+                  "what": "GPU out/lse of the timed steps against the fp64 oracle, every row of "
+                          "the oracle's heads"}
+    return res, parity
 
 
 def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
@@ -257,8 +286,208 @@ def bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms_dense):
             "staging_gbs": gbs, "staging_frac_hbm": None if gbs is None else gbs / PEAK_HBM_GBS}
 
 
+# ---------------------------------------------------------------- counters
+
+def _short_kernel_name(mangled: str) -> str:
+    """Readable name of a library kernel from its mangled name: the function
+    name and its template arguments (integers, bools, float / bf16 types)."""
+    import re
+    m = re.search(r"_GLOBAL__N_1(\d+)", mangled) or re.search(r"N8pathattn(\d+)", mangled)
+    if not m:
+        return mangled
+    n = int(m.group(1))
+    name = mangled[m.end():m.end() + n]
+    rest = mangled[m.end() + n:]
+    args = []
+    if rest.startswith("I"):
+        rest = rest[1:]
+        while rest and not rest.startswith("E"):
+            t = re.match(r"L(i|j|b)(\d+)E|DF16b|f|d", rest)
+            if not t:
+                break
+            tok = t.group(0)
+            if tok.startswith("Lb"):
+                args.append("true" if t.group(2) == "1" else "false")
+            elif tok.startswith("L"):
+                args.append(t.group(2))
+            else:
+                args.append({"DF16b": "bf16", "f": "float", "d": "double"}[tok])
+            rest = rest[len(tok):]
+    return name + (f"<{', '.join(args)}>" if args else "")
+
+
+def read_counter_dirs(dirs):
+    """Per kernel (mangled name) and counter: the list of per-dispatch values,
+    the per-dispatch durations (ns) seen with each counter, and the agent's
+    SIMD count, XCD count and peak engine clock (MHz) from run_agent_info.csv."""
+    import csv
+    import glob
+    vals, durs = {}, {}
+    agent = {"simd": 1024, "xcc": 8, "mhz": 2400}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (r["Kernel_Name"], r["Counter_Name"])
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+                    durs.setdefault(r["Kernel_Name"], []).append(
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            info = os.path.join(os.path.dirname(f), os.path.basename(f).replace(
+                "counter_collection", "agent_info"))
+            if os.path.exists(info):
+                with open(info) as fh:
+                    for r in csv.DictReader(fh):
+                        if r.get("Agent_Type") == "GPU":
+                            agent = {"simd": int(r["Simd_Count"]), "xcc": int(r["Num_Xcc"]),
+                                     "mhz": int(r["Max_Engine_Clk_Fcompute"])}
+    return vals, durs, agent
+
+
+def summarise_counters(vals, durs, agent, copy_bytes=0):
+    """Figures per kernel from the raw counters, means over its dispatches.
+
+    Matrix cores: executed flop = 512 * SQ_INSTS_VALU_MFMA_MOPS_{BF16,F32}
+    (the counters count flop / 512); busy = SQ_VALU_MFMA_BUSY_CYCLES (summed
+    over SIMDs) over the SIMD-cycles of the dispatch, GRBM_GUI_ACTIVE / XCDs
+    * SIMDs (GRBM_GUI_ACTIVE is summed over the XCDs), as rocprofv3's
+    MfmaUtil; co-execution likewise from SQ_VALU_MFMA_COEXEC_CYCLES.  HBM:
+    FETCH_SIZE and WRITE_SIZE (KiB) scaled by what they read for the plain
+    device copy of copy_bytes (torch copy_, a "copyBuffer" kernel)."""
+    import statistics
+    mean = lambda k, c: statistics.mean(vals[(k, c)]) if (k, c) in vals else None
+    kernels = sorted({k for k, _ in vals})
+    scale_f = scale_w = None
+    if copy_bytes:
+        copies = [k for k in kernels if "copyBuffer" in k or "copy" in k.lower()]
+        cf = max((v for k in copies for v in vals.get((k, "FETCH_SIZE"), [])), default=None)
+        cw = max((v for k in copies for v in vals.get((k, "WRITE_SIZE"), [])), default=None)
+        scale_f = copy_bytes / 1024 / cf if cf else None
+        scale_w = copy_bytes / 1024 / cw if cw else None
+    out = {}
+    for k in kernels:
+        dur = statistics.mean(durs[k]) * 1e-9
+        rec = {"name": _short_kernel_name(k), "dispatches": len(vals.get((k, next(
+            c for kk, c in vals if kk == k)), [])), "mean_duration_ms": dur * 1e3}
+        gui = mean(k, "GRBM_GUI_ACTIVE")
+        busy = mean(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = [mean(k, "SQ_INSTS_VALU_MFMA_MOPS_" + t) for t in ("BF16", "F32")]
+        if any(m is not None for m in mops):
+            flop = 512.0 * sum(m for m in mops if m is not None)
+            rec["mfma_flop"] = flop
+            rec["mfma_flop_bf16"] = None if mops[0] is None else 512.0 * mops[0]
+            rec["mfma_tflops"] = flop / dur / 1e12
+        if mean(k, "SQ_INSTS_MFMA") is not None:
+            rec["mfma_insts"] = mean(k, "SQ_INSTS_MFMA")
+        if gui is not None:
+            simd_cycles = gui / agent["xcc"] * agent["simd"]
+            rec["clock_mhz"] = gui / agent["xcc"] / dur / 1e6
+            if busy is not None:
+                rec["mfma_busy_frac"] = busy / simd_cycles
+            co = mean(k, "SQ_VALU_MFMA_COEXEC_CYCLES")
+            if co is not None:
+                rec["mfma_valu_coexec_frac"] = co / simd_cycles
+        if busy is not None:
+            rec["mfma_busy_frac_at_peak_clock"] = busy / (dur * agent["mhz"] * 1e6 * agent["simd"])
+        fetch, write = mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")
+        if fetch is not None:
+            rec["fetch_kib_raw"] = fetch
+        if write is not None:
+            rec["write_kib_raw"] = write
+        if fetch is not None and write is not None and scale_f and scale_w:
+            rec["hbm_bytes"] = (fetch * scale_f + write * scale_w) * 1024
+            rec["hbm_gbs"] = rec["hbm_bytes"] / dur / 1e9
+            rec["hbm_frac"] = rec["hbm_gbs"] / PEAK_HBM_GBS
+        out[k] = rec
+    return out, {"fetch_scale": scale_f, "write_scale": scale_w}
+
+
+def pmc_report(args):
+    """--pmc-report: summarise rocprofv3 counter runs (markdown + JSON)."""
+    import hashlib
+    import workloads
+    wl = workloads.BY_NAME[args.workload]
+    vals, durs, agent = read_counter_dirs(args.pmc_report)
+    copy_bytes = args.calib_copy_mb << 20
+    per, scales = summarise_counters(vals, durs, agent, copy_bytes)
+    flops = wl.flops_path()
+    want = stream_kernel_name(wl).split("<")[0]
+    stream_k = [k for k in per if want in k and ("Lb1E" in k) == wl.fox]
+    src = os.path.join(ROOT, "householder_position_encoding_amd", "csrc", "stream.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    md = os.path.join(ROOT, "profiles", f"counters_{wl.name}.md") if args.pmc_md is None else args.pmc_md
+    lines = [f"# Hardware counters: {wl.name} (B={wl.B} H={wl.H} T={wl.T} d={wl.d}, {wl.dtype}"
+             f"{', gate' if wl.fox else ''})", "",
+             "Made by `python bench.py --pmc-report <dirs> --workload " + wl.name +
+             (f" --calib-copy-mb {args.calib_copy_mb}" if args.calib_copy_mb else "") +
+             "` from these rocprofv3 runs (each its own process, after `cd /tmp && export "
+             "TMPDIR=/tmp`):", ""]
+    lines += [f"    {c}" for c in args.pmc_command] + [""]
+    lines += [f"GPU: {agent['simd']} SIMDs, {agent['xcc']} XCDs, peak engine clock {agent['mhz']} MHz.",
+              "Matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs) "
+              "(rocprofv3's MfmaUtil); executed flop = 512 x SQ_INSTS_VALU_MFMA_MOPS_*.", ""]
+    if scales["fetch_scale"]:
+        lines += [f"HBM bytes = FETCH_SIZE x {scales['fetch_scale']:.3f} + WRITE_SIZE x "
+                  f"{scales['write_scale']:.3f} (KiB): the factors make the counters read "
+                  f"{copy_bytes} bytes each way for the bench's plain device copy of that size.", ""]
+    lines += ["| kernel | dispatches | mean ms (profiled) | clock MHz | MFMA flop | MFMA busy | "
+              "MFMA+VALU co-exec | HBM bytes | HBM GB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    f = lambda x, fmt: "" if x is None else format(x, fmt)
+    for k, r in sorted(per.items(), key=lambda kv: -kv[1]["mean_duration_ms"] * kv[1]["dispatches"]):
+        if "copy" in k.lower() and "pathattn" not in k:
+            continue
+        lines.append(f"| {r['name'][:70]} | {r['dispatches']} | {r['mean_duration_ms']:.3f} | "
+                     f"{f(r.get('clock_mhz'), '.0f')} | {f(r.get('mfma_flop'), '.4g')} | "
+                     f"{f(r.get('mfma_busy_frac'), '.3f')} | {f(r.get('mfma_valu_coexec_frac'), '.3f')} | "
+                     f"{f(r.get('hbm_bytes'), '.4g')} | {f(r.get('hbm_gbs'), '.0f')} |")
+    rec = None
+    if stream_k:
+        r = per[stream_k[0]]
+        rec = {"kernel": stream_k[0], "stream_hip_sha256_16": sha,
+               "flops_path": flops,
+               "mfma_flop_per_launch": r.get("mfma_flop"),
+               "mfma_flop_over_flops_path": None if r.get("mfma_flop") is None else r["mfma_flop"] / flops,
+               "mfma_busy_frac": r.get("mfma_busy_frac"),
+               "mfma_busy_frac_at_peak_clock": r.get("mfma_busy_frac_at_peak_clock"),
+               "mfma_valu_coexec_frac": r.get("mfma_valu_coexec_frac"),
+               "clock_mhz_profiled": r.get("clock_mhz"),
+               "hbm_bytes_per_launch": r.get("hbm_bytes"),
+               "hbm_gbs_profiled": r.get("hbm_gbs"),
+               "mean_duration_ms_profiled": r["mean_duration_ms"]}
+        lines += ["", f"Stream kernel `{r['name']}`: F_path = B*H*T^2*(2d + d^2/64) = {flops:.4g} flop per "
+                  "launch" + ("" if rec["mfma_flop_over_flops_path"] is None else
+                              f"; executed matrix-core flop / F_path = {rec['mfma_flop_over_flops_path']:.4f}") + ".",
+                  f"stream.hip sha256[:16] at measurement: {sha}"]
+        db = json.load(open(args.counters)) if os.path.exists(args.counters) else {}
+        old = db.get(wl.name, {})
+        if old.get("stream_hip_sha256_16") == sha:   # merge passes of the same kernel
+            rec = {k: (v if v is not None else old.get(k)) for k, v in rec.items()}
+        db[wl.name] = rec
+        with open(args.counters, "w") as fh:
+            json.dump(db, fh, indent=1)
+    with open(md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return rec
+
+
+def counters_record(path, wl):
+    """This workload's counter record if it was taken on the current
+    stream.hip (else None: the kernel changed since)."""
+    import hashlib
+    try:
+        rec = json.load(open(path)).get(wl.name)
+        src = os.path.join(ROOT, "householder_position_encoding_amd", "csrc", "stream.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    return rec if rec is not None and rec.get("stream_hip_sha256_16") == sha else None
+
+
 def main():
     args = parse()
+    if args.pmc_report:
+        pmc_report(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -336,20 +565,19 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     stream_tflops = flops / (ms_stream * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic):
-        # HBM bytes per stream-kernel launch from rocprofv3 FETCH_SIZE/WRITE_SIZE,
-        # valid only for the kernel source they were measured on.
-        try:
-            import hashlib
-            tr = json.load(open(args.traffic)).get(wl.name)
-            src = os.path.join(ROOT, "householder_position_encoding_amd", "csrc", "stream.hip")
-            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-            if tr is not None and tr.get("stream_hip_sha256_16") == sha:
-                traffic = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
-
+    # per-launch figures of the stream kernel from rocprofv3 counters (valid
+    # only for the kernel source they were measured on)
+    crec = counters_record(args.counters, wl)
+    traffic = None if crec is None else crec.get("hbm_bytes_per_launch")
+    mfma_util = None
+    if crec is not None and crec.get("mfma_busy_frac") is not None:
+        mfma_util = {"kernel": stream_kernel_name(wl), "busy_frac": crec["mfma_busy_frac"],
+                     "busy_frac_at_peak_clock": crec.get("mfma_busy_frac_at_peak_clock"),
+                     "valu_coexec_frac": crec.get("mfma_valu_coexec_frac"),
+                     "executed_flop_per_launch": crec.get("mfma_flop_per_launch"),
+                     "executed_over_flops_path": crec.get("mfma_flop_over_flops_path"),
+                     "source": os.path.relpath(args.counters, ROOT) + " (rocprofv3 --pmc; "
+                               f"profiles/counters_{wl.name}.md)"}
     res = {
         "metric": "PaTH attn fwd tokens/s + TFLOP/s (% bf16 MFMA peak), B2 T16384 d64, 1 GPU",
         "value": wl.n_tokens / (ms * 1e-3),
@@ -377,6 +605,7 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": stream_tflops / peak,
                      "traffic": traffic,
                      "flops_per_launch": flops},
+        "mfma_util": mfma_util,
     }
     if fox_skip is not None:
         res["fox_skip"] = fox_skip
@@ -397,7 +626,9 @@ def main():
         torch.cuda.synchronize()
         res["backward"] = bench_backward(wl, q, k, v, w, beta, logf, out, lse, args)
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_heads)
+        step()
+        torch.cuda.synchronize()
+        res["cpu_baseline"], res["parity"] = cpu_baseline(wl, inp, args.cpu_heads, out, lse)
     print(json.dumps(res), flush=True)
 
 

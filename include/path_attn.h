@@ -278,14 +278,20 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
  * and "Backup: fix orientation before implementing UT products", keys of
  * earlier chunks aligned chunk by chunk as in frame "Decoding updates
  * historical keys in place", a downward sweep over query chunks, then the
- * per-chunk adjoint of the UT formulas).  Float32 arithmetic throughout.
+ * per-chunk adjoint of the UT formulas).  Precision: the per-chunk algebra
+ * (the triangular solve, the UT quantities and their adjoint) is float32;
+ * the quadratic products (logits, P.V, dP, dV, dQ, dK and the chunk
+ * transitions of the key levels and of the key gradients) take operands of
+ * the input dtype with float32 accumulation, so bf16 operands for
+ * PATH_ATTN_BF16, as the forward's; running values are float32.
  * ------------------------------------------------------------------------
  */
 
 /* Workspace bytes of path_attn_bwd, 0 for invalid or unsupported arguments.
- * It grows as B*H*d*T^2/64 elements of the input dtype (the aligned key
- * levels, stored in rows and transposed): about 27 GB at B=2, H=16, T=16384,
- * d=64 in bf16. */
+ * It grows as T^2: the aligned key levels take about B*H*d*T^2/128 elements
+ * of the input dtype (stored in rows, and at d = 128 or for float32 also
+ * transposed), next to linear per-chunk terms: 19.06 GiB at B=2, H=16,
+ * T=16384, d=64 in bf16, 26.44 GiB at B=4, H=8, T=8192, d=128 in bf16. */
 size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 
 /*

@@ -2,6 +2,9 @@
 HIP path through the C ABI binding, and call the oracle on the same values."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 import oracle
@@ -62,3 +65,26 @@ def sample_rows(T: int, rng, n_random=96):
     last = list(range(max(0, T - 64), T))
     rand = rng.choice(T, size=min(T, n_random), replace=False).tolist()
     return np.array(sorted(set(fixed + last + rand)), dtype=np.int64)
+
+
+def record(name: str, **values):
+    """Print measured errors of a case; with the environment variable
+    PATH_ATTN_ERROR_LOG set, also append them as one JSON line to that file
+    (the measured errors of a test run, kept beside its log)."""
+    msg = " ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}" for k, v in values.items())
+    print(f"{name}: {msg}", flush=True)
+    path = os.environ.get("PATH_ATTN_ERROR_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": name, **{k: (float(v) if isinstance(v, (float, np.floating)) else v)
+                                                 for k, v in values.items()}}) + "\n")
+
+
+def spread_heads(B: int, H: int):
+    """Heads (b, h) to compare at full size: eight spread over the flat head
+    index b*H + h, one in each residue class mod 8 when B*H >= 8 (the scan
+    places the blocks of head bh at block index group*B*H + bh), plus the
+    last head."""
+    BH = B * H
+    flat = sorted({(i * BH // 8 + i) % BH for i in range(8)} | {BH - 1})
+    return [(bh // H, bh % H) for bh in flat]
