@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     BF16,
     DecodeCache,
     F32,
+    NOALLOC_MAX_BYTES,
     NO_SKIP,
     PathAttnError,
     chunk_prep,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     path_attn_chunk_prep,
     path_attn_decode_step,
     path_attn_fwd,
+    path_attn_fwd_noalloc,
     path_attn_fwd_varlen,
     path_attn_prefill_cache,
     path_attn_prepare,
@@ -33,10 +35,10 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "BF16", "DecodeCache", "F32", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
+    "BF16", "DecodeCache", "F32", "NOALLOC_MAX_BYTES", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
     "load_library", "path_attn_bwd", "path_attn_bwd_varlen",
     "path_attn_bwd_varlen_workspace_bytes", "path_attn_bwd_workspace_bytes",
-    "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_varlen",
+    "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_noalloc", "path_attn_fwd_varlen",
     "path_attn_prefill_cache", "path_attn_prepare", "path_attn_stream",
     "path_attn_varlen_workspace_bytes", "path_attn_workspace_bytes", "strerror", "version",
 ]

@@ -53,6 +53,9 @@ def load_library():
     lib.path_attn_fwd_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci,
                                      ci, ctypes.c_float, ctypes.c_uint, vp, sz, vp]
     lib.path_attn_fwd_ex.restype = ci
+    lib.path_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci, ci,
+                                          ctypes.c_float, ctypes.c_uint, vp]
+    lib.path_attn_fwd_noalloc.restype = ci
     lib.path_attn_chunk_prep.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, fp,
                                          fp, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.path_attn_chunk_prep.restype = ci
@@ -196,6 +199,36 @@ def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
                               _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if st != 0:
         raise PathAttnError(st, "path_attn_fwd_ex")
+    return out, lse
+
+
+NOALLOC_MAX_BYTES = 64 << 20   # PATH_ATTN_NOALLOC_MAX_BYTES of the header
+
+
+def path_attn_fwd_noalloc(q, k, v, w, beta, logf=None, out=None, lse=None, stream=None,
+                          scale=None, flags=0):
+    """path_attn_fwd_noalloc: the forward with the library's fixed device
+    array as its workspace (no workspace argument, nothing allocated by the
+    call; problems up to NOALLOC_MAX_BYTES of workspace).  out and lse are
+    allocated here when not given; pass them to allocate nothing.  Calls on
+    one GPU share the array and must not overlap."""
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", (B, H, T), torch.float32, q.device)
+    st = lib.path_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                                   _ptr(out), _ptr(lse), B, H, T, d, dt,
+                                   0.0 if scale is None else float(scale), int(flags),
+                                   _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_fwd_noalloc")
     return out, lse
 
 

@@ -2,6 +2,9 @@
 //
 // Host side only: argument validation (before any HIP call), workspace
 // carving, and the in-order launches on the caller's stream.
+#include <atomic>
+#include <mutex>
+
 #include "path_attn.h"
 #include "path_attn_internal.h"
 
@@ -235,6 +238,78 @@ extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
                              void *stream) {
   return path_attn_fwd_ex(q, k, v, w, beta, logf, out, lse, B, H, T, d, dtype, 0.f, 0u,
                           workspace, workspace_bytes, stream);
+}
+
+// ---- the forward without a caller workspace ----------------------------------
+//
+// Its workspace is `scratch`, a fixed array in the library's device memory.
+// In host code the name `scratch` stands for a host-side shadow, not a device
+// address; the device address of each GPU's copy is looked up once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.  No
+// part of the forward's workspace has to start at zero (every region a call
+// reads is written earlier in the same call, padded staging rows included), so
+// nothing is cleared between calls.
+
+namespace {
+
+__device__ __align__(256) unsigned char scratch[PATH_ATTN_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on `dev` (looked up on first use, with that
+// device current, and kept for the life of the process).
+int scratch_address(int dev, void **addr) {
+  if (dev < 0 || dev >= kMaxDevices) return PATH_ATTN_EUNSUPPORTED;
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return PATH_ATTN_EHIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return PATH_ATTN_EHIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return PATH_ATTN_EHIP;
+      if (e != hipSuccess || !p) return PATH_ATTN_EHIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return PATH_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int path_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                     const void *w, const float *beta, const float *logf,
+                                     void *out, float *lse, int B, int H, int T, int d,
+                                     int dtype, float scale, unsigned flags, void *stream) {
+  // argument checks first, before any HIP call
+  int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (full_layout(B, H, T, d, dtype).total > (size_t)PATH_ATTN_NOALLOC_MAX_BYTES)
+    return PATH_ATTN_EINVAL;
+  if (!q || !k || !v || !w || !beta || !out || !lse) return PATH_ATTN_EINVAL;
+  const void *ptrs[] = {q, k, v, w, beta, out, lse};
+  for (const void *p : ptrs)
+    if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
+  if (logf && !aligned(logf, 16)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return PATH_ATTN_EHIP;
+  void *ws_addr = nullptr;
+  st = scratch_address(dev, &ws_addr);
+  if (st != PATH_ATTN_OK) return st;
+  const Carved ws = carve(ws_addr, B, H, T, d, dtype);
+  const FwdViews views = dense_fwd_views(H, T, d);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
+  if (st != PATH_ATTN_OK) return st;
+  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, B, H, T, d, dtype, scale,
+                    views, s);
 }
 
 namespace {

@@ -40,9 +40,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous: they enqueue kernels and return; results are valid once
  *     the caller has synchronised the stream.  The library keeps no pointer
- *     after a call returns, holds no global state and allocates no memory:
- *     all scratch space is the caller's `workspace`.  Concurrent calls on
- *     different streams must use different workspaces.
+ *     after a call returns and allocates no memory: all scratch space is the
+ *     caller's `workspace` (path_attn_fwd_noalloc alone uses a fixed array of
+ *     the library instead).  Concurrent calls on different streams must use
+ *     different workspaces.
  *   - Pointers must be 16-byte aligned, the workspace 256-byte aligned.
  *   - Errors: argument checks run before any HIP call; on failure nothing is
  *     launched and a status below is returned.  Numerical contents are not
@@ -120,6 +121,28 @@ int path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w,
                      int B, int H, int T, int d, int dtype, float scale,
                      unsigned flags, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * path_attn_fwd_ex without a caller workspace.  The workspace is a fixed
+ * array of PATH_ATTN_NOALLOC_MAX_BYTES in the library's device memory: each
+ * GPU the library's code is loaded on (its first use there, by any entry
+ * point) holds one copy until the process ends; the call allocates nothing.
+ * A problem whose workspace (path_attn_workspace_bytes) exceeds that size is
+ * EINVAL: 64 MiB holds about 80,000 token-heads (B*H*T) at d = 64 and about
+ * 38,000 at d = 128 in bf16.  The GPU is the stream's (the current device for
+ * a NULL stream); the array's address there is looked up once per device on
+ * the first call (EHIP if that lookup fails).  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (concurrent streams or host
+ * threads) race and give wrong results, so the caller must order them.
+ * Other arguments, results and errors as for path_attn_fwd_ex.
+ */
+#define PATH_ATTN_NOALLOC_MAX_BYTES (64u << 20)
+int path_attn_fwd_noalloc(const void *q, const void *k, const void *v, const void *w,
+                          const float *beta, const float *logf, void *out, float *lse,
+                          int B, int H, int T, int d, int dtype, float scale,
+                          unsigned flags, void *stream);
 
 /*
  * The two phases of path_attn_fwd, for callers that time or schedule them

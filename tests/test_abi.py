@@ -405,3 +405,27 @@ def test_varlen_binding_needs_gpu_tensors():
         pa.path_attn_fwd_varlen(x, x, x, x, torch.zeros(1, 2, 64))
     with pytest.raises(ValueError, match="GPU"):
         pa.path_attn_bwd_varlen(x, x, x, x, torch.zeros(1, 2, 64), None, x, None, x)
+
+
+@pytest.mark.parametrize("B,H,T,d,dtype,null_q,scale,flags,status", [
+    (1, 16, 8192, 64, pa.BF16, False, 0.0, 0, EINVAL),   # workspace above the fixed array
+    (1, 8, 8192, 128, pa.BF16, False, 0.0, 0, EINVAL),
+    (1, 2, 256, 64, pa.BF16, True, 0.0, 0, EINVAL),      # null q
+    (1, 2, 256, 64, pa.BF16, False, -1.0, 0, EINVAL),    # bad scale
+    (1, 2, 256, 64, pa.BF16, False, 0.0, 4, EINVAL),     # unknown flag
+    (1, 2, 256, 96, pa.BF16, False, 0.0, 0, EUNSUP),
+])
+def test_noalloc_validation(B, H, T, d, dtype, null_q, scale, flags, status):
+    """path_attn_fwd_noalloc checks its arguments, the problem size against
+    the fixed array included, before any HIP call."""
+    assert pa.path_attn_workspace_bytes(1, 16, 4096, 64, pa.BF16) <= pa.NOALLOC_MAX_BYTES
+    lib = pa.load_library()
+    q = None if null_q else FAKE
+    assert lib.path_attn_fwd_noalloc(q, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, B, H, T, d,
+                                     dtype, scale, flags, None) == status
+
+
+def test_noalloc_max_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PATH_ATTN_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_MAX_BYTES
