@@ -16,7 +16,10 @@ seeded).  value = tokens/s = B*T / (time per step).  The roofline object is
 for the dominant kernel, the streaming scan: its algorithmic flops
 B*H*T^2*(2d + d^2/64) divided by its own average duration, timed with HIP
 events over K launches of path_attn_stream alone on the same stream, against
-the bf16 dense matrix-core peak of 2.5 PFLOP/s.  cpu_baseline times the fp64
+the bf16 dense matrix-core peak of 2.5 PFLOP/s (with the forget gate, the scan
+with every key block computed, PATH_ATTN_NO_SKIP, so that the rate counts
+executed work; the exact skip's effective rate is reported in fox_skip).
+cpu_baseline times the fp64
 CPU oracle on a bounded sample (N whole heads) with all host threads and
 scales the rate to the full workload.  The decode object times decoding
 with in-place key refinement after the workload's prompt (prefill alignment of
@@ -70,6 +73,11 @@ def parse():
                     help="do not run: summarise the rocprofv3 --pmc output directories given "
                          "(run_counter_collection.csv below each) per kernel, write the "
                          "markdown summary (--pmc-md) and this workload's record in --counters")
+    ap.add_argument("--trace-report", metavar="DIR", default=None,
+                    help="do not run: summarise a rocprofv3 --kernel-trace --stats output "
+                         "directory (run_kernel_stats.csv) into --pmc-md (default "
+                         "profiles/kernel_trace_<workload>.md), with the stream kernel's "
+                         "F_path rate at its average duration")
     ap.add_argument("--pmc-md", default=None,
                     help="markdown file of --pmc-report (default profiles/counters_<workload>.md)")
     ap.add_argument("--pmc-command", action="append", default=[],
@@ -470,6 +478,47 @@ def pmc_report(args):
     return rec
 
 
+def trace_report(args):
+    """--trace-report: per-kernel durations from rocprofv3 --stats (markdown)."""
+    import csv
+    import glob
+    import workloads
+    wl = workloads.BY_NAME[args.workload]
+    files = glob.glob(os.path.join(args.trace_report, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv below {args.trace_report}")
+    rows = list(csv.DictReader(open(files[0])))
+    flops = wl.flops_path()
+    want = stream_kernel_name(wl).split("<")[0]
+    md = (os.path.join(ROOT, "profiles", f"kernel_trace_{wl.name}.md") if args.pmc_md is None
+          else args.pmc_md)
+    lines = [f"# Kernel trace: {wl.name} (B={wl.B} H={wl.H} T={wl.T} d={wl.d}, {wl.dtype}"
+             f"{', gate' if wl.fox else ''})", "",
+             "Made by `python bench.py --trace-report <dir> --workload " + wl.name +
+             "` from this rocprofv3 run (after `cd /tmp && export TMPDIR=/tmp`):", ""]
+    lines += [f"    {c}" for c in args.pmc_command] + [""]
+    lines += ["| kernel | calls | average us | min us | max us | share of GPU time |",
+              "|---|---|---|---|---|---|"]
+    stream = None
+    for r in rows:
+        name = _short_kernel_name(r["Name"])
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} % |")
+        if stream is None and want in r["Name"] and ("Lb1E" in r["Name"]) == wl.fox:
+            stream = r
+    if stream is not None:
+        avg, mn = float(stream["AverageNs"]) * 1e-9, float(stream["MinNs"]) * 1e-9
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+        lines += ["", f"Stream kernel `{_short_kernel_name(stream['Name'])}`: F_path = "
+                  f"{flops:.4g} flop per launch; at the average duration {avg * 1e3:.4f} ms that "
+                  f"is {flops / avg / 1e12:.0f} TFLOP/s = {flops / avg / 1e12 / peak:.3f} of the "
+                  f"{peak:.0f} TFLOP/s peak (at the minimum, {flops / mn / 1e12 / peak:.3f})."]
+    with open(md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def counters_record(path, wl):
     """This workload's counter record if it was taken on the current
     stream.hip (else None: the kernel changed since)."""
@@ -487,6 +536,9 @@ def main():
     args = parse()
     if args.pmc_report:
         pmc_report(args)
+        return
+    if args.trace_report:
+        trace_report(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -564,7 +616,13 @@ def main():
     flops = wl.flops_path()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-    stream_tflops = flops / (ms_stream * 1e-3) / 1e12
+    # with the gate the roofline takes the scan with every block computed
+    # (the work F_path counts); the skip's effective rate is in fox_skip
+    ms_roof = ms_stream if fox_skip is None else fox_skip["ms_stream_no_skip"]
+    stream_tflops = flops / (ms_roof * 1e-3) / 1e12
+    if fox_skip is not None:
+        fox_skip["effective_tflops_path"] = flops / (ms_stream * 1e-3) / 1e12
+        fox_skip["effective_frac"] = fox_skip["effective_tflops_path"] / peak
     # per-launch figures of the stream kernel from rocprofv3 counters (valid
     # only for the kernel source they were measured on)
     crec = counters_record(args.counters, wl)
@@ -601,7 +659,9 @@ def main():
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "ms_prep": ms_prep,
         "ms_stream": ms_stream,
-        "roofline": {"kernel": stream_kernel_name(wl), "bound": "mfma", "achieved": stream_tflops,
+        "roofline": {"kernel": stream_kernel_name(wl) + ("" if fox_skip is None else
+                                                           ", every block computed"),
+                     "bound": "mfma", "achieved": stream_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": stream_tflops / peak,
                      "traffic": traffic,
                      "flops_per_launch": flops},
