@@ -328,9 +328,7 @@ class DecodeCache:
         self.vcache = torch.zeros((B, H, T_cap, d), dtype=dtype, device=device)
         self.gcache = torch.zeros((B, H, T_cap), dtype=torch.float64, device=device) if fox else None
         need = load_library().path_attn_decode_workspace_bytes(B, H, T_cap, d)
-        # zero-filled once: it holds the per-head arrival counters of the
-        # decode step, which the library leaves at zero after every step
-        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
         self.length = 0
 
 

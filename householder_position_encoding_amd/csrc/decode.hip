@@ -345,18 +345,15 @@ constexpr int kUnroll = 4;
 template <int D>
 __host__ __device__ constexpr int partial_floats() { return D + 2; }
 
-// Decode workspace: the partials of up to ceil(T_cap / 512) splits per head,
-// then (256-byte aligned) one 32-bit arrival counter per head.
-inline size_t decode_counter_offset(int BH, int T_cap, int D) {
+// Decode workspace: the partials of up to ceil(T_cap / 512) splits per head.
+inline size_t decode_partials_size(int BH, int T_cap, int D) {
   const size_t nsplit = ((size_t)T_cap + kKeysPerSplit - 1) / kKeysPerSplit;
-  return align256((size_t)BH * (nsplit > 0 ? nsplit : 1) * (D + 2) * sizeof(float));
-}
-inline unsigned *decode_counters(float *part, int BH, int T_cap, int D) {
-  return reinterpret_cast<unsigned *>(reinterpret_cast<char *>(part) +
-                                      decode_counter_offset(BH, T_cap, D));
+  return (size_t)BH * (nsplit > 0 ? nsplit : 1) * (D + 2) * sizeof(float);
 }
 
-// The merge, run by the last split block of a head to finish (256 threads):
+// The merge, one block of 256 threads per head in a kernel of its own after
+// the split kernel (the kernel boundary orders the partials' stores before
+// the merge's loads):
 // the split partials and the new key k_t (logit scale * q_t . k_t, no gate
 // term) give o_t and lse_t; k_t, v_t and Lambda_t are appended to the caches.  The merge is an online softmax over
 // batches of up to 64 splits: each batch's partials are copied into LDS in
@@ -364,14 +361,6 @@ inline unsigned *decode_counters(float *part, int BH, int T_cap, int D) {
 // the running (M, l, o) is rescaled once per batch.  It starts from the new
 // key itself: M = x_new, l = 1, o = v_t.
 constexpr int kMergeBatch = 64;   // splits per merge batch
-
-// Device-coherent store / load of a split partial (agent scope, relaxed).
-__device__ __forceinline__ void st_coherent(float *p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int D>
 struct MergeLds {
@@ -399,7 +388,7 @@ __device__ __forceinline__ void merge_head(
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int i = tid + r * NT;
-    pre[r] = i < ns0 * PF ? ld_coherent(ph + i) : 0.f;
+    pre[r] = i < ns0 * PF ? ph[i] : 0.f;
   }
   const float vt = tid < D ? to_f(v[(size_t)bh * D + tid]) : 0.f;
   const float kt = tid < D ? to_f(k[(size_t)bh * D + tid]) : 0.f;
@@ -428,7 +417,7 @@ __device__ __forceinline__ void merge_head(
     const int ns = min(SB, nsplit - s0);
     if (s0 > 0) {
       __syncthreads();   // the previous batch is consumed
-      for (int i = tid; i < ns * PF; i += NT) sp[i] = ld_coherent(ph + (size_t)s0 * PF + i);
+      for (int i = tid; i < ns * PF; i += NT) sp[i] = ph[(size_t)s0 * PF + i];
       __syncthreads();
     }
     if (wave == 0) {
@@ -474,18 +463,6 @@ __device__ __forceinline__ void merge_head(
   }
 }
 
-// Arrival count of a head's split blocks in one decode step (a split-K
-// semaphore): each block adds 1 once it has stored its partial; the block that
-// draws ticket nsplit - 1 is the last, merges, and resets the count to 0, so
-// the counter is 0 between steps (the workspace is zero-filled before the
-// first step).  A single atomic add per block: nothing waits or retries.
-__device__ __forceinline__ bool arrive_last(unsigned *c, int nsplit) {
-  const unsigned ticket = atomicAdd(c, 1u);
-  const bool last = ticket == (unsigned)nsplit - 1u;
-  if (last) atomicExch(c, 0u);
-  return last;
-}
-
 // One block of 256 threads per (split, bh): keys [split*KPS, min(t, +KPS))
 // (an empty range when t == 0: the step then has one block with no keys).
 // A key row is spread over LPK lanes with EPL consecutive elements each
@@ -494,9 +471,8 @@ template <typename E, typename KC, int D, bool FOX>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ w, const float *__restrict__ beta, const float *__restrict__ logf,
-    KC *__restrict__ kcache, E *__restrict__ vcache, double *__restrict__ gcache, float *part,
-    unsigned *__restrict__ cnt, E *__restrict__ out, float *__restrict__ lse, int t,
-    int T_cap, int nsplit, float sl2) {
+    KC *__restrict__ kcache, E *__restrict__ vcache, double *__restrict__ gcache,
+    float *__restrict__ part, int t, int T_cap, int nsplit, float sl2) {
   constexpr int EPL = Vec16<KC>::n;
   constexpr int LPK = D / EPL;
   constexpr int KPW = 64 / LPK;
@@ -505,8 +481,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int PF = partial_floats<D>();
   __shared__ float red_m[NW * KPW], red_l[NW * KPW];
   __shared__ float red_o[NW * KPW][D];
-  __shared__ MergeLds<D> msm;
-  __shared__ int last;
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -612,24 +586,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         o = __builtin_fmaf(f, red_o[s][threadIdx.x], o);
       }
     }
-    st_coherent(dst + 2 + threadIdx.x, o);
+    dst[2 + threadIdx.x] = o;
     if (threadIdx.x == 0) {
-      st_coherent(dst, M);
-      st_coherent(dst + 1, l);
+      dst[0] = M;
+      dst[1] = l;
     }
   }
-  // the last block of this head to finish merges every split.  The partials
-  // are the only data passed between blocks: they are written and read with
-  // device-coherent (agent-scope) accesses, which go past the per-XCD L2, and
-  // every store of the block has completed (vmcnt 0 in each wave, then the
-  // barrier) before the block is counted; no whole-cache fence is needed.
-  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): this wave's stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) last = arrive_last(cnt + bh, nsplit);
-  __syncthreads();
-  if (!last) return;
-  merge_head<E, KC, D, FOX>(msm, bh, q, k, v, logf, kcache, vcache, gcache, part, out, lse, t,
-                            T_cap, nsplit, sl2);
+}
+
+// The merge of one head's split partials (see merge_head).
+template <typename E, typename KC, int D, bool FOX>
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ logf, KC *__restrict__ kcache, E *__restrict__ vcache,
+    double *__restrict__ gcache, const float *__restrict__ part, E *__restrict__ out,
+    float *__restrict__ lse, int t, int T_cap, int nsplit, float sl2) {
+  __shared__ MergeLds<D> msm;
+  merge_head<E, KC, D, FOX>(msm, (int)blockIdx.x, q, k, v, logf, kcache, vcache, gcache, part,
+                            out, lse, t, T_cap, nsplit, sl2);
 }
 
 template <typename E, typename KC, int D>
@@ -657,11 +631,12 @@ hipError_t decode_t(const void *q, const void *k, const void *v, const void *w,
                     double *gcache, void *out, float *lse, float *part, int BH, int t,
                     int T_cap, float sl2, hipStream_t stream) {
   const int nsplit = t > 0 ? (t + kKeysPerSplit - 1) / kKeysPerSplit : 1;
-  unsigned *cnt = decode_counters(part, BH, T_cap, D);
   hipLaunchKernelGGL((decode_split_kernel<E, KC, D, FOX>), dim3(nsplit, BH), dim3(256), 0, stream,
                      (const E *)q, (const E *)k, (const E *)v, (const E *)w, beta, logf,
-                     (KC *)kcache, (E *)vcache, gcache, part, cnt, (E *)out, lse, t, T_cap, nsplit,
-                     sl2);
+                     (KC *)kcache, (E *)vcache, gcache, part, t, T_cap, nsplit, sl2);
+  hipLaunchKernelGGL((decode_merge_kernel<E, KC, D, FOX>), dim3(BH), dim3(256), 0, stream,
+                     (const E *)q, (const E *)k, (const E *)v, logf, (KC *)kcache, (E *)vcache,
+                     gcache, (const float *)part, (E *)out, lse, t, T_cap, nsplit, sl2);
   return hipGetLastError();
 }
 
@@ -698,7 +673,7 @@ hipError_t decode_d(int D, const void *q, const void *k, const void *v, const vo
 }  // namespace
 
 size_t decode_partial_bytes(int BH, int T_cap, int D) {
-  return decode_counter_offset(BH, T_cap, D) + (size_t)BH * sizeof(unsigned);
+  return decode_partials_size(BH, T_cap, D);
 }
 
 hipError_t launch_prefill_cache(int dtype, int kc_dtype, int D, const void *k, const void *v,

@@ -260,12 +260,11 @@ int path_attn_prefill_cache(const void *k, const void *v, const void *w,
                             int kc_dtype, void *workspace,
                             size_t workspace_bytes, void *stream);
 
-/* Workspace bytes of path_attn_decode_step (partial softmax states and one
- * arrival counter per head), 0 for invalid arguments.  The workspace must be
- * zero-filled before its first decode step; every step leaves its counters at
- * zero again, so the same workspace serves all later steps (of any cache of
- * at most B*H heads and T_cap positions) without refilling.  Steps that share
- * a workspace must not run concurrently. */
+/* Workspace bytes of path_attn_decode_step (the partial softmax states of
+ * the key splits of every head), 0 for invalid arguments.  The workspace needs
+ * no initialisation and serves all steps of any cache of at most B*H heads
+ * and T_cap positions.  Steps that share a workspace must not run
+ * concurrently. */
 size_t path_attn_decode_workspace_bytes(int B, int H, int T_cap, int d);
 
 /*
@@ -278,9 +277,10 @@ size_t path_attn_decode_workspace_bytes(int B, int H, int T_cap, int d);
  *     lse[b,h]   = ln sum_{j<=t} exp(s_tj)                (float32)
  * with s_tj = scale * (k_j . q_t) + Lambda_t - Lambda_j (gate term only
  * with logf; scale as for path_attn_fwd_ex, 0 selects 1/sqrt(d)).  q, k, v, w, out: [B, H, d] of dtype; beta, logf, lse: [B, H]
- * float32.  Keys are split over blocks (512 per block, one block when t = 0);
- * the last block of a head to finish (counted in the workspace) merges the
- * partial softmax states, so a step is a single kernel.  Alignment: q, k, v, w, out and
+ * float32.  Keys are split over blocks (512 per block, one block when t = 0),
+ * each writing a partial softmax state into the workspace; a second kernel,
+ * one block per head, merges them (ordered after the first by the stream).
+ * Alignment: q, k, v, w, out and
  * the caches 16 bytes; beta, logf and lse 4 bytes (one value per head).
  * Errors as for path_attn_prefill_cache; t outside [0, T_cap) is EINVAL.
  */

@@ -194,18 +194,29 @@ def test_decode_full_context_sampled():
     assert eo <= tol_o and el <= tol_l and ek <= 1e-3
 
 
-def test_decode_counters_back_to_zero():
-    """The decode workspace carries one arrival counter per head after the
-    split partials (256-byte aligned); every step must leave them at zero,
-    so later steps (and other caches using the same workspace) start clean."""
+def test_decode_workspace_needs_no_initialisation():
+    """The decode workspace holds only the split partials, written by every
+    step before the merge reads them: a workspace filled with garbage (NaN
+    bytes) before the first step gives the same outputs as a zeroed one, and
+    they match the oracle's rows."""
     import torch
     dtype, d, B, H, L, n_dec, T_cap = "bf16", 64, 2, 3, 64, 5, 1100
     inp = workloads.small(dtype, B, H, L + n_dec, d, seed=5)
-    outs, lses, cache = _run(inp, dtype, "f32", L, n_dec, T_cap)
-    assert np.all(np.isfinite(outs)) and np.all(np.isfinite(lses))
-    nsplit_cap = (T_cap + 511) // 512
-    part_bytes = B * H * nsplit_cap * (d + 2) * 4
-    off = (part_bytes + 255) // 256 * 256
-    counters = cache.workspace[off:off + 4 * B * H]
-    assert counters.numel() == 4 * B * H
-    assert int(torch.count_nonzero(counters)) == 0
+    import householder_position_encoding_amd as pa
+    orig = pa.DecodeCache.__init__
+
+    def garbage_init(self, *a, **kw):
+        orig(self, *a, **kw)
+        self.workspace.fill_(0xFF)
+    pa.DecodeCache.__init__ = garbage_init
+    try:
+        outs, lses, _ = _run(inp, dtype, "f32", L, n_dec, T_cap)
+    finally:
+        pa.DecodeCache.__init__ = orig
+    outs0, lses0, _ = _run(inp, dtype, "f32", L, n_dec, T_cap)
+    assert np.array_equal(outs, outs0) and np.array_equal(lses, lses0)
+    for b in range(B):
+        for h in range(H):
+            o_ref, l_ref = _oracle_rows(inp, b, h, list(range(L, L + n_dec)))
+            assert np.max(np.abs(outs[:, b, h] - o_ref)) <= TOL["bf16"][0]
+            assert np.max(np.abs(lses[:, b, h] - l_ref)) <= TOL["bf16"][1]
