@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu] [--cpu-heads N] [--traffic FILE]
                     [--no-decode] [--decode-steps N] [--no-backward] [--backward-steps N]
+                    [--no-partial] [--no-varlen]
 
 One step = one call of path_attn_fwd (gate prefix when present, chunk
 preparation and the streaming scan) over the whole workload, inputs already
@@ -62,6 +63,8 @@ def parse():
                     help="timed decode steps after the prompt (decoding measurement)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-partial", action="store_true",
+                    help="skip the partial-PaTH (d_path = d / 2) measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the strided / packed forward measurement")
     ap.add_argument("--cpu-heads", type=int, default=8,
@@ -233,6 +236,27 @@ def bench_backward(wl, q, k, v, w, beta, logf, out, lse, args):
     del ws
     torch.cuda.empty_cache()
     return res
+
+
+def bench_partial(wl, q, k, v, w, beta, logf, args, timed, ms_full):
+    """Partial PaTH (path_attn_fwd_partial) with the factors on the leading
+    d / 2 coordinates, on the same inputs and workspace size: the time of the
+    whole call against the full forward's step.  Its algorithmic flops are
+    B*H*T^2*(2d + (d/2)^2/64): the transition product shrinks to (d/2)^2."""
+    import torch
+    import householder_position_encoding_amd as pa
+    dp = wl.d // 2
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=q.device)
+    dt_code = pa.BF16 if wl.dtype == "bf16" else pa.F32
+    ws = torch.empty(pa.path_attn_workspace_bytes(wl.B, wl.H, wl.T, wl.d, dt_code),
+                     dtype=torch.uint8, device=q.device)
+    ms = timed(lambda: pa.path_attn_fwd_partial(q, k, v, w, beta, logf, d_path=dp, out=out,
+                                                lse=lse, workspace=ws), args.steps)
+    flops = float(wl.B * wl.H) * wl.T * wl.T * (2 * wl.d + dp * dp / 64.0)
+    return {"d_path": dp, "ms": ms, "ms_full_path": ms_full, "speedup": ms_full / ms,
+            "tokens_per_s": wl.n_tokens / (ms * 1e-3),
+            "tflops_path_partial": flops / (ms * 1e-3) / 1e12}
 
 
 def bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms_dense):
@@ -676,6 +700,9 @@ def main():
         ms_copy = timed(lambda: dst.copy_(src), 5)
         res["copy_calibration"] = {"bytes_read": nbytes, "bytes_written": nbytes,
                                    "ms": ms_copy, "gbs": 2 * nbytes / (ms_copy * 1e-3) / 1e9}
+    if not args.no_partial:
+        res["partial"] = bench_partial(wl, q, k, v, w, beta, logf, args, timed, ms)
+        torch.cuda.empty_cache()
     if not args.no_varlen:
         res["varlen"] = bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms)
         torch.cuda.empty_cache()

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     path_attn_decode_step,
     path_attn_fwd,
     path_attn_fwd_noalloc,
+    path_attn_fwd_partial,
     path_attn_fwd_varlen,
     path_attn_prefill_cache,
     path_attn_prepare,
@@ -38,7 +39,8 @@ __all__ = [
     "BF16", "DecodeCache", "F32", "NOALLOC_MAX_BYTES", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
     "load_library", "path_attn_bwd", "path_attn_bwd_varlen",
     "path_attn_bwd_varlen_workspace_bytes", "path_attn_bwd_workspace_bytes",
-    "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_noalloc", "path_attn_fwd_varlen",
+    "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_noalloc", "path_attn_fwd_partial",
+    "path_attn_fwd_varlen",
     "path_attn_prefill_cache", "path_attn_prepare", "path_attn_stream",
     "path_attn_varlen_workspace_bytes", "path_attn_workspace_bytes", "strerror", "version",
 ]

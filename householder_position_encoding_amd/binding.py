@@ -56,6 +56,9 @@ def load_library():
     lib.path_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci, ci,
                                           ctypes.c_float, ctypes.c_uint, vp]
     lib.path_attn_fwd_noalloc.restype = ci
+    lib.path_attn_fwd_partial.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, ci, ci, ci, ci, ci, ci,
+                                          ctypes.c_float, ctypes.c_uint, vp, sz, vp]
+    lib.path_attn_fwd_partial.restype = ci
     lib.path_attn_chunk_prep.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp, fp,
                                          fp, ci, ci, ci, ci, ci, vp, sz, vp]
     lib.path_attn_chunk_prep.restype = ci
@@ -199,6 +202,35 @@ def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
                               _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if st != 0:
         raise PathAttnError(st, "path_attn_fwd_ex")
+    return out, lse
+
+
+def path_attn_fwd_partial(q, k, v, w, beta, logf=None, d_path=None, out=None, lse=None,
+                          workspace=None, stream=None, scale=None, flags=0):
+    """Partial PaTH (path_attn_fwd_partial): the factors act on the leading
+    d_path coordinates only (w is not read beyond them); d_path is d or d // 2
+    (None: d // 2).  Other arguments as path_attn_fwd."""
+    torch = _torch()
+    B, H, T, d, dt = _common(q, k, v, w, beta, logf)
+    lib = load_library()
+    d_path = d // 2 if d_path is None else int(d_path)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", (B, H, T), torch.float32, q.device)
+    need = lib.path_attn_workspace_bytes(B, H, T, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.path_attn_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                                   _ptr(out), _ptr(lse), B, H, T, d, d_path, dt,
+                                   0.0 if scale is None else float(scale), int(flags),
+                                   _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_fwd_partial")
     return out, lse
 
 

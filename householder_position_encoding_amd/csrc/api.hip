@@ -40,11 +40,13 @@ struct FullLayout {
   size_t q, k, v, w, beta, logf, out, lse, total;
 };
 
-FullLayout full_layout(int B, int H, int T, int d, int dtype, bool views = false) {
+// dp: the coordinates the factors act on (d, or d / 2 for partial PaTH); the
+// layout with dp = d is the largest.
+FullLayout full_layout(int B, int H, int T, int d, int dtype, bool views = false, int dp = 0) {
   const int Tp = padded(T);
   const size_t e = elem_size(dtype);
   FullLayout F{};
-  F.base = make_layout(B, H, Tp, d, e);
+  F.base = make_layout(B, H, Tp, d, e, dp > 0 ? dp : d);
   F.staged = views || Tp != T;
   size_t off = F.base.total;
   if (F.staged) {
@@ -109,15 +111,17 @@ struct Carved {
   float2 *bnd;
   char *base;
   FullLayout F;
+  int dp;
 };
 
-Carved carve(void *workspace, int B, int H, int T, int d, int dtype, bool views = false) {
-  const FullLayout F = full_layout(B, H, T, d, dtype, views);
+Carved carve(void *workspace, int B, int H, int T, int d, int dtype, bool views = false,
+             int dp = 0) {
+  const FullLayout F = full_layout(B, H, T, d, dtype, views, dp);
   char *base = static_cast<char *>(workspace);
   return Carved{reinterpret_cast<float *>(base + F.base.qa), base + F.base.kvm,
                 reinterpret_cast<float *>(base + F.base.al),
                 reinterpret_cast<float *>(base + F.base.gate),
-                reinterpret_cast<float2 *>(base + F.base.bnd), base, F};
+                reinterpret_cast<float2 *>(base + F.base.bnd), base, F, dp > 0 ? dp : d};
 }
 
 // The streaming scan at the padded length; with staging into the staging
@@ -144,7 +148,7 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
   a.H = H;
   a.so = in_place ? tok_strides(views.v[4]) : dense_strides(H, Tp, d);
   a.sl = in_place ? tok_strides(views.v[7]) : dense_strides(H, Tp, 1);
-  if (launch_stream(dtype, d, gate, a, s) != hipSuccess) return PATH_ATTN_EHIP;
+  if (launch_stream(dtype, d, ws.dp, gate, a, s) != hipSuccess) return PATH_ATTN_EHIP;
   if (staged) {
     const int e = (int)elem_size(dtype);
     if (launch_view_rows(false, a.out, out, views.v[4], B, H, T, Tp, e, d * e, s) != hipSuccess ||
@@ -196,10 +200,11 @@ int run_prep(const void *q, const void *k, const void *v, const void *w,
   }
   if (logf && launch_gate_prefix(logf, ws.gate, BH, Tp, io, s) != hipSuccess)
     return PATH_ATTN_EHIP;
-  if (launch_prep(dtype, d, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, io, s) !=
+  if (launch_prep(dtype, d, ws.dp, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, io, s) !=
       hipSuccess)
     return PATH_ATTN_EHIP;
-  if (logf && launch_chunk_bounds(dtype, d, ws.kvm, ws.gate, ws.bnd, BH, Tp, s) != hipSuccess)
+  if (logf &&
+      launch_chunk_bounds(dtype, d, ws.dp, ws.kvm, ws.gate, ws.bnd, BH, Tp, s) != hipSuccess)
     return PATH_ATTN_EHIP;
   return PATH_ATTN_OK;
 }
@@ -238,6 +243,33 @@ extern "C" int path_attn_fwd(const void *q, const void *k, const void *v,
                              void *stream) {
   return path_attn_fwd_ex(q, k, v, w, beta, logf, out, lse, B, H, T, d, dtype, 0.f, 0u,
                           workspace, workspace_bytes, stream);
+}
+
+extern "C" int path_attn_fwd_partial(const void *q, const void *k, const void *v,
+                                     const void *w, const float *beta, const float *logf,
+                                     void *out, float *lse, int B, int H, int T, int d,
+                                     int d_path, int dtype, float scale, unsigned flags,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(B, H, T, d, dtype);
+  if (st != PATH_ATTN_OK) return st;
+  if (d_path <= 0 || d_path > d) return PATH_ATTN_EINVAL;
+  if (d_path != d && 2 * d_path != d) return PATH_ATTN_EUNSUPPORTED;
+  if (!q || !k || !v || !w || !beta || !out || !lse || !workspace) return PATH_ATTN_EINVAL;
+  const void *ptrs[] = {q, k, v, w, beta, out, lse};
+  for (const void *p : ptrs)
+    if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
+  if (logf && !aligned(logf, 16)) return PATH_ATTN_EINVAL;
+  if (!aligned(workspace, 256) ||
+      workspace_bytes < full_layout(B, H, T, d, dtype, false, d_path).total)
+    return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carved ws = carve(workspace, B, H, T, d, dtype, false, d_path);
+  const FwdViews views = dense_fwd_views(H, T, d);
+  st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
+  if (st != PATH_ATTN_OK) return st;
+  return run_stream(ws, logf != nullptr, flags, nullptr, out, lse, B, H, T, d, dtype, scale,
+                    views, s);
 }
 
 // ---- the forward without a caller workspace ----------------------------------

@@ -27,10 +27,12 @@
 //   qa   float [BH][N][2][D/32][64][16]   boundary-adjusted queries <-Q
 //        (row i: H_first...H_i q_i) as register image: [query block w]
 //        [d block mb][lane][r] = <-Q[32w + lane%32][32mb + acc_row(r, lane/32)]
-//   kvm  elem  [BH][N][KVM(D)]   three A operands in fragment order:
+//   kvm  elem  [BH][N][KVM(D, DP)]   three A operands in fragment order:
 //          KF: ->K   (64 keys x D, contraction over D)
 //          VF: V^T   (D x 64 keys, contraction over keys)
-//          MF: -M^T  (D x D, contraction over D),  M = W^T U W
+//          MF: -M^T  (DP x DP, contraction over DP),  M = W^T U W
+//        DP = D, or the leading DP coordinates that the factors act on with
+//        partial PaTH (M vanishes outside its leading DP x DP block)
 //   al   float [BH][N][3][64][16]  diagonal-block raw logits as register image
 //        of the scores S^T: tiles (query block w, key block mb) = (0,0),
 //        (1,0), (1,1) (tile (0,1) lies wholly above the diagonal):
@@ -63,8 +65,9 @@ __host__ __device__ constexpr int frag_row(int s, int g, int t, int kpl) {
   return 32 * ((s * kpl + t) / 16) + acc_row((s * kpl + t) % 16, g);
 }
 
-// Elements of one chunk's kvm block.
-__host__ __device__ constexpr int kvm_elems(int D) { return 2 * kChunk * D + D * D; }
+// Elements of one chunk's kvm block (DP: the coordinates the factors act on).
+__host__ __device__ constexpr int kvm_elems(int D, int DP) { return 2 * kChunk * D + DP * DP; }
+__host__ __device__ constexpr int kvm_elems(int D) { return kvm_elems(D, D); }
 // Floats of one chunk's register images.
 __host__ __device__ constexpr int qa_floats(int D) { return kChunk * D; }
 __host__ __device__ constexpr int al_floats() { return kAlTiles * 64 * 16; }
@@ -126,14 +129,14 @@ struct Layout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline Layout make_layout(int B, int H, int T, int D, size_t esize) {
+inline Layout make_layout(int B, int H, int T, int D, size_t esize, int DP) {
   const size_t BH = (size_t)B * H, N = (size_t)T / kChunk;
   Layout L;
   size_t off = 0;
   L.qa = off;
   off = align256(off + BH * N * qa_floats(D) * sizeof(float));
   L.kvm = off;
-  off = align256(off + BH * N * kvm_elems(D) * esize);
+  off = align256(off + BH * N * kvm_elems(D, DP) * esize);
   L.al = off;
   off = align256(off + BH * N * al_floats() * sizeof(float));
   L.gate = off;
@@ -149,11 +152,13 @@ inline Layout make_layout(int B, int H, int T, int D, size_t esize) {
 // views when they are read in place: bf16 with whole chunks only).
 hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, const FwdIo &io,
                               hipStream_t stream);
-hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
+// DP: the leading coordinates the factors act on (D for PaTH on every
+// coordinate; D / 2 for partial PaTH, whose w is not read beyond them).
+hipError_t launch_prep(int dtype, int D, int DP, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
                        const FwdIo &io, hipStream_t stream);
-hipError_t launch_chunk_bounds(int dtype, int D, const void *kvm,
+hipError_t launch_chunk_bounds(int dtype, int D, int DP, const void *kvm,
                                const float *gate, float2 *bnd, int BH, int T,
                                hipStream_t stream);
 
@@ -175,7 +180,7 @@ struct StreamArgs {
   int H;                // bh = b * H + h
   TokStrides so, sl;    // out and lse row (b, h, t) at b so.b + h so.h + t so.t
 };
-hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
+hipError_t launch_stream(int dtype, int D, int DP, bool fox, const StreamArgs &a,
                          hipStream_t stream);
 hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,
                          const float *al_ws, const float *gate, float *qa,

@@ -207,7 +207,11 @@ __device__ __forceinline__ void solve_block(float *Xs, int p, int q, int lane) {
 // a d-sized dimension give each wave D/64 tiles.  Products whose result goes
 // to LDS are computed in the orientation where a lane's fixed column is the
 // destination row, so each lane stores 4 contiguous elements at a time.
-template <int D>
+// DP: the leading coordinates the factors act on (D; or D / 2 for partial
+// PaTH, where w is not read beyond them: every product with W contracts over
+// DP coordinates only, U W and M vanish outside them, and <-Q, ->K equal Q, K
+// there).
+template <int D, int DP>
 __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const __bf16 *__restrict__ w,
@@ -216,6 +220,8 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   constexpr int C = kChunk, P = 72, PX = 72;
   constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16, KSD = D / 16, KSC = C / 16;
   constexpr int TPW = D / 64;                       // d x 64 tiles per wave
+  constexpr int KSDP = DP / 16, NDBP = DP / 32, NSDP = DP / 16;
+  static_assert(DP == D || 2 * DP == D, "path coordinates: all, or the leading half");
   constexpr int PLANE = C * P * 2;                  // one 64 x 72 bf16 plane (bytes)
   constexpr int SLOT = 2 * PLANE;                   // 18432 B: hi/lo planes or 64 x 72 fp32
   constexpr int WT_BYTES = D * P * 2;
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   const __bf16 *vc = v + first(io.v);
   const __bf16 *wc = w + first(io.w);
   const int sq = (int)io.q.t, sk = (int)io.k.t, sv = (int)io.v.t, sw = (int)io.w.t;
-  __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D);
+  __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D, DP);
   __bf16 *vf = kf + C * D;
   __bf16 *mf = vf + C * D;
 
@@ -326,14 +332,18 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
           kinit[u][4 * r4 + e] = (float)kv[u][r4][e];
         }
     f32x16 gacc = zero16(), p1acc = zero16(), skacc = zero16();
-    mma_rows<KSD>(gacc, wm, wn);    // [j][s]  = w_j . w_s
-    mma_rows<KSD>(p1acc, wm, qn);   // [t][i]  = w_t . q_i
-    mma_rows<KSD>(skacc, wm, kn);   // [t][j]  = w_t . k_j
+#pragma unroll
+    for (int ks = 0; ks < KSDP; ++ks) {   // products with W: path coordinates only
+      gacc = mma32(wm[ks], wn[ks], gacc);     // [j][s]  = w_j . w_s
+      p1acc = mma32(wm[ks], qn[ks], p1acc);   // [t][i]  = w_t . q_i
+      skacc = mma32(wm[ks], kn[ks], skacc);   // [t][j]  = w_t . k_j
+    }
     mma_rows<KSD>(kq, km, qn);      // [j][i]  = k_j . q_i  (kept for the diagonal logits)
     // W^T by exact identity products: tile (t block mt, e block eb)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int eb = nt + 2 * u;
+      if (eb >= NDBP) continue;   // W^T is read only over the path coordinates
       f32x16 acc = zero16();
       acc = mma32(pick(wm, 2 * eb), eye_frag(0, lane), acc);
       acc = mma32(pick(wm, 2 * eb + 1), eye_frag(1, lane), acc);
@@ -472,9 +482,10 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
+      uw[u] = zero16();
+      if (nt + 2 * u >= NDBP) continue;   // U W vanishes beyond the path coordinates
       bf16x8 wt[KSC];
       load_rows<KSC>(wt, Wt + 32 * (nt + 2 * u) * P, P, lane);
-      uw[u] = zero16();
       mma_rows<KSC>(uw[u], uh, wt);
       mma_rows<KSC>(uw[u], ul, wt);
     }
@@ -503,11 +514,13 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     // tile tau = wv + 4h: d block eb (in this pass's columns), query / key block ib
     const int tau = wv + 4 * h, eb = tau >> 1, ib = tau & 1, ebl = eb - 2 * h;
     {
-      // <-Q^T = Q^T - (U W)^T lower(Q W^T)^T
+      // <-Q^T = Q^T - (U W)^T lower(Q W^T)^T (= Q^T beyond the path coordinates)
       f32x16 acc = zero16();
-      tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
-      tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1l + 32 * ib * P, P, lane);
-      tile_mma<C>(acc, UWl + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
+      if (eb < NDBP) {
+        tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
+        tile_mma<C>(acc, UWh + 32 * ebl * P, P, P1l + 32 * ib * P, P, lane);
+        tile_mma<C>(acc, UWl + 32 * ebl * P, P, P1h + 32 * ib * P, P, lane);
+      }
       float *dst = qa_c + ((ib * NDB + eb) * 64 + lane) * 16;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -517,9 +530,12 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
         *reinterpret_cast<f32x4 *>(dst + 4 * r4) = x;
       }
       // ->K^T = K^T - W^T T2 (tile (eb, jb = ib)), into KF fragment blobs
+      // (= K^T beyond the path coordinates)
       f32x16 kacc = zero16();
-      tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2h + 32 * ib * P, P, lane);
-      tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2l + 32 * ib * P, P, lane);
+      if (eb < NDBP) {
+        tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2h + 32 * ib * P, P, lane);
+        tile_mma<C>(kacc, Wt + 32 * eb * P, P, T2l + 32 * ib * P, P, lane);
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 x;
@@ -530,9 +546,12 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     }
     // -M^T in MF fragment blobs: M = W^T (U W), tile (ab, bb) = (tau % NDB,
     // tau / NDB) for tau = wv + 4u, so this pass's columns bb are 2h, 2h + 1.
+    // With DP < D (then DP <= 64) the DP x DP block is done in pass 0.
 #pragma unroll
-    for (int v = 0; v < MPP; ++v) {
-      const int tm = wv + 4 * (h * MPP + v), ab = tm % NDB, bb = tm / NDB, bbl = bb - 2 * h;
+    for (int v = 0; v < (DP == D ? MPP : (NDBP * NDBP + 3) / 4); ++v) {
+      if (DP < D && (h > 0 || wv + 4 * v >= NDBP * NDBP)) continue;
+      const int tm = DP == D ? wv + 4 * (h * MPP + v) : wv + 4 * v;
+      const int ab = tm % NDBP, bb = tm / NDBP, bbl = bb - 2 * h;
       f32x16 acc = zero16();
       tile_mma<C>(acc, Wt + 32 * ab * P, P, UWh + 32 * bbl * P, P, lane);
       tile_mma<C>(acc, Wt + 32 * ab * P, P, UWl + 32 * bbl * P, P, lane);
@@ -541,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
         bf16x8 x;
 #pragma unroll
         for (int t = 0; t < 8; ++t) x[t] = (__bf16)(-acc[8 * hh + t]);
-        *reinterpret_cast<bf16x8 *>(mf + ((bb * NSD + 2 * ab + hh) * 64 + lane) * 8) = x;
+        *reinterpret_cast<bf16x8 *>(mf + ((bb * NSDP + 2 * ab + hh) * 64 + lane) * 8) = x;
       }
     }
   }
@@ -568,16 +587,16 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
 // One block of 256 threads per (bh, chunk), plain float32 on the vector units.
 // LDS: W and U W (64 x D, padded), U, P1 = lower(Q W^T) and T2 = U
 // strictLower(W K^T) (64 x 64, padded).
-template <int D>
+template <int D, int DP>
 __global__ __launch_bounds__(256) void prep_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k,
     const float *__restrict__ v, const float *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa,
     float *__restrict__ kvm, float *__restrict__ al, int T) {
-  constexpr int C = kChunk, DP = D + 1, CP = C + 1, NT = 256;
+  constexpr int C = kChunk, DPW = D + 1, CP = C + 1, NT = 256;
   constexpr int KPL = 1, KSTEP = 2;
-  __shared__ float Ws[C * DP];
-  __shared__ float UWs[C * DP];
+  __shared__ float Ws[C * DPW];
+  __shared__ float UWs[C * DPW];
   __shared__ float Us[C * CP];
   __shared__ float P1s[C * CP];
   __shared__ float T2s[C * CP];
@@ -592,7 +611,9 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
   const float *vc = v + row0 * D;
   const float *wc = w + row0 * D;
 
-  for (int idx = tid; idx < C * D; idx += NT) Ws[(idx / D) * DP + idx % D] = wc[idx];
+  // w beyond the path coordinates is not read (taken as zero)
+  for (int idx = tid; idx < C * D; idx += NT)
+    Ws[(idx / D) * DPW + idx % D] = idx % D < DP ? wc[idx] : 0.f;
   if (tid < C) bs[tid] = beta[row0 + tid];
   __syncthreads();
 
@@ -601,7 +622,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
     const int i = idx / C, j = idx % C;
     float s = 0.f;
     if (j < i) {
-      for (int t = 0; t < D; ++t) s += Ws[i * DP + t] * Ws[j * DP + t];
+      for (int t = 0; t < DP; ++t) s += Ws[i * DPW + t] * Ws[j * DPW + t];
       s *= bs[i];
     }
     Us[i * CP + j] = s;
@@ -628,14 +649,14 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
   for (int idx = tid; idx < C * D; idx += NT) {
     const int s = idx / D, col = idx % D;
     float acc = 0.f;
-    for (int t = 0; t <= s; ++t) acc += Us[s * CP + t] * Ws[t * DP + col];
-    UWs[s * DP + col] = acc;
+    for (int t = 0; t <= s; ++t) acc += Us[s * CP + t] * Ws[t * DPW + col];
+    UWs[s * DPW + col] = acc;
   }
   for (int idx = tid; idx < C * C; idx += NT) {
     const int t = idx / C, j = idx % C;
     float acc = 0.f;
     if (t > j)
-      for (int e = 0; e < D; ++e) acc += Ws[t * DP + e] * kc[(size_t)j * D + e];
+      for (int e = 0; e < DP; ++e) acc += Ws[t * DPW + e] * kc[(size_t)j * D + e];
     P1s[t * CP + j] = acc;
   }
   __syncthreads();
@@ -652,7 +673,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
     const int i = idx / C, t = idx % C;
     float acc = 0.f;
     if (t <= i)
-      for (int e = 0; e < D; ++e) acc += qc[(size_t)i * D + e] * Ws[t * DP + e];
+      for (int e = 0; e < DP; ++e) acc += qc[(size_t)i * D + e] * Ws[t * DPW + e];
     P1s[i * CP + t] = acc;
   }
   __syncthreads();
@@ -664,7 +685,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
     const int wq = blk / (D / 32), mb = blk % (D / 32);
     const int i = 32 * wq + (lane & 31), col = 32 * mb + acc_row(r, lane >> 5);
     float acc = qc[(size_t)i * D + col];
-    for (int t = 0; t <= i; ++t) acc -= P1s[i * CP + t] * UWs[t * DP + col];
+    for (int t = 0; t <= i; ++t) acc -= P1s[i * CP + t] * UWs[t * DPW + col];
     qa_c[idx] = acc;
   }
   // Al = lower(Q K^T) - P1 T2, register image of the three stored tiles.
@@ -682,7 +703,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
   }
 
   // Matrix-core operands in fragment order.
-  float *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D);
+  float *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D, DP);
   float *vf = kf + C * D;
   float *mf = vf + C * D;
   {  // KF: ->K[key][dcol] = K[key][dcol] - sum_{s>key} T2[s][key] W[s][dcol]
@@ -691,7 +712,7 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
       const int blob = it / 64, lane = it % 64, mb = blob / NS, s = blob % NS;
       const int key = 32 * mb + lane % 32, dcol = frag_row(s, lane / 32, 0, KPL);
       float acc = kc[(size_t)key * D + dcol];
-      for (int r = key + 1; r < C; ++r) acc -= T2s[r * CP + key] * Ws[r * DP + dcol];
+      for (int r = key + 1; r < C; ++r) acc -= T2s[r * CP + key] * Ws[r * DPW + dcol];
       kf[it] = acc;
     }
   }
@@ -702,13 +723,13 @@ __global__ __launch_bounds__(256) void prep_f32_kernel(
       vf[it] = vc[(size_t)frag_row(s, lane / 32, 0, KPL) * D + 32 * mb + lane % 32];
     }
   }
-  {  // MF: X[b][a] = -M[a][b] = -sum_s W[s][a] UW[s][b]
-    constexpr int NS = D / KSTEP;
-    for (int it = tid; it < (D / 32) * NS * 64; it += NT) {
+  {  // MF: X[b][a] = -M[a][b] = -sum_s W[s][a] UW[s][b], a, b < DP
+    constexpr int NS = DP / KSTEP;
+    for (int it = tid; it < (DP / 32) * NS * 64; it += NT) {
       const int blob = it / 64, lane = it % 64, mb = blob / NS, s = blob % NS;
       const int b = 32 * mb + lane % 32, a = frag_row(s, lane / 32, 0, KPL);
       float acc = 0.f;
-      for (int r = 0; r < C; ++r) acc += Ws[r * DP + a] * UWs[r * DP + b];
+      for (int r = 0; r < C; ++r) acc += Ws[r * DPW + a] * UWs[r * DPW + b];
       mf[it] = -acc;
     }
   }
@@ -773,24 +794,24 @@ __global__ __launch_bounds__(256) void unpack_kernel(
   }
 }
 
-template <int D>
+template <int D, int DP>
 hipError_t launch_prep_bf16(const void *q, const void *k, const void *v,
                             const void *w, const float *beta, float *qa,
                             void *kvm, float *al, int BH, int T, const FwdIo &io,
                             hipStream_t stream) {
-  hipLaunchKernelGGL((prep_bf16_kernel<D>), dim3(BH * (T / kChunk)), dim3(256), 0,
+  hipLaunchKernelGGL((prep_bf16_kernel<D, DP>), dim3(BH * (T / kChunk)), dim3(256), 0,
                      stream, (const __bf16 *)q, (const __bf16 *)k,
                      (const __bf16 *)v, (const __bf16 *)w, beta, qa,
                      (__bf16 *)kvm, al, T, io);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DP>
 hipError_t launch_prep_f32(const void *q, const void *k, const void *v,
                            const void *w, const float *beta, float *qa,
                            void *kvm, float *al, int BH, int T,
                            hipStream_t stream) {
-  hipLaunchKernelGGL((prep_f32_kernel<D>), dim3(BH * (T / kChunk)), dim3(256), 0,
+  hipLaunchKernelGGL((prep_f32_kernel<D, DP>), dim3(BH * (T / kChunk)), dim3(256), 0,
                      stream, (const float *)q, (const float *)k,
                      (const float *)v, (const float *)w, beta, qa,
                      (float *)kvm, al, T);
@@ -802,7 +823,7 @@ hipError_t launch_prep_f32(const void *q, const void *k, const void *v,
 // squared norm of its ->K rows as stored for the scan (bf16 values squared
 // exactly, summed in float32).  One wave per chunk, four chunks per block.
 // A non-finite value makes its bound +inf, so that no block is skipped on it.
-template <typename E, int D>
+template <typename E, int D, int DP>
 __global__ __launch_bounds__(256) void chunk_bounds_kernel(
     const E *__restrict__ kvm, const float *__restrict__ gate,
     float2 *__restrict__ bnd, int n_chunks, int T) {
@@ -816,7 +837,7 @@ __global__ __launch_bounds__(256) void chunk_bounds_kernel(
   if (!(amax <= 3.0e38f)) amax = INFINITY;   // NaN or +inf
   // fragment order: in every blob of key block mb, lane l holds KPL values of
   // row 32*mb + l%32
-  const E *kf = kvm + (size_t)ci * kvm_elems(D);
+  const E *kf = kvm + (size_t)ci * kvm_elems(D, DP);
   float kmax2 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -840,11 +861,11 @@ __global__ __launch_bounds__(256) void chunk_bounds_kernel(
   if (lane == 0) bnd[ci] = make_float2(amax, kmax2);
 }
 
-template <typename E, int D>
+template <typename E, int D, int DP>
 hipError_t launch_chunk_bounds_t(const void *kvm, const float *gate, float2 *bnd,
                                  int BH, int T, hipStream_t stream) {
   const int n = BH * (T / kChunk);
-  hipLaunchKernelGGL((chunk_bounds_kernel<E, D>), dim3((n + 3) / 4), dim3(256), 0, stream,
+  hipLaunchKernelGGL((chunk_bounds_kernel<E, D, DP>), dim3((n + 3) / 4), dim3(256), 0, stream,
                      (const E *)kvm, gate, bnd, n, T);
   return hipGetLastError();
 }
@@ -870,27 +891,41 @@ hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, con
 }
 
 // float32 inputs are always read in the padded dense layout (io unused).
-hipError_t launch_prep(int dtype, int D, const void *q, const void *k,
+hipError_t launch_prep(int dtype, int D, int DP, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
                        const FwdIo &io, hipStream_t stream) {
+  const bool half = DP != D;
   if (dtype == 1) {
-    if (D == 64) return launch_prep_bf16<64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
-    return launch_prep_bf16<128>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
+    if (D == 64)
+      return half ? launch_prep_bf16<64, 32>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream)
+                  : launch_prep_bf16<64, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
+    return half ? launch_prep_bf16<128, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream)
+                : launch_prep_bf16<128, 128>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
   }
-  if (D == 64) return launch_prep_f32<64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
-  return launch_prep_f32<128>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
+  if (D == 64)
+    return half ? launch_prep_f32<64, 32>(q, k, v, w, beta, qa, kvm, al, BH, T, stream)
+                : launch_prep_f32<64, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
+  return half ? launch_prep_f32<128, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, stream)
+              : launch_prep_f32<128, 128>(q, k, v, w, beta, qa, kvm, al, BH, T, stream);
 }
 
-hipError_t launch_chunk_bounds(int dtype, int D, const void *kvm,
+hipError_t launch_chunk_bounds(int dtype, int D, int DP, const void *kvm,
                                const float *gate, float2 *bnd, int BH, int T,
                                hipStream_t stream) {
+  const bool half = DP != D;
   if (dtype == 1) {
-    if (D == 64) return launch_chunk_bounds_t<__bf16, 64>(kvm, gate, bnd, BH, T, stream);
-    return launch_chunk_bounds_t<__bf16, 128>(kvm, gate, bnd, BH, T, stream);
+    if (D == 64)
+      return half ? launch_chunk_bounds_t<__bf16, 64, 32>(kvm, gate, bnd, BH, T, stream)
+                  : launch_chunk_bounds_t<__bf16, 64, 64>(kvm, gate, bnd, BH, T, stream);
+    return half ? launch_chunk_bounds_t<__bf16, 128, 64>(kvm, gate, bnd, BH, T, stream)
+                : launch_chunk_bounds_t<__bf16, 128, 128>(kvm, gate, bnd, BH, T, stream);
   }
-  if (D == 64) return launch_chunk_bounds_t<float, 64>(kvm, gate, bnd, BH, T, stream);
-  return launch_chunk_bounds_t<float, 128>(kvm, gate, bnd, BH, T, stream);
+  if (D == 64)
+    return half ? launch_chunk_bounds_t<float, 64, 32>(kvm, gate, bnd, BH, T, stream)
+                : launch_chunk_bounds_t<float, 64, 64>(kvm, gate, bnd, BH, T, stream);
+  return half ? launch_chunk_bounds_t<float, 128, 64>(kvm, gate, bnd, BH, T, stream)
+              : launch_chunk_bounds_t<float, 128, 128>(kvm, gate, bnd, BH, T, stream);
 }
 
 hipError_t launch_unpack(int dtype, int D, const float *qa_ws, const void *kvm,

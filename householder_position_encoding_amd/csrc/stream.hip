@@ -134,7 +134,10 @@ __device__ __forceinline__ float logit_bound(float qn2, float2 b, float sl2) {
 // NQC query chunks per block, two waves per chunk.  Operand blocks are
 // prefetched PD key chunks ahead into a ring of PD + 1 LDS buffers (PD = 0:
 // one buffer, loaded synchronously, for shapes where two copies do not fit).
-template <typename E, int D, bool FOX, int NQC, int PD>
+// DP: the leading coordinates the chunk transitions act on (D, or D / 2 for
+// partial PaTH: -M^T is DP x DP and the transition product touches only the
+// first DP rows of the running tile).
+template <typename E, int D, int DP, bool FOX, int NQC, int PD>
 __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     const float *__restrict__ qa, const E *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
@@ -146,14 +149,18 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   constexpr int C = kChunk, KPL = MF::KPL, KSTEP = 2 * KPL;
   constexpr int NDB = D / 32;           // 32-row blocks over d
   constexpr int NSD = D / KSTEP;        // k-steps of a contraction over d
+  constexpr int NDBP = DP / 32;         // the same over the path coordinates
+  constexpr int NSDP = DP / KSTEP;
   constexpr int NSK = C / KSTEP;        // k-steps of a contraction over keys
-  constexpr int KVM = kvm_elems(D);
+  constexpr int KVM = kvm_elems(D, DP);
   constexpr int KVM_BYTES = KVM * (int)sizeof(E);
   constexpr int FRAG = 64 * KPL;        // elements of one A-operand fragment
   constexpr int NW = NQC * 2;           // waves per block
   constexpr int NBUF = PD + 1;
-  constexpr int NL = KVM_BYTES / 1024 / NW;   // copy instructions per wave per chunk
-  static_assert(KVM_BYTES % (1024 * NW) == 0, "operand block must split evenly over the waves");
+  constexpr int NBLK = KVM_BYTES / 1024;          // 1 KiB copy instructions per chunk
+  constexpr int NL = (NBLK + NW - 1) / NW;        // per wave (the last round partly)
+  static_assert(KVM_BYTES % 1024 == 0, "operand block in whole KiB");
+  static_assert(PD < 2 || NBLK % NW == 0, "deep prefetch counts copies per wave");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
   __shared__ __attribute__((aligned(16))) float gate_l[FOX ? NBUF * C : 1];
 
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int j = wave + i * NW;
-      copy16_to_lds(src + j * 1024 + lane * 16, lds_addr(dst + j * 1024));
+      if (NBLK % NW == 0 || j < NBLK) copy16_to_lds(src + j * 1024 + lane * 16, lds_addr(dst + j * 1024));
     }
   };
 
@@ -329,10 +336,10 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       // transition (after chunk 0 the tile is not used)
       if (c > 0) {
 #pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
+        for (int mb = 0; mb < NDBP; ++mb)
 #pragma unroll
-          for (int s = 0; s < NSD; ++s)
-            qw[mb] = MF::run(MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], qw[mb]);
+          for (int s = 0; s < NSDP; ++s)
+            qw[mb] = MF::run(MF::load(mf_l + (mb * NSDP + s) * FRAG + lane * KPL), qb[s], qw[mb]);
       }
       if (!skip_blk) softmax_pv(sc, ga, vf_l, false);
     }
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
 // p <= 2^8 and the rare rescale comes after the exponentials.  The row sums
 // are taken from the bf16-rounded weights that the P.V products use (dot with
 // (1, 1)), so numerator and denominator match.
-template <int D, bool FOX, int NQC, int PD>
+template <int D, int DP, bool FOX, int NQC, int PD>
 __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
     const float *__restrict__ qa, const __bf16 *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
@@ -416,15 +423,19 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
   constexpr int C = kChunk, KPL = MF::KPL, KSTEP = 2 * KPL;
   constexpr int NDB = D / 32;
   constexpr int NSD = D / KSTEP;
+  constexpr int NDBP = DP / 32;
+  constexpr int NSDP = DP / KSTEP;
   constexpr int NSK = C / KSTEP;
-  constexpr int KVM = kvm_elems(D);
+  constexpr int KVM = kvm_elems(D, DP);
   constexpr int KVM_BYTES = KVM * (int)sizeof(E);
   constexpr int FRAG = 64 * KPL;
   constexpr int NW = NQC;               // one wave per query chunk
   constexpr int NBUF = PD + 1;
-  constexpr int NL = KVM_BYTES / 1024 / NW;
+  constexpr int NBLK = KVM_BYTES / 1024;
+  constexpr int NL = (NBLK + NW - 1) / NW;
   static_assert(PD >= 1, "the wide kernel always prefetches");
-  static_assert(KVM_BYTES % (1024 * NW) == 0, "operand block must split evenly over the waves");
+  static_assert(KVM_BYTES % 1024 == 0, "operand block in whole KiB");
+  static_assert(PD < 2 || NBLK % NW == 0, "deep prefetch counts copies per wave");
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
   __shared__ __attribute__((aligned(16))) float gate_l[FOX ? NBUF * C : 1];
 
@@ -448,7 +459,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int jb = wave + i * NW;
-      copy16_to_lds(src + jb * 1024 + lane * 16, lds_addr(dst + jb * 1024));
+      if (NBLK % NW == 0 || jb < NBLK) copy16_to_lds(src + jb * 1024 + lane * 16, lds_addr(dst + jb * 1024));
     }
   };
 
@@ -591,10 +602,10 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       // Q_work^T <- Q_work^T - M_c^T round(Q_work^T) (unused after chunk 0)
       if (c > 0) {
 #pragma unroll
-        for (int mb = 0; mb < NDB; ++mb)
+        for (int mb = 0; mb < NDBP; ++mb)
 #pragma unroll
-          for (int s = 0; s < NSD; ++s) {
-            const frag a = MF::load(mf_l + (mb * NSD + s) * FRAG + lane * KPL);
+          for (int s = 0; s < NSDP; ++s) {
+            const frag a = MF::load(mf_l + (mb * NSDP + s) * FRAG + lane * KPL);
 #pragma unroll
             for (int j = 0; j < 2; ++j) qw[j][mb] = MF::run(a, qb[j][s], qw[j][mb]);
           }
@@ -757,7 +768,7 @@ struct Shape<float, 64> { static constexpr int NQC = 2, PD = 1; };
 template <>
 struct Shape<float, 128> { static constexpr int NQC = 2, PD = 0; };
 
-template <typename E, int D, bool FOX>
+template <typename E, int D, int DP, bool FOX>
 hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int N = a.T / kChunk;
   const float sl2 = a.sl2;
@@ -772,7 +783,7 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
     auto go = [&](auto nqc) {
       constexpr int NQC = decltype(nqc)::value;
       const int blocks = a.BH * ((N + NQC - 1) / NQC);
-      hipLaunchKernelGGL((stream_wide_kernel<D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
+      hipLaunchKernelGGL((stream_wide_kernel<D, DP, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 64), 0,
                          stream, a.qa, (const __bf16 *)a.kvm, a.al, a.gate, a.bnd, a.skip,
                          a.skipped, (__bf16 *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl);
       return hipGetLastError();
@@ -782,28 +793,32 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   }
   constexpr int NQC = Shape<E, D>::NQC, PD = Shape<E, D>::PD;
   const int blocks = a.BH * ((N + NQC - 1) / NQC);
-  hipLaunchKernelGGL((stream_kernel<E, D, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 128), 0,
+  hipLaunchKernelGGL((stream_kernel<E, D, DP, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 128), 0,
                      stream, a.qa, (const E *)a.kvm, a.al, a.gate, a.bnd, a.skip, a.skipped,
                      (E *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl);
   return hipGetLastError();
 }
 
 template <typename E, int D>
-hipError_t launch_stream_d(bool fox, const StreamArgs &a, hipStream_t stream) {
-  if (fox) return launch_stream_t<E, D, true>(a, stream);
-  return launch_stream_t<E, D, false>(a, stream);
+hipError_t launch_stream_d(int DP, bool fox, const StreamArgs &a, hipStream_t stream) {
+  if (DP == D) {
+    if (fox) return launch_stream_t<E, D, D, true>(a, stream);
+    return launch_stream_t<E, D, D, false>(a, stream);
+  }
+  if (fox) return launch_stream_t<E, D, D / 2, true>(a, stream);
+  return launch_stream_t<E, D, D / 2, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_stream(int dtype, int D, bool fox, const StreamArgs &a,
+hipError_t launch_stream(int dtype, int D, int DP, bool fox, const StreamArgs &a,
                          hipStream_t stream) {
   if (dtype == 1) {
-    if (D == 64) return launch_stream_d<__bf16, 64>(fox, a, stream);
-    return launch_stream_d<__bf16, 128>(fox, a, stream);
+    if (D == 64) return launch_stream_d<__bf16, 64>(DP, fox, a, stream);
+    return launch_stream_d<__bf16, 128>(DP, fox, a, stream);
   }
-  if (D == 64) return launch_stream_d<float, 64>(fox, a, stream);
-  return launch_stream_d<float, 128>(fox, a, stream);
+  if (D == 64) return launch_stream_d<float, 64>(DP, fox, a, stream);
+  return launch_stream_d<float, 128>(DP, fox, a, stream);
 }
 
 }  // namespace pathattn

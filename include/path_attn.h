@@ -123,6 +123,27 @@ int path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w,
                      void *stream);
 
 /*
+ * Partial PaTH (the authors' response page, remark on applying PaTH to a
+ * subset of the head dimensions for speed): the factors act on the leading
+ * d_path coordinates only, and the other d - d_path coordinates carry a plain
+ * dot product,
+ *     H_t = I - beta_t w~_t w~_t^T,  w~_t = (w_t[0 .. d_path), 0, ..., 0),
+ * i.e. the definition at the top of this header with w_t's trailing
+ * coordinates taken as zero (they are not read).  The chunk transforms are
+ * then d_path x d_path, so the chunk preparation's products with W and the
+ * scan's transition product shrink.  d_path = d is path_attn_fwd_ex;
+ * d_path = d / 2 is the other supported value (PATH_ATTN_EUNSUPPORTED for
+ * any other d_path in (0, d]; EINVAL outside it).  A workspace of
+ * path_attn_workspace_bytes(B, H, T, d, dtype) bytes suffices.  Other
+ * arguments, results and errors as for path_attn_fwd_ex.
+ */
+int path_attn_fwd_partial(const void *q, const void *k, const void *v, const void *w,
+                          const float *beta, const float *logf, void *out, float *lse,
+                          int B, int H, int T, int d, int d_path, int dtype, float scale,
+                          unsigned flags, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * path_attn_fwd_ex without a caller workspace.  The workspace is a fixed

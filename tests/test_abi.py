@@ -429,3 +429,23 @@ def test_noalloc_max_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define PATH_ATTN_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_MAX_BYTES
+
+
+@pytest.mark.parametrize("d,d_path,status", [(64, 48, EUNSUP), (128, 96, EUNSUP), (64, 0, EINVAL),
+                                             (64, 80, EINVAL), (128, -64, EINVAL)])
+def test_partial_validation(d, d_path, status):
+    """path_attn_fwd_partial: d_path must be d or d / 2 (EUNSUPPORTED for other
+    values in (0, d], EINVAL outside), checked before any HIP call."""
+    lib = pa.load_library()
+    assert lib.path_attn_fwd_partial(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 256, d,
+                                     d_path, pa.BF16, 0.0, 0, FAKE, 1 << 40, None) == status
+
+
+def test_partial_workspace_fits_the_full_one():
+    """A workspace of path_attn_workspace_bytes suffices for partial PaTH: a
+    smaller one is rejected only below the partial layout's own size."""
+    lib = pa.load_library()
+    need = pa.path_attn_workspace_bytes(1, 2, 256, 64, pa.BF16)
+    assert lib.path_attn_fwd_partial(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 256, 64,
+                                     32, pa.BF16, 0.0, 0, FAKE, 100, None) == EINVAL
+    assert need > 100
