@@ -538,6 +538,11 @@ def trace_report(args):
                   f"{flops:.4g} flop per launch; at the average duration {avg * 1e3:.4f} ms that "
                   f"is {flops / avg / 1e12:.0f} TFLOP/s = {flops / avg / 1e12 / peak:.3f} of the "
                   f"{peak:.0f} TFLOP/s peak (at the minimum, {flops / mn / 1e12 / peak:.3f})."]
+        if wl.fox:
+            lines += ["With the forget gate the bench launches the scan both with the exact block "
+                      "skip and with every block computed (PATH_ATTN_NO_SKIP), so these durations "
+                      "mix the two and the rate above is partly effective; the bench line's "
+                      "roofline takes the no-skip calls alone."]
     with open(md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -33,7 +33,7 @@ import pytest
 import workloads
 from oracle.backward import gradients as oracle_gradients
 from oracle.chunked_backward import sweep_backward
-from tests.gpu_util import to_device
+from tests.gpu_util import spread_heads, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -154,10 +154,13 @@ def test_backward_custom_scale_and_near_reflections():
         _compare("scale 0.3, near-2 betas", dtype, got, ref, 0, h)
 
 
+# Heads compared at full size: spread over the flat head index where the
+# blockwise oracle is cheap (T = 2048: about 1 s a head), fewer at T = 8192
+# and 16384 (about 20 and 45 s a head on the CPU).
 FULL = [
-    (workloads.MID_D64, [(0, 0), (15, 15)]),
-    (workloads.MID_D128_NEAR2, [(7, 3)]),
-    (workloads.FOX_D128, [(3, 7)]),
+    (workloads.MID_D64, spread_heads(16, 16)),
+    (workloads.MID_D128_NEAR2, [(0, 0), (5, 3), (10, 6), (15, 7)]),
+    (workloads.FOX_D128, [(1, 2), (3, 7)]),
     (workloads.LONG_D64, [(1, 15)]),
 ]
 
