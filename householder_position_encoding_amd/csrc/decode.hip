@@ -49,68 +49,77 @@ __device__ __forceinline__ E from_f(float x) { return (E)x; }   // RNE for bf16
 
 // ------------------------------------------------------------ prefill: chunks
 
+// acc(i, j) += sum_{k < K} A(i, k) B(k, j) for this wave's 32 x 32 output tile
+// on the float32 matrix cores (v_mfma_f32_32x32x2f32: lane l supplies A(l%32,
+// l/32) and B(l/32, l%32) per instruction), operands in LDS addressed through
+// row / column strides (A(i, k) = A[i*ars + k*acs], B(k, j) = B[k*brs +
+// j*bcs], already offset to the tile), so transposed operands need no copy.
+// With an odd pitch (65) row and column reads are both free of bank conflicts.
+template <int K>
+__device__ __forceinline__ void lds_mm(f32x16 &acc, const float *A, int ars, int acs,
+                                       const float *B, int brs, int bcs, int lane) {
+  const int i = lane & 31, k0 = lane >> 5;
+  const float *pa = A + i * ars + k0 * acs;
+  const float *pb = B + k0 * brs + i * bcs;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[k * acs], pb[k * brs], acc, 0, 0, 0);
+}
+
 // One block of 256 threads per (bh, chunk): ->K_c and M_c in float32, natural
 // layouts kb[bh][L][D] and m[bh][N][D][D] (M[a][b]).
 // U = (I + strictLower(D W W^T))^{-1} D (blocked unit-lower inverse),
 // T2 = U strictLower(W K^T), ->K = K - T2^T W, M = W^T (U W).
-// Every product is a dense 64-wide product of LDS operands (U, the strict
-// lower W K^T and T2 hold zeros outside their triangles), each thread
-// computing 4 x 4 tiles in registers.
+// Every product is a 64 x 64 (or 64 x D, D x D) block of float32
+// matrix-core products on LDS operands; wave w owns the 32 x 32 tile
+// (w >> 1, w & 1) of every 64 x 64 output block.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void align_prep_kernel(
     const E *__restrict__ k, const E *__restrict__ w, const float *__restrict__ beta,
     float *__restrict__ kb, float *__restrict__ m, int L) {
   constexpr int C = kChunk, DP = D + 1, CP = C + 1, NT = 256;
-  // LDS: W; U W, later K; N, then U, then T2; X, then strictLower(W K^T)
+  // LDS: W; N, then U, then T2 (Bs); X, then strictLower(W K^T) (Xs); U W,
+  // later K (UWs)
   __shared__ float Ws[C * DP];
   __shared__ float UWs[C * DP];
-  __shared__ float Us[C * CP];
+  __shared__ float Bs[C * CP];
   __shared__ float Xs[C * CP];
   __shared__ float bs[C];
   __shared__ float tmp[768];
   float *Ks = UWs;
-  float *T2s = Us;
   const int N = L / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
   const size_t row0 = (size_t)bh * L + (size_t)c * C;
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tr = 32 * (wv >> 1), tc = 32 * (wv & 1);   // this wave's tile of a 64 x 64 block
   const E *kc = k + row0 * D;
   const E *wc = w + row0 * D;
-  float acc[4][4];
+  f32x16 acc;
 
   for (int idx = tid; idx < C * D; idx += NT) Ws[(idx / D) * DP + idx % D] = to_f(wc[idx]);
   if (tid < C) bs[tid] = beta[row0 + tid];
   __syncthreads();
-  // N[i][j] = beta_i (w_i . w_j) for j < i (into Us)
-  tile_zero(acc);
-  tile_mm<D>(acc, Ws, DP, 1, Ws, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = r0 + 16 * r, j = c0 + 16 * q;
-      Us[i * CP + j] = j < i ? acc[r][q] * bs[i] : 0.f;
-    }
+  // N[i][j] = beta_i (w_i . w_j) for j < i (into Bs)
+  zero16(acc);
+  lds_mm<D>(acc, Ws + tr * DP, DP, 1, Ws + tc * DP, 1, DP, lane);
+  tile_each(tid, [&](int i, int j, int r) { Bs[i * CP + j] = j < i ? acc[r] * bs[i] : 0.f; });
   __syncthreads();
   // X = (I + N)^{-1}: blocked unit-lower inverse (16 x 16 diagonal blocks by
   // substitution, the off-diagonal blocks level by level with the whole block)
-  unit_lower_inverse(Us, Xs, tmp, tid);
+  unit_lower_inverse(Bs, Xs, tmp, tid);
   __syncthreads();
-  // U = X D (unit diagonal of X times beta), zero above the diagonal
+  // U = X D (unit diagonal of X times beta), zero above the diagonal (into Bs)
   for (int idx = tid; idx < C * C; idx += NT) {
     const int i = idx / C, j = idx % C;
-    Us[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);
+    Bs[i * CP + j] = j < i ? Xs[i * CP + j] * bs[j] : (j == i ? bs[i] : 0.f);
   }
   __syncthreads();
   // UW = U W (64 x D)
 #pragma unroll
   for (int h = 0; h < D / 64; ++h) {
-    tile_zero(acc);
-    tile_mm<C>(acc, Us, CP, 1, Ws + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) UWs[(r0 + 16 * r) * DP + 64 * h + c0 + 16 * q] = acc[r][q];
+    zero16(acc);
+    lds_mm<C>(acc, Bs + tr * CP, CP, 1, Ws + 64 * h + tc, DP, 1, lane);
+    tile_each(tid, [&](int i, int j, int r) { UWs[i * DP + 64 * h + j] = acc[r]; });
   }
   __syncthreads();
   // M[a][b] = sum_s W[s][a] UW[s][b]
@@ -119,77 +128,60 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
   for (int ha = 0; ha < D / 64; ++ha)
 #pragma unroll
     for (int hb = 0; hb < D / 64; ++hb) {
-      tile_zero(acc);
-      tile_mm<C>(acc, Ws + 64 * ha, 1, DP, UWs + 64 * hb, DP, 1, r0, c0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          m_c[(size_t)(64 * ha + r0 + 16 * r) * D + 64 * hb + c0 + 16 * q] = acc[r][q];
+      zero16(acc);
+      lds_mm<C>(acc, Ws + 64 * ha + tr, 1, DP, UWs + 64 * hb + tc, DP, 1, lane);
+      tile_each(tid, [&](int a, int b, int r) {
+        m_c[(size_t)(64 * ha + a) * D + 64 * hb + b] = acc[r];
+      });
     }
   __syncthreads();   // U W is no longer read: its buffer takes K
   for (int idx = tid; idx < C * D; idx += NT) Ks[(idx / D) * DP + idx % D] = to_f(kc[idx]);
   __syncthreads();
   // SK[t][j] = w_t . k_j for t > j, else 0 (into Xs)
-  tile_zero(acc);
-  tile_mm<D>(acc, Ws, DP, 1, Ks, 1, DP, r0, c0);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = r0 + 16 * r, j = c0 + 16 * q;
-      Xs[t * CP + j] = t > j ? acc[r][q] : 0.f;
-    }
+  zero16(acc);
+  lds_mm<D>(acc, Ws + tr * DP, DP, 1, Ks + tc * DP, 1, DP, lane);
+  tile_each(tid, [&](int t, int j, int r) { Xs[t * CP + j] = t > j ? acc[r] : 0.f; });
   __syncthreads();
   // T2 = U SK (both triangular, dense product), written over U once every
-  // thread has read it
-  tile_zero(acc);
-  tile_mm<C>(acc, Us, CP, 1, Xs, CP, 1, r0, c0);
+  // wave has read it
+  zero16(acc);
+  lds_mm<C>(acc, Bs + tr * CP, CP, 1, Xs + tc, CP, 1, lane);
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) T2s[(r0 + 16 * r) * CP + c0 + 16 * q] = acc[r][q];
+  tile_each(tid, [&](int sr, int j, int r) { Bs[sr * CP + j] = acc[r]; });
   __syncthreads();
   // ->K[j][col] = K[j][col] - sum_s T2[s][j] W[s][col]  (T2[s][j] = 0 for s <= j)
   float *kb_c = kb + row0 * D;
 #pragma unroll
   for (int h = 0; h < D / 64; ++h) {
-    tile_zero(acc);
-    tile_mm<C>(acc, T2s, 1, CP, Ws + 64 * h, DP, 1, r0, c0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = r0 + 16 * r, col = 64 * h + c0 + 16 * q;
-        kb_c[(size_t)j * D + col] = Ks[j * DP + col] - acc[r][q];
-      }
+    zero16(acc);
+    lds_mm<C>(acc, Bs + tr, 1, CP, Ws + 64 * h + tc, DP, 1, lane);
+    tile_each(tid, [&](int j, int col, int r) {
+      kb_c[(size_t)j * D + 64 * h + col] = Ks[j * DP + 64 * h + col] - acc[r];
+    });
   }
 }
 
 // ------------------------------------------------------------ prefill: scan
 
-// One block per (bh, slice of CB = D/8 columns of G).  Thread (rg, cb) = (tid / CB,
-// tid % CB) owns column cb of the slice, rows rg + RG*i.  Chunk by chunk from
-// the last: stage ->K_c and M_c in LDS, write the aligned rows ->K_c G_c of
-// this column slice, then G <- G - M_c^T G.
+// One block of 4 waves per (bh, slice of 32 columns of G).  Chunk by chunk
+// from the last: ->K_c and M_c are staged in LDS (loaded into registers one
+// chunk ahead), the aligned rows ->K_c G_c of this column slice are written
+// (64 x 32: waves 2 and 3), and G <- G - M_c^T G (D x 32: tile t of D/32 on
+// wave t) on the float32 matrix cores; G's slice lives in LDS.
 template <typename KC, int D>
 __global__ __launch_bounds__(256) void align_scan_kernel(
     const float *__restrict__ kb, const float *__restrict__ m, KC *__restrict__ kcache,
     int L, int T_cap) {
-  constexpr int C = kChunk, NT = 256, CB = D / 8, RG = NT / CB;   // 8 column slices per head
-  constexpr int DP = D + 1;
-  constexpr int KR = C / RG;      // rows of ->K G per thread
-  constexpr int GR = D / RG;      // rows of G per thread
-  constexpr int NSL = D / CB;     // column slices per head
+  constexpr int C = kChunk, NT = 256, DP = D + 1, SP = 33;
+  constexpr int NSL = D / 32;                                  // column slices per head
   constexpr int NK4 = C * D / 4 / NT, NM4 = D * D / 4 / NT;   // float4 loads per thread
+  constexpr int NGT = D / 32;                                  // tiles of the G update
   __shared__ float Ks[C * DP];
   __shared__ float Ms[D * DP];
-  __shared__ float Gs[D * CB];
+  __shared__ float Gs[D * SP];
   const int N = L / C;
   const int bh = blockIdx.x / NSL, sl = blockIdx.x % NSL;
-  const int tid = threadIdx.x, cb = tid % CB, rg = tid / CB;
-  const int col = sl * CB + cb;   // column of G (and of the key) this thread owns
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, cl = lane & 31;
 
   f32x4 kreg[NK4], mreg[NM4];
   auto fetch = [&](int c) {       // chunk c's ->K and M into registers
@@ -215,9 +207,9 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
     }
   };
 
-  for (int i = 0; i < GR; ++i) {
-    const int a = rg + RG * i;
-    Gs[a * CB + cb] = a == col ? 1.f : 0.f;
+  for (int idx = tid; idx < D * 32; idx += NT) {
+    const int a = idx / 32, b = idx % 32;
+    Gs[a * SP + b] = a == 32 * sl + b ? 1.f : 0.f;
   }
   if (N > 0) fetch(N - 1);
   for (int c = N - 1; c >= 0; --c) {
@@ -225,30 +217,39 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
     park();
     __syncthreads();
     if (c > 0) fetch(c - 1);   // in flight while chunk c is computed
-    // aligned rows of chunk c: (->K_c G_c)[j][col]
-    float acc[KR];
+    // aligned rows of chunk c, keys 32 (wv - 2).. (waves 2, 3): (->K_c G_c)[j][col]
+    if (wv >= 2) {
+      const int kh = wv - 2;
+      f32x16 acc;
+      zero16(acc);
+      lds_mm<D>(acc, Ks + 32 * kh * DP, DP, 1, Gs, SP, 1, lane);
+      KC *dst = kcache + ((size_t)bh * T_cap + (size_t)c * C + 32 * kh) * D + 32 * sl + cl;
 #pragma unroll
-    for (int i = 0; i < KR; ++i) acc[i] = 0.f;
-    for (int a = 0; a < D; ++a) {
-      const float g = Gs[a * CB + cb];
-#pragma unroll
-      for (int i = 0; i < KR; ++i) acc[i] = __builtin_fmaf(Ks[(rg + RG * i) * DP + a], g, acc[i]);
+      for (int r = 0; r < 16; ++r) dst[(size_t)acc_row(r, g) * D] = from_f<KC>(acc[r]);
     }
-    KC *dst = kcache + ((size_t)bh * T_cap + (size_t)c * C) * D + col;
+    // G <- G - M_c^T G: tile t (rows 32 t..) of the slice
+    f32x16 gn[(NGT + 3) / 4];
 #pragma unroll
-    for (int i = 0; i < KR; ++i) dst[(size_t)(rg + RG * i) * D] = from_f<KC>(acc[i]);
-    // G <- G - M_c^T G for this column
-    float gn[GR];
+    for (int u = 0; u < (NGT + 3) / 4; ++u) {
+      const int t = wv + 4 * u;
+      if (t < NGT) {
 #pragma unroll
-    for (int i = 0; i < GR; ++i) gn[i] = Gs[(rg + RG * i) * CB + cb];
-    for (int r = 0; r < D; ++r) {
-      const float g = Gs[r * CB + cb];
+        for (int r = 0; r < 16; ++r) gn[u][r] = Gs[(32 * t + acc_row(r, g)) * SP + cl];
+        f32x16 prod;
+        zero16(prod);
+        lds_mm<D>(prod, Ms + 32 * t, 1, DP, Gs, SP, 1, lane);   // (M^T G)[a][b] = sum_r M[r][a] G[r][b]
 #pragma unroll
-      for (int i = 0; i < GR; ++i) gn[i] = __builtin_fmaf(-Ms[r * DP + rg + RG * i], g, gn[i]);
+        for (int r = 0; r < 16; ++r) gn[u][r] -= prod[r];
+      }
     }
     __syncthreads();   // all reads of the old G are done
 #pragma unroll
-    for (int i = 0; i < GR; ++i) Gs[(rg + RG * i) * CB + cb] = gn[i];
+    for (int u = 0; u < (NGT + 3) / 4; ++u) {
+      const int t = wv + 4 * u;
+      if (t < NGT)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Gs[(32 * t + acc_row(r, g)) * SP + cl] = gn[u][r];
+    }
   }
 }
 
@@ -263,16 +264,34 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const E *__restrict__ v,
 }
 
 // Gate cache of the prompt: Lambda_j = sum_{1<=s<=j} log f_s in float64 (f_0
-// never enters a logit), one block per (b, h), sequential in one thread.
-__global__ __launch_bounds__(64) void gate_cache_kernel(const float *__restrict__ logf,
-                                                        double *__restrict__ gcache, int L, int T_cap) {
-  const int bh = blockIdx.x;
-  if (threadIdx.x != 0) return;
-  double acc = 0.0;
-  gcache[(size_t)bh * T_cap] = 0.0;
-  for (int j = 1; j < L; ++j) {
-    acc += (double)logf[(size_t)bh * L + j];
-    gcache[(size_t)bh * T_cap + j] = acc;
+// never enters a logit), one block of 256 threads per (b, h): each thread sums
+// its segment, the segment sums are prefixed, and each thread writes its
+// segment's running sums.
+__global__ __launch_bounds__(256) void gate_cache_kernel(const float *__restrict__ logf,
+                                                         double *__restrict__ gcache, int L,
+                                                         int T_cap) {
+  __shared__ double part[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const float *f = logf + (size_t)bh * L;
+  const int per = (L + 255) / 256;
+  const int t0 = min(L, tid * per), t1 = min(L, t0 + per);
+  double s = 0.0;
+  for (int t = t0 < 1 ? 1 : t0; t < t1; ++t) s += (double)f[t];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double run = 0.0;
+    for (int i = 0; i < 256; ++i) {
+      const double x = part[i];
+      part[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  double run = part[tid];
+  for (int t = t0; t < t1; ++t) {
+    if (t >= 1) run += (double)f[t];
+    gcache[(size_t)bh * T_cap + t] = run;
   }
 }
 
@@ -614,13 +633,13 @@ hipError_t prefill_t(const void *k, const void *v, const void *w, const float *b
   if (N > 0) {
     hipLaunchKernelGGL((align_prep_kernel<E, D>), dim3(BH * N), dim3(256), 0, stream,
                        (const E *)k, (const E *)w, beta, ws_kb, ws_m, L);
-    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * 8), dim3(256), 0, stream,
+    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 32)), dim3(256), 0, stream,
                        ws_kb, ws_m, (KC *)kcache, L, T_cap);
     const int gx = min(1024, (int)(((size_t)L * D + 255) / 256));
     hipLaunchKernelGGL((copy_rows_kernel<E>), dim3(gx, BH), dim3(256), 0, stream, (const E *)v,
                        (E *)vcache, L, T_cap, D);
     if (logf)
-      hipLaunchKernelGGL(gate_cache_kernel, dim3(BH), dim3(64), 0, stream, logf, gcache, L, T_cap);
+      hipLaunchKernelGGL(gate_cache_kernel, dim3(BH), dim3(256), 0, stream, logf, gcache, L, T_cap);
   }
   return hipGetLastError();
 }
