@@ -721,31 +721,88 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   float colsum = 0.f;
   const float my_lam = (FOX && member) ? lam[krow + col] : 0.f;
   const int c_low = G * grp + 1;   // last query chunk the group visits
+  // bf16: the next step's global reads are in flight during the current
+  // step: its query-side copies (into registers, stored to LDS at the top of
+  // the next step) and this wave's level rows Khat[c-1]_{c'} (B operands of
+  // S); the wave's V rows (B operands of dP) stay in registers for the whole
+  // walk.  Each step issues these loads before any other global access, so
+  // the waits of the step's later loads (crossing operands) do not wait for
+  // anything issued later.
+  using frag = typename MM<E>::frag;
+  constexpr int KPL = MM<E>::KPL, KSD = BF ? D / (2 * KPL) : 1;
+  constexpr int NV = BF ? C * D / 8 / NTH : 1;      // 16-byte copies per thread and tensor
+  static_assert(!BF || C * D / 8 % NTH == 0, "copies split evenly over the block");
+  bf16x8 cq[BF ? NV : 1], co[BF ? NV : 1], cqt[BF ? NV : 1], cot[BF ? NV : 1];
+  float4 cst = make_float4(0.f, 0.f, 0.f, 0.f);
+  frag vfr[KSD], kfr[KSD];
+  auto fetch_copy = [&](int cc) __attribute__((always_inline)) {
+    if constexpr (BF) {
+      const size_t qr = head + (size_t)cc * C;
+      const E *sq = qae + qr * D, *so = dout + qr * D;
+      const E *sqt = qat + qr * D, *sot = dot + qr * D;   // chunk block [D][64]
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int vi = tid + NTH * i, r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
+        const int rt = vi / (C / 8), ct = 8 * (vi % (C / 8));
+        cq[i] = *reinterpret_cast<const bf16x8 *>(sq + r * D + c8);
+        co[i] = *reinterpret_cast<const bf16x8 *>(so + r * D + c8);
+        cqt[i] = *reinterpret_cast<const bf16x8 *>(sqt + rt * C + ct);
+        cot[i] = *reinterpret_cast<const bf16x8 *>(sot + rt * C + ct);
+      }
+      if (tid < C)
+        cst = make_float4(lse[qr + tid], dvec[qr + tid], dlse ? dlse[qr + tid] : 0.f,
+                          FOX ? lam[qr + tid] : 0.f);
+    }
+  };
+  auto fetch_level = [&](int cc) __attribute__((always_inline)) {
+    if constexpr (BF) {   // rows Khat[cc]_{c'} of this wave's keys, B-operand fragments
+      const E *kl = levels + lev_head + lev_off(cc, cp, D) + (size_t)(32 * kh + col) * D + KPL * g;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) kfr[ks] = MM<E>::ld(kl + 2 * KPL * ks, 1);
+    }
+  };
+  if constexpr (BF) {
+    if (member) {
+      const E *vr = v + (krow + col) * D + KPL * g;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) vfr[ks] = MM<E>::ld(vr + 2 * KPL * ks, 1);
+      if (N - 1 > cp) fetch_level(N - 1);
+    }
+    if (N - 1 >= c_low) fetch_copy(N - 1);
+  }
   for (int c = N - 1; c >= c_low; --c) {
     const bool active = member && c > cp;
     const size_t qrow = head + (size_t)c * C;
     __syncthreads();
-    if constexpr (BF) {   // 16-byte copies of Qa, dO (rows) and Qa^T, dO^T
-      const E *sq = qae + qrow * D, *so = dout + qrow * D;
-      const E *sqt = qat + qrow * D, *sot = dot + qrow * D;   // chunk c block [D][64]
-      for (int vi = tid; vi < C * D / 8; vi += NTH) {
-        const int r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
-        *reinterpret_cast<bf16x8 *>(Qs + r * L::PQ + c8) = *reinterpret_cast<const bf16x8 *>(sq + r * D + c8);
-        *reinterpret_cast<bf16x8 *>(Os + r * L::PQ + c8) = *reinterpret_cast<const bf16x8 *>(so + r * D + c8);
+    if constexpr (BF) {   // the prefetched copies of Qa, dO (rows) and Qa^T, dO^T
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int vi = tid + NTH * i, r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
         const int rt = vi / (C / 8), ct = 8 * (vi % (C / 8));
-        *reinterpret_cast<bf16x8 *>(Qt + rt * L::PQT + ct) = *reinterpret_cast<const bf16x8 *>(sqt + rt * C + ct);
-        *reinterpret_cast<bf16x8 *>(Ot + rt * L::PQT + ct) = *reinterpret_cast<const bf16x8 *>(sot + rt * C + ct);
+        *reinterpret_cast<bf16x8 *>(Qs + r * L::PQ + c8) = cq[i];
+        *reinterpret_cast<bf16x8 *>(Os + r * L::PQ + c8) = co[i];
+        *reinterpret_cast<bf16x8 *>(Qt + rt * L::PQT + ct) = cqt[i];
+        *reinterpret_cast<bf16x8 *>(Ot + rt * L::PQT + ct) = cot[i];
       }
+      if (tid < C) qst[tid] = cst;
     } else {
       for (int idx = tid; idx < C * D; idx += NTH) {
         Qs[(idx / D) * L::PQ + idx % D] = qae[qrow * D + idx];
         Os[(idx / D) * L::PQ + idx % D] = dout[qrow * D + idx];
       }
+      if (tid < C)
+        qst[tid] = make_float4(lse[qrow + tid], dvec[qrow + tid], dlse ? dlse[qrow + tid] : 0.f,
+                               FOX ? lam[qrow + tid] : 0.f);
     }
-    if (tid < C)
-      qst[tid] = make_float4(lse[qrow + tid], dvec[qrow + tid], dlse ? dlse[qrow + tid] : 0.f,
-                             FOX ? lam[qrow + tid] : 0.f);
     __syncthreads();
+    frag kcur[KSD];
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) kcur[ks] = kfr[ks];
+      // next step's operands: level rows first, then the copies
+      if (member && c - 1 > cp) fetch_level(c - 1);
+      if (c - 1 >= c_low) fetch_copy(c - 1);
+    }
     if (active) {
       const E *kl = levels + lev_head + lev_off(c, cp, D) + (size_t)32 * kh * D;   // Khat[c] rows
       f32x16 s[2], dp[2];
@@ -753,8 +810,18 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
       for (int qt = 0; qt < 2; ++qt) {
         zero16(s[qt]);
         zero16(dp[qt]);
-        mma_tile<E, D>(s[qt], Qs + 32 * qt * L::PQ, L::PQ, 1, kl, D, 1, lane);
-        mma_tile<E, D>(dp[qt], Os + 32 * qt * L::PQ, L::PQ, 1, v + krow * D, D, 1, lane);
+        if constexpr (BF) {
+          const E *qa_r = Qs + (32 * qt + col) * L::PQ + KPL * g;
+          const E *do_r = Os + (32 * qt + col) * L::PQ + KPL * g;
+#pragma unroll
+          for (int ks = 0; ks < KSD; ++ks) {
+            s[qt] = MM<E>::mma(MM<E>::ld(qa_r + 2 * KPL * ks, 1), kcur[ks], s[qt]);
+            dp[qt] = MM<E>::mma(MM<E>::ld(do_r + 2 * KPL * ks, 1), vfr[ks], dp[qt]);
+          }
+        } else {
+          mma_tile<E, D>(s[qt], Qs + 32 * qt * L::PQ, L::PQ, 1, kl, D, 1, lane);
+          mma_tile<E, D>(dp[qt], Os + 32 * qt * L::PQ, L::PQ, 1, v + krow * D, D, 1, lane);
+        }
       }
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
