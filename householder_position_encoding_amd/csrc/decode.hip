@@ -163,25 +163,46 @@ __global__ __launch_bounds__(256) void align_prep_kernel(
 
 // ------------------------------------------------------------ prefill: scan
 
-// One block of 4 waves per (bh, slice of 32 columns of G).  Chunk by chunk
+// acc(i, j) += sum_{k < K} A(i, k) B(k, j) for this wave's 16 x 16 output
+// tile on the float32 matrix cores (v_mfma_f32_16x16x4f32: lane l supplies
+// A(l%16, l/16) and B(l/16, l%16) per instruction; result lane l register r
+// holds row 4 (l/16) + r, column l%16), operands in LDS through strides as
+// for lds_mm.
+template <int K>
+__device__ __forceinline__ void lds_mm16(f32x4 &acc, const float *A, int ars, int acs,
+                                         const float *B, int brs, int bcs, int lane) {
+  const int i = lane & 15, k0 = lane >> 4;
+  const float *pa = A + i * ars + k0 * acs;
+  const float *pb = B + k0 * brs + i * bcs;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * acs], pb[k * brs], acc, 0, 0, 0);
+}
+
+// One block of 8 waves per (bh, slice of 16 columns of G).  Chunk by chunk
 // from the last: ->K_c and M_c are staged in LDS (loaded into registers one
-// chunk ahead), the aligned rows ->K_c G_c of this column slice are written
-// (64 x 32: waves 2 and 3), and G <- G - M_c^T G (D x 32: tile t of D/32 on
-// wave t) on the float32 matrix cores; G's slice lives in LDS.
+// chunk ahead); the aligned rows ->K_c G_c of this column slice (64 x 16:
+// four 16 x 16 tiles) are written and G <- G - M_c^T G (D x 16: D/16 tiles)
+// is formed, one 16 x 16 tile per wave at a time, on the float32 matrix
+// cores.  G's slice lives in LDS.  The chain of dependent chunk steps is what
+// bounds the kernel, so the tiles are small: each step costs a wave at most
+// two D-deep chains of 16 x 16 x 4 products.
 template <typename KC, int D>
-__global__ __launch_bounds__(256) void align_scan_kernel(
+__global__ __launch_bounds__(512) void align_scan_kernel(
     const float *__restrict__ kb, const float *__restrict__ m, KC *__restrict__ kcache,
     int L, int T_cap) {
-  constexpr int C = kChunk, NT = 256, DP = D + 1, SP = 33;
-  constexpr int NSL = D / 32;                                  // column slices per head
-  constexpr int NK4 = C * D / 4 / NT, NM4 = D * D / 4 / NT;   // float4 loads per thread
-  constexpr int NGT = D / 32;                                  // tiles of the G update
+  constexpr int C = kChunk, NT = 512, NW = 8, DP = D + 1, SW = 16, SP = SW + 1;
+  constexpr int NSL = D / SW;                                   // column slices per head
+  constexpr int NK4 = C * D / 4 / NT, NM4 = D * D / 4 / NT;    // float4 loads per thread
+  constexpr int NRT = C / 16, NGT = D / 16, NTILE = NRT + NGT;  // row tiles, G tiles
+  constexpr int TPW = (NTILE + NW - 1) / NW;                    // tiles per wave
+  static_assert(C * D % (4 * NT) == 0 && D * D % (4 * NT) == 0, "loads split evenly");
   __shared__ float Ks[C * DP];
   __shared__ float Ms[D * DP];
   __shared__ float Gs[D * SP];
   const int N = L / C;
   const int bh = blockIdx.x / NSL, sl = blockIdx.x % NSL;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, cl = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q4 = lane >> 4, cl = lane & 15;
 
   f32x4 kreg[NK4], mreg[NM4];
   auto fetch = [&](int c) {       // chunk c's ->K and M into registers
@@ -207,9 +228,9 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
     }
   };
 
-  for (int idx = tid; idx < D * 32; idx += NT) {
-    const int a = idx / 32, b = idx % 32;
-    Gs[a * SP + b] = a == 32 * sl + b ? 1.f : 0.f;
+  for (int idx = tid; idx < D * SW; idx += NT) {
+    const int a = idx / SW, b = idx % SW;
+    Gs[a * SP + b] = a == SW * sl + b ? 1.f : 0.f;
   }
   if (N > 0) fetch(N - 1);
   for (int c = N - 1; c >= 0; --c) {
@@ -217,38 +238,33 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
     park();
     __syncthreads();
     if (c > 0) fetch(c - 1);   // in flight while chunk c is computed
-    // aligned rows of chunk c, keys 32 (wv - 2).. (waves 2, 3): (->K_c G_c)[j][col]
-    if (wv >= 2) {
-      const int kh = wv - 2;
-      f32x16 acc;
-      zero16(acc);
-      lds_mm<D>(acc, Ks + 32 * kh * DP, DP, 1, Gs, SP, 1, lane);
-      KC *dst = kcache + ((size_t)bh * T_cap + (size_t)c * C + 32 * kh) * D + 32 * sl + cl;
+    f32x4 gn[TPW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(size_t)acc_row(r, g) * D] = from_f<KC>(acc[r]);
-    }
-    // G <- G - M_c^T G: tile t (rows 32 t..) of the slice
-    f32x16 gn[(NGT + 3) / 4];
-#pragma unroll
-    for (int u = 0; u < (NGT + 3) / 4; ++u) {
-      const int t = wv + 4 * u;
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wv + NW * u;
       if (t < NGT) {
+        // G <- G - M_c^T G, rows 16 t.. of the slice: (M^T G)[a][b] = sum_r M[r][a] G[r][b]
+        f32x4 prod = {0.f, 0.f, 0.f, 0.f};
+        lds_mm16<D>(prod, Ms + 16 * t, 1, DP, Gs, SP, 1, lane);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gn[u][r] = Gs[(32 * t + acc_row(r, g)) * SP + cl];
-        f32x16 prod;
-        zero16(prod);
-        lds_mm<D>(prod, Ms + 32 * t, 1, DP, Gs, SP, 1, lane);   // (M^T G)[a][b] = sum_r M[r][a] G[r][b]
+        for (int r = 0; r < 4; ++r) gn[u][r] = Gs[(16 * t + 4 * q4 + r) * SP + cl] - prod[r];
+      } else if (t < NTILE) {
+        // aligned rows 16 (t - NGT).. of chunk c: (->K_c G_c)[j][col]
+        const int rt = t - NGT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        lds_mm16<D>(acc, Ks + 16 * rt * DP, DP, 1, Gs, SP, 1, lane);
+        KC *dst = kcache + ((size_t)bh * T_cap + (size_t)c * C + 16 * rt + 4 * q4) * D + SW * sl + cl;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gn[u][r] -= prod[r];
+        for (int r = 0; r < 4; ++r) dst[(size_t)r * D] = from_f<KC>(acc[r]);
       }
     }
     __syncthreads();   // all reads of the old G are done
 #pragma unroll
-    for (int u = 0; u < (NGT + 3) / 4; ++u) {
-      const int t = wv + 4 * u;
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wv + NW * u;
       if (t < NGT)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Gs[(32 * t + acc_row(r, g)) * SP + cl] = gn[u][r];
+        for (int r = 0; r < 4; ++r) Gs[(16 * t + 4 * q4 + r) * SP + cl] = gn[u][r];
     }
   }
 }
@@ -633,7 +649,7 @@ hipError_t prefill_t(const void *k, const void *v, const void *w, const float *b
   if (N > 0) {
     hipLaunchKernelGGL((align_prep_kernel<E, D>), dim3(BH * N), dim3(256), 0, stream,
                        (const E *)k, (const E *)w, beta, ws_kb, ws_m, L);
-    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 32)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 16)), dim3(512), 0, stream,
                        ws_kb, ws_m, (KC *)kcache, L, T_cap);
     const int gx = min(1024, (int)(((size_t)L * D + 255) / 256));
     hipLaunchKernelGGL((copy_rows_kernel<E>), dim3(gx, BH), dim3(256), 0, stream, (const E *)v,
