@@ -29,6 +29,8 @@
 // Only the operands handed to the streaming kernel's matrix cores (->K, V,
 // -M^T) are rounded to the storage type, once, at the end.
 #include "path_attn_internal.h"
+#include <algorithm>
+#include <atomic>
 
 namespace pathattn {
 
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const __bf16 *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa,
-    __bf16 *__restrict__ kvm, float *__restrict__ al, int T, FwdIo io) {
+    __bf16 *__restrict__ kvm, float *__restrict__ al, int T, int total, FwdIo io) {
   constexpr int C = kChunk, P = 72, PX = 72;
   constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16, KSD = D / 16, KSC = C / 16;
   constexpr int TPW = D / 64;                       // d x 64 tiles per wave
@@ -226,14 +228,13 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   constexpr int SLOT = 2 * PLANE;                   // 18432 B: hi/lo planes or 64 x 72 fp32
   constexpr int WT_BYTES = D * P * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[3 * SLOT + WT_BYTES + C * 4];
-  // slot 0: N / X (fp32), then U (hi/lo), then T2^T (hi/lo)
+  // slot 0: N / X (fp32), then T2^T (hi/lo)
   // slot 1: lower(Q W^T) (hi/lo)
   // slot 2: strictLower(W K^T)^T (hi/lo), then (U W)^T (hi/lo) for 64 of the
   // d columns at a time (d = 128: two halves, the second kept in registers
   // meanwhile, so that two blocks fit a CU)
   float *Xs = reinterpret_cast<float *>(smem);
-  __bf16 *Uh = reinterpret_cast<__bf16 *>(smem), *Ul = Uh + C * P;
-  __bf16 *T2h = Uh, *T2l = Ul;
+  __bf16 *T2h = reinterpret_cast<__bf16 *>(smem), *T2l = T2h + C * P;
   __bf16 *P1h = reinterpret_cast<__bf16 *>(smem + SLOT), *P1l = P1h + C * P;
   __bf16 *SKh = reinterpret_cast<__bf16 *>(smem + 2 * SLOT), *SKl = SKh + C * P;
   __bf16 *UWh = SKh, *UWl = UWh + C * P;
@@ -241,18 +242,70 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   float *bs = reinterpret_cast<float *>(smem + 3 * SLOT + WT_BYTES);
 
   const int N = T / C;
-  const int bh = blockIdx.x / N, c = blockIdx.x % N;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int sq = (int)io.q.t, sk = (int)io.k.t, sv = (int)io.v.t, sw = (int)io.w.t;
+  // the first row of chunk c of head bh in a tensor with token strides st
+  auto first_of = [&](int bh, int c, const TokStrides &st) {
+    return (long long)(bh / io.H) * st.b + (long long)(bh % io.H) * st.h + (long long)c * C * st.t;
+  };
+
+  // d = 64: q, k, v, w of a chunk (32 KiB) are staged in slots 0 and 1, rows
+  // swizzled as in sw_off, and every wave reads its operands from there.  The
+  // blocks are persistent: each walks chunks blockIdx.x, + gridDim.x, ... and
+  // holds the next chunk's inputs (eight 16-byte pieces and beta per thread)
+  // in registers while the current chunk is computed, so the load latency is
+  // paid once per block.  Piece i of a thread is tensor i / 2 (q, k, v, w),
+  // rows 8 ch.. with ch = wv + 4 (i % 2), column piece cc of row r at slot
+  // cc ^ (r % 8).  d = 128 reads its operands from global memory, one chunk
+  // per block.
+  constexpr bool STAGE = D == 64;
+  bf16x8 pre[8];
+  float bpre = 0.f;
+  auto fetch = [&](int blk) {
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int fbh = blk / N, fc = blk % N;
+    const __bf16 *src[4] = {q + first_of(fbh, fc, io.q), k + first_of(fbh, fc, io.k),
+                            v + first_of(fbh, fc, io.v), w + first_of(fbh, fc, io.w)};
+    const int pitch[4] = {sq, sk, sv, sw};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = i >> 1, ch = wv + 4 * (i & 1);
+      const int r = 8 * ch + (lane >> 3), cc = (lane & 7) ^ (r & 7);
+      pre[i] = *reinterpret_cast<const bf16x8 *>(src[t] + (long long)r * pitch[t] + cc * 8);
+    }
+    bpre = tid < C ? beta[first_of(fbh, fc, io.beta) + (long long)tid * io.beta.t] : 0.f;
+  };
+  if constexpr (STAGE) fetch(blockIdx.x);
+
+  const int blk_end = STAGE ? total : (int)blockIdx.x + 1;   // d = 128: one chunk per block
+  for (int blk = blockIdx.x; blk < blk_end; blk += gridDim.x) {
+  // The thread index is taken afresh in each chunk (through an empty asm the
+  // compiler cannot move out of the loop), so that the many addresses derived
+  // from it are not hoisted and kept live across the loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wv = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, n = lane & 31;
   const int mt = wv >> 1, nt = wv & 1;
-  // the chunk's first row of each input, and the rows' pitch (elements)
-  const long long hb = bh / io.H, hh = bh % io.H;
-  auto first = [&](const TokStrides &st) { return hb * st.b + hh * st.h + (long long)c * C * st.t; };
+  const int bh = blk / N, c = blk % N;
+  auto first = [&](const TokStrides &st) { return first_of(bh, c, st); };
+  float bval;
+  if constexpr (STAGE) {
+    __syncthreads();   // the previous chunk's reads of slots 0 and 1 are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = i >> 1, ch = wv + 4 * (i & 1);
+      *reinterpret_cast<bf16x8 *>(smem + (t >> 1) * SLOT + (t & 1) * 8192 + ch * 1024 + lane * 16) =
+          pre[i];
+    }
+    bval = bpre;
+    if (blk + (int)gridDim.x < total) fetch(blk + gridDim.x);
+  } else {
+    bval = tid < C ? beta[first(io.beta) + (long long)tid * io.beta.t] : 0.f;
+  }
   const __bf16 *qc = q + first(io.q);
   const __bf16 *kc = k + first(io.k);
   const __bf16 *vc = v + first(io.v);
   const __bf16 *wc = w + first(io.w);
-  const int sq = (int)io.q.t, sk = (int)io.k.t, sv = (int)io.v.t, sw = (int)io.w.t;
   __bf16 *kf = kvm + ((size_t)bh * N + c) * kvm_elems(D, DP);
   __bf16 *vf = kf + C * D;
   __bf16 *mf = vf + C * D;
@@ -262,28 +315,9 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   // them, so their latencies overlap.
   f32x16 kq = zero16();
   f32x16 qinit[TPW], kinit[TPW];
-  // d = 64: q, k, v, w of the chunk (32 KiB) are copied once into slots 0
-  // and 1 (direct global-to-LDS copies, 8 per wave, rows swizzled as in
-  // sw_off) and every wave reads its operands from there; the slots are
-  // overwritten only after the barrier below.  d = 128 reads from global.
-  constexpr bool STAGE = D == 64;
   const unsigned char *st_q = smem, *st_k = smem + 8192;
   const unsigned char *st_v = smem + SLOT, *st_w = smem + SLOT + 8192;
-  if constexpr (STAGE) {
-    const __bf16 *src[4] = {qc, kc, vc, wc};
-    const int pitch[4] = {sq, sk, sv, sw};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int job = wv + 4 * i, t = job >> 3, ch = job & 7;   // tensor, 8-row chunk
-      const int r = 8 * ch + (lane >> 3), cc = (lane & 7) ^ (r & 7);
-      unsigned char *dst = smem + (t >> 1) * SLOT + (t & 1) * 8192 + ch * 1024;
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void *)(src[t] + (long long)r * pitch[t] + cc * 8),
-          (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-    }
-  }
   {
-    const float bval = tid < C ? beta[first(io.beta) + (long long)tid * io.beta.t] : 0.f;
     bf16x8 wm[KSD], wn[KSD], qn[KSD], kn[KSD], km[KSD];
     // <-Q^T and ->K^T start from Q^T and K^T: tiles (eb, xb) = (tau>>1, tau&1)
     bf16x4 qv[TPW][4], kv[TPW][4];
@@ -432,45 +466,43 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
   __syncthreads();
   if (wv == 0) solve_block<PX>(Xs, 3, 0, lane);            // block (3,0)
   __syncthreads();
-  {
-    // U[i][j] = X[i][j] beta_j (j < i), beta_i (j == i), 0 (j > i); four
-    // contiguous j per item, consecutive lanes on consecutive rows i (so the
-    // transposed reads of X are conflict-free); read everything before
-    // overwriting the slot.
-    f32x4 uv[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it, i = item & 63, j0 = 4 * (item >> 6);
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if ((j0 >> 4) == (i >> 4)) {
-        x = *reinterpret_cast<const f32x4 *>(Xs + i * PX + j0);
-      } else if ((j0 >> 4) < (i >> 4)) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = Xs[(j0 + e) * PX + i];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + e;
-        uv[it][e] = j < i ? x[e] * bs[j] : (j == i ? bs[j] : 0.f);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it, i = item & 63, j0 = 4 * (item >> 6);
-      store4_split(Uh, Ul, i * P + j0, uv[it]);
-    }
-  }
-  __syncthreads();
-
   // ---- phase 3: T2 = U strictLower(W K^T) and U W, stored transposed ----
   // uw[u] holds (U W)^T tile (e block nt + 2u, s block mt): u = 0 is the
   // first 64 d columns, u = 1 (d = 128) the second.
   f32x16 uw[TPW];
   {
+    // This wave's A fragments of U = X D as hi/lo pairs, straight from X:
+    // U[i][s] = X[i][s] beta_s (s < i), beta_i (s == i), 0 (s > i).  Lane l
+    // takes row i = 32 mt + l%32 and the 8 columns s0.. = 8 (l/32) + 16 ks,
+    // which lie in one 16-block: the diagonal block of X is stored in rows,
+    // the blocks below it transposed.
     bf16x8 uh[KSC], ul[KSC];
-    load_rows<KSC>(uh, Uh + 32 * mt * P, P, lane);
-    load_rows<KSC>(ul, Ul + 32 * mt * P, P, lane);
+    {
+      const int i = 32 * mt + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        const int s0 = 8 * (lane >> 5) + 16 * ks;
+        const bool diag = (s0 >> 4) == (i >> 4);
+        const f32x4 r0 = *reinterpret_cast<const f32x4 *>(Xs + i * PX + s0);
+        const f32x4 r1 = *reinterpret_cast<const f32x4 *>(Xs + i * PX + s0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bs + s0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bs + s0 + 4);
+        float xt[8];   // read whether used or not: no branch per element
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xt[t] = Xs[(s0 + t) * PX + i];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int sc = s0 + t;
+          const float xr = t < 4 ? r0[t] : r1[t - 4];
+          const float x = diag ? xr : xt[t];
+          const float b = t < 4 ? b0[t] : b1[t - 4];
+          const float u = sc < i ? x * b : (sc == i ? b : 0.f);
+          const __bf16 h = (__bf16)u;
+          uh[ks][t] = h;
+          ul[ks][t] = (__bf16)(u - (float)h);
+        }
+      }
+    }
     f32x16 t2 = zero16();
     {
       bf16x8 sh[KSC], sl[KSC];
@@ -489,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
       mma_rows<KSC>(uw[u], uh, wt);
       mma_rows<KSC>(uw[u], ul, wt);
     }
-    __syncthreads();   // U and strictLower(W K^T)^T are dead
+    __syncthreads();   // X and strictLower(W K^T)^T are dead
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int s0 = 32 * mt + 8 * r4 + 4 * g;
@@ -580,6 +612,7 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
       *reinterpret_cast<f32x4 *>(dst + 4 * r4) = x;
     }
   }
+  }   // chunks of this block
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -794,15 +827,43 @@ __global__ __launch_bounds__(256) void unpack_kernel(
   }
 }
 
+// Compute units of the device that a stream runs on, cached per device.
+hipError_t cu_count(hipStream_t stream, int *out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  int c = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (c <= 0) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    c = c > 0 ? c : 1;
+    if (cached) cache[dev].store(c, std::memory_order_relaxed);
+  }
+  *out = c;
+  return hipSuccess;
+}
+
 template <int D, int DP>
 hipError_t launch_prep_bf16(const void *q, const void *k, const void *v,
                             const void *w, const float *beta, float *qa,
                             void *kvm, float *al, int BH, int T, const FwdIo &io,
                             hipStream_t stream) {
-  hipLaunchKernelGGL((prep_bf16_kernel<D, DP>), dim3(BH * (T / kChunk)), dim3(256), 0,
+  const int total = BH * (T / kChunk);
+  // d = 64: persistent blocks, two per compute unit (the LDS of one block is
+  // 63 KiB), each walking total / grid chunks.
+  int grid = total;
+  if (D == 64) {
+    int cus = 0;
+    const hipError_t e = cu_count(stream, &cus);
+    if (e != hipSuccess) return e;
+    grid = std::min(total, 2 * cus);
+  }
+  hipLaunchKernelGGL((prep_bf16_kernel<D, DP>), dim3(grid), dim3(256), 0,
                      stream, (const __bf16 *)q, (const __bf16 *)k,
                      (const __bf16 *)v, (const __bf16 *)w, beta, qa,
-                     (__bf16 *)kvm, al, T, io);
+                     (__bf16 *)kvm, al, T, total, io);
   return hipGetLastError();
 }
 
