@@ -203,7 +203,10 @@ def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
 
 def bench_backward(wl, q, k, v, w, beta, logf, out, lse, args):
     """path_attn_bwd over the whole workload (inputs, forward outputs and
-    cotangents resident in HBM, workspace preallocated)."""
+    cotangents resident in HBM, workspace preallocated): with the smallest
+    workspace (the default: the sweep in windows of 16 query chunks past 33
+    chunks) and, in "one_window", with the workspace of a single window
+    (every key level stored; faster, T^2 memory)."""
     import torch
     import householder_position_encoding_amd as pa
     import workloads
@@ -211,30 +214,41 @@ def bench_backward(wl, q, k, v, w, beta, logf, out, lse, args):
     dout = torch.from_numpy(cot["dout"]).to(q.device, q.dtype)
     dlse = torch.from_numpy(cot["dlse"]).to(q.device)
     dt_code = pa.BF16 if wl.dtype == "bf16" else pa.F32
-    ws = torch.empty(pa.path_attn_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.d, dt_code),
-                     dtype=torch.uint8, device=q.device)
-    fn = lambda: pa.path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, workspace=ws)
-    stream = torch.cuda.current_stream()
-    fn()
-    torch.cuda.synchronize()
-    n = max(1, args.backward_steps)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(n):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / n
     flops = float(wl.B * wl.H) * wl.T * wl.T * (5 * wl.d + 3 * wl.d * wl.d / 64.0)
-    tf = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    stream = torch.cuda.current_stream()
+    n = max(1, args.backward_steps)
+
+    def run(nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        fn = lambda: pa.path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, workspace=ws)
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del ws
+        torch.cuda.empty_cache()
+        return a.elapsed_time(b) / n
+
+    small = pa.path_attn_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.d, dt_code)
+    ms = run(small)
+    tf = flops / (ms * 1e-3) / 1e12
     res = {"ms": ms, "steps": n, "tokens_per_s": wl.n_tokens / (ms * 1e-3),
-           "workspace_gib": ws.numel() / 2**30,
+           "workspace_gib": small / 2**30,
            "roofline": {"kernel": "path_attn_bwd (whole call)", "bound": "mfma", "achieved": tf,
                         "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
                         "flops_per_call": flops}}
-    del ws
-    torch.cuda.empty_cache()
+    big = pa.path_attn_bwd_workspace_bytes_window(wl.B, wl.H, wl.T, wl.d, dt_code, 0)
+    if big > small:
+        free, _ = torch.cuda.mem_get_info()
+        if big < 0.8 * free:
+            ms1 = run(big)
+            res["one_window"] = {"ms": ms1, "workspace_gib": big / 2**30,
+                                 "frac": flops / (ms1 * 1e-3) / 1e12 / peak}
     return res
 
 

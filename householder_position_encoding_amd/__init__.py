@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     path_attn_bwd_varlen,
     path_attn_bwd_varlen_workspace_bytes,
     path_attn_bwd_workspace_bytes,
+    path_attn_bwd_workspace_bytes_window,
     path_attn_chunk_prep,
     path_attn_decode_step,
     path_attn_fwd,
@@ -39,6 +40,7 @@ __all__ = [
     "BF16", "DecodeCache", "F32", "NOALLOC_MAX_BYTES", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
     "load_library", "path_attn_bwd", "path_attn_bwd_varlen",
     "path_attn_bwd_varlen_workspace_bytes", "path_attn_bwd_workspace_bytes",
+    "path_attn_bwd_workspace_bytes_window",
     "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_noalloc", "path_attn_fwd_partial",
     "path_attn_fwd_varlen",
     "path_attn_prefill_cache", "path_attn_prepare", "path_attn_stream",

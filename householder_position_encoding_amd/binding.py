@@ -82,6 +82,8 @@ def load_library():
     lib.path_attn_decode_step.restype = ci
     lib.path_attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.path_attn_bwd_workspace_bytes.restype = sz
+    lib.path_attn_bwd_workspace_bytes_window.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.path_attn_bwd_workspace_bytes_window.restype = sz
     lib.path_attn_bwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
                                   fp, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_bwd.restype = ci
@@ -442,12 +444,20 @@ def path_attn_bwd_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) ->
     return int(load_library().path_attn_bwd_workspace_bytes(B, H, T, d, dtype))
 
 
+def path_attn_bwd_workspace_bytes_window(B: int, H: int, T: int, d: int, dtype: int,
+                                         window: int) -> int:
+    return int(load_library().path_attn_bwd_workspace_bytes_window(B, H, T, d, dtype, window))
+
+
 def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, window=None):
     """Gradients of <dout, out> + <dlse, lse> for the forward of path_attn_fwd
     (out, lse: that forward's outputs).  Returns (dq, dk, dv, dw, dbeta,
     dlogf); dlogf is None without the gate.  Any T >= 1 (padded inside the
-    library as in the forward)."""
+    library as in the forward).  Without a workspace, one of the smallest
+    size is allocated, or with window given the size of
+    path_attn_bwd_workspace_bytes_window (0: the whole sweep as one window,
+    the fastest); a larger workspace selects longer windows."""
     torch = _torch()
     B, H, T, d, dt = _common(q, k, v, w, beta, logf)
     _check(out, "out", q.shape, q.dtype, q.device)
@@ -459,7 +469,10 @@ def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
     dq, dk, dv, dw = (torch.empty_like(q) for _ in range(4))
     dbeta = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     dlogf = None if logf is None else torch.empty_like(dbeta)
-    need = lib.path_attn_bwd_workspace_bytes(B, H, T, d, dt)
+    if window is None:
+        need = lib.path_attn_bwd_workspace_bytes(B, H, T, d, dt)
+    else:
+        need = lib.path_attn_bwd_workspace_bytes_window(B, H, T, d, dt, int(window))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib.path_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),

@@ -492,12 +492,14 @@ namespace {
 struct BwdFull {
   size_t vec[10], sca[6], total;
   bool staged;
+  int window;
 };
 
-BwdFull bwd_full(int B, int H, int T, int d, int dtype, bool views = false) {
+BwdFull bwd_full(int B, int H, int T, int d, int dtype, bool views, int window) {
   const int Tp = padded(T);
   BwdFull F{};
-  size_t off = bwd_layout(B, H, Tp, d, dtype).total;
+  F.window = window;
+  size_t off = bwd_layout(B, H, Tp, d, dtype, window).total;
   F.staged = views || Tp != T;
   if (F.staged) {
     const size_t rows = (size_t)B * H * Tp;
@@ -512,6 +514,23 @@ BwdFull bwd_full(int B, int H, int T, int d, int dtype, bool views = false) {
   }
   F.total = off;
   return F;
+}
+
+// The layout for a workspace of `bytes`: the sweep in one window when that
+// fits, else in the longest windows of 128, 64, 32 or 16 query chunks that
+// fit (total = 0 when not even the default fits).
+BwdFull bwd_fit(int B, int H, int T, int d, int dtype, bool views, size_t bytes) {
+  const int nq = padded(T) / kChunk - 1 > 1 ? padded(T) / kChunk - 1 : 1;
+  const int cand[] = {nq, 128, 64, 32, kBwdWindowMin};
+  for (int w : cand) {
+    if (w > nq) continue;
+    const BwdFull F = bwd_full(B, H, T, d, dtype, views, w);
+    if (F.total <= bytes) return F;
+  }
+  const BwdFull F = bwd_full(B, H, T, d, dtype, views, 0);
+  if (F.total <= bytes) return F;
+  BwdFull none{};
+  return none;
 }
 
 // Everything after argument checks: stage (gather) the inputs when staged,
@@ -546,6 +565,7 @@ int run_bwd(const void *q, const void *k, const void *v, const void *w, const fl
   a.H = H;
   a.T = Tp;
   a.scale = scale_of(scale, d);
+  a.window = F.window;
   const int e = (int)elem_size(dtype), row = d * e;
   if (F.staged) {   // gather the inputs at the padded length
     const void *vin[] = {q, k, v, w, out, dout};
@@ -593,12 +613,19 @@ int run_bwd(const void *q, const void *k, const void *v, const void *w, const fl
 
 extern "C" size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
   if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
-  return bwd_full(B, H, T, d, dtype).total;
+  return bwd_full(B, H, T, d, dtype, false, 0).total;
+}
+
+extern "C" size_t path_attn_bwd_workspace_bytes_window(int B, int H, int T, int d, int dtype,
+                                                       int window) {
+  if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
+  const int nq = padded(T) / kChunk - 1 > 1 ? padded(T) / kChunk - 1 : 1;
+  return bwd_full(B, H, T, d, dtype, false, window > 0 ? window : nq).total;
 }
 
 extern "C" size_t path_attn_bwd_varlen_workspace_bytes(int B, int H, int T, int d, int dtype) {
   if (check_shape(B, H, T, d, dtype) != PATH_ATTN_OK) return 0;
-  return bwd_full(B, H, T, d, dtype, true).total;
+  return bwd_full(B, H, T, d, dtype, true, 0).total;
 }
 
 extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
@@ -617,8 +644,8 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   const void *all[] = {q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf};
   for (const void *p : all)
     if (p && !aligned(p, 16)) return PATH_ATTN_EINVAL;
-  const BwdFull F = bwd_full(B, H, T, d, dtype);
-  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
+  const BwdFull F = bwd_fit(B, H, T, d, dtype, false, workspace_bytes);
+  if (!aligned(workspace, 256) || F.total == 0) return PATH_ATTN_EINVAL;
   RowView views[16];
   for (int i = 0; i < 16; ++i) views[i] = dense_view(H, T, i < 10 ? d : 1);
   return run_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf, B,
@@ -647,8 +674,8 @@ extern "C" int path_attn_bwd_varlen(const void *q, const void *k, const void *v,
   const size_t e = elem_size(dtype);
   for (int i = 0; i < 16; ++i)
     if (!view_ok(all[i], strides + 3 * i, i < 10 ? e : 4)) return PATH_ATTN_EINVAL;
-  const BwdFull F = bwd_full(B, H, T, d, dtype, true);
-  if (!aligned(workspace, 256) || workspace_bytes < F.total) return PATH_ATTN_EINVAL;
+  const BwdFull F = bwd_fit(B, H, T, d, dtype, true, workspace_bytes);
+  if (!aligned(workspace, 256) || F.total == 0) return PATH_ATTN_EINVAL;
   RowView views[16];
   for (int i = 0; i < 16; ++i) views[i] = make_view(strides + 3 * i, cu_seqlens);
   return run_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf, B,

@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void bwd_gate_grad_kernel(const float *__restr
 
 }  // namespace
 
-BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
+BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   const size_t BH = (size_t)B * H, N = (size_t)T / C;
   const size_t esize = dtype == 1 ? 2 : 4;
   BwdLayout L;
@@ -495,13 +495,24 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
     off = align256(off + floats * sizeof(float));
     return o;
   };
+  const BwdPlan P = bwd_plan(T, window);
+  const bool img = dtype == 1 && D == 64;   // bf16, d = 64: operand images, no transposed levels
+  const size_t lev_elems = BH * P.win_blocks * C * D;
   L.kb = take(BH * T * D);
   L.m = take(BH * N * D * D);
   L.al = take(BH * N * C * C);
   L.lam = take(BH * T);
   L.dvec = take(BH * T);
-  L.levels = take((bwd_levels_elems((int)BH, T, D) * esize + 3) / 4);
-  L.dmpart = take(bwd_dmpart_floats(dtype, (int)BH, T, D));
+  // the sweep's buffers, whose bytes the adjoint scratch reuses afterwards
+  const size_t sweep0 = off;
+  L.levels = take((lev_elems * esize + 3) / 4);
+  L.levt = take(img ? 0 : (lev_elems * esize + 3) / 4);
+  L.dmpart = take(bwd_dmpart_floats(dtype, (int)BH, T, D, window));
+  L.ckpt = take(BH * P.ckpt_blocks * C * D);
+  L.gstate = take(P.nwin > 1 ? BH * T * D : 0);
+  const size_t adj_bytes = align256(BH * N * adj_floats(D) * sizeof(float));
+  L.adj = sweep0;
+  off = sweep0 + (off - sweep0 > adj_bytes ? off - sweep0 : adj_bytes);
   L.dv = take(BH * T * D);
   L.dlam = take(BH * T);
   L.dqa = take(BH * T * D);
@@ -516,20 +527,17 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype) {
   L.nm = take_e(BH * N * D * D);
   L.nmt = take_e(general ? BH * N * D * D : 0);
   L.dot = take_e(general ? BH * T * D : 0);
-  const bool img = dtype == 1 && D == 64;   // bf16, d = 64: operand images, no transposed levels
-  L.levt = take_e(img ? 0 : bwd_levels_elems((int)BH, T, D));
   L.qimg = take_e(img ? BH * N * kQImgElems : 0);
   L.oimg = take_e(img ? BH * N * kQImgElems : 0);
   L.mimg = take_e(img ? BH * N * kMImgElems : 0);
   L.qst = take(img ? BH * T * 4 : 0);
-  L.adj = take(BH * N * adj_floats(D));
   L.total = off;
   return L;
 }
 
 template <typename E, int D, bool FOX>
 hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
-  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D, dtype);
+  const BwdLayout L = bwd_layout(a.B, a.H, a.T, D, dtype, a.window);
   const int BH = a.B * a.H, T = a.T, N = T / C;
   auto f = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
   const E *q = (const E *)a.q, *k = (const E *)a.k, *v = (const E *)a.v, *w = (const E *)a.w;
@@ -568,9 +576,12 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.dv = f(L.dv);
   sa.dlam = f(L.dlam);
   sa.dm = f(L.dm);
+  sa.ckpt = f(L.ckpt);
+  sa.gstate = f(L.gstate);
   sa.scale = a.scale;
   sa.BH = BH;
   sa.T = T;
+  sa.window = a.window;
   if (launch_bwd_sweep(dtype, D, FOX, sa, s) != hipSuccess) return hipGetLastError();
   hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
                      f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.saved), f(L.adj), (E *)a.dq,

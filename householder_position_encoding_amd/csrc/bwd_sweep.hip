@@ -148,49 +148,99 @@ __host__ __device__ inline size_t lev_off(int c, int cp, int D) {
   return ((size_t)c * (c - 1) / 2 + cp) * (size_t)C * D;
 }
 
-// float32 inputs: each wave walks the levels of 32 keys of one key chunk
-// c' < N-1 (blocks of 2 waves, one per key half) and stores level c in rows
-// [64 keys][D] and transposed [D][64 keys] (both at lev_off(c, c')).  The
-// product takes -M_c straight from global memory (shared by every block of
-// the head) and the rounded level from its LDS copy; the row layout is
-// written from that copy too.
+// One window of query chunks [lo, hi): its level buffer holds Khat[c]_{c'}
+// for c in [lo - 1, hi), c' < c, at lev_off(c, c') - base in each head's
+// slice of `head` elements.
+struct Win {
+  int lo, hi;
+  size_t base, head;
+};
+__device__ __forceinline__ size_t lev_at(const Win &w, int bh, int c, int cp, int D) {
+  return (size_t)bh * w.head + lev_off(c, cp, D) - w.base;
+}
+// Float32 level checkpoints: level k W of key chunk c' < k W (k = 1 .. nwin-2,
+// the levels lo - 1 of the windows between the first and the last) at block
+// W k (k-1) / 2 + c' of each head's slice of `head` floats.
+struct Ckpt {
+  float *p;
+  size_t head;
+  int W;
+};
+__device__ __forceinline__ float *ck_at(const Ckpt &k, int bh, int c, int cp, int D) {
+  const int kk = c / k.W;
+  return k.p + (size_t)bh * k.head + ((size_t)k.W * kk * (kk - 1) / 2 + cp) * (size_t)C * D;
+}
+// A wave's 32 x D running level (tiles t, rows acc_row) to or from a checkpoint.
+template <int D>
+__device__ __forceinline__ void ck_store(float *dst, const f32x16 (&x)[D / 32], int lane) {
+  const int g = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[acc_row(r, g) * D + 32 * t + col] = x[t][r];
+}
+template <int D>
+__device__ __forceinline__ void ck_load(f32x16 (&x)[D / 32], const float *src, int lane) {
+  const int g = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
+}
+
+// float32 inputs: each wave walks the levels of 32 keys of one key chunk c'
+// (blocks of 2 waves, one per key half) and stores level c in rows [64
+// keys][D] and transposed [D][64 keys] (both at lev_at(c, c')).  The product
+// takes -M_c straight from global memory (shared by every block of the head)
+// and the level from its LDS copy; the row layout is written from that copy
+// too.  Window pass (ck_pass = 0): levels [max(lo - 1, c' + 1), hi), from the
+// checkpoint at lo - 1 when c' < lo - 1.  First pass (ck_pass = 1, with the
+// last window): the whole walk [c' + 1, hi), storing the checkpoint levels
+// below the window and the window's levels.
 template <int D>
 __global__ __launch_bounds__(128) void levels_f32_kernel(const float *__restrict__ kb,
                                                          const float *__restrict__ nm,
                                                          float *__restrict__ levels,
-                                                         float *__restrict__ levt, int T, int BH) {
+                                                         float *__restrict__ levt, int T, int BH,
+                                                         Win win, Ckpt ck, int ck_pass) {
   using E = float;
   constexpr int EPV = 4;            // elements per 16-byte vector
   constexpr int P = D + EPV;        // rows stay 16-byte aligned
   __shared__ __attribute__((aligned(16))) E Xs[2 * 32 * P];
   const int N = T / C;
   const int cp = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   E *Xw = Xs + wv * 32 * P;
   f32x16 x[D / 32];
-  const float *src = kb + ((size_t)bh * T + (size_t)cp * C + 32 * wv) * D;
+  const bool from_ck = !ck_pass && cp < win.lo - 1;
+  const int c0 = from_ck ? win.lo - 1 : cp + 1;
+  const int c_end = win.hi;
+  if (from_ck)
+    ck_load<D>(x, ck_at(ck, bh, win.lo - 1, cp, D) + (size_t)32 * wv * D, lane);
+  else
+    ck_load<D>(x, kb + ((size_t)bh * T + (size_t)cp * C + 32 * wv) * D, lane);
+  for (int c = c0; c < c_end; ++c) {
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+    for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
+    const bool in_win = c >= win.lo - 1;
+    if (!in_win) {   // first pass below the window: checkpoints only
+      if (c % ck.W == 0) ck_store<D>(ck_at(ck, bh, c, cp, D) + (size_t)32 * wv * D, x, lane);
+    } else {
+      const size_t off = lev_at(win, bh, c, cp, D);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
-  const size_t head = (size_t)bh * lev_off(N, 0, D);
-  for (int c = cp + 1; c < N; ++c) {
-    const size_t off = head + lev_off(c, cp, D);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
-      st_tile(Xw + 32 * t, P, 1, x[t], lane);
+      for (int t = 0; t < D / 32; ++t) st_tile(levt + off + (size_t)32 * t * C + 32 * wv, 1, C, x[t], lane);
     }
     wave_sync();
-    // level rows from the LDS copy, 16 bytes per lane
-    E *dst = levels + off + (size_t)32 * wv * D;
+    if (in_win) {   // level rows from the LDS copy, 16 bytes per lane
+      E *dst = levels + lev_at(win, bh, c, cp, D) + (size_t)32 * wv * D;
 #pragma unroll
-    for (int j = 0; j < 32 * D / EPV / 64; ++j) {
-      const int vi = j * 64 + lane, row = vi / (D / EPV), c16 = EPV * (vi % (D / EPV));
-      *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
-          *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+      for (int j = 0; j < 32 * D / EPV / 64; ++j) {
+        const int vi = j * 64 + lane, row = vi / (D / EPV), c16 = EPV * (vi % (D / EPV));
+        *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
+            *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+      }
     }
-    if (c + 1 < N) {   // Khat[c+1] = Khat[c] + Khat[c] (-M_c)^T
+    if (c + 1 < c_end) {   // Khat[c+1] = Khat[c] + Khat[c] (-M_c)^T
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
         mma_tile<E, D>(x[t], Xw, P, 1, nm + ((size_t)bh * N + c) * D * D + (size_t)32 * t * D, D,
@@ -221,7 +271,8 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
                                                             const __bf16 *__restrict__ nm,
                                                             __bf16 *__restrict__ levels,
                                                             __bf16 *__restrict__ levt, int T,
-                                                            int BH) {
+                                                            int BH, Win win, Ckpt ck,
+                                                            int ck_pass) {
   using E = __bf16;
   constexpr int G = 4, P = D + 8, WARM = G - 1;
   constexpr bool WT = D != 64;            // transposed copy
@@ -238,16 +289,18 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
   // the wave index as a scalar: member-dependent branches stay wave-uniform
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = wv & 1, cp = G * grp + (wv >> 1);
-  const bool member = cp < N - 1;   // key chunk N-1 has no level beyond its own
-  const int c_lo = G * grp + 1;
+  // levels [c_lo, c_end): the window's (from its checkpoint at lo - 1 for
+  // chunks below it), or in the first pass (the last window) every level,
+  // storing the checkpoints below the window
+  const int c_end = win.hi;
+  const bool member = cp < c_end - 1;   // a level of this chunk lies in the range
+  const int c_lo = ck_pass ? G * grp + 1 : max(win.lo - 1, G * grp + 1);
   E *Xw = Xs + wv * 32 * P;
   f32x16 x[D / 32];
-  const float *src = kb + ((size_t)bh * T + (size_t)(member ? cp : 0) * C + 32 * kh) * D;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[t][r] = src[acc_row(r, g) * D + 32 * t + col];
-  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
+  if (member && !ck_pass && cp < win.lo - 1)
+    ck_load<D>(x, ck_at(ck, bh, win.lo - 1, cp, D) + (size_t)32 * kh * D, lane);
+  else
+    ck_load<D>(x, kb + ((size_t)bh * T + (size_t)(member ? cp : 0) * C + 32 * kh) * D, lane);
   const E *nmh = nm + (size_t)bh * N * D * D;
   // piece i of this wave: row pr(i) of -M_c, 16-byte piece pp(i) of the row
   auto pr = [&](int i) __attribute__((always_inline)) { return ((wv * NP + i) * 64 + lane) / (D / 8); };
@@ -271,21 +324,28 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
     const int b = (c - c_lo) & 1;
     __syncthreads();
     if (active) {
-      const size_t off = lev_head + lev_off(c, cp, D);
+      if (c < win.lo - 1) {   // first pass below the window: checkpoints only
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        if constexpr (WT) st_tile(levt + off + (size_t)32 * t * C + 32 * kh, 1, C, x[t], lane);
-        st_tile(Xw + 32 * t, P, 1, x[t], lane);
-      }
-      wave_sync();
-      E *dst = levels + off + (size_t)32 * kh * D;
+        for (int t = 0; t < D / 32; ++t) st_tile(Xw + 32 * t, P, 1, x[t], lane);
+        if (c % ck.W == 0) ck_store<D>(ck_at(ck, bh, c, cp, D) + (size_t)32 * kh * D, x, lane);
+        wave_sync();
+      } else {
+        const size_t off = lev_at(win, bh, c, cp, D);
 #pragma unroll
-      for (int j = 0; j < RV; ++j) {
-        const int vi = j * 64 + lane, row = vi / (D / 8), c16 = 8 * (vi % (D / 8));
-        *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
-            *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+        for (int t = 0; t < D / 32; ++t) {
+          if constexpr (WT) st_tile(levt + off + (size_t)32 * t * C + 32 * kh, 1, C, x[t], lane);
+          st_tile(Xw + 32 * t, P, 1, x[t], lane);
+        }
+        wave_sync();
+        E *dst = levels + off + (size_t)32 * kh * D;
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+          const int vi = j * 64 + lane, row = vi / (D / 8), c16 = 8 * (vi % (D / 8));
+          *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
+              *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+        }
       }
-      if (c + 1 < N) {   // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
+      if (c + 1 < c_end) {   // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
         const E *pa = Xw + col * P + 8 * g;
         const unsigned char *mb = reinterpret_cast<const unsigned char *>(ring[b]);
 #pragma unroll
@@ -313,18 +373,18 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
   // warm-up: chunk c' = c_lo - 1 + j starts at level c_lo + j (register sets
   // named at compile time, so that both stay in registers)
   static_assert(WARM == 3, "three warm-up levels");
-  if (c_lo < N) level(c_lo, member && c_lo > cp, na);
-  if (c_lo + 1 < N) level(c_lo + 1, member && c_lo + 1 > cp, nb);
-  if (c_lo + 2 < N) level(c_lo + 2, member && c_lo + 2 > cp, na);
+  if (c_lo < c_end) level(c_lo, member && c_lo > cp, na);
+  if (c_lo + 1 < c_end) level(c_lo + 1, member && c_lo + 1 > cp, nb);
+  if (c_lo + 2 < c_end) level(c_lo + 2, member && c_lo + 2 > cp, na);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   // steady state: level c_lo + WARM on takes the register set (c - c_lo) & 1
   auto walk = [&](auto stores) __attribute__((always_inline)) {
     int c = c_lo + WARM;
-    for (; c + 1 < N; c += 2) {   // no exit between the halves: one wait per piece
+    for (; c + 1 < c_end; c += 2) {   // no exit between the halves: one wait per piece
       level(c, decltype(stores)::value, nb);
       level(c + 1, decltype(stores)::value, na);
     }
-    if (c < N) level(c, decltype(stores)::value, nb);
+    if (c < c_end) level(c, decltype(stores)::value, nb);
   };
   if (member) walk(std::true_type{});
   else walk(std::false_type{});
@@ -341,7 +401,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
     const E *__restrict__ qae, const E *__restrict__ dout, const float *__restrict__ lse,
     const float *__restrict__ dlse, const float *__restrict__ dvec, const float *__restrict__ lam,
     const E *__restrict__ levels, const E *__restrict__ levt, const E *__restrict__ v,
-    float scale, float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH) {
+    float scale, float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH, Win win) {
   constexpr int PQ = D + MM<E>::PAD;          // Qs, Os: [64 q][D]
   constexpr int PG = 32 + MM<E>::PAD;         // Gs: per wave [32 q][32 keys]
   __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
@@ -351,8 +411,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
   __shared__ __attribute__((aligned(16))) E KtS[(KPL_OF<E>() > 1 && D == 64) ? 4 * D * PG : 1];
   __shared__ float red[2 * 32 * (D + 1)];
   __shared__ float rsum[C];
-  const int N = T / C;
-  const int bh = blockIdx.x % BH, c = N - 1 - blockIdx.x / BH;   // longest walks first
+  const int bh = blockIdx.x % BH, c = win.hi - 1 - blockIdx.x / BH;   // longest walks first
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
   const int qh = wv & 1, kh = wv >> 1;
   const size_t qrow = (size_t)bh * T + (size_t)c * C;
@@ -384,7 +443,7 @@ __global__ __launch_bounds__(256) void dq_kernel(
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) zero16(dq[t]);
   float rowsum = 0.f;
-  const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
+  const size_t lev_c = lev_at(win, bh, c, 0, D);
   E *Gw = Gs + wv * 32 * PG;
   __syncthreads();
   // Matrix-core A operands of one key chunk for this wave: Khat[c]_{c'} rows
@@ -491,34 +550,36 @@ __global__ __launch_bounds__(256) void dq_kernel(
   }
 }
 
-// bf16, d = 64: one block of 2 waves per (bh, query chunk c); wave kh takes
-// keys 32 kh.. of each key chunk against all 64 queries, so each level block
-// is read from HBM once.  The key block's fragments (for S^T) are fetched one
-// key chunk ahead and transposed on chip for the dQa product.
+// bf16, d = 64: one block of 4 waves per (bh, query chunk c); wave (st, kh)
+// = (w >> 1, w & 1) takes keys 32 kh.. of the key chunks c' = c-1-st,
+// c-3-st, ... against all 64 queries, so each level block is read from HBM
+// once and a window's few query chunks still fill the chip.  The key block's
+// fragments (for S^T) are fetched one key chunk ahead and transposed on chip
+// for the dQa product; the four partial dQa are summed through LDS.
 template <bool FOX>
-__global__ __launch_bounds__(128) void dq64_kernel(
+__global__ __launch_bounds__(256) void dq64_kernel(
     const __bf16 *__restrict__ qae, const __bf16 *__restrict__ dout,
     const float *__restrict__ lse, const float *__restrict__ dlse,
     const float *__restrict__ dvec, const float *__restrict__ lam,
     const __bf16 *__restrict__ levels, const __bf16 *__restrict__ v, float scale,
-    float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH) {
+    float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH, Win win) {
   using E = __bf16;
   constexpr int D = 64, PQ = D + 8, PG = 32 + 8, KS = D / 16;
   __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
   __shared__ __attribute__((aligned(16))) E Os[C * PQ];
-  // per wave g[q][key] and Khat^T[d][key]; at the end the key-half reduction
-  __shared__ __attribute__((aligned(16))) E pool[2 * C * PG + 2 * D * PG];
-  __shared__ float rsum[C];
-  E *Gs = pool, *KtS = pool + 2 * C * PG;
-  const int N = T / C;
-  const int bh = blockIdx.x % BH, c = N - 1 - blockIdx.x / BH;   // longest walks first
-  const int tid = threadIdx.x, lane = tid & 63, kh = tid >> 6, g = lane >> 5, col = lane & 31;
+  // per wave g[q][key] and Khat^T[d][key]; at the end the reduction
+  __shared__ __attribute__((aligned(16))) E pool[4 * C * PG + 4 * D * PG];
+  __shared__ float rsum[2][C];
+  E *Gs = pool, *KtS = pool + 4 * C * PG;
+  const int bh = blockIdx.x % BH, c = win.hi - 1 - blockIdx.x / BH;   // longest walks first
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 5, col = lane & 31;
+  const int kh = wv & 1, st = wv >> 1;
   const size_t qrow = (size_t)bh * T + (size_t)c * C;
   if (c == 0) {
-    for (int idx = tid; idx < C * D; idx += 128) dqa[qrow * D + idx] = 0.f;
+    for (int idx = tid; idx < C * D; idx += 256) dqa[qrow * D + idx] = 0.f;
     return;
   }
-  for (int vi = tid; vi < C * D / 8; vi += 128) {
+  for (int vi = tid; vi < C * D / 8; vi += 256) {
     const int r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
     *reinterpret_cast<uint4 *>(Qs + r * PQ + c8) = *reinterpret_cast<const uint4 *>(qae + (qrow + r) * D + c8);
     *reinterpret_cast<uint4 *>(Os + r * PQ + c8) = *reinterpret_cast<const uint4 *>(dout + (qrow + r) * D + c8);
@@ -538,8 +599,8 @@ __global__ __launch_bounds__(128) void dq64_kernel(
     zero16(dq[t][0]);
     zero16(dq[t][1]);
   }
-  const size_t lev_c = (size_t)bh * lev_off(N, 0, D) + lev_off(c, 0, D);
-  E *Gw = Gs + kh * C * PG, *Kt = KtS + kh * D * PG;
+  const size_t lev_c = lev_at(win, bh, c, 0, D);
+  E *Gw = Gs + wv * C * PG, *Kt = KtS + wv * D * PG;
   __syncthreads();
   // one key chunk's operands: level rows and V rows (B operands) and, with the
   // gate, Lambda of the wave's keys
@@ -566,7 +627,7 @@ __global__ __launch_bounds__(128) void dq64_kernel(
     }
   };
   auto step = [&](int cp, Frags &fc, Frags &fn) {
-    fetch(cp - 1, fn);
+    fetch(cp - 2, fn);
     __builtin_amdgcn_sched_barrier(0);   // issue the loads before this step's products
     float kl[16];
 #pragma unroll
@@ -613,34 +674,49 @@ __global__ __launch_bounds__(128) void dq64_kernel(
     wave_sync();
   };
   Frags fa, fb;
-  fetch(c - 1, fa);
-  int cp = c - 1;
-  for (; cp >= 1; cp -= 2) {   // no exit between the halves
+  int cp = c - 1 - st;
+  fetch(cp, fa);
+  for (; cp >= 2; cp -= 4) {   // no exit between the halves
     step(cp, fa, fb);
-    step(cp - 1, fb, fa);
+    step(cp - 2, fb, fa);
   }
-  if (cp == 0) step(0, fa, fb);
-  // combine the two key halves (wave 1's partial through LDS, over Gs and KtS)
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(pool);   // [64 q][D + 1] floats
-  static_assert(C * (D + 1) * 4 <= (2 * C * PG + 2 * D * PG) * 2, "reduction area");
+  if (cp >= 0) step(cp, fa, fb);
+  // sum the four partials through LDS (over Gs and KtS): first stream 1 onto
+  // stream 0 (per key half), then key half 1 onto key half 0
+  float *red = reinterpret_cast<float *>(pool);   // [2][64 q][D + 1] floats
+  static_assert(2 * C * (D + 1) * 4 <= (4 * C * PG + 4 * D * PG) * 2, "reduction area");
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) rowsum[qt] += __shfl_xor(rowsum[qt], 32);
-  if (kh == 1) {
+  auto put = [&](float *r, float *rs) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          red[(32 * qt + col) * (D + 1) + 32 * t + acc_row(r, g)] = dq[t][qt][r];
+        for (int i = 0; i < 16; ++i) r[(32 * qt + col) * (D + 1) + 32 * t + acc_row(i, g)] = dq[t][qt][i];
     if (g == 0) {
-      rsum[col] = rowsum[0];
-      rsum[32 + col] = rowsum[1];
+      rs[col] = rowsum[0];
+      rs[32 + col] = rowsum[1];
     }
-  }
+  };
+  auto add = [&](const float *r, const float *rs) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[t][qt][i] += r[(32 * qt + col) * (D + 1) + 32 * t + acc_row(i, g)];
+    rowsum[0] += rs[col];
+    rowsum[1] += rs[32 + col];
+  };
   __syncthreads();
-  if (kh == 0) {
+  if (st == 1) put(red + kh * C * (D + 1), rsum[kh]);
+  __syncthreads();
+  if (st == 0) add(red + kh * C * (D + 1), rsum[kh]);
+  __syncthreads();
+  if (wv == 1) put(red, rsum[0]);
+  __syncthreads();
+  if (wv == 0) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int q = 32 * qt + col;
@@ -656,7 +732,7 @@ __global__ __launch_bounds__(128) void dq64_kernel(
           o.w = dq[t][qt][4 * r4 + 3] + red[q * (D + 1) + d0 + 3];
           *reinterpret_cast<float4 *>(dqa + (qrow + q) * D + d0) = o;
         }
-      if (FOX && g == 0) dlam[qrow + q] += rowsum[qt] + rsum[q];
+      if (FOX && g == 0) dlam[qrow + q] += rowsum[qt] + rsum[0][q];
     }
   }
 }
@@ -690,7 +766,7 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     const float *__restrict__ dvec, const float *__restrict__ lam, const E *__restrict__ levels,
     const E *__restrict__ levt, const E *__restrict__ v, const E *__restrict__ nmt,
     float scale, float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
-    float *__restrict__ dmpart, int T, int BH) {
+    float *__restrict__ dmpart, int T, int BH, Win win, int slots, float *__restrict__ gstate) {
   using L = DkLds<E, D, G>;
   constexpr bool BF = L::BF;
   constexpr int NW = L::WAVES, NTH = 64 * NW;
@@ -709,8 +785,11 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   E *Qt = stage + 2 * C * L::PQ, *Ot = Qt + D * L::PQT;   // bf16 only
   E *PT = pw + wv * L::PERWAVE, *GT = PT + 32 * L::PP;
   E *GR = PT;                                             // rounded Gamma rows at crossings
-  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
   const int kbase = 64 * (wv >> 1) + 32 * kh;             // this wave's keys within the group
+  const int c_low = G * grp + 1;   // last query chunk the group visits
+  // this window's steps: query chunks top down to bottom
+  const int top = win.hi - 1, bottom = max(win.lo, c_low);
+  const bool has_work = member && cp < top;
 
   f32x16 gam[D / 32], dva[D / 32];
 #pragma unroll
@@ -718,9 +797,13 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     zero16(gam[t]);
     zero16(dva[t]);
   }
+  if (has_work && win.hi < N)   // Gamma as the window above left it
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gam[t][r] = gstate[(krow + acc_row(r, g)) * D + 32 * t + col];
   float colsum = 0.f;
   const float my_lam = (FOX && member) ? lam[krow + col] : 0.f;
-  const int c_low = G * grp + 1;   // last query chunk the group visits
   // bf16: the next step's global reads are in flight during the current
   // step: its query-side copies (into registers, stored to LDS at the top of
   // the next step) and this wave's level rows Khat[c-1]_{c'} (B operands of
@@ -756,7 +839,7 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   };
   auto fetch_level = [&](int cc) __attribute__((always_inline)) {
     if constexpr (BF) {   // rows Khat[cc]_{c'} of this wave's keys, B-operand fragments
-      const E *kl = levels + lev_head + lev_off(cc, cp, D) + (size_t)(32 * kh + col) * D + KPL * g;
+      const E *kl = levels + lev_at(win, bh, cc, cp, D) + (size_t)(32 * kh + col) * D + KPL * g;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) kfr[ks] = MM<E>::ld(kl + 2 * KPL * ks, 1);
     }
@@ -766,11 +849,11 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
       const E *vr = v + (krow + col) * D + KPL * g;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) vfr[ks] = MM<E>::ld(vr + 2 * KPL * ks, 1);
-      if (N - 1 > cp) fetch_level(N - 1);
+      if (top > cp) fetch_level(top);
     }
-    if (N - 1 >= c_low) fetch_copy(N - 1);
+    if (top >= bottom) fetch_copy(top);
   }
-  for (int c = N - 1; c >= c_low; --c) {
+  for (int c = top; c >= bottom; --c) {
     const bool active = member && c > cp;
     const size_t qrow = head + (size_t)c * C;
     __syncthreads();
@@ -801,10 +884,10 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
       for (int ks = 0; ks < KSD; ++ks) kcur[ks] = kfr[ks];
       // next step's operands: level rows first, then the copies
       if (member && c - 1 > cp) fetch_level(c - 1);
-      if (c - 1 >= c_low) fetch_copy(c - 1);
+      if (c - 1 >= bottom) fetch_copy(c - 1);
     }
     if (active) {
-      const E *kl = levels + lev_head + lev_off(c, cp, D) + (size_t)32 * kh * D;   // Khat[c] rows
+      const E *kl = levels + lev_at(win, bh, c, cp, D) + (size_t)32 * kh * D;   // Khat[c] rows
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -878,8 +961,8 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     {
       constexpr int TILES = (D / 32) * (D / 32);
       const int nch = mch - G * grp < G ? mch - G * grp : G;
-      float *dst = dmpart + (((size_t)bh * N + mch) * NG + grp) * D * D;
-      const size_t lm = lev_head + lev_off(mch, G * grp, D);   // chunk blocks are consecutive
+      float *dst = dmpart + (((size_t)bh * slots + mch - (win.lo - 1)) * NG + grp) * D * D;
+      const size_t lm = lev_at(win, bh, mch, G * grp, D);   // chunk blocks are consecutive
       for (int tI = wv; tI < TILES; tI += NW) {
         const int ta = tI / (D / 32), tb = tI % (D / 32);
         f32x16 acc;
@@ -909,9 +992,13 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   }
   if (!member) return;
   if (cp == N - 1) {   // no later query chunk: dKb = 0
-    for (int e = lane; e < 32 * D; e += 64) dkb[krow * D + e] = 0.f;
+    if (win.hi == N)
+      for (int e = lane; e < 32 * D; e += 64) dkb[krow * D + e] = 0.f;
     return;
   }
+  if (!has_work) return;
+  // this window's share of dV and of the gate's column sums; Gamma for the
+  // window below when the walk goes on there
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -920,6 +1007,11 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     colsum += __shfl_xor(colsum, 32);
     if (g == 0) dlam[krow + col] -= colsum;
   }
+  if (bottom > cp + 1)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gstate[(krow + acc_row(r, g)) * D + 32 * t + col] = gam[t][r];
 }
 
 // ------------------------------------------------------------------ dk, bf16, d = 64
@@ -943,7 +1035,7 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     const float *__restrict__ lam, const __bf16 *__restrict__ levels,
     const __bf16 *__restrict__ levt, const __bf16 *__restrict__ v, float scale,
     float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
-    float *__restrict__ dmpart, int T, int BH) {
+    float *__restrict__ dmpart, int T, int BH, Win win, int slots, float *__restrict__ gstate) {
   using E = __bf16;
   constexpr int D = 64, G = 4, NW = 8, P = kImgPitch, KG = 64 * G, PGT = KG + 8;
   constexpr int QB = kQImgElems * 2, MB = kMImgElems * 2, SB = 64 * 16;   // bytes
@@ -962,8 +1054,10 @@ __global__ __launch_bounds__(512) void dk64_kernel(
   const size_t krow = head + (size_t)cp * C + 32 * kh;
   const bool member = cp < N;
   const int kbase = 64 * (wv >> 1) + 32 * kh;
-  const size_t lev_head = (size_t)bh * lev_off(N, 0, D);
   const int c_low = G * grp + 1;
+  // this window's steps: query chunks top down to bottom
+  const int top = win.hi - 1, bottom = max(win.lo, c_low);
+  const bool has_work = member && cp < top;
 
   auto stage = [&](int c, int b) {
     const size_t ch = (size_t)bh * N + c;
@@ -991,13 +1085,24 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     zero16(gamT[t]);
     zero16(dvT[t]);
   }
+  if (has_work && win.hi < N)   // Gamma^T as the window above left it (lane = key)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = *reinterpret_cast<const float4 *>(gstate + (krow + col) * D + 32 * t + 8 * q4 + 4 * g);
+        gamT[t][4 * q4] = x.x;
+        gamT[t][4 * q4 + 1] = x.y;
+        gamT[t][4 * q4 + 2] = x.z;
+        gamT[t][4 * q4 + 3] = x.w;
+      }
   float colsum = 0.f;
   const float my_lam = (FOX && member) ? lam[krow + col] : 0.f;
   bf16x8 vf[D / 16], kf[D / 16];
   if (member) load_rows(vf, v + krow * D);
-  if (N - 1 >= c_low) {
-    stage(N - 1, (N - 1) & 1);
-    if (member && N - 1 > cp) load_rows(kf, levels + lev_head + lev_off(N - 1, cp, D) + (size_t)32 * kh * D);
+  if (top >= bottom) {
+    stage(top, top & 1);
+    if (member && top > cp) load_rows(kf, levels + lev_at(win, bh, top, cp, D) + (size_t)32 * kh * D);
   }
   // one step: query chunk c with level fragments kf; the next step's go to kn
   auto step = [&](int c, bf16x8 (&kf)[D / 16], bf16x8 (&kn)[D / 16]) {
@@ -1005,11 +1110,14 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     const int b = c & 1;
     wait_vmcnt<0>();
     lds_barrier();
-    if (c - 1 >= c_low) stage(c - 1, b ^ 1);
-    // the next step's level rows; every step loads (a valid block when there
-    // is no next level), so the sequence of loads is the same in every step
-    const bool next_active = member && c - 1 > cp && c - 1 >= c_low;
-    load_rows(kn, levels + lev_head + (next_active ? lev_off(c - 1, cp, D) : 0) + (size_t)32 * kh * D);
+    if (c - 1 >= bottom) stage(c - 1, b ^ 1);
+    // the next level's rows (the next step's S operand, and Khat[c-1] at the
+    // crossing below, also after the window's last step: level lo - 1 is in
+    // the window); every step loads (a valid block when there is no next
+    // level), so the sequence of loads is the same in every step
+    const bool next_active = member && c - 1 > cp;
+    load_rows(kn, levels + (next_active ? lev_at(win, bh, c - 1, cp, D) : (size_t)bh * win.head) +
+                      (size_t)32 * kh * D);
     const E *Qs = reinterpret_cast<const E *>(sbuf + b * BUF), *QF = Qs + 64 * P;
     const E *Os = reinterpret_cast<const E *>(sbuf + b * BUF + QB), *OF = Os + 64 * P;
     const E *Ms = reinterpret_cast<const E *>(sbuf + b * BUF + 2 * QB);
@@ -1081,7 +1189,7 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     {
       constexpr int TILES = (D / 32) * (D / 32);
       const int nch = mch - G * grp < G ? mch - G * grp : G;
-      float *dst = dmpart + (((size_t)bh * N + mch) * NG + grp) * D * D;
+      float *dst = dmpart + (((size_t)bh * slots + mch - (win.lo - 1)) * NG + grp) * D * D;
       for (int tI = wv; tI < TILES; tI += NW) {
         const int ta = tI / (D / 32), tb = tI % (D / 32);
         f32x16 acc;
@@ -1110,16 +1218,25 @@ __global__ __launch_bounds__(512) void dk64_kernel(
     }
   };
   bf16x8 kf2[D / 16];
-  for (int c = N - 1; c >= c_low; c -= 2) {
+  for (int c = top; c >= bottom; c -= 2) {
     step(c, kf, kf2);
-    if (c - 1 < c_low) break;
+    if (c - 1 < bottom) break;
     step(c - 1, kf2, kf);
   }
   if (!member) return;
   if (cp == N - 1) {   // no later query chunk: dKb = 0
-    for (int e = lane; e < 32 * D; e += 64) dkb[krow * D + e] = 0.f;
+    if (win.hi == N)
+      for (int e = lane; e < 32 * D; e += 64) dkb[krow * D + e] = 0.f;
     return;
   }
+  if (!has_work) return;
+  if (bottom > cp + 1)   // Gamma^T for the window below
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4 *>(gstate + (krow + col) * D + 32 * t + 8 * q4 + 4 * g) =
+            make_float4(gamT[t][4 * q4], gamT[t][4 * q4 + 1], gamT[t][4 * q4 + 2], gamT[t][4 * q4 + 3]);
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -1138,21 +1255,23 @@ __global__ __launch_bounds__(512) void dk64_kernel(
   }
 }
 
-// dM_m = sum over the groups that cross m (m in [1, N-2]); 0 otherwise.
+// dM_m = sum over the groups that cross m (m in [1, N-2]); 0 otherwise, for
+// the nm chunks m = m0 .. m0 + nm - 1 of one window (partial slot m - m0).
 // One block per (bh, m) and slice of 1024 elements (DD / 1024 blocks per
 // matrix), four consecutive elements per thread; the partials are summed in
 // group order, eight loads in flight.
 template <int G>
 __global__ __launch_bounds__(256) void dm_reduce_kernel(const float4 *__restrict__ dmpart,
                                                         float4 *__restrict__ dm, int N, int DD,
-                                                        int XB) {
+                                                        int XB, int m0, int nm, int slots) {
   constexpr int U = 8;
   const int NG = (N + G - 1) / G, DD4 = DD / 4;
-  const size_t bm = blockIdx.x / XB;   // bh * N + m
+  const int bmi = blockIdx.x / XB;   // bh * nm + (m - m0)
+  const int bh = bmi / nm, mi = bmi % nm, mch = m0 + mi;
   const int e = (blockIdx.x % XB) * 256 + threadIdx.x;
-  const int mch = (int)(bm % N);
   const int ng = (mch >= 1 && mch <= N - 2) ? (mch + G - 1) / G : 0;
-  const float4 *src = dmpart + bm * NG * DD4 + e;
+  const size_t bm = (size_t)bh * N + mch;
+  const float4 *src = dmpart + ((size_t)bh * slots + mi) * NG * DD4 + e;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   int gi = 0;
   for (; gi + U <= ng; gi += U) {
@@ -1184,49 +1303,84 @@ constexpr int group_of() {
 
 }  // namespace
 
-size_t bwd_levels_elems(int BH, int T, int D) { return (size_t)BH * lev_off(T / C, 0, D); }
+BwdPlan bwd_plan(int T, int window) {
+  BwdPlan p{};
+  p.N = T / C;
+  const int nq = p.N - 1 > 1 ? p.N - 1 : 1;   // query chunks with earlier keys
+  p.W = window > 0 ? (window < nq ? window : nq) : (nq <= 2 * kBwdWindowMin ? nq : kBwdWindowMin);
+  p.nwin = (nq + p.W - 1) / p.W;
+  p.win_blocks = 0;
+  p.slots = 0;
+  for (int w = 0; w < p.nwin; ++w) {
+    const int lo = 1 + w * p.W, hi = p.N < lo + p.W ? p.N : lo + p.W;
+    const size_t blk = (size_t)hi * (hi - 1) / 2 - (size_t)(lo - 1) * (lo - 2) / 2;
+    p.win_blocks = blk > p.win_blocks ? blk : p.win_blocks;
+    p.slots = hi - lo + 1 > p.slots ? hi - lo + 1 : p.slots;
+  }
+  p.ckpt_blocks = p.nwin > 2 ? (size_t)p.W * (p.nwin - 1) * (p.nwin - 2) / 2 : 0;
+  return p;
+}
 
-size_t bwd_dmpart_floats(int dtype, int BH, int T, int D) {
+size_t bwd_dmpart_floats(int dtype, int BH, int T, int D, int window) {
   const int N = T / C;
   const int G = dtype == 1 ? (D == 64 ? 4 : 2) : (D == 64 ? 2 : 1);
-  return (size_t)BH * N * ((N + G - 1) / G) * D * D;
+  return (size_t)BH * bwd_plan(T, window).slots * ((N + G - 1) / G) * D * D;
 }
 
 template <typename E, int D, bool FOX>
 static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   const int BH = a.BH, T = a.T, N = T / C;
   constexpr int G = group_of<E, D>();
+  constexpr bool BF = std::is_same<E, __bf16>::value;
+  const BwdPlan P = bwd_plan(T, a.window);
+  const int NG = (N + G - 1) / G;
   E *lev = static_cast<E *>(a.levels), *levt = static_cast<E *>(a.levt);
   const E *qae = (const E *)a.qae, *dout = (const E *)a.dout, *v = (const E *)a.v;
-  if constexpr (std::is_same<E, __bf16>::value) {
-    if (N > 1)
-      hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((N - 1 + 3) / 4)), dim3(512), 0,
-                         s, a.kb, (const E *)a.nm, lev, levt, T, BH);
-  } else if (N > 1) {
-    hipLaunchKernelGGL((levels_f32_kernel<D>), dim3(BH * (N - 1)), dim3(128), 0, s, a.kb,
-                       (const float *)a.nm, lev, levt, T, BH);
-  }
-  if constexpr (std::is_same<E, __bf16>::value && D == 64)
-    hipLaunchKernelGGL((dq64_kernel<FOX>), dim3(BH * N), dim3(128), 0, s, qae, dout, a.lse, a.dlse,
-                       a.dvec, a.lam, lev, v, a.scale, a.dqa, a.dlam, T, BH);
-  else
-    hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * N), dim3(256), 0, s, qae, dout, a.lse,
-                       a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH);
-  const int NG = (N + G - 1) / G;
-  if constexpr (std::is_same<E, __bf16>::value && D == 64) {
-    static_assert(G == 4, "dk64_kernel takes groups of 4 key chunks");
-    hipLaunchKernelGGL((dk64_kernel<FOX>), dim3(BH * NG), dim3(512), 0, s, (const E *)a.qimg,
-                       (const E *)a.oimg, (const E *)a.mimg, (const float4 *)a.qst, a.lam, lev,
-                       levt, v, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
-  } else {
-    hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * NG), dim3(128 * G), 0, s, qae,
-                       (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam, lev,
-                       levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH);
-  }
+  const Ckpt ck{a.ckpt, P.ckpt_blocks * C * D, P.W};
   constexpr int XB = D * D / 1024;
   static_assert(D * D % 1024 == 0, "whole 1024-element slices");
-  hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * N * XB), dim3(256), 0, s,
-                     (const float4 *)a.dmpart, (float4 *)a.dm, N, D * D, XB);
+  // windows of query chunks, the last first (Gamma flows down); the last
+  // window's level pass is the whole walk, which also leaves the checkpoints
+  for (int w = P.nwin - 1; w >= 0; --w) {
+    const int lo = 1 + w * P.W, hi = N < lo + P.W ? N : lo + P.W;
+    const Win win{lo, hi, lev_off(lo - 1, 0, D), P.win_blocks * C * D};
+    const int first = w == P.nwin - 1;
+    if (hi - 1 > 0) {   // levels [lo - 1, hi) of the key chunks c' < hi - 1
+      if constexpr (BF)
+        hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((hi - 1 + 3) / 4)), dim3(512), 0,
+                           s, a.kb, (const E *)a.nm, lev, levt, T, BH, win, ck, first);
+      else
+        hipLaunchKernelGGL((levels_f32_kernel<D>), dim3(BH * (hi - 1)), dim3(128), 0, s, a.kb,
+                           (const float *)a.nm, lev, levt, T, BH, win, ck, first);
+    }
+    const int nq = hi - (w == 0 ? 0 : lo);   // query chunks of the window (chunk 0 in the first)
+    if constexpr (BF && D == 64)
+      hipLaunchKernelGGL((dq64_kernel<FOX>), dim3(BH * nq), dim3(256), 0, s, qae, dout, a.lse,
+                         a.dlse, a.dvec, a.lam, lev, v, a.scale, a.dqa, a.dlam, T, BH, win);
+    else
+      hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * nq), dim3(256), 0, s, qae, dout, a.lse,
+                         a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH, win);
+    // groups with a step in the window (G grp + 1 <= hi - 1); the last window
+    // also runs the rest, which store dKb = 0 for chunk N - 1
+    const int ngw = hi == N ? NG : (hi - 2) / G + 1 < NG ? (hi - 2) / G + 1 : NG;
+    if constexpr (BF && D == 64) {
+      static_assert(G == 4, "dk64_kernel takes groups of 4 key chunks");
+      hipLaunchKernelGGL((dk64_kernel<FOX>), dim3(BH * ngw), dim3(512), 0, s, (const E *)a.qimg,
+                         (const E *)a.oimg, (const E *)a.mimg, (const float4 *)a.qst, a.lam, lev,
+                         levt, v, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T, BH, win, P.slots,
+                         a.gstate);
+    } else {
+      hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * ngw), dim3(128 * G), 0, s, qae,
+                         (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam,
+                         lev, levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T,
+                         BH, win, P.slots, a.gstate);
+    }
+    // dM_m for m in [lo - 1, hi - 1), and m = N - 1 with the last window
+    const int nm = hi - lo + (hi == N ? 1 : 0);
+    hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * nm * XB), dim3(256), 0, s,
+                       (const float4 *)a.dmpart, (float4 *)a.dm, N, D * D, XB, lo - 1, nm,
+                       P.slots);
+  }
   return hipGetLastError();
 }
 

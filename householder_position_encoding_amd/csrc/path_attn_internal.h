@@ -219,16 +219,35 @@ hipError_t launch_decode_step(int dtype, int kc_dtype, int D, const void *q, con
                               void *out, float *lse, float *part, int BH, int t, int T_cap,
                               float sl2, hipStream_t s);
 
-// Backward pass (backward.hip, bwd_sweep.hip).  Workspace offsets in bytes;
-// the key levels of one head take 64*D*N(N-1)/2 elements of the input dtype,
-// N = T/64.
+// Backward pass (backward.hip, bwd_sweep.hip).
+//
+// The quadratic sweep runs over windows of query chunks, the last window
+// first: window w holds query chunks [lo, hi) with lo = 1 + w*W and
+// hi = min(N, lo + W), and the key levels c in [lo - 1, hi) of every earlier
+// key chunk.  The last window's level pass is the whole walk, which also
+// keeps float32 checkpoints at the levels lo - 1 of the other windows (but
+// the first); each of those walks its own levels from there, so a head holds
+// one window of levels instead of all N(N-1)/2 of them.  Up to 33 chunks run
+// as one window (no checkpoints) by default; a caller that gives the
+// backward more workspace gets longer windows (window > 0: that many query
+// chunks, at most N - 1; window <= 0: the default).
+constexpr int kBwdWindowMin = 16;
+struct BwdPlan {
+  int N, W, nwin;          // chunks, window length (query chunks), windows
+  size_t win_blocks;       // 64-key level blocks of the largest window, per head
+  size_t ckpt_blocks;      // float32 64-key checkpoint blocks per head
+  int slots;               // dM partial slots per head: window length + 1
+};
+BwdPlan bwd_plan(int T, int window);
+// Workspace offsets in bytes.  adj (the per-chunk adjoint scratch, used only
+// after the sweep) shares its bytes with the sweep's buffers (levels, levt,
+// ckpt, dmpart, gstate).
 struct BwdLayout {
   size_t kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
-      nm, nmt, dot, levt, qimg, oimg, mimg, qst, total;
+      nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, total;
 };
-BwdLayout bwd_layout(int B, int H, int T, int D, int dtype);
-size_t bwd_levels_elems(int BH, int T, int D);
-size_t bwd_dmpart_floats(int dtype, int BH, int T, int D);
+BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window);
+size_t bwd_dmpart_floats(int dtype, int BH, int T, int D, int window);
 
 // The quadratic part (bwd_sweep.hip): key levels, dQa (+ dLambda row sums),
 // dKb, dV (+= onto the diagonal part), dLambda column sums, dM.
@@ -242,8 +261,9 @@ struct SweepArgs {
   const float *lse, *dlse, *dvec, *lam;
   void *levels;
   float *dmpart, *dqa, *dkb, *dv, *dlam, *dm;
+  float *ckpt, *gstate;                     // level checkpoints, Gamma between windows
   float scale;
-  int BH, T;
+  int BH, T, window;
 };
 hipError_t launch_bwd_sweep(int dtype, int D, bool fox, const SweepArgs &a, hipStream_t s);
 
@@ -278,6 +298,7 @@ struct BwdArgs {
   float *dbeta, *dlogf;
   int B, H, T;
   float scale;
+  int window;   // query chunks per window of the sweep (bwd_plan)
 };
 hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipStream_t s);
 

@@ -331,12 +331,26 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
  * ------------------------------------------------------------------------
  */
 
-/* Workspace bytes of path_attn_bwd, 0 for invalid or unsupported arguments.
- * It grows as T^2: the aligned key levels take about B*H*d*T^2/128 elements
- * of the input dtype (stored in rows, and at d = 128 or for float32 also
- * transposed), next to linear per-chunk terms: 19.06 GiB at B=2, H=16,
- * T=16384, d=64 in bf16, 26.44 GiB at B=4, H=8, T=8192, d=128 in bf16. */
+/* Workspace bytes of path_attn_bwd, 0 for invalid or unsupported arguments:
+ * the smallest workspace it accepts.  The quadratic part of the backward
+ * walks the keys aligned to every later chunk (key levels, about
+ * B*H*d*T^2/128 values in all); past 33 chunks of 64 tokens it runs in
+ * windows of 16 query chunks, holding one window of levels, float32
+ * checkpoints of the walk at the window boundaries and one window of dM
+ * partials at a time, so the workspace grows as about T^1.5 next to linear
+ * per-chunk terms: 4.66 GiB at B=2, H=16, T=16384, d=64 in bf16, 6.45 GiB at
+ * B=4, H=8, T=8192, d=128 in bf16, 11.4 GiB at B=2, H=16, T=32768, d=64. */
 size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
+
+/* Workspace bytes of path_attn_bwd with windows of `window` query chunks
+ * (window <= 0: the whole sweep as one window, which stores every key level:
+ * 18.19 GiB at B=2, H=16, T=16384, d=64 in bf16).  Longer windows mean fewer
+ * passes and restarts of the walk, so a faster backward (13.8 ms instead of
+ * 15.7 ms at that shape on one MI355X).  path_attn_bwd runs one window when
+ * its workspace allows, else the longest of 128, 64, 32 and 16 query chunks
+ * whose layout fits the workspace_bytes it is given.  0 for invalid
+ * arguments. */
+size_t path_attn_bwd_workspace_bytes_window(int B, int H, int T, int d, int dtype, int window);
 
 /*
  * Gradients of  L = sum <dout, out> + sum <dlse, lse>  with respect to q, k,
@@ -358,7 +372,10 @@ size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
  * dlse and gate, lse = 0), which contribute nothing to any gradient; the
  * inputs are then staged in the workspace and the first T rows of the
  * gradients copied back.  Every pointer 16-byte aligned, the workspace
- * 256-byte aligned.
+ * 256-byte aligned; workspace_bytes at least path_attn_bwd_workspace_bytes
+ * (a larger workspace selects longer windows of the sweep, see
+ * path_attn_bwd_workspace_bytes_window; the gradients agree to float32
+ * rounding either way).
  * Errors: EINVAL for null or misaligned pointers, a bad dtype or scale,
  * logf without dlogf, or a small workspace; EUNSUPPORTED for d not in
  * {64, 128} or B*H*Tp*d >= 2^31; EHIP on a launch error.

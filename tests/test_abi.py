@@ -269,6 +269,33 @@ def test_bwd_workspace_bytes(dtype, esize, B, H, T, d):
     assert lib.path_attn_bwd_workspace_bytes(1, 1, 64, 64, 4) == 0
 
 
+@pytest.mark.parametrize("dtype", [pa.F32, pa.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_workspace_windows(dtype, d):
+    """Past 33 chunks the default backward sweep runs in windows of 16 query
+    chunks: its workspace grows as about T^1.5 instead of T^2, and longer
+    windows (window_bytes) cost more, up to the single window that stores
+    every key level."""
+    lib = pa.load_library()
+    nb = lambda T: lib.path_attn_bwd_workspace_bytes(1, 4, T, d, dtype)
+    nw = lambda T, w: lib.path_attn_bwd_workspace_bytes_window(1, 4, T, d, dtype, w)
+    # up to 33 chunks: one window by default
+    for T in (64, 1024, 2112):
+        assert nb(T) == nw(T, 0) == nw(T, 10 ** 6)
+    # 65 chunks and more: windows of 16 by default, longer windows cost more
+    for T in (4160, 8192, 16384):
+        assert nb(T) == nw(T, 16) < nw(T, 32) < nw(T, 64) <= nw(T, 0)
+    # the quadratic term is gone: doubling T at most triples the workspace
+    # (it quadruples with one window)
+    assert nb(32768) < 3.0 * nb(16384)
+    assert nw(32768, 0) > 3.5 * nw(16384, 0)
+    # the benchmark shape: 18.19 GiB with one window, under 5 GiB by default
+    big = lib.path_attn_bwd_workspace_bytes_window(2, 16, 16384, 64, pa.BF16, 0)
+    small = lib.path_attn_bwd_workspace_bytes(2, 16, 16384, 64, pa.BF16)
+    assert abs(big / 2 ** 30 - 18.19) < 0.01 and small / 2 ** 30 < 5.0
+    assert lib.path_attn_bwd_workspace_bytes_window(1, 1, 64, 96, pa.F32, 16) == 0
+
+
 def _bwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, w=FAKE, beta=FAKE, logf=None, out=FAKE, lse=FAKE,
              dout=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE, dw=FAKE, dbeta=FAKE, dlogf=None,

@@ -199,3 +199,34 @@ def test_backward_fox_d64_medium():
     ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
     _log(f"fox d64 T={T}: oracle head (0,1) in {time.time() - t0:.1f} s")
     _compare("fox d64 medium", "bf16", got, ref, 0, 1)
+
+
+# Past 33 chunks the sweep runs in windows of 16 query chunks: a float32
+# checkpoint pass of the level walk, then per window (the last first) its own
+# levels, dq, dk (Gamma handed to the window below through the workspace) and
+# the dM reduction.  T = 4160 is 65 chunks (windows [1, 17), [17, 33),
+# [33, 49), [49, 65)); T = 2176 is 34 chunks, whose last window holds one
+# query chunk.  One head each against the blockwise oracle.
+WINDOWED = [
+    # dtype, d, fox, B, H, T, head
+    ("bf16", 64, True, 1, 2, 4160, (0, 1)),
+    ("bf16", 128, False, 1, 1, 2176, (0, 0)),
+    ("bf16", 128, True, 1, 1, 4160, (0, 0)),
+    ("f32", 64, True, 1, 1, 4160, (0, 0)),
+    ("f32", 128, False, 1, 1, 2176, (0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", WINDOWED, ids=lambda c: "-".join(map(str, c[:6])))
+def test_backward_windowed_sweep(case):
+    dtype, d, fox, B, H, T, (b, h) = case
+    inp = workloads.small(dtype, B, H, T, d, seed=4096 + d + T, fox=fox)
+    cot = workloads.cotangents(dtype, B, H, T, d, seed=5120 + T)
+    got = _run_gpu(inp, cot, dtype)
+    q, k, v, w, beta, logf, do, dl = _head(inp, cot, b, h)
+    import oracle
+    o, lse = oracle.path_attn(q, k, v, w, beta, logf)
+    t0 = time.time()
+    ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
+    _log(f"windowed {dtype} d{d} T={T}: oracle head ({b},{h}) in {time.time() - t0:.1f} s")
+    _compare(f"windowed {dtype} d{d} T={T}", dtype, got, ref, b, h)
