@@ -818,6 +818,24 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
   bf16x8 cq[BF ? NV : 1], co[BF ? NV : 1], cqt[BF ? NV : 1], cot[BF ? NV : 1];
   float4 cst = make_float4(0.f, 0.f, 0.f, 0.f);
   frag vfr[KSD], kfr[KSD];
+  // bf16: -M_{c-1}^T of the step's crossing, prefetched with the level rows
+  // and parked in the staging area (free once the step's products are done)
+  // next to Khat[c-1]^T, so that the crossing's products read only LDS
+  constexpr int NM = BF ? D * D / 8 / NTH : 1;      // 16-byte pieces of -M^T per thread
+  constexpr int PMT = D + L::PAD;                   // -M^T rows [D][D] in LDS
+  static_assert(!BF || D * L::PGT + D * PMT <= L::STAGE, "crossing operands fit the staging area");
+  bf16x8 mreg[NM];
+  E *KX = stage, *MT = stage + D * L::PGT;          // crossing: Khat[m]^T [D][KG], -M_m^T [D][D]
+  auto fetch_mt = [&](int mm) __attribute__((always_inline)) {
+    if constexpr (BF) {
+      const E *src = nmt + ((size_t)bh * N + mm) * D * D;
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int vi = tid + NTH * i;
+        mreg[i] = *reinterpret_cast<const bf16x8 *>(src + (size_t)vi * 8);
+      }
+    }
+  };
   auto fetch_copy = [&](int cc) __attribute__((always_inline)) {
     if constexpr (BF) {
       const size_t qr = head + (size_t)cc * C;
@@ -882,8 +900,10 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     if constexpr (BF) {
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) kcur[ks] = kfr[ks];
-      // next step's operands: level rows first, then the copies
+      // next step's operands: level rows first, then this step's -M^T for the
+      // crossing, then the copies
       if (member && c - 1 > cp) fetch_level(c - 1);
+      if (c - 1 > G * grp) fetch_mt(c - 1);
       if (c - 1 >= bottom) fetch_copy(c - 1);
     }
     if (active) {
@@ -956,8 +976,22 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
       }
     }
     __syncthreads();
+    if constexpr (BF) {   // every wave is past its products: the staging area is free
+      // Khat[m]^T [D][KG] from this wave's next-level rows (lane = key), and -M_m^T
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+        for (int t = 0; t < KPL; ++t)
+          KX[(KPL * g + 2 * KPL * ks + t) * L::PGT + kbase + col] = crosses ? kfr[ks][t] : (E)0.f;
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        const int vi = tid + NTH * i, r = vi / (D / 8), c8 = 8 * (vi % (D / 8));
+        *reinterpret_cast<bf16x8 *>(MT + r * PMT + c8) = mreg[i];
+      }
+      __syncthreads();
+    }
     // dM_m partial of the group: -sum_keys Gamma(key, d) Khat[m](key, d'), over
-    // the chunks c' < m of the group (Khat[m]^T read from the transposed levels)
+    // the chunks c' < m of the group
     {
       constexpr int TILES = (D / 32) * (D / 32);
       const int nch = mch - G * grp < G ? mch - G * grp : G;
@@ -968,11 +1002,13 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
         f32x16 acc;
         zero16(acc);
         for (int j = 0; j < nch; ++j) {
-          const E *kt = levt + lm + (size_t)j * C * D + (size_t)32 * tb * C;   // [d'][64 keys]
-          if constexpr (BF)
-            mma_tile<E, C>(acc, gx + 32 * ta * L::PGT + 64 * j, L::PGT, 1, kt, C, 1, lane);
-          else
+          if constexpr (BF) {
+            mma_tile<E, C>(acc, gx + 32 * ta * L::PGT + 64 * j, L::PGT, 1,
+                           KX + 32 * tb * L::PGT + 64 * j, L::PGT, 1, lane);
+          } else {
+            const E *kt = levt + lm + (size_t)j * C * D + (size_t)32 * tb * C;   // [d'][64 keys]
             mma_tile<E, C>(acc, gx + 64 * j * L::PGN + 32 * ta, 1, L::PGN, kt, C, 1, lane);
+          }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -984,7 +1020,7 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
         if constexpr (BF)
-          mma_tile<E, D>(gam[t], GR, L::PGN, 1, nb + 32 * t * D, D, 1, lane);
+          mma_tile<E, D>(gam[t], GR, L::PGN, 1, MT + 32 * t * PMT, PMT, 1, lane);
         else
           mma_tile<E, D>(gam[t], gx + kbase * L::PGN, L::PGN, 1, nb + 32 * t * D, D, 1, lane);
       }
