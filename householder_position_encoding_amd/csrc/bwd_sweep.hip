@@ -397,7 +397,7 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
 // synchronises only to stage its queries and to combine the key halves.
 // Chunk 0 has no earlier keys: its dQa is zero.
 template <typename E, int D, bool FOX>
-__global__ __launch_bounds__(256) void dq_kernel(
+__global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void dq_kernel(
     const E *__restrict__ qae, const E *__restrict__ dout, const float *__restrict__ lse,
     const float *__restrict__ dlse, const float *__restrict__ dvec, const float *__restrict__ lam,
     const E *__restrict__ levels, const E *__restrict__ levt, const E *__restrict__ v,
@@ -520,12 +520,81 @@ __global__ __launch_bounds__(256) void dq_kernel(
     }
     wave_sync();
   };
-  Frags fa, fb;
-  fetch(c - 1, fa);
-  for (int cp = c - 1; cp >= 0; cp -= 2) {
-    step(cp, fa, fb);
-    if (cp - 1 < 0) break;
-    step(cp - 1, fb, fa);
+  if constexpr (KPL > 1 && D == 128) {
+    // bf16, d = 128: the key chunk's level rows and V rows are loaded one
+    // key chunk ahead into one register set, right after the products that
+    // read them are issued; its gate values and transposed level rows (A
+    // operands of the dQa product) are loaded before the next chunk's, ahead
+    // of the softmax.  No operand is read from global memory inside a
+    // product.
+    frag kf[KSD], vf[KSD], lt[D / 32][KSK];
+    float kl[16];
+    auto fetch_kv = [&](int cp) __attribute__((always_inline)) {
+      const size_t blk = lev_c + (size_t)cp * C * D;
+      const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
+      const E *pk = levels + blk + (size_t)(32 * kh + col) * D + KPL * g;
+      const E *pv = v + (krow + col) * D + KPL * g;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        kf[ks] = MM<E>::ld(pk + 2 * KPL * ks, 1);
+        vf[ks] = MM<E>::ld(pv + 2 * KPL * ks, 1);
+      }
+    };
+    auto fetch_kl = [&](int cp) __attribute__((always_inline)) {
+      const size_t krow = (size_t)bh * T + (size_t)cp * C + 32 * kh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kl[r] = FOX ? lam[krow + acc_row(r, g)] : 0.f;
+    };
+    fetch_kv(c - 1);
+    const E *qb = Qs + (32 * qh + col) * PQ + KPL * g, *ob = Os + (32 * qh + col) * PQ + KPL * g;
+    for (int cp = c - 1; cp >= 0; --cp) {
+      const size_t blk = lev_c + (size_t)cp * C * D;
+      f32x16 s, dp;
+      zero16(s);
+      zero16(dp);
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        s = MM<E>::mma(kf[ks], MM<E>::ld(qb + 2 * KPL * ks, 1), s);
+        dp = MM<E>::mma(vf[ks], MM<E>::ld(ob + 2 * KPL * ks, 1), dp);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // this key chunk's gate values and transposed rows, then the next key
+      // chunk's operands
+      if constexpr (FOX) fetch_kl(cp);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          lt[t][ks] = MM<E>::ld(levt + blk + (size_t)(32 * t + col) * C + 32 * kh + KPL * g + 2 * KPL * ks, 1);
+      fetch_kv(cp > 0 ? cp - 1 : 0);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 gt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __expf(scale * s[r] + q_lam - (FOX ? kl[r] : 0.f) - q_lse);
+        const float ds = p * (dp[r] - q_d + q_dl);
+        rowsum += ds;
+        gt[r] = scale * ds;
+      }
+      st_tile(Gw, 1, PG, gt, lane);   // Gw[q][key] = g(q, key)
+      wave_sync();
+      // dQa^T(d, q) += sum_key Khat(key, d) g(q, key)
+      const E *gb = Gw + col * PG + KPL * g;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          dq[t] = MM<E>::mma(lt[t][ks], MM<E>::ld(gb + 2 * KPL * ks, 1), dq[t]);
+      wave_sync();
+    }
+  } else {
+    Frags fa, fb;
+    fetch(c - 1, fa);
+    for (int cp = c - 1; cp >= 0; cp -= 2) {
+      step(cp, fa, fb);
+      if (cp - 1 < 0) break;
+      step(cp - 1, fb, fa);
+    }
   }
   // combine the two key halves, then store dQa rows
   float *rq = red + qh * 32 * (D + 1);
