@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     F32,
     NOALLOC_MAX_BYTES,
     NO_SKIP,
+    PRECISE,
     PathAttnError,
     chunk_prep,
     library_path,
@@ -37,7 +38,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "BF16", "DecodeCache", "F32", "NOALLOC_MAX_BYTES", "NO_SKIP", "PathAttnError", "chunk_prep", "library_path",
+    "BF16", "DecodeCache", "F32", "NOALLOC_MAX_BYTES", "NO_SKIP", "PRECISE", "PathAttnError", "chunk_prep", "library_path",
     "load_library", "path_attn_bwd", "path_attn_bwd_varlen",
     "path_attn_bwd_varlen_workspace_bytes", "path_attn_bwd_workspace_bytes",
     "path_attn_bwd_workspace_bytes_window",

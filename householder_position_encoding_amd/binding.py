@@ -182,7 +182,7 @@ def path_attn_fwd(q, k, v, w, beta, logf=None, out=None, lse=None,
     Returns (out [B, H, T, d] in q's dtype, lse [B, H, T] fp32).  A workspace
     (uint8 CUDA tensor of at least path_attn_workspace_bytes bytes) may be
     passed to avoid an allocation.  scale: softmax scale (None: 1/sqrt(d));
-    flags: 0 or NO_SKIP (path_attn_fwd_ex).
+    flags: 0, or NO_SKIP and/or PRECISE (path_attn_fwd_ex).
     """
     torch = _torch()
     B, H, T, d, dt = _common(q, k, v, w, beta, logf)
@@ -284,6 +284,7 @@ def path_attn_prepare(q, k, v, w, beta, logf=None, workspace=None, stream=None):
 
 
 NO_SKIP = 1   # PATH_ATTN_NO_SKIP
+PRECISE = 2   # PATH_ATTN_PRECISE
 
 
 def path_attn_stream(workspace, use_gate, out, lse, stream=None, flags=0,

@@ -112,16 +112,19 @@ struct Carved {
   char *base;
   FullLayout F;
   int dp;
+  void *klo;   // ->K remainders for the precise scan (bf16 with PATH_ATTN_PRECISE), else null
 };
 
 Carved carve(void *workspace, int B, int H, int T, int d, int dtype, bool views = false,
-             int dp = 0) {
+             int dp = 0, unsigned flags = 0) {
   const FullLayout F = full_layout(B, H, T, d, dtype, views, dp);
   char *base = static_cast<char *>(workspace);
+  const bool precise = dtype == PATH_ATTN_BF16 && (flags & PATH_ATTN_PRECISE);
   return Carved{reinterpret_cast<float *>(base + F.base.qa), base + F.base.kvm,
                 reinterpret_cast<float *>(base + F.base.al),
                 reinterpret_cast<float *>(base + F.base.gate),
-                reinterpret_cast<float2 *>(base + F.base.bnd), base, F, dp > 0 ? dp : d};
+                reinterpret_cast<float2 *>(base + F.base.bnd), base, F, dp > 0 ? dp : d,
+                precise ? base + F.base.klo : nullptr};
 }
 
 // The streaming scan at the padded length; with staging into the staging
@@ -139,6 +142,7 @@ int run_stream(const Carved &ws, bool gate, unsigned flags,
   a.bnd = ws.bnd;
   a.skip = gate && !(flags & PATH_ATTN_NO_SKIP);
   a.skipped = skipped;
+  a.klo = ws.klo;
   const bool staged = ws.F.staged && !in_place;
   a.out = staged ? static_cast<void *>(ws.base + ws.F.out) : out;
   a.lse = staged ? reinterpret_cast<float *>(ws.base + ws.F.lse) : lse;
@@ -200,8 +204,8 @@ int run_prep(const void *q, const void *k, const void *v, const void *w,
   }
   if (logf && launch_gate_prefix(logf, ws.gate, BH, Tp, io, s) != hipSuccess)
     return PATH_ATTN_EHIP;
-  if (launch_prep(dtype, d, ws.dp, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, io, s) !=
-      hipSuccess)
+  if (launch_prep(dtype, d, ws.dp, q, k, v, w, beta, ws.qa, ws.kvm, ws.al, BH, Tp, io, s,
+                  ws.klo) != hipSuccess)
     return PATH_ATTN_EHIP;
   if (logf &&
       launch_chunk_bounds(dtype, d, ws.dp, ws.kvm, ws.gate, ws.bnd, BH, Tp, s) != hipSuccess)
@@ -226,9 +230,9 @@ extern "C" int path_attn_fwd_ex(const void *q, const void *k, const void *v,
   if (st != PATH_ATTN_OK) return st;
   if (!out || !lse) return PATH_ATTN_EINVAL;
   if (!aligned(out, 16) || !aligned(lse, 16)) return PATH_ATTN_EINVAL;
-  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)(PATH_ATTN_NO_SKIP | PATH_ATTN_PRECISE))) return PATH_ATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Carved ws = carve(workspace, B, H, T, d, dtype);
+  const Carved ws = carve(workspace, B, H, T, d, dtype, false, 0, flags);
   const FwdViews views = dense_fwd_views(H, T, d);
   st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
   if (st != PATH_ATTN_OK) return st;
@@ -262,9 +266,9 @@ extern "C" int path_attn_fwd_partial(const void *q, const void *k, const void *v
   if (!aligned(workspace, 256) ||
       workspace_bytes < full_layout(B, H, T, d, dtype, false, d_path).total)
     return PATH_ATTN_EINVAL;
-  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)(PATH_ATTN_NO_SKIP | PATH_ATTN_PRECISE))) return PATH_ATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Carved ws = carve(workspace, B, H, T, d, dtype, false, d_path);
+  const Carved ws = carve(workspace, B, H, T, d, dtype, false, d_path, flags);
   const FwdViews views = dense_fwd_views(H, T, d);
   st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
   if (st != PATH_ATTN_OK) return st;
@@ -328,7 +332,7 @@ extern "C" int path_attn_fwd_noalloc(const void *q, const void *k, const void *v
   for (const void *p : ptrs)
     if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
   if (logf && !aligned(logf, 16)) return PATH_ATTN_EINVAL;
-  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)(PATH_ATTN_NO_SKIP | PATH_ATTN_PRECISE))) return PATH_ATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int dev = -1;
   if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
@@ -336,7 +340,7 @@ extern "C" int path_attn_fwd_noalloc(const void *q, const void *k, const void *v
   void *ws_addr = nullptr;
   st = scratch_address(dev, &ws_addr);
   if (st != PATH_ATTN_OK) return st;
-  const Carved ws = carve(ws_addr, B, H, T, d, dtype);
+  const Carved ws = carve(ws_addr, B, H, T, d, dtype, false, 0, flags);
   const FwdViews views = dense_fwd_views(H, T, d);
   st = run_prep(q, k, v, w, beta, logf, ws, B, H, T, d, dtype, views, s);
   if (st != PATH_ATTN_OK) return st;
@@ -394,7 +398,7 @@ extern "C" int path_attn_fwd_varlen(const void *q, const void *k, const void *v,
   if (st != PATH_ATTN_OK) return st;
   if (!q || !k || !v || !w || !beta || !out || !lse || !strides || !workspace)
     return PATH_ATTN_EINVAL;
-  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)(PATH_ATTN_NO_SKIP | PATH_ATTN_PRECISE))) return PATH_ATTN_EINVAL;
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return PATH_ATTN_EINVAL;
   const void *ptrs[] = {q, k, v, w, out, beta, logf, lse};
   const size_t e = elem_size(dtype);
@@ -403,7 +407,7 @@ extern "C" int path_attn_fwd_varlen(const void *q, const void *k, const void *v,
   if (!aligned(workspace, 256) || workspace_bytes < full_layout(B, H, T, d, dtype, true).total)
     return PATH_ATTN_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Carved ws = carve(workspace, B, H, T, d, dtype, true);
+  const Carved ws = carve(workspace, B, H, T, d, dtype, true, 0, flags);
   FwdViews views;
   for (int i = 0; i < 8; ++i) views.v[i] = make_view(strides + 3 * i, cu_seqlens);
   const bool direct = in_place_ok(ptrs, strides, cu_seqlens, T, dtype);
@@ -436,6 +440,7 @@ extern "C" int path_attn_stream_ex(const void *workspace, size_t workspace_bytes
   if (!workspace || !out || !lse) return PATH_ATTN_EINVAL;
   if (use_gate != 0 && use_gate != 1) return PATH_ATTN_EINVAL;
   if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
+  // PATH_ATTN_PRECISE needs ->K's remainders, which only the one-shot calls write
   if (flags & ~(unsigned)PATH_ATTN_NO_SKIP) return PATH_ATTN_EINVAL;
   if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse, 16))
     return PATH_ATTN_EINVAL;

@@ -124,7 +124,7 @@ inline FwdIo dense_io(int H, int T, int d) {
 }
 
 struct Layout {
-  size_t qa, kvm, al, gate, bnd, total;
+  size_t qa, kvm, al, gate, bnd, klo, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -143,6 +143,10 @@ inline Layout make_layout(int B, int H, int T, int D, size_t esize, int DP) {
   off = align256(off + BH * T * sizeof(float));
   L.bnd = off;
   off = align256(off + BH * N * 2 * sizeof(float));
+  // bf16: the rounding remainder of ->K (same blob order as ->K in the
+  // operand block), written only for the precise scan
+  L.klo = off;
+  off = align256(off + (esize == 2 ? BH * T * D * esize : 0));
   L.total = off;
   return L;
 }
@@ -154,10 +158,11 @@ hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, con
                               hipStream_t stream);
 // DP: the leading coordinates the factors act on (D for PaTH on every
 // coordinate; D / 2 for partial PaTH, whose w is not read beyond them).
+// klo (bf16, may be null): also store ->K's rounding remainders there.
 hipError_t launch_prep(int dtype, int D, int DP, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
-                       const FwdIo &io, hipStream_t stream);
+                       const FwdIo &io, hipStream_t stream, void *klo = nullptr);
 hipError_t launch_chunk_bounds(int dtype, int D, int DP, const void *kvm,
                                const float *gate, float2 *bnd, int BH, int T,
                                hipStream_t stream);
@@ -179,6 +184,7 @@ struct StreamArgs {
   float sl2;   // softmax scale times log2(e)
   int H;                // bh = b * H + h
   TokStrides so, sl;    // out and lse row (b, h, t) at b so.b + h so.h + t so.t
+  const void *klo;      // bf16: ->K's rounding remainders; set: the precise scan
 };
 hipError_t launch_stream(int dtype, int D, int DP, bool fox, const StreamArgs &a,
                          hipStream_t stream);

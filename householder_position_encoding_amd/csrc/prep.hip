@@ -218,7 +218,8 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k,
     const __bf16 *__restrict__ v, const __bf16 *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ qa,
-    __bf16 *__restrict__ kvm, float *__restrict__ al, int T, int total, FwdIo io) {
+    __bf16 *__restrict__ kvm, float *__restrict__ al, int T, int total, FwdIo io,
+    __bf16 *__restrict__ klo) {
   constexpr int C = kChunk, P = 72, PX = 72;
   constexpr int NDB = D / 32, NSD = D / 16, NSK = C / 16, KSD = D / 16, KSC = C / 16;
   constexpr int TPW = D / 64;                       // d x 64 tiles per wave
@@ -570,10 +571,16 @@ __global__ __launch_bounds__(256, 2) void prep_bf16_kernel(
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 x;
+        bf16x8 x, xl;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = (__bf16)(kinit[h][8 * hh + t] - kacc[8 * hh + t]);
-        *reinterpret_cast<bf16x8 *>(kf + ((ib * NSD + 2 * eb + hh) * 64 + lane) * 8) = x;
+        for (int t = 0; t < 8; ++t) {
+          const float y = kinit[h][8 * hh + t] - kacc[8 * hh + t];
+          x[t] = (__bf16)y;
+          xl[t] = (__bf16)(y - (float)x[t]);
+        }
+        const size_t o = ((ib * NSD + 2 * eb + hh) * 64 + lane) * 8;
+        *reinterpret_cast<bf16x8 *>(kf + o) = x;
+        if (klo) *reinterpret_cast<bf16x8 *>(klo + ((size_t)bh * N + c) * C * D + o) = xl;
       }
     }
     // -M^T in MF fragment blobs: M = W^T (U W), tile (ab, bb) = (tau % NDB,
@@ -849,7 +856,7 @@ template <int D, int DP>
 hipError_t launch_prep_bf16(const void *q, const void *k, const void *v,
                             const void *w, const float *beta, float *qa,
                             void *kvm, float *al, int BH, int T, const FwdIo &io,
-                            hipStream_t stream) {
+                            hipStream_t stream, void *klo) {
   const int total = BH * (T / kChunk);
   // d = 64: persistent blocks, two per compute unit (the LDS of one block is
   // 63 KiB), each walking total / grid chunks.
@@ -863,7 +870,7 @@ hipError_t launch_prep_bf16(const void *q, const void *k, const void *v,
   hipLaunchKernelGGL((prep_bf16_kernel<D, DP>), dim3(grid), dim3(256), 0,
                      stream, (const __bf16 *)q, (const __bf16 *)k,
                      (const __bf16 *)v, (const __bf16 *)w, beta, qa,
-                     (__bf16 *)kvm, al, T, total, io);
+                     (__bf16 *)kvm, al, T, total, io, (__bf16 *)klo);
   return hipGetLastError();
 }
 
@@ -955,14 +962,14 @@ hipError_t launch_gate_prefix(const float *logf, float *gate, int BH, int T, con
 hipError_t launch_prep(int dtype, int D, int DP, const void *q, const void *k,
                        const void *v, const void *w, const float *beta,
                        float *qa, void *kvm, float *al, int BH, int T,
-                       const FwdIo &io, hipStream_t stream) {
+                       const FwdIo &io, hipStream_t stream, void *klo) {
   const bool half = DP != D;
   if (dtype == 1) {
     if (D == 64)
-      return half ? launch_prep_bf16<64, 32>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream)
-                  : launch_prep_bf16<64, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
-    return half ? launch_prep_bf16<128, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream)
-                : launch_prep_bf16<128, 128>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream);
+      return half ? launch_prep_bf16<64, 32>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream, klo)
+                  : launch_prep_bf16<64, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream, klo);
+    return half ? launch_prep_bf16<128, 64>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream, klo)
+                : launch_prep_bf16<128, 128>(q, k, v, w, beta, qa, kvm, al, BH, T, io, stream, klo);
   }
   if (D == 64)
     return half ? launch_prep_f32<64, 32>(q, k, v, w, beta, qa, kvm, al, BH, T, stream)

@@ -57,6 +57,15 @@ struct Mfma<__bf16> {
     for (int t = 0; t < 8; ++t) f[t] = (__bf16)acc[(s * 8 + t) / 16][(s * 8 + t) % 16];
     return f;
   }
+  // The rounding remainder of pack(acc, s): acc - hi, rounded to bf16.
+  template <int NB>
+  __device__ static __forceinline__ frag pack_lo(const f32x16 (&acc)[NB], int s, frag hi) {
+    frag f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      f[t] = (__bf16)(acc[(s * 8 + t) / 16][(s * 8 + t) % 16] - (float)hi[t]);
+    return f;
+  }
   __device__ static __forceinline__ frag load(const __bf16 *p) {
     return *reinterpret_cast<const frag *>(p);
   }
@@ -137,13 +146,17 @@ __device__ __forceinline__ float logit_bound(float qn2, float2 b, float sl2) {
 // DP: the leading coordinates the chunk transitions act on (D, or D / 2 for
 // partial PaTH: -M^T is DP x DP and the transition product touches only the
 // first DP rows of the running tile).
-template <typename E, int D, int DP, bool FOX, int NQC, int PD>
+// PREC (bf16): the S product takes the running query tile and ->K_c as bf16
+// hi + lo pairs (Q_hi K_hi + Q_lo K_hi + Q_hi K_lo), so neither rounding
+// enters the logits; ->K_c's remainders (klo, same blob order) are staged
+// after the operand block.
+template <typename E, int D, int DP, bool FOX, int NQC, int PD, bool PREC = false>
 __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     const float *__restrict__ qa, const E *__restrict__ kvm,
     const float *__restrict__ al, const float *__restrict__ gate,
     const float2 *__restrict__ bnd, int skip, unsigned long long *__restrict__ skipped,
     E *__restrict__ out, float *__restrict__ lse, int BH, int T, float sl2, int H,
-    TokStrides so, TokStrides sl) {
+    TokStrides so, TokStrides sl, const E *__restrict__ klo) {
   using MF = Mfma<E>;
   using frag = typename MF::frag;
   constexpr int C = kChunk, KPL = MF::KPL, KSTEP = 2 * KPL;
@@ -161,7 +174,11 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   constexpr int NL = (NBLK + NW - 1) / NW;        // per wave (the last round partly)
   static_assert(KVM_BYTES % 1024 == 0, "operand block in whole KiB");
   static_assert(PD < 2 || NBLK % NW == 0, "deep prefetch counts copies per wave");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * KVM_BYTES];
+  constexpr int KLO_BYTES = PREC ? C * D * (int)sizeof(E) : 0;   // ->K remainders
+  constexpr int BUFB = KVM_BYTES + KLO_BYTES;                      // one LDS buffer
+  constexpr int NBLO = KLO_BYTES / 1024, NLL = (NBLO + NW - 1) / NW;
+  static_assert(!PREC || (PD < 2 && std::is_same<E, __bf16>::value), "precise: bf16, PD <= 1");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * BUFB];
   __shared__ __attribute__((aligned(16))) float gate_l[FOX ? NBUF * C : 1];
 
   const int N = T / C;
@@ -186,11 +203,20 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
     if (FOX && wave == 0)
       copy4_to_lds(gate_h + (size_t)c * C + lane, lds_addr(gate_l + buf * C));
     const unsigned char *src = reinterpret_cast<const unsigned char *>(kvm_h + (size_t)c * KVM);
-    unsigned char *dst = lds + buf * KVM_BYTES;
+    unsigned char *dst = lds + buf * BUFB;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int j = wave + i * NW;
       if (NBLK % NW == 0 || j < NBLK) copy16_to_lds(src + j * 1024 + lane * 16, lds_addr(dst + j * 1024));
+    }
+    if constexpr (PREC) {
+      const unsigned char *slo =
+          reinterpret_cast<const unsigned char *>(klo + ((size_t)bh * N + c) * C * D);
+#pragma unroll
+      for (int i = 0; i < NLL; ++i) {
+        const int j = wave + i * NW;
+        if (j < NBLO) copy16_to_lds(slo + j * 1024 + lane * 16, lds_addr(dst + KVM_BYTES + j * 1024));
+      }
     }
   };
 
@@ -281,8 +307,9 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
   for (int c = c_top; c >= 0; --c) {
     const int buf = c % NBUF;
     if (PD > 0 && c - PD >= 0) stage(c - PD, (c - PD) % NBUF);
-    const E *kf_l = reinterpret_cast<const E *>(lds + buf * KVM_BYTES);
+    const E *kf_l = reinterpret_cast<const E *>(lds + buf * BUFB);
     const E *vf_l = kf_l + C * D;
+    const E *kl_l = reinterpret_cast<const E *>(lds + buf * BUFB + KVM_BYTES);   // PREC
     const E *mf_l = vf_l + C * D;
     const float *ga = gate_l + buf * C + 4 * g;
 
@@ -324,12 +351,29 @@ __global__ __launch_bounds__(NQC * 128) void stream_kernel(
       if (!skip_blk) {
         // S^T = ->K_c Q_work^T
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sc[mb][r] = 0.f;
+        if constexpr (PREC) {
+          // one lo fragment live at a time
 #pragma unroll
-          for (int s = 0; s < NSD; ++s)
-            sc[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], sc[mb]);
+          for (int s = 0; s < NSD; ++s) {
+            const frag lo = MF::pack_lo(qw, s, qb[s]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+              const frag a = MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL);
+              const frag al = MF::load(kl_l + (mb * NSD + s) * FRAG + lane * KPL);
+              sc[mb] = MF::run(a, qb[s], sc[mb]);
+              sc[mb] = MF::run(a, lo, sc[mb]);
+              sc[mb] = MF::run(al, qb[s], sc[mb]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int s = 0; s < NSD; ++s)
+              sc[mb] = MF::run(MF::load(kf_l + (mb * NSD + s) * FRAG + lane * KPL), qb[s], sc[mb]);
         }
       }
       // Q_work^T <- Q_work^T - M_c^T round(Q_work^T): crossing chunk c's
@@ -772,6 +816,18 @@ template <typename E, int D, int DP, bool FOX>
 hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int N = a.T / kChunk;
   const float sl2 = a.sl2;
+  if constexpr (std::is_same<E, __bf16>::value) {
+    if (a.klo) {   // precise: the narrow kernel with hi/lo operands in S
+      // two buffers of 32 KiB at d = 64; one of 80 KiB at d = 128
+      constexpr int NQC = D == 64 ? 2 : 4, PD = D == 64 ? 1 : 0;
+      const int blocks = a.BH * ((N + NQC - 1) / NQC);
+      hipLaunchKernelGGL((stream_kernel<E, D, DP, FOX, NQC, PD, true>), dim3(blocks),
+                         dim3(NQC * 128), 0, stream, a.qa, (const E *)a.kvm, a.al, a.gate, a.bnd,
+                         a.skip, a.skipped, (E *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl,
+                         (const E *)a.klo);
+      return hipGetLastError();
+    }
+  }
   if constexpr (std::is_same<E, __bf16>::value && D == 64 && PATH_ATTN_WIDE_BF16_64) {
     // A block runs as long as its longest wave, and wave j of query group g
     // walks NQC g + j + 1 key chunks.  Eight chunks per block share each staged
@@ -795,7 +851,7 @@ hipError_t launch_stream_t(const StreamArgs &a, hipStream_t stream) {
   const int blocks = a.BH * ((N + NQC - 1) / NQC);
   hipLaunchKernelGGL((stream_kernel<E, D, DP, FOX, NQC, PD>), dim3(blocks), dim3(NQC * 128), 0,
                      stream, a.qa, (const E *)a.kvm, a.al, a.gate, a.bnd, a.skip, a.skipped,
-                     (E *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl);
+                     (E *)a.out, a.lse, a.BH, a.T, sl2, a.H, a.so, a.sl, (const E *)nullptr);
   return hipGetLastError();
 }
 

@@ -75,6 +75,10 @@ extern "C" {
 /* Flags of path_attn_stream_ex. */
 #define PATH_ATTN_NO_SKIP 1u    /* compute every key block, even those the exact
                                    forget-gate skip would leave out */
+#define PATH_ATTN_PRECISE 2u    /* bf16: cross-chunk logits from the running
+                                   query tile as a bf16 hi + lo pair (for sharp
+                                   attention; one more product per logit
+                                   block); no effect for float32 */
 
 /*
  * Workspace size in bytes that path_attn_fwd / path_attn_chunk_prep need for
@@ -83,8 +87,10 @@ extern "C" {
  * queries (float32), the transformed keys, the values and the chunk transform
  * in the matrix-core operand order, the diagonal-block logits (float32) and
  * two float32 bounds used with the forget gate; per token, the forget-gate
- * prefix (float32).  When T is not a multiple of 64, it also holds the
- * zero-padded staging copies of q, k, v, w, beta, logf, out and lse.
+ * prefix (float32) and, for bf16, the rounding remainders of the transformed
+ * keys (written only for PATH_ATTN_PRECISE).  When T is not a multiple of
+ * 64, it also holds the zero-padded staging copies of q, k, v, w, beta,
+ * logf, out and lse.
  */
 size_t path_attn_workspace_bytes(int B, int H, int T, int d, int dtype);
 
@@ -113,7 +119,15 @@ int path_attn_fwd(const void *q, const void *k, const void *v, const void *w,
  * path logits c_ij in place of 1/sqrt(d) (the authors' listing passes
  * `scale` as an argument); scale = 0 selects 1/sqrt(d).  A negative,
  * infinite or NaN scale is EINVAL (the scan takes each block's maximum on the
- * raw scores, which needs scale > 0).  flags: 0 or PATH_ATTN_NO_SKIP.
+ * raw scores, which needs scale > 0).  flags: 0, or PATH_ATTN_NO_SKIP and/or
+ * PATH_ATTN_PRECISE.  PATH_ATTN_PRECISE (bf16) feeds the S product of every
+ * cross-chunk block the running query tile as a bf16 hi + lo pair instead of
+ * its bf16 rounding, and the transformed keys ->K likewise (hi from the
+ * operand block, lo from remainders the chunk preparation then also
+ * writes): the two roundings otherwise set a relative error of about 2^-9 on
+ * those logits, which matters for sharp attention (large logits).  It runs
+ * the 32-query scan kernel with three products per S tile, slower than the
+ * default.
  * path_attn_fwd(...) == path_attn_fwd_ex(..., 0.0f, 0, ...).
  */
 int path_attn_fwd_ex(const void *q, const void *k, const void *v, const void *w,
@@ -195,7 +209,10 @@ int path_attn_stream(const void *workspace, size_t workspace_bytes,
  * "FoX adds a separate mechanism for forgetting"); the skip itself is this
  * library's, not the pages'.  The chunk transitions are always applied.
  *
- * flags:   0 or PATH_ATTN_NO_SKIP (compute every block).
+ * flags:   0 or PATH_ATTN_NO_SKIP (compute every block); PATH_ATTN_PRECISE
+ *          is EINVAL here (it needs ->K's rounding remainders, which only
+ *          the one-shot calls write: path_attn_fwd_ex, _partial, _varlen,
+ *          _noalloc).
  * skipped: NULL, or a device counter (8-byte aligned) to which the scan adds
  *          the number of steps it skipped, one per wave and key block (a
  *          wave covers 32 queries, 64 for bf16 d = 64); the caller zeroes it.
