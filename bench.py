@@ -196,7 +196,7 @@ def bench_decode(wl, q, k, v, w, beta, logf, args, timed):
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     return {"context": int(t_mean), "key_cache": "f32", "ms_per_step": ms_step,
             "tokens_per_s": B / (ms_step * 1e-3), "ms_prefill_align": ms_prefill,
-            "roofline": {"kernel": "decode step (split-key refinement, merged by the last block)", "bound": "hbm",
+            "roofline": {"kernel": "decode step (split-key refinement kernel, then the merge kernel)", "bound": "hbm",
                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": nbytes}}
 
