@@ -75,8 +75,10 @@ __host__ __device__ constexpr size_t adj_floats(int D) { return 6 * 4096 + 64 * 
 // ([N][D][D]), Al ([N][64][64], zero above the diagonal) and the saved
 // matrices of the chunk; for the matrix-core sweep Qa and -M in the input
 // dtype (Qa rows [T][D], -M per chunk), and either the bf16 d = 64 operand
-// images or Qa^T and -M^T per chunk for the general kernel.
-template <typename E, int D>
+// images or Qa^T and -M^T per chunk for the general kernel.  SAVED_ONLY:
+// only the saved matrices (their bytes are shared with the sweep's buffers,
+// so they are computed again, the same bits, after the sweep).
+template <typename E, int D, bool SAVED_ONLY = false>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ w,
     const float *__restrict__ beta, float *__restrict__ kb,
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
   for (int ma = 0; ma < D / 64; ++ma)   // M = W^T (U W)
 #pragma unroll
-    for (int nb = 0; nb < D / 64; ++nb) {
+    for (int nb = 0; nb < D / 64 && !SAVED_ONLY; ++nb) {
       zero16(acc);
       gmm<64, true, false>(acc, W + 64 * ma, D, UWg + 64 * nb, D, PX, PY, tid);
       tile_each(tid, [&](int i, int j, int r) {
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   gmm<D, false, true>(acc, Q, D, W, D, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { Ag[i * 64 + j] = j <= i ? acc[r] : 0.f; });
 #pragma unroll
-  for (int nb = 0; nb < D / 64; ++nb) {   // <-Q = Q - A (U W)
+  for (int nb = 0; nb < D / 64 && !SAVED_ONLY; ++nb) {   // <-Q = Q - A (U W)
     zero16(acc);
     gmm<64, false, false>(acc, Ag, 64, UWg + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         img[64 * kImgPitch + mimg_index(i, d)] = (E)x;  // fragment order
       }
     });
-  if (IMG)   // zero padding of the image rows
+  if (IMG && !SAVED_ONLY)   // zero padding of the image rows
     for (int idx = tid; idx < 64 * (kImgPitch - 64); idx += NT)
       qimg[(size_t)chunk * kQImgElems + (idx / (kImgPitch - 64)) * kImgPitch + 64 +
            idx % (kImgPitch - 64)] = (E)0.f;
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   zero16(acc);   // T2 = U B
   gmm<64, false, false>(acc, Ug, 64, Bg, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { T2g[i * 64 + j] = acc[r]; });
+  if constexpr (SAVED_ONLY) return;
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // ->K = K - T2^T W
     zero16(acc);
@@ -510,16 +513,19 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   L.dmpart = take(bwd_dmpart_floats(dtype, (int)BH, T, D, window));
   L.ckpt = take(BH * P.ckpt_blocks * C * D);
   L.gstate = take(P.nwin > 1 ? BH * T * D : 0);
+  // after the sweep the same bytes hold the adjoint scratch and the saved
+  // per-chunk matrices, computed again for the adjoint (bwd_t)
   const size_t adj_bytes = align256(BH * N * adj_floats(D) * sizeof(float));
+  const size_t saved_bytes = align256(BH * N * saved_floats(D) * sizeof(float));
   L.adj = sweep0;
-  off = sweep0 + (off - sweep0 > adj_bytes ? off - sweep0 : adj_bytes);
+  L.saved = sweep0 + adj_bytes;
+  off = sweep0 + (off - sweep0 > adj_bytes + saved_bytes ? off - sweep0 : adj_bytes + saved_bytes);
   L.dv = take(BH * T * D);
   L.dlam = take(BH * T);
   L.dqa = take(BH * T * D);
   L.dkb = take(BH * T * D);
   L.dm = take(BH * N * D * D);
   L.dal = take(BH * N * C * C);
-  L.saved = take(BH * N * saved_floats(D));
   auto take_e = [&](size_t elems) { return take((elems * esize + 3) / 4); };
   const bool general = !(dtype == 1 && D == 64);   // the general dk kernel's operands
   L.qae = take_e(BH * T * D);
@@ -583,6 +589,10 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.T = T;
   sa.window = a.window;
   if (launch_bwd_sweep(dtype, D, FOX, sa, s) != hipSuccess) return hipGetLastError();
+  // the sweep has reused the saved matrices' bytes: compute them again
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D, true>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
+                     f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
+                     e(L.nmt), e(L.qimg), e(L.mimg), T);
   hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
                      f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.saved), f(L.adj), (E *)a.dq,
                      (E *)a.dk, (E *)a.dw, a.dbeta, T);
