@@ -190,7 +190,7 @@ __device__ __forceinline__ void lds_mm16(f32x4 &acc, const float *A, int ars, in
 template <typename KC, int D>
 __global__ __launch_bounds__(512) void align_scan_kernel(
     const float *__restrict__ kb, const float *__restrict__ m, KC *__restrict__ kcache,
-    int L, int T_cap) {
+    int L, int T_cap, int BH) {
   constexpr int C = kChunk, NT = 512, NW = 8, DP = D + 1, SW = 16, SP = SW + 1;
   constexpr int NSL = D / SW;                                   // column slices per head
   constexpr int NK4 = C * D / 4 / NT, NM4 = D * D / 4 / NT;    // float4 loads per thread
@@ -201,7 +201,12 @@ __global__ __launch_bounds__(512) void align_scan_kernel(
   __shared__ float Ms[D * DP];
   __shared__ float Gs[D * SP];
   const int N = L / C;
-  const int bh = blockIdx.x / NSL, sl = blockIdx.x % NSL;
+  // Blocks are dealt to the 8 XCDs round robin: block 8 (NSL g + sl) + r is
+  // slice sl of head 8 g + r, so every slice of a head runs on one XCD and
+  // the head's ->K and M are fetched into that XCD's L2 once.
+  const int grp8 = blockIdx.x / (8 * NSL), rem = blockIdx.x % (8 * NSL);
+  const int sl = rem / 8, bh = 8 * grp8 + rem % 8;
+  if (bh >= BH) return;   // the last group of eight heads may be partial
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, q4 = lane >> 4, cl = lane & 15;
 
   f32x4 kreg[NK4], mreg[NM4];
@@ -649,8 +654,8 @@ hipError_t prefill_t(const void *k, const void *v, const void *w, const float *b
   if (N > 0) {
     hipLaunchKernelGGL((align_prep_kernel<E, D>), dim3(BH * N), dim3(256), 0, stream,
                        (const E *)k, (const E *)w, beta, ws_kb, ws_m, L);
-    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3(BH * (D / 16)), dim3(512), 0, stream,
-                       ws_kb, ws_m, (KC *)kcache, L, T_cap);
+    hipLaunchKernelGGL((align_scan_kernel<KC, D>), dim3((BH + 7) / 8 * 8 * (D / 16)), dim3(512), 0, stream,
+                       ws_kb, ws_m, (KC *)kcache, L, T_cap, BH);
     const int gx = min(1024, (int)(((size_t)L * D + 255) / 256));
     hipLaunchKernelGGL((copy_rows_kernel<E>), dim3(gx, BH), dim3(256), 0, stream, (const E *)v,
                        (E *)vcache, L, T_cap, D);
