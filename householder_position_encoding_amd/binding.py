@@ -87,6 +87,10 @@ def load_library():
     lib.path_attn_bwd.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
                                   fp, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_bwd.restype = ci
+    lib.path_attn_bwd_ex.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, vp, vp, vp, fp,
+                                     fp, ci, ci, ci, ci, ci, ctypes.c_float, ctypes.c_uint, vp, sz,
+                                     vp]
+    lib.path_attn_bwd_ex.restype = ci
     lib.path_attn_varlen_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.path_attn_varlen_workspace_bytes.restype = sz
     lib.path_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, fp, fp, vp, fp, vp, vp, ci, ci, ci,
@@ -451,14 +455,15 @@ def path_attn_bwd_workspace_bytes_window(B: int, H: int, T: int, d: int, dtype: 
 
 
 def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
-                  workspace=None, stream=None, window=None):
+                  workspace=None, stream=None, window=None, flags=0):
     """Gradients of <dout, out> + <dlse, lse> for the forward of path_attn_fwd
     (out, lse: that forward's outputs).  Returns (dq, dk, dv, dw, dbeta,
     dlogf); dlogf is None without the gate.  Any T >= 1 (padded inside the
     library as in the forward).  Without a workspace, one of the smallest
     size is allocated, or with window given the size of
     path_attn_bwd_workspace_bytes_window (0: the whole sweep as one window,
-    the fastest); a larger workspace selects longer windows."""
+    the fastest); a larger workspace selects longer windows.  flags: 0 or
+    NO_SKIP (path_attn_bwd_ex: every block computed, no forget-gate skip)."""
     torch = _torch()
     B, H, T, d, dt = _common(q, k, v, w, beta, logf)
     _check(out, "out", q.shape, q.dtype, q.device)
@@ -476,13 +481,13 @@ def path_attn_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse=None, scale=None,
         need = lib.path_attn_bwd_workspace_bytes_window(B, H, T, d, dt, int(window))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.path_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
-                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk),
-                           _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), B, H, T, d, dt,
-                           0.0 if scale is None else float(scale), _ptr(workspace),
-                           workspace.numel(), _stream_handle(stream))
+    st = lib.path_attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(logf),
+                              _ptr(out), _ptr(lse), _ptr(dout), _ptr(dlse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(dw), _ptr(dbeta), _ptr(dlogf), B, H, T, d, dt,
+                              0.0 if scale is None else float(scale), int(flags),
+                              _ptr(workspace), workspace.numel(), _stream_handle(stream))
     if st != 0:
-        raise PathAttnError(st, "path_attn_bwd")
+        raise PathAttnError(st, "path_attn_bwd_ex")
     return dq, dk, dv, dw, dbeta, dlogf
 
 

@@ -546,7 +546,8 @@ int run_bwd(const void *q, const void *k, const void *v, const void *w, const fl
             const float *logf, const void *out, const float *lse, const void *dout,
             const float *dlse, void *dq, void *dk, void *dv, void *dw, float *dbeta,
             float *dlogf, int B, int H, int T, int d, int dtype, float scale,
-            const RowView *views, const BwdFull &F, void *workspace, hipStream_t s) {
+            const RowView *views, const BwdFull &F, void *workspace, hipStream_t s,
+            unsigned flags = 0) {
   const int Tp = padded(T);
   char *ws = static_cast<char *>(workspace);
   BwdArgs a{};
@@ -571,6 +572,7 @@ int run_bwd(const void *q, const void *k, const void *v, const void *w, const fl
   a.T = Tp;
   a.scale = scale_of(scale, d);
   a.window = F.window;
+  a.skip = (flags & PATH_ATTN_NO_SKIP) ? 0 : 1;
   const int e = (int)elem_size(dtype), row = d * e;
   if (F.staged) {   // gather the inputs at the padded length
     const void *vin[] = {q, k, v, w, out, dout};
@@ -633,15 +635,15 @@ extern "C" size_t path_attn_bwd_varlen_workspace_bytes(int B, int H, int T, int 
   return bwd_full(B, H, T, d, dtype, true, 0).total;
 }
 
-extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
-                             const float *beta, const float *logf, const void *out,
-                             const float *lse, const void *dout, const float *dlse, void *dq,
-                             void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
-                             int H, int T, int d, int dtype, float scale, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+extern "C" int path_attn_bwd_ex(const void *q, const void *k, const void *v, const void *w,
+                                const float *beta, const float *logf, const void *out,
+                                const float *lse, const void *dout, const float *dlse, void *dq,
+                                void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
+                                int H, int T, int d, int dtype, float scale, unsigned flags,
+                                void *workspace, size_t workspace_bytes, void *stream) {
   const int st = check_shape(B, H, T, d, dtype);
   if (st != PATH_ATTN_OK) return st;
-  if (!scale_ok(scale)) return PATH_ATTN_EINVAL;
+  if (!scale_ok(scale) || (flags & ~(unsigned)PATH_ATTN_NO_SKIP)) return PATH_ATTN_EINVAL;
   const void *need[] = {q, k, v, w, beta, out, lse, dout, dq, dk, dv, dw, dbeta, workspace};
   for (const void *p : need)
     if (!p) return PATH_ATTN_EINVAL;
@@ -654,7 +656,18 @@ extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const 
   RowView views[16];
   for (int i = 0; i < 16; ++i) views[i] = dense_view(H, T, i < 10 ? d : 1);
   return run_bwd(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta, dlogf, B,
-                 H, T, d, dtype, scale, views, F, workspace, static_cast<hipStream_t>(stream));
+                 H, T, d, dtype, scale, views, F, workspace, static_cast<hipStream_t>(stream),
+                 flags);
+}
+
+extern "C" int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
+                             const float *beta, const float *logf, const void *out,
+                             const float *lse, const void *dout, const float *dlse, void *dq,
+                             void *dk, void *dv, void *dw, float *dbeta, float *dlogf, int B,
+                             int H, int T, int d, int dtype, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return path_attn_bwd_ex(q, k, v, w, beta, logf, out, lse, dout, dlse, dq, dk, dv, dw, dbeta,
+                          dlogf, B, H, T, d, dtype, scale, 0u, workspace, workspace_bytes, stream);
 }
 
 extern "C" int path_attn_bwd_varlen(const void *q, const void *k, const void *v, const void *w,

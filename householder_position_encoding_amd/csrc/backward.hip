@@ -354,7 +354,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
     const float *__restrict__ saved, float *__restrict__ adj, E *__restrict__ dq,
     E *__restrict__ dk, E *__restrict__ dw, float *__restrict__ dbeta, int T) {
   __shared__ float PX[panel_floats(D)], PY[panel_floats(D)];
-  __shared__ float bs[C], dbs[C];
+  // dbeta's two sums, reduced in a fixed order (no atomics, so the same bits
+  // on every call): [half of the block's waves][token]
+  __shared__ float bs[C], dbx[2][C], dbn[2][C];
   const int N = T / C;
   const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
   const size_t row0 = (size_t)bh * T + (size_t)c * C;
@@ -367,10 +369,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
   float *dAg = adj + (size_t)chunk * adj_floats(D);
   float *dT2g = dAg + 4096, *dXg = dT2g + 4096, *Yg = dXg + 4096, *dNg = Yg + 4096, *dBg = dNg + 4096;
   float *dUWg = dBg + 4096;
-  if (tid < C) {
-    bs[tid] = beta[row0 + tid];
-    dbs[tid] = 0.f;
-  }
+  if (tid < C) bs[tid] = beta[row0 + tid];
   f32x16 acc, acc2;
 
   zero16(acc);   // dA
@@ -401,7 +400,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
       col = j;
       dXg[i * 64 + j] = du * bs[j];
     });
-    atomicAdd(&dbs[col], part);
+    // the column's 32 rows of this wave: both halves of the lane set
+    part += __shfl_xor(part, 32);
+    if ((tid & 63) < 32) dbx[tid >> 7][col] = part;
   }
   zero16(acc);   // dB
   gmm<64, true, false>(acc, Ug, 64, dT2g, 64, PX, PY, tid);
@@ -432,6 +433,9 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
       dk[row0 * D + o] = (E)(dKb[o] + acc[r]);
     });
   }
+  float rn[16];   // w_i . (dN W)_i over this wave's columns, per tile row
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rn[r] = 0.f;
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // dW
     f32x16 accn;
@@ -448,12 +452,22 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
     tile_each(tid, [&](int i, int j, int r) {
       const size_t o = (size_t)i * D + 64 * nb + j;
       const float wv = (float)W[o];
-      atomicAdd(&dbs[i], wv * accn[r]);
+      rn[r] = __builtin_fmaf(wv, accn[r], rn[r]);
       dw[row0 * D + o] = (E)(acc[r] - acc2[r] + bs[i] * accn[r]);
     });
   }
+  {   // each tile row's 32 columns of this wave (the lanes of one half)
+    const int lane = tid & 63, g = lane >> 5, wv = tid >> 6;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = rn[r];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+      if ((lane & 31) == 0) dbn[wv & 1][32 * (wv >> 1) + acc_row(r, g)] = x;
+    }
+  }
   __syncthreads();
-  if (tid < C) dbeta[row0 + tid] = dbs[tid];
+  if (tid < C) dbeta[row0 + tid] = (dbx[0][tid] + dbx[1][tid]) + (dbn[0][tid] + dbn[1][tid]);
 }
 
 // dv = dV in the input dtype (grid-stride over all heads).
@@ -513,6 +527,7 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   L.dmpart = take(bwd_dmpart_floats(dtype, (int)BH, T, D, window));
   L.ckpt = take(BH * P.ckpt_blocks * C * D);
   L.gstate = take(P.nwin > 1 ? BH * T * D : 0);
+  L.kn2 = take(BH * P.win_blocks * 2);   // level row norms for the forget-gate skip
   // after the sweep the same bytes hold the adjoint scratch and the saved
   // per-chunk matrices, computed again for the adjoint (bwd_t)
   const size_t adj_bytes = align256(BH * N * adj_floats(D) * sizeof(float));
@@ -537,6 +552,8 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   L.oimg = take_e(img ? BH * N * kQImgElems : 0);
   L.mimg = take_e(img ? BH * N * kMImgElems : 0);
   L.qst = take(img ? BH * T * 4 : 0);
+  L.qagg = take(BH * N * 2);
+  L.kmin = take(BH * N * 2);
   L.total = off;
   return L;
 }
@@ -584,6 +601,10 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.dm = f(L.dm);
   sa.ckpt = f(L.ckpt);
   sa.gstate = f(L.gstate);
+  sa.kn2 = f(L.kn2);
+  sa.qagg = reinterpret_cast<const float2 *>(ws + L.qagg);
+  sa.kmin = f(L.kmin);
+  sa.skip = a.skip;
   sa.scale = a.scale;
   sa.BH = BH;
   sa.T = T;

@@ -272,7 +272,7 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
                                                             __bf16 *__restrict__ levels,
                                                             __bf16 *__restrict__ levt, int T,
                                                             int BH, Win win, Ckpt ck,
-                                                            int ck_pass) {
+                                                            int ck_pass, float *__restrict__ kn2) {
   using E = __bf16;
   constexpr int G = 4, P = D + 8, WARM = G - 1;
   constexpr bool WT = D != 64;            // transposed copy
@@ -338,11 +338,28 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
         }
         wave_sync();
         E *dst = levels + off + (size_t)32 * kh * D;
+        float nmax = 0.f;   // with kn2: the largest squared row norm of the stored level
 #pragma unroll
         for (int j = 0; j < RV; ++j) {
           const int vi = j * 64 + lane, row = vi / (D / 8), c16 = 8 * (vi % (D / 8));
-          *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) =
-              *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+          const uint4 val = *reinterpret_cast<const uint4 *>(Xw + row * P + c16);
+          *reinterpret_cast<uint4 *>(dst + (size_t)row * D + c16) = val;
+          if (kn2) {
+            bf16x8 x;
+            __builtin_memcpy(&x, &val, 16);
+            float ss = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) ss = __builtin_fmaf((float)x[t], (float)x[t], ss);
+#pragma unroll
+            for (int o = 1; o < D / 8; o <<= 1) ss += __shfl_xor(ss, o);   // the row's D / 8 lanes
+            nmax = fmaxf(nmax, ss);
+          }
+        }
+        if (kn2) {
+          nmax = fmaxf(nmax, __shfl_xor(nmax, 16));
+          nmax = fmaxf(nmax, __shfl_xor(nmax, 32));
+          if (D == 64) nmax = fmaxf(nmax, __shfl_xor(nmax, 8));
+          if (lane == 0) kn2[off / ((size_t)C * D) * 2 + kh] = nmax;
         }
       }
       if (c + 1 < c_end) {   // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
@@ -390,6 +407,64 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
   else walk(std::false_type{});
 }
 
+// ------------------------------------------------------------------ skip bounds
+
+// Exact forget-gate skip.  A logit of query q against key j in the sweep is
+//     scale * Qa_q . Khat_j + Lambda_q - Lambda_j,
+// and its weight exp(logit - lse_q) underflows to exactly zero in float32
+// once logit - lse_q < -112 (e^-112 is below the smallest denormal).  With
+// |Qa_q . Khat_j| <= |Qa_q| |Khat_j| (the bf16 values the products take,
+// float32 sums: the factor 1.01 covers their rounding), a block of query
+// chunk c and 32 keys (key half h of chunk c') is all zeros when
+//     scale sqrt(max_q |Qa_q|^2 * max_j |Khat_j|^2) * 1.01
+//         + max_q (Lambda_q - lse_q) - min_j Lambda_j + 1 < -112;
+// its dS is then exactly zero and leaving out its products changes no bit
+// (the level walk still crosses it).  This kernel gives the per-chunk query
+// terms and the per-half key terms; the level walk gives max |Khat_j|^2.
+constexpr float kBwdSkipBelow = -112.f;
+// Key chunks a dq wave can list (its query chunk's index, at most): the
+// host enables the skip only for N <= kBwdSkipList.
+constexpr int kBwdSkipList = 2048;
+
+__device__ __forceinline__ bool bwd_block_vanishes(float scale, float2 qa, float kn2, float kmin) {
+  const float b = __builtin_fmaf(scale * __builtin_sqrtf(qa.x * kn2), 1.01f, qa.y - kmin + 1.f);
+  return b < kBwdSkipBelow;   // false for NaN: such blocks are computed
+}
+
+// One wave per (bh, chunk): lane t is token t of the chunk.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void bwd_skip_stats_kernel(const E *__restrict__ qae,
+                                                             const float *__restrict__ lam,
+                                                             const float *__restrict__ lse,
+                                                             float2 *__restrict__ qagg,
+                                                             float *__restrict__ kmin, int T) {
+  const int N = T / C;
+  const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N, lane = threadIdx.x;
+  const size_t row = (size_t)bh * T + (size_t)c * C + lane;
+  float n2 = 0.f;
+  const E *qr = qae + row * D;
+  constexpr int V = 16 / (int)sizeof(E);   // elements per 16-byte load
+#pragma unroll
+  for (int d = 0; d < D; d += V) {
+    E x[V];
+    __builtin_memcpy(x, qr + d, 16);
+#pragma unroll
+    for (int t = 0; t < V; ++t) n2 = __builtin_fmaf((float)x[t], (float)x[t], n2);
+  }
+  float g = lam[row] - lse[row], l = lam[row];
+  if (!(n2 <= 3.0e38f)) n2 = INFINITY;   // NaN or inf: never skip
+  if (!(g <= 3.0e38f)) g = INFINITY;
+  if (!(l >= -3.0e38f)) l = -INFINITY;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    n2 = fmaxf(n2, __shfl_xor(n2, o));
+    g = fmaxf(g, __shfl_xor(g, o));
+    if (o < 32) l = fminf(l, __shfl_xor(l, o));   // per half of 32 keys
+  }
+  if (lane == 0) qagg[chunk] = make_float2(n2, g);
+  if ((lane & 31) == 0) kmin[(size_t)chunk * 2 + lane / 32] = l;
+}
+
 // ------------------------------------------------------------------ dq
 
 // One block of 4 waves per (bh, query chunk c): wave (qh, kh) = (w & 1, w >> 1)
@@ -401,7 +476,9 @@ __global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void
     const E *__restrict__ qae, const E *__restrict__ dout, const float *__restrict__ lse,
     const float *__restrict__ dlse, const float *__restrict__ dvec, const float *__restrict__ lam,
     const E *__restrict__ levels, const E *__restrict__ levt, const E *__restrict__ v,
-    float scale, float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH, Win win) {
+    float scale, float *__restrict__ dqa, float *__restrict__ dlam, int T, int BH, Win win,
+    const float *__restrict__ kn2, const float2 *__restrict__ qagg, const float *__restrict__ kmin,
+    int skip) {
   constexpr int PQ = D + MM<E>::PAD;          // Qs, Os: [64 q][D]
   constexpr int PG = 32 + MM<E>::PAD;         // Gs: per wave [32 q][32 keys]
   __shared__ __attribute__((aligned(16))) E Qs[C * PQ];
@@ -545,9 +622,9 @@ __global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void
 #pragma unroll
       for (int r = 0; r < 16; ++r) kl[r] = FOX ? lam[krow + acc_row(r, g)] : 0.f;
     };
-    fetch_kv(c - 1);
     const E *qb = Qs + (32 * qh + col) * PQ + KPL * g, *ob = Os + (32 * qh + col) * PQ + KPL * g;
-    for (int cp = c - 1; cp >= 0; --cp) {
+    // one key chunk cp; the next one in the walk is cpn
+    auto step128 = [&](int cp, int cpn) __attribute__((always_inline)) {
       const size_t blk = lev_c + (size_t)cp * C * D;
       f32x16 s, dp;
       zero16(s);
@@ -566,7 +643,7 @@ __global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
           lt[t][ks] = MM<E>::ld(levt + blk + (size_t)(32 * t + col) * C + 32 * kh + KPL * g + 2 * KPL * ks, 1);
-      fetch_kv(cp > 0 ? cp - 1 : 0);
+      fetch_kv(cpn);
       __builtin_amdgcn_sched_barrier(0);
       f32x16 gt;
 #pragma unroll
@@ -586,6 +663,38 @@ __global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void
         for (int ks = 0; ks < KSK; ++ks)
           dq[t] = MM<E>::mma(lt[t][ks], MM<E>::ld(gb + 2 * KPL * ks, 1), dq[t]);
       wave_sync();
+    };
+    static_assert(2 * 32 * (D + 1) >= 4 * kBwdSkipList, "skip lists fit the reduction area");
+    if (FOX && skip) {
+      // the key chunks whose block with this chunk's queries and this wave's
+      // key half does not vanish (bwd_block_vanishes), descending, listed in
+      // the reduction area (free until the end); the host enables the skip
+      // only when they fit
+      int *lst = reinterpret_cast<int *>(red) + wv * kBwdSkipList;
+      const float2 qa = qagg[(size_t)bh * (T / C) + c];
+      int cnt = 0;
+      for (int base = c - 1; base >= 0; base -= 64) {
+        const int cp = base - lane;
+        bool keep = cp >= 0;
+        if (keep)
+          keep = !bwd_block_vanishes(scale, qa, kn2[lev_at(win, bh, c, cp, D) / ((size_t)C * D) * 2 + kh],
+                                     kmin[((size_t)bh * (T / C) + cp) * 2 + kh]);
+        const unsigned long long m = __ballot(keep);
+        if (keep) lst[cnt + __popcll(m & ((1ull << lane) - 1ull))] = cp;
+        cnt += __popcll(m);
+      }
+      wave_sync();
+      if (cnt > 0) {
+        fetch_kv(__builtin_amdgcn_readfirstlane(lst[0]));
+        for (int i = 0; i < cnt; ++i) {
+          const int cp = __builtin_amdgcn_readfirstlane(lst[i]);
+          const int cpn = __builtin_amdgcn_readfirstlane(lst[i + 1 < cnt ? i + 1 : i]);
+          step128(cp, cpn);
+        }
+      }
+    } else {
+      fetch_kv(c - 1);
+      for (int cp = c - 1; cp >= 0; --cp) step128(cp, cp > 0 ? cp - 1 : 0);
     }
   } else {
     Frags fa, fb;
@@ -596,7 +705,9 @@ __global__ __launch_bounds__(256, (std::is_same<E, __bf16>::value ? 2 : 1)) void
       step(cp - 1, fb, fa);
     }
   }
-  // combine the two key halves, then store dQa rows
+  // combine the two key halves, then store dQa rows; the barrier keeps a wave
+  // that is done from overwriting the key lists the others still walk
+  __syncthreads();
   float *rq = red + qh * 32 * (D + 1);
   rowsum += __shfl_xor(rowsum, 32);
   if (kh == 1) {
@@ -835,7 +946,9 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     const float *__restrict__ dvec, const float *__restrict__ lam, const E *__restrict__ levels,
     const E *__restrict__ levt, const E *__restrict__ v, const E *__restrict__ nmt,
     float scale, float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
-    float *__restrict__ dmpart, int T, int BH, Win win, int slots, float *__restrict__ gstate) {
+    float *__restrict__ dmpart, int T, int BH, Win win, int slots, float *__restrict__ gstate,
+    const float *__restrict__ kn2, const float2 *__restrict__ qagg, const float *__restrict__ kmin,
+    int skip) {
   using L = DkLds<E, D, G>;
   constexpr bool BF = L::BF;
   constexpr int NW = L::WAVES, NTH = 64 * NW;
@@ -924,6 +1037,19 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
                           FOX ? lam[qr + tid] : 0.f);
     }
   };
+  // exact forget-gate skip (bf16): this wave's block against query chunk c
+  // vanishes when bwd_block_vanishes; its bound's inputs for the next step
+  // are loaded with the level rows
+  const bool do_skip = BF && FOX && skip && member;
+  const float my_kmin = do_skip ? kmin[((size_t)bh * N + cp) * 2 + kh] : 0.f;
+  float nx_kn2 = 0.f;
+  float2 nx_qa = make_float2(0.f, 0.f);
+  auto fetch_bound = [&](int cc) __attribute__((always_inline)) {
+    if (do_skip && cc > cp) {
+      nx_kn2 = kn2[lev_at(win, bh, cc, cp, D) / ((size_t)C * D) * 2 + kh];
+      nx_qa = qagg[(size_t)bh * N + cc];
+    }
+  };
   auto fetch_level = [&](int cc) __attribute__((always_inline)) {
     if constexpr (BF) {   // rows Khat[cc]_{c'} of this wave's keys, B-operand fragments
       const E *kl = levels + lev_at(win, bh, cc, cp, D) + (size_t)(32 * kh + col) * D + KPL * g;
@@ -937,6 +1063,7 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) vfr[ks] = MM<E>::ld(vr + 2 * KPL * ks, 1);
       if (top > cp) fetch_level(top);
+      fetch_bound(top);
     }
     if (top >= bottom) fetch_copy(top);
   }
@@ -966,16 +1093,18 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     }
     __syncthreads();
     frag kcur[KSD];
+    const bool vanish = do_skip && active && bwd_block_vanishes(scale, nx_qa, nx_kn2, my_kmin);
     if constexpr (BF) {
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) kcur[ks] = kfr[ks];
+      fetch_bound(c - 1);
       // next step's operands: level rows first, then this step's -M^T for the
       // crossing, then the copies
       if (member && c - 1 > cp) fetch_level(c - 1);
       if (c - 1 > G * grp) fetch_mt(c - 1);
       if (c - 1 >= bottom) fetch_copy(c - 1);
     }
-    if (active) {
+    if (active && !vanish) {
       const E *kl = levels + lev_at(win, bh, c, cp, D) + (size_t)32 * kh * D;   // Khat[c] rows
       f32x16 s[2], dp[2];
 #pragma unroll
@@ -1020,13 +1149,13 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
           mma_tile<E, C>(gam[t], GT, L::PP, 1, Qs + 32 * t, 1, L::PQ, lane);
         }
       }
-      if (c == cp + 1) {   // chunk c' is done: dKb = Gamma
+    }
+    if (active && c == cp + 1) {   // chunk c' is done: dKb = Gamma
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
+      for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            dkb[(krow + acc_row(r, g)) * D + 32 * t + col] = gam[t][r];
-      }
+        for (int r = 0; r < 16; ++r)
+          dkb[(krow + acc_row(r, g)) * D + 32 * t + col] = gam[t][r];
     }
     const int mch = c - 1;
     if (!(mch > G * grp)) continue;   // no chunk of the group crosses m = c-1
@@ -1442,6 +1571,12 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   E *lev = static_cast<E *>(a.levels), *levt = static_cast<E *>(a.levt);
   const E *qae = (const E *)a.qae, *dout = (const E *)a.dout, *v = (const E *)a.v;
   const Ckpt ck{a.ckpt, P.ckpt_blocks * C * D, P.W};
+  // exact forget-gate skip: bf16 at d = 128 (dq_kernel's key lists bound N)
+  const int skip = FOX && BF && D == 128 && a.skip && N <= kBwdSkipList ? 1 : 0;
+  float *kn2 = skip ? a.kn2 : nullptr;
+  if (skip)
+    hipLaunchKernelGGL((bwd_skip_stats_kernel<E, D>), dim3(BH * N), dim3(64), 0, s, qae, a.lam,
+                       a.lse, const_cast<float2 *>(a.qagg), const_cast<float *>(a.kmin), T);
   constexpr int XB = D * D / 1024;
   static_assert(D * D % 1024 == 0, "whole 1024-element slices");
   // windows of query chunks, the last first (Gamma flows down); the last
@@ -1453,7 +1588,7 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
     if (hi - 1 > 0) {   // levels [lo - 1, hi) of the key chunks c' < hi - 1
       if constexpr (BF)
         hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((hi - 1 + 3) / 4)), dim3(512), 0,
-                           s, a.kb, (const E *)a.nm, lev, levt, T, BH, win, ck, first);
+                           s, a.kb, (const E *)a.nm, lev, levt, T, BH, win, ck, first, kn2);
       else
         hipLaunchKernelGGL((levels_f32_kernel<D>), dim3(BH * (hi - 1)), dim3(128), 0, s, a.kb,
                            (const float *)a.nm, lev, levt, T, BH, win, ck, first);
@@ -1464,7 +1599,8 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
                          a.dlse, a.dvec, a.lam, lev, v, a.scale, a.dqa, a.dlam, T, BH, win);
     else
       hipLaunchKernelGGL((dq_kernel<E, D, FOX>), dim3(BH * nq), dim3(256), 0, s, qae, dout, a.lse,
-                         a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH, win);
+                         a.dlse, a.dvec, a.lam, lev, levt, v, a.scale, a.dqa, a.dlam, T, BH, win,
+                         kn2, a.qagg, a.kmin, skip);
     // groups with a step in the window (G grp + 1 <= hi - 1); the last window
     // also runs the rest, which store dKb = 0 for chunk N - 1
     const int ngw = hi == N ? NG : (hi - 2) / G + 1 < NG ? (hi - 2) / G + 1 : NG;
@@ -1478,7 +1614,7 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
       hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * ngw), dim3(128 * G), 0, s, qae,
                          (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam,
                          lev, levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T,
-                         BH, win, P.slots, a.gstate);
+                         BH, win, P.slots, a.gstate, kn2, a.qagg, a.kmin, skip);
     }
     // dM_m for m in [lo - 1, hi - 1), and m = N - 1 with the last window
     const int nm = hi - lo + (hi == N ? 1 : 0);

@@ -250,7 +250,7 @@ BwdPlan bwd_plan(int T, int window);
 // ckpt, dmpart, gstate).
 struct BwdLayout {
   size_t kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
-      nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, total;
+      nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, kn2, qagg, kmin, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window);
 size_t bwd_dmpart_floats(int dtype, int BH, int T, int D, int window);
@@ -268,6 +268,12 @@ struct SweepArgs {
   void *levels;
   float *dmpart, *dqa, *dkb, *dv, *dlam, *dm;
   float *ckpt, *gstate;                     // level checkpoints, Gamma between windows
+  // exact forget-gate skip (bf16, d = 128): a block of 32 keys against a query
+  // chunk whose weights exp(s - lse) all underflow to zero is left out
+  float *kn2;          // per level block and key half: max row |Khat|^2 (bf16 values)
+  const float2 *qagg;  // per query chunk: (max |Qa_q|^2, max (Lambda_q - lse_q))
+  const float *kmin;   // per key chunk half: min Lambda over its 32 keys
+  int skip;
   float scale;
   int BH, T, window;
 };
@@ -305,6 +311,7 @@ struct BwdArgs {
   int B, H, T;
   float scale;
   int window;   // query chunks per window of the sweep (bwd_plan)
+  int skip;     // exact forget-gate skip allowed (not PATH_ATTN_NO_SKIP)
 };
 hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipStream_t s);
 

@@ -392,7 +392,8 @@ size_t path_attn_bwd_workspace_bytes_window(int B, int H, int T, int d, int dtyp
  * 256-byte aligned; workspace_bytes at least path_attn_bwd_workspace_bytes
  * (a larger workspace selects longer windows of the sweep, see
  * path_attn_bwd_workspace_bytes_window; the gradients agree to float32
- * rounding either way).
+ * rounding either way).  Every sum is taken in a fixed order (no atomics):
+ * two calls with the same inputs and workspace size give the same bits.
  * Errors: EINVAL for null or misaligned pointers, a bad dtype or scale,
  * logf without dlogf, or a small workspace; EUNSUPPORTED for d not in
  * {64, 128} or B*H*Tp*d >= 2^31; EHIP on a launch error.
@@ -404,6 +405,24 @@ int path_attn_bwd(const void *q, const void *k, const void *v, const void *w,
                   float *dlogf, int B, int H, int T, int d, int dtype,
                   float scale, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * path_attn_bwd with flags: 0 or PATH_ATTN_NO_SKIP.  With the gate, the bf16
+ * d = 128 backward leaves out every block of 32 keys and a query chunk whose
+ * weights exp(s - lse) are exactly zero in float32, judged by the bound
+ *     scale * max|Qa| * max|Khat| * 1.01 + max(Lambda_q - lse_q) - min Lambda_j + 1 < -112
+ * over the block (the same reasoning as the forward's skip): its products
+ * add only zeros, so the gradients are the same bits as with every block
+ * computed (up to the sign of a zero).  PATH_ATTN_NO_SKIP computes every
+ * block.  path_attn_bwd(...) == path_attn_bwd_ex(..., scale, 0, ...).
+ */
+int path_attn_bwd_ex(const void *q, const void *k, const void *v, const void *w,
+                     const float *beta, const float *logf, const void *out,
+                     const float *lse, const void *dout, const float *dlse,
+                     void *dq, void *dk, void *dv, void *dw, float *dbeta,
+                     float *dlogf, int B, int H, int T, int d, int dtype,
+                     float scale, unsigned flags, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Strided and packed (variable-length) batches.

@@ -230,3 +230,33 @@ def test_backward_windowed_sweep(case):
     ref = sweep_backward(q, k, v, w, beta, logf, do, o, lse, dlse=dl)
     _log(f"windowed {dtype} d{d} T={T}: oracle head ({b},{h}) in {time.time() - t0:.1f} s")
     _compare(f"windowed {dtype} d{d} T={T}", dtype, got, ref, b, h)
+
+
+@pytest.mark.parametrize("T,window", [(8192, None), (4160, 0)])
+def test_backward_fox_skip_is_exact(T, window):
+    """bf16, d = 128, with the gate: the backward leaves out every block of 32
+    keys and a query chunk whose weights are exactly zero (path_attn_bwd_ex
+    without PATH_ATTN_NO_SKIP).  The gradients must be the same bits as with
+    every block computed, in the windowed sweep and with one window; the
+    decaying gate of the FoX workload makes most far blocks vanish."""
+    import torch
+    import householder_position_encoding_amd as pa
+    B, H, d = 1, 2, 128
+    inp = workloads.small("bf16", B, H, T, d, seed=8192 + T, fox=True)
+    cot = workloads.cotangents("bf16", B, H, T, d, seed=9000 + T)
+    dev = to_device(inp, "bf16")
+    dout = torch.from_numpy(cot["dout"]).to(device="cuda", dtype=torch.bfloat16).contiguous()
+    dlse = torch.from_numpy(cot["dlse"]).cuda().contiguous()
+    out, lse = pa.path_attn_fwd(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"])
+    args = (dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"], out, lse, dout, dlse)
+    g_skip = pa.path_attn_bwd(*args, window=window)
+    g_full = pa.path_attn_bwd(*args, window=window, flags=pa.NO_SKIP)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, g_skip, g_full):
+        assert torch.equal(a.float(), b.float()), f"{name} differs with the skip"
+    # every sum of the backward is taken in a fixed order: a second call
+    # gives the same bits
+    g_again = pa.path_attn_bwd(*args, window=window)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, g_again, g_skip):
+        assert torch.equal(a.float(), b.float()), f"{name} differs between two calls"
