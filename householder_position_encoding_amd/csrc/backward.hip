@@ -528,6 +528,7 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   L.ckpt = take(BH * P.ckpt_blocks * C * D);
   L.gstate = take(P.nwin > 1 ? BH * T * D : 0);
   L.kn2 = take(BH * P.win_blocks * 2);   // level row norms for the forget-gate skip
+  L.zhi = take(BH * (N + 1));             // skipped dM partials per group; a flag per head
   // after the sweep the same bytes hold the adjoint scratch and the saved
   // per-chunk matrices, computed again for the adjoint (bwd_t)
   const size_t adj_bytes = align256(BH * N * adj_floats(D) * sizeof(float));
@@ -604,6 +605,7 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.kn2 = f(L.kn2);
   sa.qagg = reinterpret_cast<const float2 *>(ws + L.qagg);
   sa.kmin = f(L.kmin);
+  sa.zhi = reinterpret_cast<int *>(ws + L.zhi);
   sa.skip = a.skip;
   sa.scale = a.scale;
   sa.BH = BH;

@@ -272,7 +272,8 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
                                                             __bf16 *__restrict__ levels,
                                                             __bf16 *__restrict__ levt, int T,
                                                             int BH, Win win, Ckpt ck,
-                                                            int ck_pass, float *__restrict__ kn2) {
+                                                            int ck_pass, float *__restrict__ kn2,
+                                                            int *__restrict__ zbad) {
   using E = __bf16;
   constexpr int G = 4, P = D + 8, WARM = G - 1;
   constexpr bool WT = D != 64;            // transposed copy
@@ -352,14 +353,17 @@ __global__ __launch_bounds__(512) void levels_shared_kernel(const float *__restr
             for (int t = 0; t < 8; ++t) ss = __builtin_fmaf((float)x[t], (float)x[t], ss);
 #pragma unroll
             for (int o = 1; o < D / 8; o <<= 1) ss += __shfl_xor(ss, o);   // the row's D / 8 lanes
-            nmax = fmaxf(nmax, ss);
+            nmax = fmaxf(nmax, ss <= 3.0e38f ? ss : INFINITY);   // NaN or inf: never skip
           }
         }
         if (kn2) {
           nmax = fmaxf(nmax, __shfl_xor(nmax, 16));
           nmax = fmaxf(nmax, __shfl_xor(nmax, 32));
           if (D == 64) nmax = fmaxf(nmax, __shfl_xor(nmax, 8));
-          if (lane == 0) kn2[off / ((size_t)C * D) * 2 + kh] = nmax;
+          if (lane == 0) {
+            kn2[off / ((size_t)C * D) * 2 + kh] = nmax;
+            if (!(nmax <= 3.0e38f)) zbad[bh] = 1;   // a level that is not finite
+          }
         }
       }
       if (c + 1 < c_end) {   // Khat[c+1] = Khat[c] + round(Khat[c]) (-M_c)^T
@@ -437,9 +441,11 @@ __global__ __launch_bounds__(64) void bwd_skip_stats_kernel(const E *__restrict_
                                                              const float *__restrict__ lam,
                                                              const float *__restrict__ lse,
                                                              float2 *__restrict__ qagg,
-                                                             float *__restrict__ kmin, int T) {
+                                                             float *__restrict__ kmin,
+                                                             int *__restrict__ zbad, int T) {
   const int N = T / C;
   const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N, lane = threadIdx.x;
+  if (c == 0 && lane == 0) zbad[bh] = 0;   // set by the level walk
   const size_t row = (size_t)bh * T + (size_t)c * C + lane;
   float n2 = 0.f;
   const E *qr = qae + row * D;
@@ -948,7 +954,7 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
     float scale, float *__restrict__ dkb, float *__restrict__ dv, float *__restrict__ dlam,
     float *__restrict__ dmpart, int T, int BH, Win win, int slots, float *__restrict__ gstate,
     const float *__restrict__ kn2, const float2 *__restrict__ qagg, const float *__restrict__ kmin,
-    int skip) {
+    int skip, int *__restrict__ zhi) {
   using L = DkLds<E, D, G>;
   constexpr bool BF = L::BF;
   constexpr int NW = L::WAVES, NTH = 64 * NW;
@@ -1057,17 +1063,64 @@ __global__ __launch_bounds__(128 * G) void dk_kernel(
       for (int ks = 0; ks < KSD; ++ks) kfr[ks] = MM<E>::ld(kl + 2 * KPL * ks, 1);
     }
   };
+  // Whole steps.  Gamma starts at zero (at the top of the walk, or as the
+  // window above left it) and stays exactly zero while every block of the
+  // group vanishes: such a step adds nothing, and its crossing only zeros
+  // (Gamma (I - M) and the dM partial, for finite levels and M; a level or
+  // an M that is not finite shows in the stored levels, which turns this off
+  // for the head).  The walk starts at the highest step of the window where
+  // a block of the group does not vanish; dm_reduce leaves out the group's
+  // partials of the transitions above it.
+  int cs = top;
+  if (BF && FOX && skip) {
+    __shared__ int zw[NW];
+    int hw = top;   // this wave's highest step with work
+    bool gz = true;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gz = gz && gam[t][r] == 0.f;
+    if (!zhi[(size_t)BH * N + bh] && __ballot(!gz) == 0ull) {
+      hw = bottom - 1;
+      if (member)
+        for (int base = top; base >= bottom; base -= 64) {
+          const int cc = base - lane;
+          bool work = false;
+          if (cc >= bottom && cc > cp)
+            work = !bwd_block_vanishes(scale, qagg[(size_t)bh * N + cc],
+                                       kn2[lev_at(win, bh, cc, cp, D) / ((size_t)C * D) * 2 + kh],
+                                       my_kmin);
+          const unsigned long long m = __ballot(work);
+          if (m) {   // the lowest such lane has the highest step
+            hw = base - (__ffsll((long long)m) - 1);
+            break;
+          }
+        }
+    }
+    if (lane == 0) zw[wv] = hw;
+    __syncthreads();
+    cs = bottom - 1;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) cs = max(cs, zw[i]);
+    if (tid == 0) zhi[(size_t)bh * NG + grp] = cs < top ? cs : 0x7fffffff;
+    // a chunk whose last step is among the skipped ones: dKb = Gamma = 0
+    if (member && cp + 1 > cs && cp + 1 <= top && cp + 1 >= bottom)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkb[(krow + acc_row(r, g)) * D + 32 * t + col] = gam[t][r];
+  }
   if constexpr (BF) {
     if (member) {
       const E *vr = v + (krow + col) * D + KPL * g;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) vfr[ks] = MM<E>::ld(vr + 2 * KPL * ks, 1);
-      if (top > cp) fetch_level(top);
-      fetch_bound(top);
+      if (cs >= bottom && cs > cp) fetch_level(cs);
+      if (cs >= bottom) fetch_bound(cs);
     }
-    if (top >= bottom) fetch_copy(top);
+    if (cs >= bottom) fetch_copy(cs);
   }
-  for (int c = top; c >= bottom; --c) {
+  for (int c = cs; c >= bottom; --c) {
     const bool active = member && c > cp;
     const size_t qrow = head + (size_t)c * C;
     __syncthreads();
@@ -1497,7 +1550,8 @@ __global__ __launch_bounds__(512) void dk64_kernel(
 template <int G>
 __global__ __launch_bounds__(256) void dm_reduce_kernel(const float4 *__restrict__ dmpart,
                                                         float4 *__restrict__ dm, int N, int DD,
-                                                        int XB, int m0, int nm, int slots) {
+                                                        int XB, int m0, int nm, int slots,
+                                                        const int *__restrict__ zhi) {
   constexpr int U = 8;
   const int NG = (N + G - 1) / G, DD4 = DD / 4;
   const int bmi = blockIdx.x / XB;   // bh * nm + (m - m0)
@@ -1506,12 +1560,18 @@ __global__ __launch_bounds__(256) void dm_reduce_kernel(const float4 *__restrict
   const int ng = (mch >= 1 && mch <= N - 2) ? (mch + G - 1) / G : 0;
   const size_t bm = (size_t)bh * N + mch;
   const float4 *src = dmpart + ((size_t)bh * slots + mi) * NG * DD4 + e;
+  // with the whole-step skip, group gi wrote no partial for m >= zhi[gi]:
+  // those are zero (adding them changes no bit of the sum)
+  const int *zh = zhi ? zhi + (size_t)bh * NG : nullptr;
+  auto part = [&](int gi) __attribute__((always_inline)) {
+    return !zh || mch < zh[gi] ? src[(size_t)gi * DD4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   int gi = 0;
   for (; gi + U <= ng; gi += U) {
     float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = src[(size_t)(gi + u) * DD4];
+    for (int u = 0; u < U; ++u) v[u] = part(gi + u);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       acc.x += v[u].x;
@@ -1521,7 +1581,7 @@ __global__ __launch_bounds__(256) void dm_reduce_kernel(const float4 *__restrict
     }
   }
   for (; gi < ng; ++gi) {
-    const float4 v = src[(size_t)gi * DD4];
+    const float4 v = part(gi);
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
@@ -1576,7 +1636,8 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
   float *kn2 = skip ? a.kn2 : nullptr;
   if (skip)
     hipLaunchKernelGGL((bwd_skip_stats_kernel<E, D>), dim3(BH * N), dim3(64), 0, s, qae, a.lam,
-                       a.lse, const_cast<float2 *>(a.qagg), const_cast<float *>(a.kmin), T);
+                       a.lse, const_cast<float2 *>(a.qagg), const_cast<float *>(a.kmin),
+                       a.zhi + (size_t)BH * N, T);
   constexpr int XB = D * D / 1024;
   static_assert(D * D % 1024 == 0, "whole 1024-element slices");
   // windows of query chunks, the last first (Gamma flows down); the last
@@ -1588,7 +1649,8 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
     if (hi - 1 > 0) {   // levels [lo - 1, hi) of the key chunks c' < hi - 1
       if constexpr (BF)
         hipLaunchKernelGGL((levels_shared_kernel<D>), dim3(BH * ((hi - 1 + 3) / 4)), dim3(512), 0,
-                           s, a.kb, (const E *)a.nm, lev, levt, T, BH, win, ck, first, kn2);
+                           s, a.kb, (const E *)a.nm, lev, levt, T, BH, win, ck, first, kn2,
+                           a.zhi + (size_t)BH * N);
       else
         hipLaunchKernelGGL((levels_f32_kernel<D>), dim3(BH * (hi - 1)), dim3(128), 0, s, a.kb,
                            (const float *)a.nm, lev, levt, T, BH, win, ck, first);
@@ -1614,13 +1676,13 @@ static hipError_t sweep_t(const SweepArgs &a, hipStream_t s) {
       hipLaunchKernelGGL((dk_kernel<E, D, G, FOX>), dim3(BH * ngw), dim3(128 * G), 0, s, qae,
                          (const E *)a.qat, dout, (const E *)a.dot, a.lse, a.dlse, a.dvec, a.lam,
                          lev, levt, v, (const E *)a.nmt, a.scale, a.dkb, a.dv, a.dlam, a.dmpart, T,
-                         BH, win, P.slots, a.gstate, kn2, a.qagg, a.kmin, skip);
+                         BH, win, P.slots, a.gstate, kn2, a.qagg, a.kmin, skip, a.zhi);
     }
     // dM_m for m in [lo - 1, hi - 1), and m = N - 1 with the last window
     const int nm = hi - lo + (hi == N ? 1 : 0);
     hipLaunchKernelGGL((dm_reduce_kernel<G>), dim3(BH * nm * XB), dim3(256), 0, s,
                        (const float4 *)a.dmpart, (float4 *)a.dm, N, D * D, XB, lo - 1, nm,
-                       P.slots);
+                       P.slots, skip ? a.zhi : nullptr);
   }
   return hipGetLastError();
 }

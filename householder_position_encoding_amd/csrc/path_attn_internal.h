@@ -250,7 +250,7 @@ BwdPlan bwd_plan(int T, int window);
 // ckpt, dmpart, gstate).
 struct BwdLayout {
   size_t kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
-      nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, kn2, qagg, kmin, total;
+      nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, kn2, zhi, qagg, kmin, total;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window);
 size_t bwd_dmpart_floats(int dtype, int BH, int T, int D, int window);
@@ -273,6 +273,10 @@ struct SweepArgs {
   float *kn2;          // per level block and key half: max row |Khat|^2 (bf16 values)
   const float2 *qagg;  // per query chunk: (max |Qa_q|^2, max (Lambda_q - lse_q))
   const float *kmin;   // per key chunk half: min Lambda over its 32 keys
+  // per (head, group of key chunks): dM partials of the transitions m >= zhi
+  // are zero and not written (the dk walk skipped those steps whole); then,
+  // at zbad = zhi + BH * N, per head: 1 if a stored level is not finite
+  int *zhi;
   int skip;
   float scale;
   int BH, T, window;
