@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     E *__restrict__ qat, E *__restrict__ nm, E *__restrict__ nmt, E *__restrict__ qimg,
     E *__restrict__ mimg, int T) {
   constexpr bool IMG = std::is_same<E, __bf16>::value && D == 64;
-  __shared__ float PX[panel_floats(D)], PY[panel_floats(D)];
+  __shared__ float PX[panel_floats_any(D)], PY[panel_floats_any(D)];
   __shared__ float tmp[768], bs[C];
   const int N = T / C;
   const int chunk = blockIdx.x, bh = chunk / N, c = chunk % N;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   f32x16 acc, acc2;
 
   zero16(acc);   // G = W W^T -> N = strictLower(D G) -> X -> U
-  gmm<D, false, true>(acc, W, D, W, D, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, W, D, W, D, PX, PY, tid);
   __syncthreads();
   tile_each(tid, [&](int i, int j, int r) { PX[i * 65 + j] = j < i ? bs[i] * acc[r] : 0.f; });
   __syncthreads();
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // U W
     zero16(acc);
-    gmm<64, false, false>(acc, Ug, 64, W + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(acc, Ug, 64, W + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) { UWg[i * D + 64 * nb + j] = acc[r]; });
   }
 #pragma unroll
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
     for (int nb = 0; nb < D / 64 && !SAVED_ONLY; ++nb) {
       zero16(acc);
-      gmm<64, true, false>(acc, W + 64 * ma, D, UWg + 64 * nb, D, PX, PY, tid);
+      gmm_e<E, 64, true, false>(acc, W + 64 * ma, D, UWg + 64 * nb, D, PX, PY, tid);
       tile_each(tid, [&](int i, int j, int r) {
         const int a = 64 * ma + i, b = 64 * nb + j;
         m_c[(size_t)a * D + b] = acc[r];
@@ -133,12 +133,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
       });
     }
   zero16(acc);   // A = lower(Q W^T)
-  gmm<D, false, true>(acc, Q, D, W, D, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, Q, D, W, D, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { Ag[i * 64 + j] = j <= i ? acc[r] : 0.f; });
 #pragma unroll
   for (int nb = 0; nb < D / 64 && !SAVED_ONLY; ++nb) {   // <-Q = Q - A (U W)
     zero16(acc);
-    gmm<64, false, false>(acc, Ag, 64, UWg + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(acc, Ag, 64, UWg + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
       const int d = 64 * nb + j;
       const float x = (float)Q[i * D + d] - acc[r];
@@ -156,24 +156,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
            idx % (kImgPitch - 64)] = (E)0.f;
   }
   zero16(acc);   // B = strictLower(W K^T)
-  gmm<D, false, true>(acc, W, D, K, D, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, W, D, K, D, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { Bg[i * 64 + j] = j < i ? acc[r] : 0.f; });
   zero16(acc);   // T2 = U B
-  gmm<64, false, false>(acc, Ug, 64, Bg, 64, PX, PY, tid);
+  gmm_e<E, 64, false, false>(acc, Ug, 64, Bg, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { T2g[i * 64 + j] = acc[r]; });
   if constexpr (SAVED_ONLY) return;
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // ->K = K - T2^T W
     zero16(acc);
-    gmm<64, true, false>(acc, T2g, 64, W + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, true, false>(acc, T2g, 64, W + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
       kb_c[i * D + 64 * nb + j] = (float)K[i * D + 64 * nb + j] - acc[r];
     });
   }
   zero16(acc);   // Al = lower(Q K^T) - A T2
-  gmm<D, false, true>(acc, Q, D, K, D, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, Q, D, K, D, PX, PY, tid);
   zero16(acc2);
-  gmm<64, false, false>(acc2, Ag, 64, T2g, 64, PX, PY, tid);
+  gmm_e<E, 64, false, false>(acc2, Ag, 64, T2g, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { al_c[i * 64 + j] = j <= i ? acc[r] - acc2[r] : 0.f; });
 }
 
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
     const float *__restrict__ dkb, const float *__restrict__ dm, const float *__restrict__ dal,
     const float *__restrict__ saved, float *__restrict__ adj, E *__restrict__ dq,
     E *__restrict__ dk, E *__restrict__ dw, float *__restrict__ dbeta, int T) {
-  __shared__ float PX[panel_floats(D)], PY[panel_floats(D)];
+  __shared__ float PX[panel_floats_any(D)], PY[panel_floats_any(D)];
   // dbeta's two sums, reduced in a fixed order (no atomics, so the same bits
   // on every call): [half of the block's waves][token]
   __shared__ float bs[C], dbx[2][C], dbn[2][C];
@@ -373,24 +373,24 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
   f32x16 acc, acc2;
 
   zero16(acc);   // dA
-  gmm<D, false, true>(acc, dQa, D, UWg, D, PX, PY, tid);
-  gmm<64, false, true>(acc, dAl, 64, T2g, 64, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, dQa, D, UWg, D, PX, PY, tid);
+  gmm_e<E, 64, false, true>(acc, dAl, 64, T2g, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { dAg[i * 64 + j] = j <= i ? -acc[r] : 0.f; });
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // dUW
     zero16(acc);
-    gmm<D, false, false>(acc, W, D, dM + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, D, false, false>(acc, W, D, dM + 64 * nb, D, PX, PY, tid);
     zero16(acc2);
-    gmm<64, true, false>(acc2, Ag, 64, dQa + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, true, false>(acc2, Ag, 64, dQa + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) { dUWg[i * D + 64 * nb + j] = acc[r] - acc2[r]; });
   }
   zero16(acc);   // dT2
-  gmm<D, false, true>(acc, W, D, dKb, D, PX, PY, tid);
-  gmm<64, true, false>(acc, Ag, 64, dAl, 64, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, W, D, dKb, D, PX, PY, tid);
+  gmm_e<E, 64, true, false>(acc, Ag, 64, dAl, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { dT2g[i * 64 + j] = -acc[r]; });
   zero16(acc);   // dU -> dX, dbeta_j
-  gmm<D, false, true>(acc, dUWg, D, W, D, PX, PY, tid);
-  gmm<64, false, true>(acc, dT2g, 64, Bg, 64, PX, PY, tid);
+  gmm_e<E, D, false, true>(acc, dUWg, D, W, D, PX, PY, tid);
+  gmm_e<E, 64, false, true>(acc, dT2g, 64, Bg, 64, PX, PY, tid);
   {
     float part = 0.f;
     int col = 0;
@@ -405,19 +405,19 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
     if ((tid & 63) < 32) dbx[tid >> 7][col] = part;
   }
   zero16(acc);   // dB
-  gmm<64, true, false>(acc, Ug, 64, dT2g, 64, PX, PY, tid);
+  gmm_e<E, 64, true, false>(acc, Ug, 64, dT2g, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { dBg[i * 64 + j] = j < i ? acc[r] : 0.f; });
   zero16(acc);   // Y = dX X^T
-  gmm<64, false, true>(acc, dXg, 64, Xg, 64, PX, PY, tid);
+  gmm_e<E, 64, false, true>(acc, dXg, 64, Xg, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { Yg[i * 64 + j] = acc[r]; });
   zero16(acc);   // dN = strictLower(-X^T Y)
-  gmm<64, true, false>(acc, Xg, 64, Yg, 64, PX, PY, tid);
+  gmm_e<E, 64, true, false>(acc, Xg, 64, Yg, 64, PX, PY, tid);
   tile_each(tid, [&](int i, int j, int r) { dNg[i * 64 + j] = j < i ? -acc[r] : 0.f; });
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // dQ
     zero16(acc);
-    gmm<64, false, false>(acc, dAl, 64, K + 64 * nb, D, PX, PY, tid);
-    gmm<64, false, false>(acc, dAg, 64, W + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(acc, dAl, 64, K + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(acc, dAg, 64, W + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
       const size_t o = (size_t)i * D + 64 * nb + j;
       dq[row0 * D + o] = (E)(dQa[o] + acc[r]);
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
 #pragma unroll
   for (int nb = 0; nb < D / 64; ++nb) {   // dK
     zero16(acc);
-    gmm<64, true, false>(acc, dAl, 64, Q + 64 * nb, D, PX, PY, tid);
-    gmm<64, true, false>(acc, dBg, 64, W + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, true, false>(acc, dAl, 64, Q + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, true, false>(acc, dBg, 64, W + 64 * nb, D, PX, PY, tid);
     tile_each(tid, [&](int i, int j, int r) {
       const size_t o = (size_t)i * D + 64 * nb + j;
       dk[row0 * D + o] = (E)(dKb[o] + acc[r]);
@@ -440,15 +440,15 @@ __global__ __launch_bounds__(256) void bwd_local_kernel(
   for (int nb = 0; nb < D / 64; ++nb) {   // dW
     f32x16 accn;
     zero16(accn);   // dN W
-    gmm<64, false, false>(accn, dNg, 64, W + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(accn, dNg, 64, W + 64 * nb, D, PX, PY, tid);
     zero16(acc2);   // T2 dKb
-    gmm<64, false, false>(acc2, T2g, 64, dKb + 64 * nb, D, PX, PY, tid);
+    gmm_e<E, 64, false, false>(acc2, T2g, 64, dKb + 64 * nb, D, PX, PY, tid);
     zero16(acc);
-    gmm<64, true, false>(acc, dNg, 64, W + 64 * nb, D, PX, PY, tid, bs);   // dG^T W
-    gmm<D, false, true>(acc, UWg, D, dM + (size_t)64 * nb * D, D, PX, PY, tid);   // UW dM^T
-    gmm<64, true, false>(acc, Ug, 64, dUWg + 64 * nb, D, PX, PY, tid);   // U^T dUW
-    gmm<64, true, false>(acc, dAg, 64, Q + 64 * nb, D, PX, PY, tid);     // dA^T Q
-    gmm<64, false, false>(acc, dBg, 64, K + 64 * nb, D, PX, PY, tid);    // dB K
+    gmm_e<E, 64, true, false>(acc, dNg, 64, W + 64 * nb, D, PX, PY, tid, bs);   // dG^T W
+    gmm_e<E, D, false, true>(acc, UWg, D, dM + (size_t)64 * nb * D, D, PX, PY, tid);   // UW dM^T
+    gmm_e<E, 64, true, false>(acc, Ug, 64, dUWg + 64 * nb, D, PX, PY, tid);   // U^T dUW
+    gmm_e<E, 64, true, false>(acc, dAg, 64, Q + 64 * nb, D, PX, PY, tid);     // dA^T Q
+    gmm_e<E, 64, false, false>(acc, dBg, 64, K + 64 * nb, D, PX, PY, tid);    // dB K
     tile_each(tid, [&](int i, int j, int r) {
       const size_t o = (size_t)i * D + 64 * nb + j;
       const float wv = (float)W[o];

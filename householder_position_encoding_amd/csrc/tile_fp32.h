@@ -1,10 +1,13 @@
 // tile_fp32.h -- float32 products of 64 x 64 blocks for 256-thread blocks:
 // 4 x 4 register tiles on the vector units (thread t owns rows t/16 + 16 r
 // and columns t%16 + 16 s), and 32 x 32 tiles on the float32 matrix cores with
-// operands staged through LDS panels; plus the blocked unit-triangular
-// inverse of the chunk algebra.  Used by the prefill alignment and the
-// backward pass, whose per-chunk algebra runs in float32.
+// operands staged through LDS panels (or, for bf16 inputs, on the bf16
+// matrix cores with float32 operands split into hi/lo pairs); plus the
+// blocked unit-triangular inverse of the chunk algebra.  Used by the prefill
+// alignment and the backward pass, whose per-chunk algebra runs in float32.
 #pragma once
+
+#include <type_traits>
 
 #include "path_attn_internal.h"
 
@@ -98,6 +101,7 @@ template <int K, bool TX, bool TY, typename TXe, typename TYe>
 __device__ __forceinline__ void gmm(f32x16 &acc, const TXe *X, int ldx, const TYe *Y, int ldy,
                                     float *PX, float *PY, int tid,
                                     const float *yscale = nullptr) {
+  asm volatile("" : "+v"(tid));   // as in gmm_hilo: addresses computed here
   __syncthreads();
   if (TX) load_panel<K, 64>(PX, X, ldx, nullptr, tid);
   else load_panel<64, K>(PX, X, ldx, nullptr, tid);
@@ -112,6 +116,135 @@ __device__ __forceinline__ void gmm(f32x16 &acc, const TXe *X, int ldx, const TY
 #pragma unroll 8
   for (int k = 0; k < K; k += 2)
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[k * a_cs], pb[k * b_rs], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// The same products on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16), for
+// blocks whose inputs are bf16: each float32 operand x is split into
+// hi = bf16(x) and lo = bf16(x - hi), and the product is hi hi + hi lo + lo hi
+// (about 16 significant bits, float32 accumulation; the lo lo term, below
+// 2^-16 of the product, is left out).  An operand that is a bf16 input is
+// exact in bf16: it has no lo part, and its lo products are left out.  The
+// output tile has the layout of gmm's.
+
+// Floats of LDS for one operand's hi and lo planes: 64 rows (the operand's
+// non-contracted index) of K + 8 bf16, the contraction index contiguous, so a
+// lane's 8 contraction values are one 16-byte read and the rows of a 16-lane
+// group fall in distinct banks.
+__host__ __device__ constexpr int planes_floats(int kmax) { return 64 * (kmax + 8); }
+// LDS floats of a panel that serves either form.
+__host__ __device__ constexpr int panel_floats_any(int kmax) {
+  return panel_floats(kmax) > planes_floats(kmax) ? panel_floats(kmax) : planes_floats(kmax);
+}
+
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &h, bf16x8 &l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+}
+
+// plane[r][k] = kscale[k] * S(r, k) for r < 64, k < K, as hi (and, unless
+// EXACT, lo) bf16 planes at P (hi) and P + 64 (K + 8) (lo); S(r, k) =
+// src[r * ld + k] with KMAJ, else src[k * ld + r].  Every thread issues its
+// global loads before its LDS stores.
+template <int K, bool KMAJ, bool EXACT, typename T>
+__device__ __forceinline__ void stage_planes(__bf16 *P, const T *src, int ld, const float *kscale,
+                                             int tid) {
+  constexpr int PK = K + 8, ITEMS = 64 * K / 8, PER = ITEMS / 256;
+  static_assert(ITEMS % 256 == 0, "items split evenly over 256 threads");
+  float v[PER][8];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int vi = tid + 256 * it;
+    // KMAJ: 8 consecutive k of row r; else row r = lane order (coalesced
+    // scalar loads down the contraction index)
+    const int r = KMAJ ? vi / (K / 8) : vi % 64, k8 = 8 * (KMAJ ? vi % (K / 8) : vi / 64);
+    if constexpr (KMAJ) {
+      if constexpr (std::is_same<T, __bf16>::value) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(src + (size_t)r * ld + k8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[it][e] = (float)x[e];
+      } else {
+        const float4 a = *reinterpret_cast<const float4 *>(src + (size_t)r * ld + k8);
+        const float4 b = *reinterpret_cast<const float4 *>(src + (size_t)r * ld + k8 + 4);
+        v[it][0] = a.x, v[it][1] = a.y, v[it][2] = a.z, v[it][3] = a.w;
+        v[it][4] = b.x, v[it][5] = b.y, v[it][6] = b.z, v[it][7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[it][e] = (float)src[(size_t)(k8 + e) * ld + r];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int vi = tid + 256 * it;
+    const int r = KMAJ ? vi / (K / 8) : vi % 64, k8 = 8 * (KMAJ ? vi % (K / 8) : vi / 64);
+    if (kscale)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[it][e] *= kscale[k8 + e];
+    bf16x8 h, l;
+    split8(v[it], h, l);
+    *reinterpret_cast<bf16x8 *>(P + r * PK + k8) = h;
+    if (!EXACT) *reinterpret_cast<bf16x8 *>(P + 64 * PK + r * PK + k8) = l;
+  }
+}
+
+// gmm's product on the bf16 matrix cores (same operands, flags and output
+// layout; PX, PY hold planes_floats(K) floats).  yscale multiplies row k of
+// Y (not with TY).
+template <int K, bool TX, bool TY, typename TXe, typename TYe>
+__device__ __forceinline__ void gmm_hilo(f32x16 &acc, const TXe *X, int ldx, const TYe *Y,
+                                         int ldy, float *PX, float *PY, int tid,
+                                         const float *yscale = nullptr) {
+  constexpr bool XE = std::is_same<TXe, __bf16>::value, YB = std::is_same<TYe, __bf16>::value;
+  constexpr int PK = K + 8;
+  __bf16 *A = reinterpret_cast<__bf16 *>(PX), *B = reinterpret_cast<__bf16 *>(PY);
+  const bool ye = YB && !yscale;   // Y exact in bf16
+  // the thread index re-derived here: otherwise the compiler computes the
+  // addresses of every product of the kernel up front and keeps them live
+  // (spilled to accumulation registers)
+  asm volatile("" : "+v"(tid));
+  __syncthreads();
+  // A[r][k] = op(X)(r, k); B[c][k] = op(Y)(k, c)
+  stage_planes<K, !TX, XE>(A, X, ldx, nullptr, tid);
+  if (ye) stage_planes<K, TY, true>(B, Y, ldy, nullptr, tid);
+  else stage_planes<K, TY, false>(B, Y, ldy, yscale, tid);
+  __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6, i = lane & 31, kg = lane >> 5;
+  const __bf16 *pa = A + (32 * (wv >> 1) + i) * PK + 8 * kg;
+  const __bf16 *pb = B + (32 * (wv & 1) + i) * PK + 8 * kg;
+  auto run = [&](auto yexact) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < K / 16; ++s) {
+      const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(pa + 16 * s);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(pb + 16 * s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+      if constexpr (!decltype(yexact)::value) {
+        const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(pb + 64 * PK + 16 * s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+      }
+      if constexpr (!XE) {
+        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(pa + 64 * PK + 16 * s);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+      }
+    }
+  };
+  if (ye) run(std::true_type{});
+  else run(std::false_type{});
+}
+
+// The block product of a kernel whose inputs have type E: the bf16 form for
+// bf16 inputs, float32 matrix cores otherwise.
+template <typename E, int K, bool TX, bool TY, typename TXe, typename TYe>
+__device__ __forceinline__ void gmm_e(f32x16 &acc, const TXe *X, int ldx, const TYe *Y, int ldy,
+                                      float *PX, float *PY, int tid,
+                                      const float *yscale = nullptr) {
+  if constexpr (std::is_same<E, __bf16>::value)
+    gmm_hilo<K, TX, TY>(acc, X, ldx, Y, ldy, PX, PY, tid, yscale);
+  else
+    gmm<K, TX, TY>(acc, X, ldx, Y, ldy, PX, PY, tid, yscale);
 }
 
 __device__ __forceinline__ void zero16(f32x16 &a) {

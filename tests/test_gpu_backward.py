@@ -33,7 +33,7 @@ import pytest
 import workloads
 from oracle.backward import gradients as oracle_gradients
 from oracle.chunked_backward import sweep_backward
-from tests.gpu_util import spread_heads, to_device
+from tests.gpu_util import record, spread_heads, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def _head(inp, cot, b, h):
 
 def _compare(tag, dtype, got, ref, b, h):
     tol = TOL[dtype]
-    worst = 0.0
+    errs = {}
     for n in NAMES:
         r = ref[n]
         if r is None:
@@ -81,13 +81,14 @@ def _compare(tag, dtype, got, ref, b, h):
         g = got[n][b, h]
         assert np.all(np.isfinite(g)), f"{tag}: {n} not finite"
         scale = max(1.0, float(np.max(np.abs(r))))
-        err = float(np.max(np.abs(g - r))) / scale
-        worst = max(worst, err)
-        _log(f"{tag} head ({b},{h}) {n}: max|err|/max(1,max|ref|) = {err:.3g} (tol {tol})")
+        errs[n] = float(np.max(np.abs(g - r))) / scale
+    # max|g - r| / max(1, max|r|) per gradient
+    record(f"backward {tag} head ({b},{h})", tol=tol, **{f"err_{n}": e for n, e in errs.items()})
+    for n, err in errs.items():
         assert err <= tol, f"{tag}: {n} of head ({b},{h}) off by {err:.3g} > {tol}"
     if ref["dlogf"] is not None:
         assert got["dlogf"][b, h, 0] == 0.0
-    return worst
+    return max(errs.values())
 
 
 SMALL = [
