@@ -213,15 +213,17 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     float *__restrict__ dv, float *__restrict__ dlam, float *__restrict__ dvec,
     E *__restrict__ dot, E *__restrict__ oimg, float4 *__restrict__ qst, int T) {
   constexpr bool IMG = std::is_same<E, __bf16>::value && D == 64;
-  constexpr int DP = D + 1, CP = C + 1;
-  __shared__ float Os[C * DP];
-  __shared__ float Vs[C * DP];
+  // dO and V rows in LDS in the input dtype (bf16 widens exactly); pitch D + 1
+  // floats or D + 2 bf16 (column reads by 16 lanes fall in 16 banks)
+  constexpr int DP = std::is_same<E, __bf16>::value ? D + 2 : D + 1, CP = C + 1;
+  __shared__ E Os[C * DP];
+  __shared__ E Vs[C * DP];
   __shared__ float Ps[C * CP];
   __shared__ float rl[C], rd[C], rg[C], rdl[C];
   const int N = T / C;
   const int bh = blockIdx.x / N, c = blockIdx.x % N;
   const size_t row0 = (size_t)bh * T + (size_t)c * C;
-  const int tid = threadIdx.x, r0 = tid / 16, c0 = tid % 16;
+  int tid = threadIdx.x;
   // dO and V rows to LDS as floats, 16 bytes per load
   using RV = Row16<E>;
   constexpr int VPR = D / RV::N;   // 16-byte loads per row
@@ -232,8 +234,8 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     RV::load(xv, v + (row0 + r) * D + e0);
 #pragma unroll
     for (int t = 0; t < RV::N; ++t) {
-      Os[r * DP + e0 + t] = xo[t];
-      Vs[r * DP + e0 + t] = xv[t];
+      Os[r * DP + e0 + t] = (E)xo[t];
+      Vs[r * DP + e0 + t] = (E)xv[t];
     }
   }
   {   // rowdot(dO, O): four threads per row, each a quarter of the columns
@@ -284,6 +286,10 @@ __global__ __launch_bounds__(256) void bwd_diag_kernel(
     }
     if (tid < C) qst[row0 + tid] = make_float4(rl[tid], rd[tid], rdl[tid], rg[tid]);
   }
+  // the thread index re-derived: the products' addresses are computed here,
+  // not kept live from the kernel's start
+  asm volatile("" : "+v"(tid));
+  const int r0 = tid / 16, c0 = tid % 16;
   const float *al_c = al + ((size_t)bh * N + c) * C * C;
   float p[4][4];
 #pragma unroll

@@ -17,16 +17,17 @@ namespace pathattn {
 // thread's 4 x 4 tile of a 64 x 64 output block, operands in LDS with
 // arbitrary row / column strides (so transposed reads need no copy).  Rows of
 // the tile are 16 apart and columns 16 apart: a wave's lanes read 4 distinct
-// A addresses and 16 consecutive B addresses per instruction.
-template <int K>
-__device__ __forceinline__ void tile_mm(float (&acc)[4][4], const float *A, int a_rs, int a_cs,
-                                        const float *B, int b_rs, int b_cs, int r0, int c0) {
+// A addresses and 16 consecutive B addresses per instruction.  Operands are
+// float or bf16 (widened exactly).
+template <int K, typename TA, typename TB>
+__device__ __forceinline__ void tile_mm(float (&acc)[4][4], const TA *A, int a_rs, int a_cs,
+                                        const TB *B, int b_rs, int b_cs, int r0, int c0) {
   for (int kk = 0; kk < K; ++kk) {
     float a[4], b[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = A[(r0 + 16 * r) * a_rs + kk * a_cs];
+    for (int r = 0; r < 4; ++r) a[r] = (float)A[(r0 + 16 * r) * a_rs + kk * a_cs];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) b[c] = B[kk * b_rs + (c0 + 16 * c) * b_cs];
+    for (int c = 0; c < 4; ++c) b[c] = (float)B[kk * b_rs + (c0 + 16 * c) * b_cs];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll

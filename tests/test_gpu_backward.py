@@ -250,14 +250,23 @@ def test_backward_fox_skip_is_exact(T, window):
     dlse = torch.from_numpy(cot["dlse"]).cuda().contiguous()
     out, lse = pa.path_attn_fwd(dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"])
     args = (dev["q"], dev["k"], dev["v"], dev["w"], dev["beta"], dev["logf"], out, lse, dout, dlse)
-    g_skip = pa.path_attn_bwd(*args, window=window)
-    g_full = pa.path_attn_bwd(*args, window=window, flags=pa.NO_SKIP)
+    code = 1
+    need = (pa.path_attn_bwd_workspace_bytes(B, H, T, d, code) if window is None
+            else pa.path_attn_bwd_workspace_bytes_window(B, H, T, d, code, window))
+
+    def nan_workspace():
+        # every byte 0xFF (a NaN in bf16 and float32): a read of anything the
+        # call did not write shows in the gradients
+        return torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+
+    g_skip = pa.path_attn_bwd(*args, window=window, workspace=nan_workspace())
+    g_full = pa.path_attn_bwd(*args, window=window, flags=pa.NO_SKIP, workspace=nan_workspace())
     torch.cuda.synchronize()
     for name, a, b in zip(NAMES, g_skip, g_full):
         assert torch.equal(a.float(), b.float()), f"{name} differs with the skip"
     # every sum of the backward is taken in a fixed order: a second call
     # gives the same bits
-    g_again = pa.path_attn_bwd(*args, window=window)
+    g_again = pa.path_attn_bwd(*args, window=window, workspace=nan_workspace())
     torch.cuda.synchronize()
     for name, a, b in zip(NAMES, g_again, g_skip):
         assert torch.equal(a.float(), b.float()), f"{name} differs between two calls"
