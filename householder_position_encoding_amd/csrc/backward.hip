@@ -535,13 +535,18 @@ BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window) {
   L.gstate = take(P.nwin > 1 ? BH * T * D : 0);
   L.kn2 = take(BH * P.win_blocks * 2);   // level row norms for the forget-gate skip
   L.zhi = take(BH * (N + 1));             // skipped dM partials per group; a flag per head
-  // after the sweep the same bytes hold the adjoint scratch and the saved
-  // per-chunk matrices, computed again for the adjoint (bwd_t)
+  // after the sweep the same bytes hold the adjoint scratch and, with
+  // windows, the saved per-chunk matrices, computed again for the adjoint
+  // (bwd_t); one window (the fast, large workspace) keeps them in bytes of
+  // their own
   const size_t adj_bytes = align256(BH * N * adj_floats(D) * sizeof(float));
   const size_t saved_bytes = align256(BH * N * saved_floats(D) * sizeof(float));
+  L.saved_kept = P.nwin == 1;
+  const size_t shared = adj_bytes + (L.saved_kept ? 0 : saved_bytes);
   L.adj = sweep0;
   L.saved = sweep0 + adj_bytes;
-  off = sweep0 + (off - sweep0 > adj_bytes + saved_bytes ? off - sweep0 : adj_bytes + saved_bytes);
+  off = sweep0 + (off - sweep0 > shared ? off - sweep0 : shared);
+  if (L.saved_kept) L.saved = take(BH * N * saved_floats(D));
   L.dv = take(BH * T * D);
   L.dlam = take(BH * T);
   L.dqa = take(BH * T * D);
@@ -618,10 +623,12 @@ hipError_t bwd_t(const BwdArgs &a, char *ws, int dtype, hipStream_t s) {
   sa.T = T;
   sa.window = a.window;
   if (launch_bwd_sweep(dtype, D, FOX, sa, s) != hipSuccess) return hipGetLastError();
-  // the sweep has reused the saved matrices' bytes: compute them again
-  hipLaunchKernelGGL((bwd_prep_kernel<E, D, true>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
-                     f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
-                     e(L.nmt), e(L.qimg), e(L.mimg), T);
+  // with windows the sweep has reused the saved matrices' bytes: compute
+  // them again
+  if (!L.saved_kept)
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D, true>), dim3(BH * N), dim3(NT), 0, s, q, k, w,
+                       a.beta, f(L.kb), f(L.m), f(L.al), f(L.saved), e(L.qae), e(L.qat), e(L.nm),
+                       e(L.nmt), e(L.qimg), e(L.mimg), T);
   hipLaunchKernelGGL((bwd_local_kernel<E, D>), dim3(BH * N), dim3(NT), 0, s, q, k, w, a.beta,
                      f(L.dqa), f(L.dkb), f(L.dm), f(L.dal), f(L.saved), f(L.adj), (E *)a.dq,
                      (E *)a.dk, (E *)a.dw, a.dbeta, T);

@@ -251,6 +251,9 @@ BwdPlan bwd_plan(int T, int window);
 struct BwdLayout {
   size_t kb, m, al, lam, dvec, levels, dmpart, dv, dlam, dqa, dkb, dm, dal, saved, adj, qae, qat,
       nm, nmt, dot, levt, qimg, oimg, mimg, qst, ckpt, gstate, kn2, zhi, qagg, kmin, total;
+  // the saved per-chunk matrices have bytes of their own (one window), so
+  // they need not be computed again after the sweep
+  bool saved_kept;
 };
 BwdLayout bwd_layout(int B, int H, int T, int D, int dtype, int window);
 size_t bwd_dmpart_floats(int dtype, int BH, int T, int D, int window);

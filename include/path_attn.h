@@ -356,14 +356,16 @@ int path_attn_decode_step(const void *q, const void *k, const void *v,
  * checkpoints of the walk at the window boundaries and one window of dM
  * partials at a time, so the workspace grows as about T^1.5 next to linear
  * per-chunk terms: 3.91 GiB at B=2, H=16, T=16384, d=64 in bf16, 6.01 GiB at
- * B=4, H=8, T=8192, d=128 in bf16, 9.90 GiB at B=2, H=16, T=32768, d=64. */
+ * B=4, H=8, T=8192, d=128 in bf16, 9.91 GiB at B=2, H=16, T=32768, d=64. */
 size_t path_attn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 
 /* Workspace bytes of path_attn_bwd with windows of `window` query chunks
- * (window <= 0: the whole sweep as one window, which stores every key level:
- * 17.44 GiB at B=2, H=16, T=16384, d=64 in bf16).  Longer windows mean fewer
- * passes and restarts of the walk, so a faster backward (13.9 ms instead of
- * 15.8 ms at that shape on one MI355X).  path_attn_bwd runs one window when
+ * (window <= 0: the whole sweep as one window, which stores every key level
+ * and keeps the per-chunk matrices of the adjoint instead of computing them
+ * again: 18.19 GiB at B=2, H=16, T=16384, d=64 in bf16).  Longer windows mean
+ * fewer passes and restarts of the walk, so a faster backward (12.8 ms
+ * instead of 15.0 ms at that shape on one MI355X).  path_attn_bwd runs one
+ * window when
  * its workspace allows, else the longest of 128, 64, 32 and 16 query chunks
  * whose layout fits the workspace_bytes it is given.  0 for invalid
  * arguments. */

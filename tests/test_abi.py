@@ -289,10 +289,11 @@ def test_bwd_workspace_windows(dtype, d):
     # (it quadruples with one window)
     assert nb(32768) < 3.0 * nb(16384)
     assert nw(32768, 0) > 3.5 * nw(16384, 0)
-    # the benchmark shape: 17.44 GiB with one window, under 4 GiB by default
+    # the benchmark shape: 18.19 GiB with one window (the saved per-chunk
+    # matrices in bytes of their own), under 4 GiB by default
     big = lib.path_attn_bwd_workspace_bytes_window(2, 16, 16384, 64, pa.BF16, 0)
     small = lib.path_attn_bwd_workspace_bytes(2, 16, 16384, 64, pa.BF16)
-    assert abs(big / 2 ** 30 - 17.44) < 0.01 and small / 2 ** 30 < 4.0
+    assert abs(big / 2 ** 30 - 18.19) < 0.01 and small / 2 ** 30 < 4.0
     assert lib.path_attn_bwd_workspace_bytes_window(1, 1, 64, 96, pa.F32, 16) == 0
 
 
