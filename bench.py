@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu] [--cpu-heads N] [--traffic FILE]
                     [--no-decode] [--decode-steps N] [--no-backward] [--backward-steps N]
-                    [--no-partial] [--no-varlen]
+                    [--no-partial] [--no-varlen] [--no-producer]
 
 One step = one call of path_attn_fwd (gate prefix when present, chunk
 preparation and the streaming scan) over the whole workload, inputs already
@@ -24,7 +24,10 @@ cpu_baseline times the fp64
 CPU oracle on a bounded sample (N whole heads) with all host threads and
 scales the rate to the full workload.  The decode object times decoding
 with in-place key refinement after the workload's prompt (prefill alignment of
-a float32 key cache, then decode steps), bound by HBM.  The backward object
+a float32 key cache, then decode steps), bound by HBM.  The producer object
+times the w / beta producer (path_attn_wbeta: low-rank projection, width-3
+convolution, per-head L2 norm; beta = 2 sigmoid) from hidden states of size
+H d, bound by HBM.  The backward object
 times path_attn_bwd (all gradients, from the forward's out and lse and seeded
 cotangents dout, dlse) on the same workload: algorithmic flops
 B*H*T^2*(5d + 3d^2/64) (the causal products S, dP, dV, dQ, dK of 2d each per
@@ -67,6 +70,8 @@ def parse():
                     help="skip the partial-PaTH (d_path = d / 2) measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the strided / packed forward measurement")
+    ap.add_argument("--no-producer", action="store_true",
+                    help="skip the w / beta producer measurement")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="whole (b, h) heads the CPU oracle runs for its baseline")
     ap.add_argument("--counters", default=os.path.join(ROOT, "profiles", "counters.json"),
@@ -271,6 +276,35 @@ def bench_partial(wl, q, k, v, w, beta, logf, args, timed, ms_full):
     return {"d_path": dp, "ms": ms, "ms_full_path": ms_full, "speedup": ms_full / ms,
             "tokens_per_s": wl.n_tokens / (ms * 1e-3),
             "tflops_path_partial": flops / (ms * 1e-3) / 1e12}
+
+
+def bench_producer(wl, args, timed):
+    """The w / beta producer (path_attn_wbeta) for the workload's B, T, H, d
+    from hidden states of size Dm = H d through a rank R = 64 projection
+    (seeded synthetic bf16 weights): HBM-bound; algorithmic bytes per call
+    B T (2 Dm + 2 H d + 4 H) (read x, write w and beta) plus the weights
+    2 (R Dm + H d R + H Dm) + 12 H d + 4 H."""
+    import torch
+    import householder_position_encoding_amd as pa
+    B, T, H, d = wl.B, wl.T, wl.H, wl.d
+    Dm, R = H * d, 64
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    rn = lambda *shape: torch.randn(*shape, generator=g, device=dev)
+    x = rn(B, T, Dm).to(torch.bfloat16)
+    wd = (rn(R, Dm) / Dm ** 0.5).to(torch.bfloat16)
+    wu = (rn(H * d, R) / R ** 0.5).to(torch.bfloat16)
+    u = (rn(H, Dm) / Dm ** 0.5).to(torch.bfloat16)
+    cw = rn(H * d, 3) / 3 ** 0.5
+    ub = rn(H)
+    wo = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    bo = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ms = timed(lambda: pa.path_attn_wbeta(x, wd, wu, cw, u, ub, H, d, w=wo, beta=bo), args.steps)
+    nbytes = B * T * (2 * Dm + 2 * H * d + 4 * H) + 2 * (R * Dm + H * d * R + H * Dm) + 12 * H * d + 4 * H
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"Dm": Dm, "R": R, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "roofline": {"kernel": "wbeta_kernel", "bound": "hbm", "achieved": gbs, "peak": 8000.0,
+                         "unit": "GB/s", "frac": gbs / 8000.0, "bytes_per_call": nbytes}}
 
 
 def bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms_dense):
@@ -724,6 +758,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_varlen:
         res["varlen"] = bench_varlen(wl, q, k, v, w, beta, logf, args, timed, ms)
+        torch.cuda.empty_cache()
+    if not args.no_producer and wl.dtype == "bf16":
+        res["producer"] = bench_producer(wl, args, timed)
         torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = bench_decode(wl, q, k, v, w, beta, logf, args, timed)

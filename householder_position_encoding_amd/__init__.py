@@ -1,4 +1,5 @@
-"""PaTH attention forward pass for AMD Instinct MI355X (gfx950).
+"""PaTH attention for AMD Instinct MI355X (gfx950): forward, backward, decoding
+and the w / beta producer.
 
 The computation lives in the HIP library ``libpath_attn.so`` (C ABI declared
 in ``include/path_attn.h``).  This package is a thin ctypes binding: it checks
@@ -32,6 +33,7 @@ from .binding import (  # noqa: F401
     path_attn_prepare,
     path_attn_stream,
     path_attn_varlen_workspace_bytes,
+    path_attn_wbeta,
     path_attn_workspace_bytes,
     strerror,
     version,
@@ -45,5 +47,6 @@ __all__ = [
     "path_attn_chunk_prep", "path_attn_decode_step", "path_attn_fwd", "path_attn_fwd_noalloc", "path_attn_fwd_partial",
     "path_attn_fwd_varlen",
     "path_attn_prefill_cache", "path_attn_prepare", "path_attn_stream",
-    "path_attn_varlen_workspace_bytes", "path_attn_workspace_bytes", "strerror", "version",
+    "path_attn_varlen_workspace_bytes", "path_attn_wbeta", "path_attn_workspace_bytes", "strerror",
+    "version",
 ]

@@ -80,6 +80,8 @@ def load_library():
     lib.path_attn_decode_step.argtypes = [vp, vp, vp, vp, fp, fp, vp, vp, vp, ci, vp, fp,
                                           ci, ci, ci, ci, ci, ci, ctypes.c_float, vp, sz, vp]
     lib.path_attn_decode_step.restype = ci
+    lib.path_attn_wbeta.argtypes = [vp, vp, vp, fp, vp, fp, vp, fp, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.path_attn_wbeta.restype = ci
     lib.path_attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.path_attn_bwd_workspace_bytes.restype = sz
     lib.path_attn_bwd_workspace_bytes_window.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -444,6 +446,35 @@ def path_attn_decode_step(cache, q, k, v, w, beta, logf=None, out=None, lse=None
 
 
 # ---------------------------------------------------------------- backward
+
+def path_attn_wbeta(x, wd, wu, cw, u, ub, H: int, d: int, w=None, beta=None, stream=None):
+    """The w / beta producer (path_attn_wbeta): x [B, T, Dm] bf16 hidden
+    states, wd [R, Dm], wu [H*d, R], u [H, Dm] bf16, cw [H*d, 3] and ub [H]
+    float32 -> (w [B, H, T, d] bf16, beta [B, H, T] float32)."""
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, Dm]")
+    B, T, Dm = x.shape
+    R = wd.shape[0]
+    _check(x, "x", (B, T, Dm), torch.bfloat16, x.device)
+    _check(wd, "wd", (R, Dm), torch.bfloat16, x.device)
+    _check(wu, "wu", (H * d, R), torch.bfloat16, x.device)
+    _check(cw, "cw", (H * d, 3), torch.float32, x.device)
+    _check(u, "u", (H, Dm), torch.bfloat16, x.device)
+    _check(ub, "ub", (H,), torch.float32, x.device)
+    if w is None:
+        w = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=x.device)
+    if beta is None:
+        beta = torch.empty((B, H, T), dtype=torch.float32, device=x.device)
+    _check(w, "w", (B, H, T, d), torch.bfloat16, x.device)
+    _check(beta, "beta", (B, H, T), torch.float32, x.device)
+    lib = load_library()
+    st = lib.path_attn_wbeta(_ptr(x), _ptr(wd), _ptr(wu), _ptr(cw), _ptr(u), _ptr(ub), _ptr(w),
+                             _ptr(beta), B, T, Dm, R, H, d, 1, _stream_handle(stream))
+    if st != 0:
+        raise PathAttnError(st, "path_attn_wbeta")
+    return w, beta
+
 
 def path_attn_bwd_workspace_bytes(B: int, H: int, T: int, d: int, dtype: int) -> int:
     return int(load_library().path_attn_bwd_workspace_bytes(B, H, T, d, dtype))

@@ -799,6 +799,29 @@ extern "C" int path_attn_decode_step(const void *q, const void *k, const void *v
              : PATH_ATTN_EHIP;
 }
 
+extern "C" int path_attn_wbeta(const void *x, const void *wd, const void *wu, const float *cw,
+                               const void *u, const float *ub, void *w, float *beta, int B,
+                               int T, int Dm, int R, int H, int d, int dtype, void *stream) {
+  if (B <= 0 || T <= 0 || Dm <= 0 || R <= 0 || H <= 0 || d <= 0) return PATH_ATTN_EINVAL;
+  if (dtype != PATH_ATTN_F32 && dtype != PATH_ATTN_BF16) return PATH_ATTN_EINVAL;
+  if (dtype != PATH_ATTN_BF16 || (d != 64 && d != 128)) return PATH_ATTN_EUNSUPPORTED;
+  if (Dm % 64 != 0 || R % 16 != 0 || R > 128) return PATH_ATTN_EUNSUPPORTED;
+  // int element offsets of a row stay below 2^31; one block per 62 tokens
+  if ((unsigned long long)B * T * Dm >= (1ull << 40) || (unsigned long long)B * H * T * d >= (1ull << 40) ||
+      (unsigned long long)B * wbeta_tiles(T) >= (1ull << 31) || (unsigned long long)H * d * R >= (1ull << 31))
+    return PATH_ATTN_EUNSUPPORTED;
+  const void *ptrs[] = {x, wd, wu, cw, u, ub, w, beta};
+  for (const void *p : ptrs)
+    if (!p) return PATH_ATTN_EINVAL;
+  const void *vecs[] = {x, wd, wu, cw, u, w};   // 16-byte loads and stores
+  for (const void *p : vecs)
+    if (!aligned(p, 16)) return PATH_ATTN_EINVAL;
+  if (!aligned(ub, 4) || !aligned(beta, 4)) return PATH_ATTN_EINVAL;
+  WbetaArgs a{x, wd, wu, u, cw, ub, w, beta, B, T, Dm, R, H, d};
+  return launch_wbeta(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PATH_ATTN_OK
+                                                                          : PATH_ATTN_EHIP;
+}
+
 extern "C" const char *path_attn_strerror(int status) {
   switch (status) {
     case PATH_ATTN_OK: return "ok";

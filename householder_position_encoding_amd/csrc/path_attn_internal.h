@@ -322,4 +322,17 @@ struct BwdArgs {
 };
 hipError_t launch_bwd(int dtype, int D, const BwdArgs &a, void *workspace, hipStream_t s);
 
+// The w / beta producer (producer.hip), bf16: x [B][T][Dm], Wd [R][Dm],
+// Wu [H d][R], cw [H d][3] (float32, oldest tap first), u [H][Dm], ub [H]
+// (float32) -> w [B][H][T][d] (bf16), beta [B][H][T] (float32).
+struct WbetaArgs {
+  const void *x, *wd, *wu, *u;
+  const float *cw, *ub;
+  void *w;
+  float *beta;
+  int B, T, Dm, R, H, d;
+};
+int wbeta_tiles(int T);   // blocks per batch row
+hipError_t launch_wbeta(const WbetaArgs &a, hipStream_t s);
+
 }  // namespace pathattn

@@ -1,0 +1,272 @@
+// producer.hip -- the w / beta producer: the inputs of the transitions from
+// the hidden states (bf16).
+//
+// From the PaTH slides, frame "PaTH inserts a learned transformation along
+// every path" (beta_t = 2 sigmoid(u^T x_t + b), ||w_t||_2 = 1, w_t from a
+// low-rank projection, a convolution of width 3 and an L2 normalisation), and
+// the discussion page's section "Model Architecture Details" (the
+// normalisation per head, the projection low-rank):
+//
+//     z_t    = Wu (Wd x_t)                              Wd: [R][Dm], Wu: [H d][R]
+//     z'_t   = cw[., 0] z_{t-2} + cw[., 1] z_{t-1} + cw[., 2] z_t   (per channel)
+//     w_t[h] = z'_t[h d .. h d + d) / || . ||_2         (0 for a zero vector)
+//     beta_t[h] = 2 sigmoid(u[h] . x_t + ub[h])        u: [H][Dm]
+//
+// One block of four waves per (batch, 62 tokens).  Its 64-row tile starts two
+// tokens early, so that the convolution's earlier tokens are in the tile (2
+// of 64 rows computed twice).  Phase 1: the tile of x times [Wd; u]^T on the
+// bf16 matrix cores (x, Wd and u are bf16 inputs, exact; float32
+// accumulation): the first R columns are y = Wd x, kept in LDS as bf16 hi/lo
+// planes for the second product; the next H columns are beta's logits,
+// finished straight from the accumulators.  Phase 2, one head at a time:
+// z = y Wu_h^T (hi and lo parts of y against the exact bf16 Wu), the head's
+// tile through LDS, then per token the three-tap convolution, the norm over
+// the head's d channels (four threads per token) and the bf16 store of w.
+#include <hip/hip_runtime.h>
+
+#include "path_attn_internal.h"
+#include "tile_fp32.h"
+
+namespace pathattn {
+namespace {
+
+constexpr int kTileRows = 64, kTileOut = kTileRows - 2;   // two halo tokens
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ f32x16 mma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int RMAX>
+__global__ __launch_bounds__(256, D == 128 && RMAX == 128 ? 1 : 2) void wbeta_kernel(
+    const __bf16 *__restrict__ x, const __bf16 *__restrict__ wd, const __bf16 *__restrict__ wu,
+    const float *__restrict__ cw, const __bf16 *__restrict__ u, const float *__restrict__ ub,
+    __bf16 *__restrict__ w, float *__restrict__ beta, int T, int Dm, int R, int H, int ntile) {
+  constexpr int PR = RMAX + 8, PZ = D + 1;   // PZ: a token row's 16 channels per thread, 16 rows per wave, fall in 64 banks
+  constexpr int KC = 64, PK = KC + 8, CG = 128;   // phase 1: k chunk, output column group
+  // LDS: the y planes (hi, then lo) [64][PR], kept from phase 1 to phase 2;
+  // then phase 1's staged chunk of x [64][PK] and of [Wd; u] [CG][PK], whose
+  // bytes phase 2 reuses for one head's z tile [64][PZ], its Wu rows [D][PR]
+  // and the taps of two heads [2][D][3]
+  constexpr int YP = 2 * kTileRows * PR * 2;
+  constexpr int ST1 = (kTileRows + CG) * PK * 2;
+  constexpr int ST2 = kTileRows * PZ * 4 + D * PR * 2 + 2 * D * 3 * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[YP + (ST1 > ST2 ? ST1 : ST2)];
+  __bf16 *yp = reinterpret_cast<__bf16 *>(smem);
+  __bf16 *xs = reinterpret_cast<__bf16 *>(smem + YP), *ws = xs + kTileRows * PK;
+  float *zs = reinterpret_cast<float *>(smem + YP);
+  __bf16 *wub = reinterpret_cast<__bf16 *>(smem + YP + kTileRows * PZ * 4);
+  float *cwl = reinterpret_cast<float *>(smem + YP + kTileRows * PZ * 4 + D * PR * 2);
+  const int b = blockIdx.x / ntile, tile = blockIdx.x % ntile;
+  const int t0 = tile * kTileOut - 2;   // token of tile row 0
+  int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, g = lane >> 5, n = lane & 31;
+  // the head's Wu rows and taps: R / 8 16-byte pieces per row, 3 D taps
+  const int wpieces = D * (R / 8);
+  constexpr int WPT = D * (RMAX / 8) / 256, CPT = (3 * D + 255) / 256;   // per thread, at most
+  bf16x8 wpre[WPT];
+  float cpre[CPT];
+  auto fetch_head = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int pi = tid + 256 * j;
+      if (pi < wpieces) {
+        const int row = pi / (R / 8), c8 = 8 * (pi % (R / 8));
+        wpre[j] = ld8(wu + ((size_t)h * D + row) * R + c8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int e = tid + 256 * j;
+      if (e < 3 * D) cpre[j] = cw[(size_t)h * D * 3 + e];
+    }
+  };
+  auto put_head = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int pi = tid + 256 * j;
+      if (pi < wpieces) {
+        const int row = pi / (R / 8), c8 = 8 * (pi % (R / 8));
+        *reinterpret_cast<bf16x8 *>(wub + row * PR + c8) = wpre[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int e = tid + 256 * j;
+      if (e < 3 * D) cwl[(h & 1) * 3 * D + e] = cpre[j];
+    }
+  };
+
+  // ---- phase 1: [y | logits] = X [Wd; u]^T, 64 x NC (NC = R + H, rounded up
+  // to 32), in groups of up to CG output columns; each group walks Dm in
+  // chunks of KC staged in LDS (16-byte pieces, whole rows), the next chunk
+  // loaded into registers while the current one is multiplied
+  const int NC = (R + H + 31) / 32 * 32;
+  constexpr int XPT = kTileRows * (KC / 8) / 256, WPC = CG * (KC / 8) / 256;   // pieces per thread
+  for (int cg = 0; cg < NC; cg += CG) {
+    const int ncg = NC - cg < CG ? NC - cg : CG, ntl = 2 * (ncg / 32);
+    bf16x8 xr[XPT], wr[WPC];
+    auto load_chunk = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int pi = tid + 256 * j, row = pi / (KC / 8), c8 = 8 * (pi % (KC / 8));
+        const int tok = t0 + row;
+        const bool ok = tok >= 0 && tok < T;
+        xr[j] = ld8(x + ((size_t)b * T + (ok ? tok : 0)) * Dm + k0 + c8);
+        if (!ok) xr[j] = bf16x8{};
+      }
+#pragma unroll
+      for (int j = 0; j < WPC; ++j) {
+        const int pi = tid + 256 * j, row = pi / (KC / 8), c8 = 8 * (pi % (KC / 8));
+        const int col = cg + row;   // output column: Wd row, u row, or zero
+        const __bf16 *src = col < R ? wd + (size_t)col * Dm : u + (size_t)(col < R + H ? col - R : 0) * Dm;
+        wr[j] = ld8(src + k0 + c8);
+        if (col >= R + H || row >= ncg) wr[j] = bf16x8{};
+      }
+    };
+    f32x16 acc[2];
+    zero16(acc[0]);
+    zero16(acc[1]);
+    load_chunk(0);
+    for (int k0 = 0; k0 < Dm; k0 += KC) {
+      __syncthreads();   // the previous chunk's fragments are read
+#pragma unroll
+      for (int j = 0; j < XPT; ++j) {
+        const int pi = tid + 256 * j;
+        *reinterpret_cast<bf16x8 *>(xs + (pi / (KC / 8)) * PK + 8 * (pi % (KC / 8))) = xr[j];
+      }
+#pragma unroll
+      for (int j = 0; j < WPC; ++j) {
+        const int pi = tid + 256 * j;
+        *reinterpret_cast<bf16x8 *>(ws + (pi / (KC / 8)) * PK + 8 * (pi % (KC / 8))) = wr[j];
+      }
+      __syncthreads();
+      if (k0 + KC < Dm) load_chunk(k0 + KC);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ti = wv + 4 * j;
+        if (ti < ntl) {
+          const int mh = ti & 1, nb = ti >> 1;
+          const __bf16 *pa = xs + (32 * mh + n) * PK + 8 * g, *pb = ws + (32 * nb + n) * PK + 8 * g;
+#pragma unroll
+          for (int s2 = 0; s2 < KC / 16; ++s2) acc[j] = mma16(ld8(pa + 16 * s2), ld8(pb + 16 * s2), acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ti = wv + 4 * j;
+      if (ti >= ntl) continue;
+      const int mh = ti & 1, col = cg + 32 * (ti >> 1) + n;
+      if (col < R) {   // y: hi / lo planes, row = tile row, column = col
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * mh + acc_row(r, g);
+          const __bf16 hi = (__bf16)acc[j][r];
+          yp[row * PR + col] = hi;
+          yp[kTileRows * PR + row * PR + col] = (__bf16)(acc[j][r] - (float)hi);
+        }
+      } else if (col < R + H) {   // beta of head col - R for the tile's output rows
+        const int h = col - R;
+        const float bh = ub[h];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * mh + acc_row(r, g), t = t0 + row;
+          if (row >= 2 && t < T)
+            beta[((size_t)b * H + h) * T + t] = 2.f / (1.f + __expf(-(acc[j][r] + bh)));
+        }
+      }
+    }
+  }
+  fetch_head(0);
+  __syncthreads();   // phase 1's staging bytes are free
+  put_head(0);
+  __syncthreads();
+
+  // ---- phase 2, per head: z = y Wu_h^T, convolution, normalisation.  The
+  // next head's Wu rows and taps are loaded while this head is finished.
+  for (int h = 0; h < H; ++h) {
+    // the thread index re-derived per head, so that the addresses below are
+    // not computed for all heads up front and kept live
+    asm volatile("" : "+v"(tid));
+    for (int ti = wv; ti < 2 * (D / 32); ti += 4) {
+      const int mh = ti & 1, nb = ti >> 1;
+      const __bf16 *ya = yp + (32 * mh + n) * PR + 8 * g;
+      const __bf16 *wb = wub + (32 * nb + n) * PR + 8 * g;
+      f32x16 acc;
+      zero16(acc);
+#pragma unroll
+      for (int s = 0; s < RMAX / 16; ++s)
+        if (s < R / 16) {
+          const bf16x8 bw = ld8(wb + 16 * s);
+          acc = mma16(ld8(ya + 16 * s), bw, acc);                    // y hi
+          acc = mma16(ld8(ya + kTileRows * PR + 16 * s), bw, acc);   // y lo
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zs[(32 * mh + acc_row(r, g)) * PZ + 32 * nb + n] = acc[r];
+    }
+    if (h + 1 < H) fetch_head(h + 1);
+    __syncthreads();   // the head's z tile is complete, and every wave is done with wub
+    const int i = tid >> 2, q4 = tid & 3, c0 = q4 * (D / 4);   // token row, quarter of d
+    const int tok = t0 + i;
+    const bool out_row = i >= 2 && tok < T;
+    float v[D / 4];
+    float ss = 0.f;
+    const float *tp = cwl + (h & 1) * 3 * D + 3 * c0;   // taps of this thread's channels
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const int cc = c0 + c;
+      const float z0 = i >= 2 ? zs[(i - 2) * PZ + cc] : 0.f;
+      const float z1 = i >= 1 ? zs[(i - 1) * PZ + cc] : 0.f;
+      const float z2 = zs[i * PZ + cc];
+      const float y = tp[3 * c] * z0 + tp[3 * c + 1] * z1 + tp[3 * c + 2] * z2;
+      v[c] = y;
+      ss = __builtin_fmaf(y, y, ss);
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);   // the token's d channels
+    if (out_row) {
+      const float inv = ss > 0.f ? 1.f / __builtin_sqrtf(ss) : 0.f;
+      __bf16 *dst = w + (((size_t)b * H + h) * T + tok) * D + c0;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 4; c8 += 8) {
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (__bf16)(v[c8 + e] * inv);
+        *reinterpret_cast<bf16x8 *>(dst + c8) = o;
+      }
+    }
+    if (h + 1 < H) put_head(h + 1);   // wub is free; the taps go to the other buffer
+    __syncthreads();   // the z tile is read, and the next head's operands are in place
+  }
+}
+
+}  // namespace
+
+int wbeta_tiles(int T) { return (T + kTileOut - 1) / kTileOut; }
+
+hipError_t launch_wbeta(const WbetaArgs &a, hipStream_t s) {
+  const int ntile = wbeta_tiles(a.T);
+  const dim3 grid((unsigned)a.B * ntile), block(256);
+  const auto *x = static_cast<const __bf16 *>(a.x), *wd = static_cast<const __bf16 *>(a.wd);
+  const auto *wu = static_cast<const __bf16 *>(a.wu), *u = static_cast<const __bf16 *>(a.u);
+  auto *w = static_cast<__bf16 *>(a.w);
+  // the LDS is sized for R <= 64 or R <= 128
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, x, wd, wu, a.cw, u, a.ub, w, a.beta, a.T, a.Dm,
+                       a.R, a.H, ntile);
+  };
+  if (a.d == 64) {
+    if (a.R <= 64) go(wbeta_kernel<64, 64>);
+    else go(wbeta_kernel<64, 128>);
+  } else {
+    if (a.R <= 64) go(wbeta_kernel<128, 64>);
+    else go(wbeta_kernel<128, 128>);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pathattn

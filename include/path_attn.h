@@ -503,6 +503,39 @@ int path_attn_bwd_varlen(const void *q, const void *k, const void *v, const void
                          int B, int H, int T, int d, int dtype, float scale,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * The w / beta producer: the transitions' inputs from the hidden states.
+ *
+ * From the slides' frame "PaTH inserts a learned transformation along every
+ * path" (beta_t = 2 sigmoid(u^T x_t + b), ||w_t||_2 = 1, w_t produced by a
+ * low-rank projection, a width-3 convolution and an L2 normalisation) and the
+ * discussion page's "Model Architecture Details" (the normalisation per head,
+ * the projection low-rank), for H heads of size d:
+ *     z_t       = Wu (Wd x_t)
+ *     z'_t[c]   = cw[c][0] z_{t-2}[c] + cw[c][1] z_{t-1}[c] + cw[c][2] z_t[c]
+ *                 (causal, z_t = 0 for t < 0)
+ *     w_t[h]    = z'_t[h d .. h d + d) / || . ||_2   (0 if the vector is zero)
+ *     beta_t[h] = 2 sigmoid(u[h] . x_t + ub[h])
+ * (no biases in the projections, no activation after the convolution).
+ *   x  : [B, T, Dm] bf16, row-major (hidden states; input)
+ *   wd : [R, Dm] bf16 (low-rank down projection, output-major; input)
+ *   wu : [H*d, R] bf16 (up projection; input)
+ *   cw : [H*d, 3] float32 (convolution taps, oldest first; input)
+ *   u  : [H, Dm] bf16, ub : [H] float32 (beta's projection and bias; inputs)
+ *   w  : [B, H, T, d] bf16 (output, overwritten: path_attn_fwd's w layout)
+ *   beta : [B, H, T] float32 (output, overwritten)
+ * dtype must be PATH_ATTN_BF16.  Any T >= 1.  x, wd, wu, cw, u and w 16-byte
+ * aligned, ub and beta 4-byte aligned.  Runs on the caller's stream; needs
+ * no workspace.
+ * Errors: EINVAL for null or misaligned pointers, sizes <= 0 or a bad dtype;
+ * EUNSUPPORTED for PATH_ATTN_F32, d not in {64, 128}, Dm not a multiple of
+ * 64, R not a multiple of 16 or above 128, or sizes beyond the library's
+ * indexing; EHIP on a launch error.
+ */
+int path_attn_wbeta(const void *x, const void *wd, const void *wu, const float *cw,
+                    const void *u, const float *ub, void *w, float *beta, int B, int T,
+                    int Dm, int R, int H, int d, int dtype, void *stream);
+
 /* Static, human-readable description of a status code. */
 const char *path_attn_strerror(int status);
 

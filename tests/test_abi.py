@@ -477,3 +477,25 @@ def test_partial_workspace_fits_the_full_one():
     assert lib.path_attn_fwd_partial(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 2, 256, 64,
                                      32, pa.BF16, 0.0, 0, FAKE, 100, None) == EINVAL
     assert need > 100
+
+
+def test_wbeta_validation():
+    """path_attn_wbeta rejects bad arguments before any HIP call: every call
+    below has exactly one invalid argument (the pointers are aligned
+    stand-ins, never dereferenced)."""
+    lib = pa.load_library()
+    P = 1 << 20
+
+    def call(x=P, wd=P, wu=P, cw=P, u=P, ub=P, w=P, beta=P, B=1, T=64, Dm=64, R=32, H=2, d=64,
+             dtype=pa.BF16):
+        return lib.path_attn_wbeta(x, wd, wu, cw, u, ub, w, beta, B, T, Dm, R, H, d, dtype, None)
+
+    for name in ("x", "wd", "wu", "cw", "u", "ub", "w", "beta"):
+        assert call(**{name: None}) == EINVAL, name
+    for name in ("x", "wd", "wu", "cw", "u", "w"):
+        assert call(**{name: P + 8}) == EINVAL, name   # 16-byte loads and stores
+    assert call(ub=P + 2) == EINVAL and call(beta=P + 2) == EINVAL
+    for kw in ({"B": 0}, {"T": 0}, {"Dm": 0}, {"R": 0}, {"H": 0}, {"d": 0}, {"dtype": 7}):
+        assert call(**kw) == EINVAL, kw
+    for kw in ({"dtype": pa.F32}, {"d": 96}, {"Dm": 40}, {"Dm": 96}, {"R": 24}, {"R": 144}):
+        assert call(**kw) == EUNSUP, kw
