@@ -384,8 +384,11 @@ size_t path_attn_bwd_workspace_bytes_window(int B, int H, int T, int d, int dtyp
  *                                                      logf, where it is required;
  *                                                      dlogf[.., 0] = 0 as f_0
  *                                                      enters no logit)
- * scale: as for path_attn_fwd_ex (0 selects 1/sqrt(d)).  Gradients with
- * dtype PATH_ATTN_BF16 are computed in float32 and rounded once (RNE).
+ * scale: as for path_attn_fwd_ex (0 selects 1/sqrt(d)).  With dtype
+ * PATH_ATTN_BF16 the gradients are accumulated in float32 and rounded once
+ * (RNE): the quadratic products take bf16 operands (the forward's), the
+ * per-chunk algebra keeps float32 values and multiplies them as bf16 hi/lo
+ * pairs (about 16 significant bits).
  * Any T >= 1: a T that is not a multiple of 64 is run at the next multiple
  * with padded tokens as in the forward (identity factors, zero q, k, v, dout,
  * dlse and gate, lse = 0), which contribute nothing to any gradient; the
