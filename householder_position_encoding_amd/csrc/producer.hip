@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256, D == 128 && RMAX == 128 ? 1 : 2) void wbeta_ke
     const __bf16 *__restrict__ x, const __bf16 *__restrict__ wd, const __bf16 *__restrict__ wu,
     const float *__restrict__ cw, const __bf16 *__restrict__ u, const float *__restrict__ ub,
     __bf16 *__restrict__ w, float *__restrict__ beta, int T, int Dm, int R, int H, int ntile) {
-  constexpr int PR = RMAX + 8, PZ = D + 1;   // PZ: a token row's 16 channels per thread, 16 rows per wave, fall in 64 banks
+  constexpr int PR = RMAX + 8, PZ = D + 1;
   constexpr int KC = 64, PK = KC + 8, CG = 128;   // phase 1: k chunk, output column group
   // LDS: the y planes (hi, then lo) [64][PR], kept from phase 1 to phase 2;
   // then phase 1's staged chunk of x [64][PK] and of [Wd; u] [CG][PK], whose
@@ -210,33 +210,44 @@ __global__ __launch_bounds__(256, D == 128 && RMAX == 128 ? 1 : 2) void wbeta_ke
     }
     if (h + 1 < H) fetch_head(h + 1);
     __syncthreads();   // the head's z tile is complete, and every wave is done with wub
-    const int i = tid >> 2, q4 = tid & 3, c0 = q4 * (D / 4);   // token row, quarter of d
-    const int tok = t0 + i;
-    const bool out_row = i >= 2 && tok < T;
-    float v[D / 4];
-    float ss = 0.f;
-    const float *tp = cwl + (h & 1) * 3 * D + 3 * c0;   // taps of this thread's channels
+    // the convolution, the norm over the head's d channels and the store of
+    // w: TPR threads per token (d = 64: four, 16 consecutive channels each;
+    // d = 128: eight, channel runs 8 q .. and 64 + 8 q ..), so that a wave's
+    // reads of a row of z fall in distinct banks (pitch D + 1)
+    constexpr int TPR = D / 16, RPP = 256 / TPR;   // threads per token, rows per pass
 #pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
-      const int cc = c0 + c;
-      const float z0 = i >= 2 ? zs[(i - 2) * PZ + cc] : 0.f;
-      const float z1 = i >= 1 ? zs[(i - 1) * PZ + cc] : 0.f;
-      const float z2 = zs[i * PZ + cc];
-      const float y = tp[3 * c] * z0 + tp[3 * c + 1] * z1 + tp[3 * c + 2] * z2;
-      v[c] = y;
-      ss = __builtin_fmaf(y, y, ss);
-    }
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);   // the token's d channels
-    if (out_row) {
-      const float inv = ss > 0.f ? 1.f / __builtin_sqrtf(ss) : 0.f;
-      __bf16 *dst = w + (((size_t)b * H + h) * T + tok) * D + c0;
+    for (int pass = 0; pass < kTileRows / RPP; ++pass) {
+      const int i = tid / TPR + RPP * pass, q = tid % TPR;
+      const int tok = t0 + i;
+      // channel e of this thread (e < 16)
+      auto chan = [&](int e) __attribute__((always_inline)) {
+        return D == 64 ? 16 * q + e : (e < 8 ? 8 * q + e : 64 + 8 * q + e - 8);
+      };
+      float v[16];
+      float ss = 0.f;
+      const float *tw = cwl + (h & 1) * 3 * D;
 #pragma unroll
-      for (int c8 = 0; c8 < D / 4; c8 += 8) {
-        bf16x8 o;
+      for (int e = 0; e < 16; ++e) {
+        const int cc = chan(e);
+        const float z0 = i >= 2 ? zs[(i - 2) * PZ + cc] : 0.f;
+        const float z1 = i >= 1 ? zs[(i - 1) * PZ + cc] : 0.f;
+        const float z2 = zs[i * PZ + cc];
+        const float y = tw[3 * cc] * z0 + tw[3 * cc + 1] * z1 + tw[3 * cc + 2] * z2;
+        v[e] = y;
+        ss = __builtin_fmaf(y, y, ss);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (__bf16)(v[c8 + e] * inv);
-        *reinterpret_cast<bf16x8 *>(dst + c8) = o;
+      for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o);   // the token's d channels
+      if (i >= 2 && tok < T) {
+        const float inv = ss > 0.f ? 1.f / __builtin_sqrtf(ss) : 0.f;
+        __bf16 *dst = w + (((size_t)b * H + h) * T + tok) * D;
+#pragma unroll
+        for (int r8 = 0; r8 < 2; ++r8) {
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (__bf16)(v[8 * r8 + e] * inv);
+          *reinterpret_cast<bf16x8 *>(dst + chan(8 * r8)) = o;
+        }
       }
     }
     if (h + 1 < H) put_head(h + 1);   // wub is free; the taps go to the other buffer
