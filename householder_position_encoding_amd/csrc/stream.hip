@@ -526,7 +526,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 x = *reinterpret_cast<const f32x4 *>(src + (j * NDB + mb) * 1024 + 4 * r4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qw[j][mb][4 * r4 + e] = x[e];
+          for (int e = 0; e < 4; ++e) qw[j][mb][4 * r4 + e] = FOX ? x[e] : x[e] * sl2;
         }
   }
 
@@ -534,25 +534,30 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
   // p = 2^(x - m), packed to the bf16 B operands of P.V; returns the lane's
   // partial sum of the packed weights.
   // x is already in log2 units when mul == 1 (diagonal, gated scores),
-  // raw scores with mul = scale * log2(e) otherwise.
-  auto exp_pack = [&](const f32x16 (&x)[2], float mul, float m, frag (&pb)[NSK]) -> float {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  // raw scores with mul = scale * log2(e) otherwise.  REL: x is already
+  // x - m (the cross steps without the gate), mul and m are not used, and
+  // the weights are summed onto l0 in one chain (the caller keeps l0).
+  auto exp_pack = [&](const f32x16 (&x)[2], float mul, float m, frag (&pb)[NSK],
+                      auto rel, float l0 = 0.f) -> float {
+    constexpr bool REL = decltype(rel)::value;
+    float part[4] = {REL ? l0 : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NSK; ++s) {
       f32x16 pr[2];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int rg = s * 8 + t;
-        pr[rg / 16][rg % 16] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rg / 16][rg % 16], mul, -m));
+        const float xv = x[rg / 16][rg % 16];
+        pr[rg / 16][rg % 16] = __builtin_amdgcn_exp2f(REL ? xv : __builtin_fmaf(xv, mul, -m));
       }
       pb[s] = MF::pack(pr, s);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const bf16x2 pair = {pb[s][2 * h], pb[s][2 * h + 1]};
-        part[h] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[h], false);
+        part[REL ? 0 : h] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[REL ? 0 : h], false);
       }
     }
-    return (part[0] + part[1]) + (part[2] + part[3]);
+    return REL ? part[0] : (part[0] + part[1]) + (part[2] + part[3]);
   };
   auto pv = [&](const frag (&pb)[2][NSK], const E *vb) {
 #pragma unroll
@@ -603,7 +608,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
             }
           }
         m_run[j] = fmaxf(mx, __shfl_xor(mx, 32));
-        l_run[j] = exp_pack(sc[j], 1.f, m_run[j], pb[j]);
+        l_run[j] = exp_pack(sc[j], 1.f, m_run[j], pb[j], std::false_type{});
       }
       pv(pb, vf_l);
     } else if (valid && c < qcw) {
@@ -629,13 +634,15 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int s = 0; s < NSD; ++s) qb[j][s] = MF::pack(qw[j], s);
-      // S^T = ->K_c Q_work^T for both column blocks
+      // S^T = ->K_c Q_work^T for both column blocks.  Without the gate the
+      // tile is pre-scaled by scale * log2(e) and the products start from
+      // -m_run, so the scores come out as x - m_run in log2 units
 #pragma unroll
       for (int kb = 0; kb < 2 && !skip_blk; ++kb) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sc[j][kb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) sc[j][kb][r] = FOX ? 0.f : -m_run[j];
 #pragma unroll
         for (int s = 0; s < NSD; ++s) {
           const frag a = MF::load(kf_l + (kb * NSD + s) * FRAG + lane * KPL);
@@ -656,16 +663,17 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       }
       if (!skip_blk) {
       if (!FOX) {
-        // weights against the running max without a max pass; a chunk whose
-        // weights exceed 2^11 (or are not finite) is redone against
-        // max(m_run, chunk max - 8) after rescaling O and l
+        // weights against the running max without a max pass (the scores
+        // are x - m_run already); a chunk whose weights exceed 2^11 (or are
+        // not finite) is redone against max(m_run, chunk max - 8) after
+        // rescaling O and l
         frag pb[2][NSK];
-        float lsum[2];
+        float lnew[2];
         bool big = false;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          lsum[j] = exp_pack(sc[j], sl2, m_run[j], pb[j]);
-          big = big || !(lsum[j] <= 2048.f);
+          lnew[j] = exp_pack(sc[j], 1.f, 0.f, pb[j], std::true_type{}, l_run[j]);
+          big = big || !(lnew[j] - l_run[j] <= 2048.f);
         }
         if (__any(big)) {   // wave-uniform, rare
 #pragma unroll
@@ -675,20 +683,20 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[j][kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-            const float m_new = fmaxf(m_run[j], mx - 8.f);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_new);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float up = fmaxf(0.f, mx - 8.f);   // m_new - m_run
+            const float alpha = __builtin_amdgcn_exp2f(-up);
             l_run[j] *= alpha;
 #pragma unroll
             for (int mb = 0; mb < NDB; ++mb)
 #pragma unroll
               for (int r = 0; r < 16; ++r) o[j][mb][r] *= alpha;
-            m_run[j] = m_new;
-            lsum[j] = exp_pack(sc[j], sl2, m_new, pb[j]);
+            m_run[j] += up;
+            lnew[j] = l_run[j] + exp_pack(sc[j], 1.f, up, pb[j], std::false_type{});
           }
         }
-        l_run[0] += lsum[0];
-        l_run[1] += lsum[1];
+        l_run[0] = lnew[0];
+        l_run[1] = lnew[1];
         pv(pb, vf_l);
       } else {
       // online softmax in log2 units, x = S * scale * log2(e) + a_key; the
@@ -724,7 +732,7 @@ __global__ __launch_bounds__(NQC * 64, 2) void stream_wide_kernel(
       frag pb[2][NSK];
       float lsum[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) lsum[j] = exp_pack(sc[j], FOX ? 1.f : sl2, m_ref[j], pb[j]);
+      for (int j = 0; j < 2; ++j) lsum[j] = exp_pack(sc[j], FOX ? 1.f : sl2, m_ref[j], pb[j], std::false_type{});
       if (__any(grow)) {   // wave-uniform
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
