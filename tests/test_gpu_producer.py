@@ -63,6 +63,8 @@ CASES = [
     (1, 1, 64, 16, 1, 64),       # a single token
     (1, 200, 128, 64, 3, 128),
     (2, 125, 64, 128, 1, 128),   # R at its maximum
+    (2, 190, 128, 96, 2, 64),    # d = 64 with R past 64 (the wider Wu staging)
+    (1, 100, 192, 32, 3, 64),    # an odd head count: the last head alone; Dm of three chunks
 ]
 
 
